@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the 2-bit draft head.
+
+This module only draws random numbers and rounds them to bf16 storage. It
+holds none of the head's arithmetic (no quantisation, packing, scoring or
+selection), so the HIP path and the CPU oracle can both be fed from it.
+
+The workload it imitates is the one the radiance_drafthead.py page describes
+in its module docstring: per tensor-parallel rank the draft head is
+x[M, 5120] @ W[5120, 124160], run once per draft slot, with M from 1 to 72.
+The page measured on hidden states captured from a live serve, which are not
+available; the stand-ins are:
+
+* W: bf16, N(0, 0.02), generated in 8192-row chunks in row order.
+* x: bf16, N(0, 1), with 1% of the hidden channels (a fixed set shared by all
+  rows) scaled by 8 to imitate activation outliers.  x is always generated as
+  72 rows and the first M are used, so M = 1, 8 and 72 nest.
+
+All arrays are returned as raw bf16 bit patterns (numpy uint16).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+# Shapes of one rank's vocabulary shard of the head (module docstring of the
+# radiance_drafthead.py page).
+HIDDEN = 5120
+VOCAB_SHARD = 124160
+X_ROWS_GENERATED = 72
+
+SEED_W = 1
+SEED_X = 2
+SEED_OUTLIERS = 3
+SEED_PLANT = 4
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); bit patterns."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    nan = np.isnan(a)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16))
+    r = r.astype(np.uint16)
+    if nan.any():
+        r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def gen_weight(n: int, k: int, seed: int = SEED_W, std: float = 0.02,
+               chunk: int = 8192) -> np.ndarray:
+    """bf16 weight [n][k] (row n = vocabulary token n), N(0, std)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = np.empty((n, k), dtype=np.uint16)
+    for i in range(0, n, chunk):
+        j = min(i + chunk, n)
+        blk = rng.standard_normal((j - i, k), dtype=np.float32)
+        blk *= np.float32(std)
+        out[i:j] = f32_to_bf16_bits(blk)
+    return out
+
+
+def outlier_channels(k: int, frac: float = 0.01, seed: int = SEED_OUTLIERS) -> np.ndarray:
+    cnt = int(round(frac * k))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.sort(rng.choice(k, size=cnt, replace=False))
+
+
+def gen_x(m: int, k: int, seed: int = SEED_X, outliers: bool = True,
+          outlier_scale: float = 8.0, rows_generated: int | None = None) -> np.ndarray:
+    """bf16 activations [m][k]: N(0, 1), optionally 1% of channels scaled by 8."""
+    rows = max(m, X_ROWS_GENERATED if rows_generated is None else rows_generated)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    xf = rng.standard_normal((rows, k), dtype=np.float32)
+    if outliers:
+        xf[:, outlier_channels(k)] *= np.float32(outlier_scale)
+    return f32_to_bf16_bits(xf[:m])
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    m: int
+    k: int
+    n: int
+    kcand: int = 8
+    rerank: int = 32
+    outliers: bool = True
+    seed_w: int = SEED_W
+    seed_x: int = SEED_X
+
+
+# The tiny case, one rank's shard at M = 1, 8 and 72, and the recall stress
+# case (planted near-ties, see plant_recall_pairs).
+CONFIGS = {
+    "tiny": Config("tiny", 1, 1024, 16384, outliers=False, seed_w=11, seed_x=12),
+    "m1": Config("m1", 1, HIDDEN, VOCAB_SHARD),
+    "m8": Config("m8", 8, HIDDEN, VOCAB_SHARD),
+    "m72": Config("m72", 72, HIDDEN, VOCAB_SHARD),
+    "recall": Config("recall", 32, HIDDEN, VOCAB_SHARD),
+}
+
+
+def make_inputs(cfg: Config):
+    """(x bits [m][k], W bits [n][k]) for a config."""
+    w = gen_weight(cfg.n, cfg.k, seed=cfg.seed_w)
+    x = gen_x(cfg.m, cfg.k, seed=cfg.seed_x, outliers=cfg.outliers)
+    return x, w
+
+
+def plant_recall_pairs(x_bits: np.ndarray, w_bits: np.ndarray, target: float = 12.0,
+                       gap: float = 0.01, seed: int = SEED_PLANT, block: int = 64):
+    """Plant, for each row m of x, two columns of one 64-column block whose exact
+    logits are `target` and `target - gap`, far above every other logit of the row.
+
+    This builds the situation the module docstring of the radiance_drafthead.py
+    page names as the reason KCAND is the recall lever: the winner shares its
+    block with another strong token.  Returns (w_bits_planted, pairs) where
+    pairs[m] = (c1, c2) is the planted (winner, runner-up).  W is modified on a
+    copy: each planted row becomes base + alpha * x_m rounded to bf16, then a
+    few single-channel corrections on large non-outlier channels of x_m bring
+    its logit to within a small fraction of `gap` of the target.  Raises if a
+    planted pair does not end up as its row's top two with a gap in
+    [gap / 2, 2 * gap].
+    """
+    m, k = x_bits.shape
+    n = w_bits.shape[0]
+    full_blocks = n // block
+    if m > full_blocks:
+        raise ValueError("need at least one full block per planted row")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    blocks = rng.choice(full_blocks, size=m, replace=False)
+    w = w_bits.copy()
+    xf = bf16_bits_to_f32(x_bits).astype(np.float64)
+    outl = set(int(v) for v in outlier_channels(k))
+    pairs = []
+    for row in range(m):
+        b = int(blocks[row])
+        c1, c2 = (int(v) for v in rng.choice(block, size=2, replace=False))
+        c1 += b * block
+        c2 += b * block
+        xm = xf[row]
+        xx = float(xm @ xm)
+        order = [int(i) for i in np.argsort(-np.abs(xm)) if int(i) not in outl]
+        for col, tgt in ((c1, target), (c2, target - gap)):
+            base = bf16_bits_to_f32(w[col]).astype(np.float64)
+            alpha = (tgt - float(base @ xm)) / xx
+            wf = bf16_bits_to_f32(f32_to_bf16_bits((base + alpha * xm).astype(np.float32))).astype(np.float64)
+            for ch in order[:16]:
+                resid = tgt - float(wf @ xm)
+                if abs(resid) < 1e-3 * gap:
+                    break
+                wf[ch] = float(bf16_bits_to_f32(f32_to_bf16_bits(
+                    np.array([wf[ch] + resid / xm[ch]], dtype=np.float32)))[0])
+            w[col] = f32_to_bf16_bits(wf.astype(np.float32))
+        pairs.append((c1, c2))
+    # verify on the final weights
+    logits = np.concatenate([bf16_bits_to_f32(w[i:i + 8192]).astype(np.float64) @ xf.T
+                             for i in range(0, n, 8192)], axis=0)
+    for row, (c1, c2) in enumerate(pairs):
+        lg = logits[:, row]
+        top = np.argsort(-lg, kind="stable")[:2]
+        d = lg[c1] - lg[c2]
+        if [int(top[0]), int(top[1])] != [c1, c2] or not (gap / 2 <= d <= 2 * gap):
+            raise RuntimeError(f"planting failed for row {row}: top {top}, gap {d}")
+    return w, pairs

@@ -1,0 +1,37 @@
+"""CPU oracle for the 2-bit speculative-draft LM head.
+
+TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, step-by-step CPU
+implementation of what the draft head computes, written from the page
+"radiance_drafthead.py" (a vLLM plug-in module; its module docstring, the
+quantiser `_quantize_head_now`, the kernels `_draft_head_int2`, `_emit`,
+`_rerank_exact` and the per-call glue `_apply_head_int2`).  Only the tests,
+`__graft_entry__.smoke()` and the `cpu_baseline` leg of `bench.py` may use it.
+The product library never imports it and it imports nothing from the product
+library.
+
+Modules
+-------
+bf16     bf16 <-> float conversions (round to nearest even), own code.
+quant    min/max asymmetric int2 quantiser, quarter-split packing, unpacking
+         and the effective weight defined by the stored scale pair.
+head     coarse scores, block top-KCAND, row top-R, exact rerank, argmax, and
+         the exact bf16 head (for agreement reports only).
+brute    pure-Python, exact-rational re-statement of every step for tiny
+         shapes; pins the vectorised code.
+
+Every function cites the passage it follows.  Where the page is silent the
+reading taken is stated in the docstring; all readings are listed in the
+design notes of the repository.
+
+Parity status: every function here is pinned by a `-m "not gpu"` test
+(tests/test_oracle_pins.py) against a page identity, a closed form, a
+hand-derived fixture under tests/golden/, a special case or exact brute force.
+The page's real-data claims (argmax agreement on 8192 captured serve inputs,
+the ~5% top-1 change of the unreranked head) are parity unpinned: the captured
+inputs and the real weights are not available.
+"""
+from . import bf16, quant, head, brute  # noqa: F401
+from .quant import (GROUP, quantize, pack_quarter_split, unpack_quarter_split,  # noqa: F401
+                    effective_weight, quantize_pack)
+from .head import (BLOCK_N, coarse, coarse_collapse, block_topk, row_topr,  # noqa: F401
+                   rerank_exact, final_argmax, exact_head, pipeline, tie_rows)

@@ -1,0 +1,210 @@
+"""Per-call steps of the draft head (oracle).
+
+Follows `_apply_head_int2` on the radiance_drafthead.py page and the kernels
+it launches: `_draft_head_int2` (coarse scores), `_emit` (top-KCAND of each
+64-column block by successive max-and-mask), the row top-R of the candidates
+(`bm.topk(RERANK)` then `bi.gather`), `_rerank_exact` (exact dot of x with
+the bf16 weight row of each candidate) and the final argmax the caller takes.
+
+Precision: coarse scores and exact logits are accumulated in float64 and
+reported both in float64 (for margins) and rounded to float32 (the page's
+kernels accumulate in float32).
+
+Readings where the page is silent (all also listed in the design notes):
+* Ties rank the lower column id first, at every stage (Triton's argmax takes
+  the first maximum; torch.topk's tie order is unspecified).
+* A block with fewer than KCAND valid columns (the partial last block) pads
+  its list with (-inf, id -1); a row with fewer than R valid candidates pads
+  the same way.
+* The final token is the argmax over the R exact values (the page writes the
+  exact values back into a bf16 row and leaves the argmax to the caller).
+  The decision is taken on the float32 values, ties to the lower id.
+* M is the true number of rows (the page pads M to a power of two >= 16 only
+  because its Triton dot needs it).
+"""
+import numpy as np
+
+from . import bf16
+from .quant import GROUP, effective_weight, unpack_quarter_split
+
+BLOCK_N = 64          # width of one selection block (module constant BLOCK_N)
+CHUNK_ROWS = 8192     # rows of W handled at once (memory bound only)
+
+
+def _x64(x_bits):
+    return bf16.to_f64(np.asarray(x_bits, dtype=np.uint16))
+
+
+def coarse(x_bits, packed, S_bits, ZS_bits):
+    """c[m][n] = sum_k x[m][k] * w_eff[n][k], float64 [M][N].
+
+    `_draft_head_int2` accumulates S * p - ZS * X per group into the fp32
+    accumulator it later selects from; algebraically that is the dot of x
+    with the effective weight (see quant.effective_weight).
+    """
+    x = _x64(x_bits)
+    n = packed.shape[0]
+    out = np.empty((x.shape[0], n), dtype=np.float64)
+    for i in range(0, n, CHUNK_ROWS):
+        j = min(i + CHUNK_ROWS, n)
+        w = effective_weight(packed, S_bits, ZS_bits, rows=slice(i, j))
+        out[:, i:j] = x @ w.T
+    return out
+
+
+def coarse_collapse(x_bits, packed, S_bits, ZS_bits):
+    """The page's own per-group form, in float64, for cross-checking `coarse`.
+
+    p_g = sum_{k in g} x_k (1 + v_k / 4) (the value the bit-pattern dequant
+    makes the dot return), X_g = sum_{k in g} x_k, and the group adds
+    S * p_g - ZS * X_g (module docstring, "Bit-pattern dequant, hoisted";
+    the scale and zero-point updates of `_draft_head_int2`).
+    """
+    x = _x64(x_bits)
+    v = unpack_quarter_split(packed).astype(np.float64)
+    S = bf16.to_f64(S_bits)
+    ZS = bf16.to_f64(ZS_bits)
+    m, k = x.shape
+    out = np.zeros((m, packed.shape[0]), dtype=np.float64)
+    for g in range(k // GROUP):
+        sl = slice(g * GROUP, (g + 1) * GROUP)
+        p = x[:, sl] @ (1.0 + v[:, sl] / 4.0).T
+        X = x[:, sl].sum(axis=1)
+        out += S[:, g][None, :] * p - ZS[:, g][None, :] * X[:, None]
+    return out
+
+
+def block_topk(c, kcand):
+    """Top-KCAND of each 64-column block, ordered (value desc, column asc).
+
+    `_emit`: KCAND rounds of max / argmax / mask over the block's columns, with
+    columns past N masked to -inf.  Returns (val64, ids) of shape
+    [M][NBLK * kcand]; padding slots hold (-inf, -1).
+    """
+    c = np.asarray(c, dtype=np.float64)
+    m, n = c.shape
+    nblk = (n + BLOCK_N - 1) // BLOCK_N
+    padded = np.full((m, nblk * BLOCK_N), -np.inf)
+    padded[:, :n] = c
+    blocks = padded.reshape(m, nblk, BLOCK_N)
+    # stable sort of the negated values: equal values keep ascending column order
+    order = np.argsort(-blocks, axis=2, kind="stable")
+    take = min(kcand, BLOCK_N)
+    top = order[:, :, :take]
+    vals = np.take_along_axis(blocks, top, axis=2)
+    ids = top + (np.arange(nblk) * BLOCK_N)[None, :, None]
+    ids = np.where(ids < n, ids, -1)
+    vals = np.where(ids >= 0, vals, -np.inf)
+    if take < kcand:
+        pad_v = np.full((m, nblk, kcand - take), -np.inf)
+        pad_i = np.full((m, nblk, kcand - take), -1)
+        vals = np.concatenate([vals, pad_v], axis=2)
+        ids = np.concatenate([ids, pad_i], axis=2)
+    return vals.reshape(m, nblk * kcand), ids.reshape(m, nblk * kcand).astype(np.int64)
+
+
+def row_topr(cand_val, cand_id, r):
+    """R best candidates of each row, ordered (value desc, id asc), id -1 skipped.
+
+    `bm.topk(RERANK, dim=1)` followed by `bi.gather` in `_apply_head_int2`.
+    Returns (ids int64 [M][R], vals float64 [M][R]); missing slots (-1, -inf).
+    """
+    cand_val = np.asarray(cand_val, dtype=np.float64)
+    cand_id = np.asarray(cand_id)
+    m = cand_val.shape[0]
+    ids = np.full((m, r), -1, dtype=np.int64)
+    vals = np.full((m, r), -np.inf)
+    for row in range(m):
+        ok = cand_id[row] >= 0
+        v = cand_val[row][ok]
+        i = cand_id[row][ok].astype(np.int64)
+        order = np.lexsort((i, -v))[:r]
+        ids[row, :len(order)] = i[order]
+        vals[row, :len(order)] = v[order]
+    return ids, vals
+
+
+def rerank_exact(x_bits, w_bits, rr_id):
+    """e[m][r] = sum_k x[m][k] * W[rr_id[m][r]][k], float64; -inf for id -1.
+
+    `_rerank_exact` (bf16 branch): one dot per (row, candidate), straight off
+    the head's own bf16 weight, accumulated in fp32 on the page (float64 here).
+    """
+    x = _x64(x_bits)
+    rr_id = np.asarray(rr_id)
+    out = np.full(rr_id.shape, -np.inf)
+    for row in range(rr_id.shape[0]):
+        ok = rr_id[row] >= 0
+        rows = bf16.to_f64(np.asarray(w_bits)[rr_id[row][ok]])
+        out[row, ok] = rows @ x[row]
+    return out
+
+
+def final_argmax(rr_id, e):
+    """Argmax over the R exact values of each row, float32 decision, ties -> lower id.
+
+    Returns (out_id int64 [M], out_val float32 [M]); (-1, -inf) for a row with
+    no valid candidate.
+    """
+    e32 = np.asarray(e, dtype=np.float64).astype(np.float32)
+    rr_id = np.asarray(rr_id)
+    m = rr_id.shape[0]
+    out_id = np.full(m, -1, dtype=np.int64)
+    out_val = np.full(m, -np.inf, dtype=np.float32)
+    for row in range(m):
+        best = None
+        for r in range(rr_id.shape[1]):
+            i = int(rr_id[row, r])
+            if i < 0:
+                continue
+            v = e32[row, r]
+            if best is None or v > best[1] or (v == best[1] and i < best[0]):
+                best = (i, v)
+        if best is not None:
+            out_id[row], out_val[row] = best
+    return out_id, out_val
+
+
+def exact_head(x_bits, w_bits):
+    """E[m][n] = x . W_bf16[n] in float64 (the bf16 head the method stands in for).
+
+    Used only to report agreement; not part of the method.
+    """
+    x = _x64(x_bits)
+    w_bits = np.asarray(w_bits)
+    n = w_bits.shape[0]
+    out = np.empty((x.shape[0], n), dtype=np.float64)
+    for i in range(0, n, CHUNK_ROWS):
+        j = min(i + CHUNK_ROWS, n)
+        out[:, i:j] = x @ bf16.to_f64(w_bits[i:j]).T
+    return out
+
+
+def argmax_lowest(E):
+    """Row argmax of a float64 matrix with ties to the lower column."""
+    return np.argmax(E, axis=1)   # numpy returns the first maximum
+
+
+def tie_rows(e, rel=1e-4):
+    """Rows whose two best exact values differ by less than rel * |best|."""
+    e = np.asarray(e, dtype=np.float64)
+    flags = np.zeros(e.shape[0], dtype=bool)
+    for row in range(e.shape[0]):
+        v = np.sort(e[row][np.isfinite(e[row])])[::-1]
+        if len(v) >= 2 and (v[0] - v[1]) < rel * abs(v[0]):
+            flags[row] = True
+    return flags
+
+
+def pipeline(x_bits, w_bits, packed, S_bits, ZS_bits, kcand=8, r=32):
+    """All per-call steps in order; returns a dict of every intermediate."""
+    c = coarse(x_bits, packed, S_bits, ZS_bits)
+    cv, ci = block_topk(c, kcand)
+    rr_id, rr_cv = row_topr(cv, ci, r)
+    e = rerank_exact(x_bits, w_bits, rr_id)
+    out_id, out_val = final_argmax(rr_id, e)
+    return {
+        "coarse": c, "cand_val": cv, "cand_id": ci, "rr_id": rr_id,
+        "rr_coarse": rr_cv, "rr_val": e, "out_id": out_id, "out_val": out_val,
+        "tie_rows": tie_rows(e),
+    }

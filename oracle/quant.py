@@ -1,0 +1,110 @@
+"""Quantiser, packing and the effective weight (oracle).
+
+Follows the quantiser `_quantize_head_now` on the radiance_drafthead.py page
+(asymmetric min/max at 2 bits, group 128 along K, quarter-split packing,
+premultiplied bf16 scale pair) and the module docstring's description of the
+packing ("Quarter-split packing") and of the collapse of the 1.0 bias
+("Bit-pattern dequant, hoisted").
+
+Arithmetic precision: the page runs the quantiser as separate torch float32
+element-wise operations, so every operation here is a separate float32
+operation (numpy evaluates each one on its own and rounds it; there is no
+fused multiply-add).  Reading: `torch.round` rounds half to even, and numpy's
+`np.round` does the same.
+"""
+import numpy as np
+
+from . import bf16
+
+GROUP = 128          # quantisation group along K (module constant GROUP)
+BITS = 2
+LEVELS = (1 << BITS) - 1   # highest code, 3
+PREMUL = 4.0         # bf16 1 + v/4 bias: the stored scales are premultiplied by 4
+
+
+def quantize(w_bits):
+    """Per (row n, group g of 128 consecutive k): min/max asymmetric int2.
+
+    Steps, as in `_quantize_head_now` (row chunk loop body):
+      lo, hi = min and max of the group (float32)
+      sc = max((hi - lo) / 3, 1e-8)
+      zp = clamp(round(-lo / sc), 0, 3)
+      q  = clamp(round(w / sc + zp), 0, 3)
+      S  = bf16(4 * sc)
+      ZS = bf16(4 * sc + zp * sc)
+    Returns (codes uint8 [N][K], S bits uint16 [N][K/128], ZS bits uint16 [N][K/128]).
+    """
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    n, k = w_bits.shape
+    if k % GROUP:
+        raise ValueError("K must be a multiple of the group size 128")
+    wf = bf16.to_f32(w_bits).reshape(n, k // GROUP, GROUP)
+    lo = wf.min(axis=2)
+    hi = wf.max(axis=2)
+    sc = (hi - lo) / np.float32(LEVELS)
+    sc = np.maximum(sc, np.float32(1e-8))
+    zp = np.clip(np.round(-lo / sc), np.float32(0), np.float32(LEVELS))
+    t = wf / sc[:, :, None]
+    t = t + zp[:, :, None]
+    q = np.clip(np.round(t), np.float32(0), np.float32(LEVELS)).astype(np.uint8)
+    s4 = np.float32(PREMUL) * sc
+    zpsc = zp * sc
+    S = bf16.from_f32(s4)
+    ZS = bf16.from_f32(s4 + zpsc)
+    return q.reshape(n, k), S, ZS
+
+
+def pack_quarter_split(codes):
+    """Byte j of a row carries k = j, K/4+j, K/2+j, 3K/4+j at bits 0-1, 2-3, 4-5, 6-7.
+
+    Module docstring, "Quarter-split packing", and the BITS == 2 branch of the
+    packing in `_quantize_head_now`.  Returns uint8 [N][K/4].
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    if k % 4:
+        raise ValueError("K must be a multiple of 4")
+    q4 = k // 4
+    out = np.zeros((n, q4), dtype=np.uint8)
+    for quarter in range(4):
+        out |= (codes[:, quarter * q4:(quarter + 1) * q4] & np.uint8(3)) << np.uint8(2 * quarter)
+    return out
+
+
+def unpack_quarter_split(packed):
+    """Inverse of pack_quarter_split: codes uint8 [N][K]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    n, q4 = packed.shape
+    out = np.empty((n, 4 * q4), dtype=np.uint8)
+    for quarter in range(4):
+        out[:, quarter * q4:(quarter + 1) * q4] = (packed >> np.uint8(2 * quarter)) & np.uint8(3)
+    return out
+
+
+def quantize_pack(w_bits):
+    """(packed uint8 [N][K/4], S bits, ZS bits), the stored form of the head."""
+    codes, S, ZS = quantize(w_bits)
+    return pack_quarter_split(codes), S, ZS
+
+
+def effective_weight(packed, S_bits, ZS_bits, rows=None):
+    """The weight the stored arrays define, float64 [n][K].
+
+    The kernel on the page computes, per group, S * sum_k x_k (1 + v_k/4) minus
+    ZS * sum_k x_k (module docstring, "Bit-pattern dequant, hoisted"), which is
+    sum_k x_k * ((S/4) v_k - (ZS - S)).  So the effective weight of code v is
+    (S/4) v - (ZS - S).  Reading: the stored bf16 pair, not the float32 sc/zp
+    of the quantiser, defines the weight.  Every value here is exact in float64.
+    `rows` optionally selects a slice of rows.
+    """
+    if rows is not None:
+        packed = packed[rows]
+        S_bits = S_bits[rows]
+        ZS_bits = ZS_bits[rows]
+    codes = unpack_quarter_split(packed).astype(np.float64)
+    n, k = codes.shape
+    s = bf16.to_f64(S_bits)
+    zs = bf16.to_f64(ZS_bits)
+    step = np.repeat(s / 4.0, GROUP, axis=1)
+    offset = np.repeat(zs - s, GROUP, axis=1)
+    return codes * step - offset

@@ -1,0 +1,297 @@
+"""Pins of the CPU oracle to what the radiance_drafthead.py page and arithmetic fix.
+
+None of these retype the oracle's own formulas: each compares the oracle with
+a page identity, a hand-derived fixture (tests/golden), a closed form, a
+special case whose answer is known without the method, a library routine, or
+an exact rational brute force (oracle/brute.py, which uses the page's own
+per-group form of the coarse score rather than the oracle's effective weight).
+"""
+from fractions import Fraction
+import struct
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import bf16 as obf
+from oracle import brute
+from bit_quantized_lm_amd import workload
+
+
+def _bf16_value(bits):
+    return struct.unpack("<f", struct.pack("<I", (bits & 0xFFFF) << 16))[0]
+
+
+def _hex(s):
+    return int(s, 16)
+
+
+# ------------------------------------------------------------ page identities
+def test_bit_pattern_identity_exhaustive(golden):
+    """0x3F80 | ((b << (5-2q)) & 0x60), or (b >> 1) & 0x60 for q = 3, reads as
+    bf16 1 + v/4 where v is the code the oracle unpacks from quarter q of b."""
+    table = golden("bit_pattern_dequant.txt")
+    for v in range(4):
+        bits, val = table[str(v)][0]
+        assert _bf16_value(_hex(bits)) == float(val) == 1.0 + v / 4.0
+    k = 512
+    q4 = k // 4
+    for b in range(256):
+        packed = np.full((1, q4), b, dtype=np.uint8)
+        codes = oracle.unpack_quarter_split(packed)[0]
+        for q in range(4):
+            if q < 3:
+                bits = 0x3F80 | ((b << (5 - 2 * q)) & 0x60)
+            else:
+                bits = 0x3F80 | ((b >> 1) & 0x60)
+            v = int(codes[q * q4])
+            assert _bf16_value(bits) == 1.0 + v / 4.0, (b, q)
+
+
+def test_collapse_identity_exact():
+    """S * sum x(1 + v/4) - ZS * sum x == sum x * w_eff, in exact rationals,
+    for the oracle's effective weight and stored pair (module docstring,
+    "Bit-pattern dequant, hoisted")."""
+    rng = np.random.default_rng(5)
+    k = 512
+    w = workload.f32_to_bf16_bits(rng.standard_normal((6, k), dtype=np.float32) * 0.03)
+    x = workload.f32_to_bf16_bits(rng.standard_normal((2, k), dtype=np.float32))
+    packed, S, ZS = oracle.quantize_pack(w)
+    w_eff = oracle.effective_weight(packed, S, ZS)
+    codes = oracle.unpack_quarter_split(packed)
+    for m in range(2):
+        xv = [Fraction(float(v)) for v in obf.to_f32(x[m])]
+        for n in range(6):
+            for g in range(k // 128):
+                sl = range(g * 128, (g + 1) * 128)
+                lhs = (Fraction(float(obf.to_f32(S[n, g]))) * sum(xv[i] * (1 + Fraction(int(codes[n, i]), 4)) for i in sl)
+                       - Fraction(float(obf.to_f32(ZS[n, g]))) * sum(xv[i] for i in sl))
+                rhs = sum(xv[i] * Fraction(float(w_eff[n, i])) for i in sl)
+                assert lhs == rhs
+
+
+def test_effective_weight_is_exact_in_float64():
+    """(S/4) v - (ZS - S) is representable: recomputing it in Fractions gives the same."""
+    w, _ = workload.gen_weight(64, 512, seed=9), None
+    packed, S, ZS = oracle.quantize_pack(w)
+    w_eff = oracle.effective_weight(packed, S, ZS)
+    codes = oracle.unpack_quarter_split(packed)
+    for n in range(0, 64, 7):
+        for kk in range(0, 512, 37):
+            g = kk // 128
+            s = Fraction(float(obf.to_f32(S[n, g])))
+            zs = Fraction(float(obf.to_f32(ZS[n, g])))
+            assert Fraction(float(w_eff[n, kk])) == s / 4 * int(codes[n, kk]) - (zs - s)
+
+
+# ------------------------------------------------------------ layout
+def test_quarter_split_layout_fixture(golden):
+    fx = golden("quarter_split_example.txt")
+    k = 512
+    codes = np.zeros((1, k), dtype=np.uint8)
+    for kk in fx["A_nonzero_k"][0]:
+        codes[0, int(kk)] = 3
+    packed = oracle.pack_quarter_split(codes)[0]
+    assert [int(v) for v in packed[:4]] == [_hex(s) for s in fx["A_bytes_0_to_3"][0]]
+    assert np.all(packed[4:] == _hex(fx["A_other_bytes"][0][0]))
+    codes_b = (np.arange(k) // 128).astype(np.uint8)[None, :]
+    assert np.all(oracle.pack_quarter_split(codes_b) == _hex(fx["B_every_byte"][0][0]))
+
+
+def test_pack_unpack_round_trip():
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 4, size=(5, 1024), dtype=np.uint8)
+    assert np.array_equal(oracle.unpack_quarter_split(oracle.pack_quarter_split(codes)), codes)
+
+
+# ------------------------------------------------------------ quantiser
+def test_quantizer_worked_example(golden):
+    fx = golden("quantizer_worked_example.txt")
+    k = int(fx["K"][0][0])
+    w = np.zeros((1, k), dtype=np.uint16)
+    w[0, :4] = [_hex(s) for s in fx["w_bits_k0_to_3"][0]]
+    codes, S, ZS = oracle.quantize(w)
+    assert [int(c) for c in codes[0, :4]] == [int(s) for s in fx["codes_k0_to_3"][0]]
+    assert np.all(codes[0, 4:128] == int(fx["code_rest_of_group0"][0][0]))
+    assert np.all(codes[0, 128:] == int(fx["code_zero_groups"][0][0]))
+    assert int(S[0, 0]) == _hex(fx["S_group0"][0][0])
+    assert int(ZS[0, 0]) == _hex(fx["ZS_group0"][0][0])
+    w_eff = oracle.effective_weight(oracle.pack_quarter_split(codes), S, ZS)[0]
+    want = {int(a): float(b) for a, b in fx["w_eff_for_code"]}
+    for kk in range(128):
+        assert w_eff[kk] == want[int(codes[0, kk])]
+    # all-zero groups decode to exactly zero
+    assert np.all(w_eff[128:] == 0.0)
+
+
+def test_quantizer_matches_exact_brute_force():
+    """numpy float32 quantiser == rational re-statement with explicit f32 rounding."""
+    rng = np.random.default_rng(17)
+    rows = [
+        rng.standard_normal(512, dtype=np.float32) * 0.02,
+        rng.standard_normal(512, dtype=np.float32) * 3.0,
+        np.full(512, 0.7, dtype=np.float32),                      # constant group
+        np.zeros(512, dtype=np.float32),                          # zero group
+        np.where(rng.random(512) < 0.5, -1.0, 1.0).astype(np.float32) * 1e-3,
+        rng.standard_normal(512, dtype=np.float32) * 1e-9,        # below the 1e-8 clamp
+        np.abs(rng.standard_normal(512, dtype=np.float32)),       # all positive: zp clamps
+        -np.abs(rng.standard_normal(512, dtype=np.float32)),      # all negative
+    ]
+    w = workload.f32_to_bf16_bits(np.stack(rows))
+    codes, S, ZS = oracle.quantize(w)
+    for i in range(w.shape[0]):
+        bc, bs, bz = brute.quantize_row([int(v) for v in w[i]])
+        assert [int(c) for c in codes[i]] == bc, i
+        assert [int(v) for v in S[i]] == bs, i
+        assert [int(v) for v in ZS[i]] == bz, i
+
+
+def test_clamp_constant_matches_exact_rounding():
+    assert Fraction(float(np.float32(1e-8))) == brute.f32(Fraction(1, 10 ** 8))
+
+
+def test_bf16_rounding_matches_exact_rounding():
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([rng.standard_normal(2000).astype(np.float32),
+                           np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8)], dtype=np.float32)])
+    bits = obf.from_f32(vals)
+    for v, b in zip(vals, bits):
+        assert brute.bf16_value_bits(brute.bf16(Fraction(float(v)))) == int(b)
+
+
+# ------------------------------------------------------------ special cases
+def _lossless_weight(n, k, rng):
+    """W built from codes with power-of-two step s and integer zero point z,
+    every group holding codes 0 and 3: the quantiser must reproduce it."""
+    codes = rng.integers(0, 4, size=(n, k)).astype(np.int64)
+    codes[:, ::128] = 0
+    codes[:, 1::128] = 3
+    s = 2.0 ** rng.integers(-9, -5, size=(n, k // 128))
+    z = rng.integers(0, 4, size=(n, k // 128)).astype(np.float64)
+    w = (codes - np.repeat(z, 128, axis=1)) * np.repeat(s, 128, axis=1)
+    return workload.f32_to_bf16_bits(w.astype(np.float32)), w
+
+
+def test_lossless_special_case():
+    rng = np.random.default_rng(23)
+    n, k = 300, 1024
+    w_bits, w = _lossless_weight(n, k, rng)
+    packed, S, ZS = oracle.quantize_pack(w_bits)
+    assert np.array_equal(oracle.effective_weight(packed, S, ZS), w)
+    x = workload.gen_x(4, k, seed=31, outliers=True)
+    out = oracle.pipeline(x, w_bits, packed, S, ZS, kcand=8, r=32)
+    E = oracle.exact_head(x, w_bits)
+    assert np.array_equal(out["coarse"], E)
+    assert np.array_equal(out["out_id"], oracle.head.argmax_lowest(E.astype(np.float32)))
+
+
+def test_all_ties_fixture(golden):
+    fx = golden("all_ties.txt")
+    n, k = int(fx["N"][0][0]), int(fx["K"][0][0])
+    kc, r = int(fx["KCAND"][0][0]), int(fx["R"][0][0])
+    w = workload.gen_weight(n, k, seed=4)
+    x = np.zeros((1, k), dtype=np.uint16)
+    packed, S, ZS = oracle.quantize_pack(w)
+    out = oracle.pipeline(x, w, packed, S, ZS, kcand=kc, r=r)
+    want_blocks = []
+    for span in fx["block_lists"][0]:
+        a, b = (int(v) for v in span.split("-"))
+        want_blocks += list(range(a, b + 1))
+    assert [int(v) for v in out["cand_id"][0]] == want_blocks
+    assert [int(v) for v in out["rr_id"][0]] == [int(v) for v in fx["row_top_r"][0]]
+    assert int(out["out_id"][0]) == int(fx["argmax"][0][0])
+
+
+def test_degenerate_selection_is_plain_argmax():
+    """KCAND = 64 and R >= N rerank every column: the result is the plain argmax
+    of the exact head; KCAND = 64, R = 32 gives the full-row top-32 of the
+    coarse scores (a library sort)."""
+    n, k = 200, 512
+    w = workload.gen_weight(n, k, seed=41)
+    x = workload.gen_x(3, k, seed=42)
+    packed, S, ZS = oracle.quantize_pack(w)
+    out = oracle.pipeline(x, w, packed, S, ZS, kcand=64, r=256)
+    E = oracle.exact_head(x, w).astype(np.float32)
+    assert np.array_equal(out["out_id"], np.argmax(E, axis=1))
+    out32 = oracle.pipeline(x, w, packed, S, ZS, kcand=64, r=32)
+    c = out32["coarse"]
+    for m in range(3):
+        order = np.lexsort((np.arange(n), -c[m]))[:32]
+        assert np.array_equal(out32["rr_id"][m], order)
+
+
+def test_partial_block_padding():
+    n, k = 70, 512                      # second block holds 6 valid columns
+    w = workload.gen_weight(n, k, seed=43)
+    x = workload.gen_x(1, k, seed=44)
+    packed, S, ZS = oracle.quantize_pack(w)
+    out = oracle.pipeline(x, w, packed, S, ZS, kcand=8, r=16)
+    ids = out["cand_id"][0].reshape(2, 8)
+    assert np.all(ids[0] >= 0) and np.all(ids[0] < 64)
+    assert np.all(ids[1][:6] >= 64) and np.all(ids[1][6:] == -1)
+    assert np.all(np.isneginf(out["cand_val"][0].reshape(2, 8)[1][6:]))
+    assert np.sum(out["rr_id"][0] >= 0) == 14 and np.all(out["rr_id"][0][14:] == -1)
+
+
+# ------------------------------------------------------------ brute force
+@pytest.mark.parametrize("m,n,kc,r", [(1, 64, 8, 32), (2, 150, 4, 8), (3, 130, 2, 5)])
+def test_pipeline_matches_exact_brute_force(m, n, kc, r):
+    k = 512
+    w = workload.gen_weight(n, k, seed=100 + n)
+    x = workload.gen_x(m, k, seed=200 + n)
+    ref = brute.run([[int(v) for v in row] for row in x], [[int(v) for v in row] for row in w], kc, r)
+    packed, S, ZS = oracle.quantize_pack(w)
+    assert [[int(v) for v in row] for row in packed] == ref["packed"]
+    assert [[int(v) for v in row] for row in S] == ref["S"]
+    assert [[int(v) for v in row] for row in ZS] == ref["ZS"]
+    out = oracle.pipeline(x, w, packed, S, ZS, kcand=kc, r=r)
+    exact = np.array([[float(v) for v in row] for row in ref["coarse"]])
+    assert np.allclose(out["coarse"], exact, rtol=1e-12, atol=1e-12)
+    cand_ids = np.array([[c for _, c in row] for row in ref["cand"]])
+    assert np.array_equal(out["cand_id"], cand_ids)
+    assert np.array_equal(out["rr_id"], np.array(ref["rr_id"]))
+    ev = np.array([[float(v) if v is not None else -np.inf for v in row] for row in ref["rr_val"]])
+    assert np.allclose(out["rr_val"], ev, rtol=1e-12, atol=1e-12)
+    assert list(out["out_id"]) == ref["out_id"]
+
+
+def test_coarse_matches_page_collapse_form():
+    """The effective-weight form and the page's S*p - ZS*X form agree in float64."""
+    w = workload.gen_weight(500, 1024, seed=50)
+    x = workload.gen_x(3, 1024, seed=51)
+    packed, S, ZS = oracle.quantize_pack(w)
+    a = oracle.coarse(x, packed, S, ZS)
+    b = oracle.coarse_collapse(x, packed, S, ZS)
+    assert np.allclose(a, b, rtol=1e-11, atol=1e-11)
+
+
+# ------------------------------------------------------------ sizes
+def test_closed_form_sizes(golden):
+    fx = golden("stored_sizes.txt")
+    k = int(fx["hidden"][0][0])
+    n = int(fx["vocab_shard"][0][0])
+    packed_bytes = n * (k // 4)
+    pair_bytes = 2 * n * (k // oracle.GROUP) * 2
+    assert packed_bytes + pair_bytes == 178_790_400
+    assert round((packed_bytes + pair_bytes) / 2 ** 30, 3) == float(fx["int2_head_gib"][0][0])
+    assert round(packed_bytes / 2 ** 20) == int(fx["int2_codes_mib"][0][0])
+    assert round(n * k * 2 / 2 ** 30, 2) == float(fx["bf16_head_gib"][0][0])
+
+
+# ------------------------------------------------------------ recall lever
+def test_kcand_is_the_recall_lever():
+    """Module docstring: at KCAND = 1 a winner that shares its block with a
+    stronger token is never a candidate; KCAND = 8 recovers it.  Planted
+    near-tie pairs (gap 0.01, far below the 2-bit coarse error) in one block."""
+    n, k, m = 4096, 512, 12
+    w = workload.gen_weight(n, k, seed=60)
+    x = workload.gen_x(m, k, seed=61)
+    w, pairs = workload.plant_recall_pairs(x, w, target=12.0, gap=0.01, seed=62)
+    E = oracle.exact_head(x, w)
+    winners = np.argmax(E, axis=1)
+    assert [int(v) for v in winners] == [p[0] for p in pairs]
+    packed, S, ZS = oracle.quantize_pack(w)
+    hit8 = oracle.pipeline(x, w, packed, S, ZS, kcand=8, r=32)["out_id"]
+    hit1 = oracle.pipeline(x, w, packed, S, ZS, kcand=1, r=32)["out_id"]
+    assert np.array_equal(hit8, winners)
+    assert np.sum(hit1 != winners) >= 2
