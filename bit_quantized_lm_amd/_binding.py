@@ -1,0 +1,237 @@
+"""ctypes binding of libdrafthead.so (include/drafthead.h), same names as the C ABI.
+
+Argument marshalling only: host functions take and return numpy arrays, device
+functions take torch CUDA tensors (torch is used for device memory and the
+current stream, nothing else) and allocate their outputs with torch.empty when
+the caller passes none.  Every step of the draft head runs in the library.
+
+Error mapping: DH_EINVAL / DH_ESHAPE / DH_EUNSUP raise ValueError, DH_EHIP
+raises DraftHeadError (a RuntimeError); the message is the library's own.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "drafthead.h")
+
+DH_OK, DH_EINVAL, DH_ESHAPE, DH_EUNSUP, DH_EHIP = 0, -1, -2, -3, -4
+BLOCK_N = 64
+GROUP = 128
+
+_lib = None
+
+
+class DraftHeadError(RuntimeError):
+    """A HIP runtime or launch error reported by the library."""
+
+
+def library_path() -> str:
+    return os.environ.get("DRAFTHEAD_LIB", os.path.join(_PKG, "libdrafthead.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree library (raises FileNotFoundError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m bit_quantized_lm_amd.build` "
+            "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.draft_head_last_error.restype = ctypes.c_char_p
+    lib.draft_head_last_error.argtypes = []
+    lib.draft_head_sizes.restype = i32
+    lib.draft_head_sizes.argtypes = [i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz),
+                                     ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.draft_head_quantize_pack.restype = i32
+    lib.draft_head_quantize_pack.argtypes = [P, i64, i64, i64, P, P, P, i32]
+    lib.draft_head_tile.restype = i32
+    lib.draft_head_tile.argtypes = [P, P, P, i64, i64, P, P]
+    lib.draft_head_coarse.restype = i32
+    lib.draft_head_coarse.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P]
+    lib.draft_head_rerank.restype = i32
+    lib.draft_head_rerank.argtypes = [P, P, i64, i32, i32, i32, P, P, i32, i32, P, P, P]
+    lib.draft_head_argmax.restype = i32
+    lib.draft_head_argmax.argtypes = [P, P, i32, i32, P, P, P]
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/drafthead.h declares."""
+    with open(_HEADER) as f:
+        text = f.read()
+    return re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(draft_head_\w+)\s*\(", text, flags=re.M)
+
+
+def draft_head_last_error() -> str:
+    return load_library().draft_head_last_error().decode()
+
+
+def _check(rc: int):
+    if rc == DH_OK:
+        return
+    msg = draft_head_last_error()
+    if rc in (DH_EINVAL, DH_ESHAPE, DH_EUNSUP):
+        raise ValueError(f"drafthead error {rc}: {msg}")
+    raise DraftHeadError(f"drafthead error {rc}: {msg}")
+
+
+def _ptr(a) -> int | None:
+    """Address of a numpy array or torch tensor (None -> NULL)."""
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        return a.ctypes.data
+    return a.data_ptr()
+
+
+# ------------------------------------------------------------------ host side
+def draft_head_sizes(N: int, K: int) -> dict:
+    lib = load_library()
+    vals = [ctypes.c_size_t() for _ in range(4)]
+    _check(lib.draft_head_sizes(N, K, *[ctypes.byref(v) for v in vals]))
+    keys = ("packed_bytes", "scale_elems", "tiled_bytes", "tiled_pairs")
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+def draft_head_quantize_pack(w_bits: np.ndarray, nthreads: int = 0):
+    """bf16 bits [N][K] -> (packed uint8 [N][K/4], S uint16 [N][K/128], ZS uint16 [N][K/128])."""
+    lib = load_library()
+    w = np.asarray(w_bits)
+    if w.dtype != np.uint16 or w.ndim != 2:
+        raise ValueError("w_bits must be a 2-D uint16 array of bf16 bit patterns")
+    if w.strides[1] != 2:
+        w = np.ascontiguousarray(w)
+    n, k = w.shape
+    ldw = w.strides[0] // 2
+    packed = np.empty((n, max(k // 4, 1)), dtype=np.uint8)
+    S = np.empty((n, max(k // GROUP, 1)), dtype=np.uint16)
+    ZS = np.empty_like(S)
+    _check(lib.draft_head_quantize_pack(_ptr(w), n, k, ldw, _ptr(packed), _ptr(S), _ptr(ZS), nthreads))
+    return packed, S, ZS
+
+
+def draft_head_tile(packed: np.ndarray, S: np.ndarray, ZS: np.ndarray):
+    """Canonical arrays -> (tiled codes uint8 [NBLK*64*K/4], pairs uint32 [NBLK*64*K/128])."""
+    lib = load_library()
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    S = np.ascontiguousarray(S, dtype=np.uint16)
+    ZS = np.ascontiguousarray(ZS, dtype=np.uint16)
+    n, q4 = packed.shape
+    k = 4 * q4
+    if S.shape != (n, k // GROUP) or ZS.shape != S.shape:
+        raise ValueError("S and ZS must be [N][K/128]")
+    sizes = draft_head_sizes(n, k)
+    tiled = np.empty(sizes["tiled_bytes"], dtype=np.uint8)
+    pairs = np.empty(sizes["tiled_pairs"], dtype=np.uint32)
+    _check(lib.draft_head_tile(_ptr(packed), _ptr(S), _ptr(ZS), n, k, _ptr(tiled), _ptr(pairs)))
+    return tiled, pairs
+
+
+# ------------------------------------------------------------------ device side
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _empty(shape, dtype, like):
+    import torch
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def draft_head_coarse(x, tiled, pairs, N: int, kcand: int = 8, cand_val=None, cand_id=None,
+                      coarse_out=None, stream=None):
+    """x: CUDA bf16 [M][K]; tiled/pairs: CUDA tensors in the draft_head_tile layout.
+    Returns (cand_val fp32 [M][NBLK*kcand], cand_id int32 [M][NBLK*kcand])."""
+    import torch
+    lib = load_library()
+    M, K = x.shape
+    nblk = (N + BLOCK_N - 1) // BLOCK_N
+    if cand_val is None:
+        cand_val = _empty((M, nblk * kcand), torch.float32, x)
+    if cand_id is None:
+        cand_id = _empty((M, nblk * kcand), torch.int32, x)
+    _check(lib.draft_head_coarse(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), kcand, _ptr(cand_val),
+                                 _ptr(cand_id), _ptr(coarse_out), _stream(stream)))
+    return cand_val, cand_id
+
+
+def draft_head_rerank(x, w, cand_val, cand_id, R: int = 32, rr_id=None, rr_val=None, N=None,
+                      stream=None):
+    """x: CUDA bf16 [M][K]; w: CUDA bf16 [N][ldw]; candidates from draft_head_coarse.
+    Returns (rr_id int32 [M][R], rr_val fp32 [M][R])."""
+    import torch
+    lib = load_library()
+    M, K = x.shape
+    n = w.shape[0] if N is None else N
+    ldw = w.stride(0)
+    ncand = cand_val.shape[1]
+    if rr_id is None:
+        rr_id = _empty((M, R), torch.int32, x)
+    if rr_val is None:
+        rr_val = _empty((M, R), torch.float32, x)
+    _check(lib.draft_head_rerank(_ptr(x), _ptr(w), ldw, M, K, n, _ptr(cand_val), _ptr(cand_id), ncand,
+                                 R, _ptr(rr_id), _ptr(rr_val), _stream(stream)))
+    return rr_id, rr_val
+
+
+def draft_head_argmax(rr_id, rr_val, out_id=None, out_val=None, stream=None):
+    """Returns (out_id int32 [M], out_val fp32 [M])."""
+    import torch
+    lib = load_library()
+    M, R = rr_id.shape
+    if out_id is None:
+        out_id = _empty((M,), torch.int32, rr_id)
+    if out_val is None:
+        out_val = _empty((M,), torch.float32, rr_id)
+    _check(lib.draft_head_argmax(_ptr(rr_id), _ptr(rr_val), M, R, _ptr(out_id), _ptr(out_val),
+                                 _stream(stream)))
+    return out_id, out_val
+
+
+class DraftHead:
+    """Device-resident head: the tiled 2-bit arrays plus the bf16 weight the rerank reads.
+
+    from_weight() quantises on the host with the library, tiles, and uploads.
+    __call__(x) runs coarse -> rerank -> argmax on the current stream and
+    returns a dict of the device tensors of every step.
+    """
+
+    def __init__(self, tiled, pairs, w, N: int, K: int, kcand: int = 8, R: int = 32):
+        self.tiled, self.pairs, self.w = tiled, pairs, w
+        self.N, self.K, self.kcand, self.R = N, K, kcand, R
+
+    @classmethod
+    def from_weight(cls, w_bits: np.ndarray, kcand: int = 8, R: int = 32, device="cuda",
+                    packed=None):
+        import torch
+        n, k = w_bits.shape
+        if packed is None:
+            packed = draft_head_quantize_pack(w_bits)
+        tiled, pairs = draft_head_tile(*packed)
+        t_tiled = torch.from_numpy(tiled).to(device)
+        t_pairs = torch.from_numpy(pairs.view(np.int32)).to(device)
+        t_w = torch.from_numpy(np.ascontiguousarray(w_bits).view(np.int16)).to(device)
+        return cls(t_tiled, t_pairs, t_w, n, k, kcand, R)
+
+    def __call__(self, x, coarse_out=None, stream=None):
+        cv, ci = draft_head_coarse(x, self.tiled, self.pairs, self.N, self.kcand,
+                                   coarse_out=coarse_out, stream=stream)
+        rr_id, rr_val = draft_head_rerank(x, self.w, cv, ci, self.R, N=self.N, stream=stream)
+        out_id, out_val = draft_head_argmax(rr_id, rr_val, stream=stream)
+        return {"cand_val": cv, "cand_id": ci, "rr_id": rr_id, "rr_val": rr_val,
+                "out_id": out_id, "out_val": out_val}

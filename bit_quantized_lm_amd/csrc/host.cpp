@@ -1,0 +1,186 @@
+// Host side of the draft-head library: error state, buffer sizes, the int2
+// quantiser with quarter-split packing, and the device-layout tiler.
+//
+// Built with -ffp-contract=off: the quantiser must round every float32
+// operation on its own, as the separate torch element-wise operations of
+// `_quantize_head_now` on the radiance_drafthead.py page do.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/drafthead.h"
+#include "common.h"
+
+namespace dh {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DH_OK;
+}
+
+}  // namespace dh
+
+namespace {
+
+inline float bf16_to_f32(uint16_t b) {
+  uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// float32 -> bf16, round to nearest, ties to even; NaN -> quiet NaN.
+inline uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;
+  uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(r >> 16);
+}
+
+int check_shape(int64_t N, int64_t K) {
+  if (N < 1) return dh::fail(DH_ESHAPE, "N must be >= 1 (got %lld)", (long long)N);
+  if (K < 512 || K % 512 != 0 || K > DH_MAX_K)
+    return dh::fail(DH_ESHAPE, "K must be a positive multiple of 512 up to %d (got %lld)",
+                    DH_MAX_K, (long long)K);
+  return DH_OK;
+}
+
+template <class F>
+void parallel_rows(int64_t N, int nthreads, F&& body) {
+  unsigned hw = std::thread::hardware_concurrency();
+  int64_t nt = nthreads > 0 ? nthreads : (hw ? hw : 1);
+  if (nt > N) nt = N;
+  if (nt <= 1) {
+    body(0, N);
+    return;
+  }
+  std::vector<std::thread> pool;
+  int64_t per = (N + nt - 1) / nt;
+  for (int64_t t = 0; t < nt; ++t) {
+    int64_t a = t * per, b = std::min<int64_t>(N, a + per);
+    if (a >= b) break;
+    pool.emplace_back([&body, a, b] { body(a, b); });
+  }
+  for (auto& th : pool) th.join();
+}
+
+// One row: codes into `codes` (K bytes), scale pair into S/ZS (K/128 each).
+void quantize_row(const uint16_t* w, int64_t K, uint8_t* codes, uint16_t* S, uint16_t* ZS) {
+  const float three = 3.0f, four = 4.0f, floor_sc = 1e-8f;
+  for (int64_t g = 0; g < K / DH_GROUP; ++g) {
+    const uint16_t* wg = w + g * DH_GROUP;
+    float lo = bf16_to_f32(wg[0]), hi = lo;
+    for (int i = 1; i < DH_GROUP; ++i) {
+      float v = bf16_to_f32(wg[i]);
+      lo = v < lo ? v : lo;
+      hi = v > hi ? v : hi;
+    }
+    float range = hi - lo;
+    float sc = range / three;
+    if (sc < floor_sc) sc = floor_sc;
+    float neg_lo = -lo;
+    float zp = std::nearbyint(neg_lo / sc);  // default rounding mode: to nearest even
+    zp = zp < 0.0f ? 0.0f : (zp > three ? three : zp);
+    for (int i = 0; i < DH_GROUP; ++i) {
+      float t = bf16_to_f32(wg[i]) / sc;
+      t = t + zp;
+      float q = std::nearbyint(t);
+      q = q < 0.0f ? 0.0f : (q > three ? three : q);
+      codes[g * DH_GROUP + i] = static_cast<uint8_t>(q);
+    }
+    float s4 = four * sc;
+    float zpsc = zp * sc;
+    float zs4 = s4 + zpsc;
+    S[g] = f32_to_bf16(s4);
+    ZS[g] = f32_to_bf16(zs4);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* draft_head_last_error(void) { return dh::g_last_error.c_str(); }
+
+int draft_head_sizes(int64_t N, int64_t K, size_t* packed_bytes, size_t* scale_elems,
+                     size_t* tiled_bytes, size_t* tiled_pairs) {
+  int rc = check_shape(N, K);
+  if (rc) return rc;
+  int64_t nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
+  if (packed_bytes) *packed_bytes = static_cast<size_t>(N) * (K / 4);
+  if (scale_elems) *scale_elems = static_cast<size_t>(N) * (K / DH_GROUP);
+  if (tiled_bytes) *tiled_bytes = static_cast<size_t>(nblk) * DH_BLOCK_N * (K / 4);
+  if (tiled_pairs) *tiled_pairs = static_cast<size_t>(nblk) * DH_BLOCK_N * (K / DH_GROUP);
+  return dh::ok();
+}
+
+int draft_head_quantize_pack(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                             uint8_t* packed, uint16_t* S, uint16_t* ZS, int nthreads) {
+  if (!w || !packed || !S || !ZS) return dh::fail(DH_EINVAL, "quantize_pack: null pointer");
+  int rc = check_shape(N, K);
+  if (rc) return rc;
+  if (ldw < K) return dh::fail(DH_EINVAL, "quantize_pack: ldw (%lld) < K (%lld)", (long long)ldw, (long long)K);
+  if (nthreads < 0) return dh::fail(DH_EINVAL, "quantize_pack: nthreads < 0");
+  const int64_t Q = K / 4;
+  parallel_rows(N, nthreads, [&](int64_t a, int64_t b) {
+    std::vector<uint8_t> codes(K);
+    for (int64_t n = a; n < b; ++n) {
+      quantize_row(w + n * ldw, K, codes.data(), S + n * (K / DH_GROUP), ZS + n * (K / DH_GROUP));
+      uint8_t* out = packed + n * Q;
+      for (int64_t j = 0; j < Q; ++j)
+        out[j] = static_cast<uint8_t>(codes[j] | (codes[Q + j] << 2) | (codes[2 * Q + j] << 4) |
+                                      (codes[3 * Q + j] << 6));
+    }
+  });
+  return dh::ok();
+}
+
+int draft_head_tile(const uint8_t* packed, const uint16_t* S, const uint16_t* ZS, int64_t N,
+                    int64_t K, uint8_t* tiled, uint32_t* pairs) {
+  if (!packed || !S || !ZS || !tiled || !pairs) return dh::fail(DH_EINVAL, "tile: null pointer");
+  int rc = check_shape(N, K);
+  if (rc) return rc;
+  const int64_t Q = K / 4, NG4 = K / 512, NG = K / DH_GROUP;
+  const int64_t nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
+  parallel_rows(nblk, 0, [&](int64_t a, int64_t bend) {
+    for (int64_t b = a; b < bend; ++b) {
+      for (int64_t col = 0; col < DH_BLOCK_N; ++col) {
+        const int64_t n = b * DH_BLOCK_N + col;
+        const bool valid = n < N;
+        const int64_t t = col / 16, c = col % 16;
+        for (int64_t j = 0; j < Q; ++j) {
+          const int64_t G = j / 128, h = (j % 128) / 64, s = (j % 64) / 16, wb = j % 16;
+          const int64_t off = ((((b * NG4 + G) * 2 + h) * 4 + t) * 64 + s * 16 + c) * 16 + wb;
+          tiled[off] = valid ? packed[n * Q + j] : 0;
+        }
+        for (int64_t g = 0; g < NG; ++g) {
+          const int64_t q = g / NG4, G = g % NG4;
+          const int64_t off = ((b * NG4 + G) * 4 + t) * 64 + c * 4 + q;
+          pairs[off] = valid ? (static_cast<uint32_t>(S[n * NG + g]) |
+                                (static_cast<uint32_t>(ZS[n * NG + g]) << 16))
+                             : 0u;
+        }
+      }
+    }
+  });
+  return dh::ok();
+}
+
+}  // extern "C"

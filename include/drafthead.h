@@ -1,0 +1,156 @@
+/*
+ * drafthead.h -- C ABI of the 2-bit speculative-draft LM head for MI355X (gfx950).
+ *
+ * The head scores x[M, K] against one tensor-parallel rank's vocabulary shard
+ * W[N, K] (row n = vocabulary token n) with 2-bit weights, keeps the best
+ * KCAND columns of every 64-column block, rescoring the best R of those
+ * exactly against the bf16 weight, and returns each row's argmax token.
+ * The method is the one the page "radiance_drafthead.py" (a vLLM plug-in
+ * module) describes in its module docstring and implements in
+ * `_quantize_head_now` (load time) and `_apply_head_int2` (per call).
+ *
+ * Call sequence:
+ *   load time (host):  draft_head_quantize_pack -> draft_head_tile -> copy to device
+ *   per call (device): draft_head_coarse -> draft_head_rerank -> draft_head_argmax
+ *
+ * Conventions for every function:
+ *   - Return value: DH_OK (0) or a negative DH_E* code; never throws.  The
+ *     message of the last error on the calling thread is draft_head_last_error().
+ *   - All argument validation happens before any HIP call, so every error
+ *     except DH_EHIP can be provoked without a GPU.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no state between calls and uses no scratch buffer.
+ *   - Device functions enqueue work asynchronously on `stream` (a hipStream_t
+ *     passed as void*, NULL = the null stream) and return once it is enqueued;
+ *     launch errors are reported by the call that launched (DH_EHIP).  Calls on
+ *     one stream see each other's results in order.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t) or as void*.
+ */
+#ifndef DRAFTHEAD_H
+#define DRAFTHEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DH_OK 0
+#define DH_EINVAL (-1)  /* null or misaligned pointer, argument out of range */
+#define DH_ESHAPE (-2)  /* K not a positive multiple of 512 (or > DH_MAX_K), N < 1 */
+#define DH_EUNSUP (-3)  /* M > DH_MAX_M, kcand outside 1..DH_MAX_KCAND, R outside 1..min(ncand, DH_MAX_R) */
+#define DH_EHIP (-4)    /* HIP runtime or kernel launch error */
+
+#define DH_GROUP 128        /* quantisation group along K (the page's GROUP) */
+#define DH_BLOCK_N 64       /* selection block width (the page's BLOCK_N) */
+#define DH_MAX_M 128
+#define DH_MAX_K 65536
+#define DH_MAX_KCAND 64
+#define DH_MAX_R 1024
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char* draft_head_last_error(void);
+
+/*
+ * Buffer sizes for an N x K head (K a multiple of 512).
+ *   packed_bytes   N * K/4        canonical quarter-split codes (draft_head_quantize_pack)
+ *   scale_elems    N * K/128      entries of S and of ZS each (bf16)
+ *   tiled_bytes    NBLK*64 * K/4  device-layout codes (draft_head_tile), NBLK = ceil(N/64)
+ *   tiled_pairs    NBLK*64 * K/128  device-layout (S, ZS) pairs, one uint32 each
+ * Any output pointer may be NULL.  Errors: DH_ESHAPE.
+ */
+int draft_head_sizes(int64_t N, int64_t K, size_t* packed_bytes, size_t* scale_elems,
+                     size_t* tiled_bytes, size_t* tiled_pairs);
+
+/*
+ * HOST.  Quantise a bf16 weight to asymmetric min/max int2 and pack it.
+ * Follows `_quantize_head_now` on the radiance_drafthead.py page: per (row n,
+ * group g of 128 consecutive k), in float32 with every operation rounded on
+ * its own (no fused multiply-add):
+ *   lo, hi = min, max of the group;  sc = max((hi - lo) / 3, 1e-8)
+ *   zp = clamp(rne(-lo / sc), 0, 3);  q = clamp(rne(w / sc + zp), 0, 3)
+ *   S = bf16(4 sc);  ZS = bf16(4 sc + zp sc)    (round to nearest even)
+ * and the quarter-split packing of the module docstring: byte j of a row holds
+ * the codes of k = j, K/4+j, K/2+j, 3K/4+j in bits 0-1, 2-3, 4-5, 6-7.
+ *   w        bf16 bits, row-major [N][ldw], ldw >= K (read only)
+ *   packed   out, uint8 [N][K/4]
+ *   S, ZS    out, bf16 bits [N][K/128] each
+ *   nthreads host threads to use (0 = all hardware threads)
+ * The effective weight of code v is (S/4) v - (ZS - S).
+ * Errors: DH_EINVAL (null pointer, ldw < K, nthreads < 0), DH_ESHAPE.
+ */
+int draft_head_quantize_pack(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                             uint8_t* packed, uint16_t* S, uint16_t* ZS, int nthreads);
+
+/*
+ * HOST.  Rearrange the canonical arrays into the device layout the coarse
+ * kernel streams (a pure permutation; the last block is padded with zero
+ * codes and zero scales).  With b = n/64, t = (n%64)/16, c = n%16 and, for
+ * code byte j, G = j/128, h = (j%128)/64, s = (j%64)/16, w = j%16:
+ *   tiled[((((b*NG4 + G)*2 + h)*4 + t)*64 + s*16 + c)*16 + w] = packed[n][j]
+ *   pairs[((b*NG4 + G)*4 + t)*64 + c*4 + q] = S[n][q*NG4 + G] | ZS[n][q*NG4 + G] << 16
+ * where NG4 = K/512 and q = 0..3 is the quarter.  Each 64-column block is one
+ * contiguous span of K/4*64 code bytes and K/128*64 pairs.
+ *   packed, S, ZS  canonical arrays (read only);  tiled, pairs  out
+ * Errors: DH_EINVAL (null pointer), DH_ESHAPE.
+ */
+int draft_head_tile(const uint8_t* packed, const uint16_t* S, const uint16_t* ZS,
+                    int64_t N, int64_t K, uint8_t* tiled, uint32_t* pairs);
+
+/*
+ * DEVICE.  Coarse scores and block top-KCAND candidates.
+ * Follows `_draft_head_int2` and `_emit` on the radiance_drafthead.py page:
+ * for every row m and column n, c[m][n] = sum over groups g of
+ * S * sum_k x (1 + v/4) - ZS * sum_k x  (fp32 accumulation), which equals
+ * sum_k x[m][k] * ((S/4) v - (ZS - S)); then, per 64-column block, the KCAND
+ * largest c ordered by (value desc, column asc).
+ *   x          device, bf16 [M][K] row-major, 16-byte aligned
+ *   tiled, pairs  device, draft_head_tile layout, 16-byte aligned
+ *   cand_val   out, fp32 [M][NBLK*kcand]; slot b*kcand + i = i-th best of block b
+ *   cand_id    out, int32, same shape: global column id, or -1 (value -inf)
+ *              when block b has fewer than kcand columns (n >= N)
+ *   coarse_out optional out (NULL = not written), fp32 [M][N] coarse scores
+ * Limits: 1 <= M <= DH_MAX_M, K % 512 == 0, N >= 1, 1 <= kcand <= DH_MAX_KCAND.
+ * Errors: DH_EINVAL, DH_ESHAPE, DH_EUNSUP, DH_EHIP.
+ */
+int draft_head_coarse(const void* x, int M, int K, int N, const uint8_t* tiled,
+                      const uint32_t* pairs, int kcand, float* cand_val, int32_t* cand_id,
+                      float* coarse_out, void* stream);
+
+/*
+ * DEVICE.  Row top-R of the candidates and their exact logits.
+ * Follows `bm.topk(RERANK)` + `bi.gather` and `_rerank_exact` (bf16 branch) on
+ * the radiance_drafthead.py page: per row, the R best (value desc, id asc)
+ * candidates with id >= 0, then e = sum_k x[m][k] * W[id][k] in fp32.
+ *   x          device, bf16 [M][K], 16-byte aligned
+ *   w          device, bf16 [N][ldw] (the head's own weight), 16-byte aligned,
+ *              ldw >= K and ldw % 8 == 0
+ *   cand_val, cand_id  device, [M][ncand] as written by draft_head_coarse
+ *   rr_id      out, int32 [M][R], ordered (coarse value desc, id asc); -1 pads
+ *              a row with fewer than R valid candidates
+ *   rr_val     out, fp32 [M][R] exact logit of rr_id (-inf where rr_id = -1)
+ * Limits: 1 <= M <= DH_MAX_M, K % 512 == 0, 1 <= R <= min(ncand, DH_MAX_R).
+ * Errors: DH_EINVAL, DH_ESHAPE, DH_EUNSUP, DH_EHIP.
+ */
+int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N,
+                      const float* cand_val, const int32_t* cand_id, int ncand, int R,
+                      int32_t* rr_id, float* rr_val, void* stream);
+
+/*
+ * DEVICE.  Final token per row: the rr_id whose exact value is largest, ties
+ * to the lower id, entries with id -1 ignored (the page leaves the argmax of
+ * the written-back row to the caller's sampler).
+ *   rr_id, rr_val  device, [M][R]
+ *   out_id     out, int32 [M] (-1 if a row has no valid entry)
+ *   out_val    out, fp32 [M] its exact logit (-inf if none)
+ * Errors: DH_EINVAL, DH_EUNSUP, DH_EHIP.
+ */
+int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R,
+                      int32_t* out_id, float* out_val, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DRAFTHEAD_H */

@@ -20,6 +20,7 @@ GROUP = 128          # quantisation group along K (module constant GROUP)
 BITS = 2
 LEVELS = (1 << BITS) - 1   # highest code, 3
 PREMUL = 4.0         # bf16 1 + v/4 bias: the stored scales are premultiplied by 4
+CHUNK_ROWS = 8192
 
 
 def quantize(w_bits):
@@ -38,6 +39,17 @@ def quantize(w_bits):
     n, k = w_bits.shape
     if k % GROUP:
         raise ValueError("K must be a multiple of the group size 128")
+    codes = np.empty((n, k), dtype=np.uint8)
+    S = np.empty((n, k // GROUP), dtype=np.uint16)
+    ZS = np.empty((n, k // GROUP), dtype=np.uint16)
+    for i in range(0, n, CHUNK_ROWS):       # row chunks bound memory only
+        j = min(i + CHUNK_ROWS, n)
+        codes[i:j], S[i:j], ZS[i:j] = _quantize_rows(w_bits[i:j])
+    return codes, S, ZS
+
+
+def _quantize_rows(w_bits):
+    n, k = w_bits.shape
     wf = bf16.to_f32(w_bits).reshape(n, k // GROUP, GROUP)
     lo = wf.min(axis=2)
     hi = wf.max(axis=2)

@@ -1,0 +1,212 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Cases span several 16-row M tiles, several 64-column blocks with a ragged
+last block, K with 1..10 byte groups, KCAND 1..64, R 1..256 (including R
+above the number of valid candidates), all-zero rows (pure ties), weights the
+quantiser reproduces exactly, determinism, and the full per-rank shard
+(K=5120, N=124160) at M = 1, 8, 72 plus the recall-stress case, in the same
+launch configuration bench.py times.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_lm_amd import _binding as B
+from bit_quantized_lm_amd import workload
+from parity_util import compare
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _log(msg):
+    print(f"[parity {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    B.load_library()          # fails loudly if the library is not built
+    return torch.device("cuda:0")
+
+
+def _to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+
+def run_gpu(head, x, dev, want_coarse=True):
+    m = x.shape[0]
+    xt = _to_dev(x, dev)
+    coarse = torch.empty((m, head.N), dtype=torch.float32, device=dev) if want_coarse else None
+    out = head(xt, coarse_out=coarse)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in out.items()}
+    res["coarse"] = coarse.cpu().numpy() if want_coarse else None
+    return res
+
+
+def check_case(dev, m, k, n, kcand, r, seed, x=None, w=None, log=True):
+    w = workload.gen_weight(n, k, seed=seed) if w is None else w
+    x = workload.gen_x(m, k, seed=seed + 1) if x is None else x
+    _log(f"case m={m} k={k} n={n} kcand={kcand} r={r} seed={seed}")
+    head = B.DraftHead.from_weight(w, kcand=kcand, R=r, device=dev)
+    got = run_gpu(head, x, dev)
+    ref = oracle.pipeline(x, w, *oracle.quantize_pack(w), kcand=kcand, r=r)
+    stats = compare(ref, got, n, kcand)
+    if log:
+        _log(f"  ok {stats}")
+    return ref, got, stats
+
+
+CASES = [
+    # m, k, n, kcand, r
+    (1, 512, 64, 8, 8),
+    (3, 1024, 1000, 8, 32),
+    (16, 512, 2048, 8, 32),
+    (17, 1024, 777, 4, 20),
+    (33, 512, 640, 8, 64),
+    (72, 1536, 1500, 8, 32),
+    (80, 512, 1100, 8, 32),
+    (81, 512, 300, 2, 8),
+    (128, 1024, 2100, 8, 32),
+    (5, 2048, 5000, 1, 1),
+    (2, 512, 200, 64, 100),
+    (4, 512, 70, 64, 100),     # fewer valid candidates than R: padded rr
+    (7, 1536, 3000, 16, 256),
+    (1, 5120, 1000, 8, 32),
+]
+
+
+@pytest.mark.parametrize("m,k,n,kcand,r", CASES)
+def test_parity_small(dev, m, k, n, kcand, r):
+    check_case(dev, m, k, n, kcand, r, seed=1000 + 7 * m + n)
+
+
+def test_parity_tiny_config(dev):
+    cfg = workload.CONFIGS["tiny"]
+    x, w = workload.make_inputs(cfg)
+    check_case(dev, cfg.m, cfg.k, cfg.n, cfg.kcand, cfg.rerank, seed=0, x=x, w=w)
+
+
+def test_all_zero_rows_are_pure_ties(dev, golden):
+    fx = golden("all_ties.txt")
+    n, k = int(fx["N"][0][0]), int(fx["K"][0][0])
+    kc, r = int(fx["KCAND"][0][0]), int(fx["R"][0][0])
+    w = workload.gen_weight(n, k, seed=4)
+    x = workload.gen_x(3, k, seed=5)
+    x[0] = 0
+    x[2] = 0
+    _, got, _ = check_case(dev, 3, k, n, kc, r, seed=0, x=x, w=w)
+    assert [int(v) for v in got["rr_id"][0]] == [int(v) for v in fx["row_top_r"][0]]
+    assert int(got["out_id"][0]) == int(fx["argmax"][0][0]) == int(got["out_id"][2])
+
+
+def test_lossless_weights_give_exact_argmax(dev):
+    rng = np.random.default_rng(23)
+    n, k = 1000, 1024
+    codes = rng.integers(0, 4, size=(n, k)).astype(np.int64)
+    codes[:, ::128] = 0
+    codes[:, 1::128] = 3
+    s = 2.0 ** rng.integers(-9, -5, size=(n, k // 128))
+    z = rng.integers(0, 4, size=(n, k // 128)).astype(np.float64)
+    wf = (codes - np.repeat(z, 128, axis=1)) * np.repeat(s, 128, axis=1)
+    w = workload.f32_to_bf16_bits(wf.astype(np.float32))
+    x = workload.gen_x(9, k, seed=31)
+    ref, got, _ = check_case(dev, 9, k, n, 8, 32, seed=0, x=x, w=w)
+    E = oracle.exact_head(x, w).astype(np.float32)
+    assert np.array_equal(got["out_id"], np.argmax(E, axis=1))
+
+
+def test_determinism(dev):
+    n, k, m = 3000, 1024, 20
+    w = workload.gen_weight(n, k, seed=91)
+    x = workload.gen_x(m, k, seed=92)
+    head = B.DraftHead.from_weight(w, kcand=8, R=32, device=dev)
+    a = run_gpu(head, x, dev)
+    b = run_gpu(head, x, dev)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_library_quantizer_matches_oracle_full_shape(full):
+    assert full["packed_equal"]
+
+
+# ------------------------------------------------------------------ full shape
+@pytest.fixture(scope="module")
+def full(dev):
+    cfg = workload.CONFIGS["m72"]
+    t0 = time.time()
+    _log("full shape: generating W and x")
+    x, w = workload.make_inputs(cfg)
+    _log(f"full shape: library quantize_pack ({time.time() - t0:.0f}s)")
+    packed = B.draft_head_quantize_pack(w)
+    _log(f"full shape: oracle quantize_pack ({time.time() - t0:.0f}s)")
+    opacked = oracle.quantize_pack(w)
+    equal = all(np.array_equal(a, b) for a, b in zip(packed, opacked))
+    _log(f"full shape: upload ({time.time() - t0:.0f}s)")
+    head = B.DraftHead.from_weight(w, kcand=cfg.kcand, R=cfg.rerank, device=dev, packed=packed)
+    _log(f"full shape: oracle coarse for 72 rows ({time.time() - t0:.0f}s)")
+    c = oracle.coarse(x, *opacked)
+    _log(f"full shape: oracle selection and rerank ({time.time() - t0:.0f}s)")
+    cv, ci = oracle.block_topk(c, cfg.kcand)
+    rr_id, _ = oracle.row_topr(cv, ci, cfg.rerank)
+    e = oracle.rerank_exact(x, w, rr_id)
+    out_id, out_val = oracle.final_argmax(rr_id, e)
+    ref = {"coarse": c, "cand_val": cv, "cand_id": ci, "rr_id": rr_id, "rr_val": e,
+           "out_id": out_id, "out_val": out_val, "tie_rows": oracle.tie_rows(e)}
+    _log(f"full shape: ready ({time.time() - t0:.0f}s)")
+    return {"x": x, "w": w, "head": head, "ref": ref, "packed_equal": equal, "cfg": cfg}
+
+
+def _prefix(ref, m):
+    return {k: (v[:m] if isinstance(v, np.ndarray) and v.ndim >= 1 else v) for k, v in ref.items()}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("m", [1, 8, 72])
+def test_parity_full_shape(dev, full, m):
+    cfg = full["cfg"]
+    got = run_gpu(full["head"], full["x"][:m], dev)
+    stats = compare(_prefix(full["ref"], m), got, cfg.n, cfg.kcand)
+    E = None
+    _log(f"full shape m={m}: {stats}")
+    if m == 72:
+        E = oracle.exact_head(full["x"], full["w"])
+        agree = int(np.sum(got["out_id"] == np.argmax(E, axis=1)))
+        _log(f"full shape m=72: argmax agreement with the exact bf16 head {agree}/72 (reported)")
+
+
+@pytest.mark.timeout(900)
+def test_recall_stress_full_shape(dev, full):
+    """Planted same-block near-ties: parity at KCAND = 8 and 1; misses reported."""
+    cfg = workload.CONFIGS["recall"]
+    x = full["x"][:cfg.m]
+    _log("recall: planting")
+    w, pairs = workload.plant_recall_pairs(x, full["w"], target=12.0, gap=0.01)
+    packed = B.draft_head_quantize_pack(w)
+    opacked = oracle.quantize_pack(w)
+    assert all(np.array_equal(a, b) for a, b in zip(packed, opacked))
+    c = oracle.coarse(x, *opacked)
+    winners = np.array([p[0] for p in pairs])
+    misses = {}
+    for kc in (8, 1):
+        head = B.DraftHead.from_weight(w, kcand=kc, R=32, device=dev, packed=packed)
+        got = run_gpu(head, x, dev, want_coarse=False)
+        cv, ci = oracle.block_topk(c, kc)
+        rr_id, _ = oracle.row_topr(cv, ci, 32)
+        e = oracle.rerank_exact(x, w, rr_id)
+        out_id, out_val = oracle.final_argmax(rr_id, e)
+        ref = {"coarse": c, "cand_val": cv, "cand_id": ci, "rr_id": rr_id, "rr_val": e,
+               "out_id": out_id, "out_val": out_val, "tie_rows": oracle.tie_rows(e)}
+        compare(ref, got, cfg.n, kc, check_coarse=False)
+        misses[kc] = int(np.sum(got["out_id"] != winners))
+        del head
+    _log(f"recall stress: argmax misses vs planted winner: KCAND=8 {misses[8]}/32, KCAND=1 {misses[1]}/32")
+    assert misses[8] == 0

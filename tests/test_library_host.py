@@ -1,0 +1,197 @@
+"""CPU tests of the C ABI: symbols, the host quantiser and tiler, and argument
+validation of every entry point (validation runs before any HIP call, so no
+GPU is needed)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_lm_amd import _binding as B
+from bit_quantized_lm_amd import workload
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return B.load_library()
+    except FileNotFoundError:
+        import __graft_entry__
+        __graft_entry__.build()
+        return B.load_library()
+
+
+def test_library_exports_every_header_symbol(lib):
+    names = B.header_functions()
+    assert set(names) == {"draft_head_last_error", "draft_head_sizes", "draft_head_quantize_pack",
+                          "draft_head_tile", "draft_head_coarse", "draft_head_rerank",
+                          "draft_head_argmax"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_sizes(lib):
+    s = B.draft_head_sizes(124160, 5120)
+    assert s["packed_bytes"] + 4 * s["scale_elems"] == 178_790_400
+    s = B.draft_head_sizes(70, 512)
+    assert s["packed_bytes"] == 70 * 128 and s["tiled_bytes"] == 128 * 128
+    assert s["scale_elems"] == 70 * 4 and s["tiled_pairs"] == 128 * 4
+    for n, k in ((0, 512), (10, 256), (10, 1000), (10, 0)):
+        with pytest.raises(ValueError):
+            B.draft_head_sizes(n, k)
+
+
+# ------------------------------------------------------------ quantiser parity
+def _edge_rows(k, rng):
+    rows = [
+        np.zeros(k, np.float32),
+        np.full(k, 0.37, np.float32),
+        rng.standard_normal(k, dtype=np.float32) * 1e-9,
+        np.abs(rng.standard_normal(k, dtype=np.float32)),
+        -np.abs(rng.standard_normal(k, dtype=np.float32)),
+        rng.standard_normal(k, dtype=np.float32) * 50,
+        np.where(rng.random(k) < 0.5, -1.0, 1.0).astype(np.float32) * 0.01,
+    ]
+    wk = np.zeros(k, np.float32)
+    wk[:4] = np.array([-3, -1, 1, 3], np.float32) * 2 ** -7   # round-half-even cases
+    rows.append(wk)
+    return workload.f32_to_bf16_bits(np.stack(rows))
+
+
+@pytest.mark.parametrize("n,k", [(8, 512), (300, 1024), (4096, 5120)])
+def test_quantize_pack_matches_oracle_bytes(lib, n, k):
+    rng = np.random.default_rng(n + k)
+    w = workload.gen_weight(n, k, seed=n)
+    w[:8] = _edge_rows(k, rng)
+    p, S, ZS = B.draft_head_quantize_pack(w, nthreads=4)
+    op, oS, oZS = oracle.quantize_pack(w)
+    assert np.array_equal(p, op)
+    assert np.array_equal(S, oS)
+    assert np.array_equal(ZS, oZS)
+
+
+def test_quantize_pack_strided_input(lib):
+    w = workload.gen_weight(64, 1536, seed=3)
+    view = w[:, :1024]                      # ldw = 1536 > K
+    p, S, ZS = B.draft_head_quantize_pack(view)
+    op, oS, oZS = oracle.quantize_pack(np.ascontiguousarray(view))
+    assert np.array_equal(p, op) and np.array_equal(S, oS) and np.array_equal(ZS, oZS)
+
+
+def test_quantize_pack_thread_count_does_not_matter(lib):
+    w = workload.gen_weight(333, 512, seed=8)
+    a = B.draft_head_quantize_pack(w, nthreads=1)
+    b = B.draft_head_quantize_pack(w, nthreads=7)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ------------------------------------------------------------ tiler
+def test_tile_layout(lib):
+    """Check the tiler against the layout documented in drafthead.h."""
+    n, k = 150, 1024                       # 3 blocks, the last one partial
+    w = workload.gen_weight(n, k, seed=12)
+    packed, S, ZS = oracle.quantize_pack(w)
+    tiled, pairs = B.draft_head_tile(packed, S, ZS)
+    q4, ng, ng4 = k // 4, k // 128, k // 512
+    nblk = (n + 63) // 64
+    assert tiled.size == nblk * 64 * q4 and pairs.size == nblk * 64 * ng
+    rng = np.random.default_rng(0)
+    for _ in range(4000):
+        col = int(rng.integers(0, nblk * 64))
+        j = int(rng.integers(0, q4))
+        b, t, c = col // 64, (col % 64) // 16, col % 16
+        G, h, s, wb = j // 128, (j % 128) // 64, (j % 64) // 16, j % 16
+        off = ((((b * ng4 + G) * 2 + h) * 4 + t) * 64 + s * 16 + c) * 16 + wb
+        assert tiled[off] == (packed[col, j] if col < n else 0)
+        g = int(rng.integers(0, ng))
+        q, G = g // ng4, g % ng4
+        off = ((b * ng4 + G) * 4 + t) * 64 + c * 4 + q
+        want = (int(S[col, g]) | (int(ZS[col, g]) << 16)) if col < n else 0
+        assert int(pairs[off]) == want
+    # a permutation: every code byte of every valid column appears exactly once
+    assert np.array_equal(np.sort(tiled[tiled != 0]), np.sort(packed.ravel()[packed.ravel() != 0]))
+
+
+# ------------------------------------------------------------ validation
+FAKE = ctypes.c_void_p(4096)      # aligned, never dereferenced: validation rejects first
+MIS = ctypes.c_void_p(4098)       # misaligned
+
+
+def _err(lib, rc, code):
+    assert rc == code, (rc, lib.draft_head_last_error())
+    assert lib.draft_head_last_error()
+
+
+def test_quantize_pack_validation(lib):
+    w = np.zeros((4, 512), np.uint16)
+    out = np.zeros(4096, np.uint8)
+    p = w.ctypes.data
+    _err(lib, lib.draft_head_quantize_pack(None, 4, 512, 512, out.ctypes.data, p, p, 0), B.DH_EINVAL)
+    _err(lib, lib.draft_head_quantize_pack(p, 4, 512, 256, out.ctypes.data, p, p, 0), B.DH_EINVAL)
+    _err(lib, lib.draft_head_quantize_pack(p, 4, 384, 512, out.ctypes.data, p, p, 0), B.DH_ESHAPE)
+    _err(lib, lib.draft_head_quantize_pack(p, 0, 512, 512, out.ctypes.data, p, p, 0), B.DH_ESHAPE)
+    _err(lib, lib.draft_head_quantize_pack(p, 4, 512, 512, out.ctypes.data, p, p, -1), B.DH_EINVAL)
+    _err(lib, lib.draft_head_tile(None, p, p, 4, 512, p, p), B.DH_EINVAL)
+    _err(lib, lib.draft_head_tile(p, p, p, 4, 500, p, p), B.DH_ESHAPE)
+
+
+def test_coarse_validation(lib):
+    f = lambda *a: lib.draft_head_coarse(*a)  # noqa: E731
+    ok = dict(x=FAKE, M=1, K=512, N=64, tiled=FAKE, pairs=FAKE, kc=8, cv=FAKE, ci=FAKE, co=None, s=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["x"], a["M"], a["K"], a["N"], a["tiled"], a["pairs"], a["kc"], a["cv"], a["ci"],
+                 a["co"], a["s"])
+    _err(lib, call(x=None), B.DH_EINVAL)
+    _err(lib, call(cv=None), B.DH_EINVAL)
+    _err(lib, call(ci=None), B.DH_EINVAL)
+    _err(lib, call(tiled=None), B.DH_EINVAL)
+    _err(lib, call(M=0), B.DH_EINVAL)
+    _err(lib, call(M=129), B.DH_EUNSUP)
+    _err(lib, call(K=256), B.DH_ESHAPE)
+    _err(lib, call(K=768), B.DH_ESHAPE)
+    _err(lib, call(K=131072), B.DH_ESHAPE)
+    _err(lib, call(N=0), B.DH_ESHAPE)
+    _err(lib, call(kc=0), B.DH_EUNSUP)
+    _err(lib, call(kc=65), B.DH_EUNSUP)
+    _err(lib, call(x=MIS), B.DH_EINVAL)
+    _err(lib, call(pairs=MIS), B.DH_EINVAL)
+
+
+def test_rerank_validation(lib):
+    ok = dict(x=FAKE, w=FAKE, ldw=512, M=2, K=512, N=100, cv=FAKE, ci=FAKE, nc=16, R=8, ri=FAKE,
+              rv=FAKE, s=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.draft_head_rerank(a["x"], a["w"], a["ldw"], a["M"], a["K"], a["N"], a["cv"], a["ci"],
+                                     a["nc"], a["R"], a["ri"], a["rv"], a["s"])
+    _err(lib, call(w=None), B.DH_EINVAL)
+    _err(lib, call(ri=None), B.DH_EINVAL)
+    _err(lib, call(M=0), B.DH_EINVAL)
+    _err(lib, call(M=200), B.DH_EUNSUP)
+    _err(lib, call(K=100), B.DH_ESHAPE)
+    _err(lib, call(N=0), B.DH_ESHAPE)
+    _err(lib, call(ldw=256), B.DH_EINVAL)
+    _err(lib, call(ldw=515), B.DH_EINVAL)
+    _err(lib, call(nc=0), B.DH_EINVAL)
+    _err(lib, call(R=0), B.DH_EUNSUP)
+    _err(lib, call(R=17), B.DH_EUNSUP)
+    _err(lib, call(R=2000, nc=4000), B.DH_EUNSUP)
+    _err(lib, call(w=MIS), B.DH_EINVAL)
+
+
+def test_argmax_validation(lib):
+    _err(lib, lib.draft_head_argmax(None, FAKE, 1, 8, FAKE, FAKE, None), B.DH_EINVAL)
+    _err(lib, lib.draft_head_argmax(FAKE, FAKE, 0, 8, FAKE, FAKE, None), B.DH_EINVAL)
+    _err(lib, lib.draft_head_argmax(FAKE, FAKE, 1, 0, FAKE, FAKE, None), B.DH_EUNSUP)
+    _err(lib, lib.draft_head_argmax(FAKE, FAKE, 1, 1025, FAKE, FAKE, None), B.DH_EUNSUP)
+
+
+def test_python_errors_are_value_errors(lib):
+    with pytest.raises(ValueError):
+        B.draft_head_quantize_pack(np.zeros((2, 300), np.uint16))
