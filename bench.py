@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the 2-bit draft head on one MI355X.
+
+One step = one full call of the head (coarse scores + block top-KCAND, row
+top-R + exact rerank, argmax) on one rank's vocabulary shard, x[M, 5120] @
+W[5120, 124160] with M = 1 (one draft slot), KCAND = 8, R = 32, on seeded
+synthetic inputs already resident in HBM.  Each timed step reads a different
+one of `--copies` device copies of the weights, so no step finds its 178.8 MB
+of packed weights in the 256 MB Infinity Cache left by the previous step.
+
+Prints one JSON line:
+  value        HBM GB/s of the call: 178,790,400 B (packed codes + scale pair,
+               the page's "0.167 GiB") / measured time per call
+  ms_per_step  time per call
+  roofline     the coarse kernel: algorithmic bytes per launch / its average
+               duration (HIP events on the launch stream) vs 8 TB/s
+  cpu_baseline the CPU oracle timed on this host on one full call at M = 1
+  extra        per-M (1, 8, 72) times, the warm (cache-resident) figure and
+               a device-copy bandwidth reference
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+K, N, KCAND, R = 5120, 124160, 8, 32
+NBLK = (N + 63) // 64
+WEIGHT_BYTES = N * (K // 4) + 2 * 2 * N * (K // 128)       # 178,790,400
+
+
+def coarse_alg_bytes(m: int) -> int:
+    """Bytes the coarse pass must move: packed codes + scale pair + x + candidates."""
+    return WEIGHT_BYTES + 2 * K * m + 8 * NBLK * KCAND * m
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "bit_quantized_lm_amd", "csrc", "device.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Rig:
+    """Device copies of the head and preallocated outputs for every M."""
+
+    def __init__(self, copies: int, max_m: int):
+        import torch
+        from bit_quantized_lm_amd import _binding as B
+        from bit_quantized_lm_amd import workload
+        self.torch, self.B = torch, B
+        dev = torch.device("cuda:0")
+        t0 = time.time()
+        log("generating W (bf16, N(0, 0.02)) and x (N(0, 1), 1% channels x8)")
+        self.x_host, w = workload.make_inputs(workload.CONFIGS["m72"])
+        log(f"host quantize_pack ({time.time() - t0:.1f}s)")
+        tq = time.time()
+        packed = B.draft_head_quantize_pack(w)
+        self.quantize_s = time.time() - tq
+        tiled, pairs = B.draft_head_tile(*packed)
+        log(f"upload {copies} copies ({time.time() - t0:.1f}s)")
+        t_tiled = torch.from_numpy(tiled).to(dev)
+        t_pairs = torch.from_numpy(pairs.view(np.int32)).to(dev)
+        t_w = torch.from_numpy(w.view(np.int16)).to(dev)
+        self.heads = []
+        for c in range(copies):
+            if c == 0:
+                self.heads.append(B.DraftHead(t_tiled, t_pairs, t_w, N, K, KCAND, R))
+            else:
+                self.heads.append(B.DraftHead(t_tiled.clone(), t_pairs.clone(), t_w.clone(),
+                                              N, K, KCAND, R))
+        self.x = torch.from_numpy(self.x_host[:max_m].view(np.int16)).to(dev)
+        self.dev = dev
+        self.stream = torch.cuda.current_stream().cuda_stream   # looked up once
+        self.out = {}
+        torch.cuda.synchronize()
+        log(f"ready ({time.time() - t0:.1f}s)")
+
+    def buffers(self, m):
+        if m not in self.out:
+            t, d = self.torch, self.dev
+            self.out[m] = dict(
+                cv=t.empty((m, NBLK * KCAND), dtype=t.float32, device=d),
+                ci=t.empty((m, NBLK * KCAND), dtype=t.int32, device=d),
+                ri=t.empty((m, R), dtype=t.int32, device=d),
+                rv=t.empty((m, R), dtype=t.float32, device=d),
+                oi=t.empty((m,), dtype=t.int32, device=d),
+                ov=t.empty((m,), dtype=t.float32, device=d))
+        return self.out[m]
+
+    def step(self, m, head, ev=None):
+        B, b = self.B, self.buffers(m)
+        x = self.x[:m]
+        if ev is not None:
+            ev[0].record()
+        s = self.stream
+        B.draft_head_coarse(x, head.tiled, head.pairs, N, KCAND, b["cv"], b["ci"], stream=s)
+        if ev is not None:
+            ev[1].record()
+        B.draft_head_rerank(x, head.w, b["cv"], b["ci"], R, b["ri"], b["rv"], N=N, stream=s)
+        B.draft_head_argmax(b["ri"], b["rv"], b["oi"], b["ov"], stream=s)
+
+    def timed(self, m, steps, warmup, copies=None):
+        """(seconds per call, seconds per coarse launch) over `steps` calls."""
+        torch = self.torch
+        heads = self.heads if copies is None else self.heads[:copies]
+        for i in range(warmup):
+            self.step(m, heads[i % len(heads)])
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            self.step(m, heads[i % len(heads)], evs[i])
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = start.elapsed_time(end)
+        coarse_ms = [a.elapsed_time(b) for a, b in evs]
+        return total_ms / 1e3 / steps, float(np.mean(coarse_ms)) / 1e3, wall
+
+    def copy_bandwidth(self, mib=1024, reps=5):
+        """Device-to-device copy of `mib` MiB: (read + write bytes) / time."""
+        torch = self.torch
+        a = torch.empty(mib << 20, dtype=torch.uint8, device=self.dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            b.copy_(a)
+        e.record()
+        torch.cuda.synchronize()
+        t = s.elapsed_time(e) / 1e3 / reps
+        del a, b
+        return 2 * (mib << 20) / t / 1e9
+
+
+def cpu_baseline(x_host, m=1):
+    """The oracle, untuned, on one full call at M = 1 (dequantise from the
+    packed arrays, float64 GEMV, block top-8, row top-32, exact rerank, argmax)."""
+    import oracle
+    from bit_quantized_lm_amd import workload
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    w = workload.gen_weight(N, K)
+    packed = oracle.quantize_pack(w)
+    x = x_host[:m]
+    t0 = time.perf_counter()
+    c = oracle.coarse(x, *packed)
+    cv, ci = oracle.block_topk(c, KCAND)
+    rr_id, _ = oracle.row_topr(cv, ci, R)
+    e = oracle.rerank_exact(x, w, rr_id)
+    oracle.final_argmax(rr_id, e)
+    t = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(WEIGHT_BYTES / t / 1e9, 4), "unit": "GB/s", "us_per_call": round(t * 1e6, 1),
+            "cores": int(blas_threads or cores), "host_cores_visible": cores, "kind": "oracle",
+            "sample": "one full call at M=1, K=5120, N=124160 (dequantise + float64 GEMV + "
+                      "selection + rerank + argmax); quantisation not timed"}
+
+
+def load_traffic(m):
+    """HBM bytes per coarse launch from the committed PMC summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"coarse_m{m}_k5120_n124160_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("device_hip_sha256_16") != source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--m", type=int, default=1, help="rows (draft slots) of the headline line")
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-M and warm figures")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run one device copy of this size (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the draft head runs on one "
+              "rank's vocabulary shard; a multi-GPU run is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calib_copy_mib:
+        a = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": args.calib_copy_mib << 20}), flush=True)
+        return
+    from bit_quantized_lm_amd import _binding as B
+    if not os.path.exists(B.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    rig = Rig(args.copies, max(72, args.m))
+    m = args.m
+    t_call, t_coarse, wall = rig.timed(m, args.steps, args.warmup)
+    log(f"M={m}: {t_call * 1e6:.1f} us/call, coarse {t_coarse * 1e6:.1f} us, wall {wall:.3f}s")
+
+    extra = {"quantize_pack_host_s": round(rig.quantize_s, 2), "copies_rotated": args.copies}
+    if not args.no_extra:
+        per_m = {}
+        for mm in (1, 8, 72):
+            tc, tk, _ = rig.timed(mm, max(20, args.steps // 2), 5)
+            per_m[str(mm)] = {"us_per_call": round(tc * 1e6, 2), "coarse_us": round(tk * 1e6, 2),
+                              "GBps": round(WEIGHT_BYTES / tc / 1e9, 1),
+                              "coarse_GBps": round(coarse_alg_bytes(mm) / tk / 1e9, 1),
+                              "coarse_frac_hbm_peak": round(coarse_alg_bytes(mm) / tk / 1e9 / HBM_PEAK_GBPS, 4),
+                              "coarse_TFLOPs": round(2.0 * mm * K * N / tk / 1e12, 2)}
+            log(f"M={mm}: {per_m[str(mm)]}")
+        extra["per_m"] = per_m
+        tw, tkw, _ = rig.timed(m, args.steps, args.warmup, copies=1)
+        extra["warm_not_hbm"] = {"us_per_call": round(tw * 1e6, 2), "coarse_us": round(tkw * 1e6, 2),
+                                 "note": "one weight copy reused back to back: Infinity-Cache resident"}
+        extra["device_copy_GBps"] = round(rig.copy_bandwidth(), 1)
+
+    alg = coarse_alg_bytes(m)
+    achieved = alg / t_coarse / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(m),
+                "kernel": "coarse_kernel", "alg_bytes_per_launch": alg,
+                "avg_launch_us": round(t_coarse * 1e6, 2)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle (one full call)")
+        cpu = cpu_baseline(rig.x_host, 1)
+        log(f"cpu oracle: {cpu}")
+
+    line = {
+        "metric": "us/call + HBM GB/s (% peak), 2-bit draft head K=5120 N=124160, M=1/8/72",
+        "value": round(WEIGHT_BYTES / t_call / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_call * 1e3, 5),
+        "us_per_call": round(t_call * 1e6, 2),
+        "frac_hbm_peak": round(WEIGHT_BYTES / t_call / 1e9 / HBM_PEAK_GBPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"2-bit draft head, one vocab shard: M={m} K={K} N={N} KCAND={KCAND} R={R}",
+                   "M": m, "K": K, "N": N, "kcand": KCAND, "rerank": R,
+                   "weights": "int2 g128 asym (bf16 scale pair), fp32 accumulation"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -2,15 +2,16 @@
 // the validating C entry points that launch them.
 //
 // Per call (radiance_drafthead.py page, `_apply_head_int2`):
-//   coarse_kernel   scores x against the 2-bit weight and keeps the top KCAND
+//   coarse_*_kernel scores x against the 2-bit weight and keeps the top KCAND
 //                   columns of every 64-column block (`_draft_head_int2` + `_emit`)
-//   select_kernel   row top-R of the candidates (`bm.topk` + `bi.gather`)
-//   dot_kernel      exact fp32 dot of x with each candidate's bf16 row (`_rerank_exact`)
+//   rerank_kernel   row top-R of the candidates (`bm.topk` + `bi.gather`), then the
+//                   exact fp32 dot of x with each one's bf16 row (`_rerank_exact`)
 //   argmax_kernel   best reranked candidate per row
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "../../include/drafthead.h"
 #include "common.h"
@@ -28,52 +29,334 @@ constexpr int kMaxMT = 5;            // 16-row M tiles per coarse launch (80 row
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Decode quarter q of two code dwords into four bf16 pairs of 1 + v/4.
+// Decode quarter q of two adjacent code dwords into four bf16 pairs of 1 + v/4.
 // Code v sits in bits 2q..2q+1 of each byte; moving it to bits 5-6 of a
 // halfword and OR-ing 0x3F80 gives the bf16 value 1 + v/4 (the bit-pattern
 // dequant of the module docstring).  Even pairs hold bytes 0 and 2 of a dword
-// (rotate left by 5 - 2q, which for q = 3 is a rotate right by 1), odd pairs
-// bytes 1 and 3 (shift right by 3 + 2q), so the element order of the result
-// is byte {0, 2, 1, 3} of d0 then {0, 2, 1, 3} of d1; the x fragments are
-// staged in the same order.  Bits rotated around land in bits 0-4 or 31 and
-// are masked off.
+// (shift left by 5 - 2q, right by 1 for q = 3), odd pairs bytes 1 and 3
+// (shift right by 3 + 2q).  Both dwords are shifted at once as one 64-bit
+// value: the bits that cross between them land in bits 0-4 or 23-31 of a
+// word, which the mask drops.  Element order of the result: byte {0, 2, 1, 3}
+// of d0 then {0, 2, 1, 3} of d1; the x fragments are staged in the same order.
 //
 // `one` must hold 0x3F803F80 in a VGPR: gfx9-family VOP3 instructions take no
 // literal operand, so with the mask in an SGPR and `one` in a VGPR each pair
-// is one shift and one v_and_or_b32.
-__device__ __forceinline__ bf16x8 decode_quarter(uint32_t d0, uint32_t d1, uint32_t rot,
-                                                 uint32_t shr, uint32_t one) {
+// is one v_and_or_b32 after the shared shift.
+template <int Q>
+__device__ __forceinline__ bf16x8 decode_quarter(uint32_t d0, uint32_t d1, uint32_t one) {
   constexpr uint32_t kMask = 0x00600060u;
-  const uint32_t e0 = (__builtin_amdgcn_alignbit(d0, d0, rot) & kMask) | one;
-  const uint32_t e1 = (__builtin_amdgcn_alignbit(d1, d1, rot) & kMask) | one;
-  const uint32_t o0 = ((d0 >> shr) & kMask) | one;
-  const uint32_t o1 = ((d1 >> shr) & kMask) | one;
-  u32x4 v = {e0, o0, e1, o1};
+  const uint64_t d = ((uint64_t)d1 << 32) | d0;
+  const uint64_t ev = Q < 3 ? (d << (5 - 2 * Q)) : (d >> 1);
+  const uint64_t od = d >> (3 + 2 * Q);
+  u32x4 v = {((uint32_t)ev & kMask) | one, ((uint32_t)od & kMask) | one,
+             ((uint32_t)(ev >> 32) & kMask) | one, ((uint32_t)(od >> 32) & kMask) | one};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Same decode for a quarter q known only at run time: the even pairs rotate
+// left by 5 - 2q (for q = 3 a rotate right by 1; rotated-around bits land in
+// bits 0-4 or 31 and are masked off), the odd pairs shift right by 3 + 2q.
+__device__ __forceinline__ bf16x8 decode_quarter_rt(uint32_t d0, uint32_t d1, uint32_t rot,
+                                                    uint32_t shr, uint32_t one) {
+  constexpr uint32_t kMask = 0x00600060u;
+  u32x4 v = {(__builtin_amdgcn_alignbit(d0, d0, rot) & kMask) | one, ((d0 >> shr) & kMask) | one,
+             (__builtin_amdgcn_alignbit(d1, d1, rot) & kMask) | one, ((d1 >> shr) & kMask) | one};
   return __builtin_bit_cast(bf16x8, v);
 }
 
 // ---------------------------------------------------------------------------
-// Coarse kernel.
+// Coarse pass building blocks.
 //
-// Workgroup = 4 waves, wave w owns 64-column block b = 4*blockIdx.x + w and
-// computes its M x 64 coarse scores with bf16 MFMA 16x16x32: the A operand is
-// x (rows), the B operand is the decoded weight (1 + v/4), one 16-column tile
-// per MFMA, four tiles per block.  The K loop walks the 4*NG4 groups in the
-// order (byte-group G, quarter q); the 128 x values of each group are staged in
-// LDS (double buffered, one barrier per group) in the permuted order the
-// decode produces, together with the group sum X = sum_k x in fp32.  After a
-// group's four MFMAs per tile the accumulator is updated with the page's
-// premultiplied pair: acc += S * p - ZS * X.
+// A wave owns one 64-column block b and computes its coarse scores for up to
+// 16*MT rows with bf16 MFMA 16x16x32: the A operand is x (rows), the B operand
+// the decoded weight (1 + v/4), one 16-column tile per MFMA, four tiles per
+// block.  Lane (hh, nn) = (lane / 16, lane % 16) supplies row nn of A and
+// column nn of B for k-slots 8hh..8hh+7; the accumulator holds rows 4hh + r,
+// column nn.  K is walked as groups (byte group G, quarter q): code byte j of
+// byte group G (j / 128 = G) carries one code of each of the groups q*NG4 + G.
+// After a group's MFMAs the accumulator takes the page's premultiplied pair:
+// acc += S * p - ZS * X, p = sum_k x (1 + v/4), X = sum_k x.
 //
-// LDS layout of one staged group: 16 fragments f = (h*2 + e)*4 + s of 8 bf16
-// per row, fragment f of row m at [f*MP + m] (16 bytes), MP = 16*MT rows
-// (rows >= M stay zero); then X[MP].  The fixed row count makes every LDS
-// offset a compile-time immediate.
+// x fragments live in LDS in the decode order: fragment f = (h*2 + e)*4 + s of
+// a group holds x at k = q*K/4 + 128*G + 64h + 16s + 8e + {0,2,1,3,4,6,5,7}.
+
+struct CoarseArgs {
+  const uint16_t* x;
+  int M, K, N, nblk;
+  const u32x4* tiled;
+  const u32x4* pairs;
+  int kcand;
+  float* cand_val;
+  int32_t* cand_id;
+  float* coarse_out;
+};
+
+// One group: MFMAs of the (h, e) fragments for all tiles, then the scale update.
+// `xb` points at this lane's fragment 0 of the group (A row nn, k-slot hh),
+// fragment f of M-tile i at xb[f * fstride + 16 * i]; `Xg` at the group's X[row].
+// Q >= 0: the quarter is a compile-time constant; Q < 0: it is `q`.
+template <int MT, int MR, int Q>
+__device__ __forceinline__ void coarse_group(f32x4 (&acc)[MT][4], const u32x4 (&raw)[2][4],
+                                             const u32x4 (&sz)[4], const u32x4* xb, int fstride,
+                                             const float* Xg, int hh, uint32_t one, int q = Q) {
+  // run-time decode: rotate-left 5 - 2q as a right rotate, odd shift 3 + 2q
+  const uint32_t rot = (uint32_t)(32 - (5 - 2 * q)) & 31u;
+  const uint32_t shr = 3u + 2u * (uint32_t)q;
+  f32x4 cg[MT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) cg[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      bf16x8 a[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        a[i] = __builtin_bit_cast(bf16x8, xb[(h * 2 + e) * 4 * fstride + 16 * i]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bf16x8 bv;
+        if constexpr (Q >= 0) bv = decode_quarter<Q>(raw[h][t][2 * e], raw[h][t][2 * e + 1], one);
+        else bv = decode_quarter_rt(raw[h][t][2 * e], raw[h][t][2 * e + 1], rot, shr, one);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          cg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bv, cg[i][t], 0, 0, 0);
+      }
+    }
+  }
+  float X[MT][MR];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < MR; ++r) X[i][r] = Xg[16 * i + 4 * hh + r];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    uint32_t pr;
+    if constexpr (Q >= 0) pr = sz[t][Q];
+    else pr = q == 0 ? sz[t][0] : q == 1 ? sz[t][1] : q == 2 ? sz[t][2] : sz[t][3];
+    const float S = lo_bf16(pr), nZS = -hi_bf16(pr);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < MR; ++r)
+        acc[i][t][r] = __builtin_fmaf(nZS, X[i][r], __builtin_fmaf(S, cg[i][t][r], acc[i][t][r]));
+  }
+}
+
+// Epilogue of one block: optional full rows, then the top-kcand of the block by
+// successive max-and-mask (`_emit`), ties to the lower column.  The four rows
+// 16i + 4hh + r of one (i, r) are handled at once, one per 16-lane row.
+template <int MT, int MR>
+__device__ __forceinline__ void block_select(const f32x4 (&acc)[MT][4], const CoarseArgs& A, int b,
+                                             int hh, int nn) {
+  const float NEG_INF = -__builtin_inff();
+  const int ncand = A.nblk * A.kcand;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      if (16 * i + r >= A.M) continue;  // no row of this (i, r) is live (wave-uniform)
+      const int m = 16 * i + 4 * hh + r;
+      const bool row_ok = m < A.M;
+      float v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int n = b * 64 + 16 * t + nn;
+        const bool ok = row_ok && n < A.N;
+        v[t] = ok ? acc[i][t][r] : NEG_INF;
+        if (A.coarse_out && ok) A.coarse_out[(size_t)m * A.N + n] = acc[i][t][r];
+      }
+      float kv[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+      int ki[4] = {-1, -1, -1, -1};
+      for (int c = 0; c < A.kcand; ++c) {
+        float bv = v[0];
+        int bn = nn;
+#pragma unroll
+        for (int t = 1; t < 4; ++t)
+          if (v[t] > bv) {
+            bv = v[t];
+            bn = 16 * t + nn;
+          }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          const float ov = __shfl_xor(bv, off, 16);
+          const int on = __shfl_xor(bn, off, 16);
+          if (ov > bv || (ov == bv && on < bn)) {
+            bv = ov;
+            bn = on;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (bn == 16 * t + nn) v[t] = NEG_INF;
+        if ((c & 15) == nn) {
+          const int slot = c >> 4;
+          const int id = (bv == NEG_INF) ? -1 : b * 64 + bn;
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            if (s == slot) {
+              kv[s] = bv;
+              ki[s] = id;
+            }
+        }
+      }
+      if (row_ok) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int c = 16 * s + nn;
+          if (c < A.kcand) {
+            const size_t o = (size_t)m * ncand + (size_t)b * A.kcand + c;
+            A.cand_val[o] = kv[s];
+            A.cand_id[o] = ki[s];
+          }
+        }
+      }
+    }
+  }
+}
+
+// Convert 8 natural-order bf16 x values into the decode order {0,2,1,3,4,6,5,7}
+// and return their fp32 sum.
+__device__ __forceinline__ u32x4 permute_x(const u32x4 v, float& sum) {
+  u32x4 o;
+  o[0] = (v[0] & 0xFFFFu) | (v[1] << 16);
+  o[1] = (v[0] >> 16) | (v[1] & 0xFFFF0000u);
+  o[2] = (v[2] & 0xFFFFu) | (v[3] << 16);
+  o[3] = (v[2] >> 16) | (v[3] & 0xFFFF0000u);
+  sum = lo_bf16(v[0]) + hi_bf16(v[0]) + lo_bf16(v[1]) + hi_bf16(v[1]) + lo_bf16(v[2]) +
+        hi_bf16(v[2]) + lo_bf16(v[3]) + hi_bf16(v[3]);
+  return o;
+}
+
+// Sum over the 16 lanes of a DPP row (the 16 pieces of one group of one row).
+__device__ __forceinline__ float row16_sum(float s) {
+  s += __shfl_xor(s, 1, 16);
+  s += __shfl_xor(s, 2, 16);
+  s += __shfl_xor(s, 4, 16);
+  s += __shfl_xor(s, 8, 16);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Coarse kernel, x resident in LDS (M <= 8 and the whole x fits).
+//
+// Workgroup = 4 waves (8 for 8 rows), one 64-column block each.  It stages all of
+// x once (MP rows, MP = the next power of two >= M; lanes whose A row nn >= MP
+// read row nn & (MP-1), whose results are never used) with the group sums X,
+// then every wave streams its block with no further barrier: the codes and
+// scale pairs of byte group G+1 are loaded while byte group G is computed.
+// LDS: fragments [group it = 4G + q][f][MP] (16 bytes each), then X[it][MP].
+template <int MP>
+constexpr int res_waves() { return MP >= 8 ? 8 : 4; }  // 8 rows: 83 KB of LDS, one workgroup per CU
+
+template <int MP>
+__global__ __launch_bounds__(64 * res_waves<MP>()) __attribute__((amdgpu_waves_per_eu(2)))
+void coarse_resident_kernel(CoarseArgs A) {
+  constexpr int kResWaves = res_waves<MP>();
+  constexpr int kResThreads = 64 * kResWaves;
+  constexpr int MR = MP < 4 ? MP : 4;  // accumulator rows r that can hold a live row
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int NG4 = A.K >> 9, Q4 = A.K >> 2, NG = A.K >> 7;
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);                          // [NG][16][MP]
+  float* Xs = reinterpret_cast<float*>(smem + (size_t)NG * 16 * MP * 16);  // [NG][MP]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 4, nn = lane & 15;
+  const int b = blockIdx.x * kResWaves + wave;
+  const bool blk_ok = b < A.nblk;
+  uint32_t one;
+  asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(one));
+
+  // stage x: piece i = (m, k0 = 8p) for all MP rows (zero rows past M).  Loads
+  // are issued kBatch at a time from clamped (always valid) addresses.
+  {
+    constexpr int kBatch = 8;
+    const int per_row = A.K >> 3;
+    const int total = MP * per_row;
+    for (int base = 0; base < total; base += kResThreads * kBatch) {
+      u32x4 v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = min(base + tid + j * kResThreads, total - 1);
+        const int m = i / per_row, k0 = (i - m * per_row) * 8;
+        v[j] = *reinterpret_cast<const u32x4*>(A.x + (size_t)(m < A.M ? m : 0) * A.K + k0);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = base + tid + j * kResThreads;
+        if (i < total) {   // uniform per 16-lane row: total is a multiple of 16
+          const int m = i / per_row, k0 = (i - m * per_row) * 8;
+          const u32x4 vm = m < A.M ? v[j] : u32x4{0u, 0u, 0u, 0u};
+          const int q = k0 / Q4, G = (k0 - q * Q4) >> 7, p = (k0 >> 3) & 15;
+          const int it = G * 4 + q;
+          float sum;
+          const u32x4 o = permute_x(vm, sum);
+          const int h = p >> 3, s = (p >> 1) & 3, e = p & 1;
+          xs[(it * 16 + (h * 2 + e) * 4 + s) * MP + m] = o;
+          sum = row16_sum(sum);
+          if (p == 0) Xs[it * MP + m] = sum;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  (void)NG;
+
+  const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
+  const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64;
+  auto load_codes = [&](int G, u32x4 (&raw)[2][4], u32x4 (&sz)[4]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) raw[h][t] = tp[((G * 2 + h) * 4 + t) * 64 + lane];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sz[t] = pp[(G * 4 + t) * 16 + nn];
+  };
+
+  f32x4 acc[1][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 raw[2][4], sz[4];
+  load_codes(0, raw, sz);
+  const int arow = nn & (MP - 1);
+  for (int G = 0; G < NG4; ++G) {
+    u32x4 rawn[2][4], szn[4];
+    if (G + 1 < NG4) load_codes(G + 1, rawn, szn);
+    const u32x4* xb = xs + (size_t)(G * 64 + hh) * MP + arow;
+    const float* Xg = Xs + G * 4 * MP + ((4 * hh) & (MP - 1));
+    coarse_group<1, MR, 0>(acc, raw, sz, xb, MP, Xg, 0, one);
+    coarse_group<1, MR, 1>(acc, raw, sz, xb + 16 * MP, MP, Xg + MP, 0, one);
+    coarse_group<1, MR, 2>(acc, raw, sz, xb + 32 * MP, MP, Xg + 2 * MP, 0, one);
+    coarse_group<1, MR, 3>(acc, raw, sz, xb + 48 * MP, MP, Xg + 3 * MP, 0, one);
+    if (G + 1 < NG4) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) raw[h][t] = rawn[h][t];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sz[t] = szn[t];
+    }
+  }
+  if (!blk_ok) return;
+  block_select<1, MR>(acc, A, b, hh, nn);
+}
+
+// ---------------------------------------------------------------------------
+// Coarse kernel, x staged per group (any M up to 80 per launch).
+//
+// Workgroup = 4 waves, one 64-column block each.  The 128 x values of each
+// group are staged in LDS for all rows (double buffered, one barrier per
+// group) with the group sum X; the next group's x is loaded into registers
+// while the current group is computed.  LDS: [2][16 fragments][MP rows]
+// (MP = 16 MT, rows >= M zero), then X[2][MP]; the fixed row count makes the
+// fragment offsets compile-time immediates.
 template <int MT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 2 : 1, MT <= 2 ? 2 : 1))) void coarse_kernel(
-    const uint16_t* __restrict__ x, int M, int K, int N, int nblk,
-    const u32x4* __restrict__ tiled, const u32x4* __restrict__ pairs, int kcand,
-    float* __restrict__ cand_val, int32_t* __restrict__ cand_id, float* __restrict__ coarse_out) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 2 : 1, MT <= 2 ? 2 : 1)))
+void coarse_chunked_kernel(CoarseArgs A) {
   constexpr int MP = 16 * MT;
   __shared__ u32x4 xs[2 * 16 * MP];
   __shared__ float Xs[2 * MP];
@@ -82,19 +365,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT <= 
   const int wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 4, nn = lane & 15;
   const int b = blockIdx.x * kWaves + wave;
-  const bool blk_ok = b < nblk;
-  const int NG4 = K >> 9, Q4 = K >> 2;
-  const int ncand = nblk * kcand;
-  // bf16 pair (1.0, 1.0), kept opaque so it stays in a VGPR (see decode_quarter)
+  const bool blk_ok = b < A.nblk;
+  const int NG4 = A.K >> 9, Q4 = A.K >> 2;
   uint32_t one;
   asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(one));
 
-  // Code tiles of this block: [G][h][t][64 lanes] u32x4; pairs: [G][t][16] u32x4.
   // A wave past the last block reads block 0 (valid memory) and writes nothing.
-  const u32x4* tp = tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
-  const u32x4* pp = pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64;
+  const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
+  const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64;
 
-  // zero the staging buffers once: rows M..MP-1 must read as zero
   for (int i = tid; i < 2 * 16 * MP; i += kThreads) xs[i] = u32x4{0u, 0u, 0u, 0u};
   for (int i = tid; i < 2 * MP; i += kThreads) Xs[i] = 0.f;
   __syncthreads();
@@ -109,49 +388,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT <= 
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        raw[h][t] = tp[((G * 2 + h) * 4 + t) * 64 + lane];
+      for (int t = 0; t < 4; ++t) raw[h][t] = tp[((G * 2 + h) * 4 + t) * 64 + lane];
 #pragma unroll
     for (int t = 0; t < 4; ++t) sz[t] = pp[(G * 4 + t) * 16 + nn];
   };
 
-  // Staging of group (G, q): thread i < 16*M loads natural piece p = i & 15 of row
+  // Staging of group (G, q): thread i < 16*M loads piece p = i & 15 of row
   // m = i >> 4, i.e. x[m][q*K/4 + 128*G + 8p .. +8].
   constexpr int kMaxStage = (16 * MP + kThreads - 1) / kThreads;
-  const int stage_n = 16 * M;
+  const int stage_n = 16 * A.M;
   auto stage_load = [&](int G, int q, u32x4 (&st)[kMaxStage]) {
     const int kbase = q * Q4 + 128 * G;
 #pragma unroll
     for (int r = 0; r < kMaxStage; ++r) {
-      int i = tid + r * kThreads;
-      if (i < stage_n) {
-        int m = i >> 4, p = i & 15;
-        st[r] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + kbase + 8 * p);
-      }
+      const int i = tid + r * kThreads;
+      const int ic = i < stage_n ? i : 0;   // clamped: the load is unconditional
+      st[r] = *reinterpret_cast<const u32x4*>(A.x + (size_t)(ic >> 4) * A.K + kbase + 8 * (ic & 15));
     }
   };
   auto stage_store = [&](int buf, const u32x4 (&st)[kMaxStage]) {
     u32x4* dst = xs + buf * 16 * MP;
 #pragma unroll
     for (int r = 0; r < kMaxStage; ++r) {
-      int i = tid + r * kThreads;
+      const int i = tid + r * kThreads;
       if (i < stage_n) {
-        int m = i >> 4, p = i & 15;
-        u32x4 v = st[r];
-        // natural [x0 x1 | x2 x3 | x4 x5 | x6 x7] -> [x0 x2 | x1 x3 | x4 x6 | x5 x7]
-        u32x4 o;
-        o[0] = (v[0] & 0xFFFFu) | (v[1] << 16);
-        o[1] = (v[0] >> 16) | (v[1] & 0xFFFF0000u);
-        o[2] = (v[2] & 0xFFFFu) | (v[3] << 16);
-        o[3] = (v[2] >> 16) | (v[3] & 0xFFFF0000u);
-        int h = p >> 3, s = (p >> 1) & 3, e = p & 1;
+        const int m = i >> 4, p = i & 15;
+        float sum;
+        const u32x4 o = permute_x(st[r], sum);
+        const int h = p >> 3, s = (p >> 1) & 3, e = p & 1;
         dst[((h * 2 + e) * 4 + s) * MP + m] = o;
-        float sum = lo_bf16(v[0]) + hi_bf16(v[0]) + lo_bf16(v[1]) + hi_bf16(v[1]) +
-                    lo_bf16(v[2]) + hi_bf16(v[2]) + lo_bf16(v[3]) + hi_bf16(v[3]);
-        sum += __shfl_xor(sum, 1, 16);
-        sum += __shfl_xor(sum, 2, 16);
-        sum += __shfl_xor(sum, 4, 16);
-        sum += __shfl_xor(sum, 8, 16);
+        sum = row16_sum(sum);
         if (p == 0) Xs[buf * MP + m] = sum;
       }
     }
@@ -169,58 +435,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT <= 
   for (int G = 0; G < NG4; ++G) {
     u32x4 rawn[2][4], szn[4];
     if (G + 1 < NG4) load_codes(G + 1, rawn, szn);
-
 #pragma nounroll
     for (int q = 0; q < 4; ++q) {
       const int cur = q & 1;  // 4 groups per G, so the buffer parity is q's
-      // prefetch the next group's x into registers
       const bool has_next = (q < 3) || (G + 1 < NG4);
       u32x4 st[kMaxStage];
       if (has_next) stage_load(q < 3 ? G : G + 1, q < 3 ? q + 1 : 0, st);
-
-      // rotate-left amount 5 - 2q (mod 32) for even pairs, shift 3 + 2q for odd ones
-      const uint32_t rot = (uint32_t)(32 - (5 - 2 * q)) & 31u;  // alignbit rotates right
-      const uint32_t shr = 3u + 2u * (uint32_t)q;
-
-      f32x4 cg[MT][4];
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) cg[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-      const u32x4* xb = xs + cur * 16 * MP + hh * MP + nn;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          bf16x8 a[MT];
-#pragma unroll
-          for (int i = 0; i < MT; ++i)
-            a[i] = __builtin_bit_cast(bf16x8, xb[(h * 2 + e) * 4 * MP + 16 * i]);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const bf16x8 bv = decode_quarter(raw[h][t][2 * e], raw[h][t][2 * e + 1], rot, shr, one);
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-              cg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bv, cg[i][t], 0, 0, 0);
-          }
-        }
-      }
-      // group (G, q) complete: acc += S * p - ZS * X for rows 4*hh + r of each tile
-      float X[MT][4];
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) X[i][r] = Xs[cur * MP + 16 * i + 4 * hh + r];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t pr = q == 0 ? sz[t][0] : q == 1 ? sz[t][1] : q == 2 ? sz[t][2] : sz[t][3];
-        const float S = lo_bf16(pr), ZS = hi_bf16(pr);
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][t][r] += S * cg[i][t][r] - ZS * X[i][r];
-      }
+      coarse_group<MT, 4, -1>(acc, raw, sz, xs + cur * 16 * MP + hh * MP + nn, MP, Xs + cur * MP, hh,
+                              one, q);
       if (has_next) stage_store(cur ^ 1, st);
       __syncthreads();
     }
@@ -233,219 +455,388 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT <= 
       for (int t = 0; t < 4; ++t) sz[t] = szn[t];
     }
   }
-
   if (!blk_ok) return;
-
-  // Epilogue: optional full row, then top-kcand of the block by successive
-  // max-and-mask (`_emit`).  Lane (hh, nn) holds columns 16t + nn of rows
-  // 16i + 4hh + r; the four rows of one (i, r) are handled at once, one per
-  // 16-lane row of the wave.
-  const float NEG_INF = -__builtin_inff();
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (16 * i + r >= M) continue;  // no row of this (i, r) is live (wave-uniform)
-      const int m = 16 * i + 4 * hh + r;
-      const bool row_ok = m < M;
-      float v[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = b * 64 + 16 * t + nn;
-        const bool ok = row_ok && n < N;
-        v[t] = ok ? acc[i][t][r] : NEG_INF;
-        if (coarse_out && ok) coarse_out[(size_t)m * N + n] = acc[i][t][r];
-      }
-      float kv[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
-      int ki[4] = {-1, -1, -1, -1};
-      for (int c = 0; c < kcand; ++c) {
-        float bv = v[0];
-        int bn = nn;
-#pragma unroll
-        for (int t = 1; t < 4; ++t)
-          if (v[t] > bv) {
-            bv = v[t];
-            bn = 16 * t + nn;
-          }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          float ov = __shfl_xor(bv, off, 16);
-          int on = __shfl_xor(bn, off, 16);
-          if (ov > bv || (ov == bv && on < bn)) {
-            bv = ov;
-            bn = on;
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (bn == 16 * t + nn) v[t] = NEG_INF;
-        if ((c & 15) == nn) {
-          const int slot = c >> 4;
-          const float val = bv;
-          const int id = (bv == NEG_INF) ? -1 : b * 64 + bn;
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            if (s == slot) {
-              kv[s] = val;
-              ki[s] = id;
-            }
-        }
-      }
-      if (row_ok) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int c = 16 * s + nn;
-          if (c < kcand) {
-            const size_t o = (size_t)m * ncand + (size_t)b * kcand + c;
-            cand_val[o] = kv[s];
-            cand_id[o] = ki[s];
-          }
-        }
-      }
-    }
-  }
+  block_select<MT, 4>(acc, A, b, hh, nn);
 }
 
 // ---------------------------------------------------------------------------
-// Row top-R: one workgroup per row.  Each candidate becomes a 64-bit key
-// (ordered float bits << 32 | ~id), so "larger key" is "larger value, then
-// lower id" and all keys of valid candidates are distinct; invalid slots
-// (id -1, or an id >= N that no coarse call writes) get key 0.  An 8-bit radix select over the 64-bit keys finds the
-// R-th largest key, the keys at or above it are gathered and bitonic-sorted.
+// Rerank: one workgroup per row.
+//
+// Selection (`bm.topk(RERANK)` + `bi.gather`): each candidate becomes a 64-bit
+// key (ordered float bits << 32 | ~id), so "larger key" is "larger value, then
+// lower id", and the keys of valid candidates are all distinct; invalid slots
+// (id -1, or an id >= N that no coarse call writes) get key 0.
+//   1. Thread t reads candidates t, t + 1024, ... (coalesced) and keeps them
+//      and their maximum.
+//   2. Wave 0 finds T, the R-th largest of the 1024 per-thread maxima, by a
+//      radix select over 8-bit digits with no workgroup barrier.  R maxima
+//      are >= T, so the R-th largest key overall is >= T.
+//   3. The keys >= T (usually a few more than R) are gathered; wave 0 sorts
+//      them with a shuffle bitonic network when there are at most 64, the
+//      workgroup with an LDS bitonic network otherwise.
+// Rows with more than 16384 candidates, R above the 1024 maxima, or more than
+// DH_MAX_R survivors take T from a workgroup radix select over all keys.
+//
+// Exact logits (`_rerank_exact`, bf16 branch): the 16 waves then take the R
+// selected rows of W in turn, one dot of length K each, fp32 products and sums,
+// all loads of a row issued before any is used.
 constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelCache = 16;
 
 __device__ __forceinline__ unsigned long long cand_key(float v, int id, int N) {
   if (id < 0 || id >= N) return 0ull;
-  uint32_t u = __float_as_uint(v);
-  uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)id);
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ cand_val,
-                                                             const int32_t* __restrict__ cand_id,
-                                                             int ncand, int N, int R,
-                                                             int32_t* __restrict__ rr_id) {
-  __shared__ unsigned int hist[256];
-  __shared__ unsigned long long keys[DH_MAX_R];
-  __shared__ unsigned long long s_prefix;
-  __shared__ int s_need;
-  __shared__ unsigned int s_valid;
-  __shared__ unsigned int s_count;
+__device__ __forceinline__ uint32_t key_id(unsigned long long k) {
+  return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull);
+}
 
-  const int m = blockIdx.x, tid = threadIdx.x;
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+__device__ __forceinline__ unsigned long long umin64(unsigned long long a, unsigned long long b) {
+  return a < b ? a : b;
+}
+
+struct SelectShared {
+  unsigned int whist[kSelWaves][256];
+  unsigned long long tmax[kSelThreads];
+  unsigned long long keys[DH_MAX_R];
+  unsigned long long wmax[kSelWaves], wmin[kSelWaves];
+  unsigned int wcnt[kSelWaves];
+  unsigned long long prefix, thresh;
+  int need, done;
+  unsigned int count;
+};
+
+// Block-wide count, max and min of per-thread values.
+__device__ void block_stats(unsigned int cnt, unsigned long long vmax, unsigned long long vmin,
+                            SelectShared& sh, unsigned int& total, unsigned long long& gmax,
+                            unsigned long long& gmin) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int off = 32; off > 0; off >>= 1) {
+    cnt += __shfl_xor(cnt, off, 64);
+    vmax = umax64(vmax, __shfl_xor(vmax, off, 64));
+    vmin = umin64(vmin, __shfl_xor(vmin, off, 64));
+  }
+  if (lane == 0) {
+    sh.wcnt[wave] = cnt;
+    sh.wmax[wave] = vmax;
+    sh.wmin[wave] = vmin;
+  }
+  __syncthreads();
+  total = 0;
+  gmax = 0ull;
+  gmin = ~0ull;
+  for (int i = 0; i < kSelWaves; ++i) {
+    total += sh.wcnt[i];
+    gmax = umax64(gmax, sh.wmax[i]);
+    gmin = umin64(gmin, sh.wmin[i]);
+  }
+  __syncthreads();
+}
+
+// One radix pass decision: given the 256 digit counts c[4 * lane + d] of the
+// keys matching the current prefix, find the digit holding the need-th largest
+// key.  Returns (in all lanes) the digit, the rank within it and whether the
+// bucket is taken whole.
+__device__ __forceinline__ void pick_digit(const unsigned int (&c)[4], int need, int& digit,
+                                           int& need_out, bool& whole) {
+  const int lane = threadIdx.x & 63;
+  const unsigned int mine = c[0] + c[1] + c[2] + c[3];
+  unsigned int incl = mine;  // sum over lanes >= l
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned int o = __shfl_down(incl, off, 64);
+    if (lane + off < 64) incl += o;
+  }
+  unsigned int above = incl - mine;
+  int my_digit = -1, my_need = 0, my_whole = 0;
+#pragma unroll
+  for (int d = 3; d >= 0; --d) {
+    if (above < (unsigned)need && above + c[d] >= (unsigned)need) {
+      my_digit = 4 * lane + d;
+      my_need = need - (int)above;
+      my_whole = above + c[d] == (unsigned)need;
+    }
+    above += c[d];
+  }
+  const unsigned long long who = __ballot(my_digit >= 0);
+  const int src = __ffsll((long long)who) - 1;
+  digit = __shfl(my_digit, src, 64);
+  need_out = __shfl(my_need, src, 64);
+  whole = __shfl(my_whole, src, 64) != 0;
+}
+
+// k-th largest (1 <= k <= count of non-zero keys) of the non-zero keys the
+// calling wave's lanes hold in v[0..NV) (wave-level, no workgroup barrier;
+// hist: 256 words of LDS private to the wave).  Skips the leading bytes all
+// keys share; stops once the bucket holding the k-th key is taken whole.
+// Returns the smallest key of that bucket: exactly k keys are >= it.
+template <int NV>
+__device__ unsigned long long wave_kth_largest(const unsigned long long (&v)[NV], int k,
+                                               unsigned int* hist) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long vmax = 0ull, vmin = ~0ull;
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+    if (v[j]) {
+      vmax = umax64(vmax, v[j]);
+      vmin = umin64(vmin, v[j]);
+    }
+  for (int off = 32; off > 0; off >>= 1) {
+    vmax = umax64(vmax, __shfl_xor(vmax, off, 64));
+    vmin = umin64(vmin, __shfl_xor(vmin, off, 64));
+  }
+  if (vmax == vmin) return vmax;
+  const int common = __builtin_clzll(vmax ^ vmin) & ~7;
+  unsigned long long pre = common ? (vmax >> (64 - common)) : 0ull;
+  int need = k, shift = 64 - common;
+  for (;;) {
+    shift -= 8;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) hist[4 * lane + d] = 0u;
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the clears land before the adds
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const unsigned long long key = v[j];
+      if (key && (shift + 8 == 64 || (key >> (shift + 8)) == pre))
+        atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    unsigned int c[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) c[d] = hist[4 * lane + d];
+    int digit, nneed;
+    bool whole;
+    pick_digit(c, need, digit, nneed, whole);
+    pre = (pre << 8) | (unsigned long long)digit;
+    need = nneed;
+    if (whole || shift == 0) break;
+  }
+  return pre << shift;
+}
+
+// Same, over the whole workgroup: keys presented by for_each_key(f).
+template <class ForEach>
+__device__ unsigned long long block_kth_largest(ForEach for_each_key, int k, unsigned long long gmax,
+                                                unsigned long long gmin, SelectShared& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (gmax == gmin) return gmax;
+  const int common = __builtin_clzll(gmax ^ gmin) & ~7;
+  unsigned long long pre = common ? (gmax >> (64 - common)) : 0ull;
+  int need = k, shift = 64 - common;
+  for (;;) {
+    shift -= 8;
+    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&sh.whist[0][0])[i] = 0u;
+    __syncthreads();
+    for_each_key([&](unsigned long long key) {
+      if (key && (shift + 8 == 64 || (key >> (shift + 8)) == pre))
+        atomicAdd(&sh.whist[wave][(key >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    if (tid < 64) {
+      unsigned int c[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        unsigned int t = 0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) t += sh.whist[w][4 * lane + d];
+        c[d] = t;
+      }
+      int digit, nneed;
+      bool whole;
+      pick_digit(c, need, digit, nneed, whole);
+      if (lane == 0) {
+        sh.prefix = (pre << 8) | (unsigned long long)digit;
+        sh.need = nneed;
+        sh.done = whole || shift == 0;
+      }
+    }
+    __syncthreads();
+    pre = sh.prefix;
+    need = sh.need;
+    const int done = sh.done;
+    __syncthreads();
+    if (done) break;
+  }
+  return pre << shift;
+}
+
+__global__ __launch_bounds__(kSelThreads) void rerank_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t ldw, int K, int N,
+    const float* __restrict__ cand_val, const int32_t* __restrict__ cand_id, int ncand, int R,
+    int32_t* __restrict__ rr_id, float* __restrict__ rr_val) {
+  __shared__ SelectShared sh;
+  const int m = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float* cv = cand_val + (size_t)m * ncand;
   const int32_t* ci = cand_id + (size_t)m * ncand;
+  const bool cached = ncand <= kSelThreads * kSelCache;
 
-  if (tid == 0) {
-    s_valid = 0;
-    s_count = 0;
-    s_prefix = 0;
-    s_need = R;
-  }
-  __syncthreads();
-  unsigned int local = 0;
-  for (int i = tid; i < ncand; i += kSelThreads) local += (ci[i] >= 0 && ci[i] < N) ? 1u : 0u;
-  atomicAdd(&s_valid, local);
-  __syncthreads();
-  const unsigned int nvalid = s_valid;
-
-  unsigned long long thresh = 1ull;  // all valid keys if there are at most R of them
-  if (nvalid > (unsigned)R) {
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-      __syncthreads();
-      const unsigned long long pre = s_prefix;
-      for (int i = tid; i < ncand; i += kSelThreads) {
-        unsigned long long k = cand_key(cv[i], ci[i], N);
-        if (k == 0) continue;
-        if (pass > 0 && (k >> (shift + 8)) != pre) continue;
-        atomicAdd(&hist[(k >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      // exact scan of the 256 bins from the top, by one thread
-      if (tid == 0) {
-        int need = s_need;
-        unsigned int cum = 0;
-        int digit = 0;
-        for (int d = 255; d >= 0; --d) {
-          if (cum + hist[d] >= (unsigned)need) {
-            digit = d;
-            break;
-          }
-          cum += hist[d];
-        }
-        s_need = need - (int)cum;
-        s_prefix = (pre << 8) | (unsigned long long)digit;
-      }
-      __syncthreads();
+  // 1. keys (thread t: candidates t + 1024 j), their count, max and min
+  unsigned long long kc[kSelCache];
+  unsigned long long tmax = 0ull, tmin = ~0ull;
+  unsigned int tcnt = 0;
+  if (cached) {
+    float vv[kSelCache];
+    int iv[kSelCache];
+#pragma unroll
+    for (int j = 0; j < kSelCache; ++j) {   // clamped, unconditional loads
+      const int i = min(tid + j * kSelThreads, ncand - 1);
+      vv[j] = cv[i];
+      iv[j] = ci[i];
     }
-    thresh = s_prefix;
-  }
-  for (int i = tid; i < ncand; i += kSelThreads) {
-    unsigned long long k = cand_key(cv[i], ci[i], N);
-    if (k != 0 && k >= thresh) {
-      unsigned int pos = atomicAdd(&s_count, 1u);
-      if (pos < (unsigned)DH_MAX_R) keys[pos] = k;
+#pragma unroll
+    for (int j = 0; j < kSelCache; ++j)
+      kc[j] = tid + j * kSelThreads < ncand ? cand_key(vv[j], iv[j], N) : 0ull;
+#pragma unroll
+    for (int j = 0; j < kSelCache; ++j)
+      if (kc[j]) {
+        ++tcnt;
+        tmax = umax64(tmax, kc[j]);
+        tmin = umin64(tmin, kc[j]);
+      }
+  } else {
+    for (int i = tid; i < ncand; i += kSelThreads) {
+      const unsigned long long key = cand_key(cv[i], ci[i], N);
+      if (key) {
+        ++tcnt;
+        tmax = umax64(tmax, key);
+        tmin = umin64(tmin, key);
+      }
     }
   }
-  __syncthreads();
-  const int cnt = (int)min(s_count, (unsigned)R);
-  int P = 1;
-  while (P < cnt) P <<= 1;
-  for (int i = cnt + tid; i < P; i += kSelThreads) keys[i] = 0ull;
-  __syncthreads();
-  // bitonic sort, descending
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < P; i += kSelThreads) {
-        int j = i ^ stride;
-        if (j > i) {
-          bool desc = (i & size) == 0;
-          unsigned long long a = keys[i], c = keys[j];
-          if (desc ? (a < c) : (a > c)) {
-            keys[i] = c;
-            keys[j] = a;
-          }
+  sh.tmax[tid] = tmax;
+  unsigned int nvalid;
+  unsigned long long gmax, gmin;
+  block_stats(tcnt, tmax, tmin, sh, nvalid, gmax, gmin);   // (its barriers publish tmax too)
+
+  auto each_key = [&](auto&& f) {
+    if (cached) {
+#pragma unroll
+      for (int j = 0; j < kSelCache; ++j) f(kc[j]);
+    } else {
+      for (int i = tid; i < ncand; i += kSelThreads) f(cand_key(cv[i], ci[i], N));
+    }
+  };
+  auto gather = [&](unsigned long long t) {
+    __syncthreads();   // earlier readers of sh.count are done
+    if (tid == 0) sh.count = 0;
+    __syncthreads();
+    each_key([&](unsigned long long key) {
+      if (key && key >= t) {
+        const unsigned int pos = atomicAdd(&sh.count, 1u);
+        if (pos < (unsigned)DH_MAX_R) sh.keys[pos] = key;
+      }
+    });
+    __syncthreads();
+    return sh.count;
+  };
+
+  // 2. threshold; 3. survivors
+  unsigned int got;
+  if (nvalid <= (unsigned)R) {
+    got = gather(1ull);                  // every valid key
+  } else {
+    bool exact = !cached;
+    if (cached) {
+      if (wave == 0) {
+        unsigned long long mv[kSelCache];
+        unsigned int nm = 0;
+#pragma unroll
+        for (int j = 0; j < kSelCache; ++j) {
+          mv[j] = sh.tmax[lane + 64 * j];
+          nm += mv[j] != 0ull;
         }
+        for (int off = 32; off > 0; off >>= 1) nm += __shfl_xor(nm, off, 64);
+        // with at most R non-empty threads every valid key is a survivor
+        const unsigned long long t = nm > (unsigned)R ? wave_kth_largest(mv, R, &sh.whist[0][0]) : 1ull;
+        if (lane == 0) sh.thresh = t;
       }
       __syncthreads();
+      got = gather(sh.thresh);
+      exact = got > (unsigned)DH_MAX_R;
+    }
+    if (exact) got = gather(block_kth_largest(each_key, R, gmax, gmin, sh));
+  }
+  const int cnt = (int)min(got, (unsigned)R);
+  const int ns = (int)min(got, (unsigned)DH_MAX_R);
+
+  // sort the survivors, descending
+  if (ns <= 64) {
+    if (wave == 0) {
+      unsigned long long v = lane < ns ? sh.keys[lane] : 0ull;
+      for (int size = 2; size <= 64; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          const unsigned long long o = __shfl_xor(v, stride, 64);
+          const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
+          v = keep_max ? umax64(v, o) : umin64(v, o);
+        }
+      if (lane < ns) sh.keys[lane] = v;
+    }
+    __syncthreads();
+  } else {
+    int P = 1;
+    while (P < ns) P <<= 1;
+    for (int i = ns + tid; i < P; i += kSelThreads) sh.keys[i] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < P; i += kSelThreads) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const bool desc = (i & size) == 0;
+            const unsigned long long a = sh.keys[i], c = sh.keys[j];
+            if (desc ? (a < c) : (a > c)) {
+              sh.keys[i] = c;
+              sh.keys[j] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
     }
   }
   for (int r = tid; r < R; r += kSelThreads)
-    rr_id[(size_t)m * R + r] = (r < cnt) ? (int32_t)(0xFFFFFFFFu - (uint32_t)(keys[r] & 0xFFFFFFFFull)) : -1;
-}
+    rr_id[(size_t)m * R + r] = (r < cnt) ? (int32_t)key_id(sh.keys[r]) : -1;
 
-// Exact logits: one wave per (row, candidate); fp32 products and sums.
-__global__ __launch_bounds__(256) void dot_kernel(const uint16_t* __restrict__ x,
-                                                  const uint16_t* __restrict__ w, int64_t ldw,
-                                                  int M, int K, int N, int R,
-                                                  const int32_t* __restrict__ rr_id,
-                                                  float* __restrict__ rr_val) {
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (gw >= M * R) return;
-  const int m = gw / R;
-  const int id = rr_id[gw];
-  if (id < 0 || id >= N) {
-    if (lane == 0) rr_val[gw] = -__builtin_inff();
-    return;
-  }
+  // exact logits of the selected rows: each wave issues all loads of a row
+  // (up to 5120 elements at a time) before using any of them
+  constexpr int kDotUnroll = 10;
   const uint16_t* xr = x + (size_t)m * K;
-  const uint16_t* wr = w + (size_t)id * ldw;
-  float s0 = 0.f, s1 = 0.f;
-  for (int k = lane * 8; k < K; k += 512) {
-    u32x4 xv = *reinterpret_cast<const u32x4*>(xr + k);
-    u32x4 wv = *reinterpret_cast<const u32x4*>(wr + k);
+  for (int r = wave; r < R; r += kSelWaves) {
+    float s0 = 0.f, s1 = 0.f;
+    const bool valid = r < cnt;
+    if (valid) {
+      const int id = (int)key_id(sh.keys[r]);
+      const uint16_t* wr = w + (size_t)id * ldw;
+      for (int k0 = 0; k0 < K; k0 += 512 * kDotUnroll) {
+        u32x4 xv[kDotUnroll], wv[kDotUnroll];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s0 += lo_bf16(xv[j]) * lo_bf16(wv[j]);
-      s1 += hi_bf16(xv[j]) * hi_bf16(wv[j]);
+        for (int j = 0; j < kDotUnroll; ++j) {   // clamped, unconditional loads
+          const int k = min(k0 + 512 * j + lane * 8, K - 8);
+          wv[j] = *reinterpret_cast<const u32x4*>(wr + k);
+          xv[j] = *reinterpret_cast<const u32x4*>(xr + k);
+        }
+#pragma unroll
+        for (int j = 0; j < kDotUnroll; ++j) {
+          if (k0 + 512 * j + lane * 8 < K) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              s0 = __builtin_fmaf(lo_bf16(xv[j][c]), lo_bf16(wv[j][c]), s0);
+              s1 = __builtin_fmaf(hi_bf16(xv[j][c]), hi_bf16(wv[j][c]), s1);
+            }
+          }
+        }
+      }
     }
+    float sum = s0 + s1;
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) rr_val[(size_t)m * R + r] = valid ? sum : -__builtin_inff();
   }
-  float s = s0 + s1;
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (lane == 0) rr_val[gw] = s;
 }
 
 // Final token: one wave per row; largest value, ties to the lower id, id -1 skipped.
@@ -502,14 +893,37 @@ int launch_error(const char* what) {
   return dh::ok();
 }
 
-template <int MT>
-void launch_coarse(const uint16_t* x, int M, int K, int N, int nblk, const u32x4* tiled,
-                   const u32x4* pairs, int kcand, float* cv, int32_t* ci, float* co,
-                   hipStream_t s) {
-  dim3 grid((nblk + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(coarse_kernel<MT>, grid, dim3(kThreads), 0, s, x, M, K, N, nblk, tiled,
-                     pairs, kcand, cv, ci, co);
+constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
+
+size_t resident_lds_bytes(int K, int MP) {
+  const size_t groups = (size_t)K / DH_GROUP;
+  return groups * 16 * MP * 16 + groups * MP * sizeof(float);
 }
+
+template <int MP>
+hipError_t launch_resident(const CoarseArgs& A, hipStream_t s) {
+  const size_t lds = resident_lds_bytes(A.K, MP);
+  static bool attr_set = false;   // the attribute only ever grows to kMaxLds
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&coarse_resident_kernel<MP>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  constexpr int waves = res_waves<MP>();
+  dim3 grid((A.nblk + waves - 1) / waves);
+  hipLaunchKernelGGL(coarse_resident_kernel<MP>, grid, dim3(64 * waves), lds, s, A);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_chunked(const CoarseArgs& A, hipStream_t s) {
+  dim3 grid((A.nblk + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL(coarse_chunked_kernel<MT>, grid, dim3(kThreads), 0, s, A);
+  return hipGetLastError();
+}
+
+int resident_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
 }  // namespace
 
@@ -530,26 +944,36 @@ int draft_head_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, 
   const int nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
   const int ncand = nblk * kcand;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const uint16_t* xb = static_cast<const uint16_t*>(x);
-  const u32x4* tp = reinterpret_cast<const u32x4*>(tiled);
-  const u32x4* pp = reinterpret_cast<const u32x4*>(pairs);
+  CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
+               reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out};
+  hipError_t e = hipSuccess;
+  if (M <= 8 && resident_lds_bytes(K, resident_rows(M)) <= kMaxLds) {
+    switch (resident_rows(M)) {
+      case 1: e = launch_resident<1>(A, s); break;
+      case 2: e = launch_resident<2>(A, s); break;
+      case 4: e = launch_resident<4>(A, s); break;
+      default: e = launch_resident<8>(A, s); break;
+    }
+    if (e != hipSuccess) return dh::fail(DH_EHIP, "coarse_resident_kernel: %s", hipGetErrorString(e));
+    return dh::ok();
+  }
   // Rows beyond one launch's 80 are handled by further launches over the
   // same weights (only for M > 80).
   for (int m0 = 0; m0 < M; m0 += 16 * kMaxMT) {
-    const int mm = std::min(M - m0, 16 * kMaxMT);
-    const int mt = (mm + 15) / 16;
-    const uint16_t* xm = xb + (size_t)m0 * K;
-    float* cv = cand_val + (size_t)m0 * ncand;
-    int32_t* ci = cand_id + (size_t)m0 * ncand;
-    float* co = coarse_out ? coarse_out + (size_t)m0 * N : nullptr;
-    switch (mt) {
-      case 1: launch_coarse<1>(xm, mm, K, N, nblk, tp, pp, kcand, cv, ci, co, s); break;
-      case 2: launch_coarse<2>(xm, mm, K, N, nblk, tp, pp, kcand, cv, ci, co, s); break;
-      case 3: launch_coarse<3>(xm, mm, K, N, nblk, tp, pp, kcand, cv, ci, co, s); break;
-      case 4: launch_coarse<4>(xm, mm, K, N, nblk, tp, pp, kcand, cv, ci, co, s); break;
-      default: launch_coarse<5>(xm, mm, K, N, nblk, tp, pp, kcand, cv, ci, co, s); break;
+    CoarseArgs B = A;
+    B.M = std::min(M - m0, 16 * kMaxMT);
+    B.x = A.x + (size_t)m0 * K;
+    B.cand_val = cand_val + (size_t)m0 * ncand;
+    B.cand_id = cand_id + (size_t)m0 * ncand;
+    B.coarse_out = coarse_out ? coarse_out + (size_t)m0 * N : nullptr;
+    switch ((B.M + 15) / 16) {
+      case 1: e = launch_chunked<1>(B, s); break;
+      case 2: e = launch_chunked<2>(B, s); break;
+      case 3: e = launch_chunked<3>(B, s); break;
+      case 4: e = launch_chunked<4>(B, s); break;
+      default: e = launch_chunked<5>(B, s); break;
     }
-    if ((rc = launch_error("coarse_kernel"))) return rc;
+    if (e != hipSuccess) return dh::fail(DH_EHIP, "coarse_chunked_kernel: %s", hipGetErrorString(e));
   }
   return dh::ok();
 }
@@ -571,15 +995,9 @@ int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, i
   if (!aligned16(x) || !aligned16(w))
     return dh::fail(DH_EINVAL, "rerank: x and w must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(select_kernel, dim3(M), dim3(kSelThreads), 0, s, cand_val, cand_id, ncand, N, R,
-                     rr_id);
-  if ((rc = launch_error("select_kernel"))) return rc;
-  const int waves = M * R;
-  hipLaunchKernelGGL(dot_kernel, dim3((waves + 3) / 4), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), ldw, M, K, N, R,
-                     rr_id, rr_val);
-  if ((rc = launch_error("dot_kernel"))) return rc;
-  return dh::ok();
+  hipLaunchKernelGGL(rerank_kernel, dim3(M), dim3(kSelThreads), 0, s, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(w), ldw, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
+  return launch_error("rerank_kernel");
 }
 
 int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, int32_t* out_id,
