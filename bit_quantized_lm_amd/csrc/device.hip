@@ -29,39 +29,39 @@ constexpr int kMaxMT = 5;            // 16-row M tiles per coarse launch (80 row
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Decode quarter q of two adjacent code dwords into four bf16 pairs of 1 + v/4.
-// Code v sits in bits 2q..2q+1 of each byte; moving it to bits 5-6 of a
-// halfword and OR-ing 0x3F80 gives the bf16 value 1 + v/4 (the bit-pattern
-// dequant of the module docstring).  Even pairs hold bytes 0 and 2 of a dword
-// (shift left by 5 - 2q, right by 1 for q = 3), odd pairs bytes 1 and 3
-// (shift right by 3 + 2q).  Both dwords are shifted at once as one 64-bit
-// value: the bits that cross between them land in bits 0-4 or 23-31 of a
-// word, which the mask drops.  Element order of the result: byte {0, 2, 1, 3}
-// of d0 then {0, 2, 1, 3} of d1; the x fragments are staged in the same order.
+// Decode quarter q of two code dwords into four bf16 pairs holding v * 2^(2q-133).
 //
-// `one` must hold 0x3F803F80 in a VGPR: gfx9-family VOP3 instructions take no
-// literal operand, so with the mask in an SGPR and `one` in a VGPR each pair
-// is one v_and_or_b32 after the shared shift.
-template <int Q>
-__device__ __forceinline__ bf16x8 decode_quarter(uint32_t d0, uint32_t d1, uint32_t one) {
-  constexpr uint32_t kMask = 0x00600060u;
-  const uint64_t d = ((uint64_t)d1 << 32) | d0;
-  const uint64_t ev = Q < 3 ? (d << (5 - 2 * Q)) : (d >> 1);
-  const uint64_t od = d >> (3 + 2 * Q);
-  u32x4 v = {((uint32_t)ev & kMask) | one, ((uint32_t)od & kMask) | one,
-             ((uint32_t)(ev >> 32) & kMask) | one, ((uint32_t)(od >> 32) & kMask) | one};
+// Code v of quarter q sits in bits 2q..2q+1 of each byte.  Masking a byte pair
+// (bytes 0 and 2, or bytes 1 and 3 after a shift right by 8) with
+// 0x00030003 << 2q leaves each code in place in a bf16 halfword whose exponent
+// field is zero: for q < 3 that is the denormal v * 2^(2q-133); for q = 3 the
+// code's high bit is the exponent's low bit, and 0x40 / 0x80 / 0xC0 read as
+// 2^-127 / 2^-126 / 1.5 * 2^-126, i.e. again exactly v * 2^(6-133).  So one AND
+// decodes two weights with no 1.0 bias to cancel (the page's bit-pattern
+// decode produced 1 + v/4; this one produces v scaled by a power of two).
+// The matrix cores keep bf16 denormal inputs, and x is staged scaled by 2^64
+// so that the products stay normal fp32 values.  Element order of the result:
+// byte {0, 2, 1, 3} of d0 then {0, 2, 1, 3} of d1 (the x fragments are staged
+// in the same order); o0, o1 are d0 >> 8 and d1 >> 8.
+__device__ __forceinline__ bf16x8 decode_quarter(uint32_t d0, uint32_t o0, uint32_t d1, uint32_t o1,
+                                                 uint32_t mask) {
+  u32x4 v = {d0 & mask, o0 & mask, d1 & mask, o1 & mask};
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Same decode for a quarter q known only at run time: the even pairs rotate
-// left by 5 - 2q (for q = 3 a rotate right by 1; rotated-around bits land in
-// bits 0-4 or 31 and are masked off), the odd pairs shift right by 3 + 2q.
-__device__ __forceinline__ bf16x8 decode_quarter_rt(uint32_t d0, uint32_t d1, uint32_t rot,
-                                                    uint32_t shr, uint32_t one) {
-  constexpr uint32_t kMask = 0x00600060u;
-  u32x4 v = {(__builtin_amdgcn_alignbit(d0, d0, rot) & kMask) | one, ((d0 >> shr) & kMask) | one,
-             (__builtin_amdgcn_alignbit(d1, d1, rot) & kMask) | one, ((d1 >> shr) & kMask) | one};
-  return __builtin_bit_cast(bf16x8, v);
+constexpr int kXScaleLog2 = 64;   // x is staged as x * 2^64
+
+// Multiplier turning the MFMA sum D = sum x 2^64 v 2^(2q-133) of quarter q into
+// (S/4) sum x v: S * 2^(133 - 64 - 2q - 2).
+__device__ __forceinline__ float quarter_scale(float S, int q) {
+  return __builtin_ldexpf(S, 133 - kXScaleLog2 - 2 - 2 * q);
+}
+
+// bf16 x (bits) scaled by 2^64, exactly (|x| < 2^63 stays finite).
+__device__ __forceinline__ uint32_t scale_x_pair(uint32_t w) {
+  const float lo = __builtin_ldexpf(lo_bf16(w), kXScaleLog2);
+  const float hi = __builtin_ldexpf(hi_bf16(w), kXScaleLog2);
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
 }
 
 // ---------------------------------------------------------------------------
@@ -94,19 +94,19 @@ struct CoarseArgs {
 // One group: MFMAs of the (h, e) fragments for all tiles, then the scale update.
 // `xb` points at this lane's fragment 0 of the group (A row nn, k-slot hh),
 // fragment f of M-tile i at xb[f * fstride + 16 * i]; `Xg` at the group's X[row].
-// Q >= 0: the quarter is a compile-time constant; Q < 0: it is `q`.
-template <int MT, int MR, int Q>
-__device__ __forceinline__ void coarse_group(f32x4 (&acc)[MT][4], const u32x4 (&raw)[2][4],
-                                             const u32x4 (&sz)[4], const u32x4* xb, int fstride,
-                                             const float* Xg, int hh, uint32_t one, int q = Q) {
-  // run-time decode: rotate-left 5 - 2q as a right rotate, odd shift 3 + 2q
-  const uint32_t rot = (uint32_t)(32 - (5 - 2 * q)) & 31u;
-  const uint32_t shr = 3u + 2u * (uint32_t)q;
-  f32x4 cg[MT][4];
+// MFMA phase of one group (quarter Q of a byte group; Q < 0: quarter `q`
+// known at run time): cg = sum over the group's k of x 2^64 * v 2^(2q-133).
+// The wave covers NT 16-column tiles; raw8 holds raw >> 8 (the odd byte pairs
+// moved down), computed once per byte group.
+template <int MT, int Q, int NT>
+__device__ __forceinline__ void group_mma(f32x4 (&cg)[MT][NT], const u32x4 (&raw)[2][NT],
+                                          const u32x4 (&raw8)[2][NT], const u32x4* xb, int fstride,
+                                          int q = Q) {
+  const uint32_t mask = 0x00030003u << (2 * q);
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) cg[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) cg[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -116,41 +116,71 @@ __device__ __forceinline__ void coarse_group(f32x4 (&acc)[MT][4], const u32x4 (&
       for (int i = 0; i < MT; ++i)
         a[i] = __builtin_bit_cast(bf16x8, xb[(h * 2 + e) * 4 * fstride + 16 * i]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bf16x8 bv;
-        if constexpr (Q >= 0) bv = decode_quarter<Q>(raw[h][t][2 * e], raw[h][t][2 * e + 1], one);
-        else bv = decode_quarter_rt(raw[h][t][2 * e], raw[h][t][2 * e + 1], rot, shr, one);
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 bv = decode_quarter(raw[h][t][2 * e], raw8[h][t][2 * e], raw[h][t][2 * e + 1],
+                                         raw8[h][t][2 * e + 1], mask);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
           cg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bv, cg[i][t], 0, 0, 0);
       }
     }
   }
+}
+
+// Scale phase of one group: acc += (S/4) sum x v - (ZS - S) sum x, with S, ZS
+// the group's premultiplied pair (the page's S * p - ZS * X written for codes
+// decoded without the 1.0 bias).  Rows 16i + 4hh + r, r < MR.
+template <int MT, int MR, int Q, int NT>
+__device__ __forceinline__ void group_scale(f32x4 (&acc)[MT][NT], const f32x4 (&cg)[MT][NT],
+                                            const u32x4 (&sz)[NT], const float* Xg, int hh, int q = Q) {
   float X[MT][MR];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int r = 0; r < MR; ++r) X[i][r] = Xg[16 * i + 4 * hh + r];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < NT; ++t) {
     uint32_t pr;
     if constexpr (Q >= 0) pr = sz[t][Q];
     else pr = q == 0 ? sz[t][0] : q == 1 ? sz[t][1] : q == 2 ? sz[t][2] : sz[t][3];
-    const float S = lo_bf16(pr), nZS = -hi_bf16(pr);
+    const float S = lo_bf16(pr);
+    const float Sq = quarter_scale(S, q), nzp = S - hi_bf16(pr);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int r = 0; r < MR; ++r)
-        acc[i][t][r] = __builtin_fmaf(nZS, X[i][r], __builtin_fmaf(S, cg[i][t][r], acc[i][t][r]));
+        acc[i][t][r] = __builtin_fmaf(nzp, X[i][r], __builtin_fmaf(Sq, cg[i][t][r], acc[i][t][r]));
   }
+}
+
+template <int MT, int MR, int Q, int NT>
+__device__ __forceinline__ void coarse_group(f32x4 (&acc)[MT][NT], const u32x4 (&raw)[2][NT],
+                                             const u32x4 (&raw8)[2][NT], const u32x4 (&sz)[NT],
+                                             const u32x4* xb, int fstride, const float* Xg, int hh,
+                                             int q = Q) {
+  f32x4 cg[MT][NT];
+  group_mma<MT, Q, NT>(cg, raw, raw8, xb, fstride, q);
+  group_scale<MT, MR, Q, NT>(acc, cg, sz, Xg, hh, q);
+}
+
+template <int NT>
+__device__ __forceinline__ void shift_codes(const u32x4 (&raw)[2][NT], u32x4 (&raw8)[2][NT]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) raw8[h][t][c] = raw[h][t][c] >> 8;
 }
 
 // Epilogue of one block: optional full rows, then the top-kcand of the block by
 // successive max-and-mask (`_emit`), ties to the lower column.  The four rows
 // 16i + 4hh + r of one (i, r) are handled at once, one per 16-lane row.
-template <int MT, int MR>
-__device__ __forceinline__ void block_select(const f32x4 (&acc)[MT][4], const CoarseArgs& A, int b,
-                                             int hh, int nn) {
+// value(i, r, t): the coarse score of row 16i + 4hh + r, column 64b + 16t + nn.
+// Passes with r % rstep != rfirst are left to another wave.
+template <int MT, int MR, class Value>
+__device__ __forceinline__ void block_select(Value value, const CoarseArgs& A, int b, int hh, int nn,
+                                             int rfirst = 0, int rstep = 1) {
   const float NEG_INF = -__builtin_inff();
   const int ncand = A.nblk * A.kcand;
 #pragma unroll
@@ -158,6 +188,7 @@ __device__ __forceinline__ void block_select(const f32x4 (&acc)[MT][4], const Co
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
       if (16 * i + r >= A.M) continue;  // no row of this (i, r) is live (wave-uniform)
+      if (r % rstep != rfirst) continue;
       const int m = 16 * i + 4 * hh + r;
       const bool row_ok = m < A.M;
       float v[4];
@@ -165,8 +196,9 @@ __device__ __forceinline__ void block_select(const f32x4 (&acc)[MT][4], const Co
       for (int t = 0; t < 4; ++t) {
         const int n = b * 64 + 16 * t + nn;
         const bool ok = row_ok && n < A.N;
-        v[t] = ok ? acc[i][t][r] : NEG_INF;
-        if (A.coarse_out && ok) A.coarse_out[(size_t)m * A.N + n] = acc[i][t][r];
+        const float c = value(i, r, t);
+        v[t] = ok ? c : NEG_INF;
+        if (A.coarse_out && ok) A.coarse_out[(size_t)m * A.N + n] = c;
       }
       float kv[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
       int ki[4] = {-1, -1, -1, -1};
@@ -217,14 +249,14 @@ __device__ __forceinline__ void block_select(const f32x4 (&acc)[MT][4], const Co
   }
 }
 
-// Convert 8 natural-order bf16 x values into the decode order {0,2,1,3,4,6,5,7}
-// and return their fp32 sum.
+// Convert 8 natural-order bf16 x values into the decode order {0,2,1,3,4,6,5,7},
+// scaled by 2^64, and return the fp32 sum of the unscaled values.
 __device__ __forceinline__ u32x4 permute_x(const u32x4 v, float& sum) {
   u32x4 o;
-  o[0] = (v[0] & 0xFFFFu) | (v[1] << 16);
-  o[1] = (v[0] >> 16) | (v[1] & 0xFFFF0000u);
-  o[2] = (v[2] & 0xFFFFu) | (v[3] << 16);
-  o[3] = (v[2] >> 16) | (v[3] & 0xFFFF0000u);
+  o[0] = scale_x_pair((v[0] & 0xFFFFu) | (v[1] << 16));
+  o[1] = scale_x_pair((v[0] >> 16) | (v[1] & 0xFFFF0000u));
+  o[2] = scale_x_pair((v[2] & 0xFFFFu) | (v[3] << 16));
+  o[3] = scale_x_pair((v[2] >> 16) | (v[3] & 0xFFFF0000u));
   sum = lo_bf16(v[0]) + hi_bf16(v[0]) + lo_bf16(v[1]) + hi_bf16(v[1]) + lo_bf16(v[2]) +
         hi_bf16(v[2]) + lo_bf16(v[3]) + hi_bf16(v[3]);
   return o;
@@ -242,38 +274,69 @@ __device__ __forceinline__ float row16_sum(float s) {
 // ---------------------------------------------------------------------------
 // Coarse kernel, x resident in LDS (M <= 8 and the whole x fits).
 //
-// Workgroup = 4 waves (8 for 8 rows), one 64-column block each.  It stages all of
-// x once (MP rows, MP = the next power of two >= M; lanes whose A row nn >= MP
-// read row nn & (MP-1), whose results are never used) with the group sums X,
-// then every wave streams its block with no further barrier: the codes and
-// scale pairs of byte group G+1 are loaded while byte group G is computed.
-// LDS: fragments [group it = 4G + q][f][MP] (16 bytes each), then X[it][MP].
-template <int MP>
-constexpr int res_waves() { return MP >= 8 ? 8 : 4; }  // 8 rows: 83 KB of LDS, one workgroup per CU
+// 4/NT waves share a 64-column block, each computing NT of its four 16-column
+// tiles, so a wave needs few registers and many waves fit per SIMD.  The
+// workgroup stages all of x once (MP rows, MP = the next power of two >= M;
+// lanes whose A row nn >= MP read row nn & (MP-1), whose results are never
+// used) with the group sums X.  Then every wave streams its tiles with no
+// further barrier, keeping the codes and scale pairs of the next D-1 byte
+// groups in flight in a ring of D register sets.  At the end the tiles of a
+// block meet in LDS and the block's top-kcand is selected.
+// LDS: x fragments [group it = 4G + q][f][MP] (16 bytes each), X[it][MP], then
+// the block scores [block][16 rows][64 columns].
+constexpr int kResDepth = 2;   // byte groups held in registers (D-1 in flight)
+
+// Tiles per wave: two for 1-2 rows (more waves to hide latency), four for 4-8
+// rows, where the per-row scale updates make a wave's share of work larger.
+constexpr int res_nt(int MP) { return MP <= 2 ? 2 : 4; }
 
 template <int MP>
-__global__ __launch_bounds__(64 * res_waves<MP>()) __attribute__((amdgpu_waves_per_eu(2)))
+constexpr int res_waves() { return 8; }
+
+template <int MP>
+__global__ __launch_bounds__(64 * res_waves<MP>())
 void coarse_resident_kernel(CoarseArgs A) {
   constexpr int kResWaves = res_waves<MP>();
   constexpr int kResThreads = 64 * kResWaves;
+  constexpr int NT = res_nt(MP), D = kResDepth;
+  constexpr int kWavesPerBlock = 4 / NT;
+  constexpr int kBlocks = kResWaves / kWavesPerBlock;
   constexpr int MR = MP < 4 ? MP : 4;  // accumulator rows r that can hold a live row
   extern __shared__ __align__(16) unsigned char smem[];
   const int NG4 = A.K >> 9, Q4 = A.K >> 2, NG = A.K >> 7;
-  u32x4* xs = reinterpret_cast<u32x4*>(smem);                          // [NG][16][MP]
-  float* Xs = reinterpret_cast<float*>(smem + (size_t)NG * 16 * MP * 16);  // [NG][MP]
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);                               // [NG][16][MP]
+  float* Xs = reinterpret_cast<float*>(smem + (size_t)NG * 16 * MP * 16);       // [NG][MP]
+  float* sel = Xs + (size_t)NG * MP;                                           // [kBlocks][16][64]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 4, nn = lane & 15;
-  const int b = blockIdx.x * kResWaves + wave;
+  const int lblk = wave / kWavesPerBlock, part = wave % kWavesPerBlock;
+  const int b = blockIdx.x * kBlocks + lblk;
   const bool blk_ok = b < A.nblk;
-  uint32_t one;
-  asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(one));
+
+  // A wave past the last block reads block 0 (valid memory) and writes nothing.
+  const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512 + NT * part * 64;
+  const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64 + NT * part * 16;
+  auto load_codes = [&](int G, u32x4 (&raw)[2][NT], u32x4 (&sz)[NT]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) raw[h][t] = tp[((G * 2 + h) * 4 + t) * 64 + lane];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sz[t] = pp[(G * 4 + t) * 16 + nn];
+  };
+
+  // the first byte groups' codes are requested before x is staged
+  u32x4 rw[D][2][NT], sw[D][NT];   // ring: set (G mod D) holds byte group G
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d)
+    if (d < NG4) load_codes(d, rw[d], sw[d]);
 
   // stage x: piece i = (m, k0 = 8p) for all MP rows (zero rows past M).  Loads
   // are issued kBatch at a time from clamped (always valid) addresses.
   {
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 4;
     const int per_row = A.K >> 3;
     const int total = MP * per_row;
     for (int base = 0; base < total; base += kResThreads * kBatch) {
@@ -303,46 +366,48 @@ void coarse_resident_kernel(CoarseArgs A) {
     }
   }
   __syncthreads();
-  (void)NG;
 
-  const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
-  const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64;
-  auto load_codes = [&](int G, u32x4 (&raw)[2][4], u32x4 (&sz)[4]) {
+  f32x4 acc[1][NT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) raw[h][t] = tp[((G * 2 + h) * 4 + t) * 64 + lane];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) sz[t] = pp[(G * 4 + t) * 16 + nn];
-  };
+  for (int t = 0; t < NT; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  f32x4 acc[1][4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 raw[2][4], sz[4];
-  load_codes(0, raw, sz);
   const int arow = nn & (MP - 1);
-  for (int G = 0; G < NG4; ++G) {
-    u32x4 rawn[2][4], szn[4];
-    if (G + 1 < NG4) load_codes(G + 1, rawn, szn);
+  auto byte_group = [&](int G, const u32x4 (&raw)[2][NT], const u32x4 (&sz)[NT]) {
     const u32x4* xb = xs + (size_t)(G * 64 + hh) * MP + arow;
     const float* Xg = Xs + G * 4 * MP + ((4 * hh) & (MP - 1));
-    coarse_group<1, MR, 0>(acc, raw, sz, xb, MP, Xg, 0, one);
-    coarse_group<1, MR, 1>(acc, raw, sz, xb + 16 * MP, MP, Xg + MP, 0, one);
-    coarse_group<1, MR, 2>(acc, raw, sz, xb + 32 * MP, MP, Xg + 2 * MP, 0, one);
-    coarse_group<1, MR, 3>(acc, raw, sz, xb + 48 * MP, MP, Xg + 3 * MP, 0, one);
-    if (G + 1 < NG4) {
+    u32x4 raw8[2][NT];
+    shift_codes(raw, raw8);
+    // each group's scale update is issued after the next group's MFMAs, so it
+    // does not wait on results that were just issued
+    f32x4 c0[1][NT], c1[1][NT];
+    group_mma<1, 0, NT>(c0, raw, raw8, xb, MP);
+    group_mma<1, 1, NT>(c1, raw, raw8, xb + 16 * MP, MP);
+    group_scale<1, MR, 0, NT>(acc, c0, sz, Xg, 0);
+    group_mma<1, 2, NT>(c0, raw, raw8, xb + 32 * MP, MP);
+    group_scale<1, MR, 1, NT>(acc, c1, sz, Xg + MP, 0);
+    group_mma<1, 3, NT>(c1, raw, raw8, xb + 48 * MP, MP);
+    group_scale<1, MR, 2, NT>(acc, c0, sz, Xg + 2 * MP, 0);
+    group_scale<1, MR, 3, NT>(acc, c1, sz, Xg + 3 * MP, 0);
+  };
+  for (int G0 = 0; G0 < NG4; G0 += D) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) raw[h][t] = rawn[h][t];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) sz[t] = szn[t];
+    for (int d = 0; d < D; ++d) {
+      const int G = G0 + d;
+      if (G + D - 1 < NG4) load_codes(G + D - 1, rw[(d + D - 1) % D], sw[(d + D - 1) % D]);
+      if (G < NG4) byte_group(G, rw[d], sw[d]);
     }
   }
+
+  // the tiles of the block meet in LDS
+  float* bs = sel + (size_t)lblk * 16 * 64;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < MR; ++r) bs[(4 * hh + r) * 64 + 16 * (NT * part + t) + nn] = acc[0][t][r];
+  __syncthreads();
   if (!blk_ok) return;
-  block_select<1, MR>(acc, A, b, hh, nn);
+  block_select<1, MR>([&](int, int r, int t) { return bs[(4 * hh + r) * 64 + 16 * t + nn]; }, A, b, hh, nn,
+                      part, kWavesPerBlock);
 }
 
 // ---------------------------------------------------------------------------
@@ -367,8 +432,6 @@ void coarse_chunked_kernel(CoarseArgs A) {
   const int b = blockIdx.x * kWaves + wave;
   const bool blk_ok = b < A.nblk;
   const int NG4 = A.K >> 9, Q4 = A.K >> 2;
-  uint32_t one;
-  asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(one));
 
   // A wave past the last block reads block 0 (valid memory) and writes nothing.
   const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
@@ -435,14 +498,16 @@ void coarse_chunked_kernel(CoarseArgs A) {
   for (int G = 0; G < NG4; ++G) {
     u32x4 rawn[2][4], szn[4];
     if (G + 1 < NG4) load_codes(G + 1, rawn, szn);
+    u32x4 raw8[2][4];
+    shift_codes(raw, raw8);
 #pragma nounroll
     for (int q = 0; q < 4; ++q) {
       const int cur = q & 1;  // 4 groups per G, so the buffer parity is q's
       const bool has_next = (q < 3) || (G + 1 < NG4);
       u32x4 st[kMaxStage];
       if (has_next) stage_load(q < 3 ? G : G + 1, q < 3 ? q + 1 : 0, st);
-      coarse_group<MT, 4, -1>(acc, raw, sz, xs + cur * 16 * MP + hh * MP + nn, MP, Xs + cur * MP, hh,
-                              one, q);
+      coarse_group<MT, 4, -1, 4>(acc, raw, raw8, sz, xs + cur * 16 * MP + hh * MP + nn, MP, Xs + cur * MP,
+                              hh, q);
       if (has_next) stage_store(cur ^ 1, st);
       __syncthreads();
     }
@@ -456,7 +521,7 @@ void coarse_chunked_kernel(CoarseArgs A) {
     }
   }
   if (!blk_ok) return;
-  block_select<MT, 4>(acc, A, b, hh, nn);
+  block_select<MT, 4>([&](int i, int r, int t) { return acc[i][t][r]; }, A, b, hh, nn);
 }
 
 // ---------------------------------------------------------------------------
@@ -897,7 +962,9 @@ constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 
 size_t resident_lds_bytes(int K, int MP) {
   const size_t groups = (size_t)K / DH_GROUP;
-  return groups * 16 * MP * 16 + groups * MP * sizeof(float);
+  const size_t blocks = (size_t)res_waves<1>() * res_nt(MP) / 4;   // 4 / res_nt waves per block
+  static_assert(res_waves<1>() == res_waves<8>(), "LDS sizing assumes one workgroup shape");
+  return groups * 16 * MP * 16 + groups * MP * sizeof(float) + blocks * 16 * 64 * sizeof(float);
 }
 
 template <int MP>
@@ -911,7 +978,8 @@ hipError_t launch_resident(const CoarseArgs& A, hipStream_t s) {
     attr_set = true;
   }
   constexpr int waves = res_waves<MP>();
-  dim3 grid((A.nblk + waves - 1) / waves);
+  constexpr int blocks = waves * res_nt(MP) / 4;   // 4 / res_nt waves per 64-column block
+  dim3 grid((A.nblk + blocks - 1) / blocks);
   hipLaunchKernelGGL(coarse_resident_kernel<MP>, grid, dim3(64 * waves), lds, s, A);
   return hipGetLastError();
 }
