@@ -13,7 +13,8 @@ Prints one JSON line:
                the page's "0.167 GiB") / measured time per call
   ms_per_step  time per call
   roofline     the coarse kernel: algorithmic bytes per launch / its average
-               duration (HIP events on the launch stream) vs 8 TB/s
+               duration (HIP events set by the kernel's own dispatch on the
+               launch stream) vs 8 TB/s
   cpu_baseline the CPU oracle timed on this host on one full call at M = 1
   extra        per-M (1, 8, 72) times, the warm (cache-resident) figure and
                a device-copy bandwidth reference
@@ -91,27 +92,13 @@ class Rig:
 
     def buffers(self, m):
         if m not in self.out:
-            t, d = self.torch, self.dev
-            self.out[m] = dict(
-                cv=t.empty((m, NBLK * KCAND), dtype=t.float32, device=d),
-                ci=t.empty((m, NBLK * KCAND), dtype=t.int32, device=d),
-                ri=t.empty((m, R), dtype=t.int32, device=d),
-                rv=t.empty((m, R), dtype=t.float32, device=d),
-                oi=t.empty((m,), dtype=t.int32, device=d),
-                ov=t.empty((m,), dtype=t.float32, device=d))
+            self.out[m] = self.B.forward_buffers(m, N, KCAND, R, self.dev)
         return self.out[m]
 
     def step(self, m, head, ev=None):
-        B, b = self.B, self.buffers(m)
-        x = self.x[:m]
-        if ev is not None:
-            ev[0].record()
-        s = self.stream
-        B.draft_head_coarse(x, head.tiled, head.pairs, N, KCAND, b["cv"], b["ci"], stream=s)
-        if ev is not None:
-            ev[1].record()
-        B.draft_head_rerank(x, head.w, b["cv"], b["ci"], R, b["ri"], b["rv"], N=N, stream=s)
-        B.draft_head_argmax(b["ri"], b["rv"], b["oi"], b["ov"], stream=s)
+        """One full call through the library's one-call entry point; `ev` takes
+        the coarse kernel's own dispatch timestamps."""
+        head(self.x[:m], stream=self.stream, out=self.buffers(m), coarse_events=ev)
 
     def timed(self, m, steps, warmup, copies=None):
         """(seconds per call, seconds per coarse launch) over `steps` calls."""
@@ -122,6 +109,9 @@ class Rig:
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
+        for a, b in evs:      # torch creates an event on its first record
+            a.record()
+            b.record()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()

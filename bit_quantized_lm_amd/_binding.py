@@ -58,6 +58,9 @@ def load_library() -> ctypes.CDLL:
     lib.draft_head_tile.argtypes = [P, P, P, i64, i64, P, P]
     lib.draft_head_coarse.restype = i32
     lib.draft_head_coarse.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P]
+    lib.draft_head_forward.restype = i32
+    lib.draft_head_forward.argtypes = [P, i32, i32, i32, P, P, P, i64, i32, i32, P, P, P, P, P, P, P, P,
+                                       P, P]
     lib.draft_head_rerank.restype = i32
     lib.draft_head_rerank.argtypes = [P, P, i64, i32, i32, i32, P, P, i32, i32, P, P, P]
     lib.draft_head_argmax.restype = i32
@@ -203,12 +206,52 @@ def draft_head_argmax(rr_id, rr_val, out_id=None, out_val=None, stream=None):
     return out_id, out_val
 
 
+def forward_buffers(M: int, N: int, kcand: int, R: int, device):
+    """Output tensors of one full call for M rows (what draft_head_forward fills)."""
+    import torch
+    ncand = ((N + BLOCK_N - 1) // BLOCK_N) * kcand
+    return {"cand_val": torch.empty((M, ncand), dtype=torch.float32, device=device),
+            "cand_id": torch.empty((M, ncand), dtype=torch.int32, device=device),
+            "rr_id": torch.empty((M, R), dtype=torch.int32, device=device),
+            "rr_val": torch.empty((M, R), dtype=torch.float32, device=device),
+            "out_id": torch.empty((M,), dtype=torch.int32, device=device),
+            "out_val": torch.empty((M,), dtype=torch.float32, device=device)}
+
+
+def _event(ev):
+    if ev is None:
+        return None
+    if ev.cuda_event == 0:
+        raise ValueError("record a timing event once (torch creates it lazily) before passing it")
+    return ev.cuda_event
+
+
+def draft_head_forward(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, out=None,
+                       coarse_out=None, stream=None, coarse_events=None):
+    """One full call (coarse -> rerank -> argmax) in one library call.
+
+    out: dict from forward_buffers (allocated when None); coarse_events: optional
+    (start, stop) torch.cuda.Event pair that takes the coarse kernel's own
+    dispatch timestamps.  Returns the dict of output tensors."""
+    lib = load_library()
+    M, K = x.shape
+    if out is None:
+        out = forward_buffers(M, N, kcand, R, x.device)
+    e0, e1 = (None, None) if coarse_events is None else (_event(coarse_events[0]), _event(coarse_events[1]))
+    _check(lib.draft_head_forward(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0), kcand,
+                                  R, _ptr(out["cand_val"]), _ptr(out["cand_id"]), _ptr(out["rr_id"]),
+                                  _ptr(out["rr_val"]), _ptr(out["out_id"]), _ptr(out["out_val"]),
+                                  _ptr(coarse_out), _stream(stream), e0, e1))
+    return out
+
+
 class DraftHead:
     """Device-resident head: the tiled 2-bit arrays plus the bf16 weight the rerank reads.
 
     from_weight() quantises on the host with the library, tiles, and uploads.
-    __call__(x) runs coarse -> rerank -> argmax on the current stream and
-    returns a dict of the device tensors of every step.
+    __call__(x) runs coarse -> rerank -> argmax on the current stream with one
+    library call and returns a dict of the device tensors of every step;
+    staged(x) does the same with one library call per step.
     """
 
     def __init__(self, tiled, pairs, w, N: int, K: int, kcand: int = 8, R: int = 32):
@@ -228,7 +271,12 @@ class DraftHead:
         t_w = torch.from_numpy(np.ascontiguousarray(w_bits).view(np.int16)).to(device)
         return cls(t_tiled, t_pairs, t_w, n, k, kcand, R)
 
-    def __call__(self, x, coarse_out=None, stream=None):
+    def __call__(self, x, coarse_out=None, stream=None, out=None, coarse_events=None):
+        return draft_head_forward(x, self.tiled, self.pairs, self.w, self.N, self.kcand, self.R, out=out,
+                                  coarse_out=coarse_out, stream=stream, coarse_events=coarse_events)
+
+    def staged(self, x, coarse_out=None, stream=None):
+        """The same call as three library calls (coarse, rerank, argmax)."""
         cv, ci = draft_head_coarse(x, self.tiled, self.pairs, self.N, self.kcand,
                                    coarse_out=coarse_out, stream=stream)
         rr_id, rr_val = draft_head_rerank(x, self.w, cv, ci, self.R, N=self.N, stream=stream)

@@ -7,6 +7,7 @@
 //   rerank_kernel   row top-R of the candidates (`bm.topk` + `bi.gather`), then the
 //                   exact fp32 dot of x with each one's bf16 row (`_rerank_exact`)
 //   argmax_kernel   best reranked candidate per row
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -968,7 +969,7 @@ size_t resident_lds_bytes(int K, int MP) {
 }
 
 template <int MP>
-hipError_t launch_resident(const CoarseArgs& A, hipStream_t s) {
+hipError_t launch_resident(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const size_t lds = resident_lds_bytes(A.K, MP);
   static bool attr_set = false;   // the attribute only ever grows to kMaxLds
   if (!attr_set) {
@@ -980,25 +981,21 @@ hipError_t launch_resident(const CoarseArgs& A, hipStream_t s) {
   constexpr int waves = res_waves<MP>();
   constexpr int blocks = waves * res_nt(MP) / 4;   // 4 / res_nt waves per 64-column block
   dim3 grid((A.nblk + blocks - 1) / blocks);
-  hipLaunchKernelGGL(coarse_resident_kernel<MP>, grid, dim3(64 * waves), lds, s, A);
+  hipExtLaunchKernelGGL(coarse_resident_kernel<MP>, grid, dim3(64 * waves), lds, s, e0, e1, 0, A);
   return hipGetLastError();
 }
 
 template <int MT>
-hipError_t launch_chunked(const CoarseArgs& A, hipStream_t s) {
+hipError_t launch_chunked(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid((A.nblk + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(coarse_chunked_kernel<MT>, grid, dim3(kThreads), 0, s, A);
+  hipExtLaunchKernelGGL(coarse_chunked_kernel<MT>, grid, dim3(kThreads), 0, s, e0, e1, 0, A);
   return hipGetLastError();
 }
 
 int resident_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
-}  // namespace
-
-extern "C" {
-
-int draft_head_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
-                      int kcand, float* cand_val, int32_t* cand_id, float* coarse_out, void* stream) {
+int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                    int kcand, const float* cand_val, const int32_t* cand_id) {
   if (!x || !tiled || !pairs || !cand_val || !cand_id)
     return dh::fail(DH_EINVAL, "coarse: null pointer");
   int rc = check_m(M);
@@ -1009,46 +1006,11 @@ int draft_head_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, 
     return dh::fail(DH_EUNSUP, "coarse: kcand must be in 1..%d (got %d)", DH_MAX_KCAND, kcand);
   if (!aligned16(x) || !aligned16(tiled) || !aligned16(pairs))
     return dh::fail(DH_EINVAL, "coarse: x, tiled and pairs must be 16-byte aligned");
-  const int nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
-  const int ncand = nblk * kcand;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
-               reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out};
-  hipError_t e = hipSuccess;
-  if (M <= 8 && resident_lds_bytes(K, resident_rows(M)) <= kMaxLds) {
-    switch (resident_rows(M)) {
-      case 1: e = launch_resident<1>(A, s); break;
-      case 2: e = launch_resident<2>(A, s); break;
-      case 4: e = launch_resident<4>(A, s); break;
-      default: e = launch_resident<8>(A, s); break;
-    }
-    if (e != hipSuccess) return dh::fail(DH_EHIP, "coarse_resident_kernel: %s", hipGetErrorString(e));
-    return dh::ok();
-  }
-  // Rows beyond one launch's 80 are handled by further launches over the
-  // same weights (only for M > 80).
-  for (int m0 = 0; m0 < M; m0 += 16 * kMaxMT) {
-    CoarseArgs B = A;
-    B.M = std::min(M - m0, 16 * kMaxMT);
-    B.x = A.x + (size_t)m0 * K;
-    B.cand_val = cand_val + (size_t)m0 * ncand;
-    B.cand_id = cand_id + (size_t)m0 * ncand;
-    B.coarse_out = coarse_out ? coarse_out + (size_t)m0 * N : nullptr;
-    switch ((B.M + 15) / 16) {
-      case 1: e = launch_chunked<1>(B, s); break;
-      case 2: e = launch_chunked<2>(B, s); break;
-      case 3: e = launch_chunked<3>(B, s); break;
-      case 4: e = launch_chunked<4>(B, s); break;
-      default: e = launch_chunked<5>(B, s); break;
-    }
-    if (e != hipSuccess) return dh::fail(DH_EHIP, "coarse_chunked_kernel: %s", hipGetErrorString(e));
-  }
-  return dh::ok();
+  return DH_OK;
 }
 
-int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N,
-                      const float* cand_val, const int32_t* cand_id, int ncand, int R,
-                      int32_t* rr_id, float* rr_val, void* stream) {
+int validate_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
+                    const int32_t* cand_id, int ncand, int R, const int32_t* rr_id, const float* rr_val) {
   if (!x || !w || !cand_val || !cand_id || !rr_id || !rr_val)
     return dh::fail(DH_EINVAL, "rerank: null pointer");
   int rc = check_m(M);
@@ -1062,21 +1024,118 @@ int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, i
     return dh::fail(DH_EUNSUP, "rerank: R must be in 1..min(ncand=%d, %d) (got %d)", ncand, DH_MAX_R, R);
   if (!aligned16(x) || !aligned16(w))
     return dh::fail(DH_EINVAL, "rerank: x and w must be 16-byte aligned");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return DH_OK;
+}
+
+int validate_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, const int32_t* out_id,
+                    const float* out_val) {
+  if (!rr_id || !rr_val || !out_id || !out_val) return dh::fail(DH_EINVAL, "argmax: null pointer");
+  int rc = check_m(M);
+  if (rc) return rc;
+  if (R < 1 || R > DH_MAX_R) return dh::fail(DH_EUNSUP, "argmax: R must be in 1..%d (got %d)", DH_MAX_R, R);
+  return DH_OK;
+}
+
+// Launches only; arguments were validated.
+int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, int kcand,
+                  float* cand_val, int32_t* cand_id, float* coarse_out, hipStream_t s, hipEvent_t ev0,
+                  hipEvent_t ev1) {
+  const int nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
+  const int ncand = nblk * kcand;
+  CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
+               reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out};
+  hipError_t e = hipSuccess;
+  if (M <= 8 && resident_lds_bytes(K, resident_rows(M)) <= kMaxLds) {
+    switch (resident_rows(M)) {
+      case 1: e = launch_resident<1>(A, s, ev0, ev1); break;
+      case 2: e = launch_resident<2>(A, s, ev0, ev1); break;
+      case 4: e = launch_resident<4>(A, s, ev0, ev1); break;
+      default: e = launch_resident<8>(A, s, ev0, ev1); break;
+    }
+    if (e != hipSuccess) return dh::fail(DH_EHIP, "coarse_resident_kernel: %s", hipGetErrorString(e));
+    return dh::ok();
+  }
+  // Rows beyond one launch's 80 are handled by further launches over the
+  // same weights (only for M > 80).
+  for (int m0 = 0; m0 < M; m0 += 16 * kMaxMT) {
+    CoarseArgs B = A;
+    B.M = std::min(M - m0, 16 * kMaxMT);
+    B.x = A.x + (size_t)m0 * K;
+    B.cand_val = cand_val + (size_t)m0 * ncand;
+    B.cand_id = cand_id + (size_t)m0 * ncand;
+    B.coarse_out = coarse_out ? coarse_out + (size_t)m0 * N : nullptr;
+    hipEvent_t b0 = m0 == 0 ? ev0 : nullptr;
+    hipEvent_t b1 = m0 + 16 * kMaxMT >= M ? ev1 : nullptr;
+    switch ((B.M + 15) / 16) {
+      case 1: e = launch_chunked<1>(B, s, b0, b1); break;
+      case 2: e = launch_chunked<2>(B, s, b0, b1); break;
+      case 3: e = launch_chunked<3>(B, s, b0, b1); break;
+      case 4: e = launch_chunked<4>(B, s, b0, b1); break;
+      default: e = launch_chunked<5>(B, s, b0, b1); break;
+    }
+    if (e != hipSuccess) return dh::fail(DH_EHIP, "coarse_chunked_kernel: %s", hipGetErrorString(e));
+  }
+  return dh::ok();
+}
+
+int launch_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
+                  const int32_t* cand_id, int ncand, int R, int32_t* rr_id, float* rr_val, hipStream_t s) {
   hipLaunchKernelGGL(rerank_kernel, dim3(M), dim3(kSelThreads), 0, s, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(w), ldw, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
   return launch_error("rerank_kernel");
 }
 
-int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, int32_t* out_id,
-                      float* out_val, void* stream) {
-  if (!rr_id || !rr_val || !out_id || !out_val) return dh::fail(DH_EINVAL, "argmax: null pointer");
-  int rc = check_m(M);
-  if (rc) return rc;
-  if (R < 1 || R > DH_MAX_R) return dh::fail(DH_EUNSUP, "argmax: R must be in 1..%d (got %d)", DH_MAX_R, R);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+int launch_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, int32_t* out_id, float* out_val,
+                  hipStream_t s) {
   hipLaunchKernelGGL(argmax_kernel, dim3((M + 3) / 4), dim3(256), 0, s, rr_id, rr_val, M, R, out_id, out_val);
   return launch_error("argmax_kernel");
+}
+
+hipStream_t as_stream(void* p) { return reinterpret_cast<hipStream_t>(p); }
+
+}  // namespace
+
+extern "C" {
+
+int draft_head_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                      int kcand, float* cand_val, int32_t* cand_id, float* coarse_out, void* stream) {
+  int rc = validate_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id);
+  if (rc) return rc;
+  return launch_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, as_stream(stream),
+                       nullptr, nullptr);
+}
+
+int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N,
+                      const float* cand_val, const int32_t* cand_id, int ncand, int R,
+                      int32_t* rr_id, float* rr_val, void* stream) {
+  int rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
+  if (rc) return rc;
+  return launch_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, as_stream(stream));
+}
+
+int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, int32_t* out_id,
+                      float* out_val, void* stream) {
+  int rc = validate_argmax(rr_id, rr_val, M, R, out_id, out_val);
+  if (rc) return rc;
+  return launch_argmax(rr_id, rr_val, M, R, out_id, out_val, as_stream(stream));
+}
+
+int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                       const void* w, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
+                       int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
+                       void* stream, void* coarse_start_event, void* coarse_stop_event) {
+  const int ncand = (N > 0 && kcand > 0) ? ((N + DH_BLOCK_N - 1) / DH_BLOCK_N) * kcand : 0;
+  int rc = validate_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id);
+  if (rc) return rc;
+  if ((rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val))) return rc;
+  if ((rc = validate_argmax(rr_id, rr_val, M, R, out_id, out_val))) return rc;
+  hipStream_t s = as_stream(stream);
+  if ((rc = launch_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, s,
+                          reinterpret_cast<hipEvent_t>(coarse_start_event),
+                          reinterpret_cast<hipEvent_t>(coarse_stop_event))))
+    return rc;
+  if ((rc = launch_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, s))) return rc;
+  return launch_argmax(rr_id, rr_val, M, R, out_id, out_val, s);
 }
 
 }  // extern "C"

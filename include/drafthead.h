@@ -11,7 +11,8 @@
  *
  * Call sequence:
  *   load time (host):  draft_head_quantize_pack -> draft_head_tile -> copy to device
- *   per call (device): draft_head_coarse -> draft_head_rerank -> draft_head_argmax
+ *   per call (device): draft_head_coarse -> draft_head_rerank -> draft_head_argmax,
+ *                      or the three in one host call: draft_head_forward
  *
  * Conventions for every function:
  *   - Return value: DH_OK (0) or a negative DH_E* code; never throws.  The
@@ -148,6 +149,27 @@ int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, i
  */
 int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R,
                       int32_t* out_id, float* out_val, void* stream);
+
+/*
+ * DEVICE.  One full call of the head: draft_head_coarse, draft_head_rerank
+ * (ncand = NBLK*kcand) and draft_head_argmax enqueued back to back on
+ * `stream` with one host call (the page's `_draft_head_int2` from x to the
+ * written-back candidates, plus the final argmax).  Every argument is
+ * validated before the first launch; the arguments mean what they mean in
+ * the three calls above.
+ *   coarse_start_event, coarse_stop_event  optional hipEvent_t (as void*,
+ *              created by the caller, NULL = none): they take the start and
+ *              end timestamps of the coarse kernel's own dispatch
+ *              (hipExtLaunchKernel), so hipEventElapsedTime gives that
+ *              kernel's duration; where M > 80 needs several coarse
+ *              launches, the first one's start and the last one's end.
+ * Errors: as the three calls.
+ */
+int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
+                       const uint32_t* pairs, const void* w, int64_t ldw, int kcand, int R,
+                       float* cand_val, int32_t* cand_id, int32_t* rr_id, float* rr_val,
+                       int32_t* out_id, float* out_val, float* coarse_out, void* stream,
+                       void* coarse_start_event, void* coarse_stop_event);
 
 #ifdef __cplusplus
 }

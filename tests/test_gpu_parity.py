@@ -210,3 +210,21 @@ def test_recall_stress_full_shape(dev, full):
         del head
     _log(f"recall stress: argmax misses vs planted winner: KCAND=8 {misses[8]}/32, KCAND=1 {misses[1]}/32")
     assert misses[8] == 0
+
+
+def test_forward_matches_staged_calls(dev):
+    """The one-call entry point equals the three separate calls, and sets the
+    coarse kernel's timing events."""
+    n, k, m, kc, r = 3000, 1024, 5, 8, 32
+    w = workload.gen_weight(n, k, seed=93)
+    x = _to_dev(workload.gen_x(m, k, seed=94), dev)
+    head = B.DraftHead.from_weight(w, kcand=kc, R=r, device=dev)
+    a = head.staged(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    b = head(x, coarse_events=(e0, e1))
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+    assert e0.elapsed_time(e1) > 0

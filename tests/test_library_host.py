@@ -25,7 +25,7 @@ def test_library_exports_every_header_symbol(lib):
     names = B.header_functions()
     assert set(names) == {"draft_head_last_error", "draft_head_sizes", "draft_head_quantize_pack",
                           "draft_head_tile", "draft_head_coarse", "draft_head_rerank",
-                          "draft_head_argmax"}
+                          "draft_head_argmax", "draft_head_forward"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -136,8 +136,13 @@ def test_quantize_pack_validation(lib):
     _err(lib, lib.draft_head_tile(p, p, p, 4, 500, p, p), B.DH_ESHAPE)
 
 
-def test_coarse_validation(lib):
-    f = lambda *a: lib.draft_head_coarse(*a)  # noqa: E731
+@pytest.mark.parametrize("via", ["coarse", "forward"])
+def test_coarse_validation(lib, via):
+    if via == "forward":    # the same checks, before any launch, in the one-call entry point
+        f = lambda x, M, K, N, t, p, kc, cv, ci, co, s: lib.draft_head_forward(  # noqa: E731
+            x, M, K, N, t, p, FAKE, K, kc, 8, cv, ci, FAKE, FAKE, FAKE, FAKE, co, s, None, None)
+    else:
+        f = lambda *a: lib.draft_head_coarse(*a)  # noqa: E731
     ok = dict(x=FAKE, M=1, K=512, N=64, tiled=FAKE, pairs=FAKE, kc=8, cv=FAKE, ci=FAKE, co=None, s=None)
 
     def call(**kw):
@@ -195,3 +200,25 @@ def test_argmax_validation(lib):
 def test_python_errors_are_value_errors(lib):
     with pytest.raises(ValueError):
         B.draft_head_quantize_pack(np.zeros((2, 300), np.uint16))
+
+
+def test_forward_validation(lib):
+    ok = dict(x=FAKE, M=2, K=512, N=640, t=FAKE, p=FAKE, w=FAKE, ldw=512, kc=8, R=32, cv=FAKE, ci=FAKE,
+              ri=FAKE, rv=FAKE, oi=FAKE, ov=FAKE, co=None, s=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.draft_head_forward(a["x"], a["M"], a["K"], a["N"], a["t"], a["p"], a["w"], a["ldw"],
+                                      a["kc"], a["R"], a["cv"], a["ci"], a["ri"], a["rv"], a["oi"],
+                                      a["ov"], a["co"], a["s"], None, None)
+    _err(lib, call(w=None), B.DH_EINVAL)
+    _err(lib, call(ri=None), B.DH_EINVAL)
+    _err(lib, call(oi=None), B.DH_EINVAL)
+    _err(lib, call(ov=None), B.DH_EINVAL)
+    _err(lib, call(ldw=256), B.DH_EINVAL)
+    _err(lib, call(R=81), B.DH_EUNSUP)          # ncand = 10 blocks * 8
+    _err(lib, call(N=64, R=9), B.DH_EUNSUP)     # ncand = 8
+    _err(lib, call(R=0), B.DH_EUNSUP)
+    _err(lib, call(M=129), B.DH_EUNSUP)
+    _err(lib, call(w=MIS), B.DH_EINVAL)
