@@ -905,6 +905,276 @@ __global__ __launch_bounds__(kSelThreads) void rerank_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rerank, block-maximum path.  It relies on the candidate arrays being the
+// ones draft_head_coarse writes: block b owns slots b*kcand .. b*kcand+kcand-1
+// in (value desc, column asc) order, so slot b*kcand holds the block maximum,
+// and among equal values slot order is column order.  Keys built from
+// (value, ~slot) therefore order the candidates exactly as (value, ~id) does.
+//   1. Wave 0 reads the nblk block maxima (lane l: blocks l, l+64, ...) and
+//      picks a threshold T that at least R of them reach: the R-th largest of
+//      every lane's two largest maxima (a bitonic sort of 128 keys), or, if
+//      that lets more than DH_MAX_R / kcand blocks through, the exact R-th
+//      largest maximum by radix select.  At least R distinct keys are >= T,
+//      so every one of the row's R best candidates is >= T and lies in a
+//      block whose maximum is >= T.
+//   2. Wave 0 tests the kcand candidates of each such block against T; the
+//      survivors (every key >= T: at least R) are sorted, and the first R are
+//      the row top-R.
+//   Meanwhile waves 1.. stage the x row in LDS.
+//   3. Exact logits: each wave takes kFastRows selected rows of W at once, all
+//      their loads in flight before any is used; with kArgmax the workgroup
+//      then writes the final token as argmax_kernel would.
+constexpr int kFastThreads = 512;
+constexpr int kFastWaves = kFastThreads / 64;
+constexpr int kFastNV = 32;        // block maxima per lane of wave 0: nblk <= 2048
+constexpr int kFastRows = 4;       // rows of W per wave in flight
+constexpr int kSurvBatch = 4;      // survivor loads per lane in flight
+
+struct FastShared {
+  unsigned int hist[256];
+  int qual[DH_MAX_R];
+  unsigned long long keys[DH_MAX_R];
+  float vals[DH_MAX_R];
+  int ns;
+};
+
+__device__ __forceinline__ unsigned long long slot_key(float v, int slot) {
+  if (v == -__builtin_inff()) return 0ull;   // padding slot
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)slot);
+}
+
+__device__ __forceinline__ int lane_prefix(unsigned long long bal) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+// Sorts keys[0..ns) descending (ns <= DH_MAX_R); called by the whole workgroup.
+// Wave 0 alone with a shuffle bitonic network when ns <= 64, else an LDS
+// bitonic network over the next power of two.  Ends with a barrier.
+template <int NT>
+__device__ void sort_desc(unsigned long long* keys, int ns) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (ns <= 64) {
+    if (tid < 64) {
+      unsigned long long v = lane < ns ? keys[lane] : 0ull;
+      for (int size = 2; size <= 64; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          const unsigned long long o = __shfl_xor(v, stride, 64);
+          const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
+          v = keep_max ? umax64(v, o) : umin64(v, o);
+        }
+      if (lane < ns) keys[lane] = v;
+    }
+    __syncthreads();
+    return;
+  }
+  int P = 1;
+  while (P < ns) P <<= 1;
+  for (int i = ns + tid; i < P; i += NT) keys[i] = 0ull;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P; i += NT) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;
+          const unsigned long long a = keys[i], c = keys[j];
+          if (desc ? (a < c) : (a > c)) {
+            keys[i] = c;
+            keys[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// A threshold for the k-th largest (k <= 128) of the keys the wave holds: the
+// k-th largest of the union of every lane's two largest keys, found with a
+// 128-element bitonic sort (two keys per lane, shuffles only).  At least k
+// keys are >= the result (it is the k-th of a subset), usually only a few more.
+template <int NV>
+__device__ unsigned long long wave_top2_threshold(const unsigned long long (&v)[NV], int k) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long a = 0ull, b = 0ull;   // a >= b: the lane's two largest
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const unsigned long long key = v[j];
+    b = umax64(b, umin64(a, key));
+    a = umax64(a, key);
+  }
+  unsigned long long e[2] = {a, b};   // element i = 64 * r + lane
+  for (int size = 2; size <= 128; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride == 64) {   // partners in the two registers of one lane; size == 128: descending
+        const unsigned long long hi = umax64(e[0], e[1]), lo = umin64(e[0], e[1]);
+        e[0] = hi;
+        e[1] = lo;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int i = 64 * r + lane;
+          const unsigned long long o = __shfl_xor(e[r], stride, 64);
+          const bool keep_max = ((i & stride) == 0) == ((i & size) == 0);
+          e[r] = keep_max ? umax64(e[r], o) : umin64(e[r], o);
+        }
+      }
+    }
+  }
+  const int r = (k - 1) >> 6, l = (k - 1) & 63;
+  return __shfl(r ? e[1] : e[0], l, 64);
+}
+
+template <bool kArgmax>
+__global__ __launch_bounds__(kFastThreads) void rerank_fast_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t ldw, int K, int N,
+    const float* __restrict__ cand_val, const int32_t* __restrict__ cand_id, int nblk, int kcand, int R,
+    int32_t* __restrict__ rr_id, float* __restrict__ rr_val, int32_t* __restrict__ out_id,
+    float* __restrict__ out_val) {
+  extern __shared__ __align__(16) unsigned char fast_dyn[];   // the x row, K bf16
+  __shared__ FastShared sh;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(fast_dyn);
+  const int m = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ncand = nblk * kcand;
+  const float* cv = cand_val + (size_t)m * ncand;
+  const int32_t* ci = cand_id + (size_t)m * ncand;
+  const uint16_t* xr = x + (size_t)m * K;
+
+  if (wave == 0) {
+    // 1. T = the R-th largest block maximum
+    float mv[kFastNV];
+#pragma unroll
+    for (int j = 0; j < kFastNV; ++j) mv[j] = cv[min(lane + 64 * j, nblk - 1) * kcand];   // clamped loads
+    unsigned long long mk[kFastNV];
+#pragma unroll
+    for (int j = 0; j < kFastNV; ++j) {
+      const int b = lane + 64 * j;
+      mk[j] = b < nblk ? slot_key(mv[j], b * kcand) : 0ull;
+    }
+    // a quick threshold first; the exact R-th largest block maximum when the
+    // quick one lets too many blocks through for the survivor buffer
+    unsigned long long T = R <= 128 ? wave_top2_threshold(mk, R) : 0ull;
+    int nq = 0;
+    if (T) {
+#pragma unroll
+      for (int j = 0; j < kFastNV; ++j) nq += __popcll(__ballot(mk[j] != 0ull && mk[j] >= T));
+    }
+    if (!T || nq * kcand > DH_MAX_R) T = wave_kth_largest(mk, R, sh.hist);
+    // the blocks whose maximum is >= T (at least R), in block order
+    nq = 0;
+#pragma unroll
+    for (int j = 0; j < kFastNV; ++j) {
+      const bool q = mk[j] != 0ull && mk[j] >= T;
+      const unsigned long long bal = __ballot(q);
+      if (q) sh.qual[nq + lane_prefix(bal)] = lane + 64 * j;
+      nq += __popcll(bal);
+    }
+    // 2. survivors: the candidates >= T of those blocks
+    const int items = nq * kcand;
+    int ns = 0;
+    for (int i0 = 0; i0 < items; i0 += 64 * kSurvBatch) {
+      float v[kSurvBatch];
+      int id[kSurvBatch], slot[kSurvBatch];
+#pragma unroll
+      for (int j = 0; j < kSurvBatch; ++j) {   // clamped loads
+        const int i = min(i0 + 64 * j + lane, items - 1);
+        slot[j] = sh.qual[i / kcand] * kcand + i % kcand;
+        v[j] = cv[slot[j]];
+        id[j] = ci[slot[j]];
+      }
+#pragma unroll
+      for (int j = 0; j < kSurvBatch; ++j) {
+        const bool in = i0 + 64 * j + lane < items;
+        const unsigned long long k = in ? slot_key(v[j], slot[j]) : 0ull;
+        const bool keep = k != 0ull && k >= T && id[j] >= 0 && id[j] < N;
+        const unsigned long long bal = __ballot(keep);
+        if (keep) sh.keys[ns + lane_prefix(bal)] = cand_key(v[j], id[j], N);
+        ns += __popcll(bal);
+      }
+    }
+    if (lane == 0) sh.ns = ns;
+  } else {
+    for (int i = tid - 64; i < K / 8; i += kFastThreads - 64)
+      reinterpret_cast<u32x4*>(xs)[i] = reinterpret_cast<const u32x4*>(xr)[i];
+  }
+  __syncthreads();
+  const int ns = sh.ns;   // R <= ns <= R * kcand <= DH_MAX_R
+  sort_desc<kFastThreads>(sh.keys, ns);
+  for (int r = tid; r < R; r += kFastThreads) rr_id[(size_t)m * R + r] = (int32_t)key_id(sh.keys[r]);
+
+  // 3. exact logits, kFastRows rows per wave at a time
+  constexpr int kDotUnroll = 10;
+  for (int r0 = wave * kFastRows; r0 < R; r0 += kFastWaves * kFastRows) {
+    const uint16_t* wr[kFastRows];
+#pragma unroll
+    for (int t = 0; t < kFastRows; ++t) wr[t] = w + (size_t)key_id(sh.keys[min(r0 + t, R - 1)]) * ldw;
+    float s0[kFastRows], s1[kFastRows];
+#pragma unroll
+    for (int t = 0; t < kFastRows; ++t) s0[t] = s1[t] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += 512 * kDotUnroll) {
+      u32x4 wv[kFastRows][kDotUnroll];
+#pragma unroll
+      for (int j = 0; j < kDotUnroll; ++j)
+#pragma unroll
+        for (int t = 0; t < kFastRows; ++t)   // clamped, unconditional loads
+          wv[t][j] = *reinterpret_cast<const u32x4*>(wr[t] + min(k0 + 512 * j + lane * 8, K - 8));
+#pragma unroll
+      for (int j = 0; j < kDotUnroll; ++j) {
+        const int k = k0 + 512 * j + lane * 8;
+        if (k < K) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + k);
+#pragma unroll
+          for (int t = 0; t < kFastRows; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              s0[t] = __builtin_fmaf(lo_bf16(xv[c]), lo_bf16(wv[t][j][c]), s0[t]);
+              s1[t] = __builtin_fmaf(hi_bf16(xv[c]), hi_bf16(wv[t][j][c]), s1[t]);
+            }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kFastRows; ++t) {
+      float sum = s0[t] + s1[t];
+      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+      if (lane == 0 && r0 + t < R) {
+        rr_val[(size_t)m * R + r0 + t] = sum;
+        sh.vals[r0 + t] = sum;
+      }
+    }
+  }
+  if constexpr (kArgmax) {
+    __syncthreads();
+    if (wave == 0) {
+      float bv = -__builtin_inff();
+      int bi = -1;
+      for (int r = lane; r < R; r += 64) {
+        const int id = (int)key_id(sh.keys[r]);
+        const float v = sh.vals[r];
+        if (bi < 0 || v > bv || (v == bv && id < bi)) {
+          bv = v;
+          bi = id;
+        }
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (lane == 0) {
+        out_id[m] = bi;
+        out_val[m] = bv;
+      }
+    }
+  }
+}
+
 // Final token: one wave per row; largest value, ties to the lower id, id -1 skipped.
 __global__ __launch_bounds__(256) void argmax_kernel(const int32_t* __restrict__ rr_id,
                                                      const float* __restrict__ rr_val, int M, int R,
@@ -1078,8 +1348,43 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
   return dh::ok();
 }
 
+// The block-maximum rerank applies when the candidates are NBLK blocks of
+// kcand slots, there are more blocks than R, wave 0 can hold every block
+// maximum, and the R blocks' slots fit the survivor buffer.
+bool fast_rerank(int N, int ncand, int R, int& nblk, int& kcand) {
+  nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
+  if (ncand % nblk) return false;
+  kcand = ncand / nblk;
+  return kcand >= 1 && kcand <= DH_MAX_KCAND && nblk > R && nblk <= 64 * kFastNV &&
+         (int64_t)R * kcand <= DH_MAX_R;
+}
+
+template <bool kArgmax>
+hipError_t launch_fast(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
+                       const int32_t* cand_id, int nblk, int kcand, int R, int32_t* rr_id, float* rr_val,
+                       int32_t* out_id, float* out_val, hipStream_t s) {
+  static bool attr_set = false;   // the x row: up to DH_MAX_K bf16 = 128 KiB
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rerank_fast_kernel<kArgmax>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, DH_MAX_K * 2);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(rerank_fast_kernel<kArgmax>, dim3(M), dim3(kFastThreads), (size_t)K * 2, s,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), ldw, K, N, cand_val,
+                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val);
+  return hipGetLastError();
+}
+
 int launch_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
                   const int32_t* cand_id, int ncand, int R, int32_t* rr_id, float* rr_val, hipStream_t s) {
+  int nblk, kcand;
+  if (fast_rerank(N, ncand, R, nblk, kcand)) {
+    hipError_t e = launch_fast<false>(x, w, ldw, M, K, N, cand_val, cand_id, nblk, kcand, R, rr_id, rr_val,
+                                      nullptr, nullptr, s);
+    if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_fast_kernel: %s", hipGetErrorString(e));
+    return dh::ok();
+  }
   hipLaunchKernelGGL(rerank_kernel, dim3(M), dim3(kSelThreads), 0, s, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(w), ldw, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
   return launch_error("rerank_kernel");
@@ -1134,6 +1439,13 @@ int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
                           reinterpret_cast<hipEvent_t>(coarse_start_event),
                           reinterpret_cast<hipEvent_t>(coarse_stop_event))))
     return rc;
+  int nblk, kc;
+  if (fast_rerank(N, ncand, R, nblk, kc)) {   // rerank and argmax in one kernel
+    hipError_t e = launch_fast<true>(x, w, ldw, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val, out_id,
+                                     out_val, s);
+    if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_fast_kernel: %s", hipGetErrorString(e));
+    return dh::ok();
+  }
   if ((rc = launch_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, s))) return rc;
   return launch_argmax(rr_id, rr_val, M, R, out_id, out_val, s);
 }

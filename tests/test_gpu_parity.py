@@ -80,6 +80,14 @@ CASES = [
     (4, 512, 70, 64, 100),     # fewer valid candidates than R: padded rr
     (7, 1536, 3000, 16, 256),
     (1, 5120, 1000, 8, 32),
+    # block-maximum rerank: survivors > 64 (LDS sort), kcand * R at the buffer
+    # limit, ragged last block with padding slots, 2048 blocks (the limit) and
+    # one more block (general path)
+    (2, 512, 70000, 8, 100),
+    (3, 512, 4000, 64, 16),
+    (4, 1024, 5000, 16, 32),
+    (2, 512, 131072, 8, 32),
+    (2, 512, 131100, 8, 32),
 ]
 
 
@@ -105,6 +113,19 @@ def test_all_zero_rows_are_pure_ties(dev, golden):
     _, got, _ = check_case(dev, 3, k, n, kc, r, seed=0, x=x, w=w)
     assert [int(v) for v in got["rr_id"][0]] == [int(v) for v in fx["row_top_r"][0]]
     assert int(got["out_id"][0]) == int(fx["argmax"][0][0]) == int(got["out_id"][2])
+
+
+def test_zero_row_many_survivors(dev):
+    """A zero x row ties every candidate: the block-maximum rerank keeps 249
+    survivors (blocks 0..31) and must return ids 0-7, 64-71, ... in order."""
+    n, k = 5000, 512
+    w = workload.gen_weight(n, k, seed=8)
+    x = workload.gen_x(2, k, seed=9)
+    x[1] = 0
+    _, got, _ = check_case(dev, 2, k, n, 8, 32, seed=0, x=x, w=w)
+    want = [64 * b + i for b in range(4) for i in range(8)]
+    assert [int(v) for v in got["rr_id"][1]] == want
+    assert int(got["out_id"][1]) == 0
 
 
 def test_lossless_weights_give_exact_argmax(dev):
