@@ -87,18 +87,21 @@ class Rig:
         self.dev = dev
         self.stream = torch.cuda.current_stream().cuda_stream   # looked up once
         self.out = {}
+        self.ws = {}
         torch.cuda.synchronize()
         log(f"ready ({time.time() - t0:.1f}s)")
 
     def buffers(self, m):
         if m not in self.out:
             self.out[m] = self.B.forward_buffers(m, N, KCAND, R, self.dev)
+            self.ws[m] = self.B.workspace_for(m, K, self.dev)
         return self.out[m]
 
     def step(self, m, head, ev=None):
         """One full call through the library's one-call entry point; `ev` takes
         the coarse kernel's own dispatch timestamps."""
-        head(self.x[:m], stream=self.stream, out=self.buffers(m), coarse_events=ev)
+        out = self.buffers(m)
+        head(self.x[:m], stream=self.stream, out=out, coarse_events=ev, workspace=self.ws[m])
 
     def timed(self, m, steps, warmup, copies=None):
         """(seconds per call, seconds per coarse launch) over `steps` calls."""

@@ -56,11 +56,13 @@ def load_library() -> ctypes.CDLL:
     lib.draft_head_quantize_pack.argtypes = [P, i64, i64, i64, P, P, P, i32]
     lib.draft_head_tile.restype = i32
     lib.draft_head_tile.argtypes = [P, P, P, i64, i64, P, P]
+    lib.draft_head_workspace_bytes.restype = i32
+    lib.draft_head_workspace_bytes.argtypes = [i32, i32, ctypes.POINTER(sz)]
     lib.draft_head_coarse.restype = i32
-    lib.draft_head_coarse.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P]
+    lib.draft_head_coarse.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P, sz, P]
     lib.draft_head_forward.restype = i32
-    lib.draft_head_forward.argtypes = [P, i32, i32, i32, P, P, P, i64, i32, i32, P, P, P, P, P, P, P, P,
-                                       P, P]
+    lib.draft_head_forward.argtypes = [P, i32, i32, i32, P, P, P, i64, i32, i32, P, P, P, P, P, P, P, P, sz,
+                                       P, P, P]
     lib.draft_head_rerank.restype = i32
     lib.draft_head_rerank.argtypes = [P, P, i64, i32, i32, i32, P, P, i32, i32, P, P, P]
     lib.draft_head_argmax.restype = i32
@@ -156,9 +158,29 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
+def draft_head_workspace_bytes(M: int, K: int) -> int:
+    """Device workspace bytes the coarse pass needs for M rows of length K."""
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.draft_head_workspace_bytes(M, K, ctypes.byref(out)))
+    return out.value
+
+
+def workspace_for(M: int, K: int, device):
+    """A device workspace for M rows of length K (None when none is needed)."""
+    import torch
+    n = draft_head_workspace_bytes(M, K)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _ws(workspace):
+    return (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+
+
 def draft_head_coarse(x, tiled, pairs, N: int, kcand: int = 8, cand_val=None, cand_id=None,
-                      coarse_out=None, stream=None):
-    """x: CUDA bf16 [M][K]; tiled/pairs: CUDA tensors in the draft_head_tile layout.
+                      coarse_out=None, workspace=None, stream=None):
+    """x: CUDA bf16 [M][K]; tiled/pairs: CUDA tensors in the draft_head_tile layout;
+    workspace: CUDA tensor of draft_head_workspace_bytes(M, K) bytes (allocated when None).
     Returns (cand_val fp32 [M][NBLK*kcand], cand_id int32 [M][NBLK*kcand])."""
     import torch
     lib = load_library()
@@ -168,8 +190,10 @@ def draft_head_coarse(x, tiled, pairs, N: int, kcand: int = 8, cand_val=None, ca
         cand_val = _empty((M, nblk * kcand), torch.float32, x)
     if cand_id is None:
         cand_id = _empty((M, nblk * kcand), torch.int32, x)
+    if workspace is None:
+        workspace = workspace_for(M, K, x.device)
     _check(lib.draft_head_coarse(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), kcand, _ptr(cand_val),
-                                 _ptr(cand_id), _ptr(coarse_out), _stream(stream)))
+                                 _ptr(cand_id), _ptr(coarse_out), *_ws(workspace), _stream(stream)))
     return cand_val, cand_id
 
 
@@ -227,21 +251,24 @@ def _event(ev):
 
 
 def draft_head_forward(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, out=None,
-                       coarse_out=None, stream=None, coarse_events=None):
+                       coarse_out=None, workspace=None, stream=None, coarse_events=None):
     """One full call (coarse -> rerank -> argmax) in one library call.
 
-    out: dict from forward_buffers (allocated when None); coarse_events: optional
-    (start, stop) torch.cuda.Event pair that takes the coarse kernel's own
-    dispatch timestamps.  Returns the dict of output tensors."""
+    out: dict from forward_buffers (allocated when None); workspace: as for
+    draft_head_coarse; coarse_events: optional (start, stop) torch.cuda.Event
+    pair that takes the coarse kernel's own dispatch timestamps.  Returns the
+    dict of output tensors."""
     lib = load_library()
     M, K = x.shape
     if out is None:
         out = forward_buffers(M, N, kcand, R, x.device)
+    if workspace is None:
+        workspace = workspace_for(M, K, x.device)
     e0, e1 = (None, None) if coarse_events is None else (_event(coarse_events[0]), _event(coarse_events[1]))
     _check(lib.draft_head_forward(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0), kcand,
                                   R, _ptr(out["cand_val"]), _ptr(out["cand_id"]), _ptr(out["rr_id"]),
                                   _ptr(out["rr_val"]), _ptr(out["out_id"]), _ptr(out["out_val"]),
-                                  _ptr(coarse_out), _stream(stream), e0, e1))
+                                  _ptr(coarse_out), *_ws(workspace), _stream(stream), e0, e1))
     return out
 
 
@@ -271,9 +298,10 @@ class DraftHead:
         t_w = torch.from_numpy(np.ascontiguousarray(w_bits).view(np.int16)).to(device)
         return cls(t_tiled, t_pairs, t_w, n, k, kcand, R)
 
-    def __call__(self, x, coarse_out=None, stream=None, out=None, coarse_events=None):
+    def __call__(self, x, coarse_out=None, stream=None, out=None, coarse_events=None, workspace=None):
         return draft_head_forward(x, self.tiled, self.pairs, self.w, self.N, self.kcand, self.R, out=out,
-                                  coarse_out=coarse_out, stream=stream, coarse_events=coarse_events)
+                                  coarse_out=coarse_out, workspace=workspace, stream=stream,
+                                  coarse_events=coarse_events)
 
     def staged(self, x, coarse_out=None, stream=None):
         """The same call as three library calls (coarse, rerank, argmax)."""

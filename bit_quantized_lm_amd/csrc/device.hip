@@ -23,9 +23,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;            // waves per coarse workgroup; one 64-column block each
-constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxMT = 5;            // 16-row M tiles per coarse launch (80 rows)
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -176,21 +173,21 @@ __device__ __forceinline__ void shift_codes(const u32x4 (&raw)[2][NT], u32x4 (&r
 
 // Epilogue of one block: optional full rows, then the top-kcand of the block by
 // successive max-and-mask (`_emit`), ties to the lower column.  The four rows
-// 16i + 4hh + r of one (i, r) are handled at once, one per 16-lane row.
-// value(i, r, t): the coarse score of row 16i + 4hh + r, column 64b + 16t + nn.
-// Passes with r % rstep != rfirst are left to another wave.
+// m0 + 16i + 4hh + r of one (i, r) are handled at once, one per 16-lane row.
+// value(i, r, t): the coarse score of row m0 + 16i + 4hh + r, column
+// 64b + 16t + nn.  Passes with r % rstep != rfirst are left to another wave.
 template <int MT, int MR, class Value>
 __device__ __forceinline__ void block_select(Value value, const CoarseArgs& A, int b, int hh, int nn,
-                                             int rfirst = 0, int rstep = 1) {
+                                             int rfirst = 0, int rstep = 1, int m0 = 0) {
   const float NEG_INF = -__builtin_inff();
   const int ncand = A.nblk * A.kcand;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
-      if (16 * i + r >= A.M) continue;  // no row of this (i, r) is live (wave-uniform)
+      if (m0 + 16 * i + r >= A.M) continue;  // no row of this (i, r) is live (wave-uniform)
       if (r % rstep != rfirst) continue;
-      const int m = 16 * i + 4 * hh + r;
+      const int m = m0 + 16 * i + 4 * hh + r;
       const bool row_ok = m < A.M;
       float v[4];
 #pragma unroll
@@ -412,117 +409,347 @@ void coarse_resident_kernel(CoarseArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// Coarse kernel, x staged per group (any M up to 80 per launch).
+// Coarse kernel for more rows (up to 80 per launch, MT 16-row tiles).
 //
-// Workgroup = 4 waves, one 64-column block each.  The 128 x values of each
-// group are staged in LDS for all rows (double buffered, one barrier per
-// group) with the group sum X; the next group's x is loaded into registers
-// while the current group is computed.  LDS: [2][16 fragments][MP rows]
-// (MP = 16 MT, rows >= M zero), then X[2][MP]; the fixed row count makes the
-// fragment offsets compile-time immediates.
+// The page's accumulator form, S * p - ZS * X per group, is computed in two
+// parts.  The code part, (S/4) sum_k x v, is one MFMA chain per group, scaled
+// on the accumulator with one FMA per score.  The zero-point part, the sum
+// over groups of (S - ZS) X, is itself a small matrix product: per byte group
+// one more MFMA per tile, whose live k-slots pair each quarter's S - ZS with
+// that group's sum X.  S - ZS is exact in bf16 (ZS lies in [S, 2S), so the
+// difference is a multiple of S's last place and smaller than S), and X is
+// split into three bf16 parts whose sum is X to 2^-27 relative, so every
+// product is exact and only fp32 sums round.
+//
+// prep_x_kernel writes x for one launch into the caller's workspace in the
+// order the kernel consumes it, rows >= M zero (MP = 16 MT rows):
+//   x slab of group g = 4G + q (byte group G, quarter q): 16 fragments x MP
+//     rows, 16 bytes each, x * 2^64 in decode order (256 MT entries);
+//   zero-point slab of byte group G: 256 entries; entry hh*MP + m (hh < 2)
+//     holds row m's k-slots 8hh..8hh+7 of that product:
+//     X_hi(q0..q3) X_mid(q0..q3) | X_lo(q0..q3) 0 0 0 0.
+//
+// Workgroup = 4 blocks of 64 columns.  From MT = 3 on, two waves share a
+// block, wave (block lb, part p) holding the row tiles [p ? MA : 0, ...), so
+// the two waves a SIMD runs (lb and lb + 4) hold MT tiles of accumulators
+// between them and hide each other's latency; below that, one wave per block.
+//
+// Every global read of the main loop is a direct-to-LDS DMA.  Iteration j
+// (j < 0: the prologue) issues, in this order and every time, even where the
+// data does not exist (then a harmless copy into a free slot):
+//   X(j + XD)  the wave's chunks of that group's x slab             NX ops
+//   C(G + 1)   at j = 4G: its chunks of byte group G + 1's codes   NC ops
+//   B(G + 1)   at j = 4G + 1: its chunk of that zero-point slab    NB ops
+// so the number of ops issued after any op depends only on j mod 4, and each
+// iteration ends with one vmcnt wait whose count is a constant (big_wait).
+// Completions are counted in issue order; with this order no wait for an x
+// slab (an L2 hit) waits for code bytes still on their way from HBM before
+// they are needed.
+constexpr int kMaxMT = 5;            // 16-row tiles per launch (80 rows)
+constexpr int kCodeChunks = 9;       // 1 KB chunks of one block's byte group: 8 code + 1 pair
+constexpr int kZpEntries = 256;      // zero-point slab entries (16 bytes)
+
 template <int MT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 2 : 1, MT <= 2 ? 2 : 1)))
-void coarse_chunked_kernel(CoarseArgs A) {
-  constexpr int MP = 16 * MT;
-  __shared__ u32x4 xs[2 * 16 * MP];
-  __shared__ float Xs[2 * MP];
+struct BigShape {
+  static constexpr int WPB = MT >= 3 ? 2 : 1;       // waves per block
+  static constexpr int MA = (MT + WPB - 1) / WPB;   // row tiles of part 0
+  static constexpr int MB = MT - MA;                // row tiles of part 1
+  static constexpr int W = 4 * WPB;                 // waves per workgroup
+  static constexpr int XD = MT >= 4 ? 3 : 4;        // x slabs requested ahead
+  // DMA ops per iteration of a wave of part p
+  static constexpr int nx(int p) { return (4 * MT - 4 * p + W - 1) / W; }
+  static constexpr int nc(int p) { return (kCodeChunks - p + WPB - 1) / WPB; }
+  static constexpr int nb(int p) { return p == 0 ? 1 : 0; }
+};
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+constexpr size_t big_lds_bytes(int MT, int XD) {
+  return (size_t)(XD + 1) * 4096 * MT + (size_t)2 * 4 * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
+}
+
+// Workspace of one launch with MT row tiles: x slabs, then zero-point slabs.
+size_t big_workspace_bytes(int MT, int K) {
+  return (size_t)(K / DH_GROUP) * 4096 * MT + (size_t)(K / 512) * kZpEntries * 16;
+}
+
+// Ops a wave of part P may leave outstanding at the end of an iteration with
+// j mod 4 == Q: those issued after X(j + 1) and, for Q == 3, after the C and
+// B of the next byte group (issued at j - 3 and j - 2).  The prologue's final
+// wait (X(0), C(0), B(0)) is the Q == 3 case.
+template <int MT, int P>
+constexpr int big_wait(int Q) {
+  using S = BigShape<MT>;
+  auto ops = [](int j) {
+    const int q = ((j % 4) + 4) % 4;
+    return S::nx(P) + (q == 0 ? S::nc(P) : 0) + (q == 1 ? S::nb(P) : 0);
+  };
+  int best = 1 << 20;
+  if (S::nx(P)) {
+    const int j1 = Q + 1 - S::XD, q1 = ((j1 % 4) + 4) % 4;
+    int n = (q1 == 0 ? S::nc(P) : 0) + (q1 == 1 ? S::nb(P) : 0);
+    for (int j = j1 + 1; j <= Q; ++j) n += ops(j);
+    best = n < best ? n : best;
+  }
+  if (Q == 3) {
+    if (S::nc(P)) {
+      int n = 0;
+      for (int j = Q - 2; j <= Q; ++j) n += ops(j);
+      best = n < best ? n : best;
+    }
+    if (S::nb(P)) {
+      int n = 0;
+      for (int j = Q - 1; j <= Q; ++j) n += ops(j);
+      best = n < best ? n : best;
+    }
+  }
+  return best;
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One direct-to-LDS DMA op: lane l's 16 bytes at base + voff land at
+// lds + 16 l (base and lds wave-uniform; voff = 16 l).
+__device__ __forceinline__ void dma16(uint32_t voff, const void* base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Thread (m, G, p): piece p (8 consecutive k) of the four groups of byte
+// group G of row m.  The 16 threads of a (m, G) are 16 consecutive lanes.
+__global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t* __restrict__ x, int M, int MP, int K,
+                                                     u32x4* __restrict__ xslab, u32x4* __restrict__ zslab) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int NG4 = K >> 9, Q4 = K >> 2;
+  if (i >= MP * NG4 * 16) return;   // whole 16-lane groups leave together
+  const int p = i & 15, G = (i >> 4) % NG4, m = (i >> 4) / NG4;
+  const int h = p >> 3, s = (p >> 1) & 3, e = p & 1, f = (h * 2 + e) * 4 + s;
+  u32x4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    v[q] = m < M ? *reinterpret_cast<const u32x4*>(x + (size_t)m * K + q * Q4 + 128 * G + 8 * p)
+                 : u32x4{0u, 0u, 0u, 0u};
+  float X[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float sum;
+    xslab[((size_t)(4 * G + q) * 16 + f) * MP + m] = permute_x(v[q], sum);
+    X[q] = row16_sum(sum);
+  }
+  if (p < 2) {
+    uint32_t part[3][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float r = X[q];
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {   // r - bf16(r) is exact in fp32
+        part[c][q] = f32_to_bf16_rne(r);
+        r -= __uint_as_float(part[c][q] << 16);
+      }
+    }
+    const u32x4 o = p == 0 ? u32x4{part[0][0] | part[0][1] << 16, part[0][2] | part[0][3] << 16,
+                                   part[1][0] | part[1][1] << 16, part[1][2] | part[1][3] << 16}
+                           : u32x4{part[2][0] | part[2][1] << 16, part[2][2] | part[2][3] << 16, 0u, 0u};
+    zslab[(size_t)G * kZpEntries + p * MP + m] = o;
+  }
+}
+
+struct BigArgs {
+  CoarseArgs c;
+  const u32x4* xslab;
+  const u32x4* zslab;
+};
+
+// MFMA phase of one group (quarter Q) for MTW row tiles and the four column
+// tiles: cg = sum over the group's k of x 2^64 * v 2^(2Q-133).  A scheduling
+// barrier per k-slice keeps one slice's operands live at a time.
+// xb: this lane's fragment 0 (A row nn, k-slot hh) in the slab.
+template <int MTW, int Q, int MP>
+__device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MTW][4], const u32x4 (&raw)[2][4],
+                                              const u32x4 (&raw8)[2][4], const u32x4* xb) {
+  constexpr uint32_t mask = 0x00030003u << (2 * Q);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int h = ks >> 1, e = ks & 1;
+    u32x4 a[MTW];
+#pragma unroll
+    for (int i = 0; i < MTW; ++i) a[i] = xb[(h * 2 + e) * 4 * MP + 16 * i];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 bv = decode_quarter(raw[h][t][2 * e], raw8[h][t][2 * e], raw[h][t][2 * e + 1],
+                                       raw8[h][t][2 * e + 1], mask);
+#pragma unroll
+      for (int i = 0; i < MTW; ++i)
+        cg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]), bv,
+                                                           ks ? cg[i][t] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One wave's share of a block: part P holds row tiles T0 .. T0 + MTW - 1 of
+// the MT, all four column tiles and the whole of K; then its rows of the
+// block's selection.
+template <int MT, int P>
+__device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem) {
+  using S = BigShape<MT>;
+  constexpr int MP = 16 * MT, XD = S::XD, NBUF = XD + 1, W = S::W, WPB = S::WPB;
+  constexpr int MTW = P ? S::MB : S::MA, T0 = P ? S::MA : 0;
+  const CoarseArgs& A = BA.c;
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);   // [NBUF][16][MP]
+  u32x4* cs = xs + NBUF * 16 * MP;              // [2 slots][4 blocks][9 chunks][64]
+  u32x4* zs = cs + 2 * 4 * kCodeChunks * 64;    // [256]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 4, nn = lane & 15;
-  const int b = blockIdx.x * kWaves + wave;
+  const int lb = wave & 3;
+  const int b = blockIdx.x * 4 + lb;
   const bool blk_ok = b < A.nblk;
-  const int NG4 = A.K >> 9, Q4 = A.K >> 2;
+  const int NG4 = A.K >> 9, NGRP = A.K >> 7;
 
-  // A wave past the last block reads block 0 (valid memory) and writes nothing.
+  // A block past the last one streams block 0 (valid memory) and writes nothing.
   const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
   const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64;
+  const uint32_t voff = lane * 16;
+  const uint32_t xs_l = lds_addr(xs), zs_l = lds_addr(zs + wave * 64);
+  const uint32_t cs_l = lds_addr(cs + lb * kCodeChunks * 64);
 
-  for (int i = tid; i < 2 * 16 * MP; i += kThreads) xs[i] = u32x4{0u, 0u, 0u, 0u};
-  for (int i = tid; i < 2 * MP; i += kThreads) Xs[i] = 0.f;
+  // Issue iteration j's ops.  Data that does not exist is replaced by a copy
+  // into a slot nothing reads before it is refilled: past the end, the last
+  // slab or byte group; before the start (X(j + XD) < 0 when XD < 4), slab
+  // j + XD + NBUF into the very slot that slab will be loaded to.
+  auto issue = [&](int j) {
+    int gx = j + XD;
+    const uint32_t xslot = (uint32_t)(gx < 0 ? gx + NBUF : gx % NBUF);
+    gx = gx < 0 ? gx + NBUF : gx < NGRP ? gx : NGRP - 1;
+    const u32x4* xsrc = BA.xslab + (size_t)gx * 256 * MT;
+#pragma unroll
+    for (int k = 0; k < S::nx(P); ++k) {   // chunks wave + W k, all below 4 MT
+      const int c = wave + W * k;
+      dma16(voff, xsrc + c * 64, xs_l + xslot * 4096 * MT + c * 1024);
+    }
+    int G1 = (j >> 2) + 1;
+    const uint32_t cslot = (uint32_t)(G1 & 1);
+    G1 = G1 < NG4 ? G1 : NG4 - 1;
+    if ((j & 3) == 0) {
+#pragma unroll
+      for (int k = 0; k < S::nc(P); ++k) {
+        const int c = P + WPB * k;
+        dma16(voff, c < 8 ? tp + (G1 * 8 + c) * 64 : pp + G1 * 64,
+              cs_l + cslot * 4 * kCodeChunks * 1024 + c * 1024);
+      }
+    } else if ((j & 3) == 1 && S::nb(P)) {
+      dma16(voff, BA.zslab + (size_t)G1 * kZpEntries + lb * 64, zs_l);
+    }
+  };
+
+#pragma unroll
+  for (int j = -4; j < 0; ++j) issue(j);
+  wait_vm<big_wait<MT, P>(3)>();
   __syncthreads();
 
-  f32x4 acc[MT][4];
+  f32x4 acc[MTW][4];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int i = 0; i < MTW; ++i)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_codes = [&](int G, u32x4 (&raw)[2][4], u32x4 (&sz)[4]) {
+  for (int G = 0; G < NG4; ++G) {
+    const u32x4* cw = cs + ((G & 1) * 4 + lb) * kCodeChunks * 64;
+    const uint32_t* cp = reinterpret_cast<const uint32_t*>(cw + 512 + nn);   // pair (t, q) at 64 t + q
+    u32x4 raw[2][4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) raw[h][t] = tp[((G * 2 + h) * 4 + t) * 64 + lane];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) sz[t] = pp[(G * 4 + t) * 16 + nn];
-  };
+      for (int t = 0; t < 4; ++t) raw[h][t] = cw[(h * 4 + t) * 64 + lane];
 
-  // Staging of group (G, q): thread i < 16*M loads piece p = i & 15 of row
-  // m = i >> 4, i.e. x[m][q*K/4 + 128*G + 8p .. +8].
-  constexpr int kMaxStage = (16 * MP + kThreads - 1) / kThreads;
-  const int stage_n = 16 * A.M;
-  auto stage_load = [&](int G, int q, u32x4 (&st)[kMaxStage]) {
-    const int kbase = q * Q4 + 128 * G;
+    // zero-point part of byte group G
+    {
+      u32x4 za[MTW];
 #pragma unroll
-    for (int r = 0; r < kMaxStage; ++r) {
-      const int i = tid + r * kThreads;
-      const int ic = i < stage_n ? i : 0;   // clamped: the load is unconditional
-      st[r] = *reinterpret_cast<const u32x4*>(A.x + (size_t)(ic >> 4) * A.K + kbase + 8 * (ic & 15));
-    }
-  };
-  auto stage_store = [&](int buf, const u32x4 (&st)[kMaxStage]) {
-    u32x4* dst = xs + buf * 16 * MP;
+      for (int i = 0; i < MTW; ++i) za[i] = zs[(hh & 1) * MP + 16 * (T0 + i) + nn];
+      if (hh >= 2) {
 #pragma unroll
-    for (int r = 0; r < kMaxStage; ++r) {
-      const int i = tid + r * kThreads;
-      if (i < stage_n) {
-        const int m = i >> 4, p = i & 15;
-        float sum;
-        const u32x4 o = permute_x(st[r], sum);
-        const int h = p >> 3, s = (p >> 1) & 3, e = p & 1;
-        dst[((h * 2 + e) * 4 + s) * MP + m] = o;
-        sum = row16_sum(sum);
-        if (p == 0) Xs[buf * MP + m] = sum;
+        for (int i = 0; i < MTW; ++i) za[i] = u32x4{0u, 0u, 0u, 0u};
       }
+      f32x4 zc[MTW][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x4 sz = cw[512 + t * 16 + nn];
+        uint32_t d[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[q] = __float_as_uint(lo_bf16(sz[q]) - hi_bf16(sz[q]));
+        const uint32_t p01 = (d[0] >> 16) | (d[1] & 0xFFFF0000u);
+        const uint32_t p23 = (d[2] >> 16) | (d[3] & 0xFFFF0000u);
+        const u32x4 zb = hh == 0 ? u32x4{p01, p23, p01, p23}
+                                 : hh == 1 ? u32x4{p01, p23, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+          zc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[i]),
+                                                            __builtin_bit_cast(bf16x8, zb),
+                                                            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < MTW; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][t] += zc[i][t];
     }
-  };
 
-  u32x4 raw[2][4], sz[4];
-  load_codes(0, raw, sz);
-  {
-    u32x4 st[kMaxStage];
-    stage_load(0, 0, st);
-    stage_store(0, st);
-  }
-  __syncthreads();
-
-  for (int G = 0; G < NG4; ++G) {
-    u32x4 rawn[2][4], szn[4];
-    if (G + 1 < NG4) load_codes(G + 1, rawn, szn);
     u32x4 raw8[2][4];
     shift_codes(raw, raw8);
-#pragma nounroll
-    for (int q = 0; q < 4; ++q) {
-      const int cur = q & 1;  // 4 groups per G, so the buffer parity is q's
-      const bool has_next = (q < 3) || (G + 1 < NG4);
-      u32x4 st[kMaxStage];
-      if (has_next) stage_load(q < 3 ? G : G + 1, q < 3 ? q + 1 : 0, st);
-      coarse_group<MT, 4, -1, 4>(acc, raw, raw8, sz, xs + cur * 16 * MP + hh * MP + nn, MP, Xs + cur * MP,
-                              hh, q);
-      if (has_next) stage_store(cur ^ 1, st);
+    auto group = [&](auto qc) {
+      constexpr int Q = decltype(qc)::value;
+      const int g = 4 * G + Q;
+      issue(g);
+      f32x4 cg[MTW][4];
+      big_group_mma<MTW, Q, MP>(cg, raw, raw8, xs + (g % NBUF) * 16 * MP + hh * MP + 16 * T0 + nn);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float Sq = quarter_scale(lo_bf16(cp[64 * t + Q]), Q);
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][t][r] = __builtin_fmaf(Sq, cg[i][t][r], acc[i][t][r]);
+      }
+      wait_vm<big_wait<MT, P>(Q)>();
       __syncthreads();
-    }
-    if (G + 1 < NG4) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) raw[h][t] = rawn[h][t];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) sz[t] = szn[t];
+    };
+    group(std::integral_constant<int, 0>{});
+    group(std::integral_constant<int, 1>{});
+    group(std::integral_constant<int, 2>{});
+    group(std::integral_constant<int, 3>{});
+  }
+  wait_vm<0>();
+  if (!blk_ok) return;
+  block_select<MTW, 4>([&](int i, int r, int t) { return acc[i][t][r]; }, A, b, hh, nn, 0, 1, 16 * T0);
+}
+
+template <int MT>
+__global__ __launch_bounds__(64 * BigShape<MT>::W) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void coarse_mfma_kernel(BigArgs BA) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if constexpr (BigShape<MT>::MB > 0) {
+    if (threadIdx.x >= 256) {
+      big_wave<MT, 1>(BA, smem);
+      return;
     }
   }
-  if (!blk_ok) return;
-  block_select<MT, 4>([&](int i, int r, int t) { return acc[i][t][r]; }, A, b, hh, nn);
+  big_wave<MT, 0>(BA, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1256,16 +1483,35 @@ hipError_t launch_resident(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hi
 }
 
 template <int MT>
-hipError_t launch_chunked(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  dim3 grid((A.nblk + kWaves - 1) / kWaves);
-  hipExtLaunchKernelGGL(coarse_chunked_kernel<MT>, grid, dim3(kThreads), 0, s, e0, e1, 0, A);
+hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD);
+  static_assert(lds <= kMaxLds, "LDS budget of the many-row kernel");
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&coarse_mfma_kernel<MT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((A.c.nblk + 3) / 4);
+  hipExtLaunchKernelGGL(coarse_mfma_kernel<MT>, grid, dim3(64 * BigShape<MT>::W), lds, s, e0, e1, 0, A);
   return hipGetLastError();
 }
 
 int resident_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
+// Up to 8 rows whose x fits the workgroup's LDS take the resident kernel (no
+// workspace); every other M the many-row kernel, in launches of up to 80 rows.
+bool use_resident(int M, int K) { return M <= 8 && resident_lds_bytes(K, resident_rows(M)) <= kMaxLds; }
+
+size_t coarse_workspace_bytes(int M, int K) {
+  if (use_resident(M, K)) return 0;
+  return big_workspace_bytes(std::min((M + 15) / 16, kMaxMT), K);
+}
+
 int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
-                    int kcand, const float* cand_val, const int32_t* cand_id) {
+                    int kcand, const float* cand_val, const int32_t* cand_id, const void* workspace,
+                    size_t workspace_bytes) {
   if (!x || !tiled || !pairs || !cand_val || !cand_id)
     return dh::fail(DH_EINVAL, "coarse: null pointer");
   int rc = check_m(M);
@@ -1276,6 +1522,10 @@ int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, co
     return dh::fail(DH_EUNSUP, "coarse: kcand must be in 1..%d (got %d)", DH_MAX_KCAND, kcand);
   if (!aligned16(x) || !aligned16(tiled) || !aligned16(pairs))
     return dh::fail(DH_EINVAL, "coarse: x, tiled and pairs must be 16-byte aligned");
+  const size_t need = coarse_workspace_bytes(M, K);
+  if (need && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+    return dh::fail(DH_EINVAL, "coarse: M=%d, K=%d needs a 16-byte aligned workspace of %zu bytes (got %p, %zu)",
+                    M, K, need, workspace, workspace_bytes);
   return DH_OK;
 }
 
@@ -1308,14 +1558,14 @@ int validate_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, con
 
 // Launches only; arguments were validated.
 int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, int kcand,
-                  float* cand_val, int32_t* cand_id, float* coarse_out, hipStream_t s, hipEvent_t ev0,
-                  hipEvent_t ev1) {
+                  float* cand_val, int32_t* cand_id, float* coarse_out, void* workspace, hipStream_t s,
+                  hipEvent_t ev0, hipEvent_t ev1) {
   const int nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
   const int ncand = nblk * kcand;
   CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
                reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out};
   hipError_t e = hipSuccess;
-  if (M <= 8 && resident_lds_bytes(K, resident_rows(M)) <= kMaxLds) {
+  if (use_resident(M, K)) {
     switch (resident_rows(M)) {
       case 1: e = launch_resident<1>(A, s, ev0, ev1); break;
       case 2: e = launch_resident<2>(A, s, ev0, ev1); break;
@@ -1325,8 +1575,9 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
     if (e != hipSuccess) return dh::fail(DH_EHIP, "coarse_resident_kernel: %s", hipGetErrorString(e));
     return dh::ok();
   }
-  // Rows beyond one launch's 80 are handled by further launches over the
-  // same weights (only for M > 80).
+  // Rows beyond one launch's 80 take further launches over the same weights;
+  // they reuse the workspace (the launches are ordered on the stream).
+  const int NG4 = K / 512;
   for (int m0 = 0; m0 < M; m0 += 16 * kMaxMT) {
     CoarseArgs B = A;
     B.M = std::min(M - m0, 16 * kMaxMT);
@@ -1334,16 +1585,24 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
     B.cand_val = cand_val + (size_t)m0 * ncand;
     B.cand_id = cand_id + (size_t)m0 * ncand;
     B.coarse_out = coarse_out ? coarse_out + (size_t)m0 * N : nullptr;
+    const int mt = (B.M + 15) / 16, mp = 16 * mt;
+    u32x4* xslab = static_cast<u32x4*>(workspace);
+    u32x4* zslab = xslab + (size_t)(K / DH_GROUP) * 256 * mt;
+    hipLaunchKernelGGL(prep_x_kernel, dim3((mp * NG4 * 16 + 255) / 256), dim3(256), 0, s, B.x, B.M, mp, K, xslab,
+                       zslab);
+    if ((e = hipGetLastError()) != hipSuccess)
+      return dh::fail(DH_EHIP, "prep_x_kernel: %s", hipGetErrorString(e));
+    const BigArgs BA{B, xslab, zslab};
     hipEvent_t b0 = m0 == 0 ? ev0 : nullptr;
     hipEvent_t b1 = m0 + 16 * kMaxMT >= M ? ev1 : nullptr;
-    switch ((B.M + 15) / 16) {
-      case 1: e = launch_chunked<1>(B, s, b0, b1); break;
-      case 2: e = launch_chunked<2>(B, s, b0, b1); break;
-      case 3: e = launch_chunked<3>(B, s, b0, b1); break;
-      case 4: e = launch_chunked<4>(B, s, b0, b1); break;
-      default: e = launch_chunked<5>(B, s, b0, b1); break;
+    switch (mt) {
+      case 1: e = launch_big<1>(BA, s, b0, b1); break;
+      case 2: e = launch_big<2>(BA, s, b0, b1); break;
+      case 3: e = launch_big<3>(BA, s, b0, b1); break;
+      case 4: e = launch_big<4>(BA, s, b0, b1); break;
+      default: e = launch_big<5>(BA, s, b0, b1); break;
     }
-    if (e != hipSuccess) return dh::fail(DH_EHIP, "coarse_chunked_kernel: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return dh::fail(DH_EHIP, "coarse_mfma_kernel: %s", hipGetErrorString(e));
   }
   return dh::ok();
 }
@@ -1402,12 +1661,22 @@ hipStream_t as_stream(void* p) { return reinterpret_cast<hipStream_t>(p); }
 
 extern "C" {
 
-int draft_head_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
-                      int kcand, float* cand_val, int32_t* cand_id, float* coarse_out, void* stream) {
-  int rc = validate_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id);
+int draft_head_workspace_bytes(int M, int K, size_t* bytes) {
+  int rc = check_m(M);
   if (rc) return rc;
-  return launch_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, as_stream(stream),
-                       nullptr, nullptr);
+  if ((rc = check_k(K))) return rc;
+  if (!bytes) return dh::fail(DH_EINVAL, "workspace_bytes: null pointer");
+  *bytes = coarse_workspace_bytes(M, K);
+  return dh::ok();
+}
+
+int draft_head_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                      int kcand, float* cand_val, int32_t* cand_id, float* coarse_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int rc = validate_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes);
+  if (rc) return rc;
+  return launch_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace,
+                       as_stream(stream), nullptr, nullptr);
 }
 
 int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N,
@@ -1428,14 +1697,15 @@ int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, i
 int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
                        const void* w, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
                        int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
-                       void* stream, void* coarse_start_event, void* coarse_stop_event) {
+                       void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
+                       void* coarse_stop_event) {
   const int ncand = (N > 0 && kcand > 0) ? ((N + DH_BLOCK_N - 1) / DH_BLOCK_N) * kcand : 0;
-  int rc = validate_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id);
+  int rc = validate_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes);
   if (rc) return rc;
   if ((rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val))) return rc;
   if ((rc = validate_argmax(rr_id, rr_val, M, R, out_id, out_val))) return rc;
   hipStream_t s = as_stream(stream);
-  if ((rc = launch_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, s,
+  if ((rc = launch_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace, s,
                           reinterpret_cast<hipEvent_t>(coarse_start_event),
                           reinterpret_cast<hipEvent_t>(coarse_stop_event))))
     return rc;

@@ -19,8 +19,10 @@
  *     message of the last error on the calling thread is draft_head_last_error().
  *   - All argument validation happens before any HIP call, so every error
  *     except DH_EHIP can be provoked without a GPU.
- *   - The caller owns every buffer.  The library allocates no device memory,
- *     keeps no state between calls and uses no scratch buffer.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and keeps no state between calls; where the coarse pass needs scratch
+ *     memory (more than 8 rows), the caller passes it in as a workspace of
+ *     draft_head_workspace_bytes() bytes.
  *   - Device functions enqueue work asynchronously on `stream` (a hipStream_t
  *     passed as void*, NULL = the null stream) and return once it is enqueued;
  *     launch errors are reported by the call that launched (DH_EHIP).  Calls on
@@ -100,6 +102,17 @@ int draft_head_tile(const uint8_t* packed, const uint16_t* S, const uint16_t* ZS
                     int64_t N, int64_t K, uint8_t* tiled, uint32_t* pairs);
 
 /*
+ * Bytes of device workspace draft_head_coarse / draft_head_forward need for M
+ * rows of length K: 0 when M <= 8 and the resident kernel holds all of x in
+ * LDS (any K at M = 1; K <= 35840, 15872, 7680 at M = 2, 3..4, 5..8), else
+ * the x of one launch of up to 80 rows laid out
+ * for the many-row kernel: (K/128) * 4096 * MT + (K/512) * 4096 bytes with
+ * MT = min(ceil(M/16), 5) (860,160 bytes at M = 72, K = 5120).
+ * Errors: DH_EINVAL (null pointer, M < 1), DH_EUNSUP (M > DH_MAX_M), DH_ESHAPE.
+ */
+int draft_head_workspace_bytes(int M, int K, size_t* bytes);
+
+/*
  * DEVICE.  Coarse scores and block top-KCAND candidates.
  * Follows `_draft_head_int2` and `_emit` on the radiance_drafthead.py page:
  * for every row m and column n, c[m][n] = sum over groups g of
@@ -112,12 +125,18 @@ int draft_head_tile(const uint8_t* packed, const uint16_t* S, const uint16_t* ZS
  *   cand_id    out, int32, same shape: global column id, or -1 (value -inf)
  *              when block b has fewer than kcand columns (n >= N)
  *   coarse_out optional out (NULL = not written), fp32 [M][N] coarse scores
+ *   workspace  device scratch of at least draft_head_workspace_bytes(M, K)
+ *              bytes, 16-byte aligned (may be NULL when that is 0); its
+ *              contents are overwritten, so calls that share one workspace
+ *              must be ordered (e.g. on one stream)
+ * x values must be finite with |x| < 2^63 (x is scaled by 2^64 on chip).
  * Limits: 1 <= M <= DH_MAX_M, K % 512 == 0, N >= 1, 1 <= kcand <= DH_MAX_KCAND.
- * Errors: DH_EINVAL, DH_ESHAPE, DH_EUNSUP, DH_EHIP.
+ * Errors: DH_EINVAL (also: workspace missing, misaligned or too small),
+ *         DH_ESHAPE, DH_EUNSUP, DH_EHIP.
  */
 int draft_head_coarse(const void* x, int M, int K, int N, const uint8_t* tiled,
                       const uint32_t* pairs, int kcand, float* cand_val, int32_t* cand_id,
-                      float* coarse_out, void* stream);
+                      float* coarse_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * DEVICE.  Row top-R of the candidates and their exact logits.
@@ -161,15 +180,18 @@ int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R,
  *              created by the caller, NULL = none): they take the start and
  *              end timestamps of the coarse kernel's own dispatch
  *              (hipExtLaunchKernel), so hipEventElapsedTime gives that
- *              kernel's duration; where M > 80 needs several coarse
- *              launches, the first one's start and the last one's end.
+ *              kernel's duration (for M > 8, the many-row kernel's, without
+ *              the small kernel that lays x out in the workspace before it);
+ *              where M > 80 needs several coarse launches, the first one's
+ *              start and the last one's end.
  * Errors: as the three calls.
  */
 int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
                        const uint32_t* pairs, const void* w, int64_t ldw, int kcand, int R,
                        float* cand_val, int32_t* cand_id, int32_t* rr_id, float* rr_val,
-                       int32_t* out_id, float* out_val, float* coarse_out, void* stream,
-                       void* coarse_start_event, void* coarse_stop_event);
+                       int32_t* out_id, float* out_val, float* coarse_out, void* workspace,
+                       size_t workspace_bytes, void* stream, void* coarse_start_event,
+                       void* coarse_stop_event);
 
 #ifdef __cplusplus
 }

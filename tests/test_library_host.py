@@ -24,8 +24,8 @@ def lib():
 def test_library_exports_every_header_symbol(lib):
     names = B.header_functions()
     assert set(names) == {"draft_head_last_error", "draft_head_sizes", "draft_head_quantize_pack",
-                          "draft_head_tile", "draft_head_coarse", "draft_head_rerank",
-                          "draft_head_argmax", "draft_head_forward"}
+                          "draft_head_tile", "draft_head_workspace_bytes", "draft_head_coarse",
+                          "draft_head_rerank", "draft_head_argmax", "draft_head_forward"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -136,20 +136,38 @@ def test_quantize_pack_validation(lib):
     _err(lib, lib.draft_head_tile(p, p, p, 4, 500, p, p), B.DH_ESHAPE)
 
 
+def test_workspace_bytes(lib):
+    # resident kernel (no workspace) up to 8 rows while x fits its LDS
+    for m, k in ((1, 5120), (1, 65536), (2, 35840), (4, 15872), (8, 5120), (8, 7680)):
+        assert B.draft_head_workspace_bytes(m, k) == 0, (m, k)
+    # many-row kernel: (K/128) * 4096 * MT + (K/512) * 4096 with MT = min(ceil(M/16), 5)
+    for m, k in ((2, 36352), (4, 16384), (8, 8192), (9, 512), (16, 1024), (17, 1024), (72, 5120),
+                 (80, 5120), (81, 5120), (128, 5120)):
+        mt = min((m + 15) // 16, 5)
+        assert B.draft_head_workspace_bytes(m, k) == (k // 128) * 4096 * mt + (k // 512) * 4096, (m, k)
+    assert B.draft_head_workspace_bytes(72, 5120) == 860_160
+    out = ctypes.c_size_t()
+    _err(lib, lib.draft_head_workspace_bytes(1, 512, None), B.DH_EINVAL)
+    _err(lib, lib.draft_head_workspace_bytes(0, 512, ctypes.byref(out)), B.DH_EINVAL)
+    _err(lib, lib.draft_head_workspace_bytes(129, 512, ctypes.byref(out)), B.DH_EUNSUP)
+    _err(lib, lib.draft_head_workspace_bytes(1, 700, ctypes.byref(out)), B.DH_ESHAPE)
+
+
 @pytest.mark.parametrize("via", ["coarse", "forward"])
 def test_coarse_validation(lib, via):
     if via == "forward":    # the same checks, before any launch, in the one-call entry point
-        f = lambda x, M, K, N, t, p, kc, cv, ci, co, s: lib.draft_head_forward(  # noqa: E731
-            x, M, K, N, t, p, FAKE, K, kc, 8, cv, ci, FAKE, FAKE, FAKE, FAKE, co, s, None, None)
+        f = lambda x, M, K, N, t, p, kc, cv, ci, co, ws, wsb, s: lib.draft_head_forward(  # noqa: E731
+            x, M, K, N, t, p, FAKE, K, kc, 8, cv, ci, FAKE, FAKE, FAKE, FAKE, co, ws, wsb, s, None, None)
     else:
         f = lambda *a: lib.draft_head_coarse(*a)  # noqa: E731
-    ok = dict(x=FAKE, M=1, K=512, N=64, tiled=FAKE, pairs=FAKE, kc=8, cv=FAKE, ci=FAKE, co=None, s=None)
+    ok = dict(x=FAKE, M=1, K=512, N=64, tiled=FAKE, pairs=FAKE, kc=8, cv=FAKE, ci=FAKE, co=None, ws=None,
+              wsb=0, s=None)
 
     def call(**kw):
         a = dict(ok)
         a.update(kw)
         return f(a["x"], a["M"], a["K"], a["N"], a["tiled"], a["pairs"], a["kc"], a["cv"], a["ci"],
-                 a["co"], a["s"])
+                 a["co"], a["ws"], a["wsb"], a["s"])
     _err(lib, call(x=None), B.DH_EINVAL)
     _err(lib, call(cv=None), B.DH_EINVAL)
     _err(lib, call(ci=None), B.DH_EINVAL)
@@ -164,6 +182,12 @@ def test_coarse_validation(lib, via):
     _err(lib, call(kc=65), B.DH_EUNSUP)
     _err(lib, call(x=MIS), B.DH_EINVAL)
     _err(lib, call(pairs=MIS), B.DH_EINVAL)
+    # more than 8 rows need the caller's workspace: present, aligned, large enough
+    need = B.draft_head_workspace_bytes(9, 512)
+    _err(lib, call(M=9), B.DH_EINVAL)
+    _err(lib, call(M=9, ws=FAKE, wsb=need - 16), B.DH_EINVAL)
+    _err(lib, call(M=9, ws=MIS, wsb=need), B.DH_EINVAL)
+    _err(lib, call(M=9, ws=None, wsb=need), B.DH_EINVAL)
 
 
 def test_rerank_validation(lib):
@@ -211,7 +235,7 @@ def test_forward_validation(lib):
         a.update(kw)
         return lib.draft_head_forward(a["x"], a["M"], a["K"], a["N"], a["t"], a["p"], a["w"], a["ldw"],
                                       a["kc"], a["R"], a["cv"], a["ci"], a["ri"], a["rv"], a["oi"],
-                                      a["ov"], a["co"], a["s"], None, None)
+                                      a["ov"], a["co"], None, 0, a["s"], None, None)
     _err(lib, call(w=None), B.DH_EINVAL)
     _err(lib, call(ri=None), B.DH_EINVAL)
     _err(lib, call(oi=None), B.DH_EINVAL)
