@@ -171,11 +171,47 @@ __device__ __forceinline__ void shift_codes(const u32x4 (&raw)[2][NT], u32x4 (&r
       for (int c = 0; c < 4; ++c) raw8[h][t][c] = raw[h][t][c] >> 8;
 }
 
-// Epilogue of one block: optional full rows, then the top-kcand of the block by
-// successive max-and-mask (`_emit`), ties to the lower column.  The four rows
-// m0 + 16i + 4hh + r of one (i, r) are handled at once, one per 16-lane row.
-// value(i, r, t): the coarse score of row m0 + 16i + 4hh + r, column
-// 64b + 16t + nn.  Passes with r % rstep != rfirst are left to another wave.
+// All-reduce max / min over each 16-lane row of the wave with DPP lane moves
+// (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror), which
+// fold into the max / min instructions: every lane of the row ends with the
+// row's result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_row(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, dpp_row<0xB1>(v));
+  v = max(v, dpp_row<0x4E>(v));
+  v = max(v, dpp_row<0x141>(v));
+  v = max(v, dpp_row<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t row16_min(uint32_t v) {
+  v = min(v, dpp_row<0xB1>(v));
+  v = min(v, dpp_row<0x4E>(v));
+  v = min(v, dpp_row<0x141>(v));
+  v = min(v, dpp_row<0x140>(v));
+  return v;
+}
+
+// fp32 <-> unsigned key with the same order (finite values and -inf; key 0
+// is below every value and marks a column past N).
+__device__ __forceinline__ uint32_t f32_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_f32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Epilogue of one block: optional full rows, then the top-kcand of the block
+// (`_emit`), ordered by value desc, column asc.  The four rows
+// m0 + 16i + 4hh + r of one (i, r) are handled at once, one per 16-lane row;
+// each lane first sorts its four scores, then every round takes the row's
+// largest head, the lowest column among the lanes holding it, and advances
+// that lane.  value(i, r, t): the coarse score of row m0 + 16i + 4hh + r,
+// column 64b + 16t + nn.  Passes with r % rstep != rfirst are left to
+// another wave.  Slots past the block's valid columns get (-inf, -1).
 template <int MT, int MR, class Value>
 __device__ __forceinline__ void block_select(Value value, const CoarseArgs& A, int b, int hh, int nn,
                                              int rfirst = 0, int rstep = 1, int m0 = 0) {
@@ -189,57 +225,61 @@ __device__ __forceinline__ void block_select(Value value, const CoarseArgs& A, i
       if (r % rstep != rfirst) continue;
       const int m = m0 + 16 * i + 4 * hh + r;
       const bool row_ok = m < A.M;
-      float v[4];
+      uint32_t k[4], c[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int n = b * 64 + 16 * t + nn;
         const bool ok = row_ok && n < A.N;
-        const float c = value(i, r, t);
-        v[t] = ok ? c : NEG_INF;
-        if (A.coarse_out && ok) A.coarse_out[(size_t)m * A.N + n] = c;
+        const float s = value(i, r, t);
+        k[t] = ok ? f32_key(s + 0.0f) : 0u;   // -0 counts as +0, as in a float compare
+        c[t] = 16 * t + nn;
+        if (A.coarse_out && ok) A.coarse_out[(size_t)m * A.N + n] = s;
       }
-      float kv[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
-      int ki[4] = {-1, -1, -1, -1};
-      for (int c = 0; c < A.kcand; ++c) {
-        float bv = v[0];
-        int bn = nn;
+      auto ce = [&](int p, int q) {   // positions p < q: (key desc, column asc)
+        const bool sw = k[q] > k[p] || (k[q] == k[p] && c[q] < c[p]);
+        const uint32_t tk = k[p], tc = c[p];
+        k[p] = sw ? k[q] : k[p];
+        c[p] = sw ? c[q] : c[p];
+        k[q] = sw ? tk : k[q];
+        c[q] = sw ? tc : c[q];
+      };
+      ce(0, 1);
+      ce(2, 3);
+      ce(0, 2);
+      ce(1, 3);
+      ce(1, 2);
+      uint32_t kk[4] = {0u, 0u, 0u, 0u}, kc[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int t = 1; t < 4; ++t)
-          if (v[t] > bv) {
-            bv = v[t];
-            bn = 16 * t + nn;
+      for (int sl = 0; sl < 4; ++sl) {
+        if (16 * sl >= A.kcand) break;
+        const int nround = min(16, A.kcand - 16 * sl);
+        for (int cc = 0; cc < nround; ++cc) {
+          const uint32_t mx = row16_max(k[0]);
+          const uint32_t mc = row16_min(k[0] == mx ? c[0] : 64u);
+          if (c[0] == mc) {   // the winner's next score becomes its head
+            k[0] = k[1];
+            k[1] = k[2];
+            k[2] = k[3];
+            k[3] = 0u;
+            c[0] = c[1];
+            c[1] = c[2];
+            c[2] = c[3];
+            c[3] = 64u;
           }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          const float ov = __shfl_xor(bv, off, 16);
-          const int on = __shfl_xor(bn, off, 16);
-          if (ov > bv || (ov == bv && on < bn)) {
-            bv = ov;
-            bn = on;
+          if (cc == nn) {
+            kk[sl] = mx;
+            kc[sl] = mc;
           }
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (bn == 16 * t + nn) v[t] = NEG_INF;
-        if ((c & 15) == nn) {
-          const int slot = c >> 4;
-          const int id = (bv == NEG_INF) ? -1 : b * 64 + bn;
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            if (s == slot) {
-              kv[s] = bv;
-              ki[s] = id;
-            }
         }
       }
       if (row_ok) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int c = 16 * s + nn;
-          if (c < A.kcand) {
-            const size_t o = (size_t)m * ncand + (size_t)b * A.kcand + c;
-            A.cand_val[o] = kv[s];
-            A.cand_id[o] = ki[s];
+        for (int sl = 0; sl < 4; ++sl) {
+          const int cs = 16 * sl + nn;
+          if (cs < A.kcand) {
+            const size_t o = (size_t)m * ncand + (size_t)b * A.kcand + cs;
+            A.cand_val[o] = kk[sl] ? key_f32(kk[sl]) : NEG_INF;
+            A.cand_id[o] = kk[sl] ? b * 64 + (int)kc[sl] : -1;
           }
         }
       }
@@ -435,13 +475,17 @@ void coarse_resident_kernel(CoarseArgs A) {
 // between them and hide each other's latency; below that, one wave per block.
 //
 // Every global read of the main loop is a direct-to-LDS DMA.  Iteration j
-// (j < 0: the prologue) issues, in this order and every time, even where the
-// data does not exist (then a harmless copy into a free slot):
-//   X(j + XD)  the wave's chunks of that group's x slab             NX ops
-//   C(G + 1)   at j = 4G: its chunks of byte group G + 1's codes   NC ops
-//   B(G + 1)   at j = 4G + 1: its chunk of that zero-point slab    NB ops
-// so the number of ops issued after any op depends only on j mod 4, and each
-// iteration ends with one vmcnt wait whose count is a constant (big_wait).
+// (group j; j < 0: the prologue) issues, in this order and every time, even
+// where the data does not exist (then a harmless copy into a free slot):
+//   X(j + XD)  the wave's chunks of that group's x slab               NX ops
+//   at j = 4G + 1 (after every wave read byte group G's codes):
+//   C(G + 1)   the wave's chunks of byte group G + 1's codes/pairs    NC ops
+//   B(G + 1)   its chunk of byte group G + 1's zero-point slab       NB ops
+// and ends with one vmcnt wait that completes X(j + 2) and, at the end of a
+// byte group, C and B of the next one, then a barrier; so after iteration j
+// slab j + 2 is visible and iteration j + 1 can read the first x fragments of
+// group j + 2 before its own barrier.  The number of ops issued after any op
+// depends only on j mod 4, so every wait count is a constant (big_wait).
 // Completions are counted in issue order; with this order no wait for an x
 // slab (an L2 hit) waits for code bytes still on their way from HBM before
 // they are needed.
@@ -455,7 +499,7 @@ struct BigShape {
   static constexpr int MA = (MT + WPB - 1) / WPB;   // row tiles of part 0
   static constexpr int MB = MT - MA;                // row tiles of part 1
   static constexpr int W = 4 * WPB;                 // waves per workgroup
-  static constexpr int XD = MT >= 4 ? 3 : 4;        // x slabs requested ahead
+  static constexpr int XD = MT >= 4 ? 4 : 6;        // x slabs requested ahead
   // DMA ops per iteration of a wave of part p
   static constexpr int nx(int p) { return (4 * MT - 4 * p + W - 1) / W; }
   static constexpr int nc(int p) { return (kCodeChunks - p + WPB - 1) / WPB; }
@@ -463,7 +507,7 @@ struct BigShape {
 };
 
 constexpr size_t big_lds_bytes(int MT, int XD) {
-  return (size_t)(XD + 1) * 4096 * MT + (size_t)2 * 4 * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
+  return (size_t)(XD + 1) * 4096 * MT + (size_t)4 * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
 }
 
 // Workspace of one launch with MT row tiles: x slabs, then zero-point slabs.
@@ -472,34 +516,26 @@ size_t big_workspace_bytes(int MT, int K) {
 }
 
 // Ops a wave of part P may leave outstanding at the end of an iteration with
-// j mod 4 == Q: those issued after X(j + 1) and, for Q == 3, after the C and
-// B of the next byte group (issued at j - 3 and j - 2).  The prologue's final
-// wait (X(0), C(0), B(0)) is the Q == 3 case.
+// j mod 4 == Q: those issued after X(j + 2) and, for Q == 3, after the C and
+// B issued at j - 2.  The prologue's final wait (X(1), C(0), B(0)) is the
+// Q == 3 case.
 template <int MT, int P>
 constexpr int big_wait(int Q) {
   using S = BigShape<MT>;
-  auto ops = [](int j) {
-    const int q = ((j % 4) + 4) % 4;
-    return S::nx(P) + (q == 0 ? S::nc(P) : 0) + (q == 1 ? S::nb(P) : 0);
-  };
+  auto m4 = [](int j) { return ((j % 4) + 4) % 4; };
+  auto ops = [&](int j) { return S::nx(P) + (m4(j) == 1 ? S::nc(P) + S::nb(P) : 0); };
   int best = 1 << 20;
   if (S::nx(P)) {
-    const int j1 = Q + 1 - S::XD, q1 = ((j1 % 4) + 4) % 4;
-    int n = (q1 == 0 ? S::nc(P) : 0) + (q1 == 1 ? S::nb(P) : 0);
+    const int j1 = Q + 2 - S::XD;
+    int n = m4(j1) == 1 ? S::nc(P) + S::nb(P) : 0;
     for (int j = j1 + 1; j <= Q; ++j) n += ops(j);
     best = n < best ? n : best;
   }
   if (Q == 3) {
-    if (S::nc(P)) {
-      int n = 0;
-      for (int j = Q - 2; j <= Q; ++j) n += ops(j);
-      best = n < best ? n : best;
-    }
-    if (S::nb(P)) {
-      int n = 0;
-      for (int j = Q - 1; j <= Q; ++j) n += ops(j);
-      best = n < best ? n : best;
-    }
+    int tail = 0;   // ops of iterations Q - 1 and Q
+    for (int j = Q - 1; j <= Q; ++j) tail += ops(j);
+    if (S::nc(P)) best = S::nb(P) + tail < best ? S::nb(P) + tail : best;
+    if (S::nb(P)) best = tail < best ? tail : best;
   }
   return best;
 }
@@ -575,26 +611,34 @@ struct BigArgs {
 };
 
 // MFMA phase of one group (quarter Q) for MTW row tiles and the four column
-// tiles: cg = sum over the group's k of x 2^64 * v 2^(2Q-133).  A scheduling
-// barrier per k-slice keeps one slice's operands live at a time.
-// xb: this lane's fragment 0 (A row nn, k-slot hh) in the slab.
+// tiles: cg = sum over the group's k of x 2^64 * v 2^(2Q-133).  On entry a[0]
+// holds k-slice 0's x fragments; each slice's MFMAs issue while the next
+// slice's fragments are read (the last slice reads slice 0 of the next
+// group, from xn).  A scheduling barrier per slice keeps one slice's decoded
+// operands live at a time.  xb, xn: this lane's fragment 0 (A row nn, k-slot
+// hh) in this group's slab and the next one's.
 template <int MTW, int Q, int MP>
-__device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MTW][4], const u32x4 (&raw)[2][4],
-                                              const u32x4 (&raw8)[2][4], const u32x4* xb) {
+__device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MTW][4], u32x4 (&a)[2][MTW], const u32x4 (&raw)[2][4],
+                                              const u32x4 (&raw8)[2][4], const u32x4* xb, const u32x4* xn) {
   constexpr uint32_t mask = 0x00030003u << (2 * Q);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int h = ks >> 1, e = ks & 1;
-    u32x4 a[MTW];
+    if (ks < 3) {
+      const int f = (((ks + 1) >> 1) * 2 + ((ks + 1) & 1)) * 4;
 #pragma unroll
-    for (int i = 0; i < MTW; ++i) a[i] = xb[(h * 2 + e) * 4 * MP + 16 * i];
+      for (int i = 0; i < MTW; ++i) a[(ks + 1) & 1][i] = xb[f * MP + 16 * i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < MTW; ++i) a[0][i] = xn[16 * i];
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const bf16x8 bv = decode_quarter(raw[h][t][2 * e], raw8[h][t][2 * e], raw[h][t][2 * e + 1],
                                        raw8[h][t][2 * e + 1], mask);
 #pragma unroll
       for (int i = 0; i < MTW; ++i)
-        cg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]), bv,
+        cg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks & 1][i]), bv,
                                                            ks ? cg[i][t] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -611,8 +655,8 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   constexpr int MTW = P ? S::MB : S::MA, T0 = P ? S::MA : 0;
   const CoarseArgs& A = BA.c;
   u32x4* xs = reinterpret_cast<u32x4*>(smem);   // [NBUF][16][MP]
-  u32x4* cs = xs + NBUF * 16 * MP;              // [2 slots][4 blocks][9 chunks][64]
-  u32x4* zs = cs + 2 * 4 * kCodeChunks * 64;    // [256]
+  u32x4* cs = xs + NBUF * 16 * MP;              // [4 blocks][9 chunks][64]
+  u32x4* zs = cs + 4 * kCodeChunks * 64;        // [256]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -629,37 +673,32 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   const uint32_t xs_l = lds_addr(xs), zs_l = lds_addr(zs + wave * 64);
   const uint32_t cs_l = lds_addr(cs + lb * kCodeChunks * 64);
 
-  // Issue iteration j's ops.  Data that does not exist is replaced by a copy
-  // into a slot nothing reads before it is refilled: past the end, the last
-  // slab or byte group; before the start (X(j + XD) < 0 when XD < 4), slab
-  // j + XD + NBUF into the very slot that slab will be loaded to.
+  // Issue iteration j's ops.  Data past the end is replaced by a copy of the
+  // last slab or byte group into a slot nothing reads before the kernel ends.
   auto issue = [&](int j) {
     int gx = j + XD;
-    const uint32_t xslot = (uint32_t)(gx < 0 ? gx + NBUF : gx % NBUF);
-    gx = gx < 0 ? gx + NBUF : gx < NGRP ? gx : NGRP - 1;
+    const uint32_t xslot = (uint32_t)(gx % NBUF);
+    gx = gx < NGRP ? gx : NGRP - 1;
     const u32x4* xsrc = BA.xslab + (size_t)gx * 256 * MT;
 #pragma unroll
     for (int k = 0; k < S::nx(P); ++k) {   // chunks wave + W k, all below 4 MT
       const int c = wave + W * k;
       dma16(voff, xsrc + c * 64, xs_l + xslot * 4096 * MT + c * 1024);
     }
-    int G1 = (j >> 2) + 1;
-    const uint32_t cslot = (uint32_t)(G1 & 1);
-    G1 = G1 < NG4 ? G1 : NG4 - 1;
-    if ((j & 3) == 0) {
+    if ((j & 3) == 1) {
+      int G1 = (j >> 2) + 1;
+      G1 = G1 < NG4 ? G1 : NG4 - 1;
 #pragma unroll
       for (int k = 0; k < S::nc(P); ++k) {
         const int c = P + WPB * k;
-        dma16(voff, c < 8 ? tp + (G1 * 8 + c) * 64 : pp + G1 * 64,
-              cs_l + cslot * 4 * kCodeChunks * 1024 + c * 1024);
+        dma16(voff, c < 8 ? tp + (G1 * 8 + c) * 64 : pp + G1 * 64, cs_l + c * 1024);
       }
-    } else if ((j & 3) == 1 && S::nb(P)) {
-      dma16(voff, BA.zslab + (size_t)G1 * kZpEntries + lb * 64, zs_l);
+      if constexpr (S::nb(P) > 0) dma16(voff, BA.zslab + (size_t)G1 * kZpEntries + lb * 64, zs_l);
     }
   };
 
 #pragma unroll
-  for (int j = -4; j < 0; ++j) issue(j);
+  for (int j = -XD; j < 0; ++j) issue(j);
   wait_vm<big_wait<MT, P>(3)>();
   __syncthreads();
 
@@ -668,15 +707,22 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   for (int i = 0; i < MTW; ++i)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4* xl = xs + hh * MP + 16 * T0 + nn;   // this lane's fragment 0 in slab 0
+  u32x4 a[2][MTW];
+#pragma unroll
+  for (int i = 0; i < MTW; ++i) a[0][i] = xl[16 * i];
 
   for (int G = 0; G < NG4; ++G) {
-    const u32x4* cw = cs + ((G & 1) * 4 + lb) * kCodeChunks * 64;
-    const uint32_t* cp = reinterpret_cast<const uint32_t*>(cw + 512 + nn);   // pair (t, q) at 64 t + q
-    u32x4 raw[2][4];
+    // byte group G's codes and scale pairs, into registers (the slot is
+    // refilled with byte group G + 1 after this iteration's barrier)
+    const u32x4* cw = cs + lb * kCodeChunks * 64;
+    u32x4 raw[2][4], sz[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int t = 0; t < 4; ++t) raw[h][t] = cw[(h * 4 + t) * 64 + lane];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sz[t] = cw[512 + t * 16 + nn];
 
     // zero-point part of byte group G
     {
@@ -687,27 +733,19 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
 #pragma unroll
         for (int i = 0; i < MTW; ++i) za[i] = u32x4{0u, 0u, 0u, 0u};
       }
-      f32x4 zc[MTW][4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const u32x4 sz = cw[512 + t * 16 + nn];
         uint32_t d[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) d[q] = __float_as_uint(lo_bf16(sz[q]) - hi_bf16(sz[q]));
+        for (int q = 0; q < 4; ++q) d[q] = __float_as_uint(lo_bf16(sz[t][q]) - hi_bf16(sz[t][q]));
         const uint32_t p01 = (d[0] >> 16) | (d[1] & 0xFFFF0000u);
         const uint32_t p23 = (d[2] >> 16) | (d[3] & 0xFFFF0000u);
-        const u32x4 zb = hh == 0 ? u32x4{p01, p23, p01, p23}
-                                 : hh == 1 ? u32x4{p01, p23, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 zb = u32x4{p01, p23, p01, p23};   // slots 8..15 meet zero x parts
 #pragma unroll
         for (int i = 0; i < MTW; ++i)
-          zc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[i]),
-                                                            __builtin_bit_cast(bf16x8, zb),
-                                                            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[i]),
+                                                             __builtin_bit_cast(bf16x8, zb), acc[i][t], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < MTW; ++i)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][t] += zc[i][t];
     }
 
     u32x4 raw8[2][4];
@@ -717,10 +755,10 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       const int g = 4 * G + Q;
       issue(g);
       f32x4 cg[MTW][4];
-      big_group_mma<MTW, Q, MP>(cg, raw, raw8, xs + (g % NBUF) * 16 * MP + hh * MP + 16 * T0 + nn);
+      big_group_mma<MTW, Q, MP>(cg, a, raw, raw8, xl + (g % NBUF) * 16 * MP, xl + ((g + 1) % NBUF) * 16 * MP);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float Sq = quarter_scale(lo_bf16(cp[64 * t + Q]), Q);
+        const float Sq = quarter_scale(lo_bf16(sz[t][Q]), Q);
 #pragma unroll
         for (int i = 0; i < MTW; ++i)
 #pragma unroll
