@@ -204,83 +204,104 @@ __device__ __forceinline__ float key_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// (a & mask) | (b & ~mask): one bitfield-insert, and no branch.
+__device__ __forceinline__ uint32_t bsel(uint32_t mask, uint32_t a, uint32_t b) {
+  return (a & mask) | (b & ~mask);
+}
+
 // Epilogue of one block: optional full rows, then the top-kcand of the block
 // (`_emit`), ordered by value desc, column asc.  The four rows
-// m0 + 16i + 4hh + r of one (i, r) are handled at once, one per 16-lane row;
-// each lane first sorts its four scores, then every round takes the row's
-// largest head, the lowest column among the lanes holding it, and advances
-// that lane.  value(i, r, t): the coarse score of row m0 + 16i + 4hh + r,
-// column 64b + 16t + nn.  Passes with r % rstep != rfirst are left to
-// another wave.  Slots past the block's valid columns get (-inf, -1).
+// m0 + 16i + 4hh + r of one pass (i, r) are handled at once, one per 16-lane
+// row.  Each lane first sorts its four scores (stable, so equal scores keep
+// column order); every round then takes the row's largest head and the
+// lowest column among the lanes holding it, lane cc of the row keeps round
+// cc's result, and the winning lane advances.  Rounds are branch-free and up
+// to four passes run interleaved, so their cross-lane chains overlap.
+// value(i, r, t): the coarse score of row m0 + 16i + 4hh + r, column
+// 64b + 16t + nn.  Passes with r % rstep != rfirst are left to another wave.
+// Slots past the block's valid columns get (-inf, -1).
 template <int MT, int MR, class Value>
 __device__ __forceinline__ void block_select(Value value, const CoarseArgs& A, int b, int hh, int nn,
                                              int rfirst = 0, int rstep = 1, int m0 = 0) {
+  constexpr int NP = MT * MR, NB = NP < 4 ? NP : 4;   // passes, passes per batch
   const float NEG_INF = -__builtin_inff();
   const int ncand = A.nblk * A.kcand;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
+  for (int p0 = 0; p0 < NP; p0 += NB) {
+    uint32_t k[NB][4], c[NB][4], kk[NB][4], kc[NB][4];
+    bool live[NB];
 #pragma unroll
-    for (int r = 0; r < MR; ++r) {
-      if (m0 + 16 * i + r >= A.M) continue;  // no row of this (i, r) is live (wave-uniform)
-      if (r % rstep != rfirst) continue;
+    for (int j = 0; j < NB; ++j) {
+      const int pi = p0 + j, i = pi / MR, r = pi % MR;
+      live[j] = pi < NP && m0 + 16 * i + r < A.M && r % rstep == rfirst;   // wave-uniform
       const int m = m0 + 16 * i + 4 * hh + r;
-      const bool row_ok = m < A.M;
-      uint32_t k[4], c[4];
+      const bool row_ok = live[j] && m < A.M;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int n = b * 64 + 16 * t + nn;
         const bool ok = row_ok && n < A.N;
-        const float s = value(i, r, t);
-        k[t] = ok ? f32_key(s + 0.0f) : 0u;   // -0 counts as +0, as in a float compare
-        c[t] = 16 * t + nn;
-        if (A.coarse_out && ok) A.coarse_out[(size_t)m * A.N + n] = s;
+        const float sv = pi < NP ? value(i, r, t) : 0.f;
+        k[j][t] = ok ? f32_key(sv + 0.0f) : 0u;   // -0 counts as +0, as in a float compare
+        c[j][t] = 16 * t + nn;
+        kk[j][t] = 0u;
+        kc[j][t] = 0u;
+        if (A.coarse_out && ok) A.coarse_out[(size_t)m * A.N + n] = sv;
       }
-      auto ce = [&](int p, int q) {   // positions p < q: (key desc, column asc)
-        const bool sw = k[q] > k[p] || (k[q] == k[p] && c[q] < c[p]);
-        const uint32_t tk = k[p], tc = c[p];
-        k[p] = sw ? k[q] : k[p];
-        c[p] = sw ? c[q] : c[p];
-        k[q] = sw ? tk : k[q];
-        c[q] = sw ? tc : c[q];
+      auto ce = [&](int p) {   // neighbours p, p + 1: stable on equal keys
+        const uint32_t sw = k[j][p + 1] > k[j][p] ? ~0u : 0u;
+        const uint32_t tk = k[j][p], tc = c[j][p];
+        k[j][p] = bsel(sw, k[j][p + 1], tk);
+        c[j][p] = bsel(sw, c[j][p + 1], tc);
+        k[j][p + 1] = bsel(sw, tk, k[j][p + 1]);
+        c[j][p + 1] = bsel(sw, tc, c[j][p + 1]);
       };
-      ce(0, 1);
-      ce(2, 3);
-      ce(0, 2);
-      ce(1, 3);
-      ce(1, 2);
-      uint32_t kk[4] = {0u, 0u, 0u, 0u}, kc[4] = {0u, 0u, 0u, 0u};
+      ce(0);
+      ce(1);
+      ce(2);
+      ce(0);
+      ce(1);
+      ce(0);
+    }
+    bool any = false;
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        if (16 * sl >= A.kcand) break;
-        const int nround = min(16, A.kcand - 16 * sl);
-        for (int cc = 0; cc < nround; ++cc) {
-          const uint32_t mx = row16_max(k[0]);
-          const uint32_t mc = row16_min(k[0] == mx ? c[0] : 64u);
-          if (c[0] == mc) {   // the winner's next score becomes its head
-            k[0] = k[1];
-            k[1] = k[2];
-            k[2] = k[3];
-            k[3] = 0u;
-            c[0] = c[1];
-            c[1] = c[2];
-            c[2] = c[3];
-            c[3] = 64u;
-          }
-          if (cc == nn) {
-            kk[sl] = mx;
-            kc[sl] = mc;
-          }
+    for (int j = 0; j < NB; ++j) any |= live[j];
+    if (!any) continue;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      if (16 * sl >= A.kcand) break;
+      const int nround = min(16, A.kcand - 16 * sl);
+      for (int cc = 0; cc < nround; ++cc) {
+        const uint32_t own = cc == nn ? ~0u : 0u;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const uint32_t mx = row16_max(k[j][0]);
+          const uint32_t mc = row16_min(k[j][0] == mx ? c[j][0] : 64u);
+          const uint32_t win = c[j][0] == mc ? ~0u : 0u;   // the winner's next score becomes its head
+          k[j][0] = bsel(win, k[j][1], k[j][0]);
+          k[j][1] = bsel(win, k[j][2], k[j][1]);
+          k[j][2] = bsel(win, k[j][3], k[j][2]);
+          k[j][3] = k[j][3] & ~win;
+          c[j][0] = bsel(win, c[j][1], c[j][0]);
+          c[j][1] = bsel(win, c[j][2], c[j][1]);
+          c[j][2] = bsel(win, c[j][3], c[j][2]);
+          c[j][3] = bsel(win, 64u, c[j][3]);
+          kk[j][sl] = bsel(own, mx, kk[j][sl]);
+          kc[j][sl] = bsel(own, mc, kc[j][sl]);
         }
       }
-      if (row_ok) {
+    }
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-          const int cs = 16 * sl + nn;
-          if (cs < A.kcand) {
-            const size_t o = (size_t)m * ncand + (size_t)b * A.kcand + cs;
-            A.cand_val[o] = kk[sl] ? key_f32(kk[sl]) : NEG_INF;
-            A.cand_id[o] = kk[sl] ? b * 64 + (int)kc[sl] : -1;
-          }
+    for (int j = 0; j < NB; ++j) {
+      const int pi = p0 + j, i = pi / MR, r = pi % MR;
+      const int m = m0 + 16 * i + 4 * hh + r;
+      if (!live[j] || m >= A.M) continue;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int cs = 16 * sl + nn;
+        if (cs < A.kcand) {
+          const size_t o = (size_t)m * ncand + (size_t)b * A.kcand + cs;
+          A.cand_val[o] = kk[j][sl] ? key_f32(kk[j][sl]) : NEG_INF;
+          A.cand_id[o] = kk[j][sl] ? b * 64 + (int)kc[j][sl] : -1;
         }
       }
     }
@@ -476,19 +497,19 @@ void coarse_resident_kernel(CoarseArgs A) {
 //
 // Every global read of the main loop is a direct-to-LDS DMA.  Iteration j
 // (group j; j < 0: the prologue) issues, in this order and every time, even
-// where the data does not exist (then a harmless copy into a free slot):
+// where the data does not exist (then a harmless copy into a slot that is
+// free, or that later receives the same bytes):
 //   X(j + XD)  the wave's chunks of that group's x slab               NX ops
 //   at j = 4G + 1 (after every wave read byte group G's codes):
-//   C(G + 1)   the wave's chunks of byte group G + 1's codes/pairs    NC ops
+//   C(G + CD)  the wave's chunks of that byte group's codes/pairs     NC ops
 //   B(G + 1)   its chunk of byte group G + 1's zero-point slab       NB ops
-// and ends with one vmcnt wait that completes X(j + 2) and, at the end of a
-// byte group, C and B of the next one, then a barrier; so after iteration j
-// slab j + 2 is visible and iteration j + 1 can read the first x fragments of
-// group j + 2 before its own barrier.  The number of ops issued after any op
-// depends only on j mod 4, so every wait count is a constant (big_wait).
-// Completions are counted in issue order; with this order no wait for an x
-// slab (an L2 hit) waits for code bytes still on their way from HBM before
-// they are needed.
+// and ends with one vmcnt wait that completes X(j + XW) and, at the end of a
+// byte group, C and B of the next one, then a barrier.  With XW = 2 the
+// next group's first x fragments are read before that barrier.  The number
+// of ops issued after any op depends only on j mod 4, so every wait count is
+// a constant (big_wait).  Completions are counted in issue order; with this
+// order no wait for an x slab (an L2 hit) waits for code bytes still on their
+// way from HBM before they are needed.
 constexpr int kMaxMT = 5;            // 16-row tiles per launch (80 rows)
 constexpr int kCodeChunks = 9;       // 1 KB chunks of one block's byte group: 8 code + 1 pair
 constexpr int kZpEntries = 256;      // zero-point slab entries (16 bytes)
@@ -499,15 +520,18 @@ struct BigShape {
   static constexpr int MA = (MT + WPB - 1) / WPB;   // row tiles of part 0
   static constexpr int MB = MT - MA;                // row tiles of part 1
   static constexpr int W = 4 * WPB;                 // waves per workgroup
-  static constexpr int XD = MT >= 4 ? 4 : 6;        // x slabs requested ahead
+  static constexpr int XD = MT >= 4 ? 3 : MT == 3 ? 5 : 6;   // x slabs requested ahead
+  static constexpr int CD = 2;                      // byte groups of codes requested ahead
+  static constexpr int XW = XD >= 4 ? 2 : 1;        // slab completed XW groups ahead
+  static constexpr int PRO = XD > 4 * CD - 1 ? XD : 4 * CD - 1;   // prologue iterations
   // DMA ops per iteration of a wave of part p
   static constexpr int nx(int p) { return (4 * MT - 4 * p + W - 1) / W; }
   static constexpr int nc(int p) { return (kCodeChunks - p + WPB - 1) / WPB; }
   static constexpr int nb(int p) { return p == 0 ? 1 : 0; }
 };
 
-constexpr size_t big_lds_bytes(int MT, int XD) {
-  return (size_t)(XD + 1) * 4096 * MT + (size_t)4 * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
+constexpr size_t big_lds_bytes(int MT, int XD, int CD) {
+  return (size_t)(XD + 1) * 4096 * MT + (size_t)CD * 4 * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
 }
 
 // Workspace of one launch with MT row tiles: x slabs, then zero-point slabs.
@@ -516,26 +540,26 @@ size_t big_workspace_bytes(int MT, int K) {
 }
 
 // Ops a wave of part P may leave outstanding at the end of an iteration with
-// j mod 4 == Q: those issued after X(j + 2) and, for Q == 3, after the C and
-// B issued at j - 2.  The prologue's final wait (X(1), C(0), B(0)) is the
-// Q == 3 case.
+// j mod 4 == Q: those issued after X(j + XW) and, for Q == 3, after the C and
+// B of the next byte group (issued at j + 2 - 4 CD and j - 2).  The
+// prologue's final wait (X(XW - 1), C(0), B(0)) is the Q == 3 case.
 template <int MT, int P>
 constexpr int big_wait(int Q) {
   using S = BigShape<MT>;
   auto m4 = [](int j) { return ((j % 4) + 4) % 4; };
-  auto ops = [&](int j) { return S::nx(P) + (m4(j) == 1 ? S::nc(P) + S::nb(P) : 0); };
+  auto cb = [&](int j) { return m4(j) == 1 ? S::nc(P) + S::nb(P) : 0; };
+  auto ops = [&](int j) { return S::nx(P) + cb(j); };
+  auto after = [&](int j0, int in_iter) {   // ops after one issued in iteration j0
+    int n = in_iter;
+    for (int j = j0 + 1; j <= Q; ++j) n += ops(j);
+    return n;
+  };
   int best = 1 << 20;
-  if (S::nx(P)) {
-    const int j1 = Q + 2 - S::XD;
-    int n = m4(j1) == 1 ? S::nc(P) + S::nb(P) : 0;
-    for (int j = j1 + 1; j <= Q; ++j) n += ops(j);
-    best = n < best ? n : best;
-  }
+  auto take = [&](int n) { best = n < best ? n : best; };
+  if (S::nx(P)) take(after(Q + S::XW - S::XD, cb(Q + S::XW - S::XD)));
   if (Q == 3) {
-    int tail = 0;   // ops of iterations Q - 1 and Q
-    for (int j = Q - 1; j <= Q; ++j) tail += ops(j);
-    if (S::nc(P)) best = S::nb(P) + tail < best ? S::nb(P) + tail : best;
-    if (S::nb(P)) best = tail < best ? tail : best;
+    if (S::nc(P)) take(after(Q + 2 - 4 * S::CD, S::nb(P)));
+    if (S::nb(P)) take(after(Q - 2, 0));
   }
   return best;
 }
@@ -613,11 +637,11 @@ struct BigArgs {
 // MFMA phase of one group (quarter Q) for MTW row tiles and the four column
 // tiles: cg = sum over the group's k of x 2^64 * v 2^(2Q-133).  On entry a[0]
 // holds k-slice 0's x fragments; each slice's MFMAs issue while the next
-// slice's fragments are read (the last slice reads slice 0 of the next
-// group, from xn).  A scheduling barrier per slice keeps one slice's decoded
+// slice's fragments are read (with kNext the last slice reads slice 0 of the
+// next group, from xn).  A scheduling barrier per slice keeps one slice's decoded
 // operands live at a time.  xb, xn: this lane's fragment 0 (A row nn, k-slot
 // hh) in this group's slab and the next one's.
-template <int MTW, int Q, int MP>
+template <int MTW, int Q, int MP, bool kNext>
 __device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MTW][4], u32x4 (&a)[2][MTW], const u32x4 (&raw)[2][4],
                                               const u32x4 (&raw8)[2][4], const u32x4* xb, const u32x4* xn) {
   constexpr uint32_t mask = 0x00030003u << (2 * Q);
@@ -628,7 +652,7 @@ __device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MTW][4], u32x4 (&a)[2]
       const int f = (((ks + 1) >> 1) * 2 + ((ks + 1) & 1)) * 4;
 #pragma unroll
       for (int i = 0; i < MTW; ++i) a[(ks + 1) & 1][i] = xb[f * MP + 16 * i];
-    } else {
+    } else if (kNext) {
 #pragma unroll
       for (int i = 0; i < MTW; ++i) a[0][i] = xn[16 * i];
     }
@@ -651,12 +675,12 @@ __device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MTW][4], u32x4 (&a)[2]
 template <int MT, int P>
 __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem) {
   using S = BigShape<MT>;
-  constexpr int MP = 16 * MT, XD = S::XD, NBUF = XD + 1, W = S::W, WPB = S::WPB;
+  constexpr int MP = 16 * MT, XD = S::XD, NBUF = XD + 1, W = S::W, WPB = S::WPB, CD = S::CD;
   constexpr int MTW = P ? S::MB : S::MA, T0 = P ? S::MA : 0;
   const CoarseArgs& A = BA.c;
   u32x4* xs = reinterpret_cast<u32x4*>(smem);   // [NBUF][16][MP]
-  u32x4* cs = xs + NBUF * 16 * MP;              // [4 blocks][9 chunks][64]
-  u32x4* zs = cs + 4 * kCodeChunks * 64;        // [256]
+  u32x4* cs = xs + NBUF * 16 * MP;              // [CD slots][4 blocks][9 chunks][64]
+  u32x4* zs = cs + CD * 4 * kCodeChunks * 64;   // [256]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -674,9 +698,12 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   const uint32_t cs_l = lds_addr(cs + lb * kCodeChunks * 64);
 
   // Issue iteration j's ops.  Data past the end is replaced by a copy of the
-  // last slab or byte group into a slot nothing reads before the kernel ends.
+  // last slab or byte group into a slot nothing reads before the kernel ends;
+  // data before the start (prologue iterations ahead of X(0) or B(0)) by the
+  // bytes its slot is about to receive.
   auto issue = [&](int j) {
     int gx = j + XD;
+    gx = gx < 0 ? gx + NBUF : gx;
     const uint32_t xslot = (uint32_t)(gx % NBUF);
     gx = gx < NGRP ? gx : NGRP - 1;
     const u32x4* xsrc = BA.xslab + (size_t)gx * 256 * MT;
@@ -686,19 +713,23 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       dma16(voff, xsrc + c * 64, xs_l + xslot * 4096 * MT + c * 1024);
     }
     if ((j & 3) == 1) {
-      int G1 = (j >> 2) + 1;
-      G1 = G1 < NG4 ? G1 : NG4 - 1;
+      int GC = (j >> 2) + CD;   // never negative: the prologue starts at 1 - 4 CD or before
+      const uint32_t cslot = (uint32_t)(GC % CD);
+      GC = GC < NG4 ? GC : NG4 - 1;
 #pragma unroll
       for (int k = 0; k < S::nc(P); ++k) {
         const int c = P + WPB * k;
-        dma16(voff, c < 8 ? tp + (G1 * 8 + c) * 64 : pp + G1 * 64, cs_l + c * 1024);
+        dma16(voff, c < 8 ? tp + (GC * 8 + c) * 64 : pp + GC * 64,
+              cs_l + cslot * 4 * kCodeChunks * 1024 + c * 1024);
       }
-      if constexpr (S::nb(P) > 0) dma16(voff, BA.zslab + (size_t)G1 * kZpEntries + lb * 64, zs_l);
+      int GB = (j >> 2) + 1;
+      GB = GB < 0 ? 0 : GB < NG4 ? GB : NG4 - 1;
+      if constexpr (S::nb(P) > 0) dma16(voff, BA.zslab + (size_t)GB * kZpEntries + lb * 64, zs_l);
     }
   };
 
 #pragma unroll
-  for (int j = -XD; j < 0; ++j) issue(j);
+  for (int j = -S::PRO; j < 0; ++j) issue(j);
   wait_vm<big_wait<MT, P>(3)>();
   __syncthreads();
 
@@ -714,8 +745,8 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
 
   for (int G = 0; G < NG4; ++G) {
     // byte group G's codes and scale pairs, into registers (the slot is
-    // refilled with byte group G + 1 after this iteration's barrier)
-    const u32x4* cw = cs + lb * kCodeChunks * 64;
+    // refilled with byte group G + CD after this iteration's barrier)
+    const u32x4* cw = cs + ((G % CD) * 4 + lb) * kCodeChunks * 64;
     u32x4 raw[2][4], sz[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -755,7 +786,8 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       const int g = 4 * G + Q;
       issue(g);
       f32x4 cg[MTW][4];
-      big_group_mma<MTW, Q, MP>(cg, a, raw, raw8, xl + (g % NBUF) * 16 * MP, xl + ((g + 1) % NBUF) * 16 * MP);
+      big_group_mma<MTW, Q, MP, S::XW == 2>(cg, a, raw, raw8, xl + (g % NBUF) * 16 * MP,
+                                            xl + ((g + 1) % NBUF) * 16 * MP);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const float Sq = quarter_scale(lo_bf16(sz[t][Q]), Q);
@@ -766,6 +798,10 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       }
       wait_vm<big_wait<MT, P>(Q)>();
       __syncthreads();
+      if constexpr (S::XW == 1) {   // the next group's first fragments, now visible
+#pragma unroll
+        for (int i = 0; i < MTW; ++i) a[0][i] = xl[((g + 1) % NBUF) * 16 * MP + 16 * i];
+      }
     };
     group(std::integral_constant<int, 0>{});
     group(std::integral_constant<int, 1>{});
@@ -1522,7 +1558,7 @@ hipError_t launch_resident(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hi
 
 template <int MT>
 hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD);
+  constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD, BigShape<MT>::CD);
   static_assert(lds <= kMaxLds, "LDS budget of the many-row kernel");
   static bool attr_set = false;
   if (!attr_set) {
