@@ -167,10 +167,10 @@ def draft_head_workspace_bytes(M: int, K: int) -> int:
 
 
 def workspace_for(M: int, K: int, device):
-    """A device workspace for M rows of length K (None when none is needed)."""
+    """A device workspace for M rows of length K (zero-filled once; the library
+    keeps the parts that must start at zero at zero)."""
     import torch
-    n = draft_head_workspace_bytes(M, K)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    return torch.zeros(draft_head_workspace_bytes(M, K), dtype=torch.uint8, device=device)
 
 
 def _ws(workspace):

@@ -87,7 +87,13 @@ struct CoarseArgs {
   float* cand_val;
   int32_t* cand_id;
   float* coarse_out;
+  uint32_t* cnt;   // per-row arrival counters of the rerank; workgroup 0 zeroes cnt[0..ncnt)
+  int ncnt;
 };
+
+__device__ __forceinline__ void zero_counters(const CoarseArgs& A) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < A.ncnt) A.cnt[threadIdx.x] = 0u;
+}
 
 // One group: MFMAs of the (h, e) fragments for all tiles, then the scale update.
 // `xb` points at this lane's fragment 0 of the group (A row nn, k-slot hh),
@@ -373,6 +379,7 @@ void coarse_resident_kernel(CoarseArgs A) {
   const int lblk = wave / kWavesPerBlock, part = wave % kWavesPerBlock;
   const int b = blockIdx.x * kBlocks + lblk;
   const bool blk_ok = b < A.nblk;
+  zero_counters(A);
 
   // A wave past the last block reads block 0 (valid memory) and writes nothing.
   const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512 + NT * part * 64;
@@ -689,6 +696,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   const int b = blockIdx.x * 4 + lb;
   const bool blk_ok = b < A.nblk;
   const int NG4 = A.K >> 9, NGRP = A.K >> 7;
+  if constexpr (P == 0) zero_counters(A);
 
   // A block past the last one streams block 0 (valid memory) and writes nothing.
   const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
@@ -1222,23 +1230,8 @@ __global__ __launch_bounds__(kSelThreads) void rerank_kernel(
 //   2. Wave 0 tests the kcand candidates of each such block against T; the
 //      survivors (every key >= T: at least R) are sorted, and the first R are
 //      the row top-R.
-//   Meanwhile waves 1.. stage the x row in LDS.
-//   3. Exact logits: each wave takes kFastRows selected rows of W at once, all
-//      their loads in flight before any is used; with kArgmax the workgroup
-//      then writes the final token as argmax_kernel would.
-constexpr int kFastThreads = 512;
-constexpr int kFastWaves = kFastThreads / 64;
 constexpr int kFastNV = 32;        // block maxima per lane of wave 0: nblk <= 2048
-constexpr int kFastRows = 4;       // rows of W per wave in flight
 constexpr int kSurvBatch = 4;      // survivor loads per lane in flight
-
-struct FastShared {
-  unsigned int hist[256];
-  int qual[DH_MAX_R];
-  unsigned long long keys[DH_MAX_R];
-  float vals[DH_MAX_R];
-  int ns;
-};
 
 __device__ __forceinline__ unsigned long long slot_key(float v, int slot) {
   if (v == -__builtin_inff()) return 0ull;   // padding slot
@@ -1329,23 +1322,38 @@ __device__ unsigned long long wave_top2_threshold(const unsigned long long (&v)[
   return __shfl(r ? e[1] : e[0], l, 64);
 }
 
+// Rerank across many workgroups: grid (ceil(R / 4), M), four waves each.  Every
+// workgroup of row m repeats the block-maximum selection above (wave 0; the
+// same list in every workgroup), then each of its waves computes the exact
+// logit of one rank, r = 4 * blockIdx.x + wave, so the R rows of W are read
+// by R waves at once.  With kArgmax the last workgroup of the row to finish
+// (a per-row arrival counter, zeroed by the coarse kernel of the same call
+// and reset here) takes the argmax over the R logits.
+constexpr int kWideThreads = 256;
+constexpr int kWideDot = 10;       // 16-byte loads of x and of W in flight per lane
+
+struct WideShared {
+  unsigned int hist[256];
+  int qual[DH_MAX_R];
+  unsigned long long keys[DH_MAX_R];
+  int ns;
+  int last;
+};
+
 template <bool kArgmax>
-__global__ __launch_bounds__(kFastThreads) void rerank_fast_kernel(
+__global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t ldw, int K, int N,
     const float* __restrict__ cand_val, const int32_t* __restrict__ cand_id, int nblk, int kcand, int R,
     int32_t* __restrict__ rr_id, float* __restrict__ rr_val, int32_t* __restrict__ out_id,
-    float* __restrict__ out_val) {
-  extern __shared__ __align__(16) unsigned char fast_dyn[];   // the x row, K bf16
-  __shared__ FastShared sh;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(fast_dyn);
-  const int m = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    float* __restrict__ out_val, uint32_t* __restrict__ cnt) {
+  __shared__ WideShared sh;
+  const int m = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ncand = nblk * kcand;
   const float* cv = cand_val + (size_t)m * ncand;
   const int32_t* ci = cand_id + (size_t)m * ncand;
-  const uint16_t* xr = x + (size_t)m * K;
 
   if (wave == 0) {
-    // 1. T = the R-th largest block maximum
+    // the R-th largest block maximum as threshold, then the candidates >= it
     float mv[kFastNV];
 #pragma unroll
     for (int j = 0; j < kFastNV; ++j) mv[j] = cv[min(lane + 64 * j, nblk - 1) * kcand];   // clamped loads
@@ -1355,8 +1363,6 @@ __global__ __launch_bounds__(kFastThreads) void rerank_fast_kernel(
       const int b = lane + 64 * j;
       mk[j] = b < nblk ? slot_key(mv[j], b * kcand) : 0ull;
     }
-    // a quick threshold first; the exact R-th largest block maximum when the
-    // quick one lets too many blocks through for the survivor buffer
     unsigned long long T = R <= 128 ? wave_top2_threshold(mk, R) : 0ull;
     int nq = 0;
     if (T) {
@@ -1364,7 +1370,6 @@ __global__ __launch_bounds__(kFastThreads) void rerank_fast_kernel(
       for (int j = 0; j < kFastNV; ++j) nq += __popcll(__ballot(mk[j] != 0ull && mk[j] >= T));
     }
     if (!T || nq * kcand > DH_MAX_R) T = wave_kth_largest(mk, R, sh.hist);
-    // the blocks whose maximum is >= T (at least R), in block order
     nq = 0;
 #pragma unroll
     for (int j = 0; j < kFastNV; ++j) {
@@ -1373,7 +1378,6 @@ __global__ __launch_bounds__(kFastThreads) void rerank_fast_kernel(
       if (q) sh.qual[nq + lane_prefix(bal)] = lane + 64 * j;
       nq += __popcll(bal);
     }
-    // 2. survivors: the candidates >= T of those blocks
     const int items = nq * kcand;
     int ns = 0;
     for (int i0 = 0; i0 < items; i0 += 64 * kSurvBatch) {
@@ -1397,64 +1401,58 @@ __global__ __launch_bounds__(kFastThreads) void rerank_fast_kernel(
       }
     }
     if (lane == 0) sh.ns = ns;
-  } else {
-    for (int i = tid - 64; i < K / 8; i += kFastThreads - 64)
-      reinterpret_cast<u32x4*>(xs)[i] = reinterpret_cast<const u32x4*>(xr)[i];
   }
   __syncthreads();
-  const int ns = sh.ns;   // R <= ns <= R * kcand <= DH_MAX_R
-  sort_desc<kFastThreads>(sh.keys, ns);
-  for (int r = tid; r < R; r += kFastThreads) rr_id[(size_t)m * R + r] = (int32_t)key_id(sh.keys[r]);
+  sort_desc<kWideThreads>(sh.keys, sh.ns);   // R <= ns <= R * kcand <= DH_MAX_R
 
-  // 3. exact logits, kFastRows rows per wave at a time
-  constexpr int kDotUnroll = 10;
-  for (int r0 = wave * kFastRows; r0 < R; r0 += kFastWaves * kFastRows) {
-    const uint16_t* wr[kFastRows];
+  // the exact logit of rank r: this wave reads W[id] and x[m] once, all loads in flight
+  const int r = 4 * blockIdx.x + wave;
+  if (r < R) {
+    const uint32_t id = key_id(sh.keys[r]);
+    const uint16_t* wr = w + (size_t)id * ldw;
+    const uint16_t* xr = x + (size_t)m * K;
+    float s0 = 0.f, s1 = 0.f;
+    for (int k0 = 0; k0 < K; k0 += 512 * kWideDot) {
+      u32x4 wv[kWideDot], xv[kWideDot];
 #pragma unroll
-    for (int t = 0; t < kFastRows; ++t) wr[t] = w + (size_t)key_id(sh.keys[min(r0 + t, R - 1)]) * ldw;
-    float s0[kFastRows], s1[kFastRows];
+      for (int j = 0; j < kWideDot; ++j) {   // clamped, unconditional loads
+        const int k = min(k0 + 512 * j + lane * 8, K - 8);
+        wv[j] = *reinterpret_cast<const u32x4*>(wr + k);
+        xv[j] = *reinterpret_cast<const u32x4*>(xr + k);
+      }
 #pragma unroll
-    for (int t = 0; t < kFastRows; ++t) s0[t] = s1[t] = 0.f;
-    for (int k0 = 0; k0 < K; k0 += 512 * kDotUnroll) {
-      u32x4 wv[kFastRows][kDotUnroll];
+      for (int j = 0; j < kWideDot; ++j) {
+        if (k0 + 512 * j + lane * 8 < K) {
 #pragma unroll
-      for (int j = 0; j < kDotUnroll; ++j)
-#pragma unroll
-        for (int t = 0; t < kFastRows; ++t)   // clamped, unconditional loads
-          wv[t][j] = *reinterpret_cast<const u32x4*>(wr[t] + min(k0 + 512 * j + lane * 8, K - 8));
-#pragma unroll
-      for (int j = 0; j < kDotUnroll; ++j) {
-        const int k = k0 + 512 * j + lane * 8;
-        if (k < K) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + k);
-#pragma unroll
-          for (int t = 0; t < kFastRows; ++t)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              s0[t] = __builtin_fmaf(lo_bf16(xv[c]), lo_bf16(wv[t][j][c]), s0[t]);
-              s1[t] = __builtin_fmaf(hi_bf16(xv[c]), hi_bf16(wv[t][j][c]), s1[t]);
-            }
+          for (int c = 0; c < 4; ++c) {
+            s0 = __builtin_fmaf(lo_bf16(xv[j][c]), lo_bf16(wv[j][c]), s0);
+            s1 = __builtin_fmaf(hi_bf16(xv[j][c]), hi_bf16(wv[j][c]), s1);
+          }
         }
       }
     }
-#pragma unroll
-    for (int t = 0; t < kFastRows; ++t) {
-      float sum = s0[t] + s1[t];
-      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-      if (lane == 0 && r0 + t < R) {
-        rr_val[(size_t)m * R + r0 + t] = sum;
-        sh.vals[r0 + t] = sum;
-      }
+    float sum = s0 + s1;
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) {
+      rr_id[(size_t)m * R + r] = (int32_t)id;
+      rr_val[(size_t)m * R + r] = sum;
     }
   }
   if constexpr (kArgmax) {
     __syncthreads();
-    if (wave == 0) {
+    if (tid == 0) {
+      __threadfence();   // this workgroup's logits are visible before it is counted
+      const uint32_t old = atomicAdd(cnt + m, 1u);
+      sh.last = old == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (sh.last && wave == 0) {
+      __threadfence();
       float bv = -__builtin_inff();
       int bi = -1;
-      for (int r = lane; r < R; r += 64) {
-        const int id = (int)key_id(sh.keys[r]);
-        const float v = sh.vals[r];
+      for (int q = lane; q < R; q += 64) {
+        const int id = __hip_atomic_load(rr_id + (size_t)m * R + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float v = __hip_atomic_load(rr_val + (size_t)m * R + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (bi < 0 || v > bv || (v == bv && id < bi)) {
           bv = v;
           bi = id;
@@ -1471,6 +1469,7 @@ __global__ __launch_bounds__(kFastThreads) void rerank_fast_kernel(
       if (lane == 0) {
         out_id[m] = bi;
         out_val[m] = bv;
+        cnt[m] = 0u;   // ready for the next call
       }
     }
   }
@@ -1578,9 +1577,13 @@ int resident_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 // workspace); every other M the many-row kernel, in launches of up to 80 rows.
 bool use_resident(int M, int K) { return M <= 8 && resident_lds_bytes(K, resident_rows(M)) <= kMaxLds; }
 
+// Workspace: the rerank's per-row arrival counters, then (many-row kernel
+// only) the x of one launch.
+constexpr size_t kCounterBytes = DH_MAX_M * sizeof(uint32_t);
+
 size_t coarse_workspace_bytes(int M, int K) {
-  if (use_resident(M, K)) return 0;
-  return big_workspace_bytes(std::min((M + 15) / 16, kMaxMT), K);
+  if (use_resident(M, K)) return kCounterBytes;
+  return kCounterBytes + big_workspace_bytes(std::min((M + 15) / 16, kMaxMT), K);
 }
 
 int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
@@ -1597,7 +1600,7 @@ int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, co
   if (!aligned16(x) || !aligned16(tiled) || !aligned16(pairs))
     return dh::fail(DH_EINVAL, "coarse: x, tiled and pairs must be 16-byte aligned");
   const size_t need = coarse_workspace_bytes(M, K);
-  if (need && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need)
     return dh::fail(DH_EINVAL, "coarse: M=%d, K=%d needs a 16-byte aligned workspace of %zu bytes (got %p, %zu)",
                     M, K, need, workspace, workspace_bytes);
   return DH_OK;
@@ -1637,7 +1640,8 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
   const int nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
   const int ncand = nblk * kcand;
   CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
-               reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out};
+               reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out,
+               static_cast<uint32_t*>(workspace), M};
   hipError_t e = hipSuccess;
   if (use_resident(M, K)) {
     switch (resident_rows(M)) {
@@ -1659,8 +1663,9 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
     B.cand_val = cand_val + (size_t)m0 * ncand;
     B.cand_id = cand_id + (size_t)m0 * ncand;
     B.coarse_out = coarse_out ? coarse_out + (size_t)m0 * N : nullptr;
+    B.ncnt = m0 == 0 ? M : 0;
     const int mt = (B.M + 15) / 16, mp = 16 * mt;
-    u32x4* xslab = static_cast<u32x4*>(workspace);
+    u32x4* xslab = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(workspace) + kCounterBytes);
     u32x4* zslab = xslab + (size_t)(K / DH_GROUP) * 256 * mt;
     hipLaunchKernelGGL(prep_x_kernel, dim3((mp * NG4 * 16 + 255) / 256), dim3(256), 0, s, B.x, B.M, mp, K, xslab,
                        zslab);
@@ -1693,19 +1698,12 @@ bool fast_rerank(int N, int ncand, int R, int& nblk, int& kcand) {
 }
 
 template <bool kArgmax>
-hipError_t launch_fast(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
+hipError_t launch_wide(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
                        const int32_t* cand_id, int nblk, int kcand, int R, int32_t* rr_id, float* rr_val,
-                       int32_t* out_id, float* out_val, hipStream_t s) {
-  static bool attr_set = false;   // the x row: up to DH_MAX_K bf16 = 128 KiB
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rerank_fast_kernel<kArgmax>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, DH_MAX_K * 2);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(rerank_fast_kernel<kArgmax>, dim3(M), dim3(kFastThreads), (size_t)K * 2, s,
+                       int32_t* out_id, float* out_val, uint32_t* cnt, hipStream_t s) {
+  hipLaunchKernelGGL(rerank_wide_kernel<kArgmax>, dim3((R + 3) / 4, M), dim3(kWideThreads), 0, s,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), ldw, K, N, cand_val,
-                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val);
+                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, cnt);
   return hipGetLastError();
 }
 
@@ -1713,9 +1711,9 @@ int launch_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N
                   const int32_t* cand_id, int ncand, int R, int32_t* rr_id, float* rr_val, hipStream_t s) {
   int nblk, kcand;
   if (fast_rerank(N, ncand, R, nblk, kcand)) {
-    hipError_t e = launch_fast<false>(x, w, ldw, M, K, N, cand_val, cand_id, nblk, kcand, R, rr_id, rr_val,
-                                      nullptr, nullptr, s);
-    if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_fast_kernel: %s", hipGetErrorString(e));
+    hipError_t e = launch_wide<false>(x, w, ldw, M, K, N, cand_val, cand_id, nblk, kcand, R, rr_id, rr_val,
+                                      nullptr, nullptr, nullptr, s);
+    if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_wide_kernel: %s", hipGetErrorString(e));
     return dh::ok();
   }
   hipLaunchKernelGGL(rerank_kernel, dim3(M), dim3(kSelThreads), 0, s, static_cast<const uint16_t*>(x),
@@ -1785,9 +1783,9 @@ int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
     return rc;
   int nblk, kc;
   if (fast_rerank(N, ncand, R, nblk, kc)) {   // rerank and argmax in one kernel
-    hipError_t e = launch_fast<true>(x, w, ldw, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val, out_id,
-                                     out_val, s);
-    if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_fast_kernel: %s", hipGetErrorString(e));
+    hipError_t e = launch_wide<true>(x, w, ldw, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val, out_id,
+                                     out_val, static_cast<uint32_t*>(workspace), s);
+    if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_wide_kernel: %s", hipGetErrorString(e));
     return dh::ok();
   }
   if ((rc = launch_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, s))) return rc;

@@ -20,8 +20,9 @@
  *   - All argument validation happens before any HIP call, so every error
  *     except DH_EHIP can be provoked without a GPU.
  *   - The caller owns every buffer.  The library allocates no device memory
- *     and keeps no state between calls; where the coarse pass needs scratch
- *     memory (more than 8 rows), the caller passes it in as a workspace of
+ *     and keeps no state between calls; the scratch memory the coarse pass
+ *     and the one-call path need (per-row counters, and for more than 8 rows
+ *     x laid out for the many-row kernel) is the caller's workspace of
  *     draft_head_workspace_bytes() bytes.
  *   - Device functions enqueue work asynchronously on `stream` (a hipStream_t
  *     passed as void*, NULL = the null stream) and return once it is enqueued;
@@ -126,9 +127,8 @@ int draft_head_workspace_bytes(int M, int K, size_t* bytes);
  *              when block b has fewer than kcand columns (n >= N)
  *   coarse_out optional out (NULL = not written), fp32 [M][N] coarse scores
  *   workspace  device scratch of at least draft_head_workspace_bytes(M, K)
- *              bytes, 16-byte aligned (may be NULL when that is 0); its
- *              contents are overwritten, so calls that share one workspace
- *              must be ordered (e.g. on one stream)
+ *              bytes, 16-byte aligned; its contents are overwritten, so calls
+ *              that share one workspace must be ordered (e.g. on one stream)
  * x values must be finite with |x| < 2^63 (x is scaled by 2^64 on chip).
  * Limits: 1 <= M <= DH_MAX_M, K % 512 == 0, N >= 1, 1 <= kcand <= DH_MAX_KCAND.
  * Errors: DH_EINVAL (also: workspace missing, misaligned or too small),

@@ -137,15 +137,16 @@ def test_quantize_pack_validation(lib):
 
 
 def test_workspace_bytes(lib):
-    # resident kernel (no workspace) up to 8 rows while x fits its LDS
+    # 512 bytes of per-row counters; the resident kernel (up to 8 rows while x
+    # fits its LDS) needs nothing more
     for m, k in ((1, 5120), (1, 65536), (2, 35840), (4, 15872), (8, 5120), (8, 7680)):
-        assert B.draft_head_workspace_bytes(m, k) == 0, (m, k)
-    # many-row kernel: (K/128) * 4096 * MT + (K/512) * 4096 with MT = min(ceil(M/16), 5)
+        assert B.draft_head_workspace_bytes(m, k) == 512, (m, k)
+    # many-row kernel: + (K/128) * 4096 * MT + (K/512) * 4096 with MT = min(ceil(M/16), 5)
     for m, k in ((2, 36352), (4, 16384), (8, 8192), (9, 512), (16, 1024), (17, 1024), (72, 5120),
                  (80, 5120), (81, 5120), (128, 5120)):
         mt = min((m + 15) // 16, 5)
-        assert B.draft_head_workspace_bytes(m, k) == (k // 128) * 4096 * mt + (k // 512) * 4096, (m, k)
-    assert B.draft_head_workspace_bytes(72, 5120) == 860_160
+        assert B.draft_head_workspace_bytes(m, k) == 512 + (k // 128) * 4096 * mt + (k // 512) * 4096, (m, k)
+    assert B.draft_head_workspace_bytes(72, 5120) == 860_672
     out = ctypes.c_size_t()
     _err(lib, lib.draft_head_workspace_bytes(1, 512, None), B.DH_EINVAL)
     _err(lib, lib.draft_head_workspace_bytes(0, 512, ctypes.byref(out)), B.DH_EINVAL)
@@ -160,8 +161,8 @@ def test_coarse_validation(lib, via):
             x, M, K, N, t, p, FAKE, K, kc, 8, cv, ci, FAKE, FAKE, FAKE, FAKE, co, ws, wsb, s, None, None)
     else:
         f = lambda *a: lib.draft_head_coarse(*a)  # noqa: E731
-    ok = dict(x=FAKE, M=1, K=512, N=64, tiled=FAKE, pairs=FAKE, kc=8, cv=FAKE, ci=FAKE, co=None, ws=None,
-              wsb=0, s=None)
+    ok = dict(x=FAKE, M=1, K=512, N=64, tiled=FAKE, pairs=FAKE, kc=8, cv=FAKE, ci=FAKE, co=None, ws=FAKE,
+              wsb=512, s=None)
 
     def call(**kw):
         a = dict(ok)
@@ -182,7 +183,10 @@ def test_coarse_validation(lib, via):
     _err(lib, call(kc=65), B.DH_EUNSUP)
     _err(lib, call(x=MIS), B.DH_EINVAL)
     _err(lib, call(pairs=MIS), B.DH_EINVAL)
-    # more than 8 rows need the caller's workspace: present, aligned, large enough
+    # the caller's workspace: present, aligned, large enough
+    _err(lib, call(ws=None), B.DH_EINVAL)
+    _err(lib, call(wsb=511), B.DH_EINVAL)
+    _err(lib, call(ws=MIS), B.DH_EINVAL)
     need = B.draft_head_workspace_bytes(9, 512)
     _err(lib, call(M=9), B.DH_EINVAL)
     _err(lib, call(M=9, ws=FAKE, wsb=need - 16), B.DH_EINVAL)
@@ -235,7 +239,7 @@ def test_forward_validation(lib):
         a.update(kw)
         return lib.draft_head_forward(a["x"], a["M"], a["K"], a["N"], a["t"], a["p"], a["w"], a["ldw"],
                                       a["kc"], a["R"], a["cv"], a["ci"], a["ri"], a["rv"], a["oi"],
-                                      a["ov"], a["co"], None, 0, a["s"], None, None)
+                                      a["ov"], a["co"], FAKE, 4096, a["s"], None, None)
     _err(lib, call(w=None), B.DH_EINVAL)
     _err(lib, call(ri=None), B.DH_EINVAL)
     _err(lib, call(oi=None), B.DH_EINVAL)
