@@ -1323,20 +1323,38 @@ __device__ unsigned long long wave_top2_threshold(const unsigned long long (&v)[
 }
 
 // Rerank across many workgroups: grid (ceil(R / 4), M), four waves each.  Every
-// workgroup of row m repeats the block-maximum selection above (wave 0; the
-// same list in every workgroup), then each of its waves computes the exact
-// logit of one rank, r = 4 * blockIdx.x + wave, so the R rows of W are read
-// by R waves at once.  With kArgmax the last workgroup of the row to finish
-// (a per-row arrival counter, zeroed by the coarse kernel of the same call
-// and reset here) takes the argmax over the R logits.
+// workgroup of row m computes the row's top-R list (the same list in every
+// workgroup), then each of its waves computes the exact logit of one rank,
+// r = 4 * blockIdx.x + wave, so the R rows of W are read by R waves at once.
+// With kArgmax the last workgroup of the row to finish (a per-row arrival
+// counter, zeroed by the coarse kernel of the same call and reset here) takes
+// the argmax over the R logits.
+//
+// The list (block-maximum selection; the candidates are the ones
+// draft_head_coarse writes, so slot b*kcand holds block b's maximum and slot
+// order is column order among equal values):
+//   1. Wave 0 reads the block maxima, 32 per lane, as (value, slot) keys.
+//      With R <= 64, T' = the R-th largest of the 64 lane maxima (ranked by
+//      counting in LDS) is at most the R-th largest block maximum, so every
+//      one of the row's R best candidates is >= T'; if T' lets more than
+//      DH_MAX_R / kcand blocks through (or R > 64), T' = the exact R-th
+//      largest block maximum (radix select).
+//   2. The candidates >= T' of the blocks whose maximum is >= T' survive
+//      (at least R, at most DH_MAX_R); each is ranked by counting the
+//      survivors above it, and the first R ranks are the list.
 constexpr int kWideThreads = 256;
 constexpr int kWideDot = 10;       // 16-byte loads of x and of W in flight per lane
 
+constexpr int kWideGather = DH_MAX_R / kWideThreads;   // candidate loads per thread in flight
+
 struct WideShared {
   unsigned int hist[256];
+  unsigned long long lmax[64];
   int qual[DH_MAX_R];
   unsigned long long keys[DH_MAX_R];
-  int ns;
+  unsigned long long list[DH_MAX_R];
+  unsigned long long T;
+  int nq, ns;
   int last;
 };
 
@@ -1353,17 +1371,28 @@ __global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(
   const int32_t* ci = cand_id + (size_t)m * ncand;
 
   if (wave == 0) {
-    // the R-th largest block maximum as threshold, then the candidates >= it
     float mv[kFastNV];
 #pragma unroll
     for (int j = 0; j < kFastNV; ++j) mv[j] = cv[min(lane + 64 * j, nblk - 1) * kcand];   // clamped loads
-    unsigned long long mk[kFastNV];
+    unsigned long long mk[kFastNV], lm = 0ull;
 #pragma unroll
     for (int j = 0; j < kFastNV; ++j) {
       const int b = lane + 64 * j;
       mk[j] = b < nblk ? slot_key(mv[j], b * kcand) : 0ull;
+      lm = umax64(lm, mk[j]);
     }
-    unsigned long long T = R <= 128 ? wave_top2_threshold(mk, R) : 0ull;
+    unsigned long long T = 0ull;
+    if (R <= 64) {   // rank of each lane's maximum among the 64 (keys are distinct or zero)
+      sh.lmax[lane] = lm;
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the lane maxima are in LDS
+      int above = 0;
+      for (int l = 0; l < 64; ++l) {
+        const unsigned long long o = sh.lmax[l];
+        above += o > lm || (o == lm && l < lane);
+      }
+      const unsigned long long hit = __ballot(above == R - 1);
+      T = __shfl(lm, (int)__ffsll((long long)hit) - 1, 64);
+    }
     int nq = 0;
     if (T) {
 #pragma unroll
@@ -1378,37 +1407,48 @@ __global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(
       if (q) sh.qual[nq + lane_prefix(bal)] = lane + 64 * j;
       nq += __popcll(bal);
     }
-    const int items = nq * kcand;
-    int ns = 0;
-    for (int i0 = 0; i0 < items; i0 += 64 * kSurvBatch) {
-      float v[kSurvBatch];
-      int id[kSurvBatch], slot[kSurvBatch];
-#pragma unroll
-      for (int j = 0; j < kSurvBatch; ++j) {   // clamped loads
-        const int i = min(i0 + 64 * j + lane, items - 1);
-        slot[j] = sh.qual[i / kcand] * kcand + i % kcand;
-        v[j] = cv[slot[j]];
-        id[j] = ci[slot[j]];
-      }
-#pragma unroll
-      for (int j = 0; j < kSurvBatch; ++j) {
-        const bool in = i0 + 64 * j + lane < items;
-        const unsigned long long k = in ? slot_key(v[j], slot[j]) : 0ull;
-        const bool keep = k != 0ull && k >= T && id[j] >= 0 && id[j] < N;
-        const unsigned long long bal = __ballot(keep);
-        if (keep) sh.keys[ns + lane_prefix(bal)] = cand_key(v[j], id[j], N);
-        ns += __popcll(bal);
-      }
+    if (lane == 0) {
+      sh.nq = nq;
+      sh.ns = 0;
+      sh.T = T;
     }
-    if (lane == 0) sh.ns = ns;
   }
   __syncthreads();
-  sort_desc<kWideThreads>(sh.keys, sh.ns);   // R <= ns <= R * kcand <= DH_MAX_R
+  {   // the survivors, gathered by the whole workgroup (their order does not matter)
+    const int items = sh.nq * kcand;   // <= DH_MAX_R
+    const unsigned long long T = sh.T;
+    float v[kWideGather];
+    int id[kWideGather], slot[kWideGather];
+#pragma unroll
+    for (int j = 0; j < kWideGather; ++j) {   // clamped loads
+      const int i = min(tid + kWideThreads * j, items - 1);
+      slot[j] = sh.qual[i / kcand] * kcand + i % kcand;
+      v[j] = cv[slot[j]];
+      id[j] = ci[slot[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < kWideGather; ++j) {
+      const bool in = tid + kWideThreads * j < items;
+      const unsigned long long k = in ? slot_key(v[j], slot[j]) : 0ull;
+      if (k != 0ull && k >= T && id[j] >= 0 && id[j] < N) sh.keys[atomicAdd(&sh.ns, 1)] = cand_key(v[j], id[j], N);
+    }
+  }
+  __syncthreads();
+  {   // rank the survivors (distinct keys): list[rank] for rank < R
+    const int ns = sh.ns;   // R <= ns <= DH_MAX_R
+    for (int i = tid; i < ns; i += kWideThreads) {
+      const unsigned long long key = sh.keys[i];
+      int above = 0;
+      for (int j = 0; j < ns; ++j) above += sh.keys[j] > key;
+      if (above < R) sh.list[above] = key;
+    }
+  }
+  __syncthreads();
 
   // the exact logit of rank r: this wave reads W[id] and x[m] once, all loads in flight
   const int r = 4 * blockIdx.x + wave;
   if (r < R) {
-    const uint32_t id = key_id(sh.keys[r]);
+    const uint32_t id = key_id(sh.list[r]);
     const uint16_t* wr = w + (size_t)id * ldw;
     const uint16_t* xr = x + (size_t)m * K;
     float s0 = 0.f, s1 = 0.f;
