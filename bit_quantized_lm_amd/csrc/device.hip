@@ -384,13 +384,15 @@ void coarse_resident_kernel(CoarseArgs A) {
   // A wave past the last block reads block 0 (valid memory) and writes nothing.
   const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512 + NT * part * 64;
   const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64 + NT * part * 16;
+  // codes and scale pairs are read once per call: nontemporal loads keep them
+  // from displacing x and the candidates in the caches
   auto load_codes = [&](int G, u32x4 (&raw)[2][NT], u32x4 (&sz)[NT]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) raw[h][t] = tp[((G * 2 + h) * 4 + t) * 64 + lane];
+      for (int t = 0; t < NT; ++t) raw[h][t] = __builtin_nontemporal_load(tp + ((G * 2 + h) * 4 + t) * 64 + lane);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) sz[t] = pp[(G * 4 + t) * 16 + nn];
+    for (int t = 0; t < NT; ++t) sz[t] = __builtin_nontemporal_load(pp + (G * 4 + t) * 16 + nn);
   };
 
   // the first byte groups' codes are requested before x is staged
@@ -577,9 +579,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // One direct-to-LDS DMA op: lane l's 16 bytes at base + voff land at
-// lds + 16 l (base and lds wave-uniform; voff = 16 l).
+// lds + 16 l (base and lds wave-uniform; voff = 16 l).  The nontemporal form
+// is for data read once per call (codes, scale pairs).
 __device__ __forceinline__ void dma16(uint32_t voff, const void* base, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_nt(uint32_t voff, const void* base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
                : "v"(voff), "s"(base), "s"(lds)
                : "memory", "m0");
@@ -727,7 +736,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
 #pragma unroll
       for (int k = 0; k < S::nc(P); ++k) {
         const int c = P + WPB * k;
-        dma16(voff, c < 8 ? tp + (GC * 8 + c) * 64 : pp + GC * 64,
+        dma16_nt(voff, c < 8 ? tp + (GC * 8 + c) * 64 : pp + GC * 64,
               cs_l + cslot * 4 * kCodeChunks * 1024 + c * 1024);
       }
       int GB = (j >> 2) + 1;
