@@ -11,10 +11,10 @@ of packed weights in the 256 MB Infinity Cache left by the previous step.
 Prints one JSON line:
   value        HBM GB/s of the call: 178,790,400 B (packed codes + scale pair,
                the page's "0.167 GiB") / measured time per call
-  ms_per_step  time per call
+  ms_per_step  time per call (calls with no per-call events)
   roofline     the coarse kernel: algorithmic bytes per launch / its average
                duration (HIP events set by the kernel's own dispatch on the
-               launch stream) vs 8 TB/s
+               launch stream, in a second pass of as many calls) vs 8 TB/s
   cpu_baseline the CPU oracle timed on this host on one full call at M = 1
   extra        per-M (1, 8, 72) times, the warm (cache-resident) figure and
                a device-copy bandwidth reference
@@ -37,6 +37,13 @@ HBM_PEAK_GBPS = 8000.0
 K, N, KCAND, R = 5120, 124160, 8, 32
 NBLK = (N + 63) // 64
 WEIGHT_BYTES = N * (K // 4) + 2 * 2 * N * (K // 128)       # 178,790,400
+
+
+def coarse_kernel_name(m: int) -> str:
+    """The coarse kernel one launch at M rows runs (K = 5120)."""
+    if m <= 8:
+        return f"coarse_resident_kernel<{1 if m == 1 else 2 if m == 2 else 4 if m <= 4 else 8}>"
+    return f"coarse_mfma_kernel<{min((m + 15) // 16, 5)}>"
 
 
 def coarse_alg_bytes(m: int) -> int:
@@ -104,27 +111,42 @@ class Rig:
         head(self.x[:m], stream=self.stream, out=out, coarse_events=ev, workspace=self.ws[m])
 
     def timed(self, m, steps, warmup, copies=None):
-        """(seconds per call, seconds per coarse launch) over `steps` calls."""
+        """(seconds per call, seconds per coarse launch, wall seconds).
+
+        The calls are timed over `steps` calls with no per-call events (the
+        coarse kernel's dispatch events cost the stream a few microseconds
+        per call); the coarse kernel's duration comes from a second pass of
+        `steps` calls that pass those events.  Warm-up runs first, at least
+        0.2 s of calls, so that the clocks have ramped."""
         torch = self.torch
         heads = self.heads if copies is None else self.heads[:copies]
-        for i in range(warmup):
+        t0 = time.perf_counter()
+        i = 0
+        while i < warmup or time.perf_counter() - t0 < 0.2:
             self.step(m, heads[i % len(heads)])
+            i += 1
+            if i % 64 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            self.step(m, heads[i % len(heads)])
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = start.elapsed_time(end)
+
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
         for a, b in evs:      # torch creates an event on its first record
             a.record()
             b.record()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record()
         for i in range(steps):
             self.step(m, heads[i % len(heads)], evs[i])
-        end.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        total_ms = start.elapsed_time(end)
         coarse_ms = [a.elapsed_time(b) for a, b in evs]
         return total_ms / 1e3 / steps, float(np.mean(coarse_ms)) / 1e3, wall
 
@@ -189,8 +211,8 @@ def load_traffic(m):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--m", type=int, default=1, help="rows (draft slots) of the headline line")
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -247,7 +269,7 @@ def main():
     achieved = alg / t_coarse / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(m),
-                "kernel": "coarse_kernel", "alg_bytes_per_launch": alg,
+                "kernel": coarse_kernel_name(m), "alg_bytes_per_launch": alg,
                 "avg_launch_us": round(t_coarse * 1e6, 2)}
     cpu = None
     if not args.no_cpu_baseline:

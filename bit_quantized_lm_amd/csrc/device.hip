@@ -78,6 +78,23 @@ __device__ __forceinline__ uint32_t scale_x_pair(uint32_t w) {
 // x fragments live in LDS in the decode order: fragment f = (h*2 + e)*4 + s of
 // a group holds x at k = q*K/4 + 128*G + 64h + 16s + 8e + {0,2,1,3,4,6,5,7}.
 
+// Arguments of the rerank (row top-R of the candidates, exact logits, and
+// with the argmax the per-row arrival counters).
+struct RerankArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  int64_t ldw;
+  int K, N;
+  const float* cand_val;
+  const int32_t* cand_id;
+  int nblk, kcand, R;
+  int32_t* rr_id;
+  float* rr_val;
+  int32_t* out_id;
+  float* out_val;
+  uint32_t* cnt;
+};
+
 struct CoarseArgs {
   const uint16_t* x;
   int M, K, N, nblk;
@@ -91,8 +108,27 @@ struct CoarseArgs {
   int ncnt;
 };
 
+// Device-coherent stores and loads (agent scope: written through to, and read
+// from, the level every XCD shares) and a wait for this wave's stores.  Data
+// handed between workgroups of one launch goes through these, so that no
+// release fence (an L2 write-back, costly when every workgroup issues one) is
+// needed: the writer stores, waits, then counts itself with an atomic; the
+// reader sees the count, then loads.
+template <class T>
+__device__ __forceinline__ void store_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T load_dev(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Counters are only ever written with device-coherent stores and atomics: a
+// plain store would leave a dirty L2 line whose later write-back could undo
+// atomic updates made meanwhile by other XCDs.
 __device__ __forceinline__ void zero_counters(const CoarseArgs& A) {
-  if (blockIdx.x == 0 && (int)threadIdx.x < A.ncnt) A.cnt[threadIdx.x] = 0u;
+  if (blockIdx.x == 0 && (int)threadIdx.x < A.ncnt) store_dev(A.cnt + threadIdx.x, 0u);
 }
 
 // One group: MFMAs of the (h, e) fragments for all tiles, then the scale update.
@@ -960,17 +996,20 @@ __device__ __forceinline__ void pick_digit(const unsigned int (&c)[4], int need,
 // hist: 256 words of LDS private to the wave).  Skips the leading bytes all
 // keys share; stops once the bucket holding the k-th key is taken whole.
 // Returns the smallest key of that bucket: exactly k keys are >= it.
-template <int NV>
-__device__ unsigned long long wave_kth_largest(const unsigned long long (&v)[NV], int k,
-                                               unsigned int* hist) {
+// The keys are presented by key(j), j < NV, computed on demand; loops over j
+// are unrolled U times (1 for keys read from memory, so that few are live).
+template <int NV, int U, class Key>
+__device__ unsigned long long wave_kth_largest_of(Key key_of, int k, unsigned int* hist) {
   const int lane = threadIdx.x & 63;
   unsigned long long vmax = 0ull, vmin = ~0ull;
-#pragma unroll
-  for (int j = 0; j < NV; ++j)
-    if (v[j]) {
-      vmax = umax64(vmax, v[j]);
-      vmin = umin64(vmin, v[j]);
+#pragma unroll U
+  for (int j = 0; j < NV; ++j) {
+    const unsigned long long v = key_of(j);
+    if (v) {
+      vmax = umax64(vmax, v);
+      vmin = umin64(vmin, v);
     }
+  }
   for (int off = 32; off > 0; off >>= 1) {
     vmax = umax64(vmax, __shfl_xor(vmax, off, 64));
     vmin = umin64(vmin, __shfl_xor(vmin, off, 64));
@@ -984,9 +1023,9 @@ __device__ unsigned long long wave_kth_largest(const unsigned long long (&v)[NV]
 #pragma unroll
     for (int d = 0; d < 4; ++d) hist[4 * lane + d] = 0u;
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the clears land before the adds
-#pragma unroll
+#pragma unroll U
     for (int j = 0; j < NV; ++j) {
-      const unsigned long long key = v[j];
+      const unsigned long long key = key_of(j);
       if (key && (shift + 8 == 64 || (key >> (shift + 8)) == pre))
         atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
@@ -1002,6 +1041,12 @@ __device__ unsigned long long wave_kth_largest(const unsigned long long (&v)[NV]
     if (whole || shift == 0) break;
   }
   return pre << shift;
+}
+
+template <int NV>
+__device__ unsigned long long wave_kth_largest(const unsigned long long (&v)[NV], int k,
+                                               unsigned int* hist) {
+  return wave_kth_largest_of<NV, NV>([&](int j) { return v[j]; }, k, hist);
 }
 
 // Same, over the whole workgroup: keys presented by for_each_key(f).
@@ -1331,13 +1376,13 @@ __device__ unsigned long long wave_top2_threshold(const unsigned long long (&v)[
   return __shfl(r ? e[1] : e[0], l, 64);
 }
 
-// Rerank across many workgroups: grid (ceil(R / 4), M), four waves each.  Every
-// workgroup of row m computes the row's top-R list (the same list in every
-// workgroup), then each of its waves computes the exact logit of one rank,
-// r = 4 * blockIdx.x + wave, so the R rows of W are read by R waves at once.
-// With kArgmax the last workgroup of the row to finish (a per-row arrival
-// counter, zeroed by the coarse kernel of the same call and reset here) takes
-// the argmax over the R logits.
+// Rerank of one row split over `nparts` workgroups of NTHR threads (NW = NTHR/64
+// waves each).  Every part of row m computes the row's top-R list (the same
+// list in every part), then each of its waves computes the exact logit of one
+// rank, r = NW * part + wave, so the R rows of W are read by R waves at once.
+// With kArgmax the last part of the row to finish (a per-row arrival counter,
+// zeroed by the coarse kernel of the same call and reset here) takes the
+// argmax over the R logits.
 //
 // The list (block-maximum selection; the candidates are the ones
 // draft_head_coarse writes, so slot b*kcand holds block b's maximum and slot
@@ -1354,11 +1399,8 @@ __device__ unsigned long long wave_top2_threshold(const unsigned long long (&v)[
 constexpr int kWideThreads = 256;
 constexpr int kWideDot = 10;       // 16-byte loads of x and of W in flight per lane
 
-constexpr int kWideGather = DH_MAX_R / kWideThreads;   // candidate loads per thread in flight
-
 struct WideShared {
   unsigned int hist[256];
-  unsigned long long lmax[64];
   int qual[DH_MAX_R];
   unsigned long long keys[DH_MAX_R];
   unsigned long long list[DH_MAX_R];
@@ -1367,51 +1409,70 @@ struct WideShared {
   int last;
 };
 
-template <bool kArgmax>
-__global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t ldw, int K, int N,
-    const float* __restrict__ cand_val, const int32_t* __restrict__ cand_id, int nblk, int kcand, int R,
-    int32_t* __restrict__ rr_id, float* __restrict__ rr_val, int32_t* __restrict__ out_id,
-    float* __restrict__ out_val, uint32_t* __restrict__ cnt) {
-  __shared__ WideShared sh;
-  const int m = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+static_assert(64 * kFastNV * sizeof(uint32_t) <= sizeof(WideShared::keys), "block maxima staged in keys");
+
+// Row m's top-R list into sh.list[0..R); called by the whole workgroup, ends
+// with a barrier.
+template <int NTHR>
+__device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
+  constexpr int kGather = DH_MAX_R / NTHR;   // candidate loads per thread in flight
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nblk = A.nblk, kcand = A.kcand, R = A.R, N = A.N;
   const int ncand = nblk * kcand;
-  const float* cv = cand_val + (size_t)m * ncand;
-  const int32_t* ci = cand_id + (size_t)m * ncand;
+  const float* cv = A.cand_val + (size_t)m * ncand;
+  const int32_t* ci = A.cand_id + (size_t)m * ncand;
 
   if (wave == 0) {
-    float mv[kFastNV];
+    // block b = lane + 64 j: its maximum's key is slot_key(value, b * kcand),
+    // held as the upper half alone (0: no such block); the lower half is
+    // ~(b * kcand), so keys compare as (upper, then lower j first)
+    uint32_t mo[kFastNV];
 #pragma unroll
-    for (int j = 0; j < kFastNV; ++j) mv[j] = cv[min(lane + 64 * j, nblk - 1) * kcand];   // clamped loads
-    unsigned long long mk[kFastNV], lm = 0ull;
+    for (int j = 0; j < kFastNV; ++j) mo[j] = __float_as_uint(cv[min(lane + 64 * j, nblk - 1) * kcand]);   // clamped loads
 #pragma unroll
-    for (int j = 0; j < kFastNV; ++j) {
-      const int b = lane + 64 * j;
-      mk[j] = b < nblk ? slot_key(mv[j], b * kcand) : 0ull;
-      lm = umax64(lm, mk[j]);
-    }
-    unsigned long long T = 0ull;
-    if (R <= 64) {   // rank of each lane's maximum among the 64 (keys are distinct or zero)
-      sh.lmax[lane] = lm;
-      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the lane maxima are in LDS
-      int above = 0;
-      for (int l = 0; l < 64; ++l) {
-        const unsigned long long o = sh.lmax[l];
-        above += o > lm || (o == lm && l < lane);
-      }
-      const unsigned long long hit = __ballot(above == R - 1);
-      T = __shfl(lm, (int)__ffsll((long long)hit) - 1, 64);
-    }
+    for (int j = 0; j < kFastNV; ++j)
+      mo[j] = lane + 64 * j < nblk ? (uint32_t)(slot_key(__uint_as_float(mo[j]), 0) >> 32) : 0u;
+    auto lower = [&](int j) { return 0xFFFFFFFFu - (uint32_t)((lane + 64 * j) * kcand); };
+    auto at_least = [&](int j, uint32_t to, uint32_t tl) {   // key of j >= (to, tl); to >= 1
+      const uint32_t o = mo[j];
+      return (o > to) | ((o == to) & (lower(j) >= tl));
+    };
+    uint32_t bo = 0u;   // the lane's largest upper half
+#pragma unroll
+    for (int j = 0; j < kFastNV; ++j) bo = max(bo, mo[j]);
+    // T' = (to, 0) with to the R-th largest of the 64 lane maxima's upper
+    // halves (bisection over its bits, counting lanes by ballot): at least R
+    // lanes hold a block maximum >= T', so T' is at most the R-th largest
+    // block maximum.
+    uint32_t to = 0u, tl = 0u;
     int nq = 0;
-    if (T) {
+    if (R <= 64) {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = to | (1u << bit);
+        if (__popcll(__ballot(bo >= t)) >= R) to = t;
+      }
 #pragma unroll
-      for (int j = 0; j < kFastNV; ++j) nq += __popcll(__ballot(mk[j] != 0ull && mk[j] >= T));
+      for (int j = 0; j < kFastNV; ++j) nq += __popcll(__ballot(at_least(j, to, 0u)));
     }
-    if (!T || nq * kcand > DH_MAX_R) T = wave_kth_largest(mk, R, sh.hist);
+    if (to == 0u || nq * kcand > DH_MAX_R) {   // exact R-th largest maximum; keys read back from LDS
+      uint32_t* so = reinterpret_cast<uint32_t*>(sh.keys);   // 64 * kFastNV words
+#pragma unroll
+      for (int j = 0; j < kFastNV; ++j) so[64 * j + lane] = mo[j];
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      const unsigned long long T = wave_kth_largest_of<kFastNV, 1>(
+          [&](int j) -> unsigned long long {
+            const uint32_t o = *reinterpret_cast<volatile uint32_t*>(so + 64 * j + lane);
+            return o ? ((unsigned long long)o << 32) | lower(j) : 0ull;
+          },
+          R, sh.hist);
+      to = (uint32_t)(T >> 32);
+      tl = (uint32_t)T;
+    }
+    const unsigned long long T = ((unsigned long long)to << 32) | tl;
     nq = 0;
 #pragma unroll
     for (int j = 0; j < kFastNV; ++j) {
-      const bool q = mk[j] != 0ull && mk[j] >= T;
+      const bool q = at_least(j, to, tl);
       const unsigned long long bal = __ballot(q);
       if (q) sh.qual[nq + lane_prefix(bal)] = lane + 64 * j;
       nq += __popcll(bal);
@@ -1426,18 +1487,18 @@ __global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(
   {   // the survivors, gathered by the whole workgroup (their order does not matter)
     const int items = sh.nq * kcand;   // <= DH_MAX_R
     const unsigned long long T = sh.T;
-    float v[kWideGather];
-    int id[kWideGather], slot[kWideGather];
+    float v[kGather];
+    int id[kGather], slot[kGather];
 #pragma unroll
-    for (int j = 0; j < kWideGather; ++j) {   // clamped loads
-      const int i = min(tid + kWideThreads * j, items - 1);
+    for (int j = 0; j < kGather; ++j) {   // clamped loads
+      const int i = min(tid + NTHR * j, items - 1);
       slot[j] = sh.qual[i / kcand] * kcand + i % kcand;
       v[j] = cv[slot[j]];
       id[j] = ci[slot[j]];
     }
 #pragma unroll
-    for (int j = 0; j < kWideGather; ++j) {
-      const bool in = tid + kWideThreads * j < items;
+    for (int j = 0; j < kGather; ++j) {
+      const bool in = tid + NTHR * j < items;
       const unsigned long long k = in ? slot_key(v[j], slot[j]) : 0ull;
       if (k != 0ull && k >= T && id[j] >= 0 && id[j] < N) sh.keys[atomicAdd(&sh.ns, 1)] = cand_key(v[j], id[j], N);
     }
@@ -1445,7 +1506,7 @@ __global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(
   __syncthreads();
   {   // rank the survivors (distinct keys): list[rank] for rank < R
     const int ns = sh.ns;   // R <= ns <= DH_MAX_R
-    for (int i = tid; i < ns; i += kWideThreads) {
+    for (int i = tid; i < ns; i += NTHR) {
       const unsigned long long key = sh.keys[i];
       int above = 0;
       for (int j = 0; j < ns; ++j) above += sh.keys[j] > key;
@@ -1453,13 +1514,21 @@ __global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(
     }
   }
   __syncthreads();
+}
+
+template <int NTHR, bool kArgmax>
+__device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part, int nparts) {
+  constexpr int NW = NTHR / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int R = A.R, K = A.K;
+  rerank_list<NTHR>(sh, A, m);
 
   // the exact logit of rank r: this wave reads W[id] and x[m] once, all loads in flight
-  const int r = 4 * blockIdx.x + wave;
+  const int r = NW * part + wave;
   if (r < R) {
     const uint32_t id = key_id(sh.list[r]);
-    const uint16_t* wr = w + (size_t)id * ldw;
-    const uint16_t* xr = x + (size_t)m * K;
+    const uint16_t* wr = A.w + (size_t)id * A.ldw;
+    const uint16_t* xr = A.x + (size_t)m * K;
     float s0 = 0.f, s1 = 0.f;
     for (int k0 = 0; k0 < K; k0 += 512 * kWideDot) {
       u32x4 wv[kWideDot], xv[kWideDot];
@@ -1483,25 +1552,26 @@ __global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(
     float sum = s0 + s1;
     for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
     if (lane == 0) {
-      rr_id[(size_t)m * R + r] = (int32_t)id;
-      rr_val[(size_t)m * R + r] = sum;
+      store_dev(A.rr_id + (size_t)m * R + r, (int32_t)id);
+      store_dev(A.rr_val + (size_t)m * R + r, sum);
     }
   }
   if constexpr (kArgmax) {
+    // Every wave's logits are written through before the part is counted (a
+    // barrier alone does not wait for other waves' stores).
+    wait_stores();
     __syncthreads();
     if (tid == 0) {
-      __threadfence();   // this workgroup's logits are visible before it is counted
-      const uint32_t old = atomicAdd(cnt + m, 1u);
-      sh.last = old == gridDim.x - 1;
+      const uint32_t old = atomicAdd(A.cnt + m, 1u);
+      sh.last = old == (uint32_t)nparts - 1;
     }
     __syncthreads();
     if (sh.last && wave == 0) {
-      __threadfence();
       float bv = -__builtin_inff();
       int bi = -1;
       for (int q = lane; q < R; q += 64) {
-        const int id = __hip_atomic_load(rr_id + (size_t)m * R + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float v = __hip_atomic_load(rr_val + (size_t)m * R + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int id = load_dev(A.rr_id + (size_t)m * R + q);
+        const float v = load_dev(A.rr_val + (size_t)m * R + q);
         if (bi < 0 || v > bv || (v == bv && id < bi)) {
           bv = v;
           bi = id;
@@ -1516,13 +1586,21 @@ __global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(
         }
       }
       if (lane == 0) {
-        out_id[m] = bi;
-        out_val[m] = bv;
-        cnt[m] = 0u;   // ready for the next call
+        A.out_id[m] = bi;
+        A.out_val[m] = bv;
+        store_dev(A.cnt + m, 0u);   // ready for the next call
       }
     }
   }
 }
+
+// Rerank kernel: grid (ceil(R / 4), M), one part of one row per workgroup.
+template <bool kArgmax>
+__global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(RerankArgs A) {
+  __shared__ WideShared sh;
+  rerank_part<kWideThreads, kArgmax>(sh, A, blockIdx.y, blockIdx.x, gridDim.x);
+}
+
 
 // Final token: one wave per row; largest value, ties to the lower id, id -1 skipped.
 __global__ __launch_bounds__(256) void argmax_kernel(const int32_t* __restrict__ rr_id,
@@ -1621,6 +1699,7 @@ hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t
 }
 
 int resident_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+
 
 // Up to 8 rows whose x fits the workgroup's LDS take the resident kernel (no
 // workspace); every other M the many-row kernel, in launches of up to 80 rows.
@@ -1750,9 +1829,9 @@ template <bool kArgmax>
 hipError_t launch_wide(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
                        const int32_t* cand_id, int nblk, int kcand, int R, int32_t* rr_id, float* rr_val,
                        int32_t* out_id, float* out_val, uint32_t* cnt, hipStream_t s) {
-  hipLaunchKernelGGL(rerank_wide_kernel<kArgmax>, dim3((R + 3) / 4, M), dim3(kWideThreads), 0, s,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), ldw, K, N, cand_val,
-                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, cnt);
+  const RerankArgs A{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), ldw, K, N, cand_val,
+                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, cnt};
+  hipLaunchKernelGGL(rerank_wide_kernel<kArgmax>, dim3((R + 3) / 4, M), dim3(kWideThreads), 0, s, A);
   return hipGetLastError();
 }
 

@@ -21,8 +21,8 @@
  *     except DH_EHIP can be provoked without a GPU.
  *   - The caller owns every buffer.  The library allocates no device memory
  *     and keeps no state between calls; the scratch memory the coarse pass
- *     and the one-call path need (per-row counters, and for more than 8 rows
- *     x laid out for the many-row kernel) is the caller's workspace of
+ *     and the one-call path need (counters, and for more than 8 rows x laid
+ *     out for the many-row kernel) is the caller's workspace of
  *     draft_head_workspace_bytes() bytes.
  *   - Device functions enqueue work asynchronously on `stream` (a hipStream_t
  *     passed as void*, NULL = the null stream) and return once it is enqueued;
@@ -104,11 +104,12 @@ int draft_head_tile(const uint8_t* packed, const uint16_t* S, const uint16_t* ZS
 
 /*
  * Bytes of device workspace draft_head_coarse / draft_head_forward need for M
- * rows of length K: 0 when M <= 8 and the resident kernel holds all of x in
- * LDS (any K at M = 1; K <= 35840, 15872, 7680 at M = 2, 3..4, 5..8), else
- * the x of one launch of up to 80 rows laid out
- * for the many-row kernel: (K/128) * 4096 * MT + (K/512) * 4096 bytes with
- * MT = min(ceil(M/16), 5) (860,160 bytes at M = 72, K = 5120).
+ * rows of length K: 512 bytes of per-row counters, plus, unless M <= 8 and
+ * the resident kernel holds all of x in LDS (any K at M = 1; K <= 35840,
+ * 15872, 7680 at M = 2, 3..4, 5..8), the x of one launch of up to 80 rows
+ * laid out for the many-row kernel: (K/128) * 4096 * MT + (K/512) * 4096
+ * bytes with MT = min(ceil(M/16), 5) (860,672 bytes in all at M = 72,
+ * K = 5120).
  * Errors: DH_EINVAL (null pointer, M < 1), DH_EUNSUP (M > DH_MAX_M), DH_ESHAPE.
  */
 int draft_head_workspace_bytes(int M, int K, size_t* bytes);

@@ -88,6 +88,8 @@ CASES = [
     (4, 1024, 5000, 16, 32),
     (2, 512, 131072, 8, 32),
     (2, 512, 131100, 8, 32),
+    # R > 64 (exact threshold by radix select) in the separate rerank kernel
+    (20, 512, 70000, 8, 100),
 ]
 
 
@@ -233,10 +235,11 @@ def test_recall_stress_full_shape(dev, full):
     assert misses[8] == 0
 
 
-def test_forward_matches_staged_calls(dev):
-    """The one-call entry point equals the three separate calls, and sets the
-    coarse kernel's timing events."""
-    n, k, m, kc, r = 3000, 1024, 5, 8, 32
+@pytest.mark.parametrize("n,m", [(3000, 5), (20000, 1), (70000, 8), (20000, 20)])
+def test_forward_matches_staged_calls(dev, n, m):
+    """The one-call entry point (rerank and argmax in one kernel) equals the
+    three separate calls, and sets the coarse kernel's timing events."""
+    k, kc, r = 1024, 8, 32
     w = workload.gen_weight(n, k, seed=93)
     x = _to_dev(workload.gen_x(m, k, seed=94), dev)
     head = B.DraftHead.from_weight(w, kcand=kc, R=r, device=dev)
@@ -249,3 +252,21 @@ def test_forward_matches_staged_calls(dev):
     for key in a:
         assert torch.equal(a[key], b[key]), key
     assert e0.elapsed_time(e1) > 0
+
+
+def test_workspace_reuse_leaves_counters_zero(dev):
+    """One workspace serves calls of several row counts in a row (resident
+    and many-row coarse kernels); each result equals a call with a fresh
+    workspace, and the per-row counters end at zero."""
+    n, k = 20000, 1024
+    w = workload.gen_weight(n, k, seed=95)
+    x = _to_dev(workload.gen_x(20, k, seed=96), dev)
+    head = B.DraftHead.from_weight(w, kcand=8, R=32, device=dev)
+    ws = B.workspace_for(20, k, dev)
+    for m in (1, 8, 2, 20, 1, 8):
+        got = head(x[:m], workspace=ws)
+        want = head(x[:m])
+        torch.cuda.synchronize()
+        for key in want:
+            assert torch.equal(got[key], want[key]), (m, key)
+        assert int(torch.count_nonzero(ws[:512])) == 0, m
