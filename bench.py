@@ -15,9 +15,12 @@ Prints one JSON line:
   roofline     the coarse kernel: algorithmic bytes per launch / its average
                duration (HIP events set by the kernel's own dispatch on the
                launch stream, in a second pass of as many calls) vs 8 TB/s
-  cpu_baseline the CPU oracle timed on this host on one full call at M = 1
-  extra        per-M (1, 8, 72) times, the warm (cache-resident) figure and
-               a device-copy bandwidth reference
+  cpu_baseline the CPU oracle timed on this host, one full call each at
+               M = 1, 8, 72 (value: M = 1)
+  extra        per-M (1, 8, 72) times with the coarse kernel's p10/p50/p90 and
+               its fractions of the HBM and bf16 MFMA peaks, the warm
+               (cache-resident) figure, and the device's achieved read rate
+               (the library's streaming-read reference) and copy rate
 """
 from __future__ import annotations
 
@@ -25,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -34,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # dense
 K, N, KCAND, R = 5120, 124160, 8, 32
 NBLK = (N + 63) // 64
 WEIGHT_BYTES = N * (K // 4) + 2 * 2 * N * (K // 128)       # 178,790,400
@@ -147,8 +152,31 @@ class Rig:
         for i in range(steps):
             self.step(m, heads[i % len(heads)], evs[i])
         torch.cuda.synchronize()
-        coarse_ms = [a.elapsed_time(b) for a, b in evs]
+        coarse_ms = np.array([a.elapsed_time(b) for a, b in evs])
+        self.last_coarse_pct = {f"p{q}": round(float(np.percentile(coarse_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
         return total_ms / 1e3 / steps, float(np.mean(coarse_ms)) / 1e3, wall
+
+    def read_bandwidth(self, reps=20):
+        """The device's streaming read rate with the library's read reference
+        (draft_head_stream_read): over four rotated buffers of the weights'
+        size (no Infinity-Cache reuse) and over one 1 GiB buffer, in GB/s."""
+        torch, B = self.torch, self.B
+        res = {}
+        for name, size, nbuf in (("weights_size_rotated", WEIGHT_BYTES, 4), ("1GiB", 1 << 30, 1)):
+            bufs = [torch.ones(size // 4, dtype=torch.int32, device=self.dev) for _ in range(nbuf)]
+            out = torch.empty(B.DH_READ_BLOCKS, dtype=torch.int32, device=self.dev)
+            for i in range(4):
+                B.draft_head_stream_read(bufs[i % nbuf], out=out, stream=self.stream)
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for i in range(reps):
+                B.draft_head_stream_read(bufs[i % nbuf], out=out, stream=self.stream)
+            e.record()
+            torch.cuda.synchronize()
+            res[name] = round(size / (s.elapsed_time(e) / 1e3 / reps) / 1e9, 1)
+            del bufs
+        return res
 
     def copy_bandwidth(self, mib=1024, reps=5):
         """Device-to-device copy of `mib` MiB: (read + write bytes) / time."""
@@ -168,9 +196,10 @@ class Rig:
         return 2 * (mib << 20) / t / 1e9
 
 
-def cpu_baseline(x_host, m=1):
-    """The oracle, untuned, on one full call at M = 1 (dequantise from the
-    packed arrays, float64 GEMV, block top-8, row top-32, exact rerank, argmax)."""
+def cpu_baseline(x_host):
+    """The oracle, untuned, on one full call each at M = 1, 8 and 72 (dequantise
+    from the packed arrays, float64 GEMV, block top-8, row top-32, exact
+    rerank, argmax); the value is the M = 1 call's."""
     import oracle
     from bit_quantized_lm_amd import workload
     try:
@@ -180,19 +209,24 @@ def cpu_baseline(x_host, m=1):
         blas_threads = None
     w = workload.gen_weight(N, K)
     packed = oracle.quantize_pack(w)
-    x = x_host[:m]
-    t0 = time.perf_counter()
-    c = oracle.coarse(x, *packed)
-    cv, ci = oracle.block_topk(c, KCAND)
-    rr_id, _ = oracle.row_topr(cv, ci, R)
-    e = oracle.rerank_exact(x, w, rr_id)
-    oracle.final_argmax(rr_id, e)
-    t = time.perf_counter() - t0
+    per_m = {}
+    for m in (1, 8, 72):
+        x = x_host[:m]
+        t0 = time.perf_counter()
+        c = oracle.coarse(x, *packed)
+        cv, ci = oracle.block_topk(c, KCAND)
+        rr_id, _ = oracle.row_topr(cv, ci, R)
+        e = oracle.rerank_exact(x, w, rr_id)
+        oracle.final_argmax(rr_id, e)
+        per_m[str(m)] = round((time.perf_counter() - t0) * 1e6, 1)
+    t = per_m["1"] / 1e6
     cores = len(os.sched_getaffinity(0))
-    return {"value": round(WEIGHT_BYTES / t / 1e9, 4), "unit": "GB/s", "us_per_call": round(t * 1e6, 1),
+    return {"value": round(WEIGHT_BYTES / t / 1e9, 4), "unit": "GB/s", "us_per_call": per_m["1"],
+            "us_per_call_per_m": per_m,
             "cores": int(blas_threads or cores), "host_cores_visible": cores, "kind": "oracle",
-            "sample": "one full call at M=1, K=5120, N=124160 (dequantise + float64 GEMV + "
-                      "selection + rerank + argmax); quantisation not timed"}
+            "cpu": platform.processor() or platform.machine(),
+            "sample": "one full call each at M=1, 8, 72, K=5120, N=124160 (dequantise + float64 GEMV + "
+                      "selection + rerank + argmax); value from M=1; quantisation not timed"}
 
 
 def load_traffic(m):
@@ -246,7 +280,8 @@ def main():
     rig = Rig(args.copies, max(72, args.m))
     m = args.m
     t_call, t_coarse, wall = rig.timed(m, args.steps, args.warmup)
-    log(f"M={m}: {t_call * 1e6:.1f} us/call, coarse {t_coarse * 1e6:.1f} us, wall {wall:.3f}s")
+    coarse_pct = rig.last_coarse_pct
+    log(f"M={m}: {t_call * 1e6:.1f} us/call, coarse {t_coarse * 1e6:.1f} us {coarse_pct}, wall {wall:.3f}s")
 
     extra = {"quantize_pack_host_s": round(rig.quantize_s, 2), "copies_rotated": args.copies}
     if not args.no_extra:
@@ -254,27 +289,32 @@ def main():
         for mm in (1, 8, 72):
             tc, tk, _ = rig.timed(mm, max(20, args.steps // 2), 5)
             per_m[str(mm)] = {"us_per_call": round(tc * 1e6, 2), "coarse_us": round(tk * 1e6, 2),
+                              "coarse_us_pct": rig.last_coarse_pct,
                               "GBps": round(WEIGHT_BYTES / tc / 1e9, 1),
+                              "frac_hbm_peak": round(WEIGHT_BYTES / tc / 1e9 / HBM_PEAK_GBPS, 4),
                               "coarse_GBps": round(coarse_alg_bytes(mm) / tk / 1e9, 1),
                               "coarse_frac_hbm_peak": round(coarse_alg_bytes(mm) / tk / 1e9 / HBM_PEAK_GBPS, 4),
-                              "coarse_TFLOPs": round(2.0 * mm * K * N / tk / 1e12, 2)}
+                              "coarse_TFLOPs": round(2.0 * mm * K * N / tk / 1e12, 2),
+                              "coarse_frac_bf16_mfma_peak": round(2.0 * mm * K * N / tk / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
             log(f"M={mm}: {per_m[str(mm)]}")
         extra["per_m"] = per_m
         tw, tkw, _ = rig.timed(m, args.steps, args.warmup, copies=1)
         extra["warm_not_hbm"] = {"us_per_call": round(tw * 1e6, 2), "coarse_us": round(tkw * 1e6, 2),
                                  "note": "one weight copy reused back to back: Infinity-Cache resident"}
         extra["device_copy_GBps"] = round(rig.copy_bandwidth(), 1)
+        extra["stream_read_GBps"] = rig.read_bandwidth()
+        log(f"read reference: {extra['stream_read_GBps']}, copy {extra['device_copy_GBps']}")
 
     alg = coarse_alg_bytes(m)
     achieved = alg / t_coarse / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(m),
                 "kernel": coarse_kernel_name(m), "alg_bytes_per_launch": alg,
-                "avg_launch_us": round(t_coarse * 1e6, 2)}
+                "avg_launch_us": round(t_coarse * 1e6, 2), "launch_us_pct": coarse_pct}
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle (one full call)")
-        cpu = cpu_baseline(rig.x_host, 1)
+        log("timing the CPU oracle (one full call at M = 1, 8, 72)")
+        cpu = cpu_baseline(rig.x_host)
         log(f"cpu oracle: {cpu}")
 
     line = {

@@ -67,6 +67,8 @@ def load_library() -> ctypes.CDLL:
     lib.draft_head_rerank.argtypes = [P, P, i64, i32, i32, i32, P, P, i32, i32, P, P, P]
     lib.draft_head_argmax.restype = i32
     lib.draft_head_argmax.argtypes = [P, P, i32, i32, P, P, P]
+    lib.draft_head_stream_read.restype = i32
+    lib.draft_head_stream_read.argtypes = [P, sz, P, P]
     _lib = lib
     return lib
 
@@ -214,6 +216,20 @@ def draft_head_rerank(x, w, cand_val, cand_id, R: int = 32, rr_id=None, rr_val=N
     _check(lib.draft_head_rerank(_ptr(x), _ptr(w), ldw, M, K, n, _ptr(cand_val), _ptr(cand_id), ncand,
                                  R, _ptr(rr_id), _ptr(rr_val), _stream(stream)))
     return rr_id, rr_val
+
+
+DH_READ_BLOCKS = 2048
+
+
+def draft_head_stream_read(buf, out=None, stream=None):
+    """Read a CUDA tensor's bytes once (the device read-rate reference);
+    returns the uint32 [DH_READ_BLOCKS] XOR folds of the workgroups' spans."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty(DH_READ_BLOCKS, dtype=torch.int32, device=buf.device)
+    _check(lib.draft_head_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), _stream(stream)))
+    return out
 
 
 def draft_head_argmax(rr_id, rr_val, out_id=None, out_val=None, stream=None):

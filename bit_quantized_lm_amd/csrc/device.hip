@@ -1857,6 +1857,35 @@ int launch_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, int32
 
 hipStream_t as_stream(void* p) { return reinterpret_cast<hipStream_t>(p); }
 
+// Streaming-read reference: the achievable HBM read rate on this device, read
+// the way the coarse kernel reads its codes (16-byte nontemporal loads, each
+// workgroup a contiguous span, eight loads per lane in flight).  Workgroup b
+// folds its span with XOR into out[b].
+constexpr int kReadBlocks = DH_READ_BLOCKS;
+constexpr int kReadUnroll = 8;
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, size_t n16,
+                                                          uint32_t* __restrict__ out) {
+  const size_t per = (n16 + kReadBlocks - 1) / kReadBlocks;
+  const size_t lo = (size_t)blockIdx.x * per, hi = std::min(n16, lo + per);
+  uint32_t acc = 0u;
+  for (size_t i = lo + threadIdx.x; i < hi; i += 256 * kReadUnroll) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) {
+      const size_t k = i + 256 * u;
+      v[u] = k < hi ? __builtin_nontemporal_load(p + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  __shared__ uint32_t wx[4];
+  if ((threadIdx.x & 63) == 0) wx[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = wx[0] ^ wx[1] ^ wx[2] ^ wx[3];
+}
+
 }  // namespace
 
 extern "C" {
@@ -1885,6 +1914,15 @@ int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, i
   int rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
   if (rc) return rc;
   return launch_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, as_stream(stream));
+}
+
+int draft_head_stream_read(const void* p, size_t bytes, uint32_t* out, void* stream) {
+  if (!p || !out) return dh::fail(DH_EINVAL, "stream_read: null pointer");
+  if (!aligned16(p) || bytes % 16 != 0 || bytes == 0)
+    return dh::fail(DH_EINVAL, "stream_read: p must be 16-byte aligned and bytes a positive multiple of 16");
+  hipLaunchKernelGGL(stream_read_kernel, dim3(kReadBlocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const u32x4*>(p), bytes / 16, out);
+  return launch_error("stream_read_kernel");
 }
 
 int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, int32_t* out_id,

@@ -194,6 +194,20 @@ int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
                        size_t workspace_bytes, void* stream, void* coarse_start_event,
                        void* coarse_stop_event);
 
+/*
+ * DEVICE.  Measurement reference, not part of the head: reads `bytes` bytes at
+ * p once, with the coarse kernel's kind of loads (16-byte nontemporal loads,
+ * each of DH_READ_BLOCKS workgroups streaming one contiguous span), so that
+ * its duration gives the read rate the device achieves.  out[b] = XOR of the
+ * 32-bit words of workgroup b's span (span b = words [b*S, (b+1)*S) of the
+ * 16-byte words, S = ceil(bytes/16 / DH_READ_BLOCKS), cut at the end).
+ *   p    device, 16-byte aligned, bytes a positive multiple of 16
+ *   out  device, uint32 [DH_READ_BLOCKS]
+ * Errors: DH_EINVAL, DH_EHIP.
+ */
+#define DH_READ_BLOCKS 2048
+int draft_head_stream_read(const void* p, size_t bytes, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

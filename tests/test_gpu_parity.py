@@ -270,3 +270,21 @@ def test_workspace_reuse_leaves_counters_zero(dev):
         for key in want:
             assert torch.equal(got[key], want[key]), (m, key)
         assert int(torch.count_nonzero(ws[:512])) == 0, m
+
+
+@pytest.mark.parametrize("words", [4, 1000, 2048 * 4 * 3 + 4 * 5, (3 << 20) + 12])
+def test_stream_read_folds_every_word(dev, words):
+    """The read-rate reference reads every word once: each workgroup's XOR
+    fold equals the fold of its span, computed on the host."""
+    rng = np.random.default_rng(words)
+    host = rng.integers(0, 2 ** 32, size=words, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(dev)
+    out = B.draft_head_stream_read(buf).cpu().numpy().view(np.uint32)
+    n16 = words // 4
+    per = -(-n16 // B.DH_READ_BLOCKS)
+    want = np.zeros(B.DH_READ_BLOCKS, np.uint32)
+    for b in range(B.DH_READ_BLOCKS):
+        lo, hi = b * per * 4, min(n16, (b + 1) * per) * 4
+        if lo < hi:
+            want[b] = np.bitwise_xor.reduce(host[lo:hi])
+    assert np.array_equal(out, want)

@@ -25,7 +25,8 @@ def test_library_exports_every_header_symbol(lib):
     names = B.header_functions()
     assert set(names) == {"draft_head_last_error", "draft_head_sizes", "draft_head_quantize_pack",
                           "draft_head_tile", "draft_head_workspace_bytes", "draft_head_coarse",
-                          "draft_head_rerank", "draft_head_argmax", "draft_head_forward"}
+                          "draft_head_rerank", "draft_head_argmax", "draft_head_forward",
+                          "draft_head_stream_read"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -223,6 +224,14 @@ def test_argmax_validation(lib):
     _err(lib, lib.draft_head_argmax(FAKE, FAKE, 0, 8, FAKE, FAKE, None), B.DH_EINVAL)
     _err(lib, lib.draft_head_argmax(FAKE, FAKE, 1, 0, FAKE, FAKE, None), B.DH_EUNSUP)
     _err(lib, lib.draft_head_argmax(FAKE, FAKE, 1, 1025, FAKE, FAKE, None), B.DH_EUNSUP)
+
+
+def test_stream_read_validation(lib):
+    _err(lib, lib.draft_head_stream_read(None, 4096, FAKE, None), B.DH_EINVAL)
+    _err(lib, lib.draft_head_stream_read(FAKE, 4096, None, None), B.DH_EINVAL)
+    _err(lib, lib.draft_head_stream_read(MIS, 4096, FAKE, None), B.DH_EINVAL)
+    _err(lib, lib.draft_head_stream_read(FAKE, 4100, FAKE, None), B.DH_EINVAL)
+    _err(lib, lib.draft_head_stream_read(FAKE, 0, FAKE, None), B.DH_EINVAL)
 
 
 def test_python_errors_are_value_errors(lib):
