@@ -1401,11 +1401,12 @@ constexpr int kWideDot = 10;       // 16-byte loads of x and of W in flight per 
 
 struct WideShared {
   unsigned int hist[256];
+  unsigned int bmax[16][64];   // per wave, each lane's largest block maximum
   int qual[DH_MAX_R];
   unsigned long long keys[DH_MAX_R];
   unsigned long long list[DH_MAX_R];
   unsigned long long T;
-  int nq, ns;
+  int nq, ns, qcur;
   int last;
 };
 
@@ -1422,67 +1423,92 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
   const float* cv = A.cand_val + (size_t)m * ncand;
   const int32_t* ci = A.cand_id + (size_t)m * ncand;
 
-  if (wave == 0) {
-    // block b = lane + 64 j: its maximum's key is slot_key(value, b * kcand),
-    // held as the upper half alone (0: no such block); the lower half is
-    // ~(b * kcand), so keys compare as (upper, then lower j first)
-    uint32_t mo[kFastNV];
+  // Block b = lane + 64 j, j = JW * wave + jj: its maximum's key is
+  // slot_key(value, b * kcand), held as the upper half alone (0: no such
+  // block); the lower half is ~(b * kcand), so keys compare as (upper, then
+  // lower j first).  Each wave holds JW of every lane's kFastNV maxima.
+  constexpr int NW = NTHR / 64, JW = kFastNV / NW;
+  static_assert(kFastNV % NW == 0 && NW <= 16, "maxima split over the waves");
+  uint32_t mo[JW];
 #pragma unroll
-    for (int j = 0; j < kFastNV; ++j) mo[j] = __float_as_uint(cv[min(lane + 64 * j, nblk - 1) * kcand]);   // clamped loads
+  for (int jj = 0; jj < JW; ++jj)
+    mo[jj] = __float_as_uint(cv[min(lane + 64 * (JW * wave + jj), nblk - 1) * kcand]);   // clamped loads
 #pragma unroll
-    for (int j = 0; j < kFastNV; ++j)
-      mo[j] = lane + 64 * j < nblk ? (uint32_t)(slot_key(__uint_as_float(mo[j]), 0) >> 32) : 0u;
-    auto lower = [&](int j) { return 0xFFFFFFFFu - (uint32_t)((lane + 64 * j) * kcand); };
-    auto at_least = [&](int j, uint32_t to, uint32_t tl) {   // key of j >= (to, tl); to >= 1
-      const uint32_t o = mo[j];
-      return (o > to) | ((o == to) & (lower(j) >= tl));
-    };
-    uint32_t bo = 0u;   // the lane's largest upper half
+  for (int jj = 0; jj < JW; ++jj)
+    mo[jj] = lane + 64 * (JW * wave + jj) < nblk ? (uint32_t)(slot_key(__uint_as_float(mo[jj]), 0) >> 32) : 0u;
+  auto lower = [&](int j) { return 0xFFFFFFFFu - (uint32_t)((lane + 64 * j) * kcand); };
+  auto at_least = [&](int jj, uint32_t to, uint32_t tl) {   // key of (lane, JW wave + jj) >= (to, tl); to >= 1
+    const uint32_t o = mo[jj];
+    return (o > to) | ((o == to) & (lower(JW * wave + jj) >= tl));
+  };
+  uint32_t* so = reinterpret_cast<uint32_t*>(sh.keys);   // every maximum, for the exact fallback
+  uint32_t bw = 0u;
 #pragma unroll
-    for (int j = 0; j < kFastNV; ++j) bo = max(bo, mo[j]);
-    // T' = (to, 0) with to the R-th largest of the 64 lane maxima's upper
-    // halves (bisection over its bits, counting lanes by ballot): at least R
-    // lanes hold a block maximum >= T', so T' is at most the R-th largest
-    // block maximum.
-    uint32_t to = 0u, tl = 0u;
-    int nq = 0;
-    if (R <= 64) {
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t t = to | (1u << bit);
-        if (__popcll(__ballot(bo >= t)) >= R) to = t;
-      }
+  for (int jj = 0; jj < JW; ++jj) {
+    bw = max(bw, mo[jj]);
+    so[64 * (JW * wave + jj) + lane] = mo[jj];
+  }
+  sh.bmax[wave][lane] = bw;
+  if (tid == 0) {
+    sh.nq = 0;
+    sh.qcur = 0;
+    sh.ns = 0;
+  }
+  __syncthreads();
+  // T' = (to, 0) with to the R-th largest of the 64 lane maxima's upper
+  // halves (bisection over its bits, counting lanes by ballot; every wave
+  // finds the same value): at least R lanes hold a block maximum >= T', so
+  // T' is at most the R-th largest block maximum.
+  uint32_t bo = 0u;
 #pragma unroll
-      for (int j = 0; j < kFastNV; ++j) nq += __popcll(__ballot(at_least(j, to, 0u)));
+  for (int w = 0; w < NW; ++w) bo = max(bo, sh.bmax[w][lane]);
+  uint32_t to = 0u, tl = 0u;
+  if (R <= 64) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t t = to | (1u << bit);
+      if (__popcll(__ballot(bo >= t)) >= R) to = t;
     }
-    if (to == 0u || nq * kcand > DH_MAX_R) {   // exact R-th largest maximum; keys read back from LDS
-      uint32_t* so = reinterpret_cast<uint32_t*>(sh.keys);   // 64 * kFastNV words
+    int nw = 0;
 #pragma unroll
-      for (int j = 0; j < kFastNV; ++j) so[64 * j + lane] = mo[j];
-      __builtin_amdgcn_s_waitcnt(0xc07f);
+    for (int jj = 0; jj < JW; ++jj) nw += __popcll(__ballot(at_least(jj, to, 0u)));
+    if (lane == 0) atomicAdd(&sh.nq, nw);
+  }
+  __syncthreads();
+  if (to == 0u || sh.nq * kcand > DH_MAX_R) {   // uniform: the exact R-th largest maximum
+    if (wave == 0) {
       const unsigned long long T = wave_kth_largest_of<kFastNV, 1>(
           [&](int j) -> unsigned long long {
             const uint32_t o = *reinterpret_cast<volatile uint32_t*>(so + 64 * j + lane);
             return o ? ((unsigned long long)o << 32) | lower(j) : 0ull;
           },
           R, sh.hist);
-      to = (uint32_t)(T >> 32);
-      tl = (uint32_t)T;
+      if (lane == 0) sh.T = T;
     }
-    const unsigned long long T = ((unsigned long long)to << 32) | tl;
-    nq = 0;
+    __syncthreads();
+    to = (uint32_t)(sh.T >> 32);
+    tl = (uint32_t)sh.T;
+  } else if (tid == 0) {
+    sh.T = (unsigned long long)to << 32;
+  }
+  {   // the qualifying blocks, compacted (their order does not matter)
+    unsigned long long bal[JW];
+    int nw = 0;
 #pragma unroll
-    for (int j = 0; j < kFastNV; ++j) {
-      const bool q = at_least(j, to, tl);
-      const unsigned long long bal = __ballot(q);
-      if (q) sh.qual[nq + lane_prefix(bal)] = lane + 64 * j;
-      nq += __popcll(bal);
+    for (int jj = 0; jj < JW; ++jj) {
+      bal[jj] = __ballot(at_least(jj, to, tl));
+      nw += __popcll(bal[jj]);
     }
-    if (lane == 0) {
-      sh.nq = nq;
-      sh.ns = 0;
-      sh.T = T;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&sh.qcur, nw);
+    base = __shfl(base, 0, 64);
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj) {
+      if ((bal[jj] >> lane) & 1ull) sh.qual[base + lane_prefix(bal[jj])] = lane + 64 * (JW * wave + jj);
+      base += __popcll(bal[jj]);
     }
   }
+  __syncthreads();
+  if (tid == 0) sh.nq = sh.qcur;
   __syncthreads();
   {   // the survivors, gathered by the whole workgroup (their order does not matter)
     const int items = sh.nq * kcand;   // <= DH_MAX_R
