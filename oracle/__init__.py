@@ -14,8 +14,9 @@ Modules
 bf16     bf16 <-> float conversions (round to nearest even), own code.
 quant    min/max asymmetric int2 quantiser, quarter-split packing, unpacking
          and the effective weight defined by the stored scale pair.
-head     coarse scores, block top-KCAND, row top-R, exact rerank, argmax, and
-         the exact bf16 head (for agreement reports only).
+head     coarse scores, block top-KCAND, row top-R, exact rerank, argmax, the
+         bf16 row handed to the caller (full or top-k only), and the exact
+         bf16 head (for agreement reports only).
 brute    pure-Python, exact-rational re-statement of every step for tiny
          shapes; pins the vectorised code.
 
@@ -34,4 +35,4 @@ from . import bf16, quant, head, brute  # noqa: F401
 from .quant import (GROUP, quantize, pack_quarter_split, unpack_quarter_split,  # noqa: F401
                     effective_weight, quantize_pack)
 from .head import (BLOCK_N, coarse, coarse_collapse, block_topk, row_topr,  # noqa: F401
-                   rerank_exact, final_argmax, exact_head, pipeline, tie_rows)
+                   rerank_exact, final_argmax, logits_row, exact_head, pipeline, tie_rows)

@@ -165,6 +165,31 @@ def final_argmax(rr_id, e):
     return out_id, out_val
 
 
+def logits_row(rr_id, rr_val, n, coarse_f32=None, topk_only=False):
+    """The bf16 row `_apply_head_int2` hands to its caller after the rerank.
+
+    The coarse scores rounded to bf16 (the row `_draft_head_int2` writes), or,
+    for a top-k caller (`_radiance_topk_only`), -inf in every entry; then each
+    reranked id's exact value, rounded to bf16, is written over its entry
+    (`y.scatter_(1, idx, ex.to(bfloat16))`).  Reading: entries of rr_id that
+    are -1 (a row with fewer than R candidates) are skipped.  `coarse_f32`:
+    float32 [M][N] (not used when topk_only); returns bf16 bit patterns [M][N].
+    """
+    rr_id = np.asarray(rr_id)
+    rr_val = np.asarray(rr_val, dtype=np.float32)
+    m, r = rr_id.shape
+    if topk_only:
+        y = np.full((m, n), 0xFF80, dtype=np.uint16)        # bf16 -inf
+    else:
+        y = bf16.from_f32(np.asarray(coarse_f32, dtype=np.float32)).reshape(m, n).copy()
+    for row in range(m):
+        for j in range(r):
+            i = int(rr_id[row, j])
+            if i >= 0:
+                y[row, i] = bf16.from_f32(rr_val[row, j:j + 1])[0]
+    return y
+
+
 def exact_head(x_bits, w_bits):
     """E[m][n] = x . W_bf16[n] in float64 (the bf16 head the method stands in for).
 

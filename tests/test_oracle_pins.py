@@ -295,3 +295,40 @@ def test_kcand_is_the_recall_lever():
     hit1 = oracle.pipeline(x, w, packed, S, ZS, kcand=1, r=32)["out_id"]
     assert np.array_equal(hit8, winners)
     assert np.sum(hit1 != winners) >= 2
+
+
+# ------------------------------------------------------- row for the caller
+def test_logits_row_fixture(golden):
+    """The row handed to the caller, hand-derived (full and top-k only)."""
+    fx = golden("logits_row_example.txt")
+    n = int(fx["N"][0][0])
+    coarse = np.array([float(v) for v in fx["coarse"][0]], dtype=np.float32)[None, :]
+    rr_id = np.array([[int(v) for v in fx["rr_id"][0]]])
+    rr_val = np.array([[float(v) for v in fx["rr_val"][0]]], dtype=np.float32)
+    full = oracle.logits_row(rr_id, rr_val, n, coarse_f32=coarse)
+    topk = oracle.logits_row(rr_id, rr_val, n, topk_only=True)
+    assert [int(b) for b in full[0]] == [int(v, 16) for v in fx["full"][0]]
+    assert [int(b) for b in topk[0]] == [int(v, 16) for v in fx["topk"][0]]
+
+
+@pytest.mark.parametrize("topk_only", [False, True])
+def test_logits_row_matches_exact_rounding(topk_only):
+    """Every entry against exact rational rounding: a reranked id holds its exact
+    value in bf16, every other entry the coarse value in bf16 (or -inf)."""
+    rng = np.random.default_rng(7)
+    m, n, r = 3, 300, 20
+    coarse = (rng.standard_normal((m, n)) * 4).astype(np.float32)
+    rr_id = np.stack([rng.choice(n, size=r, replace=False) for _ in range(m)])
+    rr_id[2, 15:] = -1
+    rr_val = (rng.standard_normal((m, r)) * 4).astype(np.float32)
+    y = oracle.logits_row(rr_id, rr_val, n, coarse_f32=coarse, topk_only=topk_only)
+    for row in range(m):
+        exact = {int(i): j for j, i in enumerate(rr_id[row]) if i >= 0}
+        for col in range(n):
+            if col in exact:
+                want = brute.bf16_value_bits(brute.bf16(Fraction(float(rr_val[row, exact[col]]))))
+            elif topk_only:
+                want = 0xFF80
+            else:
+                want = brute.bf16_value_bits(brute.bf16(Fraction(float(coarse[row, col]))))
+            assert int(y[row, col]) == want, (row, col)
