@@ -67,6 +67,8 @@ def load_library() -> ctypes.CDLL:
     lib.draft_head_rerank.argtypes = [P, P, i64, i32, i32, i32, P, P, i32, i32, P, P, P]
     lib.draft_head_argmax.restype = i32
     lib.draft_head_argmax.argtypes = [P, P, i32, i32, P, P, P]
+    lib.draft_head_logits_row.restype = i32
+    lib.draft_head_logits_row.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
     lib.draft_head_stream_read.restype = i32
     lib.draft_head_stream_read.argtypes = [P, sz, P, P]
     _lib = lib
@@ -218,6 +220,19 @@ def draft_head_rerank(x, w, cand_val, cand_id, R: int = 32, rr_id=None, rr_val=N
     return rr_id, rr_val
 
 
+def draft_head_logits_row(rr_id, rr_val, N: int, coarse=None, topk_only=False, out=None, stream=None):
+    """The bf16 row handed to the caller: bf16(coarse) (or -inf with
+    topk_only) with the reranked ids' exact values; returns int16 bits [M][N]."""
+    import torch
+    lib = load_library()
+    M, R = rr_id.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int16, device=rr_id.device)
+    _check(lib.draft_head_logits_row(_ptr(coarse), _ptr(rr_id), _ptr(rr_val), M, N, R, 1 if topk_only else 0,
+                                     _ptr(out), _stream(stream)))
+    return out
+
+
 DH_READ_BLOCKS = 2048
 
 
@@ -318,6 +333,16 @@ class DraftHead:
         return draft_head_forward(x, self.tiled, self.pairs, self.w, self.N, self.kcand, self.R, out=out,
                                   coarse_out=coarse_out, workspace=workspace, stream=stream,
                                   coarse_events=coarse_events)
+
+    def logits_row(self, x, topk_only=False, stream=None):
+        """One call plus the bf16 row the page hands to its caller (full, or
+        top-k only); returns the forward outputs with "row" added."""
+        import torch
+        coarse = None if topk_only else torch.empty((x.shape[0], self.N), dtype=torch.float32, device=x.device)
+        out = self(x, coarse_out=coarse, stream=stream)
+        out["row"] = draft_head_logits_row(out["rr_id"], out["rr_val"], self.N, coarse=coarse,
+                                           topk_only=topk_only, stream=stream)
+        return out
 
     def staged(self, x, coarse_out=None, stream=None):
         """The same call as three library calls (coarse, rerank, argmax)."""

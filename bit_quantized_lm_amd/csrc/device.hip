@@ -1883,6 +1883,39 @@ int launch_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, int32
 
 hipStream_t as_stream(void* p) { return reinterpret_cast<hipStream_t>(p); }
 
+// The bf16 row handed to the caller (`_apply_head_int2` after the rerank):
+// bf16(coarse), or -inf for a top-k caller, with each reranked id's exact
+// value (bf16) in its entry.  Grid (ceil(N / kRowChunk), M): a workgroup
+// first marks which entries of its chunk are reranked (LDS: rank, or -1),
+// then writes every entry of the chunk once.
+constexpr int kRowChunk = 4096;
+
+__global__ __launch_bounds__(256) void logits_row_kernel(const float* __restrict__ coarse,
+                                                         const int32_t* __restrict__ rr_id,
+                                                         const float* __restrict__ rr_val, int N, int R,
+                                                         int topk_only, uint16_t* __restrict__ row_out) {
+  __shared__ int16_t rank[kRowChunk];
+  const int m = blockIdx.y, n0 = blockIdx.x * kRowChunk, tid = threadIdx.x;
+  const int len = min(kRowChunk, N - n0);
+  for (int i = tid; i < kRowChunk; i += 256) rank[i] = -1;
+  __syncthreads();
+  for (int r = tid; r < R; r += 256) {
+    const int id = rr_id[(size_t)m * R + r];
+    if (id >= n0 && id < n0 + len) rank[id - n0] = (int16_t)r;
+  }
+  __syncthreads();
+  const float* cr = coarse ? coarse + (size_t)m * N + n0 : nullptr;
+  const float* vr = rr_val + (size_t)m * R;
+  uint16_t* out = row_out + (size_t)m * N + n0;
+  for (int i = tid; i < len; i += 256) {
+    const int r = rank[i];
+    uint32_t b;
+    if (r >= 0) b = f32_to_bf16_rne(vr[r]);
+    else b = topk_only ? 0xFF80u : f32_to_bf16_rne(cr[i]);
+    out[i] = (uint16_t)b;
+  }
+}
+
 // Streaming-read reference: the achievable HBM read rate on this device, read
 // the way the coarse kernel reads its codes (16-byte nontemporal loads, each
 // workgroup a contiguous span, eight loads per lane in flight).  Workgroup b
@@ -1940,6 +1973,19 @@ int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, i
   int rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
   if (rc) return rc;
   return launch_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, as_stream(stream));
+}
+
+int draft_head_logits_row(const float* coarse, const int32_t* rr_id, const float* rr_val, int M, int N, int R,
+                          int topk_only, uint16_t* row_out, void* stream) {
+  if (!rr_id || !rr_val || !row_out) return dh::fail(DH_EINVAL, "logits_row: null pointer");
+  if (!coarse && !topk_only) return dh::fail(DH_EINVAL, "logits_row: coarse is needed unless topk_only");
+  int rc = check_m(M);
+  if (rc) return rc;
+  if (N < 1) return dh::fail(DH_ESHAPE, "logits_row: N must be >= 1 (got %d)", N);
+  if (R < 1 || R > DH_MAX_R) return dh::fail(DH_EUNSUP, "logits_row: R must be in 1..%d (got %d)", DH_MAX_R, R);
+  hipLaunchKernelGGL(logits_row_kernel, dim3((N + kRowChunk - 1) / kRowChunk, M), dim3(256), 0, as_stream(stream),
+                     coarse, rr_id, rr_val, N, R, topk_only ? 1 : 0, row_out);
+  return launch_error("logits_row_kernel");
 }
 
 int draft_head_stream_read(const void* p, size_t bytes, uint32_t* out, void* stream) {

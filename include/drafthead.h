@@ -195,6 +195,25 @@ int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
                        void* coarse_stop_event);
 
 /*
+ * DEVICE.  The bf16 row the page's `_apply_head_int2` hands to its caller
+ * after the rerank: y[m][n] = bf16(coarse[m][n]) (round to nearest even), or
+ * -inf for a top-k caller (`_radiance_topk_only`, topk_only != 0: only the
+ * reranked ids stay eligible); then, for every r with rr_id[m][r] >= 0,
+ * y[m][rr_id[m][r]] = bf16(rr_val[m][r]) (`y.scatter_(1, idx, ex)`).  Ids of
+ * -1 write nothing; the ids of a row must be distinct (as draft_head_rerank
+ * writes them).
+ *   coarse     device, fp32 [M][N] (coarse_out of draft_head_coarse or
+ *              draft_head_forward); may be NULL when topk_only
+ *   rr_id, rr_val  device, [M][R] as written by draft_head_rerank / forward
+ *   row_out    out, bf16 bits [M][N]
+ * Limits: 1 <= M <= DH_MAX_M, N >= 1, 1 <= R <= DH_MAX_R.
+ * Errors: DH_EINVAL (null pointer, coarse NULL without topk_only),
+ *         DH_ESHAPE, DH_EUNSUP, DH_EHIP.
+ */
+int draft_head_logits_row(const float* coarse, const int32_t* rr_id, const float* rr_val, int M, int N,
+                          int R, int topk_only, uint16_t* row_out, void* stream);
+
+/*
  * DEVICE.  Measurement reference, not part of the head: reads `bytes` bytes at
  * p once, with the coarse kernel's kind of loads (16-byte nontemporal loads,
  * each of DH_READ_BLOCKS workgroups streaming one contiguous span), so that

@@ -288,3 +288,48 @@ def test_stream_read_folds_every_word(dev, words):
         if lo < hi:
             want[b] = np.bitwise_xor.reduce(host[lo:hi])
     assert np.array_equal(out, want)
+
+
+@pytest.mark.parametrize("m,n,r", [(1, 1, 1), (1, 4095, 32), (2, 4096, 32), (3, 4097, 100),
+                                   (4, 9000, 1024), (1, 124160, 32)])
+@pytest.mark.parametrize("topk_only", [False, True])
+def test_logits_row_bit_exact(dev, m, n, r, topk_only):
+    """The row handed to the caller, on seeded inputs: bit-exact against the oracle."""
+    rng = np.random.default_rng(1000 * m + n + r)
+    coarse = (rng.standard_normal((m, n)) * 4).astype(np.float32)
+    rr_id = np.stack([rng.choice(n, size=r, replace=False) for _ in range(m)]).astype(np.int32)
+    if r > 1:
+        rr_id[-1, r // 2:] = -1          # a padded row
+    rr_val = (rng.standard_normal((m, r)) * 4).astype(np.float32)
+    want = oracle.logits_row(rr_id, rr_val, n, coarse_f32=coarse, topk_only=topk_only)
+    _log(f"logits_row m={m} n={n} r={r} topk_only={topk_only}")
+    got = B.draft_head_logits_row(torch.from_numpy(rr_id).to(dev), torch.from_numpy(rr_val).to(dev), n,
+                                  coarse=None if topk_only else torch.from_numpy(coarse).to(dev),
+                                  topk_only=topk_only)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().view(np.uint16), want)
+
+
+@pytest.mark.parametrize("topk_only", [False, True])
+def test_logits_row_end_to_end(dev, topk_only):
+    """One call plus the row, against the oracle's own pipeline: the reranked
+    ids hold their exact values, every other entry the coarse value (or -inf),
+    within the value tolerance plus one bf16 step."""
+    m, k, n = 3, 1024, 5000
+    w = workload.gen_weight(n, k, seed=97)
+    x = workload.gen_x(m, k, seed=98)
+    head = B.DraftHead.from_weight(w, kcand=8, R=32, device=dev)
+    got = head.logits_row(_to_dev(x, dev), topk_only=topk_only)
+    torch.cuda.synchronize()
+    ref = oracle.pipeline(x, w, *oracle.quantize_pack(w), kcand=8, r=32)
+    assert np.array_equal(got["rr_id"].cpu().numpy(), ref["rr_id"])   # no near-ties at this seed
+    row = got["row"].cpu().numpy().view(np.uint16)
+    want = oracle.logits_row(ref["rr_id"], ref["rr_val"], n, coarse_f32=ref["coarse"].astype(np.float32),
+                             topk_only=topk_only)
+    gv = oracle.bf16.to_f64(row)
+    wv = oracle.bf16.to_f64(want)
+    fin = np.isfinite(wv)
+    assert np.array_equal(np.isfinite(gv), fin)
+    rms = np.sqrt(np.mean(ref["coarse"] ** 2, axis=1))[:, None]
+    lim = 2e-3 * np.abs(wv) + 2e-3 * rms + 2.0 ** -7 * np.abs(wv)
+    assert np.all(np.abs(gv - wv)[fin] <= lim[fin])

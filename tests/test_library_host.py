@@ -26,7 +26,7 @@ def test_library_exports_every_header_symbol(lib):
     assert set(names) == {"draft_head_last_error", "draft_head_sizes", "draft_head_quantize_pack",
                           "draft_head_tile", "draft_head_workspace_bytes", "draft_head_coarse",
                           "draft_head_rerank", "draft_head_argmax", "draft_head_forward",
-                          "draft_head_stream_read"}
+                          "draft_head_stream_read", "draft_head_logits_row"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -224,6 +224,19 @@ def test_argmax_validation(lib):
     _err(lib, lib.draft_head_argmax(FAKE, FAKE, 0, 8, FAKE, FAKE, None), B.DH_EINVAL)
     _err(lib, lib.draft_head_argmax(FAKE, FAKE, 1, 0, FAKE, FAKE, None), B.DH_EUNSUP)
     _err(lib, lib.draft_head_argmax(FAKE, FAKE, 1, 1025, FAKE, FAKE, None), B.DH_EUNSUP)
+
+
+def test_logits_row_validation(lib):
+    f = lib.draft_head_logits_row
+    _err(lib, f(FAKE, None, FAKE, 1, 64, 8, 0, FAKE, None), B.DH_EINVAL)
+    _err(lib, f(FAKE, FAKE, None, 1, 64, 8, 0, FAKE, None), B.DH_EINVAL)
+    _err(lib, f(FAKE, FAKE, FAKE, 1, 64, 8, 0, None, None), B.DH_EINVAL)
+    _err(lib, f(None, FAKE, FAKE, 1, 64, 8, 0, FAKE, None), B.DH_EINVAL)   # coarse needed unless top-k only
+    _err(lib, f(FAKE, FAKE, FAKE, 0, 64, 8, 0, FAKE, None), B.DH_EINVAL)
+    _err(lib, f(FAKE, FAKE, FAKE, 129, 64, 8, 0, FAKE, None), B.DH_EUNSUP)
+    _err(lib, f(FAKE, FAKE, FAKE, 1, 0, 8, 0, FAKE, None), B.DH_ESHAPE)
+    _err(lib, f(FAKE, FAKE, FAKE, 1, 64, 0, 0, FAKE, None), B.DH_EUNSUP)
+    _err(lib, f(FAKE, FAKE, FAKE, 1, 64, 1025, 0, FAKE, None), B.DH_EUNSUP)
 
 
 def test_stream_read_validation(lib):
