@@ -19,8 +19,9 @@ Prints one JSON line:
                M = 1, 8, 72 (value: M = 1)
   extra        per-M (1, 8, 72) times with the coarse kernel's p10/p50/p90 and
                its fractions of the HBM and bf16 MFMA peaks, the warm
-               (cache-resident) figure, and the device's achieved read rate
-               (the library's streaming-read reference) and copy rate
+               (cache-resident) figure, the time of the row handed to a
+               top-k caller (draft_head_logits_row), and the device's achieved
+               read rate (the library's streaming-read reference) and copy rate
 """
 from __future__ import annotations
 
@@ -155,6 +156,28 @@ class Rig:
         coarse_ms = np.array([a.elapsed_time(b) for a, b in evs])
         self.last_coarse_pct = {f"p{q}": round(float(np.percentile(coarse_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
         return total_ms / 1e3 / steps, float(np.mean(coarse_ms)) / 1e3, wall
+
+    def logits_row_us(self, m, reps=50):
+        """Time of draft_head_logits_row alone at M rows (full and top-k only)."""
+        torch, B = self.torch, self.B
+        coarse = torch.empty((m, N), dtype=torch.float32, device=self.dev)
+        out = self.heads[0](self.x[:m], coarse_out=coarse, stream=self.stream)
+        row = torch.empty((m, N), dtype=torch.int16, device=self.dev)
+        res = {}
+        for name, c, topk in (("full", coarse, False), ("topk_only", None, True)):
+            for _ in range(3):
+                B.draft_head_logits_row(out["rr_id"], out["rr_val"], N, coarse=c, topk_only=topk, out=row,
+                                        stream=self.stream)
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                B.draft_head_logits_row(out["rr_id"], out["rr_val"], N, coarse=c, topk_only=topk, out=row,
+                                        stream=self.stream)
+            e.record()
+            torch.cuda.synchronize()
+            res[name] = round(s.elapsed_time(e) / reps * 1e3, 2)
+        return res
 
     def read_bandwidth(self, reps=20):
         """The device's streaming read rate with the library's read reference
@@ -301,6 +324,8 @@ def main():
         tw, tkw, _ = rig.timed(m, args.steps, args.warmup, copies=1)
         extra["warm_not_hbm"] = {"us_per_call": round(tw * 1e6, 2), "coarse_us": round(tkw * 1e6, 2),
                                  "note": "one weight copy reused back to back: Infinity-Cache resident"}
+        extra["logits_row_us"] = {str(mm): rig.logits_row_us(mm) for mm in (1, 8, 72)}
+        log(f"row for the caller (draft_head_logits_row alone): {extra['logits_row_us']}")
         extra["device_copy_GBps"] = round(rig.copy_bandwidth(), 1)
         extra["stream_read_GBps"] = rig.read_bandwidth()
         log(f"read reference: {extra['stream_read_GBps']}, copy {extra['device_copy_GBps']}")

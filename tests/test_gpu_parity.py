@@ -204,6 +204,13 @@ def test_parity_full_shape(dev, full, m):
         E = oracle.exact_head(full["x"], full["w"])
         agree = int(np.sum(got["out_id"] == np.argmax(E, axis=1)))
         _log(f"full shape m=72: argmax agreement with the exact bf16 head {agree}/72 (reported)")
+        # a top-16 caller of the top-k-only row draws from the R reranked tokens only
+        top = np.argsort(-got["rr_val"], axis=1, kind="stable")[:, :16]
+        mine = np.take_along_axis(got["rr_id"], top, axis=1)
+        exact16 = np.argsort(-E, axis=1, kind="stable")[:, :16]
+        overlap = np.mean([len(set(mine[i]) & set(exact16[i])) / 16 for i in range(72)])
+        _log(f"full shape m=72: top-16 of the top-k-only row vs the exact head's top-16: "
+             f"{overlap:.3f} overlap (reported)")
 
 
 @pytest.mark.timeout(900)
