@@ -14,7 +14,8 @@ Modules
 bf16     bf16 <-> float conversions (round to nearest even), own code.
 quant    min/max asymmetric int2 quantiser, quarter-split packing, unpacking
          and the effective weight defined by the stored scale pair.
-head     coarse scores, block top-KCAND, row top-R, exact rerank, argmax, the
+head     coarse scores, block top-KCAND, row top-R, exact rerank (bf16 rows or
+         e4m3 rows with a per-row scale), argmax, the
          bf16 row handed to the caller (full or top-k only), and the exact
          bf16 head (for agreement reports only).
 brute    pure-Python, exact-rational re-statement of every step for tiny
@@ -35,4 +36,5 @@ from . import bf16, quant, head, brute  # noqa: F401
 from .quant import (GROUP, quantize, pack_quarter_split, unpack_quarter_split,  # noqa: F401
                     effective_weight, quantize_pack)
 from .head import (BLOCK_N, coarse, coarse_collapse, block_topk, row_topr,  # noqa: F401
-                   rerank_exact, final_argmax, logits_row, exact_head, pipeline, tie_rows)
+                   rerank_exact, final_argmax, logits_row, exact_head, pipeline, tie_rows,
+                   e4m3_value, rerank_exact_e4m3)

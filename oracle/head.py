@@ -140,6 +140,41 @@ def rerank_exact(x_bits, w_bits, rr_id):
     return out
 
 
+def e4m3_value(codes):
+    """Value of e4m3 bytes as `_rerank_exact` (FP8 branch) decodes them, float64.
+
+    The page's bit arithmetic: e = (b >> 3) & 15, mant = b & 7; magnitude
+    mant * 2^-9 when e == 0, else (1 + mant/8) * 2^(e-7); bit 7 is the sign.
+    Every byte decodes to a number (codes 0x7F / 0xFF give +-480: the page
+    does not treat them as NaN).
+    """
+    b = np.asarray(codes, dtype=np.int64)
+    e = (b >> 3) & 15
+    mant = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, mant * 2.0 ** -9, (1.0 + mant / 8.0) * np.exp2(e - 7.0))
+    return np.where((b & 128) != 0, -mag, mag)
+
+
+def rerank_exact_e4m3(x_bits, w8, scale, rr_id):
+    """e[m][r] = sum_k x[m][k] * wv[k], wv = float32(decode(W8[id][k]) * scale[id]).
+
+    `_rerank_exact` (FP8 branch): the head's own e4m3 rows, decoded by bit
+    arithmetic and multiplied by the row's float32 scale (one float32
+    rounding), accumulated in fp32 on the page (float64 here); -inf for id -1.
+    """
+    x = _x64(x_bits)
+    rr_id = np.asarray(rr_id)
+    w8 = np.asarray(w8)
+    scale = np.asarray(scale, dtype=np.float32)
+    out = np.full(rr_id.shape, -np.inf)
+    for row in range(rr_id.shape[0]):
+        ok = rr_id[row] >= 0
+        ids = rr_id[row][ok]
+        wv = (e4m3_value(w8[ids]).astype(np.float32) * scale[ids][:, None]).astype(np.float64)
+        out[row, ok] = wv @ x[row]
+    return out
+
+
 def final_argmax(rr_id, e):
     """Argmax over the R exact values of each row, float32 decision, ties -> lower id.
 

@@ -332,3 +332,58 @@ def test_logits_row_matches_exact_rounding(topk_only):
             else:
                 want = brute.bf16_value_bits(brute.bf16(Fraction(float(coarse[row, col]))))
             assert int(y[row, col]) == want, (row, col)
+
+
+# ------------------------------------------------------ e4m3 rerank source
+def test_e4m3_decode_fixture(golden):
+    fx = golden("e4m3_decode_example.txt")
+    for code, val in fx["code"]:
+        got = float(oracle.e4m3_value(np.array([int(code, 16)]))[0])
+        assert got == float(val) and np.signbit(got) == np.signbit(float(val)), code
+
+
+def test_e4m3_decode_is_the_standard_format_except_its_nan():
+    """The page's decode equals the e4m3 format's closed form (sign, 4-bit
+    exponent biased by 7, 3-bit mantissa, subnormals at exponent 0) for every
+    code but the two the format reserves for NaN, which the page reads as +-480."""
+    for b in range(256):
+        s, e, m = b >> 7, (b >> 3) & 15, b & 7
+        mag = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        want = -mag if s else mag
+        got = Fraction(float(oracle.e4m3_value(np.array([b]))[0]))
+        if (b & 0x7F) == 0x7F:
+            assert got == (-480 if s else 480)
+        else:
+            assert got == want, b
+
+
+def test_e4m3_rerank_equals_bf16_rerank_on_representable_rows():
+    """Rows that are e4m3 values times a power-of-two scale are exact in bf16
+    too: both rerank sources then give the same logits exactly."""
+    rng = np.random.default_rng(11)
+    n, k, m, r = 40, 256, 2, 6
+    codes = rng.integers(0, 256, size=(n, k)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                      # no +-480 (not a standard value)
+    scale = (2.0 ** rng.integers(-8, -4, size=n)).astype(np.float32)
+    wv = oracle.e4m3_value(codes) * scale[:, None]
+    w_bits = workload.f32_to_bf16_bits(wv.astype(np.float32))
+    assert np.array_equal(obf.to_f64(w_bits), wv)             # representable in bf16
+    x = workload.gen_x(m, k, seed=5)
+    rr_id = np.stack([rng.choice(n, size=r, replace=False) for _ in range(m)])
+    rr_id[1, 4:] = -1
+    a = oracle.rerank_exact_e4m3(x, codes, scale, rr_id)
+    b = oracle.rerank_exact(x, w_bits, rr_id)
+    assert np.array_equal(a, b)
+
+
+def test_synthetic_e4m3_head_rounds_to_nearest():
+    """The generator's codes are the nearest e4m3 value to w / scale (inputs only)."""
+    w = workload.gen_weight(64, 512, seed=3)
+    codes, scale = workload.e4m3_head(w)
+    v = obf.to_f64(w) / scale[:, None].astype(np.float64)
+    got = oracle.e4m3_value(codes)
+    table = np.unique(np.abs(oracle.e4m3_value(np.arange(0, 127))))
+    err = np.abs(got - v)
+    best = np.min(np.abs(np.abs(v)[..., None] - table[None, None, :]), axis=-1)
+    assert np.all(err <= best + 1e-12)
+    assert np.max(np.abs(got)) == 448.0
