@@ -67,6 +67,11 @@ def load_library() -> ctypes.CDLL:
     lib.draft_head_rerank.argtypes = [P, P, i64, i32, i32, i32, P, P, i32, i32, P, P, P]
     lib.draft_head_argmax.restype = i32
     lib.draft_head_argmax.argtypes = [P, P, i32, i32, P, P, P]
+    lib.draft_head_rerank_e4m3.restype = i32
+    lib.draft_head_rerank_e4m3.argtypes = [P, P, P, i64, i32, i32, i32, P, P, i32, i32, P, P, P]
+    lib.draft_head_forward_e4m3.restype = i32
+    lib.draft_head_forward_e4m3.argtypes = [P, i32, i32, i32, P, P, P, P, i64, i32, i32, P, P, P, P, P, P, P, P,
+                                            sz, P, P, P]
     lib.draft_head_logits_row.restype = i32
     lib.draft_head_logits_row.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
     lib.draft_head_stream_read.restype = i32
@@ -220,6 +225,24 @@ def draft_head_rerank(x, w, cand_val, cand_id, R: int = 32, rr_id=None, rr_val=N
     return rr_id, rr_val
 
 
+def draft_head_rerank_e4m3(x, w8, wscale, cand_val, cand_id, R: int = 32, rr_id=None, rr_val=None, N=None,
+                           stream=None):
+    """draft_head_rerank from e4m3 rows: w8 CUDA uint8 [N][ldw] (e4m3 bytes),
+    wscale CUDA fp32 [N].  Returns (rr_id int32 [M][R], rr_val fp32 [M][R])."""
+    import torch
+    lib = load_library()
+    M, K = x.shape
+    n = w8.shape[0] if N is None else N
+    ncand = cand_val.shape[1]
+    if rr_id is None:
+        rr_id = _empty((M, R), torch.int32, x)
+    if rr_val is None:
+        rr_val = _empty((M, R), torch.float32, x)
+    _check(lib.draft_head_rerank_e4m3(_ptr(x), _ptr(w8), _ptr(wscale), w8.stride(0), M, K, n, _ptr(cand_val),
+                                      _ptr(cand_id), ncand, R, _ptr(rr_id), _ptr(rr_val), _stream(stream)))
+    return rr_id, rr_val
+
+
 def draft_head_logits_row(rr_id, rr_val, N: int, coarse=None, topk_only=False, out=None, stream=None):
     """The bf16 row handed to the caller: bf16(coarse) (or -inf with
     topk_only) with the reranked ids' exact values; returns int16 bits [M][N]."""
@@ -282,13 +305,14 @@ def _event(ev):
 
 
 def draft_head_forward(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, out=None,
-                       coarse_out=None, workspace=None, stream=None, coarse_events=None):
+                       coarse_out=None, workspace=None, stream=None, coarse_events=None, wscale=None):
     """One full call (coarse -> rerank -> argmax) in one library call.
 
-    out: dict from forward_buffers (allocated when None); workspace: as for
-    draft_head_coarse; coarse_events: optional (start, stop) torch.cuda.Event
-    pair that takes the coarse kernel's own dispatch timestamps.  Returns the
-    dict of output tensors."""
+    w: the bf16 rows, or with wscale (fp32 [N]) the e4m3 rows (uint8) of the
+    rerank; out: dict from forward_buffers (allocated when None); workspace:
+    as for draft_head_coarse; coarse_events: optional (start, stop)
+    torch.cuda.Event pair that takes the coarse kernel's own dispatch
+    timestamps.  Returns the dict of output tensors."""
     lib = load_library()
     M, K = x.shape
     if out is None:
@@ -296,10 +320,14 @@ def draft_head_forward(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, 
     if workspace is None:
         workspace = workspace_for(M, K, x.device)
     e0, e1 = (None, None) if coarse_events is None else (_event(coarse_events[0]), _event(coarse_events[1]))
-    _check(lib.draft_head_forward(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0), kcand,
-                                  R, _ptr(out["cand_val"]), _ptr(out["cand_id"]), _ptr(out["rr_id"]),
-                                  _ptr(out["rr_val"]), _ptr(out["out_id"]), _ptr(out["out_val"]),
-                                  _ptr(coarse_out), *_ws(workspace), _stream(stream), e0, e1))
+    outs = (_ptr(out["cand_val"]), _ptr(out["cand_id"]), _ptr(out["rr_id"]), _ptr(out["rr_val"]),
+            _ptr(out["out_id"]), _ptr(out["out_val"]), _ptr(coarse_out), *_ws(workspace), _stream(stream), e0, e1)
+    if wscale is None:
+        _check(lib.draft_head_forward(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0), kcand,
+                                      R, *outs))
+    else:
+        _check(lib.draft_head_forward_e4m3(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), _ptr(wscale),
+                                           w.stride(0), kcand, R, *outs))
     return out
 
 
@@ -312,8 +340,10 @@ class DraftHead:
     staged(x) does the same with one library call per step.
     """
 
-    def __init__(self, tiled, pairs, w, N: int, K: int, kcand: int = 8, R: int = 32):
-        self.tiled, self.pairs, self.w = tiled, pairs, w
+    def __init__(self, tiled, pairs, w, N: int, K: int, kcand: int = 8, R: int = 32, wscale=None):
+        """w: the bf16 rows the rerank reads, or e4m3 rows (uint8) with their
+        per-row fp32 scale `wscale` (a per-channel FP8 head)."""
+        self.tiled, self.pairs, self.w, self.wscale = tiled, pairs, w, wscale
         self.N, self.K, self.kcand, self.R = N, K, kcand, R
 
     @classmethod
@@ -332,7 +362,7 @@ class DraftHead:
     def __call__(self, x, coarse_out=None, stream=None, out=None, coarse_events=None, workspace=None):
         return draft_head_forward(x, self.tiled, self.pairs, self.w, self.N, self.kcand, self.R, out=out,
                                   coarse_out=coarse_out, workspace=workspace, stream=stream,
-                                  coarse_events=coarse_events)
+                                  coarse_events=coarse_events, wscale=self.wscale)
 
     def logits_row(self, x, topk_only=False, stream=None):
         """One call plus the bf16 row the page hands to its caller (full, or
@@ -348,7 +378,10 @@ class DraftHead:
         """The same call as three library calls (coarse, rerank, argmax)."""
         cv, ci = draft_head_coarse(x, self.tiled, self.pairs, self.N, self.kcand,
                                    coarse_out=coarse_out, stream=stream)
-        rr_id, rr_val = draft_head_rerank(x, self.w, cv, ci, self.R, N=self.N, stream=stream)
+        if self.wscale is None:
+            rr_id, rr_val = draft_head_rerank(x, self.w, cv, ci, self.R, N=self.N, stream=stream)
+        else:
+            rr_id, rr_val = draft_head_rerank_e4m3(x, self.w, self.wscale, cv, ci, self.R, N=self.N, stream=stream)
         out_id, out_val = draft_head_argmax(rr_id, rr_val, stream=stream)
         return {"cand_val": cv, "cand_id": ci, "rr_id": rr_id, "rr_val": rr_val,
                 "out_id": out_id, "out_val": out_val}

@@ -82,7 +82,8 @@ __device__ __forceinline__ uint32_t scale_x_pair(uint32_t w) {
 // with the argmax the per-row arrival counters).
 struct RerankArgs {
   const uint16_t* x;
-  const uint16_t* w;
+  const void* w;          // bf16 rows (ldw elements), or e4m3 rows (ldw bytes) when wscale is set
+  const float* wscale;    // per-row scale of e4m3 rows, else null
   int64_t ldw;
   int K, N;
   const float* cand_val;
@@ -900,6 +901,82 @@ void coarse_mfma_kernel(BigArgs BA) {
 // Exact logits (`_rerank_exact`, bf16 branch): the 16 waves then take the R
 // selected rows of W in turn, one dot of length K each, fp32 products and sums,
 // all loads of a row issued before any is used.
+// Exact logit of one candidate row, x[m] . W[id], by one wave with every
+// load of the row issued before any is used (fp32 products and sums).
+//   bf16 rows (`_rerank_exact`, bf16 branch): lane l takes 8 consecutive k
+//   per 512; e4m3 rows (FP8 branch): lane l takes 16 consecutive k per 1024,
+//   each byte decoded by the page's bit arithmetic (e = (b >> 3) & 15,
+//   mant = b & 7: mant * 2^-9 if e == 0, else (1 + mant/8) * 2^(e-7); bit 7
+//   the sign) and multiplied by the row's scale, one fp32 rounding.
+constexpr int kDotBf16 = 10;   // 16-byte W loads per lane in flight (5120 k)
+constexpr int kDotE4m3 = 5;    // 16-byte W loads per lane in flight (5120 k)
+
+__device__ __forceinline__ float e4m3_page(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, mant = b & 7u;
+  const float sub = (float)mant * 0.001953125f;
+  const float nor = __uint_as_float(((e + 120u) << 23) | (mant << 20));
+  const float mag = e == 0u ? sub : nor;
+  return (b & 128u) ? -mag : mag;
+}
+
+template <bool kE4M3>
+__device__ float wave_dot(const void* w, int64_t ldw, uint32_t id, float scale, const uint16_t* xr, int K,
+                          int lane) {
+  float s0 = 0.f, s1 = 0.f;
+  if constexpr (!kE4M3) {
+    const uint16_t* wr = static_cast<const uint16_t*>(w) + (size_t)id * ldw;
+    for (int k0 = 0; k0 < K; k0 += 512 * kDotBf16) {
+      u32x4 wv[kDotBf16], xv[kDotBf16];
+#pragma unroll
+      for (int j = 0; j < kDotBf16; ++j) {   // clamped, unconditional loads
+        const int k = min(k0 + 512 * j + lane * 8, K - 8);
+        wv[j] = *reinterpret_cast<const u32x4*>(wr + k);
+        xv[j] = *reinterpret_cast<const u32x4*>(xr + k);
+      }
+#pragma unroll
+      for (int j = 0; j < kDotBf16; ++j) {
+        if (k0 + 512 * j + lane * 8 < K) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            s0 = __builtin_fmaf(lo_bf16(xv[j][c]), lo_bf16(wv[j][c]), s0);
+            s1 = __builtin_fmaf(hi_bf16(xv[j][c]), hi_bf16(wv[j][c]), s1);
+          }
+        }
+      }
+    }
+  } else {
+    const uint8_t* wr = static_cast<const uint8_t*>(w) + (size_t)id * ldw;
+    for (int k0 = 0; k0 < K; k0 += 1024 * kDotE4m3) {
+      u32x4 wv[kDotE4m3], xa[kDotE4m3], xb[kDotE4m3];
+#pragma unroll
+      for (int j = 0; j < kDotE4m3; ++j) {   // clamped, unconditional loads
+        const int k = min(k0 + 1024 * j + lane * 16, K - 16);
+        wv[j] = *reinterpret_cast<const u32x4*>(wr + k);
+        xa[j] = *reinterpret_cast<const u32x4*>(xr + k);
+        xb[j] = *reinterpret_cast<const u32x4*>(xr + k + 8);
+      }
+#pragma unroll
+      for (int j = 0; j < kDotE4m3; ++j) {
+        if (k0 + 1024 * j + lane * 16 < K) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {   // bytes 4c .. 4c+3 of the 16
+            const uint32_t b4 = wv[j][c];
+            const u32x4& xh = c < 2 ? xa[j] : xb[j];
+            const uint32_t x01 = xh[2 * (c & 1)], x23 = xh[2 * (c & 1) + 1];
+            s0 = __builtin_fmaf(lo_bf16(x01), e4m3_page(b4 & 255u) * scale, s0);
+            s1 = __builtin_fmaf(hi_bf16(x01), e4m3_page((b4 >> 8) & 255u) * scale, s1);
+            s0 = __builtin_fmaf(lo_bf16(x23), e4m3_page((b4 >> 16) & 255u) * scale, s0);
+            s1 = __builtin_fmaf(hi_bf16(x23), e4m3_page(b4 >> 24) * scale, s1);
+          }
+        }
+      }
+    }
+  }
+  float sum = s0 + s1;
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  return sum;
+}
+
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelCache = 16;
@@ -1095,9 +1172,10 @@ __device__ unsigned long long block_kth_largest(ForEach for_each_key, int k, uns
   return pre << shift;
 }
 
+template <bool kE4M3>
 __global__ __launch_bounds__(kSelThreads) void rerank_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t ldw, int K, int N,
-    const float* __restrict__ cand_val, const int32_t* __restrict__ cand_id, int ncand, int R,
+    const uint16_t* __restrict__ x, const void* __restrict__ w, const float* __restrict__ wscale, int64_t ldw,
+    int K, int N, const float* __restrict__ cand_val, const int32_t* __restrict__ cand_id, int ncand, int R,
     int32_t* __restrict__ rr_id, float* __restrict__ rr_val) {
   __shared__ SelectShared sh;
   const int m = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1232,38 +1310,15 @@ __global__ __launch_bounds__(kSelThreads) void rerank_kernel(
   for (int r = tid; r < R; r += kSelThreads)
     rr_id[(size_t)m * R + r] = (r < cnt) ? (int32_t)key_id(sh.keys[r]) : -1;
 
-  // exact logits of the selected rows: each wave issues all loads of a row
-  // (up to 5120 elements at a time) before using any of them
-  constexpr int kDotUnroll = 10;
+  // exact logits of the selected rows, one wave per row
   const uint16_t* xr = x + (size_t)m * K;
   for (int r = wave; r < R; r += kSelWaves) {
-    float s0 = 0.f, s1 = 0.f;
     const bool valid = r < cnt;
+    float sum = 0.f;
     if (valid) {
-      const int id = (int)key_id(sh.keys[r]);
-      const uint16_t* wr = w + (size_t)id * ldw;
-      for (int k0 = 0; k0 < K; k0 += 512 * kDotUnroll) {
-        u32x4 xv[kDotUnroll], wv[kDotUnroll];
-#pragma unroll
-        for (int j = 0; j < kDotUnroll; ++j) {   // clamped, unconditional loads
-          const int k = min(k0 + 512 * j + lane * 8, K - 8);
-          wv[j] = *reinterpret_cast<const u32x4*>(wr + k);
-          xv[j] = *reinterpret_cast<const u32x4*>(xr + k);
-        }
-#pragma unroll
-        for (int j = 0; j < kDotUnroll; ++j) {
-          if (k0 + 512 * j + lane * 8 < K) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              s0 = __builtin_fmaf(lo_bf16(xv[j][c]), lo_bf16(wv[j][c]), s0);
-              s1 = __builtin_fmaf(hi_bf16(xv[j][c]), hi_bf16(wv[j][c]), s1);
-            }
-          }
-        }
-      }
+      const uint32_t id = key_id(sh.keys[r]);
+      sum = wave_dot<kE4M3>(w, ldw, id, kE4M3 ? wscale[id] : 1.f, xr, K, lane);
     }
-    float sum = s0 + s1;
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
     if (lane == 0) rr_val[(size_t)m * R + r] = valid ? sum : -__builtin_inff();
   }
 }
@@ -1397,7 +1452,6 @@ __device__ unsigned long long wave_top2_threshold(const unsigned long long (&v)[
 //      (at least R, at most DH_MAX_R); each is ranked by counting the
 //      survivors above it, and the first R ranks are the list.
 constexpr int kWideThreads = 256;
-constexpr int kWideDot = 10;       // 16-byte loads of x and of W in flight per lane
 
 struct WideShared {
   unsigned int hist[256];
@@ -1542,7 +1596,7 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
   __syncthreads();
 }
 
-template <int NTHR, bool kArgmax>
+template <int NTHR, bool kArgmax, bool kE4M3>
 __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part, int nparts) {
   constexpr int NW = NTHR / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1553,30 +1607,7 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
   const int r = NW * part + wave;
   if (r < R) {
     const uint32_t id = key_id(sh.list[r]);
-    const uint16_t* wr = A.w + (size_t)id * A.ldw;
-    const uint16_t* xr = A.x + (size_t)m * K;
-    float s0 = 0.f, s1 = 0.f;
-    for (int k0 = 0; k0 < K; k0 += 512 * kWideDot) {
-      u32x4 wv[kWideDot], xv[kWideDot];
-#pragma unroll
-      for (int j = 0; j < kWideDot; ++j) {   // clamped, unconditional loads
-        const int k = min(k0 + 512 * j + lane * 8, K - 8);
-        wv[j] = *reinterpret_cast<const u32x4*>(wr + k);
-        xv[j] = *reinterpret_cast<const u32x4*>(xr + k);
-      }
-#pragma unroll
-      for (int j = 0; j < kWideDot; ++j) {
-        if (k0 + 512 * j + lane * 8 < K) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            s0 = __builtin_fmaf(lo_bf16(xv[j][c]), lo_bf16(wv[j][c]), s0);
-            s1 = __builtin_fmaf(hi_bf16(xv[j][c]), hi_bf16(wv[j][c]), s1);
-          }
-        }
-      }
-    }
-    float sum = s0 + s1;
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    const float sum = wave_dot<kE4M3>(A.w, A.ldw, id, kE4M3 ? A.wscale[id] : 1.f, A.x + (size_t)m * K, K, lane);
     if (lane == 0) {
       store_dev(A.rr_id + (size_t)m * R + r, (int32_t)id);
       store_dev(A.rr_val + (size_t)m * R + r, sum);
@@ -1621,10 +1652,10 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
 }
 
 // Rerank kernel: grid (ceil(R / 4), M), one part of one row per workgroup.
-template <bool kArgmax>
+template <bool kArgmax, bool kE4M3>
 __global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(RerankArgs A) {
   __shared__ WideShared sh;
-  rerank_part<kWideThreads, kArgmax>(sh, A, blockIdx.y, blockIdx.x, gridDim.x);
+  rerank_part<kWideThreads, kArgmax, kE4M3>(sh, A, blockIdx.y, blockIdx.x, gridDim.x);
 }
 
 
@@ -1760,16 +1791,20 @@ int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, co
   return DH_OK;
 }
 
+// e4m3: wscale non-null (rows of ldw bytes, ldw % 16 == 0); bf16: wscale null
+// (rows of ldw elements, ldw % 8 == 0).  Either way a row starts 16-byte aligned.
 int validate_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
-                    const int32_t* cand_id, int ncand, int R, const int32_t* rr_id, const float* rr_val) {
-  if (!x || !w || !cand_val || !cand_id || !rr_id || !rr_val)
+                    const int32_t* cand_id, int ncand, int R, const int32_t* rr_id, const float* rr_val,
+                    bool e4m3 = false, const float* wscale = nullptr) {
+  if (!x || !w || !cand_val || !cand_id || !rr_id || !rr_val || (e4m3 && !wscale))
     return dh::fail(DH_EINVAL, "rerank: null pointer");
   int rc = check_m(M);
   if (rc) return rc;
   if ((rc = check_k(K))) return rc;
   if (N < 1) return dh::fail(DH_ESHAPE, "rerank: N must be >= 1 (got %d)", N);
-  if (ldw < K || ldw % 8 != 0)
-    return dh::fail(DH_EINVAL, "rerank: ldw must be >= K and a multiple of 8 (got %lld)", (long long)ldw);
+  const int align = e4m3 ? 16 : 8;
+  if (ldw < K || ldw % align != 0)
+    return dh::fail(DH_EINVAL, "rerank: ldw must be >= K and a multiple of %d (got %lld)", align, (long long)ldw);
   if (ncand < 1) return dh::fail(DH_EINVAL, "rerank: ncand must be >= 1 (got %d)", ncand);
   if (R < 1 || R > ncand || R > DH_MAX_R)
     return dh::fail(DH_EUNSUP, "rerank: R must be in 1..min(ncand=%d, %d) (got %d)", ncand, DH_MAX_R, R);
@@ -1852,26 +1887,35 @@ bool fast_rerank(int N, int ncand, int R, int& nblk, int& kcand) {
 }
 
 template <bool kArgmax>
-hipError_t launch_wide(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
-                       const int32_t* cand_id, int nblk, int kcand, int R, int32_t* rr_id, float* rr_val,
-                       int32_t* out_id, float* out_val, uint32_t* cnt, hipStream_t s) {
-  const RerankArgs A{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), ldw, K, N, cand_val,
+hipError_t launch_wide(const void* x, const void* w, const float* wscale, int64_t ldw, int M, int K, int N,
+                       const float* cand_val, const int32_t* cand_id, int nblk, int kcand, int R, int32_t* rr_id,
+                       float* rr_val, int32_t* out_id, float* out_val, uint32_t* cnt, hipStream_t s) {
+  const RerankArgs A{static_cast<const uint16_t*>(x), w, wscale, ldw, K, N, cand_val,
                      cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, cnt};
-  hipLaunchKernelGGL(rerank_wide_kernel<kArgmax>, dim3((R + 3) / 4, M), dim3(kWideThreads), 0, s, A);
+  const dim3 grid((R + 3) / 4, M);
+  if (wscale) hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, true>), grid, dim3(kWideThreads), 0, s, A);
+  else hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, false>), grid, dim3(kWideThreads), 0, s, A);
   return hipGetLastError();
 }
 
-int launch_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
-                  const int32_t* cand_id, int ncand, int R, int32_t* rr_id, float* rr_val, hipStream_t s) {
+// wscale null: bf16 rows; else e4m3 rows with their scales.
+int launch_rerank(const void* x, const void* w, const float* wscale, int64_t ldw, int M, int K, int N,
+                  const float* cand_val, const int32_t* cand_id, int ncand, int R, int32_t* rr_id, float* rr_val,
+                  hipStream_t s) {
   int nblk, kcand;
   if (fast_rerank(N, ncand, R, nblk, kcand)) {
-    hipError_t e = launch_wide<false>(x, w, ldw, M, K, N, cand_val, cand_id, nblk, kcand, R, rr_id, rr_val,
-                                      nullptr, nullptr, nullptr, s);
+    hipError_t e = launch_wide<false>(x, w, wscale, ldw, M, K, N, cand_val, cand_id, nblk, kcand, R, rr_id,
+                                      rr_val, nullptr, nullptr, nullptr, s);
     if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_wide_kernel: %s", hipGetErrorString(e));
     return dh::ok();
   }
-  hipLaunchKernelGGL(rerank_kernel, dim3(M), dim3(kSelThreads), 0, s, static_cast<const uint16_t*>(x),
-                     static_cast<const uint16_t*>(w), ldw, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (wscale)
+    hipLaunchKernelGGL(rerank_kernel<true>, dim3(M), dim3(kSelThreads), 0, s, xb, w, wscale, ldw, K, N, cand_val,
+                       cand_id, ncand, R, rr_id, rr_val);
+  else
+    hipLaunchKernelGGL(rerank_kernel<false>, dim3(M), dim3(kSelThreads), 0, s, xb, w, wscale, ldw, K, N, cand_val,
+                       cand_id, ncand, R, rr_id, rr_val);
   return launch_error("rerank_kernel");
 }
 
@@ -1972,7 +2016,17 @@ int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, i
                       int32_t* rr_id, float* rr_val, void* stream) {
   int rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
   if (rc) return rc;
-  return launch_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, as_stream(stream));
+  return launch_rerank(x, w, nullptr, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val,
+                       as_stream(stream));
+}
+
+int draft_head_rerank_e4m3(const void* x, const uint8_t* w8, const float* wscale, int64_t ldw, int M, int K,
+                           int N, const float* cand_val, const int32_t* cand_id, int ncand, int R,
+                           int32_t* rr_id, float* rr_val, void* stream) {
+  int rc = validate_rerank(x, w8, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, true, wscale);
+  if (rc) return rc;
+  return launch_rerank(x, w8, wscale, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val,
+                       as_stream(stream));
 }
 
 int draft_head_logits_row(const float* coarse, const int32_t* rr_id, const float* rr_val, int M, int N, int R,
@@ -2004,15 +2058,22 @@ int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, i
   return launch_argmax(rr_id, rr_val, M, R, out_id, out_val, as_stream(stream));
 }
 
-int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
-                       const void* w, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
-                       int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
-                       void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
-                       void* coarse_stop_event) {
+}  // extern "C"
+
+namespace {
+
+// One call: coarse launch(es), then rerank + argmax.  wscale null: bf16 rows;
+// else e4m3 rows (w8) with their scales.
+int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, const void* w,
+                 const float* wscale, bool e4m3, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
+                 int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
+                 void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
+                 void* coarse_stop_event) {
   const int ncand = (N > 0 && kcand > 0) ? ((N + DH_BLOCK_N - 1) / DH_BLOCK_N) * kcand : 0;
   int rc = validate_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes);
   if (rc) return rc;
-  if ((rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val))) return rc;
+  if ((rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, e4m3, wscale)))
+    return rc;
   if ((rc = validate_argmax(rr_id, rr_val, M, R, out_id, out_val))) return rc;
   hipStream_t s = as_stream(stream);
   if ((rc = launch_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace, s,
@@ -2021,13 +2082,37 @@ int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
     return rc;
   int nblk, kc;
   if (fast_rerank(N, ncand, R, nblk, kc)) {   // rerank and argmax in one kernel
-    hipError_t e = launch_wide<true>(x, w, ldw, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val, out_id,
-                                     out_val, static_cast<uint32_t*>(workspace), s);
+    hipError_t e = launch_wide<true>(x, w, wscale, ldw, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val,
+                                     out_id, out_val, static_cast<uint32_t*>(workspace), s);
     if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_wide_kernel: %s", hipGetErrorString(e));
     return dh::ok();
   }
-  if ((rc = launch_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, s))) return rc;
+  if ((rc = launch_rerank(x, w, wscale, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, s))) return rc;
   return launch_argmax(rr_id, rr_val, M, R, out_id, out_val, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                       const void* w, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
+                       int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
+                       void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
+                       void* coarse_stop_event) {
+  return forward_impl(x, M, K, N, tiled, pairs, w, nullptr, false, ldw, kcand, R, cand_val, cand_id, rr_id, rr_val,
+                      out_id, out_val, coarse_out, workspace, workspace_bytes, stream, coarse_start_event,
+                      coarse_stop_event);
+}
+
+int draft_head_forward_e4m3(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                            const uint8_t* w8, const float* wscale, int64_t ldw, int kcand, int R, float* cand_val,
+                            int32_t* cand_id, int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val,
+                            float* coarse_out, void* workspace, size_t workspace_bytes, void* stream,
+                            void* coarse_start_event, void* coarse_stop_event) {
+  return forward_impl(x, M, K, N, tiled, pairs, w8, wscale, true, ldw, kcand, R, cand_val, cand_id, rr_id, rr_val,
+                      out_id, out_val, coarse_out, workspace, workspace_bytes, stream, coarse_start_event,
+                      coarse_stop_event);
 }
 
 }  // extern "C"

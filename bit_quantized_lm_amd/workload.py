@@ -69,23 +69,21 @@ def e4m3_head(w_bits: np.ndarray):
     lm_head): per row, scale = max |w| / 448 (float32) and codes = w / scale
     rounded to the nearest e4m3 value (ties to the even code), within +-448.
     Returns (codes uint8 [N][K], scale float32 [N])."""
-    w = bf16_bits_to_f32(w_bits).astype(np.float64)
-    amax = np.abs(w).max(axis=1)
+    w = bf16_bits_to_f32(w_bits)
+    amax = np.abs(w).max(axis=1).astype(np.float64)
     scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
-    # the 127 finite non-negative e4m3 magnitudes, code order = value order
-    codes = np.arange(0, 127)
-    e, m = codes >> 3, (codes & 7).astype(np.float64)
-    table = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
     out = np.empty(w.shape, dtype=np.uint8)
-    for i in range(0, w.shape[0], 8192):
-        v = w[i:i + 8192] / scale[i:i + 8192, None].astype(np.float64)
+    for i in range(0, w.shape[0], 512):
+        v = w[i:i + 512].astype(np.float64) / scale[i:i + 512, None].astype(np.float64)
         a = np.minimum(np.abs(v), 448.0)
-        hi = np.clip(np.searchsorted(table, a, side="left"), 1, 126)
-        lo = hi - 1
-        dlo, dhi = a - table[lo], table[hi] - a
-        pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
-        pick = np.where(a >= table[126], 126, pick)
-        out[i:i + 8192] = (pick | np.where(v < 0, 128, 0)).astype(np.uint8)
+        # step of the e4m3 grid around a: 2^(e-3) for a in [2^e, 2^(e+1)), e >= -6; 2^-9 below 2^-6
+        e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+        step = np.exp2(e - 3)
+        q = np.minimum(np.rint(a / step) * step, 448.0)          # ties to even step count = even code
+        sub = q < 2.0 ** -6
+        eq = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
+        code = np.where(sub, np.rint(q / 2.0 ** -9), (eq + 7) * 8 + np.rint(q / np.exp2(eq) * 8 - 8))
+        out[i:i + 512] = (code.astype(np.int64) | np.where(v < 0, 128, 0)).astype(np.uint8)
     return out, scale
 
 

@@ -13,6 +13,8 @@
  *   load time (host):  draft_head_quantize_pack -> draft_head_tile -> copy to device
  *   per call (device): draft_head_coarse -> draft_head_rerank -> draft_head_argmax,
  *                      or the three in one host call: draft_head_forward
+ *                      (rerank from e4m3 rows: the *_e4m3 variants); for a top-k
+ *                      caller, draft_head_logits_row after them
  *
  * Conventions for every function:
  *   - Return value: DH_OK (0) or a negative DH_E* code; never throws.  The
@@ -159,6 +161,22 @@ int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, i
                       int32_t* rr_id, float* rr_val, void* stream);
 
 /*
+ * DEVICE.  draft_head_rerank with the head's rows stored as e4m3 bytes and a
+ * per-row fp32 scale (the FP8 branch of `_rerank_exact` on the
+ * radiance_drafthead.py page: a per-channel FP8 lm_head).  Each byte b is
+ * decoded by the page's bit arithmetic: e = (b >> 3) & 15, mant = b & 7,
+ * magnitude mant * 2^-9 if e == 0 else (1 + mant/8) * 2^(e-7), bit 7 the sign
+ * (so 0x7F / 0xFF read as +-480, not NaN); the weight is that value times
+ * wscale[id] in fp32, and e = sum_k x * weight in fp32.
+ *   w8       device, e4m3 bytes [N][ldw], 16-byte aligned, ldw >= K, ldw % 16 == 0
+ *   wscale   device, fp32 [N]
+ * Everything else as draft_head_rerank.  Errors: as draft_head_rerank.
+ */
+int draft_head_rerank_e4m3(const void* x, const uint8_t* w8, const float* wscale, int64_t ldw, int M, int K,
+                           int N, const float* cand_val, const int32_t* cand_id, int ncand, int R,
+                           int32_t* rr_id, float* rr_val, void* stream);
+
+/*
  * DEVICE.  Final token per row: the rr_id whose exact value is largest, ties
  * to the lower id, entries with id -1 ignored (the page leaves the argmax of
  * the written-back row to the caller's sampler).
@@ -193,6 +211,16 @@ int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
                        int32_t* out_id, float* out_val, float* coarse_out, void* workspace,
                        size_t workspace_bytes, void* stream, void* coarse_start_event,
                        void* coarse_stop_event);
+
+/*
+ * DEVICE.  draft_head_forward with the e4m3 rerank source of
+ * draft_head_rerank_e4m3 (w8, wscale, ldw in bytes) in place of the bf16 rows.
+ */
+int draft_head_forward_e4m3(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                            const uint8_t* w8, const float* wscale, int64_t ldw, int kcand, int R,
+                            float* cand_val, int32_t* cand_id, int32_t* rr_id, float* rr_val, int32_t* out_id,
+                            float* out_val, float* coarse_out, void* workspace, size_t workspace_bytes,
+                            void* stream, void* coarse_start_event, void* coarse_stop_event);
 
 /*
  * DEVICE.  The bf16 row the page's `_apply_head_int2` hands to its caller

@@ -340,3 +340,70 @@ def test_logits_row_end_to_end(dev, topk_only):
     rms = np.sqrt(np.mean(ref["coarse"] ** 2, axis=1))[:, None]
     lim = 2e-3 * np.abs(wv) + 2e-3 * rms + 2.0 ** -7 * np.abs(wv)
     assert np.all(np.abs(gv - wv)[fin] <= lim[fin])
+
+
+# ------------------------------------------------------- e4m3 rerank source
+def _e4m3_ref(x, w, packed, w8, wscale, kcand, r):
+    """The oracle's pipeline with the rerank read from the e4m3 rows."""
+    ref = oracle.pipeline(x, w, *packed, kcand=kcand, r=r)
+    e = oracle.rerank_exact_e4m3(x, w8, wscale, ref["rr_id"])
+    ref["rr_val"] = e
+    ref["out_id"], ref["out_val"] = oracle.final_argmax(ref["rr_id"], e)
+    ref["tie_rows"] = oracle.tie_rows(e)
+    return ref
+
+
+def _e4m3_head(w, kcand, r, dev, packed=None):
+    w8, wscale = workload.e4m3_head(w)
+    head = B.DraftHead.from_weight(w, kcand=kcand, R=r, device=dev, packed=packed)
+    head.w = torch.from_numpy(w8).to(dev)
+    head.wscale = torch.from_numpy(wscale).to(dev)
+    return head, w8, wscale
+
+
+@pytest.mark.parametrize("m,k,n,kcand,r", [(3, 1024, 5000, 8, 32), (1, 512, 200, 64, 100), (17, 1024, 777, 4, 20),
+                                           (8, 5120, 20000, 8, 32), (20, 512, 70000, 8, 100)])
+def test_e4m3_rerank_parity(dev, m, k, n, kcand, r):
+    w = workload.gen_weight(n, k, seed=2000 + n)
+    x = workload.gen_x(m, k, seed=2001 + n)
+    _log(f"e4m3 case m={m} k={k} n={n} kcand={kcand} r={r}")
+    packed = oracle.quantize_pack(w)
+    head, w8, wscale = _e4m3_head(w, kcand, r, dev, packed=packed)
+    got = run_gpu(head, x, dev)
+    stats = compare(_e4m3_ref(x, w, packed, w8, wscale, kcand, r), got, n, kcand)
+    _log(f"  ok {stats}")
+
+
+def test_e4m3_forward_matches_staged_calls(dev):
+    n, k, m = 20000, 1024, 5
+    w = workload.gen_weight(n, k, seed=99)
+    head, _, _ = _e4m3_head(w, 8, 32, dev)
+    x = _to_dev(workload.gen_x(m, k, seed=100), dev)
+    a = head.staged(x)
+    b = head(x)
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.timeout(900)
+def test_e4m3_rerank_full_shape(dev, full):
+    """The per-rank shard with an e4m3 head: parity at M = 1, 8, 72 and the
+    argmax agreement with the exact bf16 head (reported)."""
+    cfg = full["cfg"]
+    w8, wscale = workload.e4m3_head(full["w"])
+    head = full["head"]
+    h8 = B.DraftHead(head.tiled, head.pairs, torch.from_numpy(w8).to(dev), cfg.n, cfg.k, cfg.kcand, cfg.rerank,
+                     wscale=torch.from_numpy(wscale).to(dev))
+    for m in (1, 8, 72):
+        x = full["x"][:m]
+        got = run_gpu(h8, x, dev, want_coarse=False)
+        ref = _prefix(full["ref"], m)
+        e = oracle.rerank_exact_e4m3(x, w8, wscale, ref["rr_id"])
+        ref = dict(ref, rr_val=e, tie_rows=oracle.tie_rows(e))
+        ref["out_id"], ref["out_val"] = oracle.final_argmax(ref["rr_id"], e)
+        stats = compare(ref, got, cfg.n, cfg.kcand, check_coarse=False)
+        _log(f"e4m3 full shape m={m}: {stats}")
+    E = oracle.exact_head(full["x"], full["w"])
+    agree = int(np.sum(got["out_id"] == np.argmax(E, axis=1)))
+    _log(f"e4m3 full shape m=72: argmax agreement with the exact bf16 head {agree}/72 (reported)")

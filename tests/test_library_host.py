@@ -26,7 +26,8 @@ def test_library_exports_every_header_symbol(lib):
     assert set(names) == {"draft_head_last_error", "draft_head_sizes", "draft_head_quantize_pack",
                           "draft_head_tile", "draft_head_workspace_bytes", "draft_head_coarse",
                           "draft_head_rerank", "draft_head_argmax", "draft_head_forward",
-                          "draft_head_stream_read", "draft_head_logits_row"}
+                          "draft_head_stream_read", "draft_head_logits_row", "draft_head_rerank_e4m3",
+                          "draft_head_forward_e4m3"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -224,6 +225,30 @@ def test_argmax_validation(lib):
     _err(lib, lib.draft_head_argmax(FAKE, FAKE, 0, 8, FAKE, FAKE, None), B.DH_EINVAL)
     _err(lib, lib.draft_head_argmax(FAKE, FAKE, 1, 0, FAKE, FAKE, None), B.DH_EUNSUP)
     _err(lib, lib.draft_head_argmax(FAKE, FAKE, 1, 1025, FAKE, FAKE, None), B.DH_EUNSUP)
+
+
+def test_rerank_e4m3_validation(lib):
+    ok = dict(x=FAKE, w=FAKE, sc=FAKE, ldw=512, M=2, K=512, N=100, cv=FAKE, ci=FAKE, nc=16, R=8, ri=FAKE,
+              rv=FAKE, s=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.draft_head_rerank_e4m3(a["x"], a["w"], a["sc"], a["ldw"], a["M"], a["K"], a["N"], a["cv"],
+                                          a["ci"], a["nc"], a["R"], a["ri"], a["rv"], a["s"])
+    _err(lib, call(sc=None), B.DH_EINVAL)          # the e4m3 rows need their scales
+    _err(lib, call(w=None), B.DH_EINVAL)
+    _err(lib, call(ldw=520), B.DH_EINVAL)          # rows of bytes: a multiple of 16
+    _err(lib, call(ldw=256), B.DH_EINVAL)
+    _err(lib, call(w=MIS), B.DH_EINVAL)
+    _err(lib, call(M=0), B.DH_EINVAL)
+    _err(lib, call(K=100), B.DH_ESHAPE)
+    _err(lib, call(R=17), B.DH_EUNSUP)
+    f = lib.draft_head_forward_e4m3              # the same checks before any launch
+    _err(lib, f(FAKE, 1, 512, 64, FAKE, FAKE, FAKE, None, 512, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                FAKE, 512, None, None, None), B.DH_EINVAL)
+    _err(lib, f(FAKE, 1, 512, 64, FAKE, FAKE, FAKE, FAKE, 520, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                FAKE, 512, None, None, None), B.DH_EINVAL)
 
 
 def test_logits_row_validation(lib):
