@@ -20,7 +20,8 @@ Prints one JSON line:
   extra        per-M (1, 8, 72) times with the coarse kernel's p10/p50/p90 and
                its fractions of the HBM and bf16 MFMA peaks, the warm
                (cache-resident) figure, the time of the row handed to a
-               top-k caller (draft_head_logits_row), and the device's achieved
+               top-k caller (draft_head_logits_row), the per-call time with
+               the e4m3 rerank source, and the device's achieved
                read rate (the library's streaming-read reference) and copy rate
 """
 from __future__ import annotations
@@ -80,6 +81,7 @@ class Rig:
         t0 = time.time()
         log("generating W (bf16, N(0, 0.02)) and x (N(0, 1), 1% channels x8)")
         self.x_host, w = workload.make_inputs(workload.CONFIGS["m72"])
+        self.w_host = w
         log(f"host quantize_pack ({time.time() - t0:.1f}s)")
         tq = time.time()
         packed = B.draft_head_quantize_pack(w)
@@ -156,6 +158,31 @@ class Rig:
         coarse_ms = np.array([a.elapsed_time(b) for a, b in evs])
         self.last_coarse_pct = {f"p{q}": round(float(np.percentile(coarse_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
         return total_ms / 1e3 / steps, float(np.mean(coarse_ms)) / 1e3, wall
+
+    def e4m3_call_us(self, ms=(1, 8, 72), steps=200):
+        """Per-call time with the rerank reading an e4m3 copy of the head
+        (a synthetic per-channel FP8 head; coarse pass unchanged)."""
+        torch, B = self.torch, self.B
+        from bit_quantized_lm_amd import workload
+        if not hasattr(self, "w8"):
+            w8, wscale = workload.e4m3_head(self.w_host)
+            self.w8 = torch.from_numpy(w8).to(self.dev)
+            self.wscale = torch.from_numpy(wscale).to(self.dev)
+        res = {}
+        for m in ms:
+            heads = [B.DraftHead(h.tiled, h.pairs, self.w8, N, K, KCAND, R, wscale=self.wscale) for h in self.heads]
+            out = self.buffers(m)
+            for i in range(20):
+                heads[i % len(heads)](self.x[:m], stream=self.stream, out=out, workspace=self.ws[m])
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for i in range(steps):
+                heads[i % len(heads)](self.x[:m], stream=self.stream, out=out, workspace=self.ws[m])
+            e.record()
+            torch.cuda.synchronize()
+            res[str(m)] = round(s.elapsed_time(e) / steps * 1e3, 2)
+        return res
 
     def logits_row_us(self, m, reps=50):
         """Time of draft_head_logits_row alone at M rows (full and top-k only)."""
@@ -325,6 +352,8 @@ def main():
         extra["warm_not_hbm"] = {"us_per_call": round(tw * 1e6, 2), "coarse_us": round(tkw * 1e6, 2),
                                  "note": "one weight copy reused back to back: Infinity-Cache resident"}
         extra["logits_row_us"] = {str(mm): rig.logits_row_us(mm) for mm in (1, 8, 72)}
+        extra["e4m3_rerank_us_per_call"] = rig.e4m3_call_us()
+        log(f"one call with the e4m3 rerank source: {extra['e4m3_rerank_us_per_call']}")
         log(f"row for the caller (draft_head_logits_row alone): {extra['logits_row_us']}")
         extra["device_copy_GBps"] = round(rig.copy_bandwidth(), 1)
         extra["stream_read_GBps"] = rig.read_bandwidth()
