@@ -1324,23 +1324,13 @@ __global__ __launch_bounds__(kSelThreads) void rerank_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Rerank, block-maximum path.  It relies on the candidate arrays being the
-// ones draft_head_coarse writes: block b owns slots b*kcand .. b*kcand+kcand-1
-// in (value desc, column asc) order, so slot b*kcand holds the block maximum,
-// and among equal values slot order is column order.  Keys built from
-// (value, ~slot) therefore order the candidates exactly as (value, ~id) does.
-//   1. Wave 0 reads the nblk block maxima (lane l: blocks l, l+64, ...) and
-//      picks a threshold T that at least R of them reach: the R-th largest of
-//      every lane's two largest maxima (a bitonic sort of 128 keys), or, if
-//      that lets more than DH_MAX_R / kcand blocks through, the exact R-th
-//      largest maximum by radix select.  At least R distinct keys are >= T,
-//      so every one of the row's R best candidates is >= T and lies in a
-//      block whose maximum is >= T.
-//   2. Wave 0 tests the kcand candidates of each such block against T; the
-//      survivors (every key >= T: at least R) are sorted, and the first R are
-//      the row top-R.
-constexpr int kFastNV = 32;        // block maxima per lane of wave 0: nblk <= 2048
-constexpr int kSurvBatch = 4;      // survivor loads per lane in flight
+// Rerank, block-maximum path (rerank_list below).  It relies on the candidate
+// arrays being the ones draft_head_coarse writes: block b owns slots
+// b*kcand .. b*kcand+kcand-1 in (value desc, column asc) order, so slot
+// b*kcand holds the block maximum, and among equal values slot order is
+// column order.  Keys built from (value, ~slot) therefore order the
+// candidates exactly as (value, ~id) does.
+constexpr int kFastNV = 32;        // block maxima per lane (over all waves): nblk <= 2048
 
 __device__ __forceinline__ unsigned long long slot_key(float v, int slot) {
   if (v == -__builtin_inff()) return 0ull;   // padding slot
@@ -1351,84 +1341,6 @@ __device__ __forceinline__ unsigned long long slot_key(float v, int slot) {
 
 __device__ __forceinline__ int lane_prefix(unsigned long long bal) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-}
-
-// Sorts keys[0..ns) descending (ns <= DH_MAX_R); called by the whole workgroup.
-// Wave 0 alone with a shuffle bitonic network when ns <= 64, else an LDS
-// bitonic network over the next power of two.  Ends with a barrier.
-template <int NT>
-__device__ void sort_desc(unsigned long long* keys, int ns) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  if (ns <= 64) {
-    if (tid < 64) {
-      unsigned long long v = lane < ns ? keys[lane] : 0ull;
-      for (int size = 2; size <= 64; size <<= 1)
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          const unsigned long long o = __shfl_xor(v, stride, 64);
-          const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
-          v = keep_max ? umax64(v, o) : umin64(v, o);
-        }
-      if (lane < ns) keys[lane] = v;
-    }
-    __syncthreads();
-    return;
-  }
-  int P = 1;
-  while (P < ns) P <<= 1;
-  for (int i = ns + tid; i < P; i += NT) keys[i] = 0ull;
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < P; i += NT) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool desc = (i & size) == 0;
-          const unsigned long long a = keys[i], c = keys[j];
-          if (desc ? (a < c) : (a > c)) {
-            keys[i] = c;
-            keys[j] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-// A threshold for the k-th largest (k <= 128) of the keys the wave holds: the
-// k-th largest of the union of every lane's two largest keys, found with a
-// 128-element bitonic sort (two keys per lane, shuffles only).  At least k
-// keys are >= the result (it is the k-th of a subset), usually only a few more.
-template <int NV>
-__device__ unsigned long long wave_top2_threshold(const unsigned long long (&v)[NV], int k) {
-  const int lane = threadIdx.x & 63;
-  unsigned long long a = 0ull, b = 0ull;   // a >= b: the lane's two largest
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const unsigned long long key = v[j];
-    b = umax64(b, umin64(a, key));
-    a = umax64(a, key);
-  }
-  unsigned long long e[2] = {a, b};   // element i = 64 * r + lane
-  for (int size = 2; size <= 128; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride == 64) {   // partners in the two registers of one lane; size == 128: descending
-        const unsigned long long hi = umax64(e[0], e[1]), lo = umin64(e[0], e[1]);
-        e[0] = hi;
-        e[1] = lo;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int i = 64 * r + lane;
-          const unsigned long long o = __shfl_xor(e[r], stride, 64);
-          const bool keep_max = ((i & stride) == 0) == ((i & size) == 0);
-          e[r] = keep_max ? umax64(e[r], o) : umin64(e[r], o);
-        }
-      }
-    }
-  }
-  const int r = (k - 1) >> 6, l = (k - 1) & 63;
-  return __shfl(r ? e[1] : e[0], l, 64);
 }
 
 // Rerank of one row split over `nparts` workgroups of NTHR threads (NW = NTHR/64
@@ -1442,12 +1354,13 @@ __device__ unsigned long long wave_top2_threshold(const unsigned long long (&v)[
 // The list (block-maximum selection; the candidates are the ones
 // draft_head_coarse writes, so slot b*kcand holds block b's maximum and slot
 // order is column order among equal values):
-//   1. Wave 0 reads the block maxima, 32 per lane, as (value, slot) keys.
-//      With R <= 64, T' = the R-th largest of the 64 lane maxima (ranked by
-//      counting in LDS) is at most the R-th largest block maximum, so every
-//      one of the row's R best candidates is >= T'; if T' lets more than
+//   1. The waves read the block maxima (block lane + 64 j: 32 per lane over
+//      all waves) as (value, slot) keys.  With R <= 64, T' = the R-th largest
+//      of the 64 lane maxima (their value halves, by bisection over the bits
+//      with ballots) is at most the R-th largest block maximum, so every one
+//      of the row's R best candidates is >= T'; if T' lets more than
 //      DH_MAX_R / kcand blocks through (or R > 64), T' = the exact R-th
-//      largest block maximum (radix select).
+//      largest block maximum (radix select by wave 0).
 //   2. The candidates >= T' of the blocks whose maximum is >= T' survive
 //      (at least R, at most DH_MAX_R); each is ranked by counting the
 //      survivors above it, and the first R ranks are the list.
