@@ -409,6 +409,7 @@ void coarse_resident_kernel(CoarseArgs A) {
   u32x4* xs = reinterpret_cast<u32x4*>(smem);                               // [NG][16][MP]
   float* Xs = reinterpret_cast<float*>(smem + (size_t)NG * 16 * MP * 16);       // [NG][MP]
   float* sel = Xs + (size_t)NG * MP;                                           // [kBlocks][16][64]
+  int* flag = reinterpret_cast<int*>(sel + (size_t)kBlocks * 16 * 64);          // [kBlocks]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -432,26 +433,25 @@ void coarse_resident_kernel(CoarseArgs A) {
     for (int t = 0; t < NT; ++t) sz[t] = __builtin_nontemporal_load(pp + (G * 4 + t) * 16 + nn);
   };
 
-  // the first byte groups' codes are requested before x is staged
   u32x4 rw[D][2][NT], sw[D][NT];   // ring: set (G mod D) holds byte group G
-#pragma unroll
-  for (int d = 0; d < D - 1; ++d)
-    if (d < NG4) load_codes(d, rw[d], sw[d]);
 
   // stage x: piece i = (m, k0 = 8p) for all MP rows (zero rows past M).  Loads
-  // are issued kBatch at a time from clamped (always valid) addresses.
+  // are issued kBatch at a time from clamped (always valid) addresses.  The
+  // first byte groups' codes are requested right after the first batch of x,
+  // so that x (from L2) is not waited for behind them.
   {
     constexpr int kBatch = 4;
     const int per_row = A.K >> 3;
     const int total = MP * per_row;
-    for (int base = 0; base < total; base += kResThreads * kBatch) {
-      u32x4 v[kBatch];
+    auto issue_x = [&](int base, u32x4 (&v)[kBatch]) {
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int i = min(base + tid + j * kResThreads, total - 1);
         const int m = i / per_row, k0 = (i - m * per_row) * 8;
         v[j] = *reinterpret_cast<const u32x4*>(A.x + (size_t)(m < A.M ? m : 0) * A.K + k0);
       }
+    };
+    auto use_x = [&](int base, const u32x4 (&v)[kBatch]) {
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int i = base + tid + j * kResThreads;
@@ -468,8 +468,19 @@ void coarse_resident_kernel(CoarseArgs A) {
           if (p == 0) Xs[it * MP + m] = sum;
         }
       }
+    };
+    u32x4 v[kBatch];
+    issue_x(0, v);
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+      if (d < NG4) load_codes(d, rw[d], sw[d]);
+    use_x(0, v);
+    for (int base = kResThreads * kBatch; base < total; base += kResThreads * kBatch) {
+      issue_x(base, v);
+      use_x(base, v);
     }
   }
+  if (tid < kBlocks) flag[tid] = 0;
   __syncthreads();
 
   f32x4 acc[1][NT];
@@ -503,16 +514,33 @@ void coarse_resident_kernel(CoarseArgs A) {
     }
   }
 
-  // the tiles of the block meet in LDS
-  float* bs = sel + (size_t)lblk * 16 * 64;
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int r = 0; r < MR; ++r) bs[(4 * hh + r) * 64 + 16 * (NT * part + t) + nn] = acc[0][t][r];
-  __syncthreads();
+  // The block's selection starts as soon as its own tiles are done, with no
+  // workgroup barrier, so that waves still streaming are not held up.  One
+  // wave per block selects from its registers; with two, part 1 hands its
+  // tiles to part 0 through LDS and a flag, and part 0 selects.
   if (!blk_ok) return;
-  block_select<1, MR>([&](int, int r, int t) { return bs[(4 * hh + r) * 64 + 16 * t + nn]; }, A, b, hh, nn,
-                      part, kWavesPerBlock);
+  if constexpr (kWavesPerBlock == 1) {
+    block_select<1, MR>([&](int, int r, int t) { return acc[0][t][r]; }, A, b, hh, nn, 0, 1);
+  } else {
+    static_assert(kWavesPerBlock == 2, "one or two waves per block");
+    float* bs = sel + (size_t)lblk * 16 * 64;
+    if (part == 1) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < MR; ++r) bs[(4 * hh + r) * 64 + 16 * (NT + t) + nn] = acc[0][t][r];
+      if (lane == 0) __hip_atomic_store(flag + lblk, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < MR; ++r) bs[(4 * hh + r) * 64 + 16 * t + nn] = acc[0][t][r];
+    while (__hip_atomic_load(flag + lblk, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(1);
+    block_select<1, MR>([&](int, int r, int t) { return bs[(4 * hh + r) * 64 + 16 * t + nn]; }, A, b, hh, nn,
+                        0, 1);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1632,7 +1660,8 @@ size_t resident_lds_bytes(int K, int MP) {
   const size_t groups = (size_t)K / DH_GROUP;
   const size_t blocks = (size_t)res_waves<1>() * res_nt(MP) / 4;   // 4 / res_nt waves per block
   static_assert(res_waves<1>() == res_waves<8>(), "LDS sizing assumes one workgroup shape");
-  return groups * 16 * MP * 16 + groups * MP * sizeof(float) + blocks * 16 * 64 * sizeof(float);
+  return groups * 16 * MP * 16 + groups * MP * sizeof(float) + blocks * 16 * 64 * sizeof(float) +
+         blocks * sizeof(int);
 }
 
 template <int MP>
