@@ -13,7 +13,8 @@ Modules
 -------
 bf16     bf16 <-> float conversions (round to nearest even), own code.
 quant    min/max asymmetric int2 quantiser, quarter-split packing, unpacking
-         and the effective weight defined by the stored scale pair.
+         and the effective weight defined by the stored scale pair; the same
+         at 4 bits (half-split packing, bias 16).
 head     coarse scores, block top-KCAND, row top-R, exact rerank (bf16 rows or
          e4m3 rows with a per-row scale), argmax, the
          bf16 row handed to the caller (full or top-k only), and the exact
@@ -34,7 +35,8 @@ inputs and the real weights are not available.
 """
 from . import bf16, quant, head, brute  # noqa: F401
 from .quant import (GROUP, quantize, pack_quarter_split, unpack_quarter_split,  # noqa: F401
-                    effective_weight, quantize_pack)
-from .head import (BLOCK_N, coarse, coarse_collapse, block_topk, row_topr,  # noqa: F401
+                    effective_weight, quantize_pack, quantize_int4, pack_half_split, unpack_half_split,
+                    quantize_pack_int4, effective_weight_int4)
+from .head import (BLOCK_N, coarse, coarse_int4, coarse_collapse, block_topk, row_topr,  # noqa: F401
                    rerank_exact, final_argmax, logits_row, exact_head, pipeline, tie_rows,
                    e4m3_value, rerank_exact_e4m3)

@@ -79,8 +79,9 @@ def round_half_even(q):
 
 
 # ---------------------------------------------------------------- quantiser
-def quantize_row(w_row_bits):
-    """One row: (codes list, S bits list, ZS bits list), each op rounded to f32."""
+def quantize_row(w_row_bits, levels=3, premul=4):
+    """One row: (codes list, S bits list, ZS bits list), each op rounded to f32.
+    levels / premul: 3 / 4 for the 2-bit head, 15 / 16 for the 4-bit one."""
     k = len(w_row_bits)
     vals = [bf16_bits_value(b) for b in w_row_bits]
     codes = [0] * k
@@ -88,16 +89,16 @@ def quantize_row(w_row_bits):
     for g in range(k // GROUP):
         grp = vals[g * GROUP:(g + 1) * GROUP]
         lo, hi = min(grp), max(grp)
-        sc = f32(f32(hi - lo) / 3)
+        sc = f32(f32(hi - lo) / levels)
         if sc < f32(Fraction(1, 10 ** 8)):
             sc = f32(Fraction(1, 10 ** 8))
         zp = round_half_even(f32(-lo / sc))
-        zp = min(max(zp, Fraction(0)), Fraction(3))
+        zp = min(max(zp, Fraction(0)), Fraction(levels))
         for i, w in enumerate(grp):
             t = f32(f32(w / sc) + zp)
-            qv = min(max(round_half_even(t), Fraction(0)), Fraction(3))
+            qv = min(max(round_half_even(t), Fraction(0)), Fraction(levels))
             codes[g * GROUP + i] = int(qv)
-        s4 = f32(4 * sc)
+        s4 = f32(premul * sc)
         s_bits.append(bf16_value_bits(bf16(s4)))
         zs_bits.append(bf16_value_bits(bf16(f32(s4 + f32(zp * sc)))))
     return codes, s_bits, zs_bits

@@ -25,7 +25,7 @@ Readings where the page is silent (all also listed in the design notes):
 import numpy as np
 
 from . import bf16
-from .quant import GROUP, effective_weight, unpack_quarter_split
+from .quant import GROUP, effective_weight, effective_weight_int4, unpack_quarter_split
 
 BLOCK_N = 64          # width of one selection block (module constant BLOCK_N)
 CHUNK_ROWS = 8192     # rows of W handled at once (memory bound only)
@@ -49,6 +49,18 @@ def coarse(x_bits, packed, S_bits, ZS_bits):
         j = min(i + CHUNK_ROWS, n)
         w = effective_weight(packed, S_bits, ZS_bits, rows=slice(i, j))
         out[:, i:j] = x @ w.T
+    return out
+
+
+def coarse_int4(x_bits, packed4, S_bits, ZS_bits):
+    """c[m][n] = sum_k x[m][k] * w_eff[n][k] for a 4-bit head (half-split
+    packing, weight (S/16) v - (ZS - S)), float64 [M][N]."""
+    x = _x64(x_bits)
+    n = np.asarray(packed4).shape[0]
+    out = np.empty((x.shape[0], n), dtype=np.float64)
+    for i in range(0, n, CHUNK_ROWS):
+        j = min(i + CHUNK_ROWS, n)
+        out[:, i:j] = x @ effective_weight_int4(packed4, S_bits, ZS_bits, rows=slice(i, j)).T
     return out
 
 
@@ -256,9 +268,10 @@ def tie_rows(e, rel=1e-4):
     return flags
 
 
-def pipeline(x_bits, w_bits, packed, S_bits, ZS_bits, kcand=8, r=32):
-    """All per-call steps in order; returns a dict of every intermediate."""
-    c = coarse(x_bits, packed, S_bits, ZS_bits)
+def pipeline(x_bits, w_bits, packed, S_bits, ZS_bits, kcand=8, r=32, bits=2):
+    """All per-call steps in order; returns a dict of every intermediate.
+    bits = 4: the head is a 4-bit one (quantize_pack_int4's arrays)."""
+    c = (coarse_int4 if bits == 4 else coarse)(x_bits, packed, S_bits, ZS_bits)
     cv, ci = block_topk(c, kcand)
     rr_id, rr_cv = row_topr(cv, ci, r)
     e = rerank_exact(x_bits, w_bits, rr_id)

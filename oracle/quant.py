@@ -48,22 +48,85 @@ def quantize(w_bits):
     return codes, S, ZS
 
 
-def _quantize_rows(w_bits):
+def _quantize_rows(w_bits, levels=LEVELS, premul=PREMUL):
     n, k = w_bits.shape
     wf = bf16.to_f32(w_bits).reshape(n, k // GROUP, GROUP)
     lo = wf.min(axis=2)
     hi = wf.max(axis=2)
-    sc = (hi - lo) / np.float32(LEVELS)
+    sc = (hi - lo) / np.float32(levels)
     sc = np.maximum(sc, np.float32(1e-8))
-    zp = np.clip(np.round(-lo / sc), np.float32(0), np.float32(LEVELS))
+    zp = np.clip(np.round(-lo / sc), np.float32(0), np.float32(levels))
     t = wf / sc[:, :, None]
     t = t + zp[:, :, None]
-    q = np.clip(np.round(t), np.float32(0), np.float32(LEVELS)).astype(np.uint8)
-    s4 = np.float32(PREMUL) * sc
+    q = np.clip(np.round(t), np.float32(0), np.float32(levels)).astype(np.uint8)
+    s4 = np.float32(premul) * sc
     zpsc = zp * sc
     S = bf16.from_f32(s4)
     ZS = bf16.from_f32(s4 + zpsc)
     return q.reshape(n, k), S, ZS
+
+
+# ------------------------------------------------------------------ 4 bits
+LEVELS4 = 15         # highest 4-bit code
+PREMUL4 = 16.0       # bf16 1 + v/16 bias: the 4-bit scales are premultiplied by 16
+
+
+def quantize_int4(w_bits):
+    """The page's quantiser at BITS = 4 (`_quantize_head_now` with lv = 15 and
+    the bias 16): per (row n, group g of 128 consecutive k)
+      sc = max((hi - lo) / 15, 1e-8);  zp = clamp(round(-lo / sc), 0, 15)
+      q  = clamp(round(w / sc + zp), 0, 15)
+      S  = bf16(16 * sc);  ZS = bf16(16 * sc + zp * sc)
+    each a separate float32 operation.  Returns (codes, S bits, ZS bits).
+    """
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    n, k = w_bits.shape
+    if k % GROUP:
+        raise ValueError("K must be a multiple of the group size 128")
+    codes = np.empty((n, k), dtype=np.uint8)
+    S = np.empty((n, k // GROUP), dtype=np.uint16)
+    ZS = np.empty((n, k // GROUP), dtype=np.uint16)
+    for i in range(0, n, CHUNK_ROWS):
+        j = min(i + CHUNK_ROWS, n)
+        codes[i:j], S[i:j], ZS[i:j] = _quantize_rows(w_bits[i:j], LEVELS4, PREMUL4)
+    return codes, S, ZS
+
+
+def pack_half_split(codes):
+    """Byte j of a row carries k = j (bits 0-3) and K/2 + j (bits 4-7): the
+    BITS == 4 branch of the packing in `_quantize_head_now`.  uint8 [N][K/2]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    if k % 2:
+        raise ValueError("K must be even")
+    h = k // 2
+    return ((codes[:, :h] & np.uint8(15)) | ((codes[:, h:] & np.uint8(15)) << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_half_split(packed):
+    """Inverse of pack_half_split: codes uint8 [N][K]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    return np.concatenate([packed & np.uint8(15), packed >> np.uint8(4)], axis=1)
+
+
+def quantize_pack_int4(w_bits):
+    """(packed uint8 [N][K/2], S bits, ZS bits), the stored form of a 4-bit head."""
+    codes, S, ZS = quantize_int4(w_bits)
+    return pack_half_split(codes), S, ZS
+
+
+def effective_weight_int4(packed, S_bits, ZS_bits, rows=None):
+    """The weight a 4-bit head's stored arrays define, float64 [n][K]: the
+    kernel forms S * sum x (1 + v/16) - ZS * sum x per group (the comment on
+    the premultiplier in `_quantize_head_now`), i.e. (S/16) v - (ZS - S)."""
+    if rows is not None:
+        packed = packed[rows]
+        S_bits = S_bits[rows]
+        ZS_bits = ZS_bits[rows]
+    codes = unpack_half_split(packed).astype(np.float64)
+    s = bf16.to_f64(S_bits)
+    zs = bf16.to_f64(ZS_bits)
+    return codes * np.repeat(s / 16.0, GROUP, axis=1) - np.repeat(zs - s, GROUP, axis=1)
 
 
 def pack_quarter_split(codes):

@@ -387,3 +387,63 @@ def test_synthetic_e4m3_head_rounds_to_nearest():
     best = np.min(np.abs(np.abs(v)[..., None] - table[None, None, :]), axis=-1)
     assert np.all(err <= best + 1e-12)
     assert np.max(np.abs(got)) == 448.0
+
+
+# ------------------------------------------------------------- 4-bit head
+def test_int4_quantizer_worked_example(golden):
+    fx = golden("quantizer_int4_worked_example.txt")
+    k = int(fx["K"][0][0])
+    w = np.zeros((1, k), dtype=np.float32)
+    w[0, :4] = np.array([float(v) for v in fx["values_group0"][0]], dtype=np.float32) * 2.0 ** -7
+    bits = obf.from_f32(w)
+    codes, S, ZS = oracle.quantize_int4(bits)
+    assert [int(c) for c in codes[0, :5]] == [int(v) for v in fx["codes_group0"][0]]
+    assert np.all(codes[0, 4:128] == 8) and np.all(codes[0, 128:] == 0)
+    assert int(S[0, 0]) == int(fx["S0"][0][0], 16) and int(ZS[0, 0]) == int(fx["ZS0"][0][0], 16)
+    packed = oracle.pack_half_split(codes)
+    assert [int(b) for b in packed[0, :5]] == [int(v, 16) for v in fx["bytes"][0]]
+    assert np.array_equal(oracle.unpack_half_split(packed), codes)
+    wv = oracle.effective_weight_int4(packed, S, ZS)[0, :128]
+    assert np.array_equal(wv, (codes[0, :128].astype(np.float64) - 8) * 2.0 ** -7)
+
+
+def test_int4_quantizer_matches_exact_brute_force():
+    rng = np.random.default_rng(41)
+    w = workload.f32_to_bf16_bits((rng.standard_normal((6, 256)) * 0.02).astype(np.float32))
+    w[5, :128] = w[5, 0]                       # a constant group: the 1e-8 clamp
+    codes, S, ZS = oracle.quantize_int4(w)
+    for i in range(w.shape[0]):
+        c, s, z = brute.quantize_row([int(b) for b in w[i]], levels=15, premul=16)
+        assert [int(v) for v in codes[i]] == c, i
+        assert [int(v) for v in S[i]] == s and [int(v) for v in ZS[i]] == z, i
+
+
+def test_int4_collapse_identity_exact():
+    """S * sum x (1 + v/16) - ZS * sum x == sum x ((S/16) v - (ZS - S)), in fractions."""
+    rng = np.random.default_rng(43)
+    for _ in range(20):
+        S = Fraction(int(rng.integers(1, 255)), 2 ** int(rng.integers(6, 12)))
+        ZS = S + Fraction(int(rng.integers(0, 15)), 16) * S
+        xs = [Fraction(int(rng.integers(-1000, 1000)), 1024) for _ in range(128)]
+        vs = [int(rng.integers(0, 16)) for _ in range(128)]
+        lhs = S * sum(x * (1 + Fraction(v, 16)) for x, v in zip(xs, vs)) - ZS * sum(xs)
+        rhs = sum(x * (S / 16 * v - (ZS - S)) for x, v in zip(xs, vs))
+        assert lhs == rhs
+
+
+def test_int4_lossless_special_case():
+    """Codes with a power-of-two step, an integer zero point and both extreme
+    codes in every group come back exactly, and the effective weight is W."""
+    rng = np.random.default_rng(47)
+    n, k = 8, 256
+    codes = rng.integers(0, 16, size=(n, k)).astype(np.int64)
+    codes[:, ::128] = 0
+    codes[:, 1::128] = 15
+    s = 2.0 ** rng.integers(-10, -6, size=(n, k // 128))
+    z = rng.integers(0, 16, size=(n, k // 128)).astype(np.float64)
+    w = (codes - np.repeat(z, 128, axis=1)) * np.repeat(s, 128, axis=1)
+    bits = workload.f32_to_bf16_bits(w.astype(np.float32))
+    assert np.array_equal(obf.to_f64(bits), w)
+    q, S, ZS = oracle.quantize_int4(bits)
+    assert np.array_equal(q, codes)
+    assert np.array_equal(oracle.effective_weight_int4(oracle.pack_half_split(q), S, ZS), w)
