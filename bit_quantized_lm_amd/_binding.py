@@ -54,6 +54,10 @@ def load_library() -> ctypes.CDLL:
                                      ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.draft_head_quantize_pack.restype = i32
     lib.draft_head_quantize_pack.argtypes = [P, i64, i64, i64, P, P, P, i32]
+    lib.draft_head_quantize_pack_int4.restype = i32
+    lib.draft_head_quantize_pack_int4.argtypes = [P, i64, i64, i64, P, P, P, i32]
+    lib.draft_head_int4_as_int2.restype = i32
+    lib.draft_head_int4_as_int2.argtypes = [P, P, P, i64, i64, P, P, P]
     lib.draft_head_tile.restype = i32
     lib.draft_head_tile.argtypes = [P, P, P, i64, i64, P, P]
     lib.draft_head_workspace_bytes.restype = i32
@@ -67,6 +71,11 @@ def load_library() -> ctypes.CDLL:
     lib.draft_head_rerank.argtypes = [P, P, i64, i32, i32, i32, P, P, i32, i32, P, P, P]
     lib.draft_head_argmax.restype = i32
     lib.draft_head_argmax.argtypes = [P, P, i32, i32, P, P, P]
+    lib.draft_head_coarse_int4.restype = i32
+    lib.draft_head_coarse_int4.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P, sz, P]
+    lib.draft_head_forward_int4.restype = i32
+    lib.draft_head_forward_int4.argtypes = [P, i32, i32, i32, P, P, P, i64, i32, i32, P, P, P, P, P, P, P, P, sz,
+                                            P, P, P]
     lib.draft_head_rerank_e4m3.restype = i32
     lib.draft_head_rerank_e4m3.argtypes = [P, P, P, i64, i32, i32, i32, P, P, i32, i32, P, P, P]
     lib.draft_head_forward_e4m3.restype = i32
@@ -135,6 +144,39 @@ def draft_head_quantize_pack(w_bits: np.ndarray, nthreads: int = 0):
     return packed, S, ZS
 
 
+def draft_head_quantize_pack_int4(w_bits: np.ndarray, nthreads: int = 0):
+    """bf16 bits [N][K] -> the 4-bit head (packed uint8 [N][K/2], S, ZS uint16 [N][K/128])."""
+    lib = load_library()
+    w = np.asarray(w_bits)
+    if w.dtype != np.uint16 or w.ndim != 2:
+        raise ValueError("w_bits must be a 2-D uint16 array of bf16 bit patterns")
+    if w.strides[1] != 2:
+        w = np.ascontiguousarray(w)
+    n, k = w.shape
+    packed = np.empty((n, max(k // 2, 1)), dtype=np.uint8)
+    S = np.empty((n, max(k // GROUP, 1)), dtype=np.uint16)
+    ZS = np.empty_like(S)
+    _check(lib.draft_head_quantize_pack_int4(_ptr(w), n, k, w.strides[0] // 2, _ptr(packed), _ptr(S), _ptr(ZS),
+                                             nthreads))
+    return packed, S, ZS
+
+
+def draft_head_int4_as_int2(packed4: np.ndarray, S: np.ndarray, ZS: np.ndarray):
+    """A 4-bit head as the 2-bit head of length 2K the device path runs:
+    (packed uint8 [N][2K/4], S2, ZS2 uint16 [N][2K/128])."""
+    lib = load_library()
+    packed4 = np.ascontiguousarray(packed4, dtype=np.uint8)
+    S = np.ascontiguousarray(S, dtype=np.uint16)
+    ZS = np.ascontiguousarray(ZS, dtype=np.uint16)
+    n, h = packed4.shape
+    k = 2 * h
+    packed2 = np.empty((n, h), dtype=np.uint8)
+    S2 = np.empty((n, 2 * (k // GROUP)), dtype=np.uint16)
+    ZS2 = np.empty_like(S2)
+    _check(lib.draft_head_int4_as_int2(_ptr(packed4), _ptr(S), _ptr(ZS), n, k, _ptr(packed2), _ptr(S2), _ptr(ZS2)))
+    return packed2, S2, ZS2
+
+
 def draft_head_tile(packed: np.ndarray, S: np.ndarray, ZS: np.ndarray):
     """Canonical arrays -> (tiled codes uint8 [NBLK*64*K/4], pairs uint32 [NBLK*64*K/128])."""
     lib = load_library()
@@ -187,9 +229,10 @@ def _ws(workspace):
 
 
 def draft_head_coarse(x, tiled, pairs, N: int, kcand: int = 8, cand_val=None, cand_id=None,
-                      coarse_out=None, workspace=None, stream=None):
-    """x: CUDA bf16 [M][K]; tiled/pairs: CUDA tensors in the draft_head_tile layout;
-    workspace: CUDA tensor of draft_head_workspace_bytes(M, K) bytes (allocated when None).
+                      coarse_out=None, workspace=None, stream=None, bits: int = 2):
+    """x: CUDA bf16 [M][K]; tiled/pairs: CUDA tensors in the draft_head_tile layout
+    (bits = 4: of the head's 2K-long 2-bit form); workspace: CUDA tensor of
+    draft_head_workspace_bytes(M, K) bytes (2K for bits = 4; allocated when None).
     Returns (cand_val fp32 [M][NBLK*kcand], cand_id int32 [M][NBLK*kcand])."""
     import torch
     lib = load_library()
@@ -200,9 +243,10 @@ def draft_head_coarse(x, tiled, pairs, N: int, kcand: int = 8, cand_val=None, ca
     if cand_id is None:
         cand_id = _empty((M, nblk * kcand), torch.int32, x)
     if workspace is None:
-        workspace = workspace_for(M, K, x.device)
-    _check(lib.draft_head_coarse(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), kcand, _ptr(cand_val),
-                                 _ptr(cand_id), _ptr(coarse_out), *_ws(workspace), _stream(stream)))
+        workspace = workspace_for(M, K * (2 if bits == 4 else 1), x.device)
+    f = lib.draft_head_coarse_int4 if bits == 4 else lib.draft_head_coarse
+    _check(f(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), kcand, _ptr(cand_val), _ptr(cand_id), _ptr(coarse_out),
+             *_ws(workspace), _stream(stream)))
     return cand_val, cand_id
 
 
@@ -305,7 +349,8 @@ def _event(ev):
 
 
 def draft_head_forward(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, out=None,
-                       coarse_out=None, workspace=None, stream=None, coarse_events=None, wscale=None):
+                       coarse_out=None, workspace=None, stream=None, coarse_events=None, wscale=None,
+                       bits: int = 2):
     """One full call (coarse -> rerank -> argmax) in one library call.
 
     w: the bf16 rows, or with wscale (fp32 [N]) the e4m3 rows (uint8) of the
@@ -318,11 +363,16 @@ def draft_head_forward(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, 
     if out is None:
         out = forward_buffers(M, N, kcand, R, x.device)
     if workspace is None:
-        workspace = workspace_for(M, K, x.device)
+        workspace = workspace_for(M, K * (2 if bits == 4 else 1), x.device)
     e0, e1 = (None, None) if coarse_events is None else (_event(coarse_events[0]), _event(coarse_events[1]))
     outs = (_ptr(out["cand_val"]), _ptr(out["cand_id"]), _ptr(out["rr_id"]), _ptr(out["rr_val"]),
             _ptr(out["out_id"]), _ptr(out["out_val"]), _ptr(coarse_out), *_ws(workspace), _stream(stream), e0, e1)
-    if wscale is None:
+    if bits == 4:
+        if wscale is not None:
+            raise ValueError("the 4-bit head reranks against bf16 rows")
+        _check(lib.draft_head_forward_int4(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0),
+                                           kcand, R, *outs))
+    elif wscale is None:
         _check(lib.draft_head_forward(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0), kcand,
                                       R, *outs))
     else:
@@ -340,29 +390,36 @@ class DraftHead:
     staged(x) does the same with one library call per step.
     """
 
-    def __init__(self, tiled, pairs, w, N: int, K: int, kcand: int = 8, R: int = 32, wscale=None):
+    def __init__(self, tiled, pairs, w, N: int, K: int, kcand: int = 8, R: int = 32, wscale=None, bits: int = 2):
         """w: the bf16 rows the rerank reads, or e4m3 rows (uint8) with their
-        per-row fp32 scale `wscale` (a per-channel FP8 head)."""
+        per-row fp32 scale `wscale` (a per-channel FP8 head).  bits = 4: tiled
+        and pairs hold a 4-bit head in its 2K-long 2-bit form."""
         self.tiled, self.pairs, self.w, self.wscale = tiled, pairs, w, wscale
-        self.N, self.K, self.kcand, self.R = N, K, kcand, R
+        self.N, self.K, self.kcand, self.R, self.bits = N, K, kcand, R, bits
 
     @classmethod
     def from_weight(cls, w_bits: np.ndarray, kcand: int = 8, R: int = 32, device="cuda",
-                    packed=None):
+                    packed=None, bits: int = 2):
+        """bits = 2: the head of the page's default configuration; bits = 4:
+        the 4-bit head (packed: draft_head_quantize_pack_int4's arrays)."""
         import torch
         n, k = w_bits.shape
-        if packed is None:
-            packed = draft_head_quantize_pack(w_bits)
-        tiled, pairs = draft_head_tile(*packed)
+        if bits == 4:
+            packed4 = packed if packed is not None else draft_head_quantize_pack_int4(w_bits)
+            tiled, pairs = draft_head_tile(*draft_head_int4_as_int2(*packed4))
+        else:
+            if packed is None:
+                packed = draft_head_quantize_pack(w_bits)
+            tiled, pairs = draft_head_tile(*packed)
         t_tiled = torch.from_numpy(tiled).to(device)
         t_pairs = torch.from_numpy(pairs.view(np.int32)).to(device)
         t_w = torch.from_numpy(np.ascontiguousarray(w_bits).view(np.int16)).to(device)
-        return cls(t_tiled, t_pairs, t_w, n, k, kcand, R)
+        return cls(t_tiled, t_pairs, t_w, n, k, kcand, R, bits=bits)
 
     def __call__(self, x, coarse_out=None, stream=None, out=None, coarse_events=None, workspace=None):
         return draft_head_forward(x, self.tiled, self.pairs, self.w, self.N, self.kcand, self.R, out=out,
                                   coarse_out=coarse_out, workspace=workspace, stream=stream,
-                                  coarse_events=coarse_events, wscale=self.wscale)
+                                  coarse_events=coarse_events, wscale=self.wscale, bits=self.bits)
 
     def logits_row(self, x, topk_only=False, stream=None):
         """One call plus the bf16 row the page hands to its caller (full, or
@@ -377,7 +434,7 @@ class DraftHead:
     def staged(self, x, coarse_out=None, stream=None):
         """The same call as three library calls (coarse, rerank, argmax)."""
         cv, ci = draft_head_coarse(x, self.tiled, self.pairs, self.N, self.kcand,
-                                   coarse_out=coarse_out, stream=stream)
+                                   coarse_out=coarse_out, stream=stream, bits=self.bits)
         if self.wscale is None:
             rr_id, rr_val = draft_head_rerank(x, self.w, cv, ci, self.R, N=self.N, stream=stream)
         else:

@@ -107,6 +107,7 @@ struct CoarseArgs {
   float* coarse_out;
   uint32_t* cnt;   // per-row arrival counters of the rerank; workgroup 0 zeroes cnt[0..ncnt)
   int ncnt;
+  int kx;          // row length of x: K, or K / 2 for a 4-bit head run at length K (x' = (x, x))
 };
 
 // Device-coherent stores and loads (agent scope: written through to, and read
@@ -448,7 +449,8 @@ void coarse_resident_kernel(CoarseArgs A) {
       for (int j = 0; j < kBatch; ++j) {
         const int i = min(base + tid + j * kResThreads, total - 1);
         const int m = i / per_row, k0 = (i - m * per_row) * 8;
-        v[j] = *reinterpret_cast<const u32x4*>(A.x + (size_t)(m < A.M ? m : 0) * A.K + k0);
+        v[j] = *reinterpret_cast<const u32x4*>(A.x + (size_t)(m < A.M ? m : 0) * A.kx +
+                                               (k0 < A.kx ? k0 : k0 - A.kx));
       }
     };
     auto use_x = [&](int base, const u32x4 (&v)[kBatch]) {
@@ -672,7 +674,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 // Thread (m, G, p): piece p (8 consecutive k) of the four groups of byte
 // group G of row m.  The 16 threads of a (m, G) are 16 consecutive lanes.
-__global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t* __restrict__ x, int M, int MP, int K,
+// x has rows of kx elements; element k of x' is x[k mod kx] (kx = K, or K/2).
+__global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t* __restrict__ x, int M, int MP, int K, int kx,
                                                      u32x4* __restrict__ xslab, u32x4* __restrict__ zslab) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int NG4 = K >> 9, Q4 = K >> 2;
@@ -681,9 +684,11 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t* __restrict_
   const int h = p >> 3, s = (p >> 1) & 3, e = p & 1, f = (h * 2 + e) * 4 + s;
   u32x4 v[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    v[q] = m < M ? *reinterpret_cast<const u32x4*>(x + (size_t)m * K + q * Q4 + 128 * G + 8 * p)
+  for (int q = 0; q < 4; ++q) {
+    const int k = q * Q4 + 128 * G + 8 * p;
+    v[q] = m < M ? *reinterpret_cast<const u32x4*>(x + (size_t)m * kx + (k < kx ? k : k - kx))
                  : u32x4{0u, 0u, 0u, 0u};
+  }
   float X[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1642,6 +1647,21 @@ int check_k(int K) {
   return DH_OK;
 }
 
+// A 4-bit head runs as a 2-bit head of length 2K.
+int check_k4(int K) {
+  if (K < 256 || K % 256 != 0 || 2 * K > DH_MAX_K)
+    return dh::fail(DH_ESHAPE, "K must be a positive multiple of 256 up to %d for a 4-bit head (got %d)",
+                    DH_MAX_K / 2, K);
+  return DH_OK;
+}
+
+// The rerank reads whole rows of K elements: any multiple of 256.
+int check_k_rerank(int K) {
+  if (K < 256 || K % 256 != 0 || K > DH_MAX_K)
+    return dh::fail(DH_ESHAPE, "K must be a positive multiple of 256 up to %d (got %d)", DH_MAX_K, K);
+  return DH_OK;
+}
+
 int check_m(int M) {
   if (M < 1) return dh::fail(DH_EINVAL, "M must be >= 1 (got %d)", M);
   if (M > DH_MAX_M) return dh::fail(DH_EUNSUP, "M must be <= %d (got %d)", DH_MAX_M, M);
@@ -1742,7 +1762,7 @@ int validate_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int
     return dh::fail(DH_EINVAL, "rerank: null pointer");
   int rc = check_m(M);
   if (rc) return rc;
-  if ((rc = check_k(K))) return rc;
+  if ((rc = check_k_rerank(K))) return rc;
   if (N < 1) return dh::fail(DH_ESHAPE, "rerank: N must be >= 1 (got %d)", N);
   const int align = e4m3 ? 16 : 8;
   if (ldw < K || ldw % align != 0)
@@ -1765,14 +1785,15 @@ int validate_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, con
 }
 
 // Launches only; arguments were validated.
+// kx: row length of x (K, or K/2 for a 4-bit head run at length K).
 int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, int kcand,
                   float* cand_val, int32_t* cand_id, float* coarse_out, void* workspace, hipStream_t s,
-                  hipEvent_t ev0, hipEvent_t ev1) {
+                  hipEvent_t ev0, hipEvent_t ev1, int kx = 0) {
   const int nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
   const int ncand = nblk * kcand;
   CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
                reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out,
-               static_cast<uint32_t*>(workspace), M};
+               static_cast<uint32_t*>(workspace), M, kx ? kx : K};
   hipError_t e = hipSuccess;
   if (use_resident(M, K)) {
     switch (resident_rows(M)) {
@@ -1790,7 +1811,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
   for (int m0 = 0; m0 < M; m0 += 16 * kMaxMT) {
     CoarseArgs B = A;
     B.M = std::min(M - m0, 16 * kMaxMT);
-    B.x = A.x + (size_t)m0 * K;
+    B.x = A.x + (size_t)m0 * A.kx;
     B.cand_val = cand_val + (size_t)m0 * ncand;
     B.cand_id = cand_id + (size_t)m0 * ncand;
     B.coarse_out = coarse_out ? coarse_out + (size_t)m0 * N : nullptr;
@@ -1798,8 +1819,8 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
     const int mt = (B.M + 15) / 16, mp = 16 * mt;
     u32x4* xslab = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(workspace) + kCounterBytes);
     u32x4* zslab = xslab + (size_t)(K / DH_GROUP) * 256 * mt;
-    hipLaunchKernelGGL(prep_x_kernel, dim3((mp * NG4 * 16 + 255) / 256), dim3(256), 0, s, B.x, B.M, mp, K, xslab,
-                       zslab);
+    hipLaunchKernelGGL(prep_x_kernel, dim3((mp * NG4 * 16 + 255) / 256), dim3(256), 0, s, B.x, B.M, mp, K, A.kx,
+                       xslab, zslab);
     if ((e = hipGetLastError()) != hipSuccess)
       return dh::fail(DH_EHIP, "prep_x_kernel: %s", hipGetErrorString(e));
     const BigArgs BA{B, xslab, zslab};
@@ -1953,6 +1974,17 @@ int draft_head_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, 
                        as_stream(stream), nullptr, nullptr);
 }
 
+int draft_head_coarse_int4(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                           int kcand, float* cand_val, int32_t* cand_id, float* coarse_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int rc = check_k4(K);
+  if (rc) return rc;
+  if ((rc = validate_coarse(x, M, 2 * K, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes)))
+    return rc;
+  return launch_coarse(x, M, 2 * K, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace,
+                       as_stream(stream), nullptr, nullptr, K);
+}
+
 int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N,
                       const float* cand_val, const int32_t* cand_id, int ncand, int R,
                       int32_t* rr_id, float* rr_val, void* stream) {
@@ -2006,21 +2038,26 @@ namespace {
 
 // One call: coarse launch(es), then rerank + argmax.  wscale null: bf16 rows;
 // else e4m3 rows (w8) with their scales.
+// int4: the coarse head is a 4-bit one in its 2K-long 2-bit form (x is read
+// twice over); the rerank reads rows of length K as always.
 int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, const void* w,
                  const float* wscale, bool e4m3, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
                  int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
                  void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
-                 void* coarse_stop_event) {
+                 void* coarse_stop_event, bool int4 = false) {
   const int ncand = (N > 0 && kcand > 0) ? ((N + DH_BLOCK_N - 1) / DH_BLOCK_N) * kcand : 0;
-  int rc = validate_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes);
+  int rc = int4 ? check_k4(K) : DH_OK;
   if (rc) return rc;
+  const int Kc = int4 ? 2 * K : K;
+  if ((rc = validate_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes)))
+    return rc;
   if ((rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, e4m3, wscale)))
     return rc;
   if ((rc = validate_argmax(rr_id, rr_val, M, R, out_id, out_val))) return rc;
   hipStream_t s = as_stream(stream);
-  if ((rc = launch_coarse(x, M, K, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace, s,
+  if ((rc = launch_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace, s,
                           reinterpret_cast<hipEvent_t>(coarse_start_event),
-                          reinterpret_cast<hipEvent_t>(coarse_stop_event))))
+                          reinterpret_cast<hipEvent_t>(coarse_stop_event), K)))
     return rc;
   int nblk, kc;
   if (fast_rerank(N, ncand, R, nblk, kc)) {   // rerank and argmax in one kernel
@@ -2045,6 +2082,16 @@ int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
   return forward_impl(x, M, K, N, tiled, pairs, w, nullptr, false, ldw, kcand, R, cand_val, cand_id, rr_id, rr_val,
                       out_id, out_val, coarse_out, workspace, workspace_bytes, stream, coarse_start_event,
                       coarse_stop_event);
+}
+
+int draft_head_forward_int4(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                            const void* w, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
+                            int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
+                            void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
+                            void* coarse_stop_event) {
+  return forward_impl(x, M, K, N, tiled, pairs, w, nullptr, false, ldw, kcand, R, cand_val, cand_id, rr_id, rr_val,
+                      out_id, out_val, coarse_out, workspace, workspace_bytes, stream, coarse_start_event,
+                      coarse_stop_event, true);
 }
 
 int draft_head_forward_e4m3(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,

@@ -54,6 +54,15 @@ inline uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(r >> 16);
 }
 
+// A 4-bit head of length K runs as a 2-bit head of length 2K.
+int check_shape4(int64_t N, int64_t K) {
+  if (N < 1) return dh::fail(DH_ESHAPE, "N must be >= 1 (got %lld)", (long long)N);
+  if (K < 256 || K % 256 != 0 || 2 * K > DH_MAX_K)
+    return dh::fail(DH_ESHAPE, "K must be a positive multiple of 256 up to %d for a 4-bit head (got %lld)",
+                    DH_MAX_K / 2, (long long)K);
+  return DH_OK;
+}
+
 int check_shape(int64_t N, int64_t K) {
   if (N < 1) return dh::fail(DH_ESHAPE, "N must be >= 1 (got %lld)", (long long)N);
   if (K < 512 || K % 512 != 0 || K > DH_MAX_K)
@@ -82,8 +91,10 @@ void parallel_rows(int64_t N, int nthreads, F&& body) {
 }
 
 // One row: codes into `codes` (K bytes), scale pair into S/ZS (K/128 each).
-void quantize_row(const uint16_t* w, int64_t K, uint8_t* codes, uint16_t* S, uint16_t* ZS) {
-  const float three = 3.0f, four = 4.0f, floor_sc = 1e-8f;
+// levels / premul: 3 / 4 for the 2-bit head, 15 / 16 for the 4-bit one.
+void quantize_row(const uint16_t* w, int64_t K, uint8_t* codes, uint16_t* S, uint16_t* ZS, float levels = 3.0f,
+                  float premul = 4.0f) {
+  const float three = levels, four = premul, floor_sc = 1e-8f;
   for (int64_t g = 0; g < K / DH_GROUP; ++g) {
     const uint16_t* wg = w + g * DH_GROUP;
     float lo = bf16_to_f32(wg[0]), hi = lo;
@@ -147,6 +158,53 @@ int draft_head_quantize_pack(const uint16_t* w, int64_t N, int64_t K, int64_t ld
       for (int64_t j = 0; j < Q; ++j)
         out[j] = static_cast<uint8_t>(codes[j] | (codes[Q + j] << 2) | (codes[2 * Q + j] << 4) |
                                       (codes[3 * Q + j] << 6));
+    }
+  });
+  return dh::ok();
+}
+
+int draft_head_quantize_pack_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed4,
+                                  uint16_t* S, uint16_t* ZS, int nthreads) {
+  if (!w || !packed4 || !S || !ZS) return dh::fail(DH_EINVAL, "quantize_pack_int4: null pointer");
+  int rc = check_shape4(N, K);
+  if (rc) return rc;
+  if (ldw < K)
+    return dh::fail(DH_EINVAL, "quantize_pack_int4: ldw (%lld) < K (%lld)", (long long)ldw, (long long)K);
+  if (nthreads < 0) return dh::fail(DH_EINVAL, "quantize_pack_int4: nthreads < 0");
+  const int64_t H = K / 2;
+  parallel_rows(N, nthreads, [&](int64_t a, int64_t b) {
+    std::vector<uint8_t> codes(K);
+    for (int64_t n = a; n < b; ++n) {
+      quantize_row(w + n * ldw, K, codes.data(), S + n * (K / DH_GROUP), ZS + n * (K / DH_GROUP), 15.0f, 16.0f);
+      uint8_t* out = packed4 + n * H;
+      for (int64_t j = 0; j < H; ++j) out[j] = static_cast<uint8_t>(codes[j] | (codes[H + j] << 4));
+    }
+  });
+  return dh::ok();
+}
+
+int draft_head_int4_as_int2(const uint8_t* packed4, const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K,
+                            uint8_t* packed2, uint16_t* S2, uint16_t* ZS2) {
+  if (!packed4 || !S || !ZS || !packed2 || !S2 || !ZS2) return dh::fail(DH_EINVAL, "int4_as_int2: null pointer");
+  int rc = check_shape4(N, K);
+  if (rc) return rc;
+  const int64_t H = K / 2, NG = K / DH_GROUP;
+  parallel_rows(N, 0, [&](int64_t a, int64_t b) {
+    for (int64_t n = a; n < b; ++n) {
+      // byte j of the 2K-long quarter-split row carries k' = j, K/2+j (high
+      // halves of codes j, K/2+j) and K+j, 3K/2+j (their low halves)
+      for (int64_t j = 0; j < H; ++j) {
+        const uint32_t b4 = packed4[n * H + j], lo = b4 & 15u, hi = b4 >> 4;
+        packed2[n * H + j] = static_cast<uint8_t>((lo >> 2) | ((hi >> 2) << 2) | ((lo & 3u) << 4) | ((hi & 3u) << 6));
+      }
+      for (int64_t g = 0; g < NG; ++g) {
+        const uint16_t s = S[n * NG + g];
+        const uint16_t s4 = f32_to_bf16(bf16_to_f32(s) * 0.25f);   // exact: a power-of-two scaling
+        S2[n * 2 * NG + g] = s;
+        ZS2[n * 2 * NG + g] = ZS[n * NG + g];
+        S2[n * 2 * NG + NG + g] = s4;
+        ZS2[n * 2 * NG + NG + g] = s4;
+      }
     }
   });
   return dh::ok();

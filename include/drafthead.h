@@ -105,6 +105,38 @@ int draft_head_tile(const uint8_t* packed, const uint16_t* S, const uint16_t* ZS
                     int64_t N, int64_t K, uint8_t* tiled, uint32_t* pairs);
 
 /*
+ * HOST.  The 4-bit head of the page (`_quantize_head_now` at BITS = 4): the
+ * quantiser of draft_head_quantize_pack with 15 levels and the premultiplier
+ * 16, per (row n, group g of 128 consecutive k), each float32 operation
+ * rounded on its own:
+ *   sc = max((hi - lo) / 15, 1e-8);  zp = clamp(rne(-lo / sc), 0, 15)
+ *   q = clamp(rne(w / sc + zp), 0, 15);  S = bf16(16 sc);  ZS = bf16(16 sc + zp sc)
+ * and half-split packing: byte j of a row holds the codes of k = j (bits 0-3)
+ * and K/2 + j (bits 4-7).  The effective weight of code v is (S/16) v - (ZS - S).
+ *   w        bf16 bits [N][ldw], ldw >= K;  packed4  out, uint8 [N][K/2]
+ *   S, ZS    out, bf16 bits [N][K/128] each
+ * Limits: K a positive multiple of 256 with 2K <= DH_MAX_K.
+ * Errors: DH_EINVAL (null pointer, ldw < K, nthreads < 0), DH_ESHAPE.
+ */
+int draft_head_quantize_pack_int4(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed4,
+                                  uint16_t* S, uint16_t* ZS, int nthreads);
+
+/*
+ * HOST.  A 4-bit head as a 2-bit head of length 2K, the form the device path
+ * runs: with v = 4 vh + vl, the weight (S/16) v - (ZS - S) of k equals the
+ * 2-bit weight of k' = k (code vh, pair S, ZS) plus that of k' = K + k (code
+ * vl, pair S/4, S/4, exact in bf16), so for x' = (x, x) the 2-bit scores of
+ * the 2K-long head are the 4-bit scores.  The output is in the canonical
+ * 2-bit form (quarter-split over 2K; pairs of groups K/128 .. 2K/128 - 1 are
+ * the S/4 ones); tile it with draft_head_tile(N, 2K).
+ *   packed4, S, ZS   draft_head_quantize_pack_int4's arrays
+ *   packed2   out, uint8 [N][K/2] (2K/4 bytes a row);  S2, ZS2  out, bf16 bits [N][2K/128]
+ * Errors: DH_EINVAL (null pointer), DH_ESHAPE (as draft_head_quantize_pack_int4).
+ */
+int draft_head_int4_as_int2(const uint8_t* packed4, const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K,
+                            uint8_t* packed2, uint16_t* S2, uint16_t* ZS2);
+
+/*
  * Bytes of device workspace draft_head_coarse / draft_head_forward need for M
  * rows of length K: 512 bytes of per-row counters, plus, unless M <= 8 and
  * the resident kernel holds all of x in LDS (any K at M = 1; K <= 35840,
@@ -153,7 +185,7 @@ int draft_head_coarse(const void* x, int M, int K, int N, const uint8_t* tiled,
  *   rr_id      out, int32 [M][R], ordered (coarse value desc, id asc); -1 pads
  *              a row with fewer than R valid candidates
  *   rr_val     out, fp32 [M][R] exact logit of rr_id (-inf where rr_id = -1)
- * Limits: 1 <= M <= DH_MAX_M, K % 512 == 0, 1 <= R <= min(ncand, DH_MAX_R).
+ * Limits: 1 <= M <= DH_MAX_M, K % 256 == 0, 1 <= R <= min(ncand, DH_MAX_R).
  * Errors: DH_EINVAL, DH_ESHAPE, DH_EUNSUP, DH_EHIP.
  */
 int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N,
@@ -221,6 +253,25 @@ int draft_head_forward_e4m3(const void* x, int M, int K, int N, const uint8_t* t
                             float* cand_val, int32_t* cand_id, int32_t* rr_id, float* rr_val, int32_t* out_id,
                             float* out_val, float* coarse_out, void* workspace, size_t workspace_bytes,
                             void* stream, void* coarse_start_event, void* coarse_stop_event);
+
+/*
+ * DEVICE.  draft_head_coarse and draft_head_forward for a 4-bit head (the
+ * page's BITS = 4 configuration, KCAND = 1 in its measurements): tiled and
+ * pairs are draft_head_tile(draft_head_int4_as_int2(...), N, 2K), the 2-bit
+ * form of length 2K, which the coarse kernels run with x read twice over
+ * (x' = (x, x)); x, w and everything else are as for the 2-bit calls with K
+ * the head's own length.  The workspace is draft_head_workspace_bytes(M, 2K).
+ * Limits: K a positive multiple of 256 with 2K <= DH_MAX_K.
+ * Errors: as draft_head_coarse / draft_head_forward.
+ */
+int draft_head_coarse_int4(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                           int kcand, float* cand_val, int32_t* cand_id, float* coarse_out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+int draft_head_forward_int4(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                            const void* w, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
+                            int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
+                            void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
+                            void* coarse_stop_event);
 
 /*
  * DEVICE.  The bf16 row the page's `_apply_head_int2` hands to its caller

@@ -407,3 +407,82 @@ def test_e4m3_rerank_full_shape(dev, full):
     E = oracle.exact_head(full["x"], full["w"])
     agree = int(np.sum(got["out_id"] == np.argmax(E, axis=1)))
     _log(f"e4m3 full shape m=72: argmax agreement with the exact bf16 head {agree}/72 (reported)")
+
+
+# ------------------------------------------------------------ 4-bit head
+@pytest.mark.parametrize("m,k,n,kcand,r", [(1, 256, 3000, 1, 32), (3, 768, 5000, 1, 32), (8, 1024, 20000, 8, 32),
+                                           (20, 512, 3000, 1, 16), (5, 2048, 5000, 4, 32), (72, 1024, 2100, 1, 32)])
+def test_int4_parity(dev, m, k, n, kcand, r):
+    """The 4-bit head (run as its 2K-long 2-bit form) against the oracle's own
+    4-bit definition."""
+    w = workload.gen_weight(n, k, seed=3000 + n)
+    x = workload.gen_x(m, k, seed=3001 + n)
+    _log(f"int4 case m={m} k={k} n={n} kcand={kcand} r={r}")
+    packed4 = oracle.quantize_pack_int4(w)
+    head = B.DraftHead.from_weight(w, kcand=kcand, R=r, device=dev, packed=packed4, bits=4)
+    got = run_gpu(head, x, dev)
+    stats = compare(oracle.pipeline(x, w, *packed4, kcand=kcand, r=r, bits=4), got, n, kcand)
+    _log(f"  ok {stats}")
+
+
+def test_int4_forward_matches_staged_calls(dev):
+    n, k, m = 20000, 1024, 5
+    w = workload.gen_weight(n, k, seed=101)
+    head = B.DraftHead.from_weight(w, kcand=1, R=32, device=dev, bits=4)
+    x = _to_dev(workload.gen_x(m, k, seed=102), dev)
+    a = head.staged(x)
+    b = head(x)
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.timeout(900)
+def test_int4_full_shape(dev, full):
+    """The per-rank shard as a 4-bit head at KCAND = 1 (the page's 4-bit
+    configuration): the library quantiser against the oracle's, parity at
+    M = 1, 8, 72, and the agreement with the exact bf16 head (reported)."""
+    cfg = full["cfg"]
+    x, w = full["x"], full["w"]
+    _log("int4 full shape: quantize_pack_int4 (library and oracle)")
+    packed4 = B.draft_head_quantize_pack_int4(w)
+    opacked4 = oracle.quantize_pack_int4(w)
+    assert all(np.array_equal(a, b) for a, b in zip(packed4, opacked4))
+    head = B.DraftHead.from_weight(w, kcand=1, R=cfg.rerank, device=dev, packed=packed4, bits=4)
+    _log("int4 full shape: oracle coarse for 72 rows")
+    c = oracle.coarse_int4(x, *opacked4)
+    cv, ci = oracle.block_topk(c, 1)
+    rr_id, _ = oracle.row_topr(cv, ci, cfg.rerank)
+    e = oracle.rerank_exact(x, w, rr_id)
+    out_id, out_val = oracle.final_argmax(rr_id, e)
+    ref = {"coarse": c, "cand_val": cv, "cand_id": ci, "rr_id": rr_id, "rr_val": e, "out_id": out_id,
+           "out_val": out_val, "tie_rows": oracle.tie_rows(e)}
+    for m in (1, 8, 72):
+        got = run_gpu(head, x[:m], dev)
+        stats = compare(_prefix(ref, m), got, cfg.n, 1)
+        _log(f"int4 full shape m={m} kcand=1: {stats}")
+    E = oracle.exact_head(x, w)
+    agree = int(np.sum(got["out_id"] == np.argmax(E, axis=1)))
+    _log(f"int4 full shape m=72 kcand=1: argmax agreement with the exact bf16 head {agree}/72 (reported)")
+
+
+@pytest.mark.timeout(900)
+def test_int4_recall_stress_full_shape(dev, full):
+    """Planted same-block near-ties with a 4-bit head: parity at KCAND = 1, misses reported."""
+    cfg = workload.CONFIGS["recall"]
+    x = full["x"][:cfg.m]
+    w, pairs = workload.plant_recall_pairs(x, full["w"], target=12.0, gap=0.01)
+    packed4 = B.draft_head_quantize_pack_int4(w)
+    head = B.DraftHead.from_weight(w, kcand=1, R=32, device=dev, packed=packed4, bits=4)
+    got = run_gpu(head, x, dev, want_coarse=False)
+    c = oracle.coarse_int4(x, *packed4)
+    cv, ci = oracle.block_topk(c, 1)
+    rr_id, _ = oracle.row_topr(cv, ci, 32)
+    e = oracle.rerank_exact(x, w, rr_id)
+    out_id, out_val = oracle.final_argmax(rr_id, e)
+    ref = {"coarse": c, "cand_val": cv, "cand_id": ci, "rr_id": rr_id, "rr_val": e, "out_id": out_id,
+           "out_val": out_val, "tie_rows": oracle.tie_rows(e)}
+    compare(ref, got, cfg.n, 1, check_coarse=False)
+    winners = np.array([p[0] for p in pairs])
+    _log(f"int4 recall stress: argmax misses vs planted winner at KCAND=1: "
+         f"{int(np.sum(got['out_id'] != winners))}/32 (reported)")

@@ -27,7 +27,8 @@ def test_library_exports_every_header_symbol(lib):
                           "draft_head_tile", "draft_head_workspace_bytes", "draft_head_coarse",
                           "draft_head_rerank", "draft_head_argmax", "draft_head_forward",
                           "draft_head_stream_read", "draft_head_logits_row", "draft_head_rerank_e4m3",
-                          "draft_head_forward_e4m3"}
+                          "draft_head_forward_e4m3", "draft_head_quantize_pack_int4",
+                          "draft_head_int4_as_int2", "draft_head_coarse_int4", "draft_head_forward_int4"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -297,3 +298,48 @@ def test_forward_validation(lib):
     _err(lib, call(R=0), B.DH_EUNSUP)
     _err(lib, call(M=129), B.DH_EUNSUP)
     _err(lib, call(w=MIS), B.DH_EINVAL)
+
+
+# ------------------------------------------------------------- 4-bit head
+@pytest.mark.parametrize("n,k", [(8, 256), (300, 1024), (2048, 5120)])
+def test_quantize_pack_int4_matches_oracle(lib, n, k):
+    w = workload.gen_weight(n, k, seed=n + k)
+    w[3, :128] = w[3, 0]                      # a constant group
+    got = B.draft_head_quantize_pack_int4(w)
+    want = oracle.quantize_pack_int4(w)
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+
+
+def test_int4_as_int2_is_the_same_head():
+    """The 2K-long 2-bit form's weights, summed over its two halves, are the
+    4-bit head's weights exactly (the oracle's definitions of both)."""
+    n, k = 200, 1024
+    w = workload.gen_weight(n, k, seed=5)
+    packed4, S, ZS = B.draft_head_quantize_pack_int4(w)
+    packed2, S2, ZS2 = B.draft_head_int4_as_int2(packed4, S, ZS)
+    w2 = oracle.effective_weight(packed2, S2, ZS2)
+    assert np.array_equal(w2[:, :k] + w2[:, k:], oracle.effective_weight_int4(packed4, S, ZS))
+
+
+def test_int4_validation(lib):
+    p = np.zeros(4096, np.uint8).ctypes.data
+    _err(lib, lib.draft_head_quantize_pack_int4(None, 4, 256, 256, p, p, p, 0), B.DH_EINVAL)
+    _err(lib, lib.draft_head_quantize_pack_int4(p, 4, 384, 384, p, p, p, 0), B.DH_ESHAPE)
+    _err(lib, lib.draft_head_quantize_pack_int4(p, 4, 256, 128, p, p, p, 0), B.DH_EINVAL)
+    _err(lib, lib.draft_head_quantize_pack_int4(p, 4, 65536, 65536, p, p, p, 0), B.DH_ESHAPE)
+    _err(lib, lib.draft_head_int4_as_int2(p, p, None, 4, 256, p, p, p), B.DH_EINVAL)
+    _err(lib, lib.draft_head_int4_as_int2(p, p, p, 0, 256, p, p, p), B.DH_ESHAPE)
+
+
+def test_int4_device_validation(lib):
+    """The 4-bit calls check the head's own K (a multiple of 256) and size the
+    workspace for its 2K-long form, before any launch."""
+    need = B.draft_head_workspace_bytes(9, 1024)           # M = 9, K = 512: the 2K = 1024 form
+    f = lib.draft_head_coarse_int4
+    _err(lib, f(FAKE, 1, 384, 64, FAKE, FAKE, 8, FAKE, FAKE, None, FAKE, 512, None), B.DH_ESHAPE)
+    _err(lib, f(FAKE, 1, 32768 + 256, 64, FAKE, FAKE, 8, FAKE, FAKE, None, FAKE, 512, None), B.DH_ESHAPE)
+    _err(lib, f(FAKE, 9, 512, 64, FAKE, FAKE, 8, FAKE, FAKE, None, FAKE, need - 16, None), B.DH_EINVAL)
+    g = lib.draft_head_forward_int4
+    _err(lib, g(FAKE, 1, 384, 64, FAKE, FAKE, FAKE, 384, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 512,
+                None, None, None), B.DH_ESHAPE)
