@@ -21,7 +21,9 @@ Prints one JSON line:
                its fractions of the HBM and bf16 MFMA peaks, the warm
                (cache-resident) figure, the time of the row handed to a
                top-k caller (draft_head_logits_row), the per-call time with
-               the e4m3 rerank source, and the device's achieved
+               the e4m3 rerank source, the 4-bit head's per-call time
+               (KCAND = 1, 357,580,800 B of codes and pairs per call),
+               and the device's achieved
                read rate (the library's streaming-read reference) and copy rate
 """
 from __future__ import annotations
@@ -182,6 +184,33 @@ class Rig:
             e.record()
             torch.cuda.synchronize()
             res[str(m)] = round(s.elapsed_time(e) / steps * 1e3, 2)
+        return res
+
+    def int4_call_us(self, ms=(1, 8, 72), steps=200, copies=2):
+        """Per-call time of the 4-bit head at KCAND = 1 (the page's 4-bit
+        configuration), run as its 2K-long 2-bit form; weights rotated."""
+        torch, B = self.torch, self.B
+        packed4 = B.draft_head_quantize_pack_int4(self.w_host)
+        tiled, pairs = B.draft_head_tile(*B.draft_head_int4_as_int2(*packed4))
+        t_t = torch.from_numpy(tiled).to(self.dev)
+        t_p = torch.from_numpy(pairs.view(np.int32)).to(self.dev)
+        heads = [B.DraftHead(t_t if c == 0 else t_t.clone(), t_p if c == 0 else t_p.clone(), self.heads[0].w,
+                             N, K, 1, R, bits=4) for c in range(copies)]
+        res = {}
+        for m in ms:
+            out = B.forward_buffers(m, N, 1, R, self.dev)
+            ws = B.workspace_for(m, 2 * K, self.dev)
+            for i in range(20):
+                heads[i % copies](self.x[:m], stream=self.stream, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for i in range(steps):
+                heads[i % copies](self.x[:m], stream=self.stream, out=out, workspace=ws)
+            e.record()
+            torch.cuda.synchronize()
+            res[str(m)] = round(s.elapsed_time(e) / steps * 1e3, 2)
+        del heads, t_t, t_p
         return res
 
     def logits_row_us(self, m, reps=50):
@@ -353,6 +382,8 @@ def main():
                                  "note": "one weight copy reused back to back: Infinity-Cache resident"}
         extra["logits_row_us"] = {str(mm): rig.logits_row_us(mm) for mm in (1, 8, 72)}
         extra["e4m3_rerank_us_per_call"] = rig.e4m3_call_us()
+        extra["int4_kcand1_us_per_call"] = rig.int4_call_us()
+        log(f"one call of the 4-bit head at KCAND=1: {extra['int4_kcand1_us_per_call']}")
         log(f"one call with the e4m3 rerank source: {extra['e4m3_rerank_us_per_call']}")
         log(f"row for the caller (draft_head_logits_row alone): {extra['logits_row_us']}")
         extra["device_copy_GBps"] = round(rig.copy_bandwidth(), 1)
