@@ -382,12 +382,13 @@ __device__ __forceinline__ float row16_sum(float s) {
 // workgroup stages all of x once (MP rows, MP = the next power of two >= M;
 // lanes whose A row nn >= MP read row nn & (MP-1), whose results are never
 // used) with the group sums X.  Then every wave streams its tiles with no
-// further barrier, keeping the codes and scale pairs of the next D-1 byte
-// groups in flight in a ring of D register sets.  At the end the tiles of a
-// block meet in LDS and the block's top-kcand is selected.
+// further barrier, keeping the codes and scale pairs of the next byte groups
+// in flight in a ring of D register sets (D-1 groups ahead at one row, D from
+// two rows on).  At the end the tiles of a block meet in LDS and the block's
+// top-kcand is selected.
 // LDS: x fragments [group it = 4G + q][f][MP] (16 bytes each), X[it][MP], then
 // the block scores [block][16 rows][64 columns].
-constexpr int kResDepth = 2;   // byte groups held in registers (D-1 in flight)
+constexpr int kResDepth = 2;   // ring sets of byte groups held in registers
 
 // Tiles per wave: two for 1-2 rows (more waves to hide latency), four for 4-8
 // rows, where the per-row scale updates make a wave's share of work larger.
@@ -395,9 +396,14 @@ constexpr int res_nt(int MP) { return MP <= 2 ? 2 : 4; }
 
 template <int MP>
 constexpr int res_waves() { return 8; }
+// Waves per SIMD the grid needs to be resident at once (1940 blocks at the
+// page's N): four at 1-2 rows (two workgroups of four blocks per CU), two at
+// 4-8 rows (one workgroup of eight blocks).
+template <int MP>
+constexpr int res_min_waves() { return MP <= 2 ? 4 : 2; }
 
 template <int MP>
-__global__ __launch_bounds__(64 * res_waves<MP>())
+__global__ __launch_bounds__(64 * res_waves<MP>()) __attribute__((amdgpu_waves_per_eu(res_min_waves<MP>())))
 void coarse_resident_kernel(CoarseArgs A) {
   constexpr int kResWaves = res_waves<MP>();
   constexpr int kResThreads = 64 * kResWaves;
@@ -453,29 +459,41 @@ void coarse_resident_kernel(CoarseArgs A) {
                                                (k0 < A.kx ? k0 : k0 - A.kx));
       }
     };
+    // Only the LDS writes are predicated: a load whose value were used only
+    // under the predicate could be sunk by the compiler behind the code loads.
     auto use_x = [&](int base, const u32x4 (&v)[kBatch]) {
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int i = base + tid + j * kResThreads;
+        const int ic = min(i, total - 1);
+        const int m = ic / per_row, k0 = (ic - m * per_row) * 8;
+        const u32x4 vm = m < A.M ? v[j] : u32x4{0u, 0u, 0u, 0u};
+        const int q = k0 / Q4, G = (k0 - q * Q4) >> 7, p = (k0 >> 3) & 15;
+        const int it = G * 4 + q;
+        float sum;
+        const u32x4 o = permute_x(vm, sum);
+        sum = row16_sum(sum);
         if (i < total) {   // uniform per 16-lane row: total is a multiple of 16
-          const int m = i / per_row, k0 = (i - m * per_row) * 8;
-          const u32x4 vm = m < A.M ? v[j] : u32x4{0u, 0u, 0u, 0u};
-          const int q = k0 / Q4, G = (k0 - q * Q4) >> 7, p = (k0 >> 3) & 15;
-          const int it = G * 4 + q;
-          float sum;
-          const u32x4 o = permute_x(vm, sum);
           const int h = p >> 3, s = (p >> 1) & 3, e = p & 1;
           xs[(it * 16 + (h * 2 + e) * 4 + s) * MP + m] = o;
-          sum = row16_sum(sum);
           if (p == 0) Xs[it * MP + m] = sum;
         }
       }
     };
     u32x4 v[kBatch];
     issue_x(0, v);
+    // The first D-1 byte groups at one row; from two rows on the first D,
+    // unconditionally (a guarded load makes the compiler wait for it before
+    // x can be used; with a single byte group, K = 512, the second set
+    // re-reads the first).
+    if constexpr (MP == 1) {
 #pragma unroll
-    for (int d = 0; d < D - 1; ++d)
-      if (d < NG4) load_codes(d, rw[d], sw[d]);
+      for (int d = 0; d < D - 1; ++d)
+        if (d < NG4) load_codes(d, rw[d], sw[d]);
+    } else {
+#pragma unroll
+      for (int d = 0; d < D; ++d) load_codes(min(d, NG4 - 1), rw[d], sw[d]);
+    }
     use_x(0, v);
     for (int base = kResThreads * kBatch; base < total; base += kResThreads * kBatch) {
       issue_x(base, v);
@@ -507,12 +525,42 @@ void coarse_resident_kernel(CoarseArgs A) {
     group_scale<1, MR, 2, NT>(acc, c0, sz, Xg + 2 * MP, 0);
     group_scale<1, MR, 3, NT>(acc, c1, sz, Xg + 3 * MP, 0);
   };
-  for (int G0 = 0; G0 < NG4; G0 += D) {
+  // Two forms of the same stream.  From two rows on, each ring set is
+  // refilled right after its byte group is done, so D byte groups are in
+  // flight while one is waited for.  Its steady state loads unconditionally,
+  // so that every wait is exact (a guarded load makes the compiler wait as if
+  // it had not been issued), and scheduling barriers keep the loads where
+  // they are (sunk towards their first use they would no longer be ahead;
+  // mixed into the byte group's work they would need other registers than
+  // the ring's, copied back after a wait).  At one row that form needs more
+  // than the 128 registers that four waves per SIMD allow (the compiler then
+  // spills), so one row keeps the guarded form, D-1 byte groups ahead (its
+  // extra waits measured no slower there than exact ones).
+  if constexpr (MP == 1) {
+    for (int G0 = 0; G0 < NG4; G0 += D) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
+      for (int d = 0; d < D; ++d) {
+        const int G = G0 + d;
+        if (G + D - 1 < NG4) load_codes(G + D - 1, rw[(d + D - 1) % D], sw[(d + D - 1) % D]);
+        if (G < NG4) byte_group(G, rw[d], sw[d]);
+      }
+    }
+  } else {
+    int G0 = 0;
+    for (; G0 + 2 * D - 1 < NG4; G0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        byte_group(G0 + d, rw[d], sw[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(G0 + d + D, rw[d], sw[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 2 * D - 1; ++d) {
       const int G = G0 + d;
-      if (G + D - 1 < NG4) load_codes(G + D - 1, rw[(d + D - 1) % D], sw[(d + D - 1) % D]);
-      if (G < NG4) byte_group(G, rw[d], sw[d]);
+      if (G < NG4) byte_group(G, rw[d % D], sw[d % D]);
+      if (G + D < NG4) load_codes(G + D, rw[d % D], sw[d % D]);
     }
   }
 
