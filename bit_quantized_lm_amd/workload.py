@@ -64,6 +64,21 @@ def gen_weight(n: int, k: int, seed: int = SEED_W, std: float = 0.02,
     return out
 
 
+def _e4m3_round(v: np.ndarray):
+    """Nearest e4m3 grid value to v (float64), ties to the even code, within
+    +-448: (value, code uint8)."""
+    a = np.minimum(np.abs(v), 448.0)
+    # step of the e4m3 grid around a: 2^(e-3) for a in [2^e, 2^(e+1)), e >= -6; 2^-9 below 2^-6
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    step = np.exp2(e - 3)
+    q = np.minimum(np.rint(a / step) * step, 448.0)          # ties to even step count = even code
+    sub = q < 2.0 ** -6
+    eq = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
+    code = np.where(sub, np.rint(q / 2.0 ** -9), (eq + 7) * 8 + np.rint(q / np.exp2(eq) * 8 - 8))
+    code = (code.astype(np.int64) | np.where(v < 0, 128, 0)).astype(np.uint8)
+    return np.where(v < 0, -q, q), code
+
+
 def e4m3_head(w_bits: np.ndarray):
     """A synthetic e4m3 head (stand-in for a checkpoint's per-channel FP8
     lm_head): per row, scale = max |w| / 448 (float32) and codes = w / scale
@@ -75,16 +90,41 @@ def e4m3_head(w_bits: np.ndarray):
     out = np.empty(w.shape, dtype=np.uint8)
     for i in range(0, w.shape[0], 512):
         v = w[i:i + 512].astype(np.float64) / scale[i:i + 512, None].astype(np.float64)
-        a = np.minimum(np.abs(v), 448.0)
-        # step of the e4m3 grid around a: 2^(e-3) for a in [2^e, 2^(e+1)), e >= -6; 2^-9 below 2^-6
-        e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
-        step = np.exp2(e - 3)
-        q = np.minimum(np.rint(a / step) * step, 448.0)          # ties to even step count = even code
-        sub = q < 2.0 ** -6
-        eq = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
-        code = np.where(sub, np.rint(q / 2.0 ** -9), (eq + 7) * 8 + np.rint(q / np.exp2(eq) * 8 - 8))
-        out[i:i + 512] = (code.astype(np.int64) | np.where(v < 0, 128, 0)).astype(np.uint8)
+        out[i:i + 512] = _e4m3_round(v)[1]
     return out, scale
+
+
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def nvfp4_head(w_bits: np.ndarray):
+    """A synthetic NVFP4 head (stand-in for a checkpoint's NVFP4 weight, the
+    two-level scaling such checkpoints use): global scale g = max |w| /
+    (6 * 448) (float32); per 16 elements an e4m3 block scale, the nearest
+    e4m3 value to the block's max |w| / (6 g); each element the nearest e2m1
+    value to w / (block scale * g).  Bytes hold element 2j in the low nibble,
+    2j+1 in the high one.
+    Returns (w4 uint8 [N][K/2], bscale uint8 [N][K/16], gscale float32)."""
+    w = bf16_bits_to_f32(w_bits)
+    n, k = w.shape
+    amax = float(np.abs(w).max())
+    g = np.float32(amax / (6.0 * 448.0) if amax > 0 else 1.0)
+    w4 = np.empty((n, k // 2), dtype=np.uint8)
+    bscale = np.empty((n, k // 16), dtype=np.uint8)
+    mids = (E2M1_GRID[1:] + E2M1_GRID[:-1]) / 2
+    for i in range(0, n, 512):
+        blk = w[i:i + 512].astype(np.float64).reshape(-1, k // 16, 16)
+        bq, bcode = _e4m3_round(np.abs(blk).max(axis=2) / (6.0 * float(g)))
+        bscale[i:i + 512] = bcode
+        den = bq[..., None] * float(g)
+        v = np.divide(blk, den, out=np.zeros_like(blk), where=den > 0)
+        a = np.abs(v)
+        idx = np.zeros(a.shape, dtype=np.int64)
+        for t in mids:
+            idx += a > t
+        codes = (idx | np.where(v < 0, 8, 0)).reshape(-1, k)
+        w4[i:i + 512] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return w4, bscale, g
 
 
 def outlier_channels(k: int, frac: float = 0.01, seed: int = SEED_OUTLIERS) -> np.ndarray:

@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, step-by-step CPU
 implementation of what the draft head computes, written from the page
 "radiance_drafthead.py" (a vLLM plug-in module; its module docstring, the
 quantiser `_quantize_head_now`, the kernels `_draft_head_int2`, `_emit`,
-`_rerank_exact` and the per-call glue `_apply_head_int2`).  Only the tests,
+`_rerank_exact` and the per-call glue `_apply_head_int2`), and, for one
+optional rerank source, the page on vLLM pull request 55713 (the NVFP4
+gathered projection `_nvfp4_gathered_bias_kernel`).  Only the tests,
 `__graft_entry__.smoke()` and the `cpu_baseline` leg of `bench.py` may use it.
 The product library never imports it and it imports nothing from the product
 library.
@@ -15,8 +17,8 @@ bf16     bf16 <-> float conversions (round to nearest even), own code.
 quant    min/max asymmetric int2 quantiser, quarter-split packing, unpacking
          and the effective weight defined by the stored scale pair; the same
          at 4 bits (half-split packing, bias 16).
-head     coarse scores, block top-KCAND, row top-R, exact rerank (bf16 rows or
-         e4m3 rows with a per-row scale), argmax, the
+head     coarse scores, block top-KCAND, row top-R, exact rerank (bf16 rows,
+         e4m3 rows with a per-row scale, or NVFP4 rows), argmax, the
          bf16 row handed to the caller (full or top-k only), and the exact
          bf16 head (for agreement reports only).
 brute    pure-Python, exact-rational re-statement of every step for tiny
@@ -39,4 +41,5 @@ from .quant import (GROUP, quantize, pack_quarter_split, unpack_quarter_split,  
                     quantize_pack_int4, effective_weight_int4)
 from .head import (BLOCK_N, coarse, coarse_int4, coarse_collapse, block_topk, row_topr,  # noqa: F401
                    rerank_exact, final_argmax, logits_row, exact_head, pipeline, tie_rows,
-                   e4m3_value, rerank_exact_e4m3)
+                   e4m3_value, rerank_exact_e4m3, e2m1_value, e4m3fn_value, nvfp4_rows,
+                   rerank_exact_nvfp4)

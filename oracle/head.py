@@ -187,6 +187,67 @@ def rerank_exact_e4m3(x_bits, w8, scale, rr_id):
     return out
 
 
+def e2m1_value(nibbles):
+    """Value of e2m1 (FP4) codes, float64, as the format defines them: sign
+    bit 3, exponent bits 2-1 with bias 1, mantissa bit 0; exponent 0 is
+    subnormal (magnitude 0.5 * mantissa), otherwise the magnitude is
+    (1 + mantissa/2) * 2^(exponent - 1).  The NVFP4 rows of the page for vLLM
+    pull request 55713 hold these codes (its kernel decodes them with
+    `_e2m1_inline`, whose body the page does not show).
+    """
+    n = np.asarray(nibbles, dtype=np.int64) & 15
+    e = (n >> 1) & 3
+    mant = (n & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * mant, (1.0 + mant / 2.0) * np.exp2(e - 1.0))
+    return np.where((n & 8) != 0, -mag, mag)
+
+
+def e4m3fn_value(codes):
+    """e4m3 bytes as the format defines them (the page for pull request 55713
+    converts its block scales through Triton's float8e4nv type): as
+    e4m3_value, except that 0x7F and 0xFF are NaN."""
+    b = np.asarray(codes, dtype=np.int64)
+    return np.where((b & 127) == 127, np.nan, e4m3_value(b))
+
+
+def nvfp4_rows(w4, bscale, gscale, ids, k):
+    """The weights of NVFP4 rows ids, float64 [len(ids)][k].
+
+    `_nvfp4_gathered_bias_kernel` (page for vLLM pull request 55713): byte j
+    of a row holds element 2j in its low nibble and 2j+1 in its high nibble
+    (`tl.interleave(low, high)`); element k is scaled by the e4m3 scale of
+    its 16-element block and by the global scale, in float32, left to right,
+    then rounded to bf16 (`.to(tl.bfloat16)`, nearest even).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    rows = np.asarray(w4)[ids][:, : k // 2].astype(np.int64)
+    codes = np.empty((len(ids), k), dtype=np.int64)
+    codes[:, 0::2] = rows & 15
+    codes[:, 1::2] = rows >> 4
+    d = e2m1_value(codes).astype(np.float32)
+    s = e4m3fn_value(np.asarray(bscale)[ids][:, : k // 16]).astype(np.float32)
+    t = (d * np.repeat(s, 16, axis=1)).astype(np.float32)
+    t = (t * np.float32(gscale)).astype(np.float32)
+    return bf16.to_f64(bf16.from_f32(t))
+
+
+def rerank_exact_nvfp4(x_bits, w4, bscale, gscale, rr_id):
+    """e[m][r] = sum_k x[m][k] * nvfp4_rows(...)[r][k], float64; -inf for id -1.
+
+    The dot of `_nvfp4_gathered_bias_kernel` (page for vLLM pull request
+    55713): float32 products of the bf16 weight and x, summed in float32 on
+    the page (float64 here).
+    """
+    x = _x64(x_bits)
+    rr_id = np.asarray(rr_id)
+    k = x.shape[1]
+    out = np.full(rr_id.shape, -np.inf)
+    for row in range(rr_id.shape[0]):
+        ok = rr_id[row] >= 0
+        out[row, ok] = nvfp4_rows(w4, bscale, gscale, rr_id[row][ok], k) @ x[row]
+    return out
+
+
 def final_argmax(rr_id, e):
     """Argmax over the R exact values of each row, float32 decision, ties -> lower id.
 

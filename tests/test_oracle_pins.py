@@ -447,3 +447,136 @@ def test_int4_lossless_special_case():
     q, S, ZS = oracle.quantize_int4(bits)
     assert np.array_equal(q, codes)
     assert np.array_equal(oracle.effective_weight_int4(oracle.pack_half_split(q), S, ZS), w)
+
+
+# ------------------------------------------------------- NVFP4 rerank source
+def _nvfp4_fixture(golden):
+    fx = golden("nvfp4_rows_example.txt")
+    g = np.float32(float(fx["gscale"][0][0]))
+    rows, scales = [], []
+    for r in fx["row"]:
+        bar = r.index("|")
+        rows.append([_hex(v) for v in r[1:bar]])
+        scales.append([_hex(v) for v in r[bar + 1:]])
+    w4 = np.array(rows, dtype=np.uint8)
+    bs = np.array(scales, dtype=np.uint8)
+    want = np.array([[float(v) for v in r[1:]] for r in fx["weights"]])
+    return fx, w4, bs, g, want
+
+
+def test_e2m1_decode_table(golden):
+    fx = golden("nvfp4_rows_example.txt")
+    mags = [float(v) for v in fx["e2m1"][0]]
+    got = oracle.e2m1_value(np.arange(16))
+    assert list(got[:8]) == mags
+    assert list(-got[8:]) == mags
+    assert all(np.signbit(got[8:]))
+
+
+def test_nvfp4_rows_fixture(golden):
+    """Hand-derived weights: nibble order, block scales, the global scale, the
+    float32 product and the bf16 rounding (two ties to even, four roundings up)."""
+    fx, w4, bs, g, want = _nvfp4_fixture(golden)
+    got = oracle.nvfp4_rows(w4, bs, g, [0, 1], 32)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))   # -0.0 kept
+    x = np.full((1, 32), 0x3F80, dtype=np.uint16)                      # x = 1
+    e = oracle.rerank_exact_nvfp4(x, w4, bs, g, np.array([[0, -1]]))
+    assert e[0, 0] == float(fx["dot_ones"][0][1])
+    assert e[0, 1] == -np.inf
+
+
+def _bf16_rne_fraction(v):
+    """bf16 value nearest to the Fraction v, ties to the even mantissa (brute force)."""
+    if v == 0:
+        return Fraction(0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    lo = Fraction(int(a * 128), 128)                                 # 7 mantissa bits
+    hi = lo + Fraction(1, 128)
+    if a - lo < hi - a or (a - lo == hi - a and int(lo * 128) % 2 == 0):
+        q = lo
+    else:
+        q = hi
+    return sign * q * Fraction(2) ** e
+
+
+def _e4m3fn_fraction(b):
+    e, mant = (b >> 3) & 15, b & 7
+    mag = Fraction(mant, 512) if e == 0 else (1 + Fraction(mant, 8)) * Fraction(2) ** (e - 7)
+    return -mag if b & 128 else mag
+
+
+def test_nvfp4_rows_brute_force():
+    """Exact rationals: d * s is exact, times g rounded once to float32 (the
+    product of a 6-bit and a 24-bit significand is exact in float64), then
+    the bf16 value nearest to it found by search."""
+    rng = np.random.default_rng(21)
+    n, k = 3, 64
+    w4 = rng.integers(0, 256, size=(n, k // 2)).astype(np.uint8)
+    bs = rng.integers(0, 127, size=(n, k // 16)).astype(np.uint8)
+    bs[bs == 0x7F] = 0x38
+    g = np.float32(0.0123)
+    mag = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+           Fraction(6)]
+    got = oracle.nvfp4_rows(w4, bs, g, np.arange(n), k)
+    for r in range(n):
+        for j in range(k):
+            byte = int(w4[r, j // 2])
+            nib = byte & 15 if j % 2 == 0 else byte >> 4
+            d = -mag[nib & 7] if nib & 8 else mag[nib & 7]
+            prod = d * _e4m3fn_fraction(int(bs[r, j // 16])) * Fraction(float(g))
+            f32 = Fraction(float(np.float32(float(prod))))
+            assert got[r, j] == float(_bf16_rne_fraction(f32)), (r, j)
+
+
+def test_nvfp4_rerank_equals_bf16_rerank_on_representable_rows():
+    """With a global scale of 1 and power-of-two block scales every weight is
+    an e2m1 value times a power of two, exact in bf16: the NVFP4 source then
+    gives exactly the bf16 rerank of those rows."""
+    rng = np.random.default_rng(12)
+    n, k, m, r = 30, 256, 2, 5
+    w4 = rng.integers(0, 256, size=(n, k // 2)).astype(np.uint8)
+    bs = ((rng.integers(4, 10, size=(n, k // 16)) << 3)).astype(np.uint8)   # 2^-3 .. 2^2, mantissa 0
+    codes = np.empty((n, k), dtype=np.int64)
+    codes[:, 0::2] = w4 & 15
+    codes[:, 1::2] = w4 >> 4
+    wv = oracle.e2m1_value(codes) * np.repeat(2.0 ** ((bs.astype(np.int64) >> 3) - 7), 16, axis=1)
+    w_bits = workload.f32_to_bf16_bits(wv.astype(np.float32))
+    assert np.array_equal(obf.to_f64(w_bits), wv)
+    x = workload.gen_x(m, k, seed=6)
+    rr_id = np.stack([rng.choice(n, size=r, replace=False) for _ in range(m)])
+    rr_id[0, 3:] = -1
+    a = oracle.rerank_exact_nvfp4(x, w4, bs, np.float32(1.0), rr_id)
+    b = oracle.rerank_exact(x, w_bits, rr_id)
+    assert np.array_equal(a, b)
+
+
+def test_synthetic_nvfp4_head_rounds_to_nearest():
+    """The generator's block scales and nibbles are nearest grid values (inputs only)."""
+    w = workload.gen_weight(32, 512, seed=4)
+    w4, bs, g = workload.nvfp4_head(w)
+    wf = obf.to_f64(w)
+    s = oracle.e4m3fn_value(bs)
+    amax = np.abs(wf.reshape(32, -1, 16)).max(axis=2)
+    table = np.unique(np.abs(oracle.e4m3_value(np.arange(0, 127))))
+    t = amax / (6.0 * float(g))
+    assert np.all(np.abs(s - t) <= np.min(np.abs(t[..., None] - table), axis=-1) + 1e-12)
+    codes = np.empty((32, 512), dtype=np.int64)
+    codes[:, 0::2] = w4 & 15
+    codes[:, 1::2] = w4 >> 4
+    d = oracle.e2m1_value(codes)
+    v = wf / (np.repeat(s, 16, axis=1) * float(g))
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    best = np.min(np.abs(np.abs(v)[..., None] - grid), axis=-1)
+    assert np.all(np.abs(np.abs(d) - np.abs(v)) <= best + 1e-12)
+    assert np.all((d == 0) | (np.sign(d) == np.sign(v)))
