@@ -21,7 +21,7 @@ Prints one JSON line:
                its fractions of the HBM and bf16 MFMA peaks, the warm
                (cache-resident) figure, the time of the row handed to a
                top-k caller (draft_head_logits_row), the per-call time with
-               the e4m3 rerank source, the 4-bit head's per-call time
+               the e4m3 and NVFP4 rerank sources, the 4-bit head's per-call time
                (KCAND = 1, 357,580,800 B of codes and pairs per call),
                and the device's achieved
                read rate (the library's streaming-read reference) and copy rate
@@ -184,6 +184,32 @@ class Rig:
             e.record()
             torch.cuda.synchronize()
             res[str(m)] = round(s.elapsed_time(e) / steps * 1e3, 2)
+        return res
+
+    def nvfp4_call_us(self, ms=(1, 8, 72), steps=200):
+        """Per-call time with the rerank reading an NVFP4 copy of the head (a
+        synthetic two-level-scaled FP4 head; coarse pass unchanged)."""
+        torch, B = self.torch, self.B
+        from bit_quantized_lm_amd import workload
+        w4, bs, g = workload.nvfp4_head(self.w_host)
+        t_w4 = torch.from_numpy(w4).to(self.dev)
+        t_bs = torch.from_numpy(bs).to(self.dev)
+        t_g = torch.tensor([g], dtype=torch.float32, device=self.dev)
+        res = {}
+        for m in ms:
+            heads = [B.DraftHead(h.tiled, h.pairs, t_w4, N, K, KCAND, R, bscale=t_bs, gscale=t_g) for h in self.heads]
+            out = self.buffers(m)
+            for i in range(20):
+                heads[i % len(heads)](self.x[:m], stream=self.stream, out=out, workspace=self.ws[m])
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for i in range(steps):
+                heads[i % len(heads)](self.x[:m], stream=self.stream, out=out, workspace=self.ws[m])
+            e.record()
+            torch.cuda.synchronize()
+            res[str(m)] = round(s.elapsed_time(e) / steps * 1e3, 2)
+        del t_w4, t_bs
         return res
 
     def int4_call_us(self, ms=(1, 8, 72), steps=200, copies=2):
@@ -382,6 +408,8 @@ def main():
                                  "note": "one weight copy reused back to back: Infinity-Cache resident"}
         extra["logits_row_us"] = {str(mm): rig.logits_row_us(mm) for mm in (1, 8, 72)}
         extra["e4m3_rerank_us_per_call"] = rig.e4m3_call_us()
+        extra["nvfp4_rerank_us_per_call"] = rig.nvfp4_call_us()
+        log(f"one call with the NVFP4 rerank source: {extra['nvfp4_rerank_us_per_call']}")
         extra["int4_kcand1_us_per_call"] = rig.int4_call_us()
         log(f"one call of the 4-bit head at KCAND=1: {extra['int4_kcand1_us_per_call']}")
         log(f"one call with the e4m3 rerank source: {extra['e4m3_rerank_us_per_call']}")

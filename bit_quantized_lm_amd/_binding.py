@@ -81,6 +81,11 @@ def load_library() -> ctypes.CDLL:
     lib.draft_head_forward_e4m3.restype = i32
     lib.draft_head_forward_e4m3.argtypes = [P, i32, i32, i32, P, P, P, P, i64, i32, i32, P, P, P, P, P, P, P, P,
                                             sz, P, P, P]
+    lib.draft_head_rerank_nvfp4.restype = i32
+    lib.draft_head_rerank_nvfp4.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, P, P, i32, i32, P, P, P]
+    lib.draft_head_forward_nvfp4.restype = i32
+    lib.draft_head_forward_nvfp4.argtypes = [P, i32, i32, i32, P, P, P, i64, P, i64, P, i32, i32, P, P, P, P, P,
+                                             P, P, P, sz, P, P, P]
     lib.draft_head_logits_row.restype = i32
     lib.draft_head_logits_row.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
     lib.draft_head_stream_read.restype = i32
@@ -287,6 +292,26 @@ def draft_head_rerank_e4m3(x, w8, wscale, cand_val, cand_id, R: int = 32, rr_id=
     return rr_id, rr_val
 
 
+def draft_head_rerank_nvfp4(x, w4, bscale, gscale, cand_val, cand_id, R: int = 32, rr_id=None, rr_val=None,
+                            N=None, stream=None):
+    """draft_head_rerank from NVFP4 rows: w4 CUDA uint8 [N][ldw] (two e2m1
+    codes per byte, low nibble first), bscale CUDA uint8 [N][lds] (e4m3 scale
+    per 16 elements), gscale CUDA fp32 [1].  Returns (rr_id, rr_val)."""
+    import torch
+    lib = load_library()
+    M, K = x.shape
+    n = w4.shape[0] if N is None else N
+    ncand = cand_val.shape[1]
+    if rr_id is None:
+        rr_id = _empty((M, R), torch.int32, x)
+    if rr_val is None:
+        rr_val = _empty((M, R), torch.float32, x)
+    _check(lib.draft_head_rerank_nvfp4(_ptr(x), _ptr(w4), w4.stride(0), _ptr(bscale), bscale.stride(0),
+                                       _ptr(gscale), M, K, n, _ptr(cand_val), _ptr(cand_id), ncand, R, _ptr(rr_id),
+                                       _ptr(rr_val), _stream(stream)))
+    return rr_id, rr_val
+
+
 def draft_head_logits_row(rr_id, rr_val, N: int, coarse=None, topk_only=False, out=None, stream=None):
     """The bf16 row handed to the caller: bf16(coarse) (or -inf with
     topk_only) with the reranked ids' exact values; returns int16 bits [M][N]."""
@@ -350,11 +375,11 @@ def _event(ev):
 
 def draft_head_forward(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, out=None,
                        coarse_out=None, workspace=None, stream=None, coarse_events=None, wscale=None,
-                       bits: int = 2):
+                       bits: int = 2, bscale=None, gscale=None):
     """One full call (coarse -> rerank -> argmax) in one library call.
 
-    w: the bf16 rows, or with wscale (fp32 [N]) the e4m3 rows (uint8) of the
-    rerank; out: dict from forward_buffers (allocated when None); workspace:
+    w: the bf16 rows, or with wscale (fp32 [N]) the e4m3 rows (uint8), or
+    with bscale and gscale the NVFP4 rows (uint8) of the rerank; out: dict from forward_buffers (allocated when None); workspace:
     as for draft_head_coarse; coarse_events: optional (start, stop)
     torch.cuda.Event pair that takes the coarse kernel's own dispatch
     timestamps.  Returns the dict of output tensors."""
@@ -368,10 +393,13 @@ def draft_head_forward(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, 
     outs = (_ptr(out["cand_val"]), _ptr(out["cand_id"]), _ptr(out["rr_id"]), _ptr(out["rr_val"]),
             _ptr(out["out_id"]), _ptr(out["out_val"]), _ptr(coarse_out), *_ws(workspace), _stream(stream), e0, e1)
     if bits == 4:
-        if wscale is not None:
+        if wscale is not None or bscale is not None:
             raise ValueError("the 4-bit head reranks against bf16 rows")
         _check(lib.draft_head_forward_int4(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0),
                                            kcand, R, *outs))
+    elif bscale is not None:
+        _check(lib.draft_head_forward_nvfp4(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0),
+                                            _ptr(bscale), bscale.stride(0), _ptr(gscale), kcand, R, *outs))
     elif wscale is None:
         _check(lib.draft_head_forward(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0), kcand,
                                       R, *outs))
@@ -390,11 +418,14 @@ class DraftHead:
     staged(x) does the same with one library call per step.
     """
 
-    def __init__(self, tiled, pairs, w, N: int, K: int, kcand: int = 8, R: int = 32, wscale=None, bits: int = 2):
+    def __init__(self, tiled, pairs, w, N: int, K: int, kcand: int = 8, R: int = 32, wscale=None, bits: int = 2,
+                 bscale=None, gscale=None):
         """w: the bf16 rows the rerank reads, or e4m3 rows (uint8) with their
-        per-row fp32 scale `wscale` (a per-channel FP8 head).  bits = 4: tiled
-        and pairs hold a 4-bit head in its 2K-long 2-bit form."""
+        per-row fp32 scale `wscale` (a per-channel FP8 head), or NVFP4 rows
+        (uint8) with their block scales `bscale` and global scale `gscale`.
+        bits = 4: tiled and pairs hold a 4-bit head in its 2K-long 2-bit form."""
         self.tiled, self.pairs, self.w, self.wscale = tiled, pairs, w, wscale
+        self.bscale, self.gscale = bscale, gscale
         self.N, self.K, self.kcand, self.R, self.bits = N, K, kcand, R, bits
 
     @classmethod
@@ -419,7 +450,8 @@ class DraftHead:
     def __call__(self, x, coarse_out=None, stream=None, out=None, coarse_events=None, workspace=None):
         return draft_head_forward(x, self.tiled, self.pairs, self.w, self.N, self.kcand, self.R, out=out,
                                   coarse_out=coarse_out, workspace=workspace, stream=stream,
-                                  coarse_events=coarse_events, wscale=self.wscale, bits=self.bits)
+                                  coarse_events=coarse_events, wscale=self.wscale, bits=self.bits,
+                                  bscale=self.bscale, gscale=self.gscale)
 
     def logits_row(self, x, topk_only=False, stream=None):
         """One call plus the bf16 row the page hands to its caller (full, or
@@ -435,7 +467,10 @@ class DraftHead:
         """The same call as three library calls (coarse, rerank, argmax)."""
         cv, ci = draft_head_coarse(x, self.tiled, self.pairs, self.N, self.kcand,
                                    coarse_out=coarse_out, stream=stream, bits=self.bits)
-        if self.wscale is None:
+        if self.bscale is not None:
+            rr_id, rr_val = draft_head_rerank_nvfp4(x, self.w, self.bscale, self.gscale, cv, ci, self.R, N=self.N,
+                                                    stream=stream)
+        elif self.wscale is None:
             rr_id, rr_val = draft_head_rerank(x, self.w, cv, ci, self.R, N=self.N, stream=stream)
         else:
             rr_id, rr_val = draft_head_rerank_e4m3(x, self.w, self.wscale, cv, ci, self.R, N=self.N, stream=stream)

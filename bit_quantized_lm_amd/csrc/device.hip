@@ -80,11 +80,23 @@ __device__ __forceinline__ uint32_t scale_x_pair(uint32_t w) {
 
 // Arguments of the rerank (row top-R of the candidates, exact logits, and
 // with the argmax the per-row arrival counters).
+// The rows the exact rerank reads: bf16 rows; e4m3 rows with a per-row fp32
+// scale; or NVFP4 rows (e2m1 nibbles, an e4m3 scale per 16 elements, one
+// global fp32 scale).
+enum RowKind { kRowsBf16 = 0, kRowsE4m3 = 1, kRowsNvfp4 = 2 };
+struct RowSrc {
+  const void* w;          // bf16 rows (ldw elements), e4m3 rows (ldw bytes) or NVFP4 rows (ldw bytes)
+  int64_t ldw;
+  const float* wscale;    // e4m3: per-row scale
+  const uint8_t* bscale;  // NVFP4: e4m3 scale per 16 elements, rows of lds bytes
+  int64_t lds;
+  const float* gscale;    // NVFP4: the global scale (one float)
+  int kind;
+};
+
 struct RerankArgs {
   const uint16_t* x;
-  const void* w;          // bf16 rows (ldw elements), or e4m3 rows (ldw bytes) when wscale is set
-  const float* wscale;    // per-row scale of e4m3 rows, else null
-  int64_t ldw;
+  RowSrc src;
   int K, N;
   const float* cand_val;
   const int32_t* cand_id;
@@ -991,6 +1003,7 @@ void coarse_mfma_kernel(BigArgs BA) {
 //   the sign) and multiplied by the row's scale, one fp32 rounding.
 constexpr int kDotBf16 = 10;   // 16-byte W loads per lane in flight (5120 k)
 constexpr int kDotE4m3 = 5;    // 16-byte W loads per lane in flight (5120 k)
+constexpr int kDotNvfp4 = 3;   // 16-byte W loads per lane in flight (6144 k)
 
 __device__ __forceinline__ float e4m3_page(uint32_t b) {
   const uint32_t e = (b >> 3) & 15u, mant = b & 7u;
@@ -1000,12 +1013,32 @@ __device__ __forceinline__ float e4m3_page(uint32_t b) {
   return (b & 128u) ? -mag : mag;
 }
 
-template <bool kE4M3>
-__device__ float wave_dot(const void* w, int64_t ldw, uint32_t id, float scale, const uint16_t* xr, int K,
-                          int lane) {
+// e2m1 (FP4) nibble: sign bit 3, exponent bits 2-1 (bias 1), mantissa bit 0;
+// exponent 0 is the subnormal 0.5 * mantissa.  Built as fp32 bits.
+__device__ __forceinline__ float e2m1_value(uint32_t n) {
+  const uint32_t e = (n >> 1) & 3u, mant = n & 1u;
+  const uint32_t mag = e ? (((e + 126u) << 23) | (mant << 22)) : (mant ? 0x3F000000u : 0u);
+  return __uint_as_float(mag | ((n & 8u) << 28));
+}
+
+// NVFP4 block scale: an e4m3 byte as the format defines it (0x7F, 0xFF NaN).
+__device__ __forceinline__ float e4m3_scale(uint32_t b) {
+  return (b & 127u) == 127u ? __builtin_nanf("") : e4m3_page(b);
+}
+
+// fp32 -> bf16 -> fp32, round to nearest even (NaN kept).
+__device__ __forceinline__ float round_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+  return f != f ? f : __uint_as_float(r);
+}
+
+// The exact logit of row id, summed by one wave (fp32 accumulation).
+template <int kKind>
+__device__ float wave_dot(const RowSrc& S, uint32_t id, const uint16_t* xr, int K, int lane) {
   float s0 = 0.f, s1 = 0.f;
-  if constexpr (!kE4M3) {
-    const uint16_t* wr = static_cast<const uint16_t*>(w) + (size_t)id * ldw;
+  if constexpr (kKind == kRowsBf16) {
+    const uint16_t* wr = static_cast<const uint16_t*>(S.w) + (size_t)id * S.ldw;
     for (int k0 = 0; k0 < K; k0 += 512 * kDotBf16) {
       u32x4 wv[kDotBf16], xv[kDotBf16];
 #pragma unroll
@@ -1025,8 +1058,9 @@ __device__ float wave_dot(const void* w, int64_t ldw, uint32_t id, float scale, 
         }
       }
     }
-  } else {
-    const uint8_t* wr = static_cast<const uint8_t*>(w) + (size_t)id * ldw;
+  } else if constexpr (kKind == kRowsE4m3) {
+    const uint8_t* wr = static_cast<const uint8_t*>(S.w) + (size_t)id * S.ldw;
+    const float scale = S.wscale[id];
     for (int k0 = 0; k0 < K; k0 += 1024 * kDotE4m3) {
       u32x4 wv[kDotE4m3], xa[kDotE4m3], xb[kDotE4m3];
 #pragma unroll
@@ -1048,6 +1082,44 @@ __device__ float wave_dot(const void* w, int64_t ldw, uint32_t id, float scale, 
             s1 = __builtin_fmaf(hi_bf16(x01), e4m3_page((b4 >> 8) & 255u) * scale, s1);
             s0 = __builtin_fmaf(lo_bf16(x23), e4m3_page((b4 >> 16) & 255u) * scale, s0);
             s1 = __builtin_fmaf(hi_bf16(x23), e4m3_page(b4 >> 24) * scale, s1);
+          }
+        }
+      }
+    }
+  } else {
+    // lane l takes 32 consecutive elements (16 bytes, two scale blocks) per 2048
+    const uint8_t* wr = static_cast<const uint8_t*>(S.w) + (size_t)id * S.ldw;
+    const uint8_t* br = S.bscale + (size_t)id * S.lds;
+    const float g = *S.gscale;
+    for (int k0 = 0; k0 < K; k0 += 2048 * kDotNvfp4) {
+      u32x4 wv[kDotNvfp4], xv[kDotNvfp4][4];
+      uint32_t bv[kDotNvfp4];
+#pragma unroll
+      for (int j = 0; j < kDotNvfp4; ++j) {   // clamped, unconditional loads
+        const int k = min(k0 + 2048 * j + lane * 32, K - 32);
+        wv[j] = *reinterpret_cast<const u32x4*>(wr + k / 2);
+        bv[j] = *reinterpret_cast<const uint16_t*>(br + k / 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[j][q] = *reinterpret_cast<const u32x4*>(xr + k + 8 * q);
+      }
+#pragma unroll
+      for (int j = 0; j < kDotNvfp4; ++j) {
+        if (k0 + 2048 * j + lane * 32 < K) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {   // scale block h: bytes 8h .. 8h+7, elements 16h .. 16h+15
+            const float bs = e4m3_scale((bv[j] >> (8 * h)) & 255u);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const uint32_t b4 = wv[j][2 * h + c];   // elements 16h + 8c .. +7, low nibble first
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t xw = xv[j][2 * h + c][e];   // x of elements 2e, 2e+1 of this word
+                const float w0 = round_bf16(e2m1_value((b4 >> (8 * e)) & 15u) * bs * g);
+                const float w1 = round_bf16(e2m1_value((b4 >> (8 * e + 4)) & 15u) * bs * g);
+                s0 = __builtin_fmaf(lo_bf16(xw), w0, s0);
+                s1 = __builtin_fmaf(hi_bf16(xw), w1, s1);
+              }
+            }
           }
         }
       }
@@ -1253,10 +1325,9 @@ __device__ unsigned long long block_kth_largest(ForEach for_each_key, int k, uns
   return pre << shift;
 }
 
-template <bool kE4M3>
+template <int kKind>
 __global__ __launch_bounds__(kSelThreads) void rerank_kernel(
-    const uint16_t* __restrict__ x, const void* __restrict__ w, const float* __restrict__ wscale, int64_t ldw,
-    int K, int N, const float* __restrict__ cand_val, const int32_t* __restrict__ cand_id, int ncand, int R,
+    const uint16_t* __restrict__ x, RowSrc src, int K, int N, const float* __restrict__ cand_val, const int32_t* __restrict__ cand_id, int ncand, int R,
     int32_t* __restrict__ rr_id, float* __restrict__ rr_val) {
   __shared__ SelectShared sh;
   const int m = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1398,7 +1469,7 @@ __global__ __launch_bounds__(kSelThreads) void rerank_kernel(
     float sum = 0.f;
     if (valid) {
       const uint32_t id = key_id(sh.keys[r]);
-      sum = wave_dot<kE4M3>(w, ldw, id, kE4M3 ? wscale[id] : 1.f, xr, K, lane);
+      sum = wave_dot<kKind>(src, id, xr, K, lane);
     }
     if (lane == 0) rr_val[(size_t)m * R + r] = valid ? sum : -__builtin_inff();
   }
@@ -1590,7 +1661,7 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
   __syncthreads();
 }
 
-template <int NTHR, bool kArgmax, bool kE4M3>
+template <int NTHR, bool kArgmax, int kKind>
 __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part, int nparts) {
   constexpr int NW = NTHR / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1601,7 +1672,7 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
   const int r = NW * part + wave;
   if (r < R) {
     const uint32_t id = key_id(sh.list[r]);
-    const float sum = wave_dot<kE4M3>(A.w, A.ldw, id, kE4M3 ? A.wscale[id] : 1.f, A.x + (size_t)m * K, K, lane);
+    const float sum = wave_dot<kKind>(A.src, id, A.x + (size_t)m * K, K, lane);
     if (lane == 0) {
       store_dev(A.rr_id + (size_t)m * R + r, (int32_t)id);
       store_dev(A.rr_val + (size_t)m * R + r, sum);
@@ -1646,10 +1717,10 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
 }
 
 // Rerank kernel: grid (ceil(R / 4), M), one part of one row per workgroup.
-template <bool kArgmax, bool kE4M3>
+template <bool kArgmax, int kKind>
 __global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(RerankArgs A) {
   __shared__ WideShared sh;
-  rerank_part<kWideThreads, kArgmax, kE4M3>(sh, A, blockIdx.y, blockIdx.x, gridDim.x);
+  rerank_part<kWideThreads, kArgmax, kKind>(sh, A, blockIdx.y, blockIdx.x, gridDim.x);
 }
 
 
@@ -1801,25 +1872,34 @@ int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, co
   return DH_OK;
 }
 
-// e4m3: wscale non-null (rows of ldw bytes, ldw % 16 == 0); bf16: wscale null
-// (rows of ldw elements, ldw % 8 == 0).  Either way a row starts 16-byte aligned.
-int validate_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N, const float* cand_val,
-                    const int32_t* cand_id, int ncand, int R, const int32_t* rr_id, const float* rr_val,
-                    bool e4m3 = false, const float* wscale = nullptr) {
-  if (!x || !w || !cand_val || !cand_id || !rr_id || !rr_val || (e4m3 && !wscale))
+// Rows: bf16 (ldw elements, ldw % 8 == 0), e4m3 (ldw bytes, ldw % 16 == 0,
+// per-row scales) or NVFP4 (ldw bytes >= K/2, ldw % 16 == 0; block scales in
+// rows of lds bytes >= K/16, lds even; the global scale).  A row starts
+// 16-byte aligned in each case.
+int validate_rerank(const void* x, const RowSrc& src, int M, int K, int N, const float* cand_val,
+                    const int32_t* cand_id, int ncand, int R, const int32_t* rr_id, const float* rr_val) {
+  const bool nv = src.kind == kRowsNvfp4;
+  if (!x || !src.w || !cand_val || !cand_id || !rr_id || !rr_val || (src.kind == kRowsE4m3 && !src.wscale) ||
+      (nv && (!src.bscale || !src.gscale)))
     return dh::fail(DH_EINVAL, "rerank: null pointer");
   int rc = check_m(M);
   if (rc) return rc;
   if ((rc = check_k_rerank(K))) return rc;
   if (N < 1) return dh::fail(DH_ESHAPE, "rerank: N must be >= 1 (got %d)", N);
-  const int align = e4m3 ? 16 : 8;
-  if (ldw < K || ldw % align != 0)
-    return dh::fail(DH_EINVAL, "rerank: ldw must be >= K and a multiple of %d (got %lld)", align, (long long)ldw);
+  const int align = src.kind == kRowsBf16 ? 8 : 16;
+  const int64_t row = nv ? K / 2 : K;
+  if (src.ldw < row || src.ldw % align != 0)
+    return dh::fail(DH_EINVAL, "rerank: ldw must be >= %lld and a multiple of %d (got %lld)", (long long)row, align,
+                    (long long)src.ldw);
+  if (nv && (src.lds < K / 16 || src.lds % 2 != 0))
+    return dh::fail(DH_EINVAL, "rerank: lds must be >= K/16 and even (got %lld)", (long long)src.lds);
   if (ncand < 1) return dh::fail(DH_EINVAL, "rerank: ncand must be >= 1 (got %d)", ncand);
   if (R < 1 || R > ncand || R > DH_MAX_R)
     return dh::fail(DH_EUNSUP, "rerank: R must be in 1..min(ncand=%d, %d) (got %d)", ncand, DH_MAX_R, R);
-  if (!aligned16(x) || !aligned16(w))
+  if (!aligned16(x) || !aligned16(src.w))
     return dh::fail(DH_EINVAL, "rerank: x and w must be 16-byte aligned");
+  if (nv && (reinterpret_cast<uintptr_t>(src.bscale) & 1u))
+    return dh::fail(DH_EINVAL, "rerank: the block scales must be 2-byte aligned");
   return DH_OK;
 }
 
@@ -1898,35 +1978,40 @@ bool fast_rerank(int N, int ncand, int R, int& nblk, int& kcand) {
 }
 
 template <bool kArgmax>
-hipError_t launch_wide(const void* x, const void* w, const float* wscale, int64_t ldw, int M, int K, int N,
-                       const float* cand_val, const int32_t* cand_id, int nblk, int kcand, int R, int32_t* rr_id,
-                       float* rr_val, int32_t* out_id, float* out_val, uint32_t* cnt, hipStream_t s) {
-  const RerankArgs A{static_cast<const uint16_t*>(x), w, wscale, ldw, K, N, cand_val,
+hipError_t launch_wide(const void* x, const RowSrc& src, int M, int K, int N, const float* cand_val,
+                       const int32_t* cand_id, int nblk, int kcand, int R, int32_t* rr_id, float* rr_val,
+                       int32_t* out_id, float* out_val, uint32_t* cnt, hipStream_t s) {
+  const RerankArgs A{static_cast<const uint16_t*>(x), src, K, N, cand_val,
                      cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, cnt};
   const dim3 grid((R + 3) / 4, M);
-  if (wscale) hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, true>), grid, dim3(kWideThreads), 0, s, A);
-  else hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, false>), grid, dim3(kWideThreads), 0, s, A);
+  if (src.kind == kRowsE4m3)
+    hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsE4m3>), grid, dim3(kWideThreads), 0, s, A);
+  else if (src.kind == kRowsNvfp4)
+    hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsNvfp4>), grid, dim3(kWideThreads), 0, s, A);
+  else
+    hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsBf16>), grid, dim3(kWideThreads), 0, s, A);
   return hipGetLastError();
 }
 
-// wscale null: bf16 rows; else e4m3 rows with their scales.
-int launch_rerank(const void* x, const void* w, const float* wscale, int64_t ldw, int M, int K, int N,
-                  const float* cand_val, const int32_t* cand_id, int ncand, int R, int32_t* rr_id, float* rr_val,
-                  hipStream_t s) {
+int launch_rerank(const void* x, const RowSrc& src, int M, int K, int N, const float* cand_val,
+                  const int32_t* cand_id, int ncand, int R, int32_t* rr_id, float* rr_val, hipStream_t s) {
   int nblk, kcand;
   if (fast_rerank(N, ncand, R, nblk, kcand)) {
-    hipError_t e = launch_wide<false>(x, w, wscale, ldw, M, K, N, cand_val, cand_id, nblk, kcand, R, rr_id,
-                                      rr_val, nullptr, nullptr, nullptr, s);
+    hipError_t e = launch_wide<false>(x, src, M, K, N, cand_val, cand_id, nblk, kcand, R, rr_id, rr_val, nullptr,
+                                      nullptr, nullptr, s);
     if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_wide_kernel: %s", hipGetErrorString(e));
     return dh::ok();
   }
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  if (wscale)
-    hipLaunchKernelGGL(rerank_kernel<true>, dim3(M), dim3(kSelThreads), 0, s, xb, w, wscale, ldw, K, N, cand_val,
+  if (src.kind == kRowsE4m3)
+    hipLaunchKernelGGL(rerank_kernel<kRowsE4m3>, dim3(M), dim3(kSelThreads), 0, s, xb, src, K, N, cand_val, cand_id,
+                       ncand, R, rr_id, rr_val);
+  else if (src.kind == kRowsNvfp4)
+    hipLaunchKernelGGL(rerank_kernel<kRowsNvfp4>, dim3(M), dim3(kSelThreads), 0, s, xb, src, K, N, cand_val,
                        cand_id, ncand, R, rr_id, rr_val);
   else
-    hipLaunchKernelGGL(rerank_kernel<false>, dim3(M), dim3(kSelThreads), 0, s, xb, w, wscale, ldw, K, N, cand_val,
-                       cand_id, ncand, R, rr_id, rr_val);
+    hipLaunchKernelGGL(rerank_kernel<kRowsBf16>, dim3(M), dim3(kSelThreads), 0, s, xb, src, K, N, cand_val, cand_id,
+                       ncand, R, rr_id, rr_val);
   return launch_error("rerank_kernel");
 }
 
@@ -2036,19 +2121,28 @@ int draft_head_coarse_int4(const void* x, int M, int K, int N, const uint8_t* ti
 int draft_head_rerank(const void* x, const void* w, int64_t ldw, int M, int K, int N,
                       const float* cand_val, const int32_t* cand_id, int ncand, int R,
                       int32_t* rr_id, float* rr_val, void* stream) {
-  int rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
+  const RowSrc src{w, ldw, nullptr, nullptr, 0, nullptr, kRowsBf16};
+  int rc = validate_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
   if (rc) return rc;
-  return launch_rerank(x, w, nullptr, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val,
-                       as_stream(stream));
+  return launch_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, as_stream(stream));
 }
 
 int draft_head_rerank_e4m3(const void* x, const uint8_t* w8, const float* wscale, int64_t ldw, int M, int K,
                            int N, const float* cand_val, const int32_t* cand_id, int ncand, int R,
                            int32_t* rr_id, float* rr_val, void* stream) {
-  int rc = validate_rerank(x, w8, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, true, wscale);
+  const RowSrc src{w8, ldw, wscale, nullptr, 0, nullptr, kRowsE4m3};
+  int rc = validate_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
   if (rc) return rc;
-  return launch_rerank(x, w8, wscale, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val,
-                       as_stream(stream));
+  return launch_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, as_stream(stream));
+}
+
+int draft_head_rerank_nvfp4(const void* x, const uint8_t* w4, int64_t ldw, const uint8_t* bscale, int64_t lds,
+                            const float* gscale, int M, int K, int N, const float* cand_val, const int32_t* cand_id,
+                            int ncand, int R, int32_t* rr_id, float* rr_val, void* stream) {
+  const RowSrc src{w4, ldw, nullptr, bscale, lds, gscale, kRowsNvfp4};
+  int rc = validate_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val);
+  if (rc) return rc;
+  return launch_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, as_stream(stream));
 }
 
 int draft_head_logits_row(const float* coarse, const int32_t* rr_id, const float* rr_val, int M, int N, int R,
@@ -2084,12 +2178,11 @@ int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, i
 
 namespace {
 
-// One call: coarse launch(es), then rerank + argmax.  wscale null: bf16 rows;
-// else e4m3 rows (w8) with their scales.
+// One call: coarse launch(es), then rerank + argmax on the rows src describes.
 // int4: the coarse head is a 4-bit one in its 2K-long 2-bit form (x is read
 // twice over); the rerank reads rows of length K as always.
-int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, const void* w,
-                 const float* wscale, bool e4m3, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
+int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, const RowSrc& src,
+                 int kcand, int R, float* cand_val, int32_t* cand_id,
                  int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
                  void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
                  void* coarse_stop_event, bool int4 = false) {
@@ -2099,8 +2192,7 @@ int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const
   const int Kc = int4 ? 2 * K : K;
   if ((rc = validate_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes)))
     return rc;
-  if ((rc = validate_rerank(x, w, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, e4m3, wscale)))
-    return rc;
+  if ((rc = validate_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val))) return rc;
   if ((rc = validate_argmax(rr_id, rr_val, M, R, out_id, out_val))) return rc;
   hipStream_t s = as_stream(stream);
   if ((rc = launch_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace, s,
@@ -2109,12 +2201,12 @@ int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const
     return rc;
   int nblk, kc;
   if (fast_rerank(N, ncand, R, nblk, kc)) {   // rerank and argmax in one kernel
-    hipError_t e = launch_wide<true>(x, w, wscale, ldw, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val,
-                                     out_id, out_val, static_cast<uint32_t*>(workspace), s);
+    hipError_t e = launch_wide<true>(x, src, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val, out_id, out_val,
+                                     static_cast<uint32_t*>(workspace), s);
     if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_wide_kernel: %s", hipGetErrorString(e));
     return dh::ok();
   }
-  if ((rc = launch_rerank(x, w, wscale, ldw, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, s))) return rc;
+  if ((rc = launch_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, s))) return rc;
   return launch_argmax(rr_id, rr_val, M, R, out_id, out_val, s);
 }
 
@@ -2127,9 +2219,9 @@ int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
                        int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
                        void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
                        void* coarse_stop_event) {
-  return forward_impl(x, M, K, N, tiled, pairs, w, nullptr, false, ldw, kcand, R, cand_val, cand_id, rr_id, rr_val,
-                      out_id, out_val, coarse_out, workspace, workspace_bytes, stream, coarse_start_event,
-                      coarse_stop_event);
+  return forward_impl(x, M, K, N, tiled, pairs, RowSrc{w, ldw, nullptr, nullptr, 0, nullptr, kRowsBf16}, kcand, R,
+                      cand_val, cand_id, rr_id, rr_val, out_id, out_val, coarse_out, workspace, workspace_bytes,
+                      stream, coarse_start_event, coarse_stop_event);
 }
 
 int draft_head_forward_int4(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
@@ -2137,9 +2229,9 @@ int draft_head_forward_int4(const void* x, int M, int K, int N, const uint8_t* t
                             int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
                             void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
                             void* coarse_stop_event) {
-  return forward_impl(x, M, K, N, tiled, pairs, w, nullptr, false, ldw, kcand, R, cand_val, cand_id, rr_id, rr_val,
-                      out_id, out_val, coarse_out, workspace, workspace_bytes, stream, coarse_start_event,
-                      coarse_stop_event, true);
+  return forward_impl(x, M, K, N, tiled, pairs, RowSrc{w, ldw, nullptr, nullptr, 0, nullptr, kRowsBf16}, kcand, R,
+                      cand_val, cand_id, rr_id, rr_val, out_id, out_val, coarse_out, workspace, workspace_bytes,
+                      stream, coarse_start_event, coarse_stop_event, true);
 }
 
 int draft_head_forward_e4m3(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
@@ -2147,9 +2239,20 @@ int draft_head_forward_e4m3(const void* x, int M, int K, int N, const uint8_t* t
                             int32_t* cand_id, int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val,
                             float* coarse_out, void* workspace, size_t workspace_bytes, void* stream,
                             void* coarse_start_event, void* coarse_stop_event) {
-  return forward_impl(x, M, K, N, tiled, pairs, w8, wscale, true, ldw, kcand, R, cand_val, cand_id, rr_id, rr_val,
-                      out_id, out_val, coarse_out, workspace, workspace_bytes, stream, coarse_start_event,
-                      coarse_stop_event);
+  return forward_impl(x, M, K, N, tiled, pairs, RowSrc{w8, ldw, wscale, nullptr, 0, nullptr, kRowsE4m3}, kcand, R,
+                      cand_val, cand_id, rr_id, rr_val, out_id, out_val, coarse_out, workspace, workspace_bytes,
+                      stream, coarse_start_event, coarse_stop_event);
+}
+
+int draft_head_forward_nvfp4(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                             const uint8_t* w4, int64_t ldw, const uint8_t* bscale, int64_t lds, const float* gscale,
+                             int kcand, int R, float* cand_val, int32_t* cand_id, int32_t* rr_id, float* rr_val,
+                             int32_t* out_id, float* out_val, float* coarse_out, void* workspace,
+                             size_t workspace_bytes, void* stream, void* coarse_start_event,
+                             void* coarse_stop_event) {
+  return forward_impl(x, M, K, N, tiled, pairs, RowSrc{w4, ldw, nullptr, bscale, lds, gscale, kRowsNvfp4}, kcand, R,
+                      cand_val, cand_id, rr_id, rr_val, out_id, out_val, coarse_out, workspace, workspace_bytes,
+                      stream, coarse_start_event, coarse_stop_event);
 }
 
 }  // extern "C"

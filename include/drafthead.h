@@ -209,6 +209,25 @@ int draft_head_rerank_e4m3(const void* x, const uint8_t* w8, const float* wscale
                            int32_t* rr_id, float* rr_val, void* stream);
 
 /*
+ * DEVICE.  draft_head_rerank with the head's rows in NVFP4 (the gathered
+ * projection `_nvfp4_gathered_bias_kernel` on the page for vLLM pull request
+ * 55713): per row, K/2 bytes of e2m1 codes, byte j holding element 2j in its
+ * low nibble and element 2j+1 in its high nibble; an e4m3 scale byte per 16
+ * elements (the format's own decode: 0x7F / 0xFF are NaN); one global fp32
+ * scale.  An e2m1 nibble has sign bit 3, exponent bits 2-1 with bias 1 and
+ * mantissa bit 0 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).  The weight is
+ * bf16(fp32(fp32(value * block scale) * global scale)), rounded to nearest
+ * even, and e = sum_k x * weight in fp32.
+ *   w4       device, uint8 [N][ldw], 16-byte aligned, ldw >= K/2, ldw % 16 == 0
+ *   bscale   device, e4m3 bytes [N][lds], 2-byte aligned, lds >= K/16, lds even
+ *   gscale   device, one fp32
+ * Everything else as draft_head_rerank.  Errors: as draft_head_rerank.
+ */
+int draft_head_rerank_nvfp4(const void* x, const uint8_t* w4, int64_t ldw, const uint8_t* bscale, int64_t lds,
+                            const float* gscale, int M, int K, int N, const float* cand_val, const int32_t* cand_id,
+                            int ncand, int R, int32_t* rr_id, float* rr_val, void* stream);
+
+/*
  * DEVICE.  Final token per row: the rr_id whose exact value is largest, ties
  * to the lower id, entries with id -1 ignored (the page leaves the argmax of
  * the written-back row to the caller's sampler).
@@ -253,6 +272,18 @@ int draft_head_forward_e4m3(const void* x, int M, int K, int N, const uint8_t* t
                             float* cand_val, int32_t* cand_id, int32_t* rr_id, float* rr_val, int32_t* out_id,
                             float* out_val, float* coarse_out, void* workspace, size_t workspace_bytes,
                             void* stream, void* coarse_start_event, void* coarse_stop_event);
+
+/*
+ * DEVICE.  draft_head_forward with the NVFP4 rerank source of
+ * draft_head_rerank_nvfp4 (w4, ldw and lds in bytes, bscale, gscale) in place
+ * of the bf16 rows.
+ */
+int draft_head_forward_nvfp4(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                             const uint8_t* w4, int64_t ldw, const uint8_t* bscale, int64_t lds, const float* gscale,
+                             int kcand, int R, float* cand_val, int32_t* cand_id, int32_t* rr_id, float* rr_val,
+                             int32_t* out_id, float* out_val, float* coarse_out, void* workspace,
+                             size_t workspace_bytes, void* stream, void* coarse_start_event,
+                             void* coarse_stop_event);
 
 /*
  * DEVICE.  draft_head_coarse and draft_head_forward for a 4-bit head (the

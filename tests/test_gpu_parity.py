@@ -409,6 +409,112 @@ def test_e4m3_rerank_full_shape(dev, full):
     _log(f"e4m3 full shape m=72: argmax agreement with the exact bf16 head {agree}/72 (reported)")
 
 
+# ------------------------------------------------------ NVFP4 rerank source
+def _nvfp4_ref(x, w, packed, w4, bs, g, kcand, r):
+    """The oracle's pipeline with the rerank read from the NVFP4 rows."""
+    ref = oracle.pipeline(x, w, *packed, kcand=kcand, r=r)
+    e = oracle.rerank_exact_nvfp4(x, w4, bs, g, ref["rr_id"])
+    ref["rr_val"] = e
+    ref["out_id"], ref["out_val"] = oracle.final_argmax(ref["rr_id"], e)
+    ref["tie_rows"] = oracle.tie_rows(e)
+    return ref
+
+
+def _nvfp4_dev(w4, bs, g, dev):
+    return (torch.from_numpy(w4).to(dev), torch.from_numpy(bs).to(dev),
+            torch.tensor([g], dtype=torch.float32, device=dev))
+
+
+def _nvfp4_head(w, kcand, r, dev, packed=None):
+    w4, bs, g = workload.nvfp4_head(w)
+    head = B.DraftHead.from_weight(w, kcand=kcand, R=r, device=dev, packed=packed)
+    head.w, head.bscale, head.gscale = _nvfp4_dev(w4, bs, g, dev)
+    return head, w4, bs, g
+
+
+@pytest.mark.parametrize("m,k,n,kcand,r", [(3, 1024, 5000, 8, 32), (1, 512, 200, 64, 100), (17, 1536, 777, 4, 20),
+                                           (8, 5120, 20000, 8, 32), (20, 512, 70000, 8, 100)])
+def test_nvfp4_rerank_parity(dev, m, k, n, kcand, r):
+    w = workload.gen_weight(n, k, seed=4000 + n)
+    x = workload.gen_x(m, k, seed=4001 + n)
+    _log(f"nvfp4 case m={m} k={k} n={n} kcand={kcand} r={r}")
+    packed = oracle.quantize_pack(w)
+    head, w4, bs, g = _nvfp4_head(w, kcand, r, dev, packed=packed)
+    got = run_gpu(head, x, dev)
+    stats = compare(_nvfp4_ref(x, w, packed, w4, bs, g, kcand, r), got, n, kcand)
+    _log(f"  ok {stats}")
+
+
+def test_nvfp4_forward_matches_staged_calls(dev):
+    n, k, m = 20000, 1024, 5
+    w = workload.gen_weight(n, k, seed=103)
+    head, _, _, _ = _nvfp4_head(w, 8, 32, dev)
+    x = _to_dev(workload.gen_x(m, k, seed=104), dev)
+    a = head.staged(x)
+    b = head(x)
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("k,n,r", [(256, 3000, 32), (768, 3000, 32), (2304, 200, 16)])
+def test_nvfp4_rerank_alone(dev, k, n, r):
+    """The NVFP4 rerank by itself at row lengths the 2-bit coarse pass does not
+    take (K % 512 != 0, last 2048-element pass partly empty), on candidate
+    lists with the coarse kernel's block structure drawn at random; n = 200
+    (fewer blocks than R) takes the general rerank kernel."""
+    m, kcand = 4, 8
+    rng = np.random.default_rng(k + n)
+    w = workload.gen_weight(n, k, seed=4100 + k)
+    x = workload.gen_x(m, k, seed=4101 + k)
+    w4, bs, g = workload.nvfp4_head(w)
+    nblk = (n + 63) // 64
+    cv = np.full((m, nblk * kcand), -np.inf, dtype=np.float32)
+    ci = np.full((m, nblk * kcand), -1, dtype=np.int32)
+    for row in range(m):
+        for b in range(nblk):
+            cols = np.arange(64 * b, min(64 * b + 64, n))
+            pick = rng.choice(cols, size=min(kcand, len(cols)), replace=False)
+            vals = np.sort(rng.standard_normal(len(pick)).astype(np.float32))[::-1]
+            order = np.lexsort((pick, -vals.astype(np.float64)))
+            cv[row, b * kcand:b * kcand + len(pick)] = vals[order]
+            ci[row, b * kcand:b * kcand + len(pick)] = pick[order]
+    _log(f"nvfp4 rerank alone k={k} n={n} r={r}")
+    rr_id, _ = oracle.row_topr(cv, ci, r)
+    e = oracle.rerank_exact_nvfp4(x, w4, bs, g, rr_id)
+    t_w4, t_bs, t_g = _nvfp4_dev(w4, bs, g, dev)
+    got_id, got_val = B.draft_head_rerank_nvfp4(_to_dev(x, dev), t_w4, t_bs, t_g, torch.from_numpy(cv).to(dev),
+                                                torch.from_numpy(ci).to(dev), R=r, N=n)
+    torch.cuda.synchronize()
+    assert np.array_equal(got_id.cpu().numpy(), rr_id)
+    gv = got_val.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(gv - e) <= 2e-3 * np.abs(e) + 1e-5)
+
+
+@pytest.mark.timeout(900)
+def test_nvfp4_rerank_full_shape(dev, full):
+    """The per-rank shard with an NVFP4 rerank source: parity at M = 1, 8, 72
+    and the argmax agreement with the exact bf16 head (reported)."""
+    cfg = full["cfg"]
+    _log("nvfp4 full shape: synthetic NVFP4 head")
+    w4, bs, g = workload.nvfp4_head(full["w"])
+    head = full["head"]
+    t_w4, t_bs, t_g = _nvfp4_dev(w4, bs, g, dev)
+    h4 = B.DraftHead(head.tiled, head.pairs, t_w4, cfg.n, cfg.k, cfg.kcand, cfg.rerank, bscale=t_bs, gscale=t_g)
+    for m in (1, 8, 72):
+        x = full["x"][:m]
+        got = run_gpu(h4, x, dev, want_coarse=False)
+        ref = _prefix(full["ref"], m)
+        e = oracle.rerank_exact_nvfp4(x, w4, bs, g, ref["rr_id"])
+        ref = dict(ref, rr_val=e, tie_rows=oracle.tie_rows(e))
+        ref["out_id"], ref["out_val"] = oracle.final_argmax(ref["rr_id"], e)
+        stats = compare(ref, got, cfg.n, cfg.kcand, check_coarse=False)
+        _log(f"nvfp4 full shape m={m}: {stats}")
+    E = oracle.exact_head(full["x"], full["w"])
+    agree = int(np.sum(got["out_id"] == np.argmax(E, axis=1)))
+    _log(f"nvfp4 full shape m=72: argmax agreement with the exact bf16 head {agree}/72 (reported)")
+
+
 # ------------------------------------------------------------ 4-bit head
 @pytest.mark.parametrize("m,k,n,kcand,r", [(1, 256, 3000, 1, 32), (3, 768, 5000, 1, 32), (8, 1024, 20000, 8, 32),
                                            (20, 512, 3000, 1, 16), (5, 2048, 5000, 4, 32), (72, 1024, 2100, 1, 32)])

@@ -27,7 +27,8 @@ def test_library_exports_every_header_symbol(lib):
                           "draft_head_tile", "draft_head_workspace_bytes", "draft_head_coarse",
                           "draft_head_rerank", "draft_head_argmax", "draft_head_forward",
                           "draft_head_stream_read", "draft_head_logits_row", "draft_head_rerank_e4m3",
-                          "draft_head_forward_e4m3", "draft_head_quantize_pack_int4",
+                          "draft_head_forward_e4m3", "draft_head_rerank_nvfp4", "draft_head_forward_nvfp4",
+                          "draft_head_quantize_pack_int4",
                           "draft_head_int4_as_int2", "draft_head_coarse_int4", "draft_head_forward_int4"}
     for name in names:
         assert hasattr(lib, name), name
@@ -250,6 +251,34 @@ def test_rerank_e4m3_validation(lib):
                 FAKE, 512, None, None, None), B.DH_EINVAL)
     _err(lib, f(FAKE, 1, 512, 64, FAKE, FAKE, FAKE, FAKE, 520, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                 FAKE, 512, None, None, None), B.DH_EINVAL)
+
+
+def test_rerank_nvfp4_validation(lib):
+    ok = dict(x=FAKE, w=FAKE, ldw=256, bs=FAKE, lds=32, g=FAKE, M=2, K=512, N=100, cv=FAKE, ci=FAKE, nc=16, R=8,
+              ri=FAKE, rv=FAKE, s=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.draft_head_rerank_nvfp4(a["x"], a["w"], a["ldw"], a["bs"], a["lds"], a["g"], a["M"], a["K"],
+                                           a["N"], a["cv"], a["ci"], a["nc"], a["R"], a["ri"], a["rv"], a["s"])
+    _err(lib, call(bs=None), B.DH_EINVAL)          # the block scales
+    _err(lib, call(g=None), B.DH_EINVAL)           # the global scale
+    _err(lib, call(w=None), B.DH_EINVAL)
+    _err(lib, call(ldw=240), B.DH_EINVAL)          # a row holds K/2 bytes
+    _err(lib, call(ldw=264), B.DH_EINVAL)          # rows of bytes: a multiple of 16
+    _err(lib, call(lds=30), B.DH_EINVAL)           # K/16 scale bytes per row
+    _err(lib, call(lds=33), B.DH_EINVAL)           # even, for 2-byte scale loads
+    _err(lib, call(bs=ctypes.c_void_p(4097)), B.DH_EINVAL)   # 2-byte aligned
+    _err(lib, call(w=MIS), B.DH_EINVAL)
+    _err(lib, call(M=0), B.DH_EINVAL)
+    _err(lib, call(K=100), B.DH_ESHAPE)
+    _err(lib, call(R=17), B.DH_EUNSUP)
+    f = lib.draft_head_forward_nvfp4             # the same checks before any launch
+    _err(lib, f(FAKE, 1, 512, 64, FAKE, FAKE, FAKE, 256, None, 32, FAKE, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                None, FAKE, 512, None, None, None), B.DH_EINVAL)
+    _err(lib, f(FAKE, 1, 512, 64, FAKE, FAKE, FAKE, 256, FAKE, 31, FAKE, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                None, FAKE, 512, None, None, None), B.DH_EINVAL)
 
 
 def test_logits_row_validation(lib):
