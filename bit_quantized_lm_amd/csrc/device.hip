@@ -276,12 +276,83 @@ __device__ __forceinline__ uint32_t bsel(uint32_t mask, uint32_t a, uint32_t b) 
 // value(i, r, t): the coarse score of row m0 + 16i + 4hh + r, column
 // 64b + 16t + nn.  Passes with r % rstep != rfirst are left to another wave.
 // Slots past the block's valid columns get (-inf, -1).
+// The selection rounds, for NB lists at a time per 16-lane row: lane nn of a
+// row holds keys k[t] of columns c[t] (t = 0..3).  Each lane first sorts its
+// four (stable on equal keys); each round then takes the row's largest head
+// (row16_max) and the lowest column holding it (row16_min), lane cc keeps
+// round cc's result and the winning lane advances.  On return lane nn holds
+// the list's entry 16 sl + nn in kk[sl], kc[sl] (key 0: none).
+template <int NB>
+__device__ __forceinline__ void row16_select(uint32_t (&k)[NB][4], uint32_t (&c)[NB][4], int kcand, int nn,
+                                             uint32_t (&kk)[NB][4], uint32_t (&kc)[NB][4]) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kk[j][t] = kc[j][t] = 0u;
+    auto ce = [&](int p) {   // neighbours p, p + 1: stable on equal keys
+      const uint32_t sw = k[j][p + 1] > k[j][p] ? ~0u : 0u;
+      const uint32_t tk = k[j][p], tc = c[j][p];
+      k[j][p] = bsel(sw, k[j][p + 1], tk);
+      c[j][p] = bsel(sw, c[j][p + 1], tc);
+      k[j][p + 1] = bsel(sw, tk, k[j][p + 1]);
+      c[j][p + 1] = bsel(sw, tc, c[j][p + 1]);
+    };
+    ce(0);
+    ce(1);
+    ce(2);
+    ce(0);
+    ce(1);
+    ce(0);
+  }
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    if (16 * sl >= kcand) break;
+    const int nround = min(16, kcand - 16 * sl);
+    for (int cc = 0; cc < nround; ++cc) {
+      const uint32_t own = cc == nn ? ~0u : 0u;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint32_t mx = row16_max(k[j][0]);
+        const uint32_t mc = row16_min(k[j][0] == mx ? c[j][0] : 64u);
+        const uint32_t win = c[j][0] == mc ? ~0u : 0u;   // the winner's next score becomes its head
+        k[j][0] = bsel(win, k[j][1], k[j][0]);
+        k[j][1] = bsel(win, k[j][2], k[j][1]);
+        k[j][2] = bsel(win, k[j][3], k[j][2]);
+        k[j][3] = k[j][3] & ~win;
+        c[j][0] = bsel(win, c[j][1], c[j][0]);
+        c[j][1] = bsel(win, c[j][2], c[j][1]);
+        c[j][2] = bsel(win, c[j][3], c[j][2]);
+        c[j][3] = bsel(win, 64u, c[j][3]);
+        kk[j][sl] = bsel(own, mx, kk[j][sl]);
+        kc[j][sl] = bsel(own, mc, kc[j][sl]);
+      }
+    }
+  }
+}
+
+// Lane nn's entries of the list of (row m, block b): slots 16 sl + nn.
+__device__ __forceinline__ void write_list(const CoarseArgs& A, int m, int b, const uint32_t (&kk)[4],
+                                           const uint32_t (&kc)[4], int nn) {
+  const float NEG_INF = -__builtin_inff();
+  const size_t base = (size_t)m * A.nblk * A.kcand + (size_t)b * A.kcand;
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    const int cs = 16 * sl + nn;
+    if (cs < A.kcand) {
+      A.cand_val[base + cs] = kk[sl] ? key_f32(kk[sl]) : NEG_INF;
+      A.cand_id[base + cs] = kk[sl] ? b * 64 + (int)kc[sl] : -1;
+    }
+  }
+}
+
+// Top-kcand of block b for the rows a wave's accumulators hold: rows m0 + 16 i
+// + 4 hh + r, one list per 16-lane row and pass, up to four passes at once
+// so that the cross-lane chains overlap.  Keys are order-preserving unsigned
+// images of the fp32 scores; ties go to the lower column.
 template <int MT, int MR, class Value>
 __device__ __forceinline__ void block_select(Value value, const CoarseArgs& A, int b, int hh, int nn,
                                              int rfirst = 0, int rstep = 1, int m0 = 0) {
   constexpr int NP = MT * MR, NB = NP < 4 ? NP : 4;   // passes, passes per batch
-  const float NEG_INF = -__builtin_inff();
-  const int ncand = A.nblk * A.kcand;
 #pragma unroll
   for (int p0 = 0; p0 < NP; p0 += NB) {
     uint32_t k[NB][4], c[NB][4], kk[NB][4], kc[NB][4];
@@ -299,69 +370,56 @@ __device__ __forceinline__ void block_select(Value value, const CoarseArgs& A, i
         const float sv = pi < NP ? value(i, r, t) : 0.f;
         k[j][t] = ok ? f32_key(sv + 0.0f) : 0u;   // -0 counts as +0, as in a float compare
         c[j][t] = 16 * t + nn;
-        kk[j][t] = 0u;
-        kc[j][t] = 0u;
         if (A.coarse_out && ok) A.coarse_out[(size_t)m * A.N + n] = sv;
       }
-      auto ce = [&](int p) {   // neighbours p, p + 1: stable on equal keys
-        const uint32_t sw = k[j][p + 1] > k[j][p] ? ~0u : 0u;
-        const uint32_t tk = k[j][p], tc = c[j][p];
-        k[j][p] = bsel(sw, k[j][p + 1], tk);
-        c[j][p] = bsel(sw, c[j][p + 1], tc);
-        k[j][p + 1] = bsel(sw, tk, k[j][p + 1]);
-        c[j][p + 1] = bsel(sw, tc, c[j][p + 1]);
-      };
-      ce(0);
-      ce(1);
-      ce(2);
-      ce(0);
-      ce(1);
-      ce(0);
     }
     bool any = false;
 #pragma unroll
     for (int j = 0; j < NB; ++j) any |= live[j];
     if (!any) continue;
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      if (16 * sl >= A.kcand) break;
-      const int nround = min(16, A.kcand - 16 * sl);
-      for (int cc = 0; cc < nround; ++cc) {
-        const uint32_t own = cc == nn ? ~0u : 0u;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const uint32_t mx = row16_max(k[j][0]);
-          const uint32_t mc = row16_min(k[j][0] == mx ? c[j][0] : 64u);
-          const uint32_t win = c[j][0] == mc ? ~0u : 0u;   // the winner's next score becomes its head
-          k[j][0] = bsel(win, k[j][1], k[j][0]);
-          k[j][1] = bsel(win, k[j][2], k[j][1]);
-          k[j][2] = bsel(win, k[j][3], k[j][2]);
-          k[j][3] = k[j][3] & ~win;
-          c[j][0] = bsel(win, c[j][1], c[j][0]);
-          c[j][1] = bsel(win, c[j][2], c[j][1]);
-          c[j][2] = bsel(win, c[j][3], c[j][2]);
-          c[j][3] = bsel(win, 64u, c[j][3]);
-          kk[j][sl] = bsel(own, mx, kk[j][sl]);
-          kc[j][sl] = bsel(own, mc, kc[j][sl]);
-        }
-      }
-    }
+    row16_select<NB>(k, c, A.kcand, nn, kk, kc);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int pi = p0 + j, i = pi / MR, r = pi % MR;
       const int m = m0 + 16 * i + 4 * hh + r;
-      if (!live[j] || m >= A.M) continue;
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const int cs = 16 * sl + nn;
-        if (cs < A.kcand) {
-          const size_t o = (size_t)m * ncand + (size_t)b * A.kcand + cs;
-          A.cand_val[o] = kk[j][sl] ? key_f32(kk[j][sl]) : NEG_INF;
-          A.cand_id[o] = kk[j][sl] ? b * 64 + (int)kc[j][sl] : -1;
-        }
-      }
+      if (live[j] && m < A.M) write_list(A, m, b, kk[j], kc[j], nn);
     }
   }
+}
+
+// The resident kernel's selection: the lists of all (block, row) pairs of the
+// workgroup, read from LDS (sc: [kBlocks][MP][64] scores), packed densely
+// onto the 16-lane rows of the waves (list q = 4 (wave + W pass) + hh is row
+// q % M of block q / M), so that each selection round serves four lists.
+template <int MP, int kBlocks, int W>
+__device__ __forceinline__ void res_select(const float* sc, const CoarseArgs& A, int b0, int wave, int hh,
+                                           int nn) {
+  constexpr int NB = (kBlocks * MP + 4 * W - 1) / (4 * W);   // passes per wave
+  const int nl = kBlocks * A.M;
+  if (4 * wave >= nl) return;   // wave-uniform: no list in any pass
+  uint32_t k[NB][4], c[NB][4], kk[NB][4], kc[NB][4];
+  int lbq[NB], mq[NB];
+  bool live[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int q = 4 * (wave + W * j) + hh;
+    lbq[j] = q / A.M;
+    mq[j] = q - lbq[j] * A.M;
+    live[j] = q < nl && b0 + lbq[j] < A.nblk;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = (b0 + lbq[j]) * 64 + 16 * t + nn;
+      const bool ok = live[j] && n < A.N;
+      const float sv = ok ? sc[(lbq[j] * MP + mq[j]) * 64 + 16 * t + nn] : 0.f;
+      k[j][t] = ok ? f32_key(sv + 0.0f) : 0u;   // -0 counts as +0, as in a float compare
+      c[j][t] = 16 * t + nn;
+      if (A.coarse_out && ok) A.coarse_out[(size_t)mq[j] * A.N + n] = sv;
+    }
+  }
+  row16_select<NB>(k, c, A.kcand, nn, kk, kc);
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    if (live[j]) write_list(A, mq[j], b0 + lbq[j], kk[j], kc[j], nn);
 }
 
 // Convert 8 natural-order bf16 x values into the decode order {0,2,1,3,4,6,5,7},
@@ -396,10 +454,10 @@ __device__ __forceinline__ float row16_sum(float s) {
 // used) with the group sums X.  Then every wave streams its tiles with no
 // further barrier, keeping the codes and scale pairs of the next byte groups
 // in flight in a ring of D register sets (D-1 groups ahead at one row, D from
-// two rows on).  At the end the tiles of a block meet in LDS and the block's
-// top-kcand is selected.
+// two rows on).  At the end the scores of every tile meet in LDS and the
+// workgroup's (block, row) lists are selected, four per wave at a time.
 // LDS: x fragments [group it = 4G + q][f][MP] (16 bytes each), X[it][MP], then
-// the block scores [block][16 rows][64 columns].
+// the block scores [block][MP rows][64 columns].
 constexpr int kResDepth = 2;   // ring sets of byte groups held in registers
 
 // Tiles per wave: two for 1-2 rows (more waves to hide latency), four for 4-8
@@ -427,8 +485,7 @@ void coarse_resident_kernel(CoarseArgs A) {
   const int NG4 = A.K >> 9, Q4 = A.K >> 2, NG = A.K >> 7;
   u32x4* xs = reinterpret_cast<u32x4*>(smem);                               // [NG][16][MP]
   float* Xs = reinterpret_cast<float*>(smem + (size_t)NG * 16 * MP * 16);       // [NG][MP]
-  float* sel = Xs + (size_t)NG * MP;                                           // [kBlocks][16][64]
-  int* flag = reinterpret_cast<int*>(sel + (size_t)kBlocks * 16 * 64);          // [kBlocks]
+  float* sel = Xs + (size_t)NG * MP;                                           // [kBlocks][MP][64]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -512,7 +569,6 @@ void coarse_resident_kernel(CoarseArgs A) {
       use_x(base, v);
     }
   }
-  if (tid < kBlocks) flag[tid] = 0;
   __syncthreads();
 
   f32x4 acc[1][NT];
@@ -576,33 +632,17 @@ void coarse_resident_kernel(CoarseArgs A) {
     }
   }
 
-  // The block's selection starts as soon as its own tiles are done, with no
-  // workgroup barrier, so that waves still streaming are not held up.  One
-  // wave per block selects from its registers; with two, part 1 hands its
-  // tiles to part 0 through LDS and a flag, and part 0 selects.
-  if (!blk_ok) return;
-  if constexpr (kWavesPerBlock == 1) {
-    block_select<1, MR>([&](int, int r, int t) { return acc[0][t][r]; }, A, b, hh, nn, 0, 1);
-  } else {
-    static_assert(kWavesPerBlock == 2, "one or two waves per block");
-    float* bs = sel + (size_t)lblk * 16 * 64;
-    if (part == 1) {
+  // Every wave puts the scores of its tiles' live rows in LDS; after one
+  // barrier the (block, row) lists are selected four at a time per wave.
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < MR; ++r) bs[(4 * hh + r) * 64 + 16 * (NT + t) + nn] = acc[0][t][r];
-      if (lane == 0) __hip_atomic_store(flag + lblk, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      return;
+    for (int r = 0; r < MR; ++r) {
+      const int row = 4 * hh + r;
+      if (row < MP) sel[(lblk * MP + row) * 64 + 16 * (NT * part + t) + nn] = acc[0][t][r];
     }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < MR; ++r) bs[(4 * hh + r) * 64 + 16 * t + nn] = acc[0][t][r];
-    while (__hip_atomic_load(flag + lblk, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-      __builtin_amdgcn_s_sleep(1);
-    block_select<1, MR>([&](int, int r, int t) { return bs[(4 * hh + r) * 64 + 16 * t + nn]; }, A, b, hh, nn,
-                        0, 1);
-  }
+  __syncthreads();
+  res_select<MP, kBlocks, kResWaves>(sel, A, blockIdx.x * kBlocks, wave, hh, nn);
 }
 
 // ---------------------------------------------------------------------------
@@ -1799,8 +1839,7 @@ size_t resident_lds_bytes(int K, int MP) {
   const size_t groups = (size_t)K / DH_GROUP;
   const size_t blocks = (size_t)res_waves<1>() * res_nt(MP) / 4;   // 4 / res_nt waves per block
   static_assert(res_waves<1>() == res_waves<8>(), "LDS sizing assumes one workgroup shape");
-  return groups * 16 * MP * 16 + groups * MP * sizeof(float) + blocks * 16 * 64 * sizeof(float) +
-         blocks * sizeof(int);
+  return groups * 16 * MP * 16 + groups * MP * sizeof(float) + blocks * MP * 64 * sizeof(float);
 }
 
 template <int MP>
