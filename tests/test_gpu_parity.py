@@ -90,6 +90,12 @@ CASES = [
     (2, 512, 131100, 8, 32),
     # R > 64 (exact threshold by radix select) in the separate rerank kernel
     (20, 512, 70000, 8, 100),
+    # the resident kernel at its largest LDS (x of the longest rows it takes),
+    # and the many-row kernel just past it
+    (2, 39424, 300, 8, 32),
+    (4, 18944, 300, 8, 32),
+    (8, 8704, 500, 8, 32),
+    (8, 9216, 500, 8, 32),
 ]
 
 
