@@ -49,9 +49,10 @@ WEIGHT_BYTES = N * (K // 4) + 2 * 2 * N * (K // 128)       # 178,790,400
 
 
 def coarse_kernel_name(m: int) -> str:
-    """The coarse kernel one launch at M rows runs (K = 5120)."""
+    """The coarse kernel one launch at M rows runs (K = 5120; one row runs the
+    two-row instance)."""
     if m <= 8:
-        return f"coarse_resident_kernel<{1 if m == 1 else 2 if m == 2 else 4 if m <= 4 else 8}>"
+        return f"coarse_resident_kernel<{2 if m <= 2 else 4 if m <= 4 else 8}>"
     return f"coarse_mfma_kernel<{min((m + 15) // 16, 5)}>"
 
 

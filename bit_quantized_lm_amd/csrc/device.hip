@@ -1875,12 +1875,19 @@ hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t
   return hipGetLastError();
 }
 
-int resident_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+// Rows the resident kernel is instantiated for (M padded up).  One row runs
+// the two-row kernel, whose ring keeps two byte groups in flight (1.7 us
+// faster at K = 5120; the one-row form cannot within 128 registers), unless
+// x of two rows would not fit the LDS.
+int resident_rows(int M, int K) {
+  if (M <= 1) return resident_lds_bytes(K, 2) <= kMaxLds ? 2 : 1;
+  return M <= 2 ? 2 : M <= 4 ? 4 : 8;
+}
 
 
 // Up to 8 rows whose x fits the workgroup's LDS take the resident kernel (no
 // workspace); every other M the many-row kernel, in launches of up to 80 rows.
-bool use_resident(int M, int K) { return M <= 8 && resident_lds_bytes(K, resident_rows(M)) <= kMaxLds; }
+bool use_resident(int M, int K) { return M <= 8 && resident_lds_bytes(K, resident_rows(M, K)) <= kMaxLds; }
 
 // Workspace: the rerank's per-row arrival counters, then (many-row kernel
 // only) the x of one launch.
@@ -1963,7 +1970,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
                static_cast<uint32_t*>(workspace), M, kx ? kx : K};
   hipError_t e = hipSuccess;
   if (use_resident(M, K)) {
-    switch (resident_rows(M)) {
+    switch (resident_rows(M, K)) {
       case 1: e = launch_resident<1>(A, s, ev0, ev1); break;
       case 2: e = launch_resident<2>(A, s, ev0, ev1); break;
       case 4: e = launch_resident<4>(A, s, ev0, ev1); break;

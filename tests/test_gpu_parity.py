@@ -92,6 +92,8 @@ CASES = [
     (20, 512, 70000, 8, 100),
     # the resident kernel at its largest LDS (x of the longest rows it takes),
     # and the many-row kernel just past it
+    (1, 39424, 300, 8, 32),
+    (1, 40960, 300, 8, 32),    # one row past the two-row instance's LDS: the one-row instance
     (2, 39424, 300, 8, 32),
     (4, 18944, 300, 8, 32),
     (8, 8704, 500, 8, 32),
