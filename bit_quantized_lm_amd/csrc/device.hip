@@ -460,17 +460,18 @@ __device__ __forceinline__ float row16_sum(float s) {
 // the block scores [block][MP rows][64 columns].
 constexpr int kResDepth = 2;   // ring sets of byte groups held in registers
 
-// Tiles per wave: two for 1-2 rows (more waves to hide latency), four for 4-8
-// rows, where the per-row scale updates make a wave's share of work larger.
-constexpr int res_nt(int MP) { return MP <= 2 ? 2 : 4; }
+// Tiles per wave: two for 1-4 rows (more waves to hide latency; 1.1-2.2 us
+// faster at three and four rows than four tiles), four for 8 rows (at two
+// tiles, x of eight rows would leave LDS for one workgroup per CU only).
+constexpr int res_nt(int MP) { return MP <= 4 ? 2 : 4; }
 
 template <int MP>
 constexpr int res_waves() { return 8; }
 // Waves per SIMD the grid needs to be resident at once (1940 blocks at the
-// page's N): four at 1-2 rows (two workgroups of four blocks per CU), two at
-// 4-8 rows (one workgroup of eight blocks).
+// page's N): four at two tiles per wave (two workgroups of four blocks per
+// CU), two at four (one workgroup of eight blocks).
 template <int MP>
-constexpr int res_min_waves() { return MP <= 2 ? 4 : 2; }
+constexpr int res_min_waves() { return res_nt(MP) == 2 ? 4 : 2; }
 
 template <int MP>
 __global__ __launch_bounds__(64 * res_waves<MP>()) __attribute__((amdgpu_waves_per_eu(res_min_waves<MP>())))

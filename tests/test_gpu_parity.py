@@ -95,7 +95,8 @@ CASES = [
     (1, 39424, 300, 8, 32),
     (1, 40960, 300, 8, 32),    # one row past the two-row instance's LDS: the one-row instance
     (2, 39424, 300, 8, 32),
-    (4, 18944, 300, 8, 32),
+    (4, 19456, 300, 8, 32),
+    (4, 19968, 300, 8, 32),
     (8, 8704, 500, 8, 32),
     (8, 9216, 500, 8, 32),
 ]

@@ -144,10 +144,10 @@ def test_workspace_bytes(lib):
     # 512 bytes of per-row counters; the resident kernel (up to 8 rows while x
     # fits its LDS) needs nothing more
     # (LDS (K/128) * (256 MP + 4 MP) + blocks * MP * 256 within 160 KB)
-    for m, k in ((1, 5120), (1, 65536), (2, 39424), (4, 18944), (8, 5120), (8, 8704)):
+    for m, k in ((1, 5120), (1, 65536), (2, 39424), (4, 19456), (8, 5120), (8, 8704)):
         assert B.draft_head_workspace_bytes(m, k) == 512, (m, k)
     # many-row kernel: + (K/128) * 4096 * MT + (K/512) * 4096 with MT = min(ceil(M/16), 5)
-    for m, k in ((2, 39936), (4, 19456), (8, 9216), (9, 512), (16, 1024), (17, 1024), (72, 5120),
+    for m, k in ((2, 39936), (4, 19968), (8, 9216), (9, 512), (16, 1024), (17, 1024), (72, 5120),
                  (80, 5120), (81, 5120), (128, 5120)):
         mt = min((m + 15) // 16, 5)
         assert B.draft_head_workspace_bytes(m, k) == 512 + (k // 128) * 4096 * mt + (k // 512) * 4096, (m, k)
