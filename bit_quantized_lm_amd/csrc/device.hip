@@ -460,18 +460,20 @@ __device__ __forceinline__ float row16_sum(float s) {
 // the block scores [block][MP rows][64 columns].
 constexpr int kResDepth = 2;   // ring sets of byte groups held in registers
 
-// Tiles per wave: two for 1-4 rows (more waves to hide latency; 1.1-2.2 us
-// faster at three and four rows than four tiles), four for 8 rows (at two
-// tiles, x of eight rows would leave LDS for one workgroup per CU only).
-constexpr int res_nt(int MP) { return MP <= 4 ? 2 : 4; }
+// Two tiles per wave, so that four waves fit each SIMD and hide each other's
+// latency (four tiles per wave, two waves per SIMD, measured 1.1-4.0 us
+// slower at three to eight rows).  Eight waves (four blocks) per workgroup up
+// to four rows, two workgroups per CU; sixteen (eight blocks) at eight rows,
+// where x of eight rows leaves LDS for one workgroup per CU.
+constexpr int res_nt(int MP) { return 2; }
+constexpr int res_waves_of(int MP) { return MP == 8 ? 16 : 8; }
 
 template <int MP>
-constexpr int res_waves() { return 8; }
+constexpr int res_waves() { return res_waves_of(MP); }
 // Waves per SIMD the grid needs to be resident at once (1940 blocks at the
-// page's N): four at two tiles per wave (two workgroups of four blocks per
-// CU), two at four (one workgroup of eight blocks).
+// page's N): four.
 template <int MP>
-constexpr int res_min_waves() { return res_nt(MP) == 2 ? 4 : 2; }
+constexpr int res_min_waves() { return 4; }
 
 template <int MP>
 __global__ __launch_bounds__(64 * res_waves<MP>()) __attribute__((amdgpu_waves_per_eu(res_min_waves<MP>())))
@@ -514,11 +516,12 @@ void coarse_resident_kernel(CoarseArgs A) {
 
   // stage x: piece i = (m, k0 = 8p) for all MP rows (zero rows past M).  Loads
   // are issued kBatch at a time from clamped (always valid) addresses: at
-  // K = 5120 all of x in one round (1.0 us less at four rows than rounds of 4).  The
+  // K = 5120 all of x in one round (1.0 us less at four rows than rounds of
+  // four loads).  The
   // first byte groups' codes are requested right after the first batch of x,
   // so that x (from L2) is not waited for behind them.
   {
-    constexpr int kBatch = MP <= 2 ? 4 : MP == 4 ? 5 : 10;
+    constexpr int kBatch = MP <= 2 ? 4 : 5;
     const int per_row = A.K >> 3;
     const int total = MP * per_row;
     auto issue_x = [&](int base, u32x4 (&v)[kBatch]) {
@@ -1839,8 +1842,7 @@ constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 
 size_t resident_lds_bytes(int K, int MP) {
   const size_t groups = (size_t)K / DH_GROUP;
-  const size_t blocks = (size_t)res_waves<1>() * res_nt(MP) / 4;   // 4 / res_nt waves per block
-  static_assert(res_waves<1>() == res_waves<8>(), "LDS sizing assumes one workgroup shape");
+  const size_t blocks = (size_t)res_waves_of(MP) * res_nt(MP) / 4;   // 4 / res_nt waves per block
   return groups * 16 * MP * 16 + groups * MP * sizeof(float) + blocks * MP * 64 * sizeof(float);
 }
 
