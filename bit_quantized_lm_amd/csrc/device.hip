@@ -485,10 +485,14 @@ void coarse_resident_kernel(CoarseArgs A) {
   constexpr int kBlocks = kResWaves / kWavesPerBlock;
   constexpr int MR = MP < 4 ? MP : 4;  // accumulator rows r that can hold a live row
   extern __shared__ __align__(16) unsigned char smem[];
-  const int NG4 = A.K >> 9, Q4 = A.K >> 2, NG = A.K >> 7;
-  u32x4* xs = reinterpret_cast<u32x4*>(smem);                               // [NG][16][MP]
-  float* Xs = reinterpret_cast<float*>(smem + (size_t)NG * 16 * MP * 16);       // [NG][MP]
-  float* sel = Xs + (size_t)NG * MP;                                           // [kBlocks][MP][64]
+  const int NG4 = A.K >> 9, Q4 = A.K >> 2;
+  // x rows of length kx < K (a 4-bit head in its 2K-long form, read as
+  // (x, x)): quarters 2 and 3 see the x of quarters 0 and 1, so only those
+  // are staged (QN = 2 quarters per byte group; else 4).
+  const int QN = A.kx < A.K ? 2 : 4, NGS = A.kx >> 7;   // staged quarters, staged groups
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);                               // [NGS][16][MP]
+  float* Xs = reinterpret_cast<float*>(smem + (size_t)NGS * 16 * MP * 16);      // [NGS][MP]
+  float* sel = Xs + (size_t)NGS * MP;                                          // [kBlocks][MP][64]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -522,15 +526,14 @@ void coarse_resident_kernel(CoarseArgs A) {
   // so that x (from L2) is not waited for behind them.
   {
     constexpr int kBatch = MP <= 2 ? 4 : 5;
-    const int per_row = A.K >> 3;
+    const int per_row = A.kx >> 3;
     const int total = MP * per_row;
     auto issue_x = [&](int base, u32x4 (&v)[kBatch]) {
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int i = min(base + tid + j * kResThreads, total - 1);
         const int m = i / per_row, k0 = (i - m * per_row) * 8;
-        v[j] = *reinterpret_cast<const u32x4*>(A.x + (size_t)(m < A.M ? m : 0) * A.kx +
-                                               (k0 < A.kx ? k0 : k0 - A.kx));
+        v[j] = *reinterpret_cast<const u32x4*>(A.x + (size_t)(m < A.M ? m : 0) * A.kx + k0);
       }
     };
     // Only the LDS writes are predicated: a load whose value were used only
@@ -543,7 +546,7 @@ void coarse_resident_kernel(CoarseArgs A) {
         const int m = ic / per_row, k0 = (ic - m * per_row) * 8;
         const u32x4 vm = m < A.M ? v[j] : u32x4{0u, 0u, 0u, 0u};
         const int q = k0 / Q4, G = (k0 - q * Q4) >> 7, p = (k0 >> 3) & 15;
-        const int it = G * 4 + q;
+        const int it = G * QN + q;
         float sum;
         const u32x4 o = permute_x(vm, sum);
         sum = row16_sum(sum);
@@ -582,8 +585,9 @@ void coarse_resident_kernel(CoarseArgs A) {
 
   const int arow = nn & (MP - 1);
   auto byte_group = [&](int G, const u32x4 (&raw)[2][NT], const u32x4 (&sz)[NT]) {
-    const u32x4* xb = xs + (size_t)(G * 64 + hh) * MP + arow;
-    const float* Xg = Xs + G * 4 * MP + ((4 * hh) & (MP - 1));
+    const u32x4* xb = xs + (size_t)(G * QN * 16 + hh) * MP + arow;
+    const float* Xg = Xs + G * QN * MP + ((4 * hh) & (MP - 1));
+    const int q2 = QN == 4 ? 2 : 0, q3 = QN == 4 ? 3 : 1;   // staged quarter of quarters 2, 3
     u32x4 raw8[2][NT];
     shift_codes(raw, raw8);
     // each group's scale update is issued after the next group's MFMAs, so it
@@ -592,11 +596,11 @@ void coarse_resident_kernel(CoarseArgs A) {
     group_mma<1, 0, NT>(c0, raw, raw8, xb, MP);
     group_mma<1, 1, NT>(c1, raw, raw8, xb + 16 * MP, MP);
     group_scale<1, MR, 0, NT>(acc, c0, sz, Xg, 0);
-    group_mma<1, 2, NT>(c0, raw, raw8, xb + 32 * MP, MP);
+    group_mma<1, 2, NT>(c0, raw, raw8, xb + q2 * 16 * MP, MP);
     group_scale<1, MR, 1, NT>(acc, c1, sz, Xg + MP, 0);
-    group_mma<1, 3, NT>(c1, raw, raw8, xb + 48 * MP, MP);
-    group_scale<1, MR, 2, NT>(acc, c0, sz, Xg + 2 * MP, 0);
-    group_scale<1, MR, 3, NT>(acc, c1, sz, Xg + 3 * MP, 0);
+    group_mma<1, 3, NT>(c1, raw, raw8, xb + q3 * 16 * MP, MP);
+    group_scale<1, MR, 2, NT>(acc, c0, sz, Xg + q2 * MP, 0);
+    group_scale<1, MR, 3, NT>(acc, c1, sz, Xg + q3 * MP, 0);
   };
   // Two forms of the same stream.  From two rows on, each ring set is
   // refilled right after its byte group is done, so D byte groups are in
@@ -1848,7 +1852,7 @@ size_t resident_lds_bytes(int K, int MP) {
 
 template <int MP>
 hipError_t launch_resident(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const size_t lds = resident_lds_bytes(A.K, MP);
+  const size_t lds = resident_lds_bytes(A.kx, MP);
   static bool attr_set = false;   // the attribute only ever grows to kMaxLds
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&coarse_resident_kernel<MP>),
@@ -1891,20 +1895,22 @@ int resident_rows(int M, int K) {
 
 // Up to 8 rows whose x fits the workgroup's LDS take the resident kernel (no
 // workspace); every other M the many-row kernel, in launches of up to 80 rows.
-bool use_resident(int M, int K) { return M <= 8 && resident_lds_bytes(K, resident_rows(M, K)) <= kMaxLds; }
+// ks: the staged row length of x (K, or K/2 for a 4-bit head in its 2K-long form).
+bool use_resident(int M, int ks) { return M <= 8 && resident_lds_bytes(ks, resident_rows(M, ks)) <= kMaxLds; }
 
 // Workspace: the rerank's per-row arrival counters, then (many-row kernel
 // only) the x of one launch.
 constexpr size_t kCounterBytes = DH_MAX_M * sizeof(uint32_t);
 
-size_t coarse_workspace_bytes(int M, int K) {
-  if (use_resident(M, K)) return kCounterBytes;
+// ks: the staged row length of x when it differs from K (0: K).
+size_t coarse_workspace_bytes(int M, int K, int ks = 0) {
+  if (use_resident(M, ks ? ks : K)) return kCounterBytes;
   return kCounterBytes + big_workspace_bytes(std::min((M + 15) / 16, kMaxMT), K);
 }
 
 int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
                     int kcand, const float* cand_val, const int32_t* cand_id, const void* workspace,
-                    size_t workspace_bytes) {
+                    size_t workspace_bytes, int ks = 0) {
   if (!x || !tiled || !pairs || !cand_val || !cand_id)
     return dh::fail(DH_EINVAL, "coarse: null pointer");
   int rc = check_m(M);
@@ -1915,7 +1921,7 @@ int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, co
     return dh::fail(DH_EUNSUP, "coarse: kcand must be in 1..%d (got %d)", DH_MAX_KCAND, kcand);
   if (!aligned16(x) || !aligned16(tiled) || !aligned16(pairs))
     return dh::fail(DH_EINVAL, "coarse: x, tiled and pairs must be 16-byte aligned");
-  const size_t need = coarse_workspace_bytes(M, K);
+  const size_t need = coarse_workspace_bytes(M, K, ks);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need)
     return dh::fail(DH_EINVAL, "coarse: M=%d, K=%d needs a 16-byte aligned workspace of %zu bytes (got %p, %zu)",
                     M, K, need, workspace, workspace_bytes);
@@ -1973,8 +1979,9 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
                reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out,
                static_cast<uint32_t*>(workspace), M, kx ? kx : K};
   hipError_t e = hipSuccess;
-  if (use_resident(M, K)) {
-    switch (resident_rows(M, K)) {
+  const int ks = A.kx;   // the row length of x the resident kernel stages
+  if (use_resident(M, ks)) {
+    switch (resident_rows(M, ks)) {
       case 1: e = launch_resident<1>(A, s, ev0, ev1); break;
       case 2: e = launch_resident<2>(A, s, ev0, ev1); break;
       case 4: e = launch_resident<4>(A, s, ev0, ev1); break;
@@ -2162,7 +2169,8 @@ int draft_head_coarse_int4(const void* x, int M, int K, int N, const uint8_t* ti
                            size_t workspace_bytes, void* stream) {
   int rc = check_k4(K);
   if (rc) return rc;
-  if ((rc = validate_coarse(x, M, 2 * K, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes)))
+  if ((rc = validate_coarse(x, M, 2 * K, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes,
+                            K)))
     return rc;
   return launch_coarse(x, M, 2 * K, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace,
                        as_stream(stream), nullptr, nullptr, K);
@@ -2240,7 +2248,8 @@ int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const
   int rc = int4 ? check_k4(K) : DH_OK;
   if (rc) return rc;
   const int Kc = int4 ? 2 * K : K;
-  if ((rc = validate_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes)))
+  if ((rc = validate_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, workspace, workspace_bytes,
+                            int4 ? K : 0)))
     return rc;
   if ((rc = validate_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val))) return rc;
   if ((rc = validate_argmax(rr_id, rr_val, M, R, out_id, out_val))) return rc;
