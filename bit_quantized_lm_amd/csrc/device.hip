@@ -1566,6 +1566,12 @@ __device__ __forceinline__ int lane_prefix(unsigned long long bal) {
 //      (at least R, at most DH_MAX_R); each is ranked by counting the
 //      survivors above it, and the first R ranks are the list.
 constexpr int kWideThreads = 256;
+// From this many rows on, 1024 threads per workgroup (two per row at R = 32):
+// each workgroup recomputes its row's list, and at many rows that redundant
+// work outweighs the latency of more dots per workgroup (M = 72: 6 us less per
+// call; no difference at 16).
+constexpr int kWideBigM = 32;
+constexpr int kWideBigThreads = 1024;
 
 struct WideShared {
   unsigned int hist[256];
@@ -1765,11 +1771,11 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
   }
 }
 
-// Rerank kernel: grid (ceil(R / 4), M), one part of one row per workgroup.
-template <bool kArgmax, int kKind>
-__global__ __launch_bounds__(kWideThreads) void rerank_wide_kernel(RerankArgs A) {
+// Rerank kernel: grid (ceil(R / (NTHR / 64)), M), one part of one row per workgroup.
+template <bool kArgmax, int kKind, int NTHR>
+__global__ __launch_bounds__(NTHR) void rerank_wide_kernel(RerankArgs A) {
   __shared__ WideShared sh;
-  rerank_part<kWideThreads, kArgmax, kKind>(sh, A, blockIdx.y, blockIdx.x, gridDim.x);
+  rerank_part<NTHR, kArgmax, kKind>(sh, A, blockIdx.y, blockIdx.x, gridDim.x);
 }
 
 
@@ -2040,13 +2046,18 @@ hipError_t launch_wide(const void* x, const RowSrc& src, int M, int K, int N, co
                        int32_t* out_id, float* out_val, uint32_t* cnt, hipStream_t s) {
   const RerankArgs A{static_cast<const uint16_t*>(x), src, K, N, cand_val,
                      cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, cnt};
-  const dim3 grid((R + 3) / 4, M);
-  if (src.kind == kRowsE4m3)
-    hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsE4m3>), grid, dim3(kWideThreads), 0, s, A);
-  else if (src.kind == kRowsNvfp4)
-    hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsNvfp4>), grid, dim3(kWideThreads), 0, s, A);
-  else
-    hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsBf16>), grid, dim3(kWideThreads), 0, s, A);
+  auto go = [&](auto nthr) {
+    constexpr int NTHR = decltype(nthr)::value, NW = NTHR / 64;
+    const dim3 grid((R + NW - 1) / NW, M);
+    if (src.kind == kRowsE4m3)
+      hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsE4m3, NTHR>), grid, dim3(NTHR), 0, s, A);
+    else if (src.kind == kRowsNvfp4)
+      hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsNvfp4, NTHR>), grid, dim3(NTHR), 0, s, A);
+    else
+      hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsBf16, NTHR>), grid, dim3(NTHR), 0, s, A);
+  };
+  if (M >= kWideBigM) go(std::integral_constant<int, kWideBigThreads>{});
+  else go(std::integral_constant<int, kWideThreads>{});
   return hipGetLastError();
 }
 
