@@ -21,7 +21,9 @@ Prints one JSON line:
                its fractions of the HBM and bf16 MFMA peaks, the warm
                (cache-resident) figure, the time of the row handed to a
                top-k caller (draft_head_logits_row), the per-call time with
-               the e4m3 and NVFP4 rerank sources, the 4-bit head's per-call time
+               the e4m3 and NVFP4 rerank sources, the per-call time of forwards
+               replayed from a HIP graph (launch gaps removed; not the
+               headline), the 4-bit head's per-call time
                (KCAND = 1, 357,580,800 B of codes and pairs per call),
                and the device's achieved
                read rate (the library's streaming-read reference) and copy rate
@@ -240,6 +242,26 @@ class Rig:
         del heads, t_t, t_p
         return res
 
+    def graph_us(self, m=1, calls=8, reps=50):
+        """Per-call time of `calls` forwards (weight copies rotated) captured in
+        one HIP graph and replayed: the launch gaps between calls removed."""
+        torch = self.torch
+        out = self.buffers(m)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(calls):
+                self.heads[i % len(self.heads)](self.x[:m], out=out, workspace=self.ws[m])
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        return round(s.elapsed_time(e) / (reps * calls) * 1e3, 2)
+
     def logits_row_us(self, m, reps=50):
         """Time of draft_head_logits_row alone at M rows (full and top-k only)."""
         torch, B = self.torch, self.B
@@ -409,6 +431,8 @@ def main():
                                  "note": "one weight copy reused back to back: Infinity-Cache resident"}
         extra["logits_row_us"] = {str(mm): rig.logits_row_us(mm) for mm in (1, 8, 72)}
         extra["e4m3_rerank_us_per_call"] = rig.e4m3_call_us()
+        extra["graph_replay_us_per_call"] = {str(m): rig.graph_us(m) for m in (1, 8, 72)}
+        log(f"one call inside a replayed HIP graph: {extra['graph_replay_us_per_call']}")
         extra["nvfp4_rerank_us_per_call"] = rig.nvfp4_call_us()
         log(f"one call with the NVFP4 rerank source: {extra['nvfp4_rerank_us_per_call']}")
         extra["int4_kcand1_us_per_call"] = rig.int4_call_us()

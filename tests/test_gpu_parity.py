@@ -418,6 +418,43 @@ def test_e4m3_rerank_full_shape(dev, full):
     _log(f"e4m3 full shape m=72: argmax agreement with the exact bf16 head {agree}/72 (reported)")
 
 
+# ------------------------------------------------------------- graph capture
+@pytest.mark.parametrize("m", [1, 4, 20])
+def test_forward_graph_replay(dev, m):
+    """The one-call forward captured in a HIP graph (torch.cuda.CUDAGraph):
+    every replay, with eager calls and synchronisations between replays, gives
+    the eager call's outputs on the same input bit for bit (the library
+    records no memset; its counters are cleared by its own kernels)."""
+    n, k = 20000, 1024
+    w = workload.gen_weight(n, k, seed=105)
+    head = B.DraftHead.from_weight(w, kcand=8, R=32, device=dev)
+    xs = [_to_dev(workload.gen_x(m, k, seed=106 + i), dev) for i in range(3)]
+    x_static = torch.empty_like(xs[0])
+    out = B.forward_buffers(m, n, 8, 32, dev)
+    ws = B.workspace_for(m, k, dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture
+        x_static.copy_(xs[0])
+        head(x_static, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        head(x_static, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    _log(f"graph replay m={m}")
+    for rep in range(3):
+        for i, x in enumerate(xs):
+            eager = head(x)
+            torch.cuda.synchronize()
+            x_static.copy_(x)
+            g.replay()
+            torch.cuda.synchronize()
+            for key in ("cand_val", "cand_id", "rr_id", "rr_val", "out_id", "out_val"):
+                assert torch.equal(out[key], eager[key]), (rep, i, key)
+
+
 # ------------------------------------------------------ NVFP4 rerank source
 def _nvfp4_ref(x, w, packed, w4, bs, g, kcand, r):
     """The oracle's pipeline with the rerank read from the NVFP4 rows."""
