@@ -705,8 +705,14 @@ struct BigShape {
   static constexpr int MA = (MT + WPB - 1) / WPB;   // row tiles of part 0
   static constexpr int MB = MT - MA;                // row tiles of part 1
   static constexpr int W = 4 * WPB;                 // waves per workgroup
-  static constexpr int XD = MT >= 4 ? 3 : MT == 3 ? 5 : 6;   // x slabs requested ahead
-  static constexpr int CD = 2;                      // byte groups of codes requested ahead
+  // x slabs and byte groups of codes requested ahead.  One or two row tiles
+  // run four waves per workgroup: with one byte group of codes ahead (its
+  // slot refilled after the first group of the byte group has read it) and,
+  // at two tiles, three slabs, two workgroups fit a CU's LDS, so each SIMD
+  // runs two waves instead of one (M = 16: 59.9 -> 43.7 us, M = 32: 76.6 ->
+  // 58.2 us).  From three tiles on, two waves per block already fill that.
+  static constexpr int XD = MT >= 4 ? 3 : MT == 3 ? 5 : MT == 2 ? 3 : 6;
+  static constexpr int CD = MT <= 2 ? 1 : 2;
   static constexpr int XW = XD >= 4 ? 2 : 1;        // slab completed XW groups ahead
   static constexpr int PRO = XD > 4 * CD - 1 ? XD : 4 * CD - 1;   // prologue iterations
   // DMA ops per iteration of a wave of part p
