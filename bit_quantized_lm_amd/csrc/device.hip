@@ -1060,20 +1060,21 @@ constexpr int kDotBf16 = 10;   // 16-byte W loads per lane in flight (5120 k)
 constexpr int kDotE4m3 = 5;    // 16-byte W loads per lane in flight (5120 k)
 constexpr int kDotNvfp4 = 3;   // 16-byte W loads per lane in flight (6144 k)
 
+// e4m3 byte b as the page decodes it: magnitude mant * 2^-9 for e = 0, else
+// (1 + mant/8) * 2^(e-7), bit 7 the sign (0x7F reads as 480).  Bits 6..0
+// placed at fp32 bits 26..20 give 2^(e-127) (1 + mant/8), or the fp32
+// denormal mant * 2^-129 for e = 0 (denormals are kept: the kernels run
+// with fp32 denormal mode "preserve"); times 2^120, exactly, the values above.
 __device__ __forceinline__ float e4m3_page(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, mant = b & 7u;
-  const float sub = (float)mant * 0.001953125f;
-  const float nor = __uint_as_float(((e + 120u) << 23) | (mant << 20));
-  const float mag = e == 0u ? sub : nor;
-  return (b & 128u) ? -mag : mag;
+  return __uint_as_float(((b & 127u) << 20) | ((b & 128u) << 24)) * 0x1p120f;
 }
 
 // e2m1 (FP4) nibble: sign bit 3, exponent bits 2-1 (bias 1), mantissa bit 0;
-// exponent 0 is the subnormal 0.5 * mantissa.  Built as fp32 bits.
+// exponent 0 is the subnormal 0.5 * mantissa.  Bits 2..0 placed at fp32 bits
+// 24..22 give 2^(e-127) (1 + mant/2), or the fp32 denormal mant * 2^-127 for
+// e = 0; times 2^126, exactly, the e2m1 values.
 __device__ __forceinline__ float e2m1_value(uint32_t n) {
-  const uint32_t e = (n >> 1) & 3u, mant = n & 1u;
-  const uint32_t mag = e ? (((e + 126u) << 23) | (mant << 22)) : (mant ? 0x3F000000u : 0u);
-  return __uint_as_float(mag | ((n & 8u) << 28));
+  return __uint_as_float(((n & 7u) << 22) | ((n & 8u) << 28)) * 0x1p126f;
 }
 
 // NVFP4 block scale: an e4m3 byte as the format defines it (0x7F, 0xFF NaN).
