@@ -435,12 +435,15 @@ __device__ __forceinline__ u32x4 permute_x(const u32x4 v, float& sum) {
   return o;
 }
 
-// Sum over the 16 lanes of a DPP row (the 16 pieces of one group of one row).
+// Sum over the 16 lanes of a DPP row (the 16 pieces of one group of one row),
+// by DPP moves (lane pairs 1 apart, 2 apart, then the half rows and the row
+// mirrored): the tree of an xor butterfly, so every lane gets the same sum,
+// without the LDS round trips of a shuffle.
 __device__ __forceinline__ float row16_sum(float s) {
-  s += __shfl_xor(s, 1, 16);
-  s += __shfl_xor(s, 2, 16);
-  s += __shfl_xor(s, 4, 16);
-  s += __shfl_xor(s, 8, 16);
+  s += __uint_as_float(dpp_row<0xB1>(__float_as_uint(s)));
+  s += __uint_as_float(dpp_row<0x4E>(__float_as_uint(s)));
+  s += __uint_as_float(dpp_row<0x141>(__float_as_uint(s)));
+  s += __uint_as_float(dpp_row<0x140>(__float_as_uint(s)));
   return s;
 }
 
