@@ -385,7 +385,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the draft head runs on one "
-              "rank's vocabulary shard; a multi-GPU run is not part of this build.", file=sys.stderr)
+              "rank's vocabulary shard, and the cross-rank exchange of the per-row results is not "
+              "implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
