@@ -679,9 +679,14 @@ void coarse_resident_kernel(CoarseArgs A) {
 //     X_hi(q0..q3) X_mid(q0..q3) | X_lo(q0..q3) 0 0 0 0.
 //
 // Workgroup = 4 blocks of 64 columns.  From MT = 3 on, two waves share a
-// block, wave (block lb, part p) holding the row tiles [p ? MA : 0, ...), so
-// the two waves a SIMD runs (lb and lb + 4) hold MT tiles of accumulators
-// between them and hide each other's latency; below that, one wave per block.
+// block, wave (block lb, part p) holding column tiles 2p and 2p + 1 for all
+// MT row tiles, so each weight fragment is decoded once (a split by rows
+// would have both waves decode every fragment) and the two waves a SIMD runs
+// (lb and lb + 4) hide each other's latency; their scores meet in LDS for the
+// selection.  Below that, one wave per block holds all four column tiles.
+// Each group's scale update (one FMA per score) is issued during the next
+// group's MFMAs, component ks of every tile in k-slice ks, so the VALU work
+// runs beside the matrix cores instead of between two MFMA phases.
 //
 // Every global read of the main loop is a direct-to-LDS DMA.  Iteration j
 // (group j; j < 0: the prologue) issues, in this order and every time, even
@@ -705,8 +710,7 @@ constexpr int kZpEntries = 256;      // zero-point slab entries (16 bytes)
 template <int MT>
 struct BigShape {
   static constexpr int WPB = MT >= 3 ? 2 : 1;       // waves per block
-  static constexpr int MA = (MT + WPB - 1) / WPB;   // row tiles of part 0
-  static constexpr int MB = MT - MA;                // row tiles of part 1
+  static constexpr int NTW = 4 / WPB;               // column tiles per wave
   static constexpr int W = 4 * WPB;                 // waves per workgroup
   // x slabs and byte groups of codes requested ahead.  One or two row tiles
   // run four waves per workgroup: with one byte group of codes ahead (its
@@ -838,16 +842,193 @@ struct BigArgs {
   const u32x4* zslab;
 };
 
-// MFMA phase of one group (quarter Q) for MTW row tiles and the four column
-// tiles: cg = sum over the group's k of x 2^64 * v 2^(2Q-133).  On entry a[0]
-// holds k-slice 0's x fragments; each slice's MFMAs issue while the next
-// slice's fragments are read (with kNext the last slice reads slice 0 of the
-// next group, from xn).  A scheduling barrier per slice keeps one slice's decoded
-// operands live at a time.  xb, xn: this lane's fragment 0 (A row nn, k-slot
-// hh) in this group's slab and the next one's.
-template <int MTW, int Q, int MP, bool kNext>
-__device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MTW][4], u32x4 (&a)[2][MTW], const u32x4 (&raw)[2][4],
-                                              const u32x4 (&raw8)[2][4], const u32x4* xb, const u32x4* xn) {
+// The many-row kernel's score area in LDS holds, per (block, row), the 64
+// order-preserving keys of the row's coarse scores (f32_key of the score, -0
+// as +0; 0 for a column past N), rows kScStride words apart: a multiple of
+// four, so a row is read in 16-byte pieces, and 68 mod 64 = 4, so the rows of
+// sixteen neighbouring lists cover the 64 banks once.
+constexpr int kScStride = 68;
+
+// Compare-exchange of two keys, the larger first.
+__device__ __forceinline__ void cx_desc(uint32_t& a, uint32_t& b) {
+  const uint32_t hi = max(a, b);
+  b = min(a, b);
+  a = hi;
+}
+
+// Eight keys sorted descending: Batcher's odd-even merge sort (19 comparators).
+__device__ __forceinline__ void sort8_desc(uint32_t (&v)[8]) {
+  constexpr int P[19][2] = {{0, 1}, {2, 3}, {4, 5}, {6, 7}, {0, 2}, {1, 3}, {4, 6}, {5, 7}, {1, 2}, {5, 6},
+                            {0, 4}, {1, 5}, {2, 6}, {3, 7}, {2, 4}, {3, 5}, {1, 2}, {3, 4}, {5, 6}};
+#pragma unroll
+  for (int i = 0; i < 19; ++i) cx_desc(v[P[i][0]], v[P[i][1]]);
+}
+
+// A bitonic sequence of eight keys sorted descending (12 comparators).
+__device__ __forceinline__ void bitonic8_desc(uint32_t (&v)[8]) {
+#pragma unroll
+  for (int d = 4; d > 0; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & d) == 0) cx_desc(v[i], v[i + d]);
+}
+
+// Top-kcand lists (kcand <= 8) of every (block, row) pair of a many-row
+// workgroup, one list per thread, from the keys in LDS (row lb * MP + m).
+// Each key's low 6 bits are replaced by 63 - column, so the keys of a row are
+// distinct and, between scores whose keys differ above bit 5, order as (score
+// desc, column asc).  Eight sorted runs of eight (Batcher's network) are merged
+// into the eight largest (bitonic merge of the current eight with the next
+// run reversed), tracking the largest key left out.  That is the exact list
+// unless two of the eight, or the eighth and the best key left out, agree
+// above bit 5 (scores within 63 units in the last place of each other); such
+// a list is rebuilt with 64-bit keys (full key, then 63 - column) over the
+// columns whose keys reach the eighth's upper bits.
+// Lists go to the first min(W, 4) waves (one per SIMD) while they fit, else
+// to all W; wave w takes the consecutive lists w * cnt .. w * cnt + cnt - 1.
+template <int MP>
+__device__ __forceinline__ void lane_select8(const uint32_t* sk, const CoarseArgs& A, int b0, int wave, int W,
+                                             int lane) {
+  const int nl = 4 * A.M;
+  const int nw = nl <= 64 * min(W, 4) ? min(W, 4) : W;
+  const int cnt = (nl + nw - 1) / nw;
+  if (wave >= nw) return;
+  for (int j = lane; j < cnt; j += 64) {
+    const int q = wave * cnt + j;
+    if (q >= nl) break;
+    const int lb = q / A.M, m = q - lb * A.M;
+    const int b = b0 + lb;
+    if (b >= A.nblk) continue;
+    const uint32_t* row = sk + (lb * MP + m) * kScStride;
+    uint32_t key[64];
+#pragma unroll
+    for (int c4 = 0; c4 < 16; ++c4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(row + 4 * c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[4 * c4 + e] = (v[e] & ~63u) | (uint32_t)(63 - 4 * c4 - e);
+    }
+    uint32_t run[8], ninth = 0u;
+#pragma unroll
+    for (int c8 = 0; c8 < 8; ++c8) {
+      uint32_t ch[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ch[e] = key[8 * c8 + e];
+      sort8_desc(ch);
+      if (c8 == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) run[i] = ch[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t hi = max(run[i], ch[7 - i]);
+          ninth = max(ninth, min(run[i], ch[7 - i]));
+          run[i] = hi;
+        }
+        bitonic8_desc(run);
+      }
+    }
+    // exact unless upper parts agree where the order or the cut depends on them
+    const uint32_t p8 = run[7] >> 6;
+    bool exact = (ninth >> 6) < p8 || p8 == 0u;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) exact &= (run[i] >> 6) != (run[i + 1] >> 6) || (run[i + 1] >> 6) == 0u;
+    uint32_t slot[8];   // 63 - column, or 64 for an empty slot
+#pragma unroll
+    for (int i = 0; i < 8; ++i) slot[i] = run[i] >> 6 ? run[i] & 63u : 64u;
+    if (!exact) {
+      unsigned long long top[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) top[i] = 0ull;
+      for (int c = 0; c < 64; ++c) {
+        const uint32_t k = row[c];
+        if (k != 0u && (k >> 6) >= p8) {
+          unsigned long long t = ((unsigned long long)k << 32) | (uint32_t)(63 - c);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const unsigned long long u = top[i];
+            const bool gt = t > u;
+            top[i] = gt ? t : u;
+            t = gt ? u : t;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) slot[i] = top[i] ? (uint32_t)(top[i] & 63ull) : 64u;
+    }
+    float val[8];
+    int32_t id[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = slot[i] < 64u;
+      const int col = 63 - (int)(ok ? slot[i] : 63u);
+      val[i] = ok ? key_f32(row[col]) : -__builtin_inff();
+      id[i] = ok ? b * 64 + col : -1;
+    }
+    const size_t base = ((size_t)m * A.nblk + b) * A.kcand;
+    if (A.kcand == 8) {   // 32-byte aligned: the list is two 16-byte pieces
+      reinterpret_cast<f32x4*>(A.cand_val + base)[0] = f32x4{val[0], val[1], val[2], val[3]};
+      reinterpret_cast<f32x4*>(A.cand_val + base)[1] = f32x4{val[4], val[5], val[6], val[7]};
+      reinterpret_cast<u32x4*>(A.cand_id + base)[0] =
+          u32x4{(uint32_t)id[0], (uint32_t)id[1], (uint32_t)id[2], (uint32_t)id[3]};
+      reinterpret_cast<u32x4*>(A.cand_id + base)[1] =
+          u32x4{(uint32_t)id[4], (uint32_t)id[5], (uint32_t)id[6], (uint32_t)id[7]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < A.kcand) {
+          A.cand_val[base + i] = val[i];
+          A.cand_id[base + i] = id[i];
+        }
+    }
+  }
+}
+
+// Top-kcand lists (any kcand) of every (block, row) pair of a many-row
+// workgroup from the keys in LDS, by the 16-lane selection rounds: four lists
+// per wave and pass (list q = 4 (wave + W pass) + hh is row q % M of block
+// q / M), four passes at a time.
+template <int MP, int W>
+__device__ __forceinline__ void big_select(const uint32_t* sk, const CoarseArgs& A, int b0, int wave, int hh,
+                                           int nn) {
+  constexpr int NB = 4;
+  const int nl = 4 * A.M;
+  for (int p0 = 0; 4 * (wave + W * p0) < nl; p0 += NB) {   // wave-uniform
+    uint32_t k[NB][4], c[NB][4], kk[NB][4], kc[NB][4];
+    int lbq[NB], mq[NB];
+    bool live[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int q = 4 * (wave + W * (p0 + j)) + hh;
+      lbq[j] = q / A.M;
+      mq[j] = q - lbq[j] * A.M;
+      live[j] = q < nl && b0 + lbq[j] < A.nblk;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        k[j][t] = live[j] ? sk[(lbq[j] * MP + mq[j]) * kScStride + 16 * t + nn] : 0u;
+        c[j][t] = 16 * t + nn;
+      }
+    }
+    row16_select<NB>(k, c, A.kcand, nn, kk, kc);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (live[j]) write_list(A, mq[j], b0 + lbq[j], kk[j], kc[j], nn);
+  }
+}
+
+// MFMA phase of one group (quarter Q) for the MT row tiles and the wave's NTW
+// column tiles: cg = sum over the group's k of x 2^64 * v 2^(2Q-133).  On
+// entry a[0] holds k-slice 0's x fragments; each slice's MFMAs issue while the
+// next slice's fragments are read (with kNext the last slice reads slice 0 of
+// the next group, from xn).  Beside them runs the previous group's scale
+// update, acc += sp * cp, component ks of every tile in slice ks.  A
+// scheduling barrier per slice keeps one slice's decoded operands live at a
+// time.  xb, xn: this lane's fragment 0 (A row nn, k-slot hh) in this group's
+// slab and the next one's.
+template <int MT, int NTW, int Q, int MP, bool kNext>
+__device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MT][NTW], f32x4 (&acc)[MT][NTW],
+                                              const f32x4 (&cp)[MT][NTW], const float (&sp)[NTW],
+                                              u32x4 (&a)[2][MT], const u32x4 (&raw)[2][NTW],
+                                              const u32x4 (&raw8)[2][NTW], const u32x4* xb, const u32x4* xn) {
   constexpr uint32_t mask = 0x00030003u << (2 * Q);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -855,32 +1036,34 @@ __device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MTW][4], u32x4 (&a)[2]
     if (ks < 3) {
       const int f = (((ks + 1) >> 1) * 2 + ((ks + 1) & 1)) * 4;
 #pragma unroll
-      for (int i = 0; i < MTW; ++i) a[(ks + 1) & 1][i] = xb[f * MP + 16 * i];
+      for (int i = 0; i < MT; ++i) a[(ks + 1) & 1][i] = xb[f * MP + 16 * i];
     } else if (kNext) {
 #pragma unroll
-      for (int i = 0; i < MTW; ++i) a[0][i] = xn[16 * i];
+      for (int i = 0; i < MT; ++i) a[0][i] = xn[16 * i];
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NTW; ++t) {
       const bf16x8 bv = decode_quarter(raw[h][t][2 * e], raw8[h][t][2 * e], raw[h][t][2 * e + 1],
                                        raw8[h][t][2 * e + 1], mask);
 #pragma unroll
-      for (int i = 0; i < MTW; ++i)
+      for (int i = 0; i < MT; ++i) {
         cg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks & 1][i]), bv,
                                                            ks ? cg[i][t] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        acc[i][t][ks] = __builtin_fmaf(sp[t], cp[i][t][ks], acc[i][t][ks]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// One wave's share of a block: part P holds row tiles T0 .. T0 + MTW - 1 of
-// the MT, all four column tiles and the whole of K; then its rows of the
-// block's selection.
+// One wave's share of a block: part P holds column tiles P NTW .. P NTW +
+// NTW - 1 of the block, all MT row tiles and the whole of K; then the
+// block's selection (from LDS when two waves share the block).
 template <int MT, int P>
 __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem) {
   using S = BigShape<MT>;
   constexpr int MP = 16 * MT, XD = S::XD, NBUF = XD + 1, W = S::W, WPB = S::WPB, CD = S::CD;
-  constexpr int MTW = P ? S::MB : S::MA, T0 = P ? S::MA : 0;
+  constexpr int NTW = S::NTW, T0 = P * NTW;
   const CoarseArgs& A = BA.c;
   u32x4* xs = reinterpret_cast<u32x4*>(smem);   // [NBUF][16][MP]
   u32x4* cs = xs + NBUF * 16 * MP;              // [CD slots][4 blocks][9 chunks][64]
@@ -903,9 +1086,9 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   const uint32_t cs_l = lds_addr(cs + lb * kCodeChunks * 64);
 
   // Issue iteration j's ops.  Data past the end is replaced by a copy of the
-  // last slab or byte group into a slot nothing reads before the kernel ends;
-  // data before the start (prologue iterations ahead of X(0) or B(0)) by the
-  // bytes its slot is about to receive.
+  // last slab or byte group into a slot nothing reads before the main loop
+  // ends; data before the start (prologue iterations ahead of X(0) or B(0))
+  // by the bytes its slot is about to receive.
   auto issue = [&](int j) {
     int gx = j + XD;
     gx = gx < 0 ? gx + NBUF : gx;
@@ -938,39 +1121,45 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   wait_vm<big_wait<MT, P>(3)>();
   __syncthreads();
 
-  f32x4 acc[MTW][4];
+  // cgs[Q & 1] receives group Q's MFMA sums; the other set still holds the
+  // previous group's, scaled into acc (by sp) during group Q.
+  f32x4 acc[MT][NTW], cgs[2][MT][NTW];
+  float sp[NTW];
 #pragma unroll
-  for (int i = 0; i < MTW; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4* xl = xs + hh * MP + 16 * T0 + nn;   // this lane's fragment 0 in slab 0
-  u32x4 a[2][MTW];
+    for (int t = 0; t < NTW; ++t) acc[i][t] = cgs[1][i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < MTW; ++i) a[0][i] = xl[16 * i];
+  for (int t = 0; t < NTW; ++t) sp[t] = 0.f;
+  const u32x4* xl = xs + hh * MP + nn;   // this lane's fragment 0 in slab 0
+  u32x4 a[2][MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) a[0][i] = xl[16 * i];
 
   for (int G = 0; G < NG4; ++G) {
-    // byte group G's codes and scale pairs, into registers (the slot is
-    // refilled with byte group G + CD after this iteration's barrier)
+    // byte group G's codes and scale pairs of the wave's column tiles, into
+    // registers (the slot is refilled with byte group G + CD after this
+    // iteration's barrier)
     const u32x4* cw = cs + ((G % CD) * 4 + lb) * kCodeChunks * 64;
-    u32x4 raw[2][4], sz[4];
+    u32x4 raw[2][NTW], sz[NTW];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) raw[h][t] = cw[(h * 4 + t) * 64 + lane];
+      for (int t = 0; t < NTW; ++t) raw[h][t] = cw[(h * 4 + T0 + t) * 64 + lane];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sz[t] = cw[512 + t * 16 + nn];
+    for (int t = 0; t < NTW; ++t) sz[t] = cw[512 + (T0 + t) * 16 + nn];
 
     // zero-point part of byte group G
     {
-      u32x4 za[MTW];
+      u32x4 za[MT];
 #pragma unroll
-      for (int i = 0; i < MTW; ++i) za[i] = zs[(hh & 1) * MP + 16 * (T0 + i) + nn];
+      for (int i = 0; i < MT; ++i) za[i] = zs[(hh & 1) * MP + 16 * i + nn];
       if (hh >= 2) {
 #pragma unroll
-        for (int i = 0; i < MTW; ++i) za[i] = u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < MT; ++i) za[i] = u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < NTW; ++t) {
         uint32_t d[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) d[q] = __float_as_uint(lo_bf16(sz[t][q]) - hi_bf16(sz[t][q]));
@@ -978,34 +1167,30 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
         const uint32_t p23 = (d[2] >> 16) | (d[3] & 0xFFFF0000u);
         const u32x4 zb = u32x4{p01, p23, p01, p23};   // slots 8..15 meet zero x parts
 #pragma unroll
-        for (int i = 0; i < MTW; ++i)
+        for (int i = 0; i < MT; ++i)
           acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[i]),
                                                              __builtin_bit_cast(bf16x8, zb), acc[i][t], 0, 0, 0);
       }
     }
 
-    u32x4 raw8[2][4];
+    u32x4 raw8[2][NTW];
     shift_codes(raw, raw8);
     auto group = [&](auto qc) {
       constexpr int Q = decltype(qc)::value;
       const int g = 4 * G + Q;
       issue(g);
-      f32x4 cg[MTW][4];
-      big_group_mma<MTW, Q, MP, S::XW == 2>(cg, a, raw, raw8, xl + (g % NBUF) * 16 * MP,
-                                            xl + ((g + 1) % NBUF) * 16 * MP);
+      float sq[NTW];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float Sq = quarter_scale(lo_bf16(sz[t][Q]), Q);
+      for (int t = 0; t < NTW; ++t) sq[t] = quarter_scale(lo_bf16(sz[t][Q]), Q);
+      big_group_mma<MT, NTW, Q, MP, S::XW == 2>(cgs[Q & 1], acc, cgs[(Q + 1) & 1], sp, a, raw, raw8,
+                                                xl + (g % NBUF) * 16 * MP, xl + ((g + 1) % NBUF) * 16 * MP);
 #pragma unroll
-        for (int i = 0; i < MTW; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][t][r] = __builtin_fmaf(Sq, cg[i][t][r], acc[i][t][r]);
-      }
+      for (int t = 0; t < NTW; ++t) sp[t] = sq[t];
       wait_vm<big_wait<MT, P>(Q)>();
       __syncthreads();
       if constexpr (S::XW == 1) {   // the next group's first fragments, now visible
 #pragma unroll
-        for (int i = 0; i < MTW; ++i) a[0][i] = xl[((g + 1) % NBUF) * 16 * MP + 16 * i];
+        for (int i = 0; i < MT; ++i) a[0][i] = xl[((g + 1) % NBUF) * 16 * MP + 16 * i];
       }
     };
     group(std::integral_constant<int, 0>{});
@@ -1013,16 +1198,47 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
     group(std::integral_constant<int, 2>{});
     group(std::integral_constant<int, 3>{});
   }
+  // the last group's scale update
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][t][r] = __builtin_fmaf(sp[t], cgs[1][i][t][r], acc[i][t][r]);
   wait_vm<0>();
-  if (!blk_ok) return;
-  block_select<MTW, 4>([&](int i, int r, int t) { return acc[i][t][r]; }, A, b, hh, nn, 0, 1, 16 * T0);
+  if constexpr (WPB == 1) {   // one wave holds the whole block: its lists from registers
+    if (!blk_ok) return;
+    block_select<MT, 4>([&](int i, int r, int t) { return acc[i][t][r]; }, A, b, hh, nn);
+    return;
+  }
+  // every wave's DMA writes have landed and every wave is done with the ring:
+  // its LDS now takes the workgroup's score keys (and the optional full rows
+  // are written from the accumulators)
+  __syncthreads();
+  uint32_t* sk = reinterpret_cast<uint32_t*>(smem);
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int col = 16 * (T0 + t) + nn, n = 64 * b + col;
+    const bool n_ok = blk_ok && n < A.N;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * i + 4 * hh + r;
+        sk[(lb * MP + row) * kScStride + col] = n_ok ? f32_key(acc[i][t][r] + 0.0f) : 0u;   // -0 as +0
+        if (A.coarse_out && n_ok && row < A.M) A.coarse_out[(size_t)row * A.N + n] = acc[i][t][r];
+      }
+  }
+  __syncthreads();
+  if (A.kcand <= 8) lane_select8<MP>(sk, A, blockIdx.x * 4, wave, W, lane);
+  else big_select<MP, W>(sk, A, blockIdx.x * 4, wave, hh, nn);
 }
 
 template <int MT>
 __global__ __launch_bounds__(64 * BigShape<MT>::W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void coarse_mfma_kernel(BigArgs BA) {
   extern __shared__ __align__(16) unsigned char smem[];
-  if constexpr (BigShape<MT>::MB > 0) {
+  if constexpr (BigShape<MT>::WPB == 2) {
     if (threadIdx.x >= 256) {
       big_wave<MT, 1>(BA, smem);
       return;
@@ -1621,9 +1837,12 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
   for (int jj = 0; jj < JW; ++jj)
     mo[jj] = lane + 64 * (JW * wave + jj) < nblk ? (uint32_t)(slot_key(__uint_as_float(mo[jj]), 0) >> 32) : 0u;
   auto lower = [&](int j) { return 0xFFFFFFFFu - (uint32_t)((lane + 64 * j) * kcand); };
-  auto at_least = [&](int jj, uint32_t to, uint32_t tl) {   // key of (lane, JW wave + jj) >= (to, tl); to >= 1
+  // key of (lane, JW wave + jj) >= (to, tl), for a block that exists and has
+  // a maximum (o != 0: so at most R blocks qualify against an exact T, even
+  // where fewer than R blocks have a maximum and T is 0)
+  auto at_least = [&](int jj, uint32_t to, uint32_t tl) {
     const uint32_t o = mo[jj];
-    return (o > to) | ((o == to) & (lower(JW * wave + jj) >= tl));
+    return (o != 0u) & ((o > to) | ((o == to) & (lower(JW * wave + jj) >= tl)));
   };
   uint32_t* so = reinterpret_cast<uint32_t*>(sh.keys);   // every maximum, for the exact fallback
   uint32_t bw = 0u;
@@ -1694,8 +1913,9 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
   __syncthreads();
   if (tid == 0) sh.nq = sh.qcur;
   __syncthreads();
-  {   // the survivors, gathered by the whole workgroup (their order does not matter)
-    const int items = sh.nq * kcand;   // <= DH_MAX_R
+  for (int i = tid; i < R; i += NTHR) sh.list[i] = 0ull;   // a rank no survivor takes stays empty
+  if (sh.nq > 0) {   // the survivors, gathered by the whole workgroup (their order does not matter)
+    const int items = sh.nq * kcand;   // <= DH_MAX_R; no block qualifies only where none has a maximum
     const unsigned long long T = sh.T;
     float v[kGather];
     int id[kGather], slot[kGather];
@@ -1735,11 +1955,14 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
 
   // the exact logit of rank r: this wave reads W[id] and x[m] once, all loads in flight
   const int r = NW * part + wave;
+  // An empty rank (key 0: fewer survivors than R, which candidates written
+  // by the coarse pass never leave) is (-1, -inf) and reads no row.
   if (r < R) {
-    const uint32_t id = key_id(sh.list[r]);
-    const float sum = wave_dot<kKind>(A.src, id, A.x + (size_t)m * K, K, lane);
+    const unsigned long long key = sh.list[r];
+    const uint32_t id = key_id(key);
+    const float sum = key ? wave_dot<kKind>(A.src, id, A.x + (size_t)m * K, K, lane) : -__builtin_inff();
     if (lane == 0) {
-      store_dev(A.rr_id + (size_t)m * R + r, (int32_t)id);
+      store_dev(A.rr_id + (size_t)m * R + r, key ? (int32_t)id : -1);
       store_dev(A.rr_val + (size_t)m * R + r, sum);
     }
   }
@@ -1887,6 +2110,7 @@ template <int MT>
 hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD, BigShape<MT>::CD);
   static_assert(lds <= kMaxLds, "LDS budget of the many-row kernel");
+  static_assert((size_t)4 * 16 * MT * kScStride * sizeof(float) <= lds, "the score area reuses the ring's LDS");
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&coarse_mfma_kernel<MT>),

@@ -99,6 +99,12 @@ CASES = [
     (4, 19968, 300, 8, 32),
     (8, 8704, 500, 8, 32),
     (8, 9216, 500, 8, 32),
+    # the many-row kernel's selections: one list per thread (kcand <= 8) and
+    # the 16-lane rounds for longer lists, with one and two waves per block
+    (48, 1024, 5000, 1, 16),
+    (20, 512, 3000, 16, 64),
+    (40, 1024, 2000, 12, 32),
+    (72, 512, 1000, 64, 100),
 ]
 
 
@@ -501,6 +507,35 @@ def test_nvfp4_forward_matches_staged_calls(dev):
     torch.cuda.synchronize()
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+def test_rerank_degenerate_candidates(dev):
+    """The block-maximum rerank on candidate arrays no coarse call writes:
+    every slot the same (value 0, id 0), so the survivors share one key and
+    ranks 1.. stay empty; and every slot padding (-inf, -1), so no block has
+    a maximum.  Empty ranks come back as (-1, -inf) and read no row."""
+    m, k, n, kcand, r = 3, 1024, 20000, 8, 32
+    w = workload.gen_weight(n, k, seed=4300)
+    x = workload.gen_x(m, k, seed=4301)
+    nblk = (n + 63) // 64
+    wt, xt = _to_dev(w, dev), _to_dev(x, dev)
+    exact0 = oracle.bf16.to_f64(x) @ oracle.bf16.to_f64(w[0])
+    for name, val, idv in (("duplicates", 0.0, 0), ("padding", -np.inf, -1)):
+        _log(f"degenerate candidates: {name}")
+        cv = torch.full((m, nblk * kcand), val, dtype=torch.float32, device=dev)
+        ci = torch.full((m, nblk * kcand), idv, dtype=torch.int32, device=dev)
+        got_id, got_val = B.draft_head_rerank(xt, wt, cv, ci, R=r)
+        out_id, out_val = B.draft_head_argmax(got_id, got_val)
+        torch.cuda.synchronize()
+        gi, gv = got_id.cpu().numpy(), got_val.cpu().numpy().astype(np.float64)
+        if name == "duplicates":
+            assert np.all(gi[:, 0] == 0) and np.all(gi[:, 1:] == -1)
+            assert np.all(np.abs(gv[:, 0] - exact0) <= 2e-3 * np.abs(exact0) + 1e-5)
+            assert np.all(gv[:, 1:] == -np.inf)
+            assert np.array_equal(out_id.cpu().numpy(), np.zeros(m, dtype=np.int32))
+        else:
+            assert np.all(gi == -1) and np.all(gv == -np.inf)
+            assert np.all(out_id.cpu().numpy() == -1)
 
 
 @pytest.mark.parametrize("k,n,r", [(256, 3000, 32), (768, 3000, 32), (2304, 200, 16)])
