@@ -700,9 +700,12 @@ void coarse_resident_kernel(CoarseArgs A) {
 // byte group, C and B of the next one, then a barrier.  With XW = 2 the
 // next group's first x fragments are read before that barrier.  The number
 // of ops issued after any op depends only on j mod 4, so every wait count is
-// a constant (big_wait).  Completions are counted in issue order; with this
-// order no wait for an x slab (an L2 hit) waits for code bytes still on their
-// way from HBM before they are needed.
+// a constant (big_wait).  Completions are counted in issue order, so with two
+// waves per block the x slabs and the codes are issued by different waves
+// (BigShape::nx, nc): a wait for an x slab (an L2 hit) never waits for code
+// bytes still on their way from HBM, and the codes have CD byte groups to
+// arrive.  With one wave per block (one or two row tiles) both streams share
+// the wave's counter, and x runs XD = 3..6 groups ahead.
 constexpr int kMaxMT = 5;            // 16-row tiles per launch (80 rows)
 constexpr int kCodeChunks = 9;       // 1 KB chunks of one block's byte group: 8 code + 1 pair
 constexpr int kZpEntries = 256;      // zero-point slab entries (16 bytes)
@@ -722,9 +725,14 @@ struct BigShape {
   static constexpr int CD = MT <= 2 ? 1 : 2;
   static constexpr int XW = XD >= 4 ? 2 : 1;        // slab completed XW groups ahead
   static constexpr int PRO = XD > 4 * CD - 1 ? XD : 4 * CD - 1;   // prologue iterations
-  // DMA ops per iteration of a wave of part p
-  static constexpr int nx(int p) { return (4 * MT - 4 * p + W - 1) / W; }
-  static constexpr int nc(int p) { return (kCodeChunks - p + WPB - 1) / WPB; }
+  // DMA ops per iteration of a wave of part p.  With two waves per block the
+  // parts issue different streams: part 1 the x slabs (chunks lb + 4k), part
+  // 0 its block's codes and scale pairs and the zero-point slab.  A wave's
+  // vmcnt completes in issue order, so a wait for an x slab (an L2 read)
+  // never waits behind code bytes on their way from HBM, and the codes get
+  // their full distance (CD byte groups) before anyone waits for them.
+  static constexpr int nx(int p) { return WPB == 1 || p == 1 ? MT : 0; }
+  static constexpr int nc(int p) { return p == 0 ? kCodeChunks : 0; }
   static constexpr int nb(int p) { return p == 0 ? 1 : 0; }
 };
 
@@ -759,7 +767,7 @@ constexpr int big_wait(int Q) {
     if (S::nc(P)) take(after(Q + 2 - 4 * S::CD, S::nb(P)));
     if (S::nb(P)) take(after(Q - 2, 0));
   }
-  return best;
+  return best < 63 ? best : 63;   // 63: nothing this iteration must complete
 }
 
 // LDS byte address of a pointer into __shared__ memory.
@@ -1096,8 +1104,8 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
     gx = gx < NGRP ? gx : NGRP - 1;
     const u32x4* xsrc = BA.xslab + (size_t)gx * 256 * MT;
 #pragma unroll
-    for (int k = 0; k < S::nx(P); ++k) {   // chunks wave + W k, all below 4 MT
-      const int c = wave + W * k;
+    for (int k = 0; k < S::nx(P); ++k) {   // chunks lb + 4 k, all below 4 MT
+      const int c = lb + 4 * k;
       dma16(voff, xsrc + c * 64, xs_l + xslot * 4096 * MT + c * 1024);
     }
     if ((j & 3) == 1) {
@@ -1106,7 +1114,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       GC = GC < NG4 ? GC : NG4 - 1;
 #pragma unroll
       for (int k = 0; k < S::nc(P); ++k) {
-        const int c = P + WPB * k;
+        const int c = k;
         dma16_nt(voff, c < 8 ? tp + (GC * 8 + c) * 64 : pp + GC * 64,
               cs_l + cslot * 4 * kCodeChunks * 1024 + c * 1024);
       }
