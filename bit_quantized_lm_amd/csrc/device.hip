@@ -683,7 +683,8 @@ void coarse_resident_kernel(CoarseArgs A) {
 // MT row tiles, so each weight fragment is decoded once (a split by rows
 // would have both waves decode every fragment) and the two waves a SIMD runs
 // (lb and lb + 4) hide each other's latency; their scores meet in LDS for the
-// selection.  Below that, one wave per block holds all four column tiles.
+// selection.  Below that, one wave per block holds all four column tiles and
+// two workgroups share a CU.
 // Each group's scale update (one FMA per score) is issued during the next
 // group's MFMAs, component ks of every tile in k-slice ks, so the VALU work
 // runs beside the matrix cores instead of between two MFMA phases.
@@ -694,8 +695,8 @@ void coarse_resident_kernel(CoarseArgs A) {
 // free, or that later receives the same bytes):
 //   X(j + XD)  the wave's chunks of that group's x slab               NX ops
 //   at j = 4G + 1 (after every wave read byte group G's codes):
+//   B(G + 1)   its chunks of byte group G + 1's zero-point slab      NB ops
 //   C(G + CD)  the wave's chunks of that byte group's codes/pairs     NC ops
-//   B(G + 1)   its chunk of byte group G + 1's zero-point slab       NB ops
 // and ends with one vmcnt wait that completes X(j + XW) and, at the end of a
 // byte group, C and B of the next one, then a barrier.  With XW = 2 the
 // next group's first x fragments are read before that barrier.  The number
@@ -713,31 +714,35 @@ constexpr int kZpEntries = 256;      // zero-point slab entries (16 bytes)
 template <int MT>
 struct BigShape {
   static constexpr int WPB = MT >= 3 ? 2 : 1;       // waves per block
+  static constexpr int BPW = 4;                     // blocks per workgroup
   static constexpr int NTW = 4 / WPB;               // column tiles per wave
-  static constexpr int W = 4 * WPB;                 // waves per workgroup
+  static constexpr int W = BPW * WPB;               // waves per workgroup
   // x slabs and byte groups of codes requested ahead.  One or two row tiles
   // run four waves per workgroup: with one byte group of codes ahead (its
   // slot refilled after the first group of the byte group has read it) and,
   // at two tiles, three slabs, two workgroups fit a CU's LDS, so each SIMD
   // runs two waves instead of one (M = 16: 59.9 -> 43.7 us, M = 32: 76.6 ->
-  // 58.2 us).  From three tiles on, two waves per block already fill that.
+  // 58.2 us).  From three tiles on, two waves per block already fill that
+  // (two workgroups of two blocks per CU, with one x slab ahead, measured
+  // 3-7 % slower at M = 48..72).
   static constexpr int XD = MT >= 4 ? 3 : MT == 3 ? 5 : MT == 2 ? 3 : 6;
   static constexpr int CD = MT <= 2 ? 1 : 2;
   static constexpr int XW = XD >= 4 ? 2 : 1;        // slab completed XW groups ahead
   static constexpr int PRO = XD > 4 * CD - 1 ? XD : 4 * CD - 1;   // prologue iterations
   // DMA ops per iteration of a wave of part p.  With two waves per block the
-  // parts issue different streams: part 1 the x slabs (chunks lb + 4k), part
-  // 0 its block's codes and scale pairs and the zero-point slab.  A wave's
-  // vmcnt completes in issue order, so a wait for an x slab (an L2 read)
-  // never waits behind code bytes on their way from HBM, and the codes get
-  // their full distance (CD byte groups) before anyone waits for them.
-  static constexpr int nx(int p) { return WPB == 1 || p == 1 ? MT : 0; }
+  // parts issue different streams: part 1 the x slabs (chunks lb + BPW k),
+  // part 0 its block's codes and scale pairs and its share of the zero-point
+  // slab.  A wave's vmcnt completes in issue order, so a wait for an x slab
+  // (an L2 read) never waits behind code bytes on their way from HBM, and the
+  // codes get their full distance (CD byte groups) before anyone waits for
+  // them.  With one wave per block every wave issues both.
+  static constexpr int nx(int p) { return WPB == 1 || p == 1 ? 4 * MT / BPW : 0; }
   static constexpr int nc(int p) { return p == 0 ? kCodeChunks : 0; }
-  static constexpr int nb(int p) { return p == 0 ? 1 : 0; }
+  static constexpr int nb(int p) { return p == 0 ? 4 / BPW : 0; }
 };
 
-constexpr size_t big_lds_bytes(int MT, int XD, int CD) {
-  return (size_t)(XD + 1) * 4096 * MT + (size_t)CD * 4 * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
+constexpr size_t big_lds_bytes(int MT, int XD, int CD, int BPW) {
+  return (size_t)(XD + 1) * 4096 * MT + (size_t)CD * BPW * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
 }
 
 // Workspace of one launch with MT row tiles: x slabs, then zero-point slabs.
@@ -746,8 +751,8 @@ size_t big_workspace_bytes(int MT, int K) {
 }
 
 // Ops a wave of part P may leave outstanding at the end of an iteration with
-// j mod 4 == Q: those issued after X(j + XW) and, for Q == 3, after the C and
-// B of the next byte group (issued at j + 2 - 4 CD and j - 2).  The
+// j mod 4 == Q: those issued after X(j + XW) and, for Q == 3, after the B and
+// C of the next byte group (issued at j - 2 and j + 2 - 4 CD).  The
 // prologue's final wait (X(XW - 1), C(0), B(0)) is the Q == 3 case.
 template <int MT, int P>
 constexpr int big_wait(int Q) {
@@ -764,8 +769,8 @@ constexpr int big_wait(int Q) {
   auto take = [&](int n) { best = n < best ? n : best; };
   if (S::nx(P)) take(after(Q + S::XW - S::XD, cb(Q + S::XW - S::XD)));
   if (Q == 3) {
-    if (S::nc(P)) take(after(Q + 2 - 4 * S::CD, S::nb(P)));
-    if (S::nb(P)) take(after(Q - 2, 0));
+    if (S::nc(P)) take(after(Q + 2 - 4 * S::CD, 0));   // C last in its iteration
+    if (S::nb(P)) take(after(Q - 2, S::nc(P)));        // B followed by that iteration's C
   }
   return best < 63 ? best : 63;   // 63: nothing this iteration must complete
 }
@@ -894,10 +899,10 @@ __device__ __forceinline__ void bitonic8_desc(uint32_t (&v)[8]) {
 // columns whose keys reach the eighth's upper bits.
 // Lists go to the first min(W, 4) waves (one per SIMD) while they fit, else
 // to all W; wave w takes the consecutive lists w * cnt .. w * cnt + cnt - 1.
-template <int MP>
+template <int MP, int BPW>
 __device__ __forceinline__ void lane_select8(const uint32_t* sk, const CoarseArgs& A, int b0, int wave, int W,
                                              int lane) {
-  const int nl = 4 * A.M;
+  const int nl = BPW * A.M;
   const int nw = nl <= 64 * min(W, 4) ? min(W, 4) : W;
   const int cnt = (nl + nw - 1) / nw;
   if (wave >= nw) return;
@@ -995,11 +1000,11 @@ __device__ __forceinline__ void lane_select8(const uint32_t* sk, const CoarseArg
 // workgroup from the keys in LDS, by the 16-lane selection rounds: four lists
 // per wave and pass (list q = 4 (wave + W pass) + hh is row q % M of block
 // q / M), four passes at a time.
-template <int MP, int W>
+template <int MP, int W, int BPW>
 __device__ __forceinline__ void big_select(const uint32_t* sk, const CoarseArgs& A, int b0, int wave, int hh,
                                            int nn) {
   constexpr int NB = 4;
-  const int nl = 4 * A.M;
+  const int nl = BPW * A.M;
   for (int p0 = 0; 4 * (wave + W * p0) < nl; p0 += NB) {   // wave-uniform
     uint32_t k[NB][4], c[NB][4], kk[NB][4], kc[NB][4];
     int lbq[NB], mq[NB];
@@ -1070,18 +1075,18 @@ __device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MT][NTW], f32x4 (&acc)
 template <int MT, int P>
 __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem) {
   using S = BigShape<MT>;
-  constexpr int MP = 16 * MT, XD = S::XD, NBUF = XD + 1, W = S::W, WPB = S::WPB, CD = S::CD;
+  constexpr int MP = 16 * MT, XD = S::XD, NBUF = XD + 1, W = S::W, WPB = S::WPB, CD = S::CD, BPW = S::BPW;
   constexpr int NTW = S::NTW, T0 = P * NTW;
   const CoarseArgs& A = BA.c;
-  u32x4* xs = reinterpret_cast<u32x4*>(smem);   // [NBUF][16][MP]
-  u32x4* cs = xs + NBUF * 16 * MP;              // [CD slots][4 blocks][9 chunks][64]
-  u32x4* zs = cs + CD * 4 * kCodeChunks * 64;   // [256]
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);     // [NBUF][16][MP]
+  u32x4* cs = xs + NBUF * 16 * MP;                // [CD slots][BPW blocks][9 chunks][64]
+  u32x4* zs = cs + CD * BPW * kCodeChunks * 64;   // [256]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 4, nn = lane & 15;
-  const int lb = wave & 3;
-  const int b = blockIdx.x * 4 + lb;
+  const int lb = wave & (BPW - 1);
+  const int b = blockIdx.x * BPW + lb;
   const bool blk_ok = b < A.nblk;
   const int NG4 = A.K >> 9, NGRP = A.K >> 7;
   if constexpr (P == 0) zero_counters(A);
@@ -1090,7 +1095,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
   const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64;
   const uint32_t voff = lane * 16;
-  const uint32_t xs_l = lds_addr(xs), zs_l = lds_addr(zs + wave * 64);
+  const uint32_t xs_l = lds_addr(xs), zs_l = lds_addr(zs);
   const uint32_t cs_l = lds_addr(cs + lb * kCodeChunks * 64);
 
   // Issue iteration j's ops.  Data past the end is replaced by a copy of the
@@ -1099,16 +1104,25 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   // by the bytes its slot is about to receive.
   auto issue = [&](int j) {
     int gx = j + XD;
-    gx = gx < 0 ? gx + NBUF : gx;
+    if (gx < 0) gx = (gx % NBUF + NBUF) % NBUF;   // a slot's first slab, fetched early
     const uint32_t xslot = (uint32_t)(gx % NBUF);
     gx = gx < NGRP ? gx : NGRP - 1;
     const u32x4* xsrc = BA.xslab + (size_t)gx * 256 * MT;
 #pragma unroll
-    for (int k = 0; k < S::nx(P); ++k) {   // chunks lb + 4 k, all below 4 MT
-      const int c = lb + 4 * k;
+    for (int k = 0; k < S::nx(P); ++k) {   // chunks lb + BPW k, all below 4 MT
+      const int c = lb + BPW * k;
       dma16(voff, xsrc + c * 64, xs_l + xslot * 4096 * MT + c * 1024);
     }
     if ((j & 3) == 1) {
+      // the zero-point slab first: it is waited for two groups later, the
+      // codes (issued after it, so not waited for with it) CD byte groups later
+      int GB = (j >> 2) + 1;
+      GB = GB < 0 ? 0 : GB < NG4 ? GB : NG4 - 1;
+#pragma unroll
+      for (int k = 0; k < S::nb(P); ++k) {   // zero-point chunks lb nb + k of four
+        const int c = lb * S::nb(P) + k;
+        dma16(voff, BA.zslab + (size_t)GB * kZpEntries + c * 64, zs_l + c * 1024);
+      }
       int GC = (j >> 2) + CD;   // never negative: the prologue starts at 1 - 4 CD or before
       const uint32_t cslot = (uint32_t)(GC % CD);
       GC = GC < NG4 ? GC : NG4 - 1;
@@ -1116,11 +1130,8 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       for (int k = 0; k < S::nc(P); ++k) {
         const int c = k;
         dma16_nt(voff, c < 8 ? tp + (GC * 8 + c) * 64 : pp + GC * 64,
-              cs_l + cslot * 4 * kCodeChunks * 1024 + c * 1024);
+              cs_l + cslot * BPW * kCodeChunks * 1024 + c * 1024);
       }
-      int GB = (j >> 2) + 1;
-      GB = GB < 0 ? 0 : GB < NG4 ? GB : NG4 - 1;
-      if constexpr (S::nb(P) > 0) dma16(voff, BA.zslab + (size_t)GB * kZpEntries + lb * 64, zs_l);
     }
   };
 
@@ -1148,7 +1159,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
     // byte group G's codes and scale pairs of the wave's column tiles, into
     // registers (the slot is refilled with byte group G + CD after this
     // iteration's barrier)
-    const u32x4* cw = cs + ((G % CD) * 4 + lb) * kCodeChunks * 64;
+    const u32x4* cw = cs + ((G % CD) * BPW + lb) * kCodeChunks * 64;
     u32x4 raw[2][NTW], sz[NTW];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -1238,8 +1249,8 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       }
   }
   __syncthreads();
-  if (A.kcand <= 8) lane_select8<MP>(sk, A, blockIdx.x * 4, wave, W, lane);
-  else big_select<MP, W>(sk, A, blockIdx.x * 4, wave, hh, nn);
+  if (A.kcand <= 8) lane_select8<MP, BPW>(sk, A, blockIdx.x * BPW, wave, W, lane);
+  else big_select<MP, W, BPW>(sk, A, blockIdx.x * BPW, wave, hh, nn);
 }
 
 template <int MT>
@@ -1247,7 +1258,7 @@ __global__ __launch_bounds__(64 * BigShape<MT>::W) __attribute__((amdgpu_waves_p
 void coarse_mfma_kernel(BigArgs BA) {
   extern __shared__ __align__(16) unsigned char smem[];
   if constexpr (BigShape<MT>::WPB == 2) {
-    if (threadIdx.x >= 256) {
+    if (threadIdx.x >= 64 * BigShape<MT>::BPW) {
       big_wave<MT, 1>(BA, smem);
       return;
     }
@@ -2116,9 +2127,11 @@ hipError_t launch_resident(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hi
 
 template <int MT>
 hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD, BigShape<MT>::CD);
+  constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD, BigShape<MT>::CD, BigShape<MT>::BPW);
   static_assert(lds <= kMaxLds, "LDS budget of the many-row kernel");
-  static_assert((size_t)4 * 16 * MT * kScStride * sizeof(float) <= lds, "the score area reuses the ring's LDS");
+  static_assert((size_t)BigShape<MT>::BPW * 16 * MT * kScStride * sizeof(float) <= lds,
+                "the score area reuses the ring's LDS");
+  static_assert(lds <= kMaxLds, "LDS of one workgroup");
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&coarse_mfma_kernel<MT>),
@@ -2126,7 +2139,7 @@ hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((A.c.nblk + 3) / 4);
+  dim3 grid((A.c.nblk + BigShape<MT>::BPW - 1) / BigShape<MT>::BPW);
   hipExtLaunchKernelGGL(coarse_mfma_kernel<MT>, grid, dim3(64 * BigShape<MT>::W), lds, s, e0, e1, 0, A);
   return hipGetLastError();
 }
