@@ -145,6 +145,25 @@ def test_zero_row_many_survivors(dev):
     assert int(got["out_id"][1]) == 0
 
 
+@pytest.mark.parametrize("m", [40, 72])
+def test_many_row_ties(dev, m):
+    """The many-row kernel's per-thread lists over exact ties: duplicated head
+    rows give bit-identical coarse scores (keys equal above bit 5, so the list
+    is rebuilt from full keys and columns; ties go to the lower column), and
+    zero x rows tie every column of every block."""
+    n, k = 3000, 1024
+    w = workload.gen_weight(n, k, seed=4400 + m)
+    for b in range(n // 64):
+        w[64 * b + 1] = w[64 * b]
+        w[64 * b + 7] = w[64 * b + 3]
+        w[64 * b + 8] = w[64 * b + 3]
+    x = workload.gen_x(m, k, seed=4401 + m)
+    x[5] = 0
+    x[m - 1] = 0
+    _, got, _ = check_case(dev, m, k, n, 8, 32, seed=0, x=x, w=w)
+    assert [int(v) for v in got["rr_id"][5][:8]] == [0, 1, 2, 3, 4, 5, 6, 7]
+
+
 def test_lossless_weights_give_exact_argmax(dev):
     rng = np.random.default_rng(23)
     n, k = 1000, 1024
