@@ -725,10 +725,15 @@ struct BigShape {
   // 58.2 us).  From three tiles on, two waves per block already fill that
   // (two workgroups of two blocks per CU, with one x slab ahead, measured
   // 3-7 % slower at M = 48..72).
-  static constexpr int XD = MT >= 4 ? 3 : MT == 3 ? 5 : MT == 2 ? 3 : 6;
+  // From four row tiles on a stage (the unit of the x ring, of the DMA
+  // schedule and of the barriers) is two groups, so the eight waves meet at
+  // half as many barriers; below, a stage is one group.  XD and XW count stages.
+  static constexpr int GPS = MT >= 4 ? 2 : 1;       // groups per stage
+  static constexpr int SPB = 4 / GPS;               // stages per byte group
+  static constexpr int XD = MT >= 4 ? 1 : MT == 3 ? 5 : MT == 2 ? 3 : 6;
   static constexpr int CD = MT <= 2 ? 1 : 2;
-  static constexpr int XW = XD >= 4 ? 2 : 1;        // slab completed XW groups ahead
-  static constexpr int PRO = XD > 4 * CD - 1 ? XD : 4 * CD - 1;   // prologue iterations
+  static constexpr int XW = XD >= 4 ? 2 : 1;        // stage's slabs completed XW stages ahead
+  static constexpr int PRO = XD > SPB * CD - 1 ? XD : SPB * CD - 1;   // prologue stages
   // DMA ops per iteration of a wave of part p.  With two waves per block the
   // parts issue different streams: part 1 the x slabs (chunks lb + BPW k),
   // part 0 its block's codes and scale pairs and its share of the zero-point
@@ -736,13 +741,13 @@ struct BigShape {
   // (an L2 read) never waits behind code bytes on their way from HBM, and the
   // codes get their full distance (CD byte groups) before anyone waits for
   // them.  With one wave per block every wave issues both.
-  static constexpr int nx(int p) { return WPB == 1 || p == 1 ? 4 * MT / BPW : 0; }
+  static constexpr int nx(int p) { return WPB == 1 || p == 1 ? GPS * 4 * MT / BPW : 0; }
   static constexpr int nc(int p) { return p == 0 ? kCodeChunks : 0; }
   static constexpr int nb(int p) { return p == 0 ? 4 / BPW : 0; }
 };
 
-constexpr size_t big_lds_bytes(int MT, int XD, int CD, int BPW) {
-  return (size_t)(XD + 1) * 4096 * MT + (size_t)CD * BPW * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
+constexpr size_t big_lds_bytes(int MT, int XD, int CD, int BPW, int GPS) {
+  return (size_t)(XD + 1) * GPS * 4096 * MT + (size_t)CD * BPW * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
 }
 
 // Workspace of one launch with MT row tiles: x slabs, then zero-point slabs.
@@ -750,15 +755,16 @@ size_t big_workspace_bytes(int MT, int K) {
   return (size_t)(K / DH_GROUP) * 4096 * MT + (size_t)(K / 512) * kZpEntries * 16;
 }
 
-// Ops a wave of part P may leave outstanding at the end of an iteration with
-// j mod 4 == Q: those issued after X(j + XW) and, for Q == 3, after the B and
-// C of the next byte group (issued at j - 2 and j + 2 - 4 CD).  The
-// prologue's final wait (X(XW - 1), C(0), B(0)) is the Q == 3 case.
+// Ops a wave of part P may leave outstanding at the end of a stage with
+// j mod SPB == Q: those issued after X(j + XW) and, for the byte group's last
+// stage (Q == SPB - 1), after the B and C of the next byte group (issued at
+// j + 2 - SPB and j + 2 - SPB CD).  The prologue's final wait (X(XW - 1),
+// C(0), B(0)) is the Q == SPB - 1 case.
 template <int MT, int P>
 constexpr int big_wait(int Q) {
   using S = BigShape<MT>;
-  auto m4 = [](int j) { return ((j % 4) + 4) % 4; };
-  auto cb = [&](int j) { return m4(j) == 1 ? S::nc(P) + S::nb(P) : 0; };
+  auto m4 = [](int j) { return ((j % S::SPB) + S::SPB) % S::SPB; };
+  auto cb = [&](int j) { return m4(j) == 1 % S::SPB ? S::nc(P) + S::nb(P) : 0; };
   auto ops = [&](int j) { return S::nx(P) + cb(j); };
   auto after = [&](int j0, int in_iter) {   // ops after one issued in iteration j0
     int n = in_iter;
@@ -768,9 +774,9 @@ constexpr int big_wait(int Q) {
   int best = 1 << 20;
   auto take = [&](int n) { best = n < best ? n : best; };
   if (S::nx(P)) take(after(Q + S::XW - S::XD, cb(Q + S::XW - S::XD)));
-  if (Q == 3) {
-    if (S::nc(P)) take(after(Q + 2 - 4 * S::CD, 0));   // C last in its iteration
-    if (S::nb(P)) take(after(Q - 2, S::nc(P)));        // B followed by that iteration's C
+  if (Q == S::SPB - 1) {
+    if (S::nc(P)) take(after(Q + 2 - S::SPB * S::CD, 0));   // C last in its stage
+    if (S::nb(P)) take(after(Q + 2 - S::SPB, S::nc(P)));     // B followed by that stage's C
   }
   return best < 63 ? best : 63;   // 63: nothing this iteration must complete
 }
@@ -1078,8 +1084,9 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   constexpr int MP = 16 * MT, XD = S::XD, NBUF = XD + 1, W = S::W, WPB = S::WPB, CD = S::CD, BPW = S::BPW;
   constexpr int NTW = S::NTW, T0 = P * NTW;
   const CoarseArgs& A = BA.c;
-  u32x4* xs = reinterpret_cast<u32x4*>(smem);     // [NBUF][16][MP]
-  u32x4* cs = xs + NBUF * 16 * MP;                // [CD slots][BPW blocks][9 chunks][64]
+  constexpr int GPS = S::GPS, SPB = S::SPB, LSPB = SPB == 4 ? 2 : SPB == 2 ? 1 : 0;
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);     // [NBUF][GPS][16][MP]
+  u32x4* cs = xs + NBUF * GPS * 16 * MP;          // [CD slots][BPW blocks][9 chunks][64]
   u32x4* zs = cs + CD * BPW * kCodeChunks * 64;   // [256]
 
   const int lane = threadIdx.x & 63;
@@ -1098,32 +1105,32 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   const uint32_t xs_l = lds_addr(xs), zs_l = lds_addr(zs);
   const uint32_t cs_l = lds_addr(cs + lb * kCodeChunks * 64);
 
-  // Issue iteration j's ops.  Data past the end is replaced by a copy of the
+  // Issue stage j's ops.  Data past the end is replaced by a copy of the
   // last slab or byte group into a slot nothing reads before the main loop
-  // ends; data before the start (prologue iterations ahead of X(0) or B(0))
-  // by the bytes its slot is about to receive.
+  // ends; data before the start (prologue stages ahead of X(0) or B(0)) by
+  // the bytes its slot is about to receive.
   auto issue = [&](int j) {
     int gx = j + XD;
-    if (gx < 0) gx = (gx % NBUF + NBUF) % NBUF;   // a slot's first slab, fetched early
+    if (gx < 0) gx = (gx % NBUF + NBUF) % NBUF;   // a slot's first stage, fetched early
     const uint32_t xslot = (uint32_t)(gx % NBUF);
-    gx = gx < NGRP ? gx : NGRP - 1;
-    const u32x4* xsrc = BA.xslab + (size_t)gx * 256 * MT;
 #pragma unroll
-    for (int k = 0; k < S::nx(P); ++k) {   // chunks lb + BPW k, all below 4 MT
-      const int c = lb + BPW * k;
-      dma16(voff, xsrc + c * 64, xs_l + xslot * 4096 * MT + c * 1024);
+    for (int k = 0; k < S::nx(P); ++k) {   // chunks lb + BPW k of the stage's GPS slabs
+      const int c = lb + BPW * k, t = c / (4 * MT), cc = c - t * 4 * MT;
+      const int g = min(GPS * gx + t, NGRP - 1);
+      dma16(voff, BA.xslab + (size_t)g * 256 * MT + cc * 64, xs_l + (xslot * GPS + t) * 4096 * MT + cc * 1024);
     }
-    if ((j & 3) == 1) {
-      // the zero-point slab first: it is waited for two groups later, the
-      // codes (issued after it, so not waited for with it) CD byte groups later
-      int GB = (j >> 2) + 1;
+    if ((j & (SPB - 1)) == 1 % SPB) {
+      // the zero-point slab first: it is waited for at the byte group's end,
+      // the codes (issued after it, so not waited for with it) CD byte groups
+      // later
+      int GB = (j >> LSPB) + 1;
       GB = GB < 0 ? 0 : GB < NG4 ? GB : NG4 - 1;
 #pragma unroll
       for (int k = 0; k < S::nb(P); ++k) {   // zero-point chunks lb nb + k of four
         const int c = lb * S::nb(P) + k;
         dma16(voff, BA.zslab + (size_t)GB * kZpEntries + c * 64, zs_l + c * 1024);
       }
-      int GC = (j >> 2) + CD;   // never negative: the prologue starts at 1 - 4 CD or before
+      int GC = (j >> LSPB) + CD;   // never negative: the prologue starts at 1 - SPB CD or before
       const uint32_t cslot = (uint32_t)(GC % CD);
       GC = GC < NG4 ? GC : NG4 - 1;
 #pragma unroll
@@ -1137,7 +1144,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
 
 #pragma unroll
   for (int j = -S::PRO; j < 0; ++j) issue(j);
-  wait_vm<big_wait<MT, P>(3)>();
+  wait_vm<big_wait<MT, P>(SPB - 1)>();
   __syncthreads();
 
   // cgs[Q & 1] receives group Q's MFMA sums; the other set still holds the
@@ -1194,28 +1201,39 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
 
     u32x4 raw8[2][NTW];
     shift_codes(raw, raw8);
-    auto group = [&](auto qc) {
-      constexpr int Q = decltype(qc)::value;
-      const int g = 4 * G + Q;
-      issue(g);
+    // one group's MFMAs (quarter Q, the stage's slab t), its scale kept for
+    // the next group
+    auto group = [&](auto qc, int j) {
+      constexpr int Q = decltype(qc)::value, t = Q % GPS;
       float sq[NTW];
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) sq[t] = quarter_scale(lo_bf16(sz[t][Q]), Q);
-      big_group_mma<MT, NTW, Q, MP, S::XW == 2>(cgs[Q & 1], acc, cgs[(Q + 1) & 1], sp, a, raw, raw8,
-                                                xl + (g % NBUF) * 16 * MP, xl + ((g + 1) % NBUF) * 16 * MP);
+      for (int u = 0; u < NTW; ++u) sq[u] = quarter_scale(lo_bf16(sz[u][Q]), Q);
+      const u32x4* xb = xl + ((j % NBUF) * GPS + t) * 16 * MP;
+      const u32x4* xn = t + 1 < GPS ? xb + 16 * MP : xl + ((j + 1) % NBUF) * GPS * 16 * MP;
+      big_group_mma<MT, NTW, Q, MP, (t + 1 < GPS) || S::XW == 2>(cgs[Q & 1], acc, cgs[(Q + 1) & 1], sp, a, raw,
+                                                                 raw8, xb, xn);
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) sp[t] = sq[t];
-      wait_vm<big_wait<MT, P>(Q)>();
+      for (int u = 0; u < NTW; ++u) sp[u] = sq[u];
+    };
+    auto stage = [&](auto qs) {
+      constexpr int Qs = decltype(qs)::value;
+      const int j = SPB * G + Qs;
+      issue(j);
+      group(std::integral_constant<int, GPS * Qs>{}, j);
+      if constexpr (GPS == 2) group(std::integral_constant<int, GPS * Qs + 1>{}, j);
+      wait_vm<big_wait<MT, P>(Qs)>();
       __syncthreads();
-      if constexpr (S::XW == 1) {   // the next group's first fragments, now visible
+      if constexpr (S::XW == 1) {   // the next stage's first fragments, now visible
 #pragma unroll
-        for (int i = 0; i < MT; ++i) a[0][i] = xl[((g + 1) % NBUF) * 16 * MP + 16 * i];
+        for (int i = 0; i < MT; ++i) a[0][i] = xl[((j + 1) % NBUF) * GPS * 16 * MP + 16 * i];
       }
     };
-    group(std::integral_constant<int, 0>{});
-    group(std::integral_constant<int, 1>{});
-    group(std::integral_constant<int, 2>{});
-    group(std::integral_constant<int, 3>{});
+    stage(std::integral_constant<int, 0>{});
+    stage(std::integral_constant<int, 1>{});
+    if constexpr (SPB == 4) {
+      stage(std::integral_constant<int, 2>{});
+      stage(std::integral_constant<int, 3>{});
+    }
   }
   // the last group's scale update
 #pragma unroll
@@ -2127,7 +2145,7 @@ hipError_t launch_resident(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hi
 
 template <int MT>
 hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD, BigShape<MT>::CD, BigShape<MT>::BPW);
+  constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD, BigShape<MT>::CD, BigShape<MT>::BPW, BigShape<MT>::GPS);
   static_assert(lds <= kMaxLds, "LDS budget of the many-row kernel");
   static_assert((size_t)BigShape<MT>::BPW * 16 * MT * kScStride * sizeof(float) <= lds,
                 "the score area reuses the ring's LDS");
