@@ -813,45 +813,42 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Thread (m, G, p): piece p (8 consecutive k) of the four groups of byte
-// group G of row m.  The 16 threads of a (m, G) are 16 consecutive lanes.
-// x has rows of kx elements; element k of x' is x[k mod kx] (kx = K, or K/2).
+// One wave per (m, G): lane q * 16 + p takes piece p (8 consecutive k) of
+// group 4G + q of row m, so every lane issues one load and one store and the
+// 16 lanes of a group sum its x in one DPP reduction; lanes 0 and 1 gather the
+// four group sums for the zero-point slab.  x has rows of kx elements;
+// element k of x' is x[k mod kx] (kx = K, or K/2).
 __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t* __restrict__ x, int M, int MP, int K, int kx,
                                                      u32x4* __restrict__ xslab, u32x4* __restrict__ zslab) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int NG4 = K >> 9, Q4 = K >> 2;
-  if (i >= MP * NG4 * 16) return;   // whole 16-lane groups leave together
-  const int p = i & 15, G = (i >> 4) % NG4, m = (i >> 4) / NG4;
+  if (w >= MP * NG4) return;   // whole waves leave together
+  const int G = w % NG4, m = w / NG4, q = lane >> 4, p = lane & 15;
   const int h = p >> 3, s = (p >> 1) & 3, e = p & 1, f = (h * 2 + e) * 4 + s;
-  u32x4 v[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int k = q * Q4 + 128 * G + 8 * p;
-    v[q] = m < M ? *reinterpret_cast<const u32x4*>(x + (size_t)m * kx + (k < kx ? k : k - kx))
-                 : u32x4{0u, 0u, 0u, 0u};
-  }
+  const int k = q * Q4 + 128 * G + 8 * p;
+  const u32x4 v = m < M ? *reinterpret_cast<const u32x4*>(x + (size_t)m * kx + (k < kx ? k : k - kx))
+                        : u32x4{0u, 0u, 0u, 0u};
+  float sum;
+  xslab[((size_t)(4 * G + q) * 16 + f) * MP + m] = permute_x(v, sum);
+  sum = row16_sum(sum);
   float X[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float sum;
-    xslab[((size_t)(4 * G + q) * 16 + f) * MP + m] = permute_x(v[q], sum);
-    X[q] = row16_sum(sum);
-  }
-  if (p < 2) {
+  for (int u = 0; u < 4; ++u) X[u] = __shfl(sum, 16 * u, 64);
+  if (lane < 2) {
     uint32_t part[3][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float r = X[q];
+    for (int u = 0; u < 4; ++u) {
+      float r = X[u];
 #pragma unroll
       for (int c = 0; c < 3; ++c) {   // r - bf16(r) is exact in fp32
-        part[c][q] = f32_to_bf16_rne(r);
-        r -= __uint_as_float(part[c][q] << 16);
+        part[c][u] = f32_to_bf16_rne(r);
+        r -= __uint_as_float(part[c][u] << 16);
       }
     }
-    const u32x4 o = p == 0 ? u32x4{part[0][0] | part[0][1] << 16, part[0][2] | part[0][3] << 16,
-                                   part[1][0] | part[1][1] << 16, part[1][2] | part[1][3] << 16}
-                           : u32x4{part[2][0] | part[2][1] << 16, part[2][2] | part[2][3] << 16, 0u, 0u};
-    zslab[(size_t)G * kZpEntries + p * MP + m] = o;
+    const u32x4 o = lane == 0 ? u32x4{part[0][0] | part[0][1] << 16, part[0][2] | part[0][3] << 16,
+                                      part[1][0] | part[1][1] << 16, part[1][2] | part[1][3] << 16}
+                              : u32x4{part[2][0] | part[2][1] << 16, part[2][2] | part[2][3] << 16, 0u, 0u};
+    zslab[(size_t)G * kZpEntries + lane * MP + m] = o;
   }
 }
 
@@ -2283,7 +2280,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
     const int mt = (B.M + 15) / 16, mp = 16 * mt;
     u32x4* xslab = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(workspace) + kCounterBytes);
     u32x4* zslab = xslab + (size_t)(K / DH_GROUP) * 256 * mt;
-    hipLaunchKernelGGL(prep_x_kernel, dim3((mp * NG4 * 16 + 255) / 256), dim3(256), 0, s, B.x, B.M, mp, K, A.kx,
+    hipLaunchKernelGGL(prep_x_kernel, dim3((mp * NG4 + 3) / 4), dim3(256), 0, s, B.x, B.M, mp, K, A.kx,
                        xslab, zslab);
     if ((e = hipGetLastError()) != hipSuccess)
       return dh::fail(DH_EHIP, "prep_x_kernel: %s", hipGetErrorString(e));
