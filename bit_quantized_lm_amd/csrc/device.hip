@@ -689,24 +689,25 @@ void coarse_resident_kernel(CoarseArgs A) {
 // group's MFMAs, component ks of every tile in k-slice ks, so the VALU work
 // runs beside the matrix cores instead of between two MFMA phases.
 //
-// Every global read of the main loop is a direct-to-LDS DMA.  Iteration j
-// (group j; j < 0: the prologue) issues, in this order and every time, even
-// where the data does not exist (then a harmless copy into a slot that is
-// free, or that later receives the same bytes):
-//   X(j + XD)  the wave's chunks of that group's x slab               NX ops
-//   at j = 4G + 1 (after every wave read byte group G's codes):
-//   B(G + 1)   its chunks of byte group G + 1's zero-point slab      NB ops
-//   C(G + CD)  the wave's chunks of that byte group's codes/pairs     NC ops
+// Every global read of the main loop is a direct-to-LDS DMA.  Stage j (GPS
+// groups, GPS = 1 or 2, SPB = 4 / GPS stages per byte group; j < 0: the
+// prologue) issues, in this order and every time, even where the data does
+// not exist (then a harmless copy into a slot that is free, or that later
+// receives the same bytes):
+//   X(j + XD)  the wave's chunks of that stage's x slabs               NX ops
+//   at j = SPB G + 1 (after every wave read byte group G's codes):
+//   B(G + 1)   its chunks of byte group G + 1's zero-point slab       NB ops
+//   C(G + CD)  the wave's chunks of that byte group's codes/pairs      NC ops
 // and ends with one vmcnt wait that completes X(j + XW) and, at the end of a
 // byte group, C and B of the next one, then a barrier.  With XW = 2 the
-// next group's first x fragments are read before that barrier.  The number
-// of ops issued after any op depends only on j mod 4, so every wait count is
-// a constant (big_wait).  Completions are counted in issue order, so with two
+// next stage's first x fragments are read before that barrier.  The number
+// of ops issued after any op depends only on j mod SPB, so every wait count
+// is a constant (big_wait).  Completions are counted in issue order, so with two
 // waves per block the x slabs and the codes are issued by different waves
 // (BigShape::nx, nc): a wait for an x slab (an L2 hit) never waits for code
 // bytes still on their way from HBM, and the codes have CD byte groups to
 // arrive.  With one wave per block (one or two row tiles) both streams share
-// the wave's counter, and x runs XD = 3..6 groups ahead.
+// the wave's counter, and x runs XD = 3..6 stages (groups) ahead.
 constexpr int kMaxMT = 5;            // 16-row tiles per launch (80 rows)
 constexpr int kCodeChunks = 9;       // 1 KB chunks of one block's byte group: 8 code + 1 pair
 constexpr int kZpEntries = 256;      // zero-point slab entries (16 bytes)
