@@ -105,6 +105,11 @@ CASES = [
     (20, 512, 3000, 16, 64),
     (40, 1024, 2000, 12, 32),
     (72, 512, 1000, 64, 100),
+    # every row-tile count of the many-row kernel: 9 rows (one tile, just past
+    # the resident kernel), 57 and 64 (four tiles, two-group stages)
+    (9, 1024, 3000, 8, 32),
+    (57, 1536, 2500, 8, 32),
+    (64, 512, 700, 8, 32),
 ]
 
 
