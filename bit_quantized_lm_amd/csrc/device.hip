@@ -725,7 +725,7 @@ struct BigShape {
   // runs two waves instead of one (M = 16: 59.9 -> 43.7 us, M = 32: 76.6 ->
   // 58.2 us).  From three tiles on, two waves per block already fill that
   // (two workgroups of two blocks per CU, with one x slab ahead, measured
-  // 3-7 % slower at M = 48..72).
+  // 2-3 % slower at M = 48 and 72 on the same box).
   // From four row tiles on a stage (the unit of the x ring, of the DMA
   // schedule and of the barriers) is two groups, so the eight waves meet at
   // half as many barriers; below, a stage is one group.  XD and XW count stages.
