@@ -16,8 +16,16 @@
 
 #include "../../include/drafthead.h"
 #include "common.h"
+#include "ring_plan.h"
 
 namespace {
+
+using dh::BigShape;
+using dh::big_lds_bytes;
+using dh::big_wait;
+using dh::kCodeChunks;
+using dh::kMaxMT;
+using dh::kZpEntries;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -708,78 +716,9 @@ void coarse_resident_kernel(CoarseArgs A) {
 // bytes still on their way from HBM, and the codes have CD byte groups to
 // arrive.  With one wave per block (one or two row tiles) both streams share
 // the wave's counter, and x runs XD = 3..6 stages (groups) ahead.
-constexpr int kMaxMT = 5;            // 16-row tiles per launch (80 rows)
-constexpr int kCodeChunks = 9;       // 1 KB chunks of one block's byte group: 8 code + 1 pair
-constexpr int kZpEntries = 256;      // zero-point slab entries (16 bytes)
-
-template <int MT>
-struct BigShape {
-  static constexpr int WPB = MT >= 3 ? 2 : 1;       // waves per block
-  static constexpr int BPW = 4;                     // blocks per workgroup
-  static constexpr int NTW = 4 / WPB;               // column tiles per wave
-  static constexpr int W = BPW * WPB;               // waves per workgroup
-  // x slabs and byte groups of codes requested ahead.  One or two row tiles
-  // run four waves per workgroup: with one byte group of codes ahead (its
-  // slot refilled after the first group of the byte group has read it) and,
-  // at two tiles, three slabs, two workgroups fit a CU's LDS, so each SIMD
-  // runs two waves instead of one (M = 16: 59.9 -> 43.7 us, M = 32: 76.6 ->
-  // 58.2 us).  From three tiles on, two waves per block already fill that
-  // (two workgroups of two blocks per CU, with one x slab ahead, measured
-  // 2-3 % slower at M = 48 and 72 on the same box).
-  // From four row tiles on a stage (the unit of the x ring, of the DMA
-  // schedule and of the barriers) is two groups, so the eight waves meet at
-  // half as many barriers; below, a stage is one group.  XD and XW count stages.
-  static constexpr int GPS = MT >= 4 ? 2 : 1;       // groups per stage
-  static constexpr int SPB = 4 / GPS;               // stages per byte group
-  static constexpr int XD = MT >= 4 ? 1 : MT == 3 ? 5 : MT == 2 ? 3 : 6;
-  static constexpr int CD = MT <= 2 ? 1 : 2;
-  static constexpr int XW = XD >= 4 ? 2 : 1;        // stage's slabs completed XW stages ahead
-  static constexpr int PRO = XD > SPB * CD - 1 ? XD : SPB * CD - 1;   // prologue stages
-  // DMA ops per iteration of a wave of part p.  With two waves per block the
-  // parts issue different streams: part 1 the x slabs (chunks lb + BPW k),
-  // part 0 its block's codes and scale pairs and its share of the zero-point
-  // slab.  A wave's vmcnt completes in issue order, so a wait for an x slab
-  // (an L2 read) never waits behind code bytes on their way from HBM, and the
-  // codes get their full distance (CD byte groups) before anyone waits for
-  // them.  With one wave per block every wave issues both.
-  static constexpr int nx(int p) { return WPB == 1 || p == 1 ? GPS * 4 * MT / BPW : 0; }
-  static constexpr int nc(int p) { return p == 0 ? kCodeChunks : 0; }
-  static constexpr int nb(int p) { return p == 0 ? 4 / BPW : 0; }
-};
-
-constexpr size_t big_lds_bytes(int MT, int XD, int CD, int BPW, int GPS) {
-  return (size_t)(XD + 1) * GPS * 4096 * MT + (size_t)CD * BPW * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
-}
-
 // Workspace of one launch with MT row tiles: x slabs, then zero-point slabs.
 size_t big_workspace_bytes(int MT, int K) {
   return (size_t)(K / DH_GROUP) * 4096 * MT + (size_t)(K / 512) * kZpEntries * 16;
-}
-
-// Ops a wave of part P may leave outstanding at the end of a stage with
-// j mod SPB == Q: those issued after X(j + XW) and, for the byte group's last
-// stage (Q == SPB - 1), after the B and C of the next byte group (issued at
-// j + 2 - SPB and j + 2 - SPB CD).  The prologue's final wait (X(XW - 1),
-// C(0), B(0)) is the Q == SPB - 1 case.
-template <int MT, int P>
-constexpr int big_wait(int Q) {
-  using S = BigShape<MT>;
-  auto m4 = [](int j) { return ((j % S::SPB) + S::SPB) % S::SPB; };
-  auto cb = [&](int j) { return m4(j) == 1 % S::SPB ? S::nc(P) + S::nb(P) : 0; };
-  auto ops = [&](int j) { return S::nx(P) + cb(j); };
-  auto after = [&](int j0, int in_iter) {   // ops after one issued in iteration j0
-    int n = in_iter;
-    for (int j = j0 + 1; j <= Q; ++j) n += ops(j);
-    return n;
-  };
-  int best = 1 << 20;
-  auto take = [&](int n) { best = n < best ? n : best; };
-  if (S::nx(P)) take(after(Q + S::XW - S::XD, cb(Q + S::XW - S::XD)));
-  if (Q == S::SPB - 1) {
-    if (S::nc(P)) take(after(Q + 2 - S::SPB * S::CD, 0));   // C last in its stage
-    if (S::nb(P)) take(after(Q + 2 - S::SPB, S::nc(P)));     // B followed by that stage's C
-  }
-  return best < 63 ? best : 63;   // 63: nothing this iteration must complete
 }
 
 // LDS byte address of a pointer into __shared__ memory.
@@ -1082,7 +1021,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   constexpr int MP = 16 * MT, XD = S::XD, NBUF = XD + 1, W = S::W, WPB = S::WPB, CD = S::CD, BPW = S::BPW;
   constexpr int NTW = S::NTW, T0 = P * NTW;
   const CoarseArgs& A = BA.c;
-  constexpr int GPS = S::GPS, SPB = S::SPB, LSPB = SPB == 4 ? 2 : SPB == 2 ? 1 : 0;
+  constexpr int GPS = S::GPS, SPB = S::SPB;
   u32x4* xs = reinterpret_cast<u32x4*>(smem);     // [NBUF][GPS][16][MP]
   u32x4* cs = xs + NBUF * GPS * 16 * MP;          // [CD slots][BPW blocks][9 chunks][64]
   u32x4* zs = cs + CD * BPW * kCodeChunks * 64;   // [256]
@@ -1108,29 +1047,23 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   // ends; data before the start (prologue stages ahead of X(0) or B(0)) by
   // the bytes its slot is about to receive.
   auto issue = [&](int j) {
-    int gx = j + XD;
-    if (gx < 0) gx = (gx % NBUF + NBUF) % NBUF;   // a slot's first stage, fetched early
-    const uint32_t xslot = (uint32_t)(gx % NBUF);
 #pragma unroll
     for (int k = 0; k < S::nx(P); ++k) {   // chunks lb + BPW k of the stage's GPS slabs
-      const int c = lb + BPW * k, t = c / (4 * MT), cc = c - t * 4 * MT;
-      const int g = min(GPS * gx + t, NGRP - 1);
-      dma16(voff, BA.xslab + (size_t)g * 256 * MT + cc * 64, xs_l + (xslot * GPS + t) * 4096 * MT + cc * 1024);
+      const dh::XOp o = dh::x_op<MT>(j, lb, k, NGRP);
+      dma16(voff, BA.xslab + (size_t)o.slab * 256 * MT + o.chunk * 64, xs_l + o.dst * 1024);
     }
-    if ((j & (SPB - 1)) == 1 % SPB) {
+    if (dh::stage_has_byte_ops<MT>(j)) {
       // the zero-point slab first: it is waited for at the byte group's end,
       // the codes (issued after it, so not waited for with it) CD byte groups
       // later
-      int GB = (j >> LSPB) + 1;
-      GB = GB < 0 ? 0 : GB < NG4 ? GB : NG4 - 1;
+      const int GB = dh::zp_group<MT>(j, NG4);
 #pragma unroll
       for (int k = 0; k < S::nb(P); ++k) {   // zero-point chunks lb nb + k of four
         const int c = lb * S::nb(P) + k;
         dma16(voff, BA.zslab + (size_t)GB * kZpEntries + c * 64, zs_l + c * 1024);
       }
-      int GC = (j >> LSPB) + CD;   // never negative: the prologue starts at 1 - SPB CD or before
-      const uint32_t cslot = (uint32_t)(GC % CD);
-      GC = GC < NG4 ? GC : NG4 - 1;
+      const int GC = dh::code_group<MT>(j, NG4);   // never negative: the prologue starts at 1 - SPB CD or before
+      const uint32_t cslot = (uint32_t)dh::code_slot<MT>(j);
 #pragma unroll
       for (int k = 0; k < S::nc(P); ++k) {
         const int c = k;

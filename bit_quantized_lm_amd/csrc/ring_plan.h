@@ -1,0 +1,132 @@
+// DMA ring schedule of the many-row coarse kernel: its shape per row-tile
+// count, the wait counts, and the source and destination of every DMA op a
+// wave issues.  Plain constexpr C++ with no HIP types, so the host tests
+// compile it and check every op of every stage against the buffers it
+// addresses.  Internal to the library (not part of the public ABI).
+#pragma once
+
+#include <stddef.h>
+
+namespace dh {
+
+constexpr int kMaxMT = 5;            // 16-row tiles per launch (80 rows)
+constexpr int kCodeChunks = 9;       // 1 KB chunks of one block's byte group: 8 code + 1 pair
+constexpr int kZpEntries = 256;      // zero-point slab entries (16 bytes)
+
+template <int MT>
+struct BigShape {
+  static constexpr int WPB = MT >= 3 ? 2 : 1;       // waves per block
+  static constexpr int BPW = 4;                     // blocks per workgroup
+  static constexpr int NTW = 4 / WPB;               // column tiles per wave
+  static constexpr int W = BPW * WPB;               // waves per workgroup
+  // x slabs and byte groups of codes requested ahead.  One or two row tiles
+  // run four waves per workgroup: with one byte group of codes ahead (its
+  // slot refilled after the first group of the byte group has read it) and,
+  // at two tiles, three slabs, two workgroups fit a CU's LDS, so each SIMD
+  // runs two waves instead of one (M = 16: 59.9 -> 43.7 us, M = 32: 76.6 ->
+  // 58.2 us).  From three tiles on, two waves per block already fill that
+  // (two workgroups of two blocks per CU, with one x slab ahead, measured
+  // 2-3 % slower at M = 48 and 72 on the same box).
+  // From four row tiles on a stage (the unit of the x ring, of the DMA
+  // schedule and of the barriers) is two groups, so the eight waves meet at
+  // half as many barriers; below, a stage is one group.  XD and XW count stages.
+  static constexpr int GPS = MT >= 4 ? 2 : 1;       // groups per stage
+  static constexpr int SPB = 4 / GPS;               // stages per byte group
+  static constexpr int XD = MT >= 4 ? 1 : MT == 3 ? 5 : MT == 2 ? 3 : 6;
+  static constexpr int CD = MT <= 2 ? 1 : 2;
+  static constexpr int XW = XD >= 4 ? 2 : 1;        // stage's slabs completed XW stages ahead
+  static constexpr int PRO = XD > SPB * CD - 1 ? XD : SPB * CD - 1;   // prologue stages
+  // DMA ops per iteration of a wave of part p.  With two waves per block the
+  // parts issue different streams: part 1 the x slabs (chunks lb + BPW k),
+  // part 0 its block's codes and scale pairs and its share of the zero-point
+  // slab.  A wave's vmcnt completes in issue order, so a wait for an x slab
+  // (an L2 read) never waits behind code bytes on their way from HBM, and the
+  // codes get their full distance (CD byte groups) before anyone waits for
+  // them.  With one wave per block every wave issues both.
+  static constexpr int nx(int p) { return WPB == 1 || p == 1 ? GPS * 4 * MT / BPW : 0; }
+  static constexpr int nc(int p) { return p == 0 ? kCodeChunks : 0; }
+  static constexpr int nb(int p) { return p == 0 ? 4 / BPW : 0; }
+};
+
+constexpr size_t big_lds_bytes(int MT, int XD, int CD, int BPW, int GPS) {
+  return (size_t)(XD + 1) * GPS * 4096 * MT + (size_t)CD * BPW * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
+}
+
+// One stage's x-slab ops: stage j fetches the slabs of stage gx = j + XD into
+// slot gx mod NBUF; before the start (gx < 0, prologue) a slot's first stage,
+// which that slot receives again later.  Op k of a wave of block lb is chunk
+// c = lb + BPW k of the stage's GPS slabs: slab t = c / (4 MT), chunk cc.
+struct XOp {
+  int slab;    // source slab (group) index, clamped to the last group
+  int chunk;   // 1 KB chunk of the slab (64 entries of 16 bytes)
+  int dst;     // destination: 1 KB chunk index in the x ring
+};
+template <int MT>
+constexpr XOp x_op(int j, int lb, int k, int NGRP) {
+  using S = BigShape<MT>;
+  constexpr int NBUF = S::XD + 1;
+  int gx = j + S::XD;
+  if (gx < 0) gx = (gx % NBUF + NBUF) % NBUF;
+  const int xslot = gx % NBUF;
+  const int c = lb + S::BPW * k, t = c / (4 * MT), cc = c - t * 4 * MT;
+  const int g = S::GPS * gx + t < NGRP - 1 ? S::GPS * gx + t : NGRP - 1;
+  return XOp{g, cc, (xslot * S::GPS + t) * 4 * MT + cc};
+}
+
+// Whether stage j issues the byte-group ops (zero-point slab, then codes):
+// the second stage of a byte group, after every wave read that byte group's
+// codes.
+template <int MT>
+constexpr bool stage_has_byte_ops(int j) {
+  using S = BigShape<MT>;
+  return (j & (S::SPB - 1)) == 1 % S::SPB;
+}
+template <int MT>
+constexpr int stage_byte_group(int j) {   // floor(j / SPB)
+  using S = BigShape<MT>;
+  return j >> (S::SPB == 4 ? 2 : S::SPB == 2 ? 1 : 0);
+}
+// Byte group whose zero-point slab stage j fetches (the next one, clamped).
+template <int MT>
+constexpr int zp_group(int j, int NG4) {
+  const int GB = stage_byte_group<MT>(j) + 1;
+  return GB < 0 ? 0 : GB < NG4 ? GB : NG4 - 1;
+}
+// Byte group whose codes stage j fetches (CD ahead, clamped) and its slot.
+template <int MT>
+constexpr int code_slot(int j) {
+  return (stage_byte_group<MT>(j) + BigShape<MT>::CD) % BigShape<MT>::CD;
+}
+template <int MT>
+constexpr int code_group(int j, int NG4) {
+  const int GC = stage_byte_group<MT>(j) + BigShape<MT>::CD;
+  return GC < NG4 ? GC : NG4 - 1;
+}
+
+// Ops a wave of part P may leave outstanding at the end of a stage with
+// j mod SPB == Q: those issued after X(j + XW) and, for the byte group's last
+// stage (Q == SPB - 1), after the B and C of the next byte group (issued at
+// j + 2 - SPB and j + 2 - SPB CD).  The prologue's final wait (X(XW - 1),
+// C(0), B(0)) is the Q == SPB - 1 case.
+template <int MT, int P>
+constexpr int big_wait(int Q) {
+  using S = BigShape<MT>;
+  auto m4 = [](int j) { return ((j % S::SPB) + S::SPB) % S::SPB; };
+  auto cb = [&](int j) { return m4(j) == 1 % S::SPB ? S::nc(P) + S::nb(P) : 0; };
+  auto ops = [&](int j) { return S::nx(P) + cb(j); };
+  auto after = [&](int j0, int in_iter) {   // ops after one issued in iteration j0
+    int n = in_iter;
+    for (int j = j0 + 1; j <= Q; ++j) n += ops(j);
+    return n;
+  };
+  int best = 1 << 20;
+  auto take = [&](int n) { best = n < best ? n : best; };
+  if (S::nx(P)) take(after(Q + S::XW - S::XD, cb(Q + S::XW - S::XD)));
+  if (Q == S::SPB - 1) {
+    if (S::nc(P)) take(after(Q + 2 - S::SPB * S::CD, 0));   // C last in its stage
+    if (S::nb(P)) take(after(Q + 2 - S::SPB, S::nc(P)));     // B followed by that stage's C
+  }
+  return best < 63 ? best : 63;   // 63: nothing this iteration must complete
+}
+
+}  // namespace dh
