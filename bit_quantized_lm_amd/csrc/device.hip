@@ -17,6 +17,7 @@
 #include "../../include/drafthead.h"
 #include "common.h"
 #include "ring_plan.h"
+#include "select8.h"
 
 namespace {
 
@@ -805,30 +806,6 @@ struct BigArgs {
 // sixteen neighbouring lists cover the 64 banks once.
 constexpr int kScStride = 68;
 
-// Compare-exchange of two keys, the larger first.
-__device__ __forceinline__ void cx_desc(uint32_t& a, uint32_t& b) {
-  const uint32_t hi = max(a, b);
-  b = min(a, b);
-  a = hi;
-}
-
-// Eight keys sorted descending: Batcher's odd-even merge sort (19 comparators).
-__device__ __forceinline__ void sort8_desc(uint32_t (&v)[8]) {
-  constexpr int P[19][2] = {{0, 1}, {2, 3}, {4, 5}, {6, 7}, {0, 2}, {1, 3}, {4, 6}, {5, 7}, {1, 2}, {5, 6},
-                            {0, 4}, {1, 5}, {2, 6}, {3, 7}, {2, 4}, {3, 5}, {1, 2}, {3, 4}, {5, 6}};
-#pragma unroll
-  for (int i = 0; i < 19; ++i) cx_desc(v[P[i][0]], v[P[i][1]]);
-}
-
-// A bitonic sequence of eight keys sorted descending (12 comparators).
-__device__ __forceinline__ void bitonic8_desc(uint32_t (&v)[8]) {
-#pragma unroll
-  for (int d = 4; d > 0; d >>= 1)
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if ((i & d) == 0) cx_desc(v[i], v[i + d]);
-}
-
 // Top-kcand lists (kcand <= 8) of every (block, row) pair of a many-row
 // workgroup, one list per thread, from the keys in LDS (row lb * MP + m).
 // Each key's low 6 bits are replaced by 63 - column, so the keys of a row are
@@ -861,56 +838,10 @@ __device__ __forceinline__ void lane_select8(const uint32_t* sk, const CoarseArg
     for (int c4 = 0; c4 < 16; ++c4) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(row + 4 * c4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) key[4 * c4 + e] = (v[e] & ~63u) | (uint32_t)(63 - 4 * c4 - e);
+      for (int e = 0; e < 4; ++e) key[4 * c4 + e] = v[e];
     }
-    uint32_t run[8], ninth = 0u;
-#pragma unroll
-    for (int c8 = 0; c8 < 8; ++c8) {
-      uint32_t ch[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ch[e] = key[8 * c8 + e];
-      sort8_desc(ch);
-      if (c8 == 0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) run[i] = ch[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t hi = max(run[i], ch[7 - i]);
-          ninth = max(ninth, min(run[i], ch[7 - i]));
-          run[i] = hi;
-        }
-        bitonic8_desc(run);
-      }
-    }
-    // exact unless upper parts agree where the order or the cut depends on them
-    const uint32_t p8 = run[7] >> 6;
-    bool exact = (ninth >> 6) < p8 || p8 == 0u;
-#pragma unroll
-    for (int i = 0; i < 7; ++i) exact &= (run[i] >> 6) != (run[i + 1] >> 6) || (run[i + 1] >> 6) == 0u;
     uint32_t slot[8];   // 63 - column, or 64 for an empty slot
-#pragma unroll
-    for (int i = 0; i < 8; ++i) slot[i] = run[i] >> 6 ? run[i] & 63u : 64u;
-    if (!exact) {
-      unsigned long long top[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) top[i] = 0ull;
-      for (int c = 0; c < 64; ++c) {
-        const uint32_t k = row[c];
-        if (k != 0u && (k >> 6) >= p8) {
-          unsigned long long t = ((unsigned long long)k << 32) | (uint32_t)(63 - c);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const unsigned long long u = top[i];
-            const bool gt = t > u;
-            top[i] = gt ? t : u;
-            t = gt ? u : t;
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) slot[i] = top[i] ? (uint32_t)(top[i] & 63ull) : 64u;
-    }
+    dh::select8_row(key, [&](int c) { return row[c]; }, slot);
     float val[8];
     int32_t id[8];
 #pragma unroll

@@ -1,0 +1,66 @@
+// Host check of the per-thread top-8 selection (select8.h), the code the
+// many-row coarse kernel runs: against a sort by (key desc, column asc) on
+// random rows, rows with exact ties, rows with near-ties (keys a few units
+// apart, so their upper 26 bits agree) and rows with missing columns (key 0),
+// plus the sorting networks on all 256 zero-one inputs.  Exit status 0 = all
+// agree.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <random>
+#include <vector>
+
+#include "../bit_quantized_lm_amd/csrc/select8.h"
+
+static uint32_t key_of(float f) {   // order-preserving unsigned image of a float
+  f += 0.0f;                        // -0 as +0
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+int main() {
+  int failures = 0;
+  for (int bits = 0; bits < 256; ++bits) {   // zero-one principle for the network
+    uint32_t v[8];
+    for (int i = 0; i < 8; ++i) v[i] = (bits >> i) & 1u;
+    dh::sort8_desc(v);
+    for (int i = 0; i < 7; ++i) failures += v[i] < v[i + 1];
+  }
+  std::mt19937_64 rng(17);
+  std::normal_distribution<float> nrm(0.f, 1.f);
+  long slow = 0;
+  for (int trial = 0; trial < 300000; ++trial) {
+    const int mode = trial % 6;
+    uint32_t key[64];
+    const float base = nrm(rng);
+    for (int c = 0; c < 64; ++c) {
+      float s = nrm(rng);
+      if (mode == 1) s = std::round(s * 2.f);                       // many exact ties
+      if (mode == 2) s = base;                                      // one value, then nudged
+      if (mode == 4) s = (c % 5 == 0) ? base : s * 1e-3f;           // a repeated maximum
+      key[c] = key_of(s);
+      if (mode == 2 || mode == 3) key[c] += (uint32_t)(rng() % 64);  // near-ties within 63 units
+    }
+    const int nvalid = mode == 5 ? 1 + (int)(rng() % 64) : 64;
+    for (int c = nvalid; c < 64; ++c) key[c] = 0u;
+    uint32_t slot[8];
+    dh::select8_row(key, [&](int c) { return key[c]; }, slot);
+    std::vector<int> cols;
+    for (int c = 0; c < 64; ++c)
+      if (key[c]) cols.push_back(c);
+    std::stable_sort(cols.begin(), cols.end(), [&](int a, int b) { return key[a] > key[b]; });
+    bool fast = true;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t want = i < (int)cols.size() ? (uint32_t)(63 - cols[i]) : 64u;
+      if (slot[i] != want) {
+        if (failures < 10) std::printf("trial %d mode %d slot %d: got %u want %u\n", trial, mode, i, slot[i], want);
+        ++failures;
+      }
+    }
+    for (int i = 0; i + 1 < (int)cols.size() && i < 8; ++i) fast &= (key[cols[i]] >> 6) != (key[cols[i + 1]] >> 6);
+    slow += !fast;
+  }
+  std::printf("%s (%d failures; rows with agreeing upper bits: %ld)\n", failures ? "FAIL" : "ok", failures, slow);
+  return failures ? 1 : 0;
+}
