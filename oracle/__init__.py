@@ -40,6 +40,6 @@ from .quant import (GROUP, quantize, pack_quarter_split, unpack_quarter_split,  
                     effective_weight, quantize_pack, quantize_int4, pack_half_split, unpack_half_split,
                     quantize_pack_int4, effective_weight_int4)
 from .head import (BLOCK_N, coarse, coarse_int4, coarse_collapse, block_topk, row_topr,  # noqa: F401
-                   rerank_exact, final_argmax, logits_row, exact_head, pipeline, tie_rows,
+                   rerank_exact, final_argmax, logits_row, exact_head, pipeline, tie_rows, tied_ids,
                    e4m3_value, rerank_exact_e4m3, e2m1_value, e4m3fn_value, nvfp4_rows,
                    rerank_exact_nvfp4)

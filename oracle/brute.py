@@ -112,7 +112,33 @@ def pack_row(codes):
             for j in range(q4)]
 
 
+def pack_row_int4(codes):
+    """4-bit head: byte j holds the code of k = j in bits 0-3 and of K/2+j in bits 4-7."""
+    h = len(codes) // 2
+    return [codes[j] | (codes[h + j] << 4) for j in range(h)]
+
+
 # ---------------------------------------------------------------- per call
+def coarse_row_int4(x_vals, packed_row, s_bits, zs_bits):
+    """Exact coarse logit of one column of a 4-bit head, in the page's form:
+    per group S * sum x (1 + v/16) - ZS * sum x, the 1 + v/16 being what the
+    page's 4-bit bit-pattern decode yields and S, ZS its pair premultiplied
+    by 16 (`_quantize_head_now`, comment on the premultiplier)."""
+    h = len(packed_row)
+    k = 2 * h
+    total = Fraction(0)
+    for g in range(k // GROUP):
+        p = Fraction(0)
+        xs = Fraction(0)
+        for kk in range(g * GROUP, (g + 1) * GROUP):
+            half, j = divmod(kk, h)
+            v = (packed_row[j] >> (4 * half)) & 15
+            p += x_vals[kk] * (1 + Fraction(v, 16))
+            xs += x_vals[kk]
+        total += bf16_bits_value(s_bits[g]) * p - bf16_bits_value(zs_bits[g]) * xs
+    return total
+
+
 def coarse_row(x_vals, packed_row, s_bits, zs_bits):
     """Exact coarse logit of one column: sum over groups of S * p - ZS * X."""
     q4 = len(packed_row)
@@ -130,19 +156,25 @@ def coarse_row(x_vals, packed_row, s_bits, zs_bits):
     return total
 
 
-def run(x_bits, w_bits, kcand, r):
-    """Whole head, exact.  x_bits [M][K], w_bits [N][K] as nested lists of ints."""
+def run(x_bits, w_bits, kcand, r, bits=2):
+    """Whole head, exact.  x_bits [M][K], w_bits [N][K] as nested lists of ints.
+    bits = 4: the 4-bit head (15 levels, premultiplier 16, half-split bytes)."""
     m = len(x_bits)
     n = len(w_bits)
     xv = [[bf16_bits_value(b) for b in row] for row in x_bits]
     packed, S, ZS, codes = [], [], [], []
     for row in w_bits:
-        c, s, z = quantize_row(row)
+        if bits == 4:
+            c, s, z = quantize_row(row, levels=15, premul=16)
+            packed.append(pack_row_int4(c))
+        else:
+            c, s, z = quantize_row(row)
+            packed.append(pack_row(c))
         codes.append(c)
-        packed.append(pack_row(c))
         S.append(s)
         ZS.append(z)
-    coarse = [[coarse_row(xv[i], packed[col], S[col], ZS[col]) for col in range(n)]
+    score = coarse_row_int4 if bits == 4 else coarse_row
+    coarse = [[score(xv[i], packed[col], S[col], ZS[col]) for col in range(n)]
               for i in range(m)]
     nblk = (n + BLOCK_N - 1) // BLOCK_N
     cand = []
@@ -166,6 +198,7 @@ def run(x_bits, w_bits, kcand, r):
         rr.append(ids)
     exact = []
     out = []
+    out_val = []
     for i in range(m):
         ev = []
         for c in rr[i]:
@@ -182,5 +215,6 @@ def run(x_bits, w_bits, kcand, r):
             if best is None or e32 > best[1] or (e32 == best[1] and c < best[0]):
                 best = (c, e32)
         out.append(best[0] if best else -1)
+        out_val.append(best[1] if best else None)
     return {"codes": codes, "packed": packed, "S": S, "ZS": ZS, "coarse": coarse,
-            "cand": cand, "rr_id": rr, "rr_val": exact, "out_id": out}
+            "cand": cand, "rr_id": rr, "rr_val": exact, "out_id": out, "out_val": out_val}

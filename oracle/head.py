@@ -251,6 +251,10 @@ def rerank_exact_nvfp4(x_bits, w4, bscale, gscale, rr_id):
 def final_argmax(rr_id, e):
     """Argmax over the R exact values of each row, float32 decision, ties -> lower id.
 
+    Reading (the page leaves the caller's argmax unshown): a NaN exact value
+    (an NVFP4 row whose block scale is the e4m3 NaN code) ranks below every
+    number, -inf included, so it is returned only when every reranked value
+    of the row is NaN (then the lowest such id, with value NaN).
     Returns (out_id int64 [M], out_val float32 [M]); (-1, -inf) for a row with
     no valid candidate.
     """
@@ -266,10 +270,12 @@ def final_argmax(rr_id, e):
             if i < 0:
                 continue
             v = e32[row, r]
-            if best is None or v > best[1] or (v == best[1] and i < best[0]):
-                best = (i, v)
+            # order key: (is a number, value, lower id first)
+            key = (not np.isnan(v), v if not np.isnan(v) else 0.0, -i)
+            if best is None or key > best[0]:
+                best = (key, i, v)
         if best is not None:
-            out_id[row], out_val[row] = best
+            out_id[row], out_val[row] = best[1], best[2]
     return out_id, out_val
 
 
@@ -319,7 +325,13 @@ def argmax_lowest(E):
 
 
 def tie_rows(e, rel=1e-4):
-    """Rows whose two best exact values differ by less than rel * |best|."""
+    """Rows whose two best exact values differ by less than rel * |best|.
+
+    `e` holds the reranked exact values of each row (the values the final
+    argmax decides between), -inf for padding; a row with fewer than two
+    finite values is never a tie row.  Reading of the acceptance rule "the
+    top two exact logits differ by less than 1e-4 relative".
+    """
     e = np.asarray(e, dtype=np.float64)
     flags = np.zeros(e.shape[0], dtype=bool)
     for row in range(e.shape[0]):
@@ -327,6 +339,27 @@ def tie_rows(e, rel=1e-4):
         if len(v) >= 2 and (v[0] - v[1]) < rel * abs(v[0]):
             flags[row] = True
     return flags
+
+
+def tied_ids(rr_id, e, rel=1e-4):
+    """Per row, the set of reranked ids a tie row may return: every valid id
+    whose exact value equals the row's best or lies within rel * |best| below
+    it.  On a tie row the final token is any one of these (the float32 order
+    of the summation decides between them); on other rows only the oracle's
+    own out_id is accepted.  Returns a list of sets of ints.
+    """
+    rr_id = np.asarray(rr_id)
+    e = np.asarray(e, dtype=np.float64)
+    out = []
+    for row in range(rr_id.shape[0]):
+        ok = (rr_id[row] >= 0) & np.isfinite(e[row])
+        if not np.any(ok):
+            out.append(set())
+            continue
+        best = np.max(e[row][ok])
+        near = ok & ((e[row] == best) | ((best - e[row]) < rel * abs(best)))
+        out.append({int(i) for i in rr_id[row][near]})
+    return out
 
 
 def pipeline(x_bits, w_bits, packed, S_bits, ZS_bits, kcand=8, r=32, bits=2):
@@ -340,5 +373,5 @@ def pipeline(x_bits, w_bits, packed, S_bits, ZS_bits, kcand=8, r=32, bits=2):
     return {
         "coarse": c, "cand_val": cv, "cand_id": ci, "rr_id": rr_id,
         "rr_coarse": rr_cv, "rr_val": e, "out_id": out_id, "out_val": out_val,
-        "tie_rows": tie_rows(e),
+        "tie_rows": tie_rows(e), "tied_ids": tied_ids(rr_id, e),
     }

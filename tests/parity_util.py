@@ -8,12 +8,18 @@ Acceptance rules:
   oracle put at that position (a reordering or a boundary swap among values
   closer than fp32 accumulation can resolve).  Such lists are counted.
 * final ids may differ only on tie rows: rows whose two best exact logits
-  (oracle, float64) differ by less than 1e-4 relative.  Counted.
+  (oracle, float64) differ by less than 1e-4 relative; there the GPU's id
+  must still be one of the oracle's reranked ids within that window of the
+  best (oracle.tied_ids).  Counted.
 * coarse and candidate values: |gpu - ref| <= 2e-3 |ref| + 2e-3 rms(row);
-  exact rerank values: |gpu - ref| <= 2e-3 |ref| + 1e-5.
+  exact rerank values and the returned token's value (out_val, compared
+  with the oracle's exact value of the GPU's token):
+  |gpu - ref| <= 2e-3 |ref| + 1e-5.
 Every comparison uses oracle values of ids; no oracle input comes from the GPU.
 """
 import numpy as np
+
+import oracle
 
 TAU_REL = 1e-5
 VAL_REL = 2e-3
@@ -54,7 +60,7 @@ def compare(ref, gpu, n, kcand, check_coarse=True):
     rms = np.sqrt(np.mean(c ** 2, axis=1))
     stats = {"rows": m, "blocks": 0, "blocks_excused": 0, "rows_rr_excused": 0,
              "tie_rows": int(np.sum(ref["tie_rows"])), "final_mismatch_on_tie_rows": 0,
-             "max_coarse_abs_err": 0.0, "max_rr_abs_err": 0.0}
+             "max_coarse_abs_err": 0.0, "max_rr_abs_err": 0.0, "max_out_val_abs_err": 0.0}
     if check_coarse and gpu.get("coarse") is not None:
         g = gpu["coarse"].astype(np.float64)
         err = np.abs(g - c)
@@ -97,10 +103,32 @@ def compare(ref, gpu, n, kcand, check_coarse=True):
         if err.size:
             stats["max_rr_abs_err"] = max(stats["max_rr_abs_err"], float(err.max()))
         assert np.all(err <= VAL_REL * np.abs(want[fin]) + 1e-5), f"row {row}: exact values"
+        nan = same & np.isnan(want)
+        assert np.all(np.isnan(ev[nan])), f"row {row}: oracle NaN exact value, gpu {ev[nan]}"
         assert np.all(np.isneginf(ev[same & (ref["rr_id"][row] < 0)])), f"row {row}: padded rr value"
     g_out = gpu["out_id"].astype(np.int64)
+    g_outv = gpu["out_val"].astype(np.float64)
+    tied = ref.get("tied_ids")
+    if tied is None:
+        tied = oracle.tied_ids(ref["rr_id"], ref["rr_val"])
     for row in range(m):
         if g_out[row] != ref["out_id"][row]:
             assert ref["tie_rows"][row], f"row {row}: final id gpu {g_out[row]} oracle {ref['out_id'][row]}"
+            assert int(g_out[row]) in tied[row], \
+                f"row {row}: tie row, gpu id {g_out[row]} outside the tied set {sorted(tied[row])}"
             stats["final_mismatch_on_tie_rows"] += 1
+        # the returned value is the exact logit of the returned token
+        if g_out[row] < 0:
+            assert np.isneginf(g_outv[row]), f"row {row}: no token but out_val {g_outv[row]}"
+            continue
+        pos = np.nonzero(ref["rr_id"][row] == g_out[row])[0]
+        assert pos.size == 1, f"row {row}: gpu token {g_out[row]} not among the oracle's reranked ids"
+        want = float(ref["rr_val"][row][pos[0]])
+        if np.isnan(want):
+            assert np.isnan(g_outv[row]), f"row {row}: oracle value NaN, gpu out_val {g_outv[row]}"
+            continue
+        err = abs(g_outv[row] - want)
+        stats["max_out_val_abs_err"] = max(stats["max_out_val_abs_err"], float(err))
+        assert err <= VAL_REL * abs(want) + 1e-5, f"row {row}: out_val gpu {g_outv[row]} oracle {want}"
     return stats
+

@@ -580,3 +580,134 @@ def test_synthetic_nvfp4_head_rounds_to_nearest():
     best = np.min(np.abs(np.abs(v)[..., None] - grid), axis=-1)
     assert np.all(np.abs(np.abs(d) - np.abs(v)) <= best + 1e-12)
     assert np.all((d == 0) | (np.sign(d) == np.sign(v)))
+
+
+# ------------------------------------------------------------- tie rows
+def _tie_cases(golden):
+    fx = golden("tie_rows_example.txt")
+    cases = []
+    for ids, e, tie, tied in zip(fx["id"], fx["e"], fx["tie"], fx["tied"]):
+        cases.append((np.array([int(v) for v in ids]), np.array([float(v) for v in e]),
+                      bool(int(tie[0])), {int(v) for v in tied}))
+    return cases
+
+
+def test_tie_rows_fixture(golden):
+    """tie_rows and tied_ids against hand-derived rows: gaps just inside and
+    just outside 1e-4 |e1|, a negative best, unsorted values, -inf padding, a
+    single candidate, a three-way tie, exact equality at and away from zero."""
+    cases = _tie_cases(golden)
+    assert len(cases) == 10
+    for i, (ids, e, tie, tied) in enumerate(cases):
+        assert bool(oracle.tie_rows(e[None, :])[0]) == tie, i
+        assert oracle.tied_ids(ids[None, :], e[None, :])[0] == tied, i
+        # the oracle's own final id is always in the tied set
+        out_id, _ = oracle.final_argmax(ids[None, :], e[None, :])
+        if tied:
+            assert int(out_id[0]) in tied, i
+        else:
+            assert int(out_id[0]) == -1, i
+
+
+def test_pipeline_tie_rows_are_over_the_reranked_set():
+    """With weights the quantiser reproduces (coarse == exact), two columns of
+    one block with identical rows tie exactly in the full row; at KCAND = 1
+    only the lower one is a candidate, so the reranked set holds no tie: the
+    pipeline's tie flag follows the reranked values, not the full row."""
+    rng = np.random.default_rng(29)
+    n, k = 256, 512
+    w_bits, _ = _lossless_weight(n, k, rng)
+    x = workload.gen_x(2, k, seed=30)
+    E = oracle.exact_head(x, w_bits)
+    top = [int(np.argmax(E[i])) for i in range(2)]
+    for i in range(2):   # a twin of the row's winner in the same block
+        twin = top[i] + 1 if top[i] % 64 < 63 else top[i] - 1
+        w_bits[twin] = w_bits[top[i]]
+    E = oracle.exact_head(x, w_bits)
+    assert np.all(oracle.tie_rows(E))                        # full row: a tie in each row
+    packed, S, ZS = oracle.quantize_pack(w_bits)
+    out1 = oracle.pipeline(x, w_bits, packed, S, ZS, kcand=1, r=32)
+    assert np.array_equal(out1["coarse"], E)
+    assert not np.any(out1["tie_rows"])                      # reranked set: one of the twins only
+    out8 = oracle.pipeline(x, w_bits, packed, S, ZS, kcand=8, r=32)
+    assert np.all(out8["tie_rows"])                          # both twins reranked
+    for i in range(2):
+        twins = {int(v) for v in np.nonzero(E[i] == E[i].max())[0]}
+        assert out8["tied_ids"][i] == twins and int(out8["out_id"][i]) == min(twins)
+
+
+# ------------------------------------------------------- 4-bit pipeline pins
+@pytest.mark.parametrize("m,n,kc,r", [(1, 64, 1, 8), (2, 130, 4, 8), (2, 100, 1, 3)])
+def test_int4_pipeline_matches_exact_brute_force(m, n, kc, r):
+    """The 4-bit head, every step, against exact rationals: the brute force
+    scores each column in the page's form S sum x (1 + v/16) - ZS sum x from
+    its own half-split bytes, independently of the oracle's effective weight."""
+    k = 256
+    w = workload.gen_weight(n, k, seed=300 + n)
+    x = workload.gen_x(m, k, seed=400 + n)
+    ref = brute.run([[int(v) for v in row] for row in x], [[int(v) for v in row] for row in w], kc, r, bits=4)
+    packed4, S, ZS = oracle.quantize_pack_int4(w)
+    assert [[int(v) for v in row] for row in packed4] == ref["packed"]
+    assert [[int(v) for v in row] for row in S] == ref["S"]
+    assert [[int(v) for v in row] for row in ZS] == ref["ZS"]
+    c = oracle.coarse_int4(x, packed4, S, ZS)
+    exact = np.array([[float(v) for v in row] for row in ref["coarse"]])
+    assert np.allclose(c, exact, rtol=1e-12, atol=1e-12)
+    out = oracle.pipeline(x, w, packed4, S, ZS, kcand=kc, r=r, bits=4)
+    assert np.array_equal(out["coarse"], c)
+    assert np.array_equal(out["cand_id"], np.array([[cc for _, cc in row] for row in ref["cand"]]))
+    assert np.array_equal(out["rr_id"], np.array(ref["rr_id"]))
+    assert list(out["out_id"]) == ref["out_id"]
+    assert [float(v) for v in out["out_val"]] == [float(v) for v in ref["out_val"]]
+
+
+def test_int4_lossless_pipeline_is_the_exact_head():
+    """A weight already on a 16-level grid (power-of-two step, integer zero
+    point, codes 0 and 15 in every group): the 4-bit coarse scores equal the
+    exact head, and the pipeline's token is the exact argmax on every row."""
+    rng = np.random.default_rng(53)
+    n, k = 300, 512
+    codes = rng.integers(0, 16, size=(n, k)).astype(np.int64)
+    codes[:, ::128] = 0
+    codes[:, 1::128] = 15
+    s = 2.0 ** rng.integers(-10, -7, size=(n, k // 128))
+    z = rng.integers(0, 16, size=(n, k // 128)).astype(np.float64)
+    wf = (codes - np.repeat(z, 128, axis=1)) * np.repeat(s, 128, axis=1)
+    w_bits = workload.f32_to_bf16_bits(wf.astype(np.float32))
+    x = workload.gen_x(5, k, seed=54)
+    out = oracle.pipeline(x, w_bits, *oracle.quantize_pack_int4(w_bits), kcand=1, r=32, bits=4)
+    E = oracle.exact_head(x, w_bits)
+    assert np.array_equal(out["coarse"], E)
+    assert np.array_equal(out["out_id"], np.argmax(E.astype(np.float32), axis=1))
+
+
+def test_int4_coarse_is_the_split_of_a_long_int2_head():
+    """An exact identity of the 4-bit weight: code v = 4 vh + vl, so
+    (S/16) v - (ZS - S) = [(S/4) vh - (ZS - S)] + [(S/16) vl].  The 4-bit
+    coarse score equals the 2-bit oracle's score of the 2K-long head built
+    from those halves (second pair (S/4, S/4): weight (S/16) vl), in x' = (x, x)."""
+    n, k = 70, 512
+    w = workload.gen_weight(n, k, seed=55)
+    x = workload.gen_x(3, k, seed=56)
+    packed4, S, ZS = oracle.quantize_pack_int4(w)
+    v = oracle.unpack_half_split(packed4).astype(np.uint8)
+    codes2 = np.concatenate([v >> 2, v & 3], axis=1)
+    s_quarter = obf.from_f32((obf.to_f32(S) * np.float32(0.25)).astype(np.float32))
+    S2 = np.concatenate([S, s_quarter], axis=1)
+    ZS2 = np.concatenate([ZS, s_quarter], axis=1)
+    long = oracle.coarse(np.concatenate([x, x], axis=1), oracle.pack_quarter_split(codes2), S2, ZS2)
+    assert np.allclose(oracle.coarse_int4(x, packed4, S, ZS), long, rtol=1e-12, atol=1e-12)
+
+
+def test_final_argmax_nan_reading():
+    """The final argmax's reading for NaN exact values (hand-made rows): a NaN
+    never beats a number, -inf included; an all-NaN row returns its lowest id;
+    equal values go to the lower id; padding (-1) is skipped."""
+    ids = np.array([[5, 3, 9, -1], [4, 2, -1, -1], [1, 2, 3, 4], [7, 6, -1, -1], [8, -1, -1, -1]])
+    nan, inf = np.nan, np.inf
+    e = np.array([[nan, 2.0, 2.0, -inf], [nan, nan, -inf, -inf], [-inf, nan, -inf, 1.0],
+                  [nan, -inf, -inf, -inf], [-inf, -inf, -inf, -inf]])
+    out_id, out_val = oracle.final_argmax(ids, e)
+    assert [int(v) for v in out_id] == [3, 2, 4, 6, 8]
+    assert out_val[0] == 2.0 and np.isnan(out_val[1]) and out_val[2] == 1.0
+    assert np.isneginf(out_val[3]) and np.isneginf(out_val[4])
