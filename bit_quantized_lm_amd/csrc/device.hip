@@ -1845,6 +1845,19 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
   __syncthreads();
 }
 
+// (v, id) ranks above (bv, bi) in the final argmax: a larger value, or an
+// equal one with a lower id.  A NaN value (an NVFP4 row with a NaN block
+// scale) ranks below every number, -inf included; id < 0 is an empty slot
+// and never ranks above anything, bi < 0 (nothing yet) is below everything.
+__device__ __forceinline__ bool ranks_above(float v, int id, float bv, int bi) {
+  if (id < 0) return false;
+  if (bi < 0) return true;
+  const bool vn = v != v, bn = bv != bv;
+  if (vn != bn) return bn;
+  if (vn) return id < bi;
+  return v > bv || (v == bv && id < bi);
+}
+
 template <int NTHR, bool kArgmax, int kKind>
 __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part, int nparts) {
   constexpr int NW = NTHR / 64;
@@ -1881,7 +1894,7 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
       for (int q = lane; q < R; q += 64) {
         const int id = load_dev(A.rr_id + (size_t)m * R + q);
         const float v = load_dev(A.rr_val + (size_t)m * R + q);
-        if (bi < 0 || v > bv || (v == bv && id < bi)) {
+        if (ranks_above(v, id, bv, bi)) {
           bv = v;
           bi = id;
         }
@@ -1889,7 +1902,7 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
       for (int off = 32; off > 0; off >>= 1) {
         const float ov = __shfl_xor(bv, off, 64);
         const int oi = __shfl_xor(bi, off, 64);
-        if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+        if (ranks_above(ov, oi, bv, bi)) {
           bv = ov;
           bi = oi;
         }
@@ -1922,19 +1935,17 @@ __global__ __launch_bounds__(256) void argmax_kernel(const int32_t* __restrict__
   float bv = -__builtin_inff();
   int bi = -1;
   for (int r = lane; r < R; r += 64) {
-    int id = rr_id[(size_t)m * R + r];
-    if (id < 0) continue;
-    float v = rr_val[(size_t)m * R + r];
-    if (bi < 0 || v > bv || (v == bv && id < bi)) {
+    const int id = rr_id[(size_t)m * R + r];
+    const float v = rr_val[(size_t)m * R + r];
+    if (ranks_above(v, id, bv, bi)) {
       bv = v;
       bi = id;
     }
   }
   for (int off = 32; off > 0; off >>= 1) {
-    float ov = __shfl_xor(bv, off, 64);
-    int oi = __shfl_xor(bi, off, 64);
-    bool take = (oi >= 0) && (bi < 0 || ov > bv || (ov == bv && oi < bi));
-    if (take) {
+    const float ov = __shfl_xor(bv, off, 64);
+    const int oi = __shfl_xor(bi, off, 64);
+    if (ranks_above(ov, oi, bv, bi)) {
       bv = ov;
       bi = oi;
     }

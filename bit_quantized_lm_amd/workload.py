@@ -94,6 +94,21 @@ def e4m3_head(w_bits: np.ndarray):
     return out, scale
 
 
+def plant_codes(a: np.ndarray, rows, codes, frac: float = 0.02, seed: int = 5) -> np.ndarray:
+    """A copy of the byte array `a` [N][L] in which about `frac` of the bytes of
+    each row in `rows` are replaced by values drawn from `codes` (seeded):
+    the edge codes of a stored format (the e4m3 codes 0x7F / 0xFF, a NaN block
+    scale) placed where a test will read them."""
+    out = np.array(a, copy=True)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    codes = np.asarray(codes, dtype=out.dtype)
+    for r in rows:
+        cnt = max(1, int(round(frac * out.shape[1])))
+        pos = rng.choice(out.shape[1], size=cnt, replace=False)
+        out[r, pos] = rng.choice(codes, size=cnt)
+    return out
+
+
 E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 

@@ -1,4 +1,8 @@
-"""Comparison of the HIP path's outputs with the oracle's.
+"""Acceptance rules: comparison of the HIP path's outputs with the oracle's.
+
+Test infrastructure, like the rest of this package: used by the GPU parity
+tests and by the benchmark's CPU-baseline leg (which reports the counts this
+returns); never by the library.
 
 Acceptance rules:
 * ids (block candidate lists, row top-R lists, final tokens) are bit-exact,
@@ -10,7 +14,7 @@ Acceptance rules:
 * final ids may differ only on tie rows: rows whose two best exact logits
   (oracle, float64) differ by less than 1e-4 relative; there the GPU's id
   must still be one of the oracle's reranked ids within that window of the
-  best (oracle.tied_ids).  Counted.
+  best (head.tied_ids).  Counted.
 * coarse and candidate values: |gpu - ref| <= 2e-3 |ref| + 2e-3 rms(row);
   exact rerank values and the returned token's value (out_val, compared
   with the oracle's exact value of the GPU's token):
@@ -19,7 +23,7 @@ Every comparison uses oracle values of ids; no oracle input comes from the GPU.
 """
 import numpy as np
 
-import oracle
+from . import head as _head
 
 TAU_REL = 1e-5
 VAL_REL = 2e-3
@@ -110,7 +114,7 @@ def compare(ref, gpu, n, kcand, check_coarse=True):
     g_outv = gpu["out_val"].astype(np.float64)
     tied = ref.get("tied_ids")
     if tied is None:
-        tied = oracle.tied_ids(ref["rr_id"], ref["rr_val"])
+        tied = _head.tied_ids(ref["rr_id"], ref["rr_val"])
     for row in range(m):
         if g_out[row] != ref["out_id"][row]:
             assert ref["tie_rows"][row], f"row {row}: final id gpu {g_out[row]} oracle {ref['out_id'][row]}"

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from bit_quantized_lm_amd import workload
-from parity_util import compare
+from oracle.acceptance import compare
 
 
 @pytest.fixture(scope="module")

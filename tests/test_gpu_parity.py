@@ -16,7 +16,7 @@ import pytest
 import oracle
 from bit_quantized_lm_amd import _binding as B
 from bit_quantized_lm_amd import workload
-from parity_util import compare
+from oracle.acceptance import compare
 
 pytestmark = pytest.mark.gpu
 
@@ -232,8 +232,12 @@ def _prefix(ref, m):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("m", [1, 8, 72])
+@pytest.mark.parametrize("m", [1, 2, 8, 9, 16, 32, 48, 64, 72])
 def test_parity_full_shape(dev, full, m):
+    """The full shard (K = 5120, N = 124160) at the resident kernel's row
+    counts (1, 2, 8) and at every row-tile count of the many-row kernel
+    (9 and 16: one tile; 32, 48, 64, 72: two to five), coarse values
+    included; the rows are a prefix of the 72 the oracle scored once."""
     cfg = full["cfg"]
     got = run_gpu(full["head"], full["x"][:m], dev)
     stats = compare(_prefix(full["ref"], m), got, cfg.n, cfg.kcand)
@@ -381,6 +385,13 @@ def test_logits_row_end_to_end(dev, topk_only):
     assert np.all(np.abs(gv - wv)[fin] <= lim[fin])
 
 
+def _library_packed(w):
+    """The library's quantiser output, checked byte for byte against the oracle's."""
+    packed = B.draft_head_quantize_pack(w)
+    assert all(np.array_equal(a, b) for a, b in zip(packed, oracle.quantize_pack(w)))
+    return packed
+
+
 # ------------------------------------------------------- e4m3 rerank source
 def _e4m3_ref(x, w, packed, w8, wscale, kcand, r):
     """The oracle's pipeline with the rerank read from the e4m3 rows."""
@@ -406,11 +417,32 @@ def test_e4m3_rerank_parity(dev, m, k, n, kcand, r):
     w = workload.gen_weight(n, k, seed=2000 + n)
     x = workload.gen_x(m, k, seed=2001 + n)
     _log(f"e4m3 case m={m} k={k} n={n} kcand={kcand} r={r}")
-    packed = oracle.quantize_pack(w)
+    packed = _library_packed(w)
     head, w8, wscale = _e4m3_head(w, kcand, r, dev, packed=packed)
     got = run_gpu(head, x, dev)
     stats = compare(_e4m3_ref(x, w, packed, w8, wscale, kcand, r), got, n, kcand)
     _log(f"  ok {stats}")
+
+
+def test_e4m3_rerank_edge_codes(dev):
+    """e4m3 rows holding the codes 0x7F / 0xFF (the page's decode reads them as
+    +-480; the e4m3 format reserves them for NaN) in every head row, 2 % of
+    each row's bytes, so every reranked row carries some."""
+    m, k, n, kcand, r = 4, 1024, 5000, 8, 32
+    w = workload.gen_weight(n, k, seed=2100)
+    x = workload.gen_x(m, k, seed=2101)
+    packed = _library_packed(w)
+    w8, wscale = workload.e4m3_head(w)
+    w8 = workload.plant_codes(w8, range(n), [0x7F, 0xFF], frac=0.02, seed=2102)
+    assert np.any(w8 == 0x7F) and np.any(w8 == 0xFF)
+    head = B.DraftHead.from_weight(w, kcand=kcand, R=r, device=dev, packed=packed)
+    head.w = torch.from_numpy(w8).to(dev)
+    head.wscale = torch.from_numpy(wscale).to(dev)
+    got = run_gpu(head, x, dev)
+    ref = _e4m3_ref(x, w, packed, w8, wscale, kcand, r)
+    assert np.all(np.isfinite(ref["rr_val"]))
+    stats = compare(ref, got, n, kcand)
+    _log(f"e4m3 edge codes: {stats}")
 
 
 def test_e4m3_forward_matches_staged_calls(dev):
@@ -514,11 +546,43 @@ def test_nvfp4_rerank_parity(dev, m, k, n, kcand, r):
     w = workload.gen_weight(n, k, seed=4000 + n)
     x = workload.gen_x(m, k, seed=4001 + n)
     _log(f"nvfp4 case m={m} k={k} n={n} kcand={kcand} r={r}")
-    packed = oracle.quantize_pack(w)
+    packed = _library_packed(w)
     head, w4, bs, g = _nvfp4_head(w, kcand, r, dev, packed=packed)
     got = run_gpu(head, x, dev)
     stats = compare(_nvfp4_ref(x, w, packed, w4, bs, g, kcand, r), got, n, kcand)
     _log(f"  ok {stats}")
+
+
+@pytest.mark.parametrize("all_nan", [False, True])
+def test_nvfp4_nan_block_scale(dev, all_nan):
+    """NVFP4 rows with the block scale 0x7F (NaN through the e4m3 format):
+    the exact value of every such candidate is NaN on both sides, and a NaN
+    value never wins the final argmax (a number, -inf included, ranks above
+    it).  The rows of every row's oracle winner get a NaN block scale, so the
+    token must move to the next candidate; with all_nan, every block scale of
+    every head row is NaN and each row returns its lowest reranked id with
+    value NaN."""
+    m, k, n, kcand, r = 5, 1024, 5000, 8, 32
+    w = workload.gen_weight(n, k, seed=4200)
+    x = workload.gen_x(m, k, seed=4201)
+    packed = _library_packed(w)
+    w4, bs, g = workload.nvfp4_head(w)
+    if all_nan:
+        bs = np.full_like(bs, 0x7F)
+    else:
+        first = oracle.pipeline(x, w, *packed, kcand=kcand, r=r)
+        bs = workload.plant_codes(bs, sorted({int(v) for v in first["out_id"]}), [0x7F], frac=0.05, seed=4202)
+    head = B.DraftHead.from_weight(w, kcand=kcand, R=r, device=dev, packed=packed)
+    head.w, head.bscale, head.gscale = _nvfp4_dev(w4, bs, g, dev)
+    got = run_gpu(head, x, dev)
+    ref = _nvfp4_ref(x, w, packed, w4, bs, g, kcand, r)
+    assert np.any(np.isnan(ref["rr_val"]))
+    if all_nan:
+        assert np.array_equal(ref["out_id"], ref["rr_id"].min(axis=1, where=ref["rr_id"] >= 0, initial=n))
+    else:
+        assert not np.any(np.isin(ref["out_id"], first["out_id"]))
+    stats = compare(ref, got, n, kcand)
+    _log(f"nvfp4 NaN block scales (all={all_nan}): {stats}")
 
 
 def test_nvfp4_forward_matches_staged_calls(dev):
@@ -629,10 +693,12 @@ def test_int4_parity(dev, m, k, n, kcand, r):
     w = workload.gen_weight(n, k, seed=3000 + n)
     x = workload.gen_x(m, k, seed=3001 + n)
     _log(f"int4 case m={m} k={k} n={n} kcand={kcand} r={r}")
-    packed4 = oracle.quantize_pack_int4(w)
+    packed4 = B.draft_head_quantize_pack_int4(w)
+    opacked4 = oracle.quantize_pack_int4(w)
+    assert all(np.array_equal(a, b) for a, b in zip(packed4, opacked4))
     head = B.DraftHead.from_weight(w, kcand=kcand, R=r, device=dev, packed=packed4, bits=4)
     got = run_gpu(head, x, dev)
-    stats = compare(oracle.pipeline(x, w, *packed4, kcand=kcand, r=r, bits=4), got, n, kcand)
+    stats = compare(oracle.pipeline(x, w, *opacked4, kcand=kcand, r=r, bits=4), got, n, kcand)
     _log(f"  ok {stats}")
 
 
@@ -684,9 +750,11 @@ def test_int4_recall_stress_full_shape(dev, full):
     x = full["x"][:cfg.m]
     w, pairs = workload.plant_recall_pairs(x, full["w"], target=12.0, gap=0.01)
     packed4 = B.draft_head_quantize_pack_int4(w)
+    opacked4 = oracle.quantize_pack_int4(w)
+    assert all(np.array_equal(a, b) for a, b in zip(packed4, opacked4))
     head = B.DraftHead.from_weight(w, kcand=1, R=32, device=dev, packed=packed4, bits=4)
     got = run_gpu(head, x, dev, want_coarse=False)
-    c = oracle.coarse_int4(x, *packed4)
+    c = oracle.coarse_int4(x, *opacked4)
     cv, ci = oracle.block_topk(c, 1)
     rr_id, _ = oracle.row_topr(cv, ci, 32)
     e = oracle.rerank_exact(x, w, rr_id)
