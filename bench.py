@@ -16,7 +16,13 @@ Prints one JSON line:
                duration (HIP events set by the kernel's own dispatch on the
                launch stream, in a second pass of as many calls) vs 8 TB/s
   cpu_baseline the CPU oracle timed on this host, one full call each at
-               M = 1, 8, 72 (value: M = 1)
+               M = 1, 8, 72 (value: M = 1), with the CPU model, the cores
+               visible and the BLAS threads
+  extra.parity the acceptance report on the same inputs: per M = 1, 8, 72
+               the comparator's counts (tie rows, excused near-tie lists,
+               final-id differences on tie rows, value errors) and the argmax
+               agreement with the exact bf16 head; the recall-stress case
+               (M = 32, KCAND = 8 and 1) with its argmax misses
   extra        per-M (1, 8, 72) times with the coarse kernel's p10/p50/p90 and
                its fractions of the HBM and bf16 MFMA peaks, the warm
                (cache-resident) figure, the time of the row handed to a
@@ -324,37 +330,137 @@ class Rig:
         return 2 * (mib << 20) / t / 1e9
 
 
-def cpu_baseline(x_host):
-    """The oracle, untuned, on one full call each at M = 1, 8 and 72 (dequantise
-    from the packed arrays, float64 GEMV, block top-8, row top-32, exact
-    rerank, argmax); the value is the M = 1 call's."""
-    import oracle
-    from bit_quantized_lm_amd import workload
+def host_cpu():
+    """CPU model, cores visible to this process, logical CPUs of the host, and
+    the BLAS thread count numpy runs with."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        blas_threads = None
-    w = workload.gen_weight(N, K)
-    packed = oracle.quantize_pack(w)
+        blas = None
+    return {"model": model or platform.machine(), "cores": len(os.sched_getaffinity(0)),
+            "host_logical_cpus": os.cpu_count(), "blas_threads": blas}
+
+
+def cpu_baseline(x_host, w_host):
+    """The oracle, untuned, on one full call each at M = 1, 8 and 72 (dequantise
+    from the packed arrays, float64 GEMV, block top-8, row top-32, exact
+    rerank, argmax); the value is the M = 1 call's.  Also returns the oracle's
+    packed arrays and its M = 72 outputs (the rows are independent, so M = 1
+    and 8 are prefixes) for the acceptance report."""
+    import oracle
+    cpu = host_cpu()
+    packed = oracle.quantize_pack(w_host)
     per_m = {}
+    ref = None
     for m in (1, 8, 72):
         x = x_host[:m]
         t0 = time.perf_counter()
         c = oracle.coarse(x, *packed)
         cv, ci = oracle.block_topk(c, KCAND)
         rr_id, _ = oracle.row_topr(cv, ci, R)
-        e = oracle.rerank_exact(x, w, rr_id)
-        oracle.final_argmax(rr_id, e)
+        e = oracle.rerank_exact(x, w_host, rr_id)
+        out_id, out_val = oracle.final_argmax(rr_id, e)
         per_m[str(m)] = round((time.perf_counter() - t0) * 1e6, 1)
+        ref = {"coarse": c, "cand_val": cv, "cand_id": ci, "rr_id": rr_id, "rr_val": e,
+               "out_id": out_id, "out_val": out_val, "tie_rows": oracle.tie_rows(e),
+               "tied_ids": oracle.tied_ids(rr_id, e)}
     t = per_m["1"] / 1e6
-    cores = len(os.sched_getaffinity(0))
-    return {"value": round(WEIGHT_BYTES / t / 1e9, 4), "unit": "GB/s", "us_per_call": per_m["1"],
+    base = {"value": round(WEIGHT_BYTES / t / 1e9, 4), "unit": "GB/s", "us_per_call": per_m["1"],
             "us_per_call_per_m": per_m,
-            "cores": int(blas_threads or cores), "host_cores_visible": cores, "kind": "oracle",
-            "cpu": platform.processor() or platform.machine(),
+            "cores": int(cpu["blas_threads"] or cpu["cores"]), "cpu": cpu["model"],
+            "host_cores_visible": cpu["cores"], "host_logical_cpus": cpu["host_logical_cpus"],
+            "blas_threads": cpu["blas_threads"], "kind": "oracle",
             "sample": "one full call each at M=1, 8, 72, K=5120, N=124160 (dequantise + float64 GEMV + "
-                      "selection + rerank + argmax); value from M=1; quantisation not timed"}
+                      "selection + rerank + argmax); value from M=1; quantisation not timed; cores = the "
+                      "BLAS threads the oracle's GEMV ran on"}
+    return base, packed, ref
+
+
+def _prefix(ref, m):
+    return {k: (v[:m] if isinstance(v, (np.ndarray, list)) else v) for k, v in ref.items()}
+
+
+def acceptance_report(rig, packed, ref):
+    """The acceptance figures on the benchmark's own inputs (part of the CPU
+    baseline leg: the oracle's outputs against the GPU's on the same seeded
+    inputs).  Per M = 1, 8, 72: the comparator's counts (tie rows, near-tie
+    block and rerank lists it excused, final-id differences on tie rows, the
+    largest value errors) and the argmax agreement of the GPU and of the
+    oracle with the exact bf16 head; then the recall-stress case (M = 32,
+    planted same-block pairs with a 0.01 logit gap) at KCAND = 8 and 1: parity
+    with the oracle and the argmax misses against the planted winners."""
+    import oracle
+    from oracle.acceptance import compare
+    from bit_quantized_lm_amd import workload
+    torch, B = rig.torch, rig.B
+    x_host, w_host = rig.x_host, rig.w_host
+    t0 = time.perf_counter()
+    E = oracle.exact_head(x_host[:72], w_host)
+    exact_id = np.argmax(E, axis=1)
+    res = {"per_m": {}}
+    head = rig.heads[0]
+    for m in (1, 8, 72):
+        coarse = torch.empty((m, N), dtype=torch.float32, device=rig.dev)
+        out = head(rig.x[:m], coarse_out=coarse)
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in out.items()}
+        got["coarse"] = coarse.cpu().numpy()
+        st = compare(_prefix(ref, m), got, N, KCAND)
+        st["argmax_agree_exact_head_gpu"] = int(np.sum(got["out_id"] == exact_id[:m]))
+        st["argmax_agree_exact_head_oracle"] = int(np.sum(ref["out_id"][:m] == exact_id[:m]))
+        st["parity"] = "pass"
+        res["per_m"][str(m)] = st
+        log(f"acceptance M={m}: {st}")
+    # recall stress: only the planted rows of W change, so the oracle quantises
+    # those rows and keeps its own arrays for the rest (rows are independent)
+    cfg = workload.CONFIGS["recall"]
+    xr = x_host[:cfg.m]
+    wp, pairs = workload.plant_recall_pairs(xr, w_host, target=12.0, gap=0.01)
+    rows = sorted({c for p in pairs for c in p})
+    opacked = [a.copy() for a in packed]
+    for a, b in zip(opacked, oracle.quantize_pack(wp[rows])):
+        a[rows] = b
+    lpacked = B.draft_head_quantize_pack(wp)
+    same_bytes = all(np.array_equal(a, b) for a, b in zip(lpacked, opacked))
+    c = oracle.coarse(xr, *opacked)
+    winners = np.array([p[0] for p in pairs])
+    tiled, tpairs = B.draft_head_tile(*lpacked)
+    t_t = torch.from_numpy(tiled).to(rig.dev)
+    t_p = torch.from_numpy(tpairs.view(np.int32)).to(rig.dev)
+    t_w = torch.from_numpy(wp.view(np.int16)).to(rig.dev)
+    rec = {"rows": cfg.m, "quantiser_bytes_equal": bool(same_bytes)}
+    for kc in (8, 1):
+        h = B.DraftHead(t_t, t_p, t_w, N, K, kc, R)
+        out = h(rig.x[:cfg.m])
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in out.items()}
+        cv, ci = oracle.block_topk(c, kc)
+        rr_id, _ = oracle.row_topr(cv, ci, R)
+        e = oracle.rerank_exact(xr, wp, rr_id)
+        out_id, out_val = oracle.final_argmax(rr_id, e)
+        r = {"coarse": c, "cand_val": cv, "cand_id": ci, "rr_id": rr_id, "rr_val": e, "out_id": out_id,
+             "out_val": out_val, "tie_rows": oracle.tie_rows(e), "tied_ids": oracle.tied_ids(rr_id, e)}
+        st = compare(r, got, N, kc, check_coarse=False)
+        rec[f"kcand{kc}"] = {"misses_gpu": int(np.sum(got["out_id"] != winners)),
+                             "misses_oracle": int(np.sum(out_id != winners)),
+                             "tie_rows": st["tie_rows"], "blocks_excused": st["blocks_excused"],
+                             "rows_rr_excused": st["rows_rr_excused"],
+                             "final_mismatch_on_tie_rows": st["final_mismatch_on_tie_rows"], "parity": "pass"}
+    del t_t, t_p, t_w
+    res["recall_stress"] = rec
+    res["seconds"] = round(time.perf_counter() - t0, 1)
+    log(f"acceptance recall stress: {rec}")
+    return res
 
 
 def load_traffic(m):
@@ -453,8 +559,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (one full call at M = 1, 8, 72)")
-        cpu = cpu_baseline(rig.x_host)
+        cpu, opacked, ref = cpu_baseline(rig.x_host, rig.w_host)
         log(f"cpu oracle: {cpu}")
+        log("acceptance: the GPU's outputs against the oracle's on the same inputs")
+        extra["parity"] = acceptance_report(rig, opacked, ref)
 
     line = {
         "metric": "us/call + HBM GB/s (% peak), 2-bit draft head K=5120 N=124160, M=1/8/72",

@@ -114,7 +114,7 @@ struct RerankArgs {
   float* rr_val;
   int32_t* out_id;
   float* out_val;
-  uint32_t* cnt;
+  unsigned long long* hand;   // per-row hand-off words (rows split over several workgroups)
 };
 
 struct CoarseArgs {
@@ -126,32 +126,19 @@ struct CoarseArgs {
   float* cand_val;
   int32_t* cand_id;
   float* coarse_out;
-  uint32_t* cnt;   // per-row arrival counters of the rerank; workgroup 0 zeroes cnt[0..ncnt)
+  unsigned long long* hand;   // per-row hand-off words of the rerank; workgroup 0 zeroes hand[0..ncnt)
   int ncnt;
   int kx;          // row length of x: K, or K / 2 for a 4-bit head run at length K (x' = (x, x))
 };
 
-// Device-coherent stores and loads (agent scope: written through to, and read
-// from, the level every XCD shares) and a wait for this wave's stores.  Data
-// handed between workgroups of one launch goes through these, so that no
-// release fence (an L2 write-back, costly when every workgroup issues one) is
-// needed: the writer stores, waits, then counts itself with an atomic; the
-// reader sees the count, then loads.
-template <class T>
-__device__ __forceinline__ void store_dev(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <class T>
-__device__ __forceinline__ T load_dev(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Counters are only ever written with device-coherent stores and atomics: a
-// plain store would leave a dirty L2 line whose later write-back could undo
-// atomic updates made meanwhile by other XCDs.
+// The rerank's per-row hand-off words are only ever written with agent-scope
+// atomics (a plain store would leave a dirty L2 line whose later write-back
+// could undo atomic updates made meanwhile on other XCDs).  The coarse kernel
+// of each call zeroes them; the next kernel on the stream sees the zeros
+// (kernel boundary).
 __device__ __forceinline__ void zero_counters(const CoarseArgs& A) {
-  if (blockIdx.x == 0 && (int)threadIdx.x < A.ncnt) store_dev(A.cnt + threadIdx.x, 0u);
+  if (blockIdx.x == 0 && (int)threadIdx.x < A.ncnt)
+    __hip_atomic_store(A.hand + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One group: MFMAs of the (h, e) fragments for all tiles, then the scale update.
@@ -1671,11 +1658,12 @@ __device__ __forceinline__ int lane_prefix(unsigned long long bal) {
 
 // Rerank of one row split over `nparts` workgroups of NTHR threads (NW = NTHR/64
 // waves each).  Every part of row m computes the row's top-R list (the same
-// list in every part), then each of its waves computes the exact logit of one
-// rank, r = NW * part + wave, so the R rows of W are read by R waves at once.
-// With kArgmax the last part of the row to finish (a per-row arrival counter,
-// zeroed by the coarse kernel of the same call and reset here) takes the
-// argmax over the R logits.
+// list in every part), then each of its waves computes the exact logits of
+// ranks r = NW (part + nparts i) + wave, so the R rows of W are read by up to
+// NW * nparts waves at once.  With kArgmax each part takes the best of its
+// ranks, and the last part of the row to finish (a per-row arrival counter,
+// zeroed by the coarse kernel of the same call and reset here) takes the best
+// of the parts' bests.
 //
 // The list (block-maximum selection; the candidates are the ones
 // draft_head_coarse writes, so slot b*kcand holds block b's maximum and slot
@@ -1690,13 +1678,13 @@ __device__ __forceinline__ int lane_prefix(unsigned long long bal) {
 //   2. The candidates >= T' of the blocks whose maximum is >= T' survive
 //      (at least R, at most DH_MAX_R); each is ranked by counting the
 //      survivors above it, and the first R ranks are the list.
-constexpr int kWideThreads = 256;
-// From this many rows on, 1024 threads per workgroup (two per row at R = 32):
-// each workgroup recomputes its row's list, and at many rows that redundant
-// work outweighs the latency of more dots per workgroup (M = 72: 6 us less per
-// call; no difference at 16).
-constexpr int kWideBigM = 32;
-constexpr int kWideBigThreads = 1024;
+// Eight waves per workgroup, four workgroups per row at R = 32: measured per
+// call (K = 5120, N = 124160) against four waves in eight parts, sixteen in
+// two and sixteen in one: 41.2 / 42.5 / 42.9 / 45.3 us at M = 1, 46.4 / 48.2
+// / 48.3 / 50.0 us at M = 8, within 0.3 us of each other at M = 72 except
+// four waves (+3 us): fewer parts repeat the list less, but load the R rows
+// of W through fewer CUs.
+constexpr int kWideThreads = 512;
 
 struct WideShared {
   unsigned int hist[256];
@@ -1706,7 +1694,7 @@ struct WideShared {
   unsigned long long list[DH_MAX_R];
   unsigned long long T;
   int nq, ns, qcur;
-  int last;
+  uint32_t wbest[16][2];   // per wave: its best exact logit (value bits, id)
 };
 
 static_assert(64 * kFastNV * sizeof(uint32_t) <= sizeof(WideShared::keys), "block maxima staged in keys");
@@ -1845,6 +1833,29 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
   __syncthreads();
 }
 
+// A row's hand-off word between the parts of its rerank: bits 63..4 the best
+// (value, id) seen so far as a 60-bit key that orders exactly as ranks_above
+// does, bits 3..0 the number of parts counted.  Key: the value's
+// order-preserving 32 bits (-0 taken as +0; a NaN as 0, below -inf's key),
+// then 2^28 - 1 - id (a lower id above), so that 0 is "nothing yet" and no
+// candidate's key is 0 (ids are below 2^28 - 1).
+constexpr int kHandIdBits = 28;
+__device__ __forceinline__ unsigned long long hand_key(float v, int id) {
+  if (id < 0) return 0ull;
+  const uint32_t vk = v != v ? 0u : f32_key(v + 0.0f);
+  return ((unsigned long long)vk << kHandIdBits) | (unsigned long long)((1u << kHandIdBits) - 1u - (uint32_t)id);
+}
+__device__ __forceinline__ void hand_decode(unsigned long long key, float& v, int& id) {
+  if (key == 0ull) {
+    v = -__builtin_inff();
+    id = -1;
+    return;
+  }
+  const uint32_t vk = (uint32_t)(key >> kHandIdBits);
+  v = vk == 0u ? __builtin_nanf("") : key_f32(vk);
+  id = (int)((1u << kHandIdBits) - 1u - (uint32_t)(key & ((1u << kHandIdBits) - 1u)));
+}
+
 // (v, id) ranks above (bv, bi) in the final argmax: a larger value, or an
 // equal one with a lower id.  A NaN value (an NVFP4 row with a NaN block
 // scale) ranks below every number, -inf included; id < 0 is an empty slot
@@ -1858,6 +1869,12 @@ __device__ __forceinline__ bool ranks_above(float v, int id, float bv, int bi) {
   return v > bv || (v == bv && id < bi);
 }
 
+constexpr int kMaxParts = 8;   // workgroups one row's exact logits are split over, at most
+
+// Ranks r = NW (part + nparts i) + wave of row m: this part's share of the
+// exact logits.  With kArgmax the part also takes the best of its ranks; a
+// row split over several parts hands the parts' bests to the part that
+// arrives last.
 template <int NTHR, bool kArgmax, int kKind>
 __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part, int nparts) {
   constexpr int NW = NTHR / 64;
@@ -1865,58 +1882,75 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
   const int R = A.R, K = A.K;
   rerank_list<NTHR>(sh, A, m);
 
-  // the exact logit of rank r: this wave reads W[id] and x[m] once, all loads in flight
-  const int r = NW * part + wave;
-  // An empty rank (key 0: fewer survivors than R, which candidates written
-  // by the coarse pass never leave) is (-1, -inf) and reads no row.
-  if (r < R) {
+  // the exact logit of rank r: this wave reads W[id] and x[m] once, all
+  // loads in flight.  An empty rank (key 0: fewer survivors than R, which
+  // candidates written by the coarse pass never leave) is (-1, -inf) and
+  // reads no row.
+  float bv = -__builtin_inff();
+  int bi = -1;
+  for (int r = NW * part + wave; r < R; r += NW * nparts) {   // wave-uniform
     const unsigned long long key = sh.list[r];
-    const uint32_t id = key_id(key);
-    const float sum = key ? wave_dot<kKind>(A.src, id, A.x + (size_t)m * K, K, lane) : -__builtin_inff();
+    const int id = key ? (int)key_id(key) : -1;
+    const float sum = key ? wave_dot<kKind>(A.src, (uint32_t)id, A.x + (size_t)m * K, K, lane) : -__builtin_inff();
     if (lane == 0) {
-      store_dev(A.rr_id + (size_t)m * R + r, key ? (int32_t)id : -1);
-      store_dev(A.rr_val + (size_t)m * R + r, sum);
+      A.rr_id[(size_t)m * R + r] = id;
+      A.rr_val[(size_t)m * R + r] = sum;
+    }
+    if (ranks_above(sum, id, bv, bi)) {
+      bv = sum;
+      bi = id;
     }
   }
   if constexpr (kArgmax) {
-    // Every wave's logits are written through before the part is counted (a
-    // barrier alone does not wait for other waves' stores).
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t old = atomicAdd(A.cnt + m, 1u);
-      sh.last = old == (uint32_t)nparts - 1;
+    // the part's best: each wave's, then thread 0 over the NW waves
+    if (lane == 0) {
+      sh.wbest[wave][0] = __float_as_uint(bv);
+      sh.wbest[wave][1] = (uint32_t)bi;
     }
     __syncthreads();
-    if (sh.last && wave == 0) {
-      float bv = -__builtin_inff();
-      int bi = -1;
-      for (int q = lane; q < R; q += 64) {
-        const int id = load_dev(A.rr_id + (size_t)m * R + q);
-        const float v = load_dev(A.rr_val + (size_t)m * R + q);
+    if (tid == 0) {
+      for (int w = 1; w < NW; ++w) {
+        const float v = __uint_as_float(sh.wbest[w][0]);
+        const int id = (int)sh.wbest[w][1];
         if (ranks_above(v, id, bv, bi)) {
           bv = v;
           bi = id;
         }
       }
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (ranks_above(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (lane == 0) {
+      if (nparts == 1) {
         A.out_id[m] = bi;
         A.out_val[m] = bv;
-        store_dev(A.cnt + m, 0u);   // ready for the next call
+      } else {
+        // Several parts: each folds its best into the row's hand-off word
+        // with one compare-and-swap, which also counts the part; the part
+        // that brings the count to nparts holds the row's best and writes it.
+        // Everything handed over travels in that one atomic word, so no
+        // other memory has to be made visible between the workgroups.
+        unsigned long long* word = A.hand + m;
+        const unsigned long long mine = hand_key(bv, bi);
+        unsigned long long old = 0ull, next;
+        for (;;) {
+          const unsigned long long best = (old >> 4) > mine ? old >> 4 : mine;
+          next = (best << 4) | ((old & 15ull) + 1ull);
+          unsigned long long seen = old;
+          if (__hip_atomic_compare_exchange_strong(word, &seen, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT))
+            break;
+          old = seen;
+        }
+        if ((int)(next & 15ull) == nparts) {
+          hand_decode(next >> 4, bv, bi);
+          A.out_id[m] = bi;
+          A.out_val[m] = bv;
+          // ready for the next call (ordered before it by the kernel boundary)
+          __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   }
 }
 
-// Rerank kernel: grid (ceil(R / (NTHR / 64)), M), one part of one row per workgroup.
+// Rerank kernel: grid (nparts, M), one part of one row per workgroup.
 template <bool kArgmax, int kKind, int NTHR>
 __global__ __launch_bounds__(NTHR) void rerank_wide_kernel(RerankArgs A) {
   __shared__ WideShared sh;
@@ -2050,14 +2084,14 @@ int resident_rows(int M, int K) {
 // ks: the staged row length of x (K, or K/2 for a 4-bit head in its 2K-long form).
 bool use_resident(int M, int ks) { return M <= 8 && resident_lds_bytes(ks, resident_rows(M, ks)) <= kMaxLds; }
 
-// Workspace: the rerank's per-row arrival counters, then (many-row kernel
+// Workspace: the rerank's per-row hand-off words, then (many-row kernel
 // only) the x of one launch.
-constexpr size_t kCounterBytes = DH_MAX_M * sizeof(uint32_t);
+constexpr size_t kHeaderBytes = DH_MAX_M * sizeof(unsigned long long);
 
 // ks: the staged row length of x when it differs from K (0: K).
 size_t coarse_workspace_bytes(int M, int K, int ks = 0) {
-  if (use_resident(M, ks ? ks : K)) return kCounterBytes;
-  return kCounterBytes + big_workspace_bytes(std::min((M + 15) / 16, kMaxMT), K);
+  if (use_resident(M, ks ? ks : K)) return kHeaderBytes;
+  return kHeaderBytes + big_workspace_bytes(std::min((M + 15) / 16, kMaxMT), K);
 }
 
 int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
@@ -2129,7 +2163,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
   const int ncand = nblk * kcand;
   CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
                reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out,
-               static_cast<uint32_t*>(workspace), M, kx ? kx : K};
+               static_cast<unsigned long long*>(workspace), M, kx ? kx : K};
   hipError_t e = hipSuccess;
   const int ks = A.kx;   // the row length of x the resident kernel stages
   if (use_resident(M, ks)) {
@@ -2154,7 +2188,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
     B.coarse_out = coarse_out ? coarse_out + (size_t)m0 * N : nullptr;
     B.ncnt = m0 == 0 ? M : 0;
     const int mt = (B.M + 15) / 16, mp = 16 * mt;
-    u32x4* xslab = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(workspace) + kCounterBytes);
+    u32x4* xslab = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(workspace) + kHeaderBytes);
     u32x4* zslab = xslab + (size_t)(K / DH_GROUP) * 256 * mt;
     hipLaunchKernelGGL(prep_x_kernel, dim3((mp * NG4 + 3) / 4), dim3(256), 0, s, B.x, B.M, mp, K, A.kx,
                        xslab, zslab);
@@ -2189,12 +2223,14 @@ bool fast_rerank(int N, int ncand, int R, int& nblk, int& kcand) {
 template <bool kArgmax>
 hipError_t launch_wide(const void* x, const RowSrc& src, int M, int K, int N, const float* cand_val,
                        const int32_t* cand_id, int nblk, int kcand, int R, int32_t* rr_id, float* rr_val,
-                       int32_t* out_id, float* out_val, uint32_t* cnt, hipStream_t s) {
+                       int32_t* out_id, float* out_val, unsigned long long* hand, hipStream_t s) {
   const RerankArgs A{static_cast<const uint16_t*>(x), src, K, N, cand_val,
-                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, cnt};
+                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, hand};
   auto go = [&](auto nthr) {
     constexpr int NTHR = decltype(nthr)::value, NW = NTHR / 64;
-    const dim3 grid((R + NW - 1) / NW, M);
+    // ids must fit the hand-off key to split a row; otherwise one part per row
+    const int parts = (!kArgmax || N < (1 << kHandIdBits) - 1) ? std::min((R + NW - 1) / NW, kMaxParts) : 1;
+    const dim3 grid(parts, M);
     if (src.kind == kRowsE4m3)
       hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsE4m3, NTHR>), grid, dim3(NTHR), 0, s, A);
     else if (src.kind == kRowsNvfp4)
@@ -2202,8 +2238,7 @@ hipError_t launch_wide(const void* x, const RowSrc& src, int M, int K, int N, co
     else
       hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsBf16, NTHR>), grid, dim3(NTHR), 0, s, A);
   };
-  if (M >= kWideBigM) go(std::integral_constant<int, kWideBigThreads>{});
-  else go(std::integral_constant<int, kWideThreads>{});
+  go(std::integral_constant<int, kWideThreads>{});
   return hipGetLastError();
 }
 
@@ -2418,7 +2453,7 @@ int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const
   int nblk, kc;
   if (fast_rerank(N, ncand, R, nblk, kc)) {   // rerank and argmax in one kernel
     hipError_t e = launch_wide<true>(x, src, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val, out_id, out_val,
-                                     static_cast<uint32_t*>(workspace), s);
+                                     static_cast<unsigned long long*>(workspace), s);
     if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_wide_kernel: %s", hipGetErrorString(e));
     return dh::ok();
   }

@@ -23,7 +23,7 @@
  *     except DH_EHIP can be provoked without a GPU.
  *   - The caller owns every buffer.  The library allocates no device memory
  *     and keeps no state between calls; the scratch memory the coarse pass
- *     and the one-call path need (counters, and for more than 8 rows x laid
+ *     and the one-call path need (hand-off words, and for more than 8 rows x laid
  *     out for the many-row kernel) is the caller's workspace of
  *     draft_head_workspace_bytes() bytes.
  *   - Device functions enqueue work asynchronously on `stream` (a hipStream_t
@@ -138,12 +138,13 @@ int draft_head_int4_as_int2(const uint8_t* packed4, const uint16_t* S, const uin
 
 /*
  * Bytes of device workspace draft_head_coarse / draft_head_forward need for M
- * rows of length K: 512 bytes of per-row counters, plus, unless M <= 8 and
- * the resident kernel holds all of x in LDS (any K at M = 1; K <= 35840,
- * 15872, 7680 at M = 2, 3..4, 5..8), the x of one launch of up to 80 rows
- * laid out for the many-row kernel: (K/128) * 4096 * MT + (K/512) * 4096
- * bytes with MT = min(ceil(M/16), 5) (860,672 bytes in all at M = 72,
- * K = 5120).
+ * rows of length K: 1,024 bytes of per-row hand-off words for the one-call
+ * path's rerank (a row's exact logits may be split over several workgroups),
+ * plus, unless M <= 8 and the resident kernel holds all of x in LDS (any K at
+ * M = 1; K <= 35840, 15872, 7680 at M = 2, 3..4, 5..8), the x of one launch
+ * of up to 80 rows laid out for the many-row kernel: (K/128) * 4096 * MT +
+ * (K/512) * 4096 bytes with MT = min(ceil(M/16), 5) (861,184 bytes in all at
+ * M = 72, K = 5120).
  * Errors: DH_EINVAL (null pointer, M < 1), DH_EUNSUP (M > DH_MAX_M), DH_ESHAPE.
  */
 int draft_head_workspace_bytes(int M, int K, size_t* bytes);

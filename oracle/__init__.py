@@ -23,6 +23,9 @@ head     coarse scores, block top-KCAND, row top-R, exact rerank (bf16 rows,
          bf16 head (for agreement reports only).
 brute    pure-Python, exact-rational re-statement of every step for tiny
          shapes; pins the vectorised code.
+acceptance
+         the acceptance rules: a HIP result against the oracle's (ids exact
+         up to counted near-ties and tie rows, values within tolerance).
 
 Every function cites the passage it follows.  Where the page is silent the
 reading taken is stated in the docstring; all readings are listed in the
@@ -35,7 +38,7 @@ The page's real-data claims (argmax agreement on 8192 captured serve inputs,
 the ~5% top-1 change of the unreranked head) are parity unpinned: the captured
 inputs and the real weights are not available.
 """
-from . import bf16, quant, head, brute  # noqa: F401
+from . import bf16, quant, head, brute, acceptance  # noqa: F401
 from .quant import (GROUP, quantize, pack_quarter_split, unpack_quarter_split,  # noqa: F401
                     effective_weight, quantize_pack, quantize_int4, pack_half_split, unpack_half_split,
                     quantize_pack_int4, effective_weight_int4)

@@ -307,7 +307,7 @@ def test_forward_matches_staged_calls(dev, n, m):
 def test_workspace_reuse_leaves_counters_zero(dev):
     """One workspace serves calls of several row counts in a row (resident
     and many-row coarse kernels); each result equals a call with a fresh
-    workspace, and the per-row counters end at zero."""
+    workspace, and the per-row hand-off words of the rerank end at zero."""
     n, k = 20000, 1024
     w = workload.gen_weight(n, k, seed=95)
     x = _to_dev(workload.gen_x(20, k, seed=96), dev)
@@ -319,7 +319,7 @@ def test_workspace_reuse_leaves_counters_zero(dev):
         torch.cuda.synchronize()
         for key in want:
             assert torch.equal(got[key], want[key]), (m, key)
-        assert int(torch.count_nonzero(ws[:512])) == 0, m
+        assert int(torch.count_nonzero(ws[:1024])) == 0, m
 
 
 @pytest.mark.parametrize("words", [4, 1000, 2048 * 4 * 3 + 4 * 5, (3 << 20) + 12])

@@ -141,17 +141,18 @@ def test_quantize_pack_validation(lib):
 
 
 def test_workspace_bytes(lib):
-    # 512 bytes of per-row counters; the resident kernel (up to 8 rows while x
-    # fits its LDS) needs nothing more
+    # 1 KiB of per-row hand-off words (128 rows, 8 bytes); the resident
+    # kernel (up to 8 rows while x fits its LDS) needs nothing more
     # (LDS (K/128) * (256 MP + 4 MP) + blocks * MP * 256 within 160 KB)
+    head = 1024
     for m, k in ((1, 5120), (1, 65536), (2, 39424), (4, 19456), (8, 5120), (8, 8704)):
-        assert B.draft_head_workspace_bytes(m, k) == 512, (m, k)
+        assert B.draft_head_workspace_bytes(m, k) == head, (m, k)
     # many-row kernel: + (K/128) * 4096 * MT + (K/512) * 4096 with MT = min(ceil(M/16), 5)
     for m, k in ((2, 39936), (4, 19968), (8, 9216), (9, 512), (16, 1024), (17, 1024), (72, 5120),
                  (80, 5120), (81, 5120), (128, 5120)):
         mt = min((m + 15) // 16, 5)
-        assert B.draft_head_workspace_bytes(m, k) == 512 + (k // 128) * 4096 * mt + (k // 512) * 4096, (m, k)
-    assert B.draft_head_workspace_bytes(72, 5120) == 860_672
+        assert B.draft_head_workspace_bytes(m, k) == head + (k // 128) * 4096 * mt + (k // 512) * 4096, (m, k)
+    assert B.draft_head_workspace_bytes(72, 5120) == 861_184
     out = ctypes.c_size_t()
     _err(lib, lib.draft_head_workspace_bytes(1, 512, None), B.DH_EINVAL)
     _err(lib, lib.draft_head_workspace_bytes(0, 512, ctypes.byref(out)), B.DH_EINVAL)
@@ -167,7 +168,7 @@ def test_coarse_validation(lib, via):
     else:
         f = lambda *a: lib.draft_head_coarse(*a)  # noqa: E731
     ok = dict(x=FAKE, M=1, K=512, N=64, tiled=FAKE, pairs=FAKE, kc=8, cv=FAKE, ci=FAKE, co=None, ws=FAKE,
-              wsb=512, s=None)
+              wsb=B.draft_head_workspace_bytes(1, 512), s=None)
 
     def call(**kw):
         a = dict(ok)
@@ -190,7 +191,7 @@ def test_coarse_validation(lib, via):
     _err(lib, call(pairs=MIS), B.DH_EINVAL)
     # the caller's workspace: present, aligned, large enough
     _err(lib, call(ws=None), B.DH_EINVAL)
-    _err(lib, call(wsb=511), B.DH_EINVAL)
+    _err(lib, call(wsb=B.draft_head_workspace_bytes(1, 512) - 1), B.DH_EINVAL)
     _err(lib, call(ws=MIS), B.DH_EINVAL)
     need = B.draft_head_workspace_bytes(9, 512)
     _err(lib, call(M=9), B.DH_EINVAL)
@@ -317,7 +318,7 @@ def test_forward_validation(lib):
         a.update(kw)
         return lib.draft_head_forward(a["x"], a["M"], a["K"], a["N"], a["t"], a["p"], a["w"], a["ldw"],
                                       a["kc"], a["R"], a["cv"], a["ci"], a["ri"], a["rv"], a["oi"],
-                                      a["ov"], a["co"], FAKE, 4096, a["s"], None, None)
+                                      a["ov"], a["co"], FAKE, 16384, a["s"], None, None)
     _err(lib, call(w=None), B.DH_EINVAL)
     _err(lib, call(ri=None), B.DH_EINVAL)
     _err(lib, call(oi=None), B.DH_EINVAL)
