@@ -20,6 +20,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "drafthead.h")
 
 DH_OK, DH_EINVAL, DH_ESHAPE, DH_EUNSUP, DH_EHIP = 0, -1, -2, -3, -4
+DH_NOALLOC_SCRATCH_BYTES = 2 << 20
 BLOCK_N = 64
 GROUP = 128
 
@@ -73,6 +74,9 @@ def load_library() -> ctypes.CDLL:
     lib.draft_head_argmax.argtypes = [P, P, i32, i32, P, P, P]
     lib.draft_head_coarse_int4.restype = i32
     lib.draft_head_coarse_int4.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P, sz, P]
+    lib.draft_head_forward_noalloc.restype = i32
+    lib.draft_head_forward_noalloc.argtypes = [P, i32, i32, i32, P, P, P, i64, i32, i32, P, P, P, P, P, P, P, P,
+                                               P, P]
     lib.draft_head_forward_int4.restype = i32
     lib.draft_head_forward_int4.argtypes = [P, i32, i32, i32, P, P, P, i64, i32, i32, P, P, P, P, P, P, P, P, sz,
                                             P, P, P]
@@ -406,6 +410,23 @@ def draft_head_forward(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, 
     else:
         _check(lib.draft_head_forward_e4m3(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), _ptr(wscale),
                                            w.stride(0), kcand, R, *outs))
+    return out
+
+
+def draft_head_forward_noalloc(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, out=None,
+                               coarse_out=None, stream=None, coarse_events=None):
+    """draft_head_forward with the library's static scratch instead of a
+    workspace (bf16 rerank rows); out: dict from forward_buffers (allocated
+    here when None, which a caller that cannot allocate passes)."""
+    lib = load_library()
+    M, K = x.shape
+    if out is None:
+        out = forward_buffers(M, N, kcand, R, x.device)
+    e0, e1 = (None, None) if coarse_events is None else (_event(coarse_events[0]), _event(coarse_events[1]))
+    _check(lib.draft_head_forward_noalloc(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0), kcand,
+                                          R, _ptr(out["cand_val"]), _ptr(out["cand_id"]), _ptr(out["rr_id"]),
+                                          _ptr(out["rr_val"]), _ptr(out["out_id"]), _ptr(out["out_val"]),
+                                          _ptr(coarse_out), _stream(stream), e0, e1))
     return out
 
 

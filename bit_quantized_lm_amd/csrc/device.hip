@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/drafthead.h"
@@ -2431,11 +2432,10 @@ namespace {
 // One call: coarse launch(es), then rerank + argmax on the rows src describes.
 // int4: the coarse head is a 4-bit one in its 2K-long 2-bit form (x is read
 // twice over); the rerank reads rows of length K as always.
-int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, const RowSrc& src,
-                 int kcand, int R, float* cand_val, int32_t* cand_id,
-                 int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
-                 void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
-                 void* coarse_stop_event, bool int4 = false) {
+int validate_forward(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                     const RowSrc& src, int kcand, int R, const float* cand_val, const int32_t* cand_id,
+                     const int32_t* rr_id, const float* rr_val, const int32_t* out_id, const float* out_val,
+                     const void* workspace, size_t workspace_bytes, bool int4) {
   const int ncand = (N > 0 && kcand > 0) ? ((N + DH_BLOCK_N - 1) / DH_BLOCK_N) * kcand : 0;
   int rc = int4 ? check_k4(K) : DH_OK;
   if (rc) return rc;
@@ -2444,12 +2444,20 @@ int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const
                             int4 ? K : 0)))
     return rc;
   if ((rc = validate_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val))) return rc;
-  if ((rc = validate_argmax(rr_id, rr_val, M, R, out_id, out_val))) return rc;
-  hipStream_t s = as_stream(stream);
-  if ((rc = launch_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace, s,
-                          reinterpret_cast<hipEvent_t>(coarse_start_event),
-                          reinterpret_cast<hipEvent_t>(coarse_stop_event), K)))
-    return rc;
+  return validate_argmax(rr_id, rr_val, M, R, out_id, out_val);
+}
+
+// Launches of one validated call.
+int launch_forward(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                   const RowSrc& src, int kcand, int R, float* cand_val, int32_t* cand_id, int32_t* rr_id,
+                   float* rr_val, int32_t* out_id, float* out_val, float* coarse_out, void* workspace,
+                   hipStream_t s, void* coarse_start_event, void* coarse_stop_event, bool int4) {
+  const int ncand = ((N + DH_BLOCK_N - 1) / DH_BLOCK_N) * kcand;
+  const int Kc = int4 ? 2 * K : K;
+  int rc = launch_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace, s,
+                         reinterpret_cast<hipEvent_t>(coarse_start_event),
+                         reinterpret_cast<hipEvent_t>(coarse_stop_event), K);
+  if (rc) return rc;
   int nblk, kc;
   if (fast_rerank(N, ncand, R, nblk, kc)) {   // rerank and argmax in one kernel
     hipError_t e = launch_wide<true>(x, src, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val, out_id, out_val,
@@ -2459,6 +2467,63 @@ int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const
   }
   if ((rc = launch_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, s))) return rc;
   return launch_argmax(rr_id, rr_val, M, R, out_id, out_val, s);
+}
+
+int forward_impl(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, const RowSrc& src,
+                 int kcand, int R, float* cand_val, int32_t* cand_id,
+                 int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
+                 void* workspace, size_t workspace_bytes, void* stream, void* coarse_start_event,
+                 void* coarse_stop_event, bool int4 = false) {
+  int rc = validate_forward(x, M, K, N, tiled, pairs, src, kcand, R, cand_val, cand_id, rr_id, rr_val, out_id,
+                            out_val, workspace, workspace_bytes, int4);
+  if (rc) return rc;
+  return launch_forward(x, M, K, N, tiled, pairs, src, kcand, R, cand_val, cand_id, rr_id, rr_val, out_id, out_val,
+                        coarse_out, workspace, as_stream(stream), coarse_start_event, coarse_stop_event, int4);
+}
+
+// ---------------------------------------------------------------------------
+// The one-call path for callers that cannot allocate (code under graph
+// capture, serving loops or harnesses that forbid allocation): its workspace
+// is `scratch`, a static device array that every GPU the library runs on
+// holds until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the memory is reached only through the
+// address hipGetSymbolAddress gives, once per device, kept in scratch_ptr.
+// Every call on a GPU shares that GPU's array (calls that overlap on one GPU
+// race); the kernels clear what must start at zero themselves (the coarse
+// kernel zeroes the rerank's hand-off words of every call).
+constexpr size_t kScratchBytes = DH_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The scratch address on the stream's device, which must be the current one.
+int scratch_for(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return dh::fail(DH_EHIP, "forward_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (s) {
+    hipDevice_t sdev = -1;
+    if ((e = hipStreamGetDevice(s, &sdev)) != hipSuccess)
+      return dh::fail(DH_EHIP, "forward_noalloc: hipStreamGetDevice: %s", hipGetErrorString(e));
+    if ((int)sdev != dev)
+      return dh::fail(DH_EINVAL, "forward_noalloc: the stream belongs to device %d but device %d is current",
+                      (int)sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return dh::fail(DH_EUNSUP, "forward_noalloc: device %d beyond the %d the library keeps scratch for", dev,
+                    kMaxDevices);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess || !p)
+      return dh::fail(DH_EHIP, "forward_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                      hipGetErrorString(e));
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return DH_OK;
 }
 
 }  // namespace
@@ -2493,6 +2558,27 @@ int draft_head_forward_e4m3(const void* x, int M, int K, int N, const uint8_t* t
   return forward_impl(x, M, K, N, tiled, pairs, RowSrc{w8, ldw, wscale, nullptr, 0, nullptr, kRowsE4m3}, kcand, R,
                       cand_val, cand_id, rr_id, rr_val, out_id, out_val, coarse_out, workspace, workspace_bytes,
                       stream, coarse_start_event, coarse_stop_event);
+}
+
+int draft_head_forward_noalloc(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                               const void* w, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
+                               int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, float* coarse_out,
+                               void* stream, void* coarse_start_event, void* coarse_stop_event) {
+  const RowSrc src{w, ldw, nullptr, nullptr, 0, nullptr, kRowsBf16};
+  // Validated as draft_head_forward with a workspace of the scratch's size,
+  // before any HIP call: a call that needs more is rejected here.
+  if (M >= 1 && M <= DH_MAX_M && check_k(K) == DH_OK && coarse_workspace_bytes(M, K) > kScratchBytes)
+    return dh::fail(DH_EUNSUP,
+                    "forward_noalloc: M=%d, K=%d needs %zu bytes of scratch; the static scratch holds %zu",
+                    M, K, coarse_workspace_bytes(M, K), kScratchBytes);
+  int rc = validate_forward(x, M, K, N, tiled, pairs, src, kcand, R, cand_val, cand_id, rr_id, rr_val, out_id,
+                            out_val, reinterpret_cast<const void*>(uintptr_t{256}), kScratchBytes, false);
+  if (rc) return rc;
+  const hipStream_t s = as_stream(stream);
+  void* ws = nullptr;
+  if ((rc = scratch_for(s, &ws))) return rc;
+  return launch_forward(x, M, K, N, tiled, pairs, src, kcand, R, cand_val, cand_id, rr_id, rr_val, out_id, out_val,
+                        coarse_out, ws, s, coarse_start_event, coarse_stop_event, false);
 }
 
 int draft_head_forward_nvfp4(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,

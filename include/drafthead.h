@@ -54,6 +54,7 @@ extern "C" {
 #define DH_MAX_K 65536
 #define DH_MAX_KCAND 64
 #define DH_MAX_R 1024
+#define DH_NOALLOC_SCRATCH_BYTES (2u << 20)   /* draft_head_forward_noalloc's static scratch per GPU */
 
 /* Message describing the last error returned on the calling thread ("" if none). */
 const char* draft_head_last_error(void);
@@ -263,6 +264,30 @@ int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
                        int32_t* out_id, float* out_val, float* coarse_out, void* workspace,
                        size_t workspace_bytes, void* stream, void* coarse_start_event,
                        void* coarse_stop_event);
+
+/*
+ * DEVICE.  draft_head_forward without a workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  The scratch the call needs lives in a
+ * static device array of DH_NOALLOC_SCRATCH_BYTES (2 MiB) that the library
+ * holds on every GPU it runs on until the process ends; the call itself
+ * makes no hipMalloc, hipFree or other allocating call.  The caller still
+ * passes every input and output, as for draft_head_forward.
+ * Limit: draft_head_workspace_bytes(M, K) <= DH_NOALLOC_SCRATCH_BYTES (any M
+ * up to DH_MAX_M at K <= 12,288; M <= 8 wherever the resident kernel holds
+ * x).  Every call on one GPU shares that GPU's array and overwrites it:
+ * calls that overlap on one GPU race, so order them (one stream).  The
+ * stream must belong to the current device.
+ * Errors: as draft_head_forward; DH_EUNSUP when the call needs more scratch
+ * than the array holds (before any HIP call); DH_EINVAL when the stream's
+ * device is not the current one; DH_EHIP when the array's address cannot
+ * be obtained.
+ */
+int draft_head_forward_noalloc(const void* x, int M, int K, int N, const uint8_t* tiled,
+                               const uint32_t* pairs, const void* w, int64_t ldw, int kcand, int R,
+                               float* cand_val, int32_t* cand_id, int32_t* rr_id, float* rr_val,
+                               int32_t* out_id, float* out_val, float* coarse_out, void* stream,
+                               void* coarse_start_event, void* coarse_stop_event);
 
 /*
  * DEVICE.  draft_head_forward with the e4m3 rerank source of

@@ -29,7 +29,8 @@ def test_library_exports_every_header_symbol(lib):
                           "draft_head_stream_read", "draft_head_logits_row", "draft_head_rerank_e4m3",
                           "draft_head_forward_e4m3", "draft_head_rerank_nvfp4", "draft_head_forward_nvfp4",
                           "draft_head_quantize_pack_int4",
-                          "draft_head_int4_as_int2", "draft_head_coarse_int4", "draft_head_forward_int4"}
+                          "draft_head_int4_as_int2", "draft_head_coarse_int4", "draft_head_forward_int4",
+                          "draft_head_forward_noalloc"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -374,3 +375,28 @@ def test_int4_device_validation(lib):
     g = lib.draft_head_forward_int4
     _err(lib, g(FAKE, 1, 384, 64, FAKE, FAKE, FAKE, 384, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 512,
                 None, None, None), B.DH_ESHAPE)
+
+
+def test_forward_noalloc_validation(lib):
+    """The entry point without a workspace validates like draft_head_forward,
+    and rejects a call that needs more than its static scratch, before any
+    HIP call."""
+    def call(**kw):
+        a = dict(x=FAKE, M=2, K=512, N=640, t=FAKE, p=FAKE, w=FAKE, ldw=512, kc=8, R=32, cv=FAKE, ci=FAKE,
+                 ri=FAKE, rv=FAKE, oi=FAKE, ov=FAKE)
+        a.update(kw)
+        return lib.draft_head_forward_noalloc(a["x"], a["M"], a["K"], a["N"], a["t"], a["p"], a["w"], a["ldw"],
+                                              a["kc"], a["R"], a["cv"], a["ci"], a["ri"], a["rv"], a["oi"],
+                                              a["ov"], None, None, None, None)
+    _err(lib, call(x=None), B.DH_EINVAL)
+    _err(lib, call(oi=None), B.DH_EINVAL)
+    _err(lib, call(M=0), B.DH_EINVAL)
+    _err(lib, call(M=129), B.DH_EUNSUP)
+    _err(lib, call(K=768), B.DH_ESHAPE)
+    _err(lib, call(R=81), B.DH_EUNSUP)
+    # the largest K the scratch takes at 80 rows, and the next multiple of 512
+    assert B.draft_head_workspace_bytes(80, 12288) <= B.DH_NOALLOC_SCRATCH_BYTES
+    assert B.draft_head_workspace_bytes(80, 12800) > B.DH_NOALLOC_SCRATCH_BYTES
+    _err(lib, call(M=80, K=12800, ldw=12800), B.DH_EUNSUP)
+    assert b"scratch" in lib.draft_head_last_error()
+    _err(lib, call(M=72, K=65536, ldw=65536), B.DH_EUNSUP)
