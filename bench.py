@@ -27,7 +27,9 @@ Prints one JSON line:
                its fractions of the HBM and bf16 MFMA peaks, the warm
                (cache-resident) figure, the time of the row handed to a
                top-k caller (draft_head_logits_row), the per-call time with
-               the e4m3 and NVFP4 rerank sources, the per-call time of forwards
+               the e4m3 and NVFP4 rerank sources, the per-call time of the call
+               that also builds the caller's bf16 row (draft_head_forward_row,
+               full and top-k only, beside the plain call), of forwards
                replayed from a HIP graph (launch gaps removed; not the
                headline), the 4-bit head's per-call time
                (KCAND = 1, 357,580,800 B of codes and pairs per call),
@@ -267,6 +269,34 @@ class Rig:
         e.record()
         torch.cuda.synchronize()
         return round(s.elapsed_time(e) / (reps * calls) * 1e3, 2)
+
+    def forward_row_us(self, m, reps=100):
+        """Per-call time of draft_head_forward_row (the call with the caller's
+        bf16 row built inside it; full and top-k only) beside the plain call,
+        weights rotated."""
+        torch, B = self.torch, self.B
+        out = self.buffers(m)
+        row = torch.empty((m, N), dtype=torch.int16, device=self.dev)
+        res = {}
+        for name in ("plain", "full", "topk_only"):
+            def call(i):
+                h = self.heads[i % len(self.heads)]
+                if name == "plain":
+                    h(self.x[:m], stream=self.stream, out=out, workspace=self.ws[m])
+                else:
+                    h.logits_row(self.x[:m], topk_only=name == "topk_only", stream=self.stream, out=out, row=row,
+                                 workspace=self.ws[m])
+            for i in range(10):
+                call(i)
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for i in range(reps):
+                call(i)
+            e.record()
+            torch.cuda.synchronize()
+            res[name] = round(s.elapsed_time(e) / reps * 1e3, 2)
+        return res
 
     def logits_row_us(self, m, reps=50):
         """Time of draft_head_logits_row alone at M rows (full and top-k only)."""
@@ -537,6 +567,8 @@ def main():
         extra["warm_not_hbm"] = {"us_per_call": round(tw * 1e6, 2), "coarse_us": round(tkw * 1e6, 2),
                                  "note": "one weight copy reused back to back: Infinity-Cache resident"}
         extra["logits_row_us"] = {str(mm): rig.logits_row_us(mm) for mm in (1, 8, 72)}
+        extra["forward_row_us_per_call"] = {str(mm): rig.forward_row_us(mm) for mm in (1, 8, 72)}
+        log(f"one call with the caller's bf16 row built inside it: {extra['forward_row_us_per_call']}")
         extra["e4m3_rerank_us_per_call"] = rig.e4m3_call_us()
         extra["graph_replay_us_per_call"] = {str(m): rig.graph_us(m) for m in (1, 8, 72)}
         log(f"one call inside a replayed HIP graph: {extra['graph_replay_us_per_call']}")

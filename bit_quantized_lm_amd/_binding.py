@@ -74,6 +74,9 @@ def load_library() -> ctypes.CDLL:
     lib.draft_head_argmax.argtypes = [P, P, i32, i32, P, P, P]
     lib.draft_head_coarse_int4.restype = i32
     lib.draft_head_coarse_int4.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P, sz, P]
+    lib.draft_head_forward_row.restype = i32
+    lib.draft_head_forward_row.argtypes = [P, i32, i32, i32, P, P, P, i64, i32, i32, P, P, P, P, P, P, P, i32, P, sz,
+                                           P]
     lib.draft_head_forward_noalloc.restype = i32
     lib.draft_head_forward_noalloc.argtypes = [P, i32, i32, i32, P, P, P, i64, i32, i32, P, P, P, P, P, P, P, P,
                                                P, P]
@@ -413,6 +416,27 @@ def draft_head_forward(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, 
     return out
 
 
+def draft_head_forward_row(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, topk_only: bool = False,
+                           out=None, row=None, workspace=None, stream=None):
+    """One call plus the bf16 row for the caller (bf16 rerank rows); returns
+    the forward outputs with "row" (int16 [M][N] holding bf16 bits) added."""
+    import torch
+    lib = load_library()
+    M, K = x.shape
+    if out is None:
+        out = forward_buffers(M, N, kcand, R, x.device)
+    if row is None:
+        row = torch.empty((M, N), dtype=torch.int16, device=x.device)
+    if workspace is None:
+        workspace = workspace_for(M, K, x.device)
+    _check(lib.draft_head_forward_row(_ptr(x), M, K, N, _ptr(tiled), _ptr(pairs), _ptr(w), w.stride(0), kcand, R,
+                                      _ptr(out["cand_val"]), _ptr(out["cand_id"]), _ptr(out["rr_id"]),
+                                      _ptr(out["rr_val"]), _ptr(out["out_id"]), _ptr(out["out_val"]), _ptr(row),
+                                      1 if topk_only else 0, *_ws(workspace), _stream(stream)))
+    out["row"] = row
+    return out
+
+
 def draft_head_forward_noalloc(x, tiled, pairs, w, N: int, kcand: int = 8, R: int = 32, out=None,
                                coarse_out=None, stream=None, coarse_events=None):
     """draft_head_forward with the library's static scratch instead of a
@@ -474,14 +498,25 @@ class DraftHead:
                                   coarse_events=coarse_events, wscale=self.wscale, bits=self.bits,
                                   bscale=self.bscale, gscale=self.gscale)
 
-    def logits_row(self, x, topk_only=False, stream=None):
+    def logits_row(self, x, topk_only=False, stream=None, out=None, row=None, workspace=None):
         """One call plus the bf16 row the page hands to its caller (full, or
-        top-k only); returns the forward outputs with "row" added."""
+        top-k only), in one library call; returns the forward outputs with
+        "row" added."""
+        if self.bits != 2 or self.wscale is not None or self.bscale is not None:
+            raise ValueError("the row for the caller is built with the 2-bit head and bf16 rerank rows")
+        return draft_head_forward_row(x, self.tiled, self.pairs, self.w, self.N, self.kcand, self.R, topk_only,
+                                      out=out, row=row, workspace=workspace, stream=stream)
+
+    def logits_row_staged(self, x, topk_only=False, stream=None):
+        """The same row from the fp32 coarse row: a forward with coarse_out,
+        then draft_head_logits_row."""
         import torch
-        coarse = None if topk_only else torch.empty((x.shape[0], self.N), dtype=torch.float32, device=x.device)
+        coarse = torch.empty((x.shape[0], self.N), dtype=torch.float32, device=x.device)
         out = self(x, coarse_out=coarse, stream=stream)
-        out["row"] = draft_head_logits_row(out["rr_id"], out["rr_val"], self.N, coarse=coarse,
-                                           topk_only=topk_only, stream=stream)
+        out["row"] = draft_head_logits_row(out["rr_id"], out["rr_val"], self.N,
+                                           coarse=None if topk_only else coarse, topk_only=topk_only,
+                                           stream=stream)
+        out["coarse"] = coarse
         return out
 
     def staged(self, x, coarse_out=None, stream=None):

@@ -116,6 +116,7 @@ struct RerankArgs {
   int32_t* out_id;
   float* out_val;
   unsigned long long* hand;   // per-row hand-off words (rows split over several workgroups)
+  uint16_t* row_out;          // optional bf16 row [M][N]: each reranked id's exact value is written over it
 };
 
 struct CoarseArgs {
@@ -127,6 +128,8 @@ struct CoarseArgs {
   float* cand_val;
   int32_t* cand_id;
   float* coarse_out;
+  uint16_t* row_out;   // optional bf16 row [M][N] for the caller (the rerank scatters the exact values)
+  int topk_only;       // row_out holds -inf instead of the coarse scores
   unsigned long long* hand;   // per-row hand-off words of the rerank; workgroup 0 zeroes hand[0..ncnt)
   int ncnt;
   int kx;          // row length of x: K, or K / 2 for a 4-bit head run at length K (x' = (x, x))
@@ -140,6 +143,20 @@ struct CoarseArgs {
 __device__ __forceinline__ void zero_counters(const CoarseArgs& A) {
   if (blockIdx.x == 0 && (int)threadIdx.x < A.ncnt)
     __hip_atomic_store(A.hand + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The optional outputs of a coarse score: the fp32 row, and the bf16 row the
+// page hands to its caller (`_draft_head_int2`'s store of Y: the coarse score
+// rounded to bf16, or -inf everywhere for a top-k caller), into which the
+// rerank then writes the exact values.
+__device__ __forceinline__ void store_scores(const CoarseArgs& A, int m, int n, float sv) {
+  if (A.coarse_out) A.coarse_out[(size_t)m * A.N + n] = sv;
+  if (A.row_out) A.row_out[(size_t)m * A.N + n] = (uint16_t)(A.topk_only ? 0xFF80u : f32_to_bf16_rne(sv));
 }
 
 // One group: MFMAs of the (h, e) fragments for all tiles, then the scale update.
@@ -367,7 +384,7 @@ __device__ __forceinline__ void block_select(Value value, const CoarseArgs& A, i
         const float sv = pi < NP ? value(i, r, t) : 0.f;
         k[j][t] = ok ? f32_key(sv + 0.0f) : 0u;   // -0 counts as +0, as in a float compare
         c[j][t] = 16 * t + nn;
-        if (A.coarse_out && ok) A.coarse_out[(size_t)m * A.N + n] = sv;
+        if (ok) store_scores(A, m, n, sv);
       }
     }
     bool any = false;
@@ -410,7 +427,7 @@ __device__ __forceinline__ void res_select(const float* sc, const CoarseArgs& A,
       const float sv = ok ? sc[(lbq[j] * MP + mq[j]) * 64 + 16 * t + nn] : 0.f;
       k[j][t] = ok ? f32_key(sv + 0.0f) : 0u;   // -0 counts as +0, as in a float compare
       c[j][t] = 16 * t + nn;
-      if (A.coarse_out && ok) A.coarse_out[(size_t)mq[j] * A.N + n] = sv;
+      if (ok) store_scores(A, mq[j], n, sv);
     }
   }
   row16_select<NB>(k, c, A.kcand, nn, kk, kc);
@@ -735,11 +752,6 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 // One wave per (m, G): lane q * 16 + p takes piece p (8 consecutive k) of
@@ -1113,7 +1125,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * i + 4 * hh + r;
         sk[(lb * MP + row) * kScStride + col] = n_ok ? f32_key(acc[i][t][r] + 0.0f) : 0u;   // -0 as +0
-        if (A.coarse_out && n_ok && row < A.M) A.coarse_out[(size_t)row * A.N + n] = acc[i][t][r];
+        if (n_ok && row < A.M) store_scores(A, row, n, acc[i][t][r]);
       }
   }
   __syncthreads();
@@ -1896,6 +1908,8 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
     if (lane == 0) {
       A.rr_id[(size_t)m * R + r] = id;
       A.rr_val[(size_t)m * R + r] = sum;
+      // `y.scatter_(1, idx, ex.to(bfloat16))`: ids of one row are distinct
+      if (A.row_out && id >= 0) A.row_out[(size_t)m * A.N + id] = (uint16_t)f32_to_bf16_rne(sum);
     }
     if (ranks_above(sum, id, bv, bi)) {
       bv = sum;
@@ -2159,11 +2173,11 @@ int validate_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, con
 // kx: row length of x (K, or K/2 for a 4-bit head run at length K).
 int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, int kcand,
                   float* cand_val, int32_t* cand_id, float* coarse_out, void* workspace, hipStream_t s,
-                  hipEvent_t ev0, hipEvent_t ev1, int kx = 0) {
+                  hipEvent_t ev0, hipEvent_t ev1, int kx = 0, uint16_t* row_out = nullptr, int topk_only = 0) {
   const int nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
   const int ncand = nblk * kcand;
   CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
-               reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out,
+               reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out, row_out, topk_only,
                static_cast<unsigned long long*>(workspace), M, kx ? kx : K};
   hipError_t e = hipSuccess;
   const int ks = A.kx;   // the row length of x the resident kernel stages
@@ -2187,6 +2201,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
     B.cand_val = cand_val + (size_t)m0 * ncand;
     B.cand_id = cand_id + (size_t)m0 * ncand;
     B.coarse_out = coarse_out ? coarse_out + (size_t)m0 * N : nullptr;
+    B.row_out = row_out ? row_out + (size_t)m0 * N : nullptr;
     B.ncnt = m0 == 0 ? M : 0;
     const int mt = (B.M + 15) / 16, mp = 16 * mt;
     u32x4* xslab = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(workspace) + kHeaderBytes);
@@ -2224,9 +2239,10 @@ bool fast_rerank(int N, int ncand, int R, int& nblk, int& kcand) {
 template <bool kArgmax>
 hipError_t launch_wide(const void* x, const RowSrc& src, int M, int K, int N, const float* cand_val,
                        const int32_t* cand_id, int nblk, int kcand, int R, int32_t* rr_id, float* rr_val,
-                       int32_t* out_id, float* out_val, unsigned long long* hand, hipStream_t s) {
+                       int32_t* out_id, float* out_val, unsigned long long* hand, hipStream_t s,
+                       uint16_t* row_out = nullptr) {
   const RerankArgs A{static_cast<const uint16_t*>(x), src, K, N, cand_val,
-                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, hand};
+                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, hand, row_out};
   auto go = [&](auto nthr) {
     constexpr int NTHR = decltype(nthr)::value, NW = NTHR / 64;
     // ids must fit the hand-off key to split a row; otherwise one part per row
@@ -2304,6 +2320,17 @@ __global__ __launch_bounds__(256) void logits_row_kernel(const float* __restrict
     else b = topk_only ? 0xFF80u : f32_to_bf16_rne(cr[i]);
     out[i] = (uint16_t)b;
   }
+}
+
+// The exact values written over the bf16 row (the general rerank path; the
+// block-maximum rerank writes them itself): one thread per (row, rank).
+__global__ __launch_bounds__(256) void scatter_row_kernel(const int32_t* __restrict__ rr_id,
+                                                          const float* __restrict__ rr_val, int M, int N, int R,
+                                                          uint16_t* __restrict__ row_out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * R) return;
+  const int m = i / R, id = rr_id[i];
+  if (id >= 0 && id < N) row_out[(size_t)m * N + id] = (uint16_t)f32_to_bf16_rne(rr_val[i]);
 }
 
 // Streaming-read reference: the achievable HBM read rate on this device, read
@@ -2448,24 +2475,33 @@ int validate_forward(const void* x, int M, int K, int N, const uint8_t* tiled, c
 }
 
 // Launches of one validated call.
+// row_out (optional): the bf16 row for the caller, filled by the coarse
+// kernel (coarse scores, or -inf with topk_only) and overwritten at the
+// reranked ids with their exact values.
 int launch_forward(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
                    const RowSrc& src, int kcand, int R, float* cand_val, int32_t* cand_id, int32_t* rr_id,
                    float* rr_val, int32_t* out_id, float* out_val, float* coarse_out, void* workspace,
-                   hipStream_t s, void* coarse_start_event, void* coarse_stop_event, bool int4) {
+                   hipStream_t s, void* coarse_start_event, void* coarse_stop_event, bool int4,
+                   uint16_t* row_out = nullptr, int topk_only = 0) {
   const int ncand = ((N + DH_BLOCK_N - 1) / DH_BLOCK_N) * kcand;
   const int Kc = int4 ? 2 * K : K;
   int rc = launch_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace, s,
                          reinterpret_cast<hipEvent_t>(coarse_start_event),
-                         reinterpret_cast<hipEvent_t>(coarse_stop_event), K);
+                         reinterpret_cast<hipEvent_t>(coarse_stop_event), K, row_out, topk_only);
   if (rc) return rc;
   int nblk, kc;
   if (fast_rerank(N, ncand, R, nblk, kc)) {   // rerank and argmax in one kernel
     hipError_t e = launch_wide<true>(x, src, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val, out_id, out_val,
-                                     static_cast<unsigned long long*>(workspace), s);
+                                     static_cast<unsigned long long*>(workspace), s, row_out);
     if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_wide_kernel: %s", hipGetErrorString(e));
     return dh::ok();
   }
   if ((rc = launch_rerank(x, src, M, K, N, cand_val, cand_id, ncand, R, rr_id, rr_val, s))) return rc;
+  if (row_out) {
+    hipLaunchKernelGGL(scatter_row_kernel, dim3((M * R + 255) / 256), dim3(256), 0, s, rr_id, rr_val, M, N, R,
+                       row_out);
+    if ((rc = launch_error("scatter_row_kernel"))) return rc;
+  }
   return launch_argmax(rr_id, rr_val, M, R, out_id, out_val, s);
 }
 
@@ -2558,6 +2594,19 @@ int draft_head_forward_e4m3(const void* x, int M, int K, int N, const uint8_t* t
   return forward_impl(x, M, K, N, tiled, pairs, RowSrc{w8, ldw, wscale, nullptr, 0, nullptr, kRowsE4m3}, kcand, R,
                       cand_val, cand_id, rr_id, rr_val, out_id, out_val, coarse_out, workspace, workspace_bytes,
                       stream, coarse_start_event, coarse_stop_event);
+}
+
+int draft_head_forward_row(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
+                           const void* w, int64_t ldw, int kcand, int R, float* cand_val, int32_t* cand_id,
+                           int32_t* rr_id, float* rr_val, int32_t* out_id, float* out_val, uint16_t* row_out,
+                           int topk_only, void* workspace, size_t workspace_bytes, void* stream) {
+  const RowSrc src{w, ldw, nullptr, nullptr, 0, nullptr, kRowsBf16};
+  if (!row_out) return dh::fail(DH_EINVAL, "forward_row: null row_out");
+  int rc = validate_forward(x, M, K, N, tiled, pairs, src, kcand, R, cand_val, cand_id, rr_id, rr_val, out_id,
+                            out_val, workspace, workspace_bytes, false);
+  if (rc) return rc;
+  return launch_forward(x, M, K, N, tiled, pairs, src, kcand, R, cand_val, cand_id, rr_id, rr_val, out_id, out_val,
+                        nullptr, workspace, as_stream(stream), nullptr, nullptr, false, row_out, topk_only ? 1 : 0);
 }
 
 int draft_head_forward_noalloc(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,

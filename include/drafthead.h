@@ -14,7 +14,8 @@
  *   per call (device): draft_head_coarse -> draft_head_rerank -> draft_head_argmax,
  *                      or the three in one host call: draft_head_forward
  *                      (rerank from e4m3 rows: the *_e4m3 variants); for a top-k
- *                      caller, draft_head_logits_row after them
+ *                      caller, draft_head_forward_row (the call and the row
+ *                      together) or draft_head_logits_row after a call
  *
  * Conventions for every function:
  *   - Return value: DH_OK (0) or a negative DH_E* code; never throws.  The
@@ -348,6 +349,26 @@ int draft_head_forward_int4(const void* x, int M, int K, int N, const uint8_t* t
  */
 int draft_head_logits_row(const float* coarse, const int32_t* rr_id, const float* rr_val, int M, int N,
                           int R, int topk_only, uint16_t* row_out, void* stream);
+
+/*
+ * DEVICE.  draft_head_forward plus the bf16 row for the caller, with no fp32
+ * row in between (the page's `_draft_head_int2` stores Y as bf16 from its
+ * accumulator; `_apply_head_int2` then scatters the exact values over it):
+ * the coarse kernel writes row_out[m][n] = bf16(coarse score) (round to
+ * nearest even), or -inf when topk_only != 0 (`_radiance_topk_only`), in its
+ * epilogue, and the rerank writes bf16(rr_val[m][r]) at every reranked id.
+ * The result equals draft_head_logits_row applied to this call's own coarse
+ * scores and reranked values.
+ *   row_out    out, bf16 bits [M][N]
+ *   the other arguments as draft_head_forward (bf16 rerank rows; no fp32
+ *   coarse row and no timing events)
+ * Errors: as draft_head_forward; DH_EINVAL for a null row_out.
+ */
+int draft_head_forward_row(const void* x, int M, int K, int N, const uint8_t* tiled,
+                           const uint32_t* pairs, const void* w, int64_t ldw, int kcand, int R,
+                           float* cand_val, int32_t* cand_id, int32_t* rr_id, float* rr_val,
+                           int32_t* out_id, float* out_val, uint16_t* row_out, int topk_only,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * DEVICE.  Measurement reference, not part of the head: reads `bytes` bytes at

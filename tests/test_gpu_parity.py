@@ -360,6 +360,56 @@ def test_logits_row_bit_exact(dev, m, n, r, topk_only):
     assert np.array_equal(got.cpu().numpy().view(np.uint16), want)
 
 
+@pytest.mark.parametrize("m,k,n,kc,r", [(1, 1024, 5000, 8, 32), (9, 512, 3000, 8, 32), (3, 512, 200, 8, 32),
+                                         (20, 512, 70000, 8, 100), (72, 1024, 2100, 8, 32)])
+@pytest.mark.parametrize("topk_only", [False, True])
+def test_forward_row_equals_the_row_of_its_own_call(dev, m, k, n, kc, r, topk_only):
+    """The row built inside the call (bf16 from the coarse epilogue, exact
+    values scattered by the rerank, or by its own small kernel on the general
+    rerank path: n = 200 has fewer blocks than R, R = 100 exceeds the
+    block-maximum rerank's limit) equals draft_head_logits_row applied to the
+    same call's fp32 coarse row and reranked values, bit for bit; the other
+    outputs equal the plain call's."""
+    w = workload.gen_weight(n, k, seed=4600 + n)
+    x = _to_dev(workload.gen_x(m, k, seed=4601 + n), dev)
+    head = B.DraftHead.from_weight(w, kcand=kc, R=r, device=dev)
+    got = head.logits_row(x, topk_only=topk_only)
+    want = head.logits_row_staged(x, topk_only=topk_only)
+    torch.cuda.synchronize()
+    assert torch.equal(got["row"], want["row"])
+    for key in ("cand_val", "cand_id", "rr_id", "rr_val", "out_id", "out_val"):
+        assert torch.equal(got[key], want[key]), key
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("topk_only", [False, True])
+def test_forward_row_full_shape(dev, full, topk_only):
+    """The full shard at M = 1, 8, 72: the row built inside the call equals the
+    staged row of the same call, and holds the oracle's values (exact values at
+    the reranked ids, the coarse values or -inf elsewhere) within the value
+    tolerance plus one bf16 step."""
+    cfg = full["cfg"]
+    head = full["head"]
+    for m in (1, 8, 72):
+        x = _to_dev(full["x"][:m], dev)
+        got = head.logits_row(x, topk_only=topk_only)
+        want = head.logits_row_staged(x, topk_only=topk_only)
+        torch.cuda.synchronize()
+        assert torch.equal(got["row"], want["row"]), m
+        ref = _prefix(full["ref"], m)
+        row = oracle.bf16.to_f64(got["row"].cpu().numpy().view(np.uint16))
+        exp = oracle.bf16.to_f64(oracle.logits_row(ref["rr_id"], ref["rr_val"], cfg.n,
+                                                    coarse_f32=ref["coarse"].astype(np.float32),
+                                                    topk_only=topk_only))
+        fin = np.isfinite(exp)
+        if np.array_equal(got["rr_id"].cpu().numpy(), ref["rr_id"]):   # else a counted near-tie list
+            assert np.array_equal(np.isfinite(row), fin), m
+        rms = np.sqrt(np.mean(ref["coarse"] ** 2, axis=1))[:, None]
+        lim = 2e-3 * np.abs(exp) + 2e-3 * rms + 2.0 ** -7 * np.abs(exp)
+        both = fin & np.isfinite(row)
+        assert np.all(np.abs(row - exp)[both] <= np.broadcast_to(lim, row.shape)[both]), m
+
+
 @pytest.mark.parametrize("topk_only", [False, True])
 def test_logits_row_end_to_end(dev, topk_only):
     """One call plus the row, against the oracle's own pipeline: the reranked

@@ -30,7 +30,7 @@ def test_library_exports_every_header_symbol(lib):
                           "draft_head_forward_e4m3", "draft_head_rerank_nvfp4", "draft_head_forward_nvfp4",
                           "draft_head_quantize_pack_int4",
                           "draft_head_int4_as_int2", "draft_head_coarse_int4", "draft_head_forward_int4",
-                          "draft_head_forward_noalloc"}
+                          "draft_head_forward_noalloc", "draft_head_forward_row"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -400,3 +400,20 @@ def test_forward_noalloc_validation(lib):
     _err(lib, call(M=80, K=12800, ldw=12800), B.DH_EUNSUP)
     assert b"scratch" in lib.draft_head_last_error()
     _err(lib, call(M=72, K=65536, ldw=65536), B.DH_EUNSUP)
+
+
+def test_forward_row_validation(lib):
+    """The call with the caller's bf16 row validates like draft_head_forward,
+    plus the row pointer."""
+    def call(**kw):
+        a = dict(x=FAKE, M=2, K=512, N=640, t=FAKE, p=FAKE, w=FAKE, ldw=512, kc=8, R=32, row=FAKE, ws=FAKE,
+                 wsb=B.draft_head_workspace_bytes(2, 512))
+        a.update(kw)
+        return lib.draft_head_forward_row(a["x"], a["M"], a["K"], a["N"], a["t"], a["p"], a["w"], a["ldw"], a["kc"],
+                                          a["R"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["row"], 0, a["ws"], a["wsb"],
+                                          None)
+    _err(lib, call(row=None), B.DH_EINVAL)
+    _err(lib, call(x=None), B.DH_EINVAL)
+    _err(lib, call(ws=None), B.DH_EINVAL)
+    _err(lib, call(K=768), B.DH_ESHAPE)
+    _err(lib, call(R=81), B.DH_EUNSUP)
