@@ -1207,101 +1207,160 @@ __device__ __forceinline__ float round_bf16(float f) {
   return f != f ? f : __uint_as_float(r);
 }
 
-// The exact logit of row id, summed by one wave (fp32 accumulation).
+// x of one row in the lane layout of the rerank's dot for rows of kind kKind:
+// one chunk of the row (K elements, K a multiple of 256), clamped loads
+// (positions past K read the last valid piece and are masked in the dot).
+//   bf16 rows:  lane l holds x[c0 + 512 j + 8 l .. +8) for j < kDotBf16
+//   e4m3 rows:  lane l holds x[c0 + 1024 j + 16 l .. +16) for j < kDotE4m3
+//   NVFP4 rows: lane l holds x[c0 + 2048 j + 32 l .. +32) for j < kDotNvfp4
 template <int kKind>
-__device__ float wave_dot(const RowSrc& S, uint32_t id, const uint16_t* xr, int K, int lane) {
-  float s0 = 0.f, s1 = 0.f;
-  if constexpr (kKind == kRowsBf16) {
-    const uint16_t* wr = static_cast<const uint16_t*>(S.w) + (size_t)id * S.ldw;
-    for (int k0 = 0; k0 < K; k0 += 512 * kDotBf16) {
-      u32x4 wv[kDotBf16], xv[kDotBf16];
+struct XChunk {
+  static constexpr int kPass = kKind == kRowsBf16 ? 512 : kKind == kRowsE4m3 ? 1024 : 2048;   // k per pass
+  static constexpr int kPasses = kKind == kRowsBf16 ? kDotBf16 : kKind == kRowsE4m3 ? kDotE4m3 : kDotNvfp4;
+  static constexpr int kPieces = kKind == kRowsBf16 ? 1 : kKind == kRowsE4m3 ? 2 : 4;   // 16-byte pieces per pass
+  static constexpr int kLen = kPass * kPasses;                                             // k per chunk
+  u32x4 v[kPasses][kPieces];
+  __device__ __forceinline__ void load(const uint16_t* xr, int K, int c0, int lane) {
 #pragma unroll
-      for (int j = 0; j < kDotBf16; ++j) {   // clamped, unconditional loads
-        const int k = min(k0 + 512 * j + lane * 8, K - 8);
-        wv[j] = *reinterpret_cast<const u32x4*>(wr + k);
-        xv[j] = *reinterpret_cast<const u32x4*>(xr + k);
+    for (int j = 0; j < kPasses; ++j) {
+      const int k = min(c0 + kPass * j + lane * 8 * kPieces, K - 8 * kPieces);
+#pragma unroll
+      for (int q = 0; q < kPieces; ++q) v[j][q] = *reinterpret_cast<const u32x4*>(xr + k + 8 * q);
+    }
+  }
+};
+
+// The exact logits of NR candidate rows, one wave, fp32 accumulation: per
+// chunk of k, every load of the NR rows and of x (from global memory, or from
+// LDS where the caller staged the row) issued before any is used.  ids[i] < 0:
+// no row (reads row 0, returns -inf).
+//   bf16 rows (`_rerank_exact`, bf16 branch): x . W[id].
+//   e4m3 rows (FP8 branch): each byte decoded by the page's bit arithmetic
+//     (e = (b >> 3) & 15, mant = b & 7: mant * 2^-9 if e == 0, else
+//     (1 + mant/8) * 2^(e-7); bit 7 the sign) and multiplied by the row's
+//     scale, one fp32 rounding.
+//   NVFP4 rows: e2m1 nibbles (low nibble first) times the e4m3 scale of their
+//     16-element block times the global scale, rounded to bf16.
+template <int kKind, int NR>
+__device__ void wave_dots(const RowSrc& S, const int (&ids)[NR], const uint16_t* xr, int K, int lane,
+                          float (&out)[NR]) {
+  using XC = XChunk<kKind>;
+  float s0[NR], s1[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) s0[i] = s1[i] = 0.f;
+  // one chunk of k: the NR rows' loads, then their products with x
+  auto chunk = [&](const XC& xc, int c0) {
+    if constexpr (kKind == kRowsBf16) {
+      u32x4 wv[NR][kDotBf16];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const uint16_t* wr = static_cast<const uint16_t*>(S.w) + (size_t)(ids[i] < 0 ? 0 : ids[i]) * S.ldw;
+#pragma unroll
+        for (int j = 0; j < kDotBf16; ++j)
+          wv[i][j] = *reinterpret_cast<const u32x4*>(wr + min(c0 + 512 * j + lane * 8, K - 8));
       }
 #pragma unroll
       for (int j = 0; j < kDotBf16; ++j) {
-        if (k0 + 512 * j + lane * 8 < K) {
+        if (c0 + 512 * j + lane * 8 < K) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            s0 = __builtin_fmaf(lo_bf16(xv[j][c]), lo_bf16(wv[j][c]), s0);
-            s1 = __builtin_fmaf(hi_bf16(xv[j][c]), hi_bf16(wv[j][c]), s1);
-          }
+          for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              s0[i] = __builtin_fmaf(lo_bf16(xc.v[j][0][c]), lo_bf16(wv[i][j][c]), s0[i]);
+              s1[i] = __builtin_fmaf(hi_bf16(xc.v[j][0][c]), hi_bf16(wv[i][j][c]), s1[i]);
+            }
         }
       }
-    }
-  } else if constexpr (kKind == kRowsE4m3) {
-    const uint8_t* wr = static_cast<const uint8_t*>(S.w) + (size_t)id * S.ldw;
-    const float scale = S.wscale[id];
-    for (int k0 = 0; k0 < K; k0 += 1024 * kDotE4m3) {
-      u32x4 wv[kDotE4m3], xa[kDotE4m3], xb[kDotE4m3];
+    } else if constexpr (kKind == kRowsE4m3) {
+      u32x4 wv[NR][kDotE4m3];
+      float scale[NR];
 #pragma unroll
-      for (int j = 0; j < kDotE4m3; ++j) {   // clamped, unconditional loads
-        const int k = min(k0 + 1024 * j + lane * 16, K - 16);
-        wv[j] = *reinterpret_cast<const u32x4*>(wr + k);
-        xa[j] = *reinterpret_cast<const u32x4*>(xr + k);
-        xb[j] = *reinterpret_cast<const u32x4*>(xr + k + 8);
+      for (int i = 0; i < NR; ++i) {
+        const int id = ids[i] < 0 ? 0 : ids[i];
+        const uint8_t* wr = static_cast<const uint8_t*>(S.w) + (size_t)id * S.ldw;
+        scale[i] = S.wscale[id];
+#pragma unroll
+        for (int j = 0; j < kDotE4m3; ++j)
+          wv[i][j] = *reinterpret_cast<const u32x4*>(wr + min(c0 + 1024 * j + lane * 16, K - 16));
       }
 #pragma unroll
       for (int j = 0; j < kDotE4m3; ++j) {
-        if (k0 + 1024 * j + lane * 16 < K) {
+        if (c0 + 1024 * j + lane * 16 < K) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {   // bytes 4c .. 4c+3 of the 16
-            const uint32_t b4 = wv[j][c];
-            const u32x4& xh = c < 2 ? xa[j] : xb[j];
-            const uint32_t x01 = xh[2 * (c & 1)], x23 = xh[2 * (c & 1) + 1];
-            s0 = __builtin_fmaf(lo_bf16(x01), e4m3_page(b4 & 255u) * scale, s0);
-            s1 = __builtin_fmaf(hi_bf16(x01), e4m3_page((b4 >> 8) & 255u) * scale, s1);
-            s0 = __builtin_fmaf(lo_bf16(x23), e4m3_page((b4 >> 16) & 255u) * scale, s0);
-            s1 = __builtin_fmaf(hi_bf16(x23), e4m3_page(b4 >> 24) * scale, s1);
-          }
+          for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {   // bytes 4c .. 4c+3 of the 16
+              const uint32_t b4 = wv[i][j][c];
+              const u32x4& xh = xc.v[j][c >> 1];
+              const uint32_t x01 = xh[2 * (c & 1)], x23 = xh[2 * (c & 1) + 1];
+              s0[i] = __builtin_fmaf(lo_bf16(x01), e4m3_page(b4 & 255u) * scale[i], s0[i]);
+              s1[i] = __builtin_fmaf(hi_bf16(x01), e4m3_page((b4 >> 8) & 255u) * scale[i], s1[i]);
+              s0[i] = __builtin_fmaf(lo_bf16(x23), e4m3_page((b4 >> 16) & 255u) * scale[i], s0[i]);
+              s1[i] = __builtin_fmaf(hi_bf16(x23), e4m3_page(b4 >> 24) * scale[i], s1[i]);
+            }
         }
       }
-    }
-  } else {
-    // lane l takes 32 consecutive elements (16 bytes, two scale blocks) per 2048
-    const uint8_t* wr = static_cast<const uint8_t*>(S.w) + (size_t)id * S.ldw;
-    const uint8_t* br = S.bscale + (size_t)id * S.lds;
-    const float g = *S.gscale;
-    for (int k0 = 0; k0 < K; k0 += 2048 * kDotNvfp4) {
-      u32x4 wv[kDotNvfp4], xv[kDotNvfp4][4];
-      uint32_t bv[kDotNvfp4];
+    } else {
+      const float g = *S.gscale;
+      u32x4 wv[NR][kDotNvfp4];
+      uint32_t bv[NR][kDotNvfp4];
 #pragma unroll
-      for (int j = 0; j < kDotNvfp4; ++j) {   // clamped, unconditional loads
-        const int k = min(k0 + 2048 * j + lane * 32, K - 32);
-        wv[j] = *reinterpret_cast<const u32x4*>(wr + k / 2);
-        bv[j] = *reinterpret_cast<const uint16_t*>(br + k / 16);
+      for (int i = 0; i < NR; ++i) {
+        const int id = ids[i] < 0 ? 0 : ids[i];
+        const uint8_t* wr = static_cast<const uint8_t*>(S.w) + (size_t)id * S.ldw;
+        const uint8_t* br = S.bscale + (size_t)id * S.lds;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xv[j][q] = *reinterpret_cast<const u32x4*>(xr + k + 8 * q);
+        for (int j = 0; j < kDotNvfp4; ++j) {
+          const int k = min(c0 + 2048 * j + lane * 32, K - 32);
+          wv[i][j] = *reinterpret_cast<const u32x4*>(wr + k / 2);
+          bv[i][j] = *reinterpret_cast<const uint16_t*>(br + k / 16);
+        }
       }
 #pragma unroll
       for (int j = 0; j < kDotNvfp4; ++j) {
-        if (k0 + 2048 * j + lane * 32 < K) {
+        if (c0 + 2048 * j + lane * 32 < K) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {   // scale block h: bytes 8h .. 8h+7, elements 16h .. 16h+15
-            const float bs = e4m3_scale((bv[j] >> (8 * h)) & 255u);
+          for (int i = 0; i < NR; ++i)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              const uint32_t b4 = wv[j][2 * h + c];   // elements 16h + 8c .. +7, low nibble first
+            for (int h = 0; h < 2; ++h) {   // scale block h: bytes 8h .. 8h+7, elements 16h .. 16h+15
+              const float bs = e4m3_scale((bv[i][j] >> (8 * h)) & 255u);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const uint32_t xw = xv[j][2 * h + c][e];   // x of elements 2e, 2e+1 of this word
-                const float w0 = round_bf16(e2m1_value((b4 >> (8 * e)) & 15u) * bs * g);
-                const float w1 = round_bf16(e2m1_value((b4 >> (8 * e + 4)) & 15u) * bs * g);
-                s0 = __builtin_fmaf(lo_bf16(xw), w0, s0);
-                s1 = __builtin_fmaf(hi_bf16(xw), w1, s1);
+              for (int c = 0; c < 2; ++c) {
+                const uint32_t b4 = wv[i][j][2 * h + c];   // elements 16h + 8c .. +7, low nibble first
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const uint32_t xw = xc.v[j][2 * h + c][e];   // x of elements 2e, 2e+1 of this word
+                  const float w0 = round_bf16(e2m1_value((b4 >> (8 * e)) & 15u) * bs * g);
+                  const float w1 = round_bf16(e2m1_value((b4 >> (8 * e + 4)) & 15u) * bs * g);
+                  s0[i] = __builtin_fmaf(lo_bf16(xw), w0, s0[i]);
+                  s1[i] = __builtin_fmaf(hi_bf16(xw), w1, s1[i]);
+                }
               }
             }
-          }
         }
       }
     }
+  };
+  for (int c0 = 0; c0 < K; c0 += XC::kLen) {
+    XC xc;
+    xc.load(xr, K, c0, lane);
+    chunk(xc, c0);
   }
-  float sum = s0 + s1;
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  return sum;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    float sum = s0[i] + s1[i];
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    out[i] = ids[i] < 0 ? -__builtin_inff() : sum;
+  }
+}
+
+// The exact logit of one row (see wave_dots).
+template <int kKind>
+__device__ float wave_dot(const RowSrc& S, uint32_t id, const uint16_t* xr, int K, int lane) {
+  const int ids[1] = {(int)id};
+  float out[1];
+  wave_dots<kKind, 1>(S, ids, xr, K, lane, out);
+  return out[0];
 }
 
 constexpr int kSelThreads = 1024;
@@ -1698,6 +1757,17 @@ __device__ __forceinline__ int lane_prefix(unsigned long long bal) {
 // four waves (+3 us): fewer parts repeat the list less, but load the R rows
 // of W through fewer CUs.
 constexpr int kWideThreads = 512;
+// From this many rows on, the one-call path takes each row in one
+// workgroup, each wave holding the loads of kRerankRows candidate rows at
+// once (32 rows in flight at R = 32): no hand-off between workgroups, and
+// with this many rows the R rows of W still arrive through enough CUs
+// (per call, one part against four: 132.4 / 133.5 us at M = 72, 99.4 /
+// 99.1 at 48, 73.8 / 71.5 at 32, 50.2 / 47.8 at 8: with few rows, a row's
+// 320 KB of W through one CU takes longer than the hand-off).
+constexpr int kRerankOnePartM = 64;
+constexpr int kRerankRows = 4;
+// Dynamic LDS of the block-maximum rerank: x of one row (K <= DH_MAX_K).
+constexpr size_t kWideMaxLds = (size_t)2 * DH_MAX_K;
 
 struct WideShared {
   unsigned int hist[256];
@@ -1888,32 +1958,58 @@ constexpr int kMaxParts = 8;   // workgroups one row's exact logits are split ov
 // exact logits.  With kArgmax the part also takes the best of its ranks; a
 // row split over several parts hands the parts' bests to the part that
 // arrives last.
-template <int NTHR, bool kArgmax, int kKind>
-__device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part, int nparts) {
+template <int NTHR, bool kArgmax, int kKind, int NR>
+__device__ void rerank_part(WideShared& sh, u32x4* xlds, const RerankArgs& A, int m, int part, int nparts) {
   constexpr int NW = NTHR / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int R = A.R, K = A.K;
+  // x[m] into LDS by DMA while the list is selected: op o of wave w (o = w,
+  // w + NW, ...) moves bytes 1024 o .. 1024 o + 1023 of the row, lanes past
+  // the row's end re-reading its last 16 bytes into the padding
+  {
+    const uint16_t* xg = A.x + (size_t)m * K;
+    const int bytes = 2 * K, ops = (bytes + 1023) / 1024;
+    const int w0 = __builtin_amdgcn_readfirstlane(wave);
+    for (int o = w0; o < ops; o += NW) {   // wave-uniform
+      const uint32_t voff = (uint32_t)min(1024 * o + 16 * lane, bytes - 16);
+      dma16(voff, xg, __builtin_amdgcn_readfirstlane(lds_addr(xlds) + 1024 * o));
+    }
+  }
   rerank_list<NTHR>(sh, A, m);
+  wait_vm<0>();   // this wave's DMA has landed; after the barrier, every wave's
+  __syncthreads();
+  const uint16_t* xr = reinterpret_cast<const uint16_t*>(xlds);
 
-  // the exact logit of rank r: this wave reads W[id] and x[m] once, all
-  // loads in flight.  An empty rank (key 0: fewer survivors than R, which
-  // candidates written by the coarse pass never leave) is (-1, -inf) and
-  // reads no row.
+  // The exact logits of ranks NR s .. NR s + NR - 1, slot s = NW (part +
+  // nparts i) + wave: this wave reads the NR rows of W once, all loads in
+  // flight.  An empty rank (key 0: fewer survivors than R, which candidates
+  // written by the coarse pass never leave) is (-1, -inf).
   float bv = -__builtin_inff();
   int bi = -1;
-  for (int r = NW * part + wave; r < R; r += NW * nparts) {   // wave-uniform
-    const unsigned long long key = sh.list[r];
-    const int id = key ? (int)key_id(key) : -1;
-    const float sum = key ? wave_dot<kKind>(A.src, (uint32_t)id, A.x + (size_t)m * K, K, lane) : -__builtin_inff();
-    if (lane == 0) {
-      A.rr_id[(size_t)m * R + r] = id;
-      A.rr_val[(size_t)m * R + r] = sum;
-      // `y.scatter_(1, idx, ex.to(bfloat16))`: ids of one row are distinct
-      if (A.row_out && id >= 0) A.row_out[(size_t)m * A.N + id] = (uint16_t)f32_to_bf16_rne(sum);
+  for (int sl = NW * part + wave; NR * sl < R; sl += NW * nparts) {   // wave-uniform
+    int ids[NR];
+    float sums[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = NR * sl + i;
+      const unsigned long long key = r < R ? sh.list[r] : 0ull;
+      ids[i] = key ? (int)key_id(key) : -1;
     }
-    if (ranks_above(sum, id, bv, bi)) {
-      bv = sum;
-      bi = id;
+    wave_dots<kKind, NR>(A.src, ids, xr, K, lane, sums);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = NR * sl + i;
+      if (r >= R) break;
+      if (lane == 0) {
+        A.rr_id[(size_t)m * R + r] = ids[i];
+        A.rr_val[(size_t)m * R + r] = sums[i];
+        // `y.scatter_(1, idx, ex.to(bfloat16))`: ids of one row are distinct
+        if (A.row_out && ids[i] >= 0) A.row_out[(size_t)m * A.N + ids[i]] = (uint16_t)f32_to_bf16_rne(sums[i]);
+      }
+      if (ranks_above(sums[i], ids[i], bv, bi)) {
+        bv = sums[i];
+        bi = ids[i];
+      }
     }
   }
   if constexpr (kArgmax) {
@@ -1965,11 +2061,13 @@ __device__ void rerank_part(WideShared& sh, const RerankArgs& A, int m, int part
   }
 }
 
-// Rerank kernel: grid (nparts, M), one part of one row per workgroup.
-template <bool kArgmax, int kKind, int NTHR>
+// Rerank kernel: grid (nparts, M), one part of one row per workgroup, NR
+// candidate rows per wave at a time.
+template <bool kArgmax, int kKind, int NTHR, int NR>
 __global__ __launch_bounds__(NTHR) void rerank_wide_kernel(RerankArgs A) {
   __shared__ WideShared sh;
-  rerank_part<NTHR, kArgmax, kKind>(sh, A, blockIdx.y, blockIdx.x, gridDim.x);
+  extern __shared__ __align__(16) u32x4 xlds[];   // x[m], rounded up to 1 KB
+  rerank_part<NTHR, kArgmax, kKind, NR>(sh, xlds, A, blockIdx.y, blockIdx.x, gridDim.x);
 }
 
 
@@ -2243,20 +2341,31 @@ hipError_t launch_wide(const void* x, const RowSrc& src, int M, int K, int N, co
                        uint16_t* row_out = nullptr) {
   const RerankArgs A{static_cast<const uint16_t*>(x), src, K, N, cand_val,
                      cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, hand, row_out};
-  auto go = [&](auto nthr) {
-    constexpr int NTHR = decltype(nthr)::value, NW = NTHR / 64;
+  auto go = [&](auto nthr, auto nr) {
+    constexpr int NTHR = decltype(nthr)::value, NW = NTHR / 64, NR = decltype(nr)::value;
     // ids must fit the hand-off key to split a row; otherwise one part per row
-    const int parts = (!kArgmax || N < (1 << kHandIdBits) - 1) ? std::min((R + NW - 1) / NW, kMaxParts) : 1;
+    const int parts = (!kArgmax || N < (1 << kHandIdBits) - 1)
+                          ? std::max(1, std::min((R + NW * NR - 1) / (NW * NR), kMaxParts)) : 1;
     const dim3 grid(parts, M);
-    if (src.kind == kRowsE4m3)
-      hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsE4m3, NTHR>), grid, dim3(NTHR), 0, s, A);
-    else if (src.kind == kRowsNvfp4)
-      hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsNvfp4, NTHR>), grid, dim3(NTHR), 0, s, A);
-    else
-      hipLaunchKernelGGL((rerank_wide_kernel<kArgmax, kRowsBf16, NTHR>), grid, dim3(NTHR), 0, s, A);
+    const size_t lds = ((size_t)2 * K + 1023) / 1024 * 1024;   // x[m] in LDS
+    auto launch = [&](auto kernel) -> hipError_t {
+      static bool attr_set = false;   // per instantiation; the attribute only ever grows to kWideMaxLds
+      if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideMaxLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+      }
+      hipLaunchKernelGGL(kernel, grid, dim3(NTHR), lds, s, A);
+      return hipGetLastError();
+    };
+    if (src.kind == kRowsE4m3) return launch(rerank_wide_kernel<kArgmax, kRowsE4m3, NTHR, NR>);
+    if (src.kind == kRowsNvfp4) return launch(rerank_wide_kernel<kArgmax, kRowsNvfp4, NTHR, NR>);
+    return launch(rerank_wide_kernel<kArgmax, kRowsBf16, NTHR, NR>);
   };
-  go(std::integral_constant<int, kWideThreads>{});
-  return hipGetLastError();
+  if (kArgmax && M >= kRerankOnePartM)
+    return go(std::integral_constant<int, kWideThreads>{}, std::integral_constant<int, kRerankRows>{});
+  return go(std::integral_constant<int, kWideThreads>{}, std::integral_constant<int, 1>{});
 }
 
 int launch_rerank(const void* x, const RowSrc& src, int M, int K, int N, const float* cand_val,
