@@ -722,9 +722,11 @@ void coarse_resident_kernel(CoarseArgs A) {
 // bytes still on their way from HBM, and the codes have CD byte groups to
 // arrive.  With one wave per block (one or two row tiles) both streams share
 // the wave's counter, and x runs XD = 3..6 stages (groups) ahead.
-// Workspace of one launch with MT row tiles: x slabs, then zero-point slabs.
+// Workspace of one launch with MT row tiles: x slabs, zero-point slabs, then
+// the rows' scale exponents (fp16 kernel).
+constexpr size_t kFexpBytes = 512;
 size_t big_workspace_bytes(int MT, int K) {
-  return (size_t)(K / DH_GROUP) * 4096 * MT + (size_t)(K / 512) * kZpEntries * 16;
+  return (size_t)(K / DH_GROUP) * 4096 * MT + (size_t)(K / 512) * kZpEntries * 16 + kFexpBytes;
 }
 
 // LDS byte address of a pointer into __shared__ memory.
@@ -806,6 +808,41 @@ struct BigArgs {
 // sixteen neighbouring lists cover the 64 banks once.
 constexpr int kScStride = 68;
 
+// The top-kcand list (kcand <= 8) of row m, block b, selected by this thread
+// alone from the row's 64 keys (key[c] of column c in registers, key_at(c)
+// the same key read from LDS).
+template <class KeyAt>
+__device__ __forceinline__ void emit_list8(const uint32_t (&key)[64], KeyAt key_at, const CoarseArgs& A, int m,
+                                           int b) {
+  uint32_t slot[8];   // 63 - column, or 64 for an empty slot
+  dh::select8_row(key, key_at, slot);
+  float val[8];
+  int32_t id[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool ok = slot[i] < 64u;
+    const int col = 63 - (int)(ok ? slot[i] : 63u);
+    val[i] = ok ? key_f32(key_at(col)) : -__builtin_inff();
+    id[i] = ok ? b * 64 + col : -1;
+  }
+  const size_t base = ((size_t)m * A.nblk + b) * A.kcand;
+  if (A.kcand == 8) {   // 32-byte aligned: the list is two 16-byte pieces
+    reinterpret_cast<f32x4*>(A.cand_val + base)[0] = f32x4{val[0], val[1], val[2], val[3]};
+    reinterpret_cast<f32x4*>(A.cand_val + base)[1] = f32x4{val[4], val[5], val[6], val[7]};
+    reinterpret_cast<u32x4*>(A.cand_id + base)[0] =
+        u32x4{(uint32_t)id[0], (uint32_t)id[1], (uint32_t)id[2], (uint32_t)id[3]};
+    reinterpret_cast<u32x4*>(A.cand_id + base)[1] =
+        u32x4{(uint32_t)id[4], (uint32_t)id[5], (uint32_t)id[6], (uint32_t)id[7]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < A.kcand) {
+        A.cand_val[base + i] = val[i];
+        A.cand_id[base + i] = id[i];
+      }
+  }
+}
+
 // Top-kcand lists (kcand <= 8) of every (block, row) pair of a many-row
 // workgroup, one list per thread, from the keys in LDS (row lb * MP + m).
 // Each key's low 6 bits are replaced by 63 - column, so the keys of a row are
@@ -840,33 +877,7 @@ __device__ __forceinline__ void lane_select8(const uint32_t* sk, const CoarseArg
 #pragma unroll
       for (int e = 0; e < 4; ++e) key[4 * c4 + e] = v[e];
     }
-    uint32_t slot[8];   // 63 - column, or 64 for an empty slot
-    dh::select8_row(key, [&](int c) { return row[c]; }, slot);
-    float val[8];
-    int32_t id[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = slot[i] < 64u;
-      const int col = 63 - (int)(ok ? slot[i] : 63u);
-      val[i] = ok ? key_f32(row[col]) : -__builtin_inff();
-      id[i] = ok ? b * 64 + col : -1;
-    }
-    const size_t base = ((size_t)m * A.nblk + b) * A.kcand;
-    if (A.kcand == 8) {   // 32-byte aligned: the list is two 16-byte pieces
-      reinterpret_cast<f32x4*>(A.cand_val + base)[0] = f32x4{val[0], val[1], val[2], val[3]};
-      reinterpret_cast<f32x4*>(A.cand_val + base)[1] = f32x4{val[4], val[5], val[6], val[7]};
-      reinterpret_cast<u32x4*>(A.cand_id + base)[0] =
-          u32x4{(uint32_t)id[0], (uint32_t)id[1], (uint32_t)id[2], (uint32_t)id[3]};
-      reinterpret_cast<u32x4*>(A.cand_id + base)[1] =
-          u32x4{(uint32_t)id[4], (uint32_t)id[5], (uint32_t)id[6], (uint32_t)id[7]};
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < A.kcand) {
-          A.cand_val[base + i] = val[i];
-          A.cand_id[base + i] = id[i];
-        }
-    }
+    emit_list8(key, [&](int c) { return row[c]; }, A, m, b);
   }
 }
 
@@ -1144,6 +1155,343 @@ void coarse_mfma_kernel(BigArgs BA) {
     }
   }
   big_wave<MT, 0>(BA, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Coarse kernel for more rows, scale folded into the weights (fp16 MFMA).
+//
+// Each group's contribution is x . (S/4) v, with v the 2-bit code and S the
+// bf16 scale: (S/4) v has at most 10 significant bits (S has 8, v <= 3), so
+// it is an exact fp16 value wherever |S| lies in [2^-15, 255] (below 2^-15 it
+// rounds to the fp16 subnormal step, 2^-24), and x scaled by a power of two
+// per row is an exact fp16 value for every element of at least 2^-31 times
+// the row's largest magnitude (smaller ones round to that step as well).  The
+// products are then exact in fp32, as with the page's bf16 decode, and the
+// per-group scale needs neither its own
+// accumulator nor an update per score: the MFMAs accumulate the whole row of
+// K into one accumulator per tile, and the zero-point part, sum_g (S - ZS)
+// X_g, joins it through one bf16 MFMA per byte group as in the many-row
+// kernel.  The coarse score is the accumulator times 2^-f, f the row's scale.
+//
+// Decode of quarter q (code at bits 2q..2q+1 of each byte of a 16-bit half):
+// OR-ing in the fp16 exponent of 1.0 gives 1 + v 2^(2q-10); a packed fp16
+// fused multiply-add with T = (S/4) 2^(10-2q), d * T - T = v (S/4), rounds
+// once, exactly.
+//
+// Workgroup = 8 waves = 8 blocks of 64 columns, one wave per block holding
+// its 4 column tiles for all MT row tiles, so every x fragment read from LDS
+// feeds 4 MFMAs, and 1940 blocks take 243 workgroups (one per CU).  Stage j
+// = 4G + q is group q of byte group G.  Direct-to-LDS DMA ring:
+//   x slabs (one group, 4 MT chunks of 1 KB) kH16XD stages ahead, in
+//   kH16XD + 1 slots; every wave issues h16_xops(MT) ops per stage (chunk
+//   wave + 8 k; chunks past the slab repeat chunk c - 4 MT into the same
+//   place, the same bytes);
+//   at stage 4G + 1 (after every wave took byte group G's codes into
+//   registers): byte group G + 1's zero-point slab (chunk wave mod 4, again
+//   issued twice) and its codes and scale pairs (each wave its own block, 9
+//   chunks) into the single code slot.
+// Every wave issues the same ops in the same order, so each wait is a
+// constant: at the end of stage j it completes slab j + 1 and, at q = 3, the
+// next byte group's codes and zero-point slab.
+// (The schedule's shape, op addresses and wait counts: dh::h16_* in ring_plan.h.)
+constexpr int kHBlocks = dh::kH16Blocks;
+constexpr size_t h16_lds_bytes(int MT) {
+  const size_t ring = dh::h16_ring_bytes(MT);
+  const size_t keys = (size_t)kHBlocks * 16 * MT * 64 * 4;   // the epilogue's keys: 64 per (block, row)
+  return ring > keys ? ring : keys;
+}
+
+// x for one launch of up to 80 rows in the workspace for the fp16 kernel,
+// written by prep_xh_kernel: per row the scale exponent f (int), then slabs
+// and zero-point slabs in the many-row kernel's layout, with x * 2^f as fp16
+// and the group sums X * 2^f split in three bf16 parts.
+struct HArgs {
+  CoarseArgs c;
+  const u32x4* xslab;
+  const u32x4* zslab;
+  const int* fexp;
+};
+
+// One workgroup (4 waves) per row m of a launch: wave w takes the byte groups
+// G = w, w + 4, ...; lane q * 16 + p takes piece p (8 consecutive k) of group
+// 4G + q.  The row's largest |x| (an exact max) gives f = 15 - e with
+// max = m 2^e, 1/2 <= m < 1, so that every |x| 2^f < 2^15.
+constexpr int kPrepHMaxG = 8;   // byte groups per wave held in registers: K <= 8 * 4 * 512
+__global__ __launch_bounds__(256) void prep_xh_kernel(const uint16_t* __restrict__ x, int M, int MP, int K,
+                                                      u32x4* __restrict__ xslab, u32x4* __restrict__ zslab,
+                                                      int* __restrict__ fexp) {
+  __shared__ float wmax[4];
+  const int m = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int NG4 = K >> 9, Q4 = K >> 2;
+  const int q = lane >> 4, p = lane & 15;
+  const int h = p >> 3, s = (p >> 1) & 3, e = p & 1, f = (h * 2 + e) * 4 + s;
+  u32x4 v[kPrepHMaxG];
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPrepHMaxG; ++i) {
+    const int G = wave + 4 * i;
+    v[i] = u32x4{0u, 0u, 0u, 0u};
+    if (G < NG4 && m < M) v[i] = *reinterpret_cast<const u32x4*>(x + (size_t)m * K + q * Q4 + 128 * G + 8 * p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fmaxf(fabsf(lo_bf16(v[i][c])), fabsf(hi_bf16(v[i][c]))));
+  }
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) wmax[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  int ex = 0;
+  if (mx > 0.f) (void)__builtin_frexpf(mx, &ex);
+  const int fx = mx > 0.f ? 15 - ex : 0;
+  if (threadIdx.x == 0) fexp[m] = fx;
+#pragma unroll
+  for (int i = 0; i < kPrepHMaxG; ++i) {
+    const int G = wave + 4 * i;
+    if (G >= NG4) break;   // wave-uniform
+    // fp16 x * 2^fx in the decode order {0,2,1,3,4,6,5,7}, and the unscaled sum
+    float xs[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      xs[2 * c] = lo_bf16(v[i][c]);
+      xs[2 * c + 1] = hi_bf16(v[i][c]);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) sum += xs[c];
+    const int order[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+    uint32_t hw[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const _Float16 hv = (_Float16)__builtin_ldexpf(xs[order[c]], fx);
+      hw[c] = (uint32_t)__builtin_bit_cast(uint16_t, hv);
+    }
+    xslab[((size_t)(4 * G + q) * 16 + f) * MP + m] =
+        u32x4{hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16};
+    sum = row16_sum(sum);
+    float X[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) X[u] = __builtin_ldexpf(__shfl(sum, 16 * u, 64), fx);
+    if (lane < 2) {
+      uint32_t part[3][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float r = X[u];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {   // r - bf16(r) is exact in fp32
+          part[c][u] = f32_to_bf16_rne(r);
+          r -= __uint_as_float(part[c][u] << 16);
+        }
+      }
+      const u32x4 o = lane == 0 ? u32x4{part[0][0] | part[0][1] << 16, part[0][2] | part[0][3] << 16,
+                                        part[1][0] | part[1][1] << 16, part[1][2] | part[1][3] << 16}
+                                : u32x4{part[2][0] | part[2][1] << 16, part[2][2] | part[2][3] << 16, 0u, 0u};
+      zslab[(size_t)G * kZpEntries + lane * MP + m] = o;
+    }
+  }
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Quarter q's weights (S/4) v of one k-slice of a tile, as fp16 in the decode
+// order: d = code bits | 1.0, then d * T - T per packed pair (one rounding).
+// (d & mask) | one in one instruction (the compiler otherwise splits it in
+// two, as its three-operand form takes no literal constants on this target).
+__device__ __forceinline__ uint32_t and_or(uint32_t d, uint32_t mask, uint32_t one) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(d), "s"(mask), "v"(one));
+  return r;
+}
+// mask (wave-uniform) and one: one AND-OR per pair.
+__device__ __forceinline__ f16x8 decode_h16(uint32_t d0, uint32_t o0, uint32_t d1, uint32_t o1, uint32_t mask,
+                                            uint32_t one, f16x2 tt) {
+  const uint32_t w[4] = {and_or(d0, mask, one), and_or(o0, mask, one), and_or(d1, mask, one), and_or(o1, mask, one)};
+  f16x8 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 dv = __builtin_bit_cast(f16x2, w[i]);
+    const f16x2 r = __builtin_elementwise_fma(dv, tt, -tt);
+    out[2 * i] = r[0];
+    out[2 * i + 1] = r[1];
+  }
+  return out;
+}
+
+template <int MT>
+__global__ __launch_bounds__(64 * kHBlocks) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void coarse_h16_kernel(HArgs HA) {
+  constexpr int MP = 16 * MT, NX = dh::h16_xops(MT), SLOTS = dh::kH16Slots;
+  const CoarseArgs& A = HA.c;
+  extern __shared__ __align__(16) unsigned char smem[];
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);                     // [SLOTS][16][MP]
+  u32x4* cs = xs + SLOTS * 16 * MP;                                // [8 blocks][9 chunks][64]
+  u32x4* zs = cs + kHBlocks * kCodeChunks * 64;                    // [2][256]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 4, nn = lane & 15;
+  const int b = blockIdx.x * kHBlocks + wave;
+  const bool blk_ok = b < A.nblk;
+  const int NG4 = A.K >> 9, NSTAGE = 4 * NG4;
+  zero_counters(A);
+
+  // A block past the last one streams block 0 (valid memory) and writes nothing.
+  const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
+  const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64;
+  const uint32_t voff = lane * 16;
+  const uint32_t xs_l = lds_addr(xs), zs_l = lds_addr(zs), cs_l = lds_addr(cs + wave * kCodeChunks * 64);
+
+  auto issue_x = [&](int j) {   // slab of stage j (clamped to the last) into its slot
+    const int slab = dh::h16_slab(j, NSTAGE);
+    const uint32_t dst = xs_l + (uint32_t)((j % SLOTS) * 16 * MP * 16);
+#pragma unroll
+    for (int k = 0; k < NX; ++k) {
+      const int c = dh::h16_xchunk(MT, wave, k);
+      dma16(voff, HA.xslab + (size_t)slab * 256 * MT + c * 64, dst + c * 1024);
+    }
+  };
+  auto issue_bytes = [&](int G) {   // zero-point slab and codes of byte group G (clamped)
+    const int Gc = dh::h16_byte_group(G, NG4);
+    const int c = wave & 3;
+    dma16(voff, HA.zslab + (size_t)Gc * kZpEntries + c * 64, zs_l + (uint32_t)((Gc & 1) * 4096 + c * 1024));
+#pragma unroll
+    for (int k = 0; k < kCodeChunks; ++k)
+      dma16_nt(voff, k < 8 ? tp + (Gc * 8 + k) * 64 : pp + Gc * 64, cs_l + k * 1024);
+  };
+
+  // prologue: slabs of stages 0 .. kH16XD - 1, byte group 0
+#pragma unroll
+  for (int j = 0; j < dh::kH16XD; ++j) issue_x(j);
+  issue_bytes(0);
+  wait_vm<0>();
+  __syncthreads();
+
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const u32x4* xl = xs + hh * MP + nn;   // this lane's fragment 0 (A row nn, k-slot hh) of slot 0
+  const u32x4* cw = cs + wave * kCodeChunks * 64;
+  for (int G = 0; G < NG4; ++G) {
+    // byte group G's codes and scale pairs (the slot is refilled at stage 4G + 1)
+    u32x4 raw[2][4], raw8[2][4], sz[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) raw[h][t] = cw[(h * 4 + t) * 64 + lane];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sz[t] = cw[512 + t * 16 + nn];
+    shift_codes(raw, raw8);
+    // zero-point part of byte group G: rows' X parts against S - ZS (exact in bf16)
+    {
+      const u32x4* zg = zs + (G & 1) * kZpEntries;
+      u32x4 za[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) za[i] = hh < 2 ? zg[(hh & 1) * MP + 16 * i + nn] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t d[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) d[qq] = __float_as_uint(lo_bf16(sz[t][qq]) - hi_bf16(sz[t][qq]));
+        const uint32_t p01 = (d[0] >> 16) | (d[1] & 0xFFFF0000u);
+        const uint32_t p23 = (d[2] >> 16) | (d[3] & 0xFFFF0000u);
+        const u32x4 zb = u32x4{p01, p23, p01, p23};   // slots 8..15 meet zero x parts
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[i]),
+                                                             __builtin_bit_cast(bf16x8, zb), acc[i][t], 0, 0, 0);
+      }
+    }
+    auto stage = [&](auto qc) {
+      constexpr int Q = decltype(qc)::value;
+      const int j = 4 * G + Q;
+      issue_x(j + dh::kH16XD);
+      if constexpr (Q == 1) issue_bytes(G + 1);
+      // the code bits of quarter Q, and the exponent field of 1.0 (disjoint from them)
+      const uint32_t mask = __builtin_amdgcn_readfirstlane(0x00030003u << (2 * Q));
+      const uint32_t one = 0x3C003C00u;
+      f16x2 tt[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {   // T = (S/4) 2^(10 - 2Q) = S 2^(8 - 2Q), exact in fp16
+        const _Float16 tv = (_Float16)__builtin_ldexpf(lo_bf16(sz[t][Q]), 8 - 2 * Q);
+        tt[t] = f16x2{tv, tv};
+      }
+      const u32x4* xb = xl + (j % SLOTS) * 16 * MP;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int h = ks >> 1, e = ks & 1;
+        u32x4 a[MT];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) a[i] = xb[((h * 2 + e) * 4) * MP + 16 * i];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const f16x8 bv = decode_h16(raw[h][t][2 * e], raw8[h][t][2 * e], raw[h][t][2 * e + 1],
+                                      raw8[h][t][2 * e + 1], mask, one, tt[t]);
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[i]), bv, acc[i][t], 0,
+                                                              0, 0);
+        }
+      }
+      wait_vm<dh::h16_wait(MT, Q)>();
+      __syncthreads();
+    };
+    stage(std::integral_constant<int, 0>{});
+    stage(std::integral_constant<int, 1>{});
+    stage(std::integral_constant<int, 2>{});
+    stage(std::integral_constant<int, 3>{});
+  }
+  wait_vm<0>();
+  // the coarse scores: the accumulators times 2^-f of their rows
+  float rs[MT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rs[i][r] = __builtin_ldexpf(1.0f, -HA.fexp[16 * i + 4 * hh + r]);
+  if (A.kcand > 8) {   // lists longer than eight: the 16-lane rounds, from registers
+    if (!blk_ok) return;
+    block_select<MT, 4>([&](int i, int r, int t) { return acc[i][t][r] * rs[i][r]; }, A, b, hh, nn);
+    return;
+  }
+  // Every wave's DMA writes have landed and every wave is done with the ring:
+  // the LDS takes the keys of the workgroup's 8 blocks, row rho = lb MP + m
+  // (block lb, row m) in 64 words whose 16-byte pieces are XOR-swizzled by rho
+  // mod 16 (piece c at c ^ (rho & 15): conflict-free for the writes below and
+  // for sixteen consecutive rows read piece by piece).  Then thread q selects
+  // the lists q and q + 512 (list l: block l / M, row l % M).
+  u32x4* sk = reinterpret_cast<u32x4*>(smem);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int col = 16 * t + nn, n = 64 * b + col;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * i + 4 * hh + r, rho = wave * MP + row;
+        const bool ok = blk_ok && n < A.N && row < A.M;
+        const float sv = acc[i][t][r] * rs[i][r];
+        reinterpret_cast<uint32_t*>(sk + rho * 16 + ((col >> 2) ^ (row & 15)))[col & 3] =
+            ok ? f32_key(sv + 0.0f) : 0u;   // -0 as +0
+        if (ok) store_scores(A, row, n, sv);
+      }
+    }
+  __syncthreads();
+  for (int l = threadIdx.x; l < kHBlocks * A.M; l += 64 * kHBlocks) {
+    const int lb = l / A.M, m = l - lb * A.M, bq = blockIdx.x * kHBlocks + lb;
+    if (bq >= A.nblk) continue;
+    const u32x4* row = sk + (lb * MP + m) * 16;
+    const int sw = m & 15;
+    uint32_t key[64];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const u32x4 v = row[c ^ sw];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[4 * c + e] = v[e];
+    }
+    emit_list8(key, [&](int c) { return reinterpret_cast<const uint32_t*>(row + ((c >> 2) ^ sw))[c & 3]; }, A, m, bq);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2164,6 +2512,22 @@ hipError_t launch_resident(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hi
 }
 
 template <int MT>
+hipError_t launch_h16(const HArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  constexpr size_t lds = h16_lds_bytes(MT);
+  static_assert(lds <= kMaxLds, "LDS budget of the fp16 many-row kernel");
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&coarse_h16_kernel<MT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((A.c.nblk + kHBlocks - 1) / kHBlocks);
+  hipExtLaunchKernelGGL(coarse_h16_kernel<MT>, grid, dim3(64 * kHBlocks), lds, s, e0, e1, 0, A);
+  return hipGetLastError();
+}
+
+template <int MT>
 hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD, BigShape<MT>::CD, BigShape<MT>::BPW, BigShape<MT>::GPS);
   static_assert(lds <= kMaxLds, "LDS budget of the many-row kernel");
@@ -2191,6 +2555,15 @@ int resident_rows(int M, int K) {
   return M <= 2 ? 2 : M <= 4 ? 4 : 8;
 }
 
+
+// The many-row path of a 2-bit head with rows of up to 16384 runs the fp16
+// kernel (its x preparation holds a row's pieces in registers); a 4-bit head
+// (x read modulo kx < K) and longer rows run the bf16 kernel.
+// The fp16 many-row kernel from three row tiles on (one or two tiles: the
+// bf16 kernel, faster there on the same box: M = 16 54.7 against 68.0 us, M =
+// 32 70.6 against 78.3 us per call; M = 48, 64, 72: 92.7, 106.0, 120.1 us
+// against 98.4, 113.4, 130.8 us).
+bool use_h16(int K, int kx, int mt) { return mt >= 3 && kx == K && K <= kPrepHMaxG * 4 * 512; }
 
 // Up to 8 rows whose x fits the workgroup's LDS take the resident kernel (no
 // workspace); every other M the many-row kernel, in launches of up to 80 rows.
@@ -2304,13 +2677,27 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
     const int mt = (B.M + 15) / 16, mp = 16 * mt;
     u32x4* xslab = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(workspace) + kHeaderBytes);
     u32x4* zslab = xslab + (size_t)(K / DH_GROUP) * 256 * mt;
+    int* fexp = reinterpret_cast<int*>(zslab + (size_t)NG4 * kZpEntries);
+    hipEvent_t b0 = m0 == 0 ? ev0 : nullptr;
+    hipEvent_t b1 = m0 + 16 * kMaxMT >= M ? ev1 : nullptr;
+    if (use_h16(K, A.kx, mt)) {
+      hipLaunchKernelGGL(prep_xh_kernel, dim3(mp), dim3(256), 0, s, B.x, B.M, mp, K, xslab, zslab, fexp);
+      if ((e = hipGetLastError()) != hipSuccess)
+        return dh::fail(DH_EHIP, "prep_xh_kernel: %s", hipGetErrorString(e));
+      const HArgs HA{B, xslab, zslab, fexp};
+      switch (mt) {
+        case 3: e = launch_h16<3>(HA, s, b0, b1); break;
+        case 4: e = launch_h16<4>(HA, s, b0, b1); break;
+        default: e = launch_h16<5>(HA, s, b0, b1); break;
+      }
+      if (e != hipSuccess) return dh::fail(DH_EHIP, "coarse_h16_kernel: %s", hipGetErrorString(e));
+      continue;
+    }
     hipLaunchKernelGGL(prep_x_kernel, dim3((mp * NG4 + 3) / 4), dim3(256), 0, s, B.x, B.M, mp, K, A.kx,
                        xslab, zslab);
     if ((e = hipGetLastError()) != hipSuccess)
       return dh::fail(DH_EHIP, "prep_x_kernel: %s", hipGetErrorString(e));
     const BigArgs BA{B, xslab, zslab};
-    hipEvent_t b0 = m0 == 0 ? ev0 : nullptr;
-    hipEvent_t b1 = m0 + 16 * kMaxMT >= M ? ev1 : nullptr;
     switch (mt) {
       case 1: e = launch_big<1>(BA, s, b0, b1); break;
       case 2: e = launch_big<2>(BA, s, b0, b1); break;

@@ -216,6 +216,25 @@ int draft_head_tile(const uint8_t* packed, const uint16_t* S, const uint16_t* ZS
   int rc = check_shape(N, K);
   if (rc) return rc;
   const int64_t Q = K / 4, NG4 = K / 512, NG = K / DH_GROUP;
+  // The many-row kernels take each group's zero-point term as the one bf16
+  // weight S - ZS against the group's x sum, and the fp16 one forms each
+  // weight (S/4) v as an fp16 value, exact for |S| <= 255.  The page's
+  // quantiser meets both: S = bf16(4 (hi - lo) / 3) (under 255 for a group
+  // range under about 191) and ZS = bf16((4 + z) (hi - lo) / 3), z in 0..3,
+  // within a factor 1.75 of S, so that S - ZS has at most 8 significant bits.
+  for (int64_t i = 0; i < N * NG; ++i) {
+    const float s = bf16_to_f32(S[i]), zs = bf16_to_f32(ZS[i]);
+    if (!(s >= -255.0f && s <= 255.0f))
+      return dh::fail(DH_EUNSUP, "tile: scale S[%lld][%lld] = %g is outside [-255, 255], the range the device "
+                      "kernels represent exactly", (long long)(i / NG), (long long)(i % NG), (double)s);
+    const float d = s - zs;
+    uint32_t db;
+    std::memcpy(&db, &d, 4);
+    if (!std::isfinite(zs) || (double)d != (double)s - (double)zs || (db & 0xFFFFu) != 0u)
+      return dh::fail(DH_EUNSUP, "tile: S - ZS at [%lld][%lld] (%g - %g) is not a bf16 value, the form the device "
+                      "kernels take the zero-point term in", (long long)(i / NG), (long long)(i % NG), (double)s,
+                      (double)zs);
+  }
   const int64_t nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
   parallel_rows(nblk, 0, [&](int64_t a, int64_t bend) {
     for (int64_t b = a; b < bend; ++b) {

@@ -101,7 +101,13 @@ int draft_head_quantize_pack(const uint16_t* w, int64_t N, int64_t K, int64_t ld
  * where NG4 = K/512 and q = 0..3 is the quarter.  Each 64-column block is one
  * contiguous span of K/4*64 code bytes and K/128*64 pairs.
  *   packed, S, ZS  canonical arrays (read only);  tiled, pairs  out
- * Errors: DH_EINVAL (null pointer), DH_ESHAPE.
+ * Limits: every |S| <= 255 (the fp16 many-row kernel forms each weight
+ * (S/4) v as an exact fp16 value; the quantiser's S = bf16(4 (hi - lo) / 3)
+ * stays below it for any group whose range is under about 191), and every
+ * S - ZS a bf16 value (the many-row kernels take the zero-point term as that
+ * one weight; the quantiser's ZS lies within a factor 1.75 of S).
+ * Errors: DH_EINVAL (null pointer), DH_ESHAPE, DH_EUNSUP (a pair beyond the
+ * limits, or not finite).
  */
 int draft_head_tile(const uint8_t* packed, const uint16_t* S, const uint16_t* ZS,
                     int64_t N, int64_t K, uint8_t* tiled, uint32_t* pairs);
@@ -145,8 +151,8 @@ int draft_head_int4_as_int2(const uint8_t* packed4, const uint16_t* S, const uin
  * plus, unless M <= 8 and the resident kernel holds all of x in LDS (any K at
  * M = 1; K <= 35840, 15872, 7680 at M = 2, 3..4, 5..8), the x of one launch
  * of up to 80 rows laid out for the many-row kernel: (K/128) * 4096 * MT +
- * (K/512) * 4096 bytes with MT = min(ceil(M/16), 5) (861,184 bytes in all at
- * M = 72, K = 5120).
+ * (K/512) * 4096 + 512 bytes with MT = min(ceil(M/16), 5) (861,696 bytes in
+ * all at M = 72, K = 5120).
  * Errors: DH_EINVAL (null pointer, M < 1), DH_EUNSUP (M > DH_MAX_M), DH_ESHAPE.
  */
 int draft_head_workspace_bytes(int M, int K, size_t* bytes);

@@ -148,12 +148,12 @@ def test_workspace_bytes(lib):
     head = 1024
     for m, k in ((1, 5120), (1, 65536), (2, 39424), (4, 19456), (8, 5120), (8, 8704)):
         assert B.draft_head_workspace_bytes(m, k) == head, (m, k)
-    # many-row kernel: + (K/128) * 4096 * MT + (K/512) * 4096 with MT = min(ceil(M/16), 5)
+    # many-row kernel: + (K/128) * 4096 * MT + (K/512) * 4096 + 512 with MT = min(ceil(M/16), 5)
     for m, k in ((2, 39936), (4, 19968), (8, 9216), (9, 512), (16, 1024), (17, 1024), (72, 5120),
                  (80, 5120), (81, 5120), (128, 5120)):
         mt = min((m + 15) // 16, 5)
-        assert B.draft_head_workspace_bytes(m, k) == head + (k // 128) * 4096 * mt + (k // 512) * 4096, (m, k)
-    assert B.draft_head_workspace_bytes(72, 5120) == 861_184
+        assert B.draft_head_workspace_bytes(m, k) == head + (k // 128) * 4096 * mt + (k // 512) * 4096 + 512, (m, k)
+    assert B.draft_head_workspace_bytes(72, 5120) == 861_696
     out = ctypes.c_size_t()
     _err(lib, lib.draft_head_workspace_bytes(1, 512, None), B.DH_EINVAL)
     _err(lib, lib.draft_head_workspace_bytes(0, 512, ctypes.byref(out)), B.DH_EINVAL)
@@ -417,3 +417,37 @@ def test_forward_row_validation(lib):
     _err(lib, call(ws=None), B.DH_EINVAL)
     _err(lib, call(K=768), B.DH_ESHAPE)
     _err(lib, call(R=81), B.DH_EUNSUP)
+
+
+def test_tile_rejects_pairs_beyond_the_exact_range(lib):
+    """Every |S| <= 255 (the fp16 many-row kernel's weights (S/4) v are exact
+    there) and every S - ZS a bf16 value (the many-row kernels' zero-point
+    weight); other pairs, or non-finite ones, are rejected."""
+    n, k = 64, 512
+    packed = np.zeros((n, k // 4), np.uint8)
+    bits = lambda v: oracle.bf16.from_f32(np.array([v], np.float32))[0]
+    cases = ((255.0, 0.0, None), (-255.0, 0.0, None), (256.0, 0.0, "outside"), (float("inf"), 0.0, "outside"),
+             (float("nan"), 0.0, "outside"), (1.0, 1.75, None), (1.0, 2.0 ** -10, "not a bf16"),
+             (1.0, float("inf"), "not a bf16"), (3.0e-8, 4.0e-8, None))
+    for s_val, zs_val, err in cases:
+        S = np.full((n, k // 128), bits(1.0), np.uint16)
+        ZS = np.full((n, k // 128), bits(1.25), np.uint16)
+        S[7, 2], ZS[7, 2] = bits(s_val), bits(zs_val)
+        if err is None:
+            B.draft_head_tile(packed, S, ZS)
+        else:
+            with pytest.raises(ValueError, match=err):
+                B.draft_head_tile(packed, S, ZS)
+
+
+def test_quantiser_pairs_meet_the_tile_limits(lib):
+    """The quantiser's pairs pass the tile's limits for the workloads' weight
+    scales, wide groups and constant groups alike."""
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((96, 1024)) * 0.02).astype(np.float32)
+    w[3] = 0.0
+    w[4] = 0.37
+    w[5, :128] = 20.0 * rng.standard_normal(128)
+    w[6, :128] = 1e-30
+    packed, S, ZS = B.draft_head_quantize_pack(oracle.bf16.from_f32(w))
+    B.draft_head_tile(packed, S, ZS)
