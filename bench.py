@@ -225,10 +225,11 @@ class Rig:
 
     def int4_call_us(self, ms=(1, 8, 72), steps=200, copies=2):
         """Per-call time of the 4-bit head at KCAND = 1 (the page's 4-bit
-        configuration), run as its 2K-long 2-bit form; weights rotated."""
+        configuration), run as its 2K-long 2-bit form with the head's own
+        pairs (N K/2 + 4 N K/128 = 337,715,200 bytes a call); weights rotated."""
         torch, B = self.torch, self.B
         packed4 = B.draft_head_quantize_pack_int4(self.w_host)
-        tiled, pairs = B.draft_head_tile(*B.draft_head_int4_as_int2(*packed4))
+        tiled, pairs = B.draft_head_tile_int4(*packed4)
         t_t = torch.from_numpy(tiled).to(self.dev)
         t_p = torch.from_numpy(pairs.view(np.int32)).to(self.dev)
         heads = [B.DraftHead(t_t if c == 0 else t_t.clone(), t_p if c == 0 else t_p.clone(), self.heads[0].w,
@@ -575,6 +576,7 @@ def main():
         extra["nvfp4_rerank_us_per_call"] = rig.nvfp4_call_us()
         log(f"one call with the NVFP4 rerank source: {extra['nvfp4_rerank_us_per_call']}")
         extra["int4_kcand1_us_per_call"] = rig.int4_call_us()
+        extra["int4_bytes_per_call"] = N * K // 2 + 4 * N * (K // 128)
         log(f"one call of the 4-bit head at KCAND=1: {extra['int4_kcand1_us_per_call']}")
         log(f"one call with the e4m3 rerank source: {extra['e4m3_rerank_us_per_call']}")
         log(f"row for the caller (draft_head_logits_row alone): {extra['logits_row_us']}")

@@ -59,6 +59,8 @@ def load_library() -> ctypes.CDLL:
     lib.draft_head_quantize_pack_int4.argtypes = [P, i64, i64, i64, P, P, P, i32]
     lib.draft_head_int4_as_int2.restype = i32
     lib.draft_head_int4_as_int2.argtypes = [P, P, P, i64, i64, P, P, P]
+    lib.draft_head_tile_int4.restype = i32
+    lib.draft_head_tile_int4.argtypes = [P, P, P, i64, i64, P, P]
     lib.draft_head_tile.restype = i32
     lib.draft_head_tile.argtypes = [P, P, P, i64, i64, P, P]
     lib.draft_head_workspace_bytes.restype = i32
@@ -203,6 +205,25 @@ def draft_head_tile(packed: np.ndarray, S: np.ndarray, ZS: np.ndarray):
     tiled = np.empty(sizes["tiled_bytes"], dtype=np.uint8)
     pairs = np.empty(sizes["tiled_pairs"], dtype=np.uint32)
     _check(lib.draft_head_tile(_ptr(packed), _ptr(S), _ptr(ZS), n, k, _ptr(tiled), _ptr(pairs)))
+    return tiled, pairs
+
+
+def draft_head_tile_int4(packed4: np.ndarray, S: np.ndarray, ZS: np.ndarray):
+    """A 4-bit head's canonical arrays -> the device form of its 2K-long 2-bit
+    form: (tiled codes uint8 [NBLK*64*K/2], pairs uint32 [NBLK*64*K/128], the
+    head's own pairs only)."""
+    lib = load_library()
+    packed4 = np.ascontiguousarray(packed4, dtype=np.uint8)
+    S = np.ascontiguousarray(S, dtype=np.uint16)
+    ZS = np.ascontiguousarray(ZS, dtype=np.uint16)
+    n, h = packed4.shape
+    k = 2 * h
+    if S.shape != (n, k // GROUP) or ZS.shape != S.shape:
+        raise ValueError("S and ZS must be [N][K/128]")
+    sizes = draft_head_sizes(n, 2 * k)
+    tiled = np.empty(sizes["tiled_bytes"], dtype=np.uint8)
+    pairs = np.empty(sizes["tiled_pairs"] // 2, dtype=np.uint32)
+    _check(lib.draft_head_tile_int4(_ptr(packed4), _ptr(S), _ptr(ZS), n, k, _ptr(tiled), _ptr(pairs)))
     return tiled, pairs
 
 
@@ -468,7 +489,7 @@ class DraftHead:
         """w: the bf16 rows the rerank reads, or e4m3 rows (uint8) with their
         per-row fp32 scale `wscale` (a per-channel FP8 head), or NVFP4 rows
         (uint8) with their block scales `bscale` and global scale `gscale`.
-        bits = 4: tiled and pairs hold a 4-bit head in its 2K-long 2-bit form."""
+        bits = 4: tiled and pairs hold a 4-bit head (draft_head_tile_int4)."""
         self.tiled, self.pairs, self.w, self.wscale = tiled, pairs, w, wscale
         self.bscale, self.gscale = bscale, gscale
         self.N, self.K, self.kcand, self.R, self.bits = N, K, kcand, R, bits
@@ -482,7 +503,7 @@ class DraftHead:
         n, k = w_bits.shape
         if bits == 4:
             packed4 = packed if packed is not None else draft_head_quantize_pack_int4(w_bits)
-            tiled, pairs = draft_head_tile(*draft_head_int4_as_int2(*packed4))
+            tiled, pairs = draft_head_tile_int4(*packed4)
         else:
             if packed is None:
                 packed = draft_head_quantize_pack(w_bits)

@@ -32,6 +32,7 @@ using dh::kZpEntries;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
@@ -133,6 +134,7 @@ struct CoarseArgs {
   unsigned long long* hand;   // per-row hand-off words of the rerank; workgroup 0 zeroes hand[0..ncnt)
   int ncnt;
   int kx;          // row length of x: K, or K / 2 for a 4-bit head run at length K (x' = (x, x))
+  int half_pairs;  // pairs hold quarters 0 and 1 only (a 4-bit head's form, draft_head_tile_int4)
 };
 
 // The rerank's per-row hand-off words are only ever written with agent-scope
@@ -143,6 +145,16 @@ struct CoarseArgs {
 __device__ __forceinline__ void zero_counters(const CoarseArgs& A) {
   if (blockIdx.x == 0 && (int)threadIdx.x < A.ncnt)
     __hip_atomic_store(A.hand + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A 4-bit head's pairs in its 2K-long form (draft_head_tile_int4): for each
+// (column, byte group) the pairs of quarters 0 and 1 are stored, the head's
+// own (S, ZS); quarters 2 and 3 carry (S/4, S/4) of the same columns, formed
+// here (S/4 is exact in bf16, so the truncation drops only zero bits).
+__device__ __forceinline__ u32x4 expand_pairs(u32x2 p) {
+  const uint32_t s0 = __float_as_uint(__uint_as_float(p[0] << 16) * 0.25f) >> 16;
+  const uint32_t s1 = __float_as_uint(__uint_as_float(p[1] << 16) * 0.25f) >> 16;
+  return u32x4{p[0], p[1], s0 | (s0 << 16), s1 | (s1 << 16)};
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -492,7 +504,7 @@ constexpr int res_waves() { return res_waves_of(MP); }
 template <int MP>
 constexpr int res_min_waves() { return 4; }
 
-template <int MP>
+template <int MP, bool kHalf>
 __global__ __launch_bounds__(64 * res_waves<MP>()) __attribute__((amdgpu_waves_per_eu(res_min_waves<MP>())))
 void coarse_resident_kernel(CoarseArgs A) {
   constexpr int kResWaves = res_waves<MP>();
@@ -522,6 +534,7 @@ void coarse_resident_kernel(CoarseArgs A) {
   // A wave past the last block reads block 0 (valid memory) and writes nothing.
   const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512 + NT * part * 64;
   const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64 + NT * part * 16;
+  const u32x2* pp2 = reinterpret_cast<const u32x2*>(A.pairs) + (size_t)(blk_ok ? b : 0) * NG4 * 64 + NT * part * 16;
   // codes and scale pairs are read once per call: nontemporal loads keep them
   // from displacing x and the candidates in the caches
   auto load_codes = [&](int G, u32x4 (&raw)[2][NT], u32x4 (&sz)[NT]) {
@@ -530,7 +543,10 @@ void coarse_resident_kernel(CoarseArgs A) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) raw[h][t] = __builtin_nontemporal_load(tp + ((G * 2 + h) * 4 + t) * 64 + lane);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) sz[t] = __builtin_nontemporal_load(pp + (G * 4 + t) * 16 + nn);
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (kHalf) sz[t] = expand_pairs(__builtin_nontemporal_load(pp2 + (G * 4 + t) * 16 + nn));
+      else sz[t] = __builtin_nontemporal_load(pp + (G * 4 + t) * 16 + nn);
+    }
   };
 
   u32x4 rw[D][2][NT], sw[D][NT];   // ring: set (G mod D) holds byte group G
@@ -957,7 +973,7 @@ __device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MT][NTW], f32x4 (&acc)
 // One wave's share of a block: part P holds column tiles P NTW .. P NTW +
 // NTW - 1 of the block, all MT row tiles and the whole of K; then the
 // block's selection (from LDS when two waves share the block).
-template <int MT, int P>
+template <int MT, int P, bool kHalf>
 __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem) {
   using S = BigShape<MT>;
   constexpr int MP = 16 * MT, XD = S::XD, NBUF = XD + 1, W = S::W, WPB = S::WPB, CD = S::CD, BPW = S::BPW;
@@ -979,8 +995,11 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
 
   // A block past the last one streams block 0 (valid memory) and writes nothing.
   const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
-  const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64;
-  const uint32_t voff = lane * 16;
+  // pairs: 1 KB per byte group, or 512 B with half pairs (fetched by lanes
+  // 0-31 and again by lanes 32-63 into the chunk's second half, unread)
+  constexpr int PB = kHalf ? 32 : 64;
+  const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * PB;
+  const uint32_t voff = lane * 16, voff_p = (lane % PB) * 16;
   const uint32_t xs_l = lds_addr(xs), zs_l = lds_addr(zs);
   const uint32_t cs_l = lds_addr(cs + lb * kCodeChunks * 64);
 
@@ -1009,8 +1028,9 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
 #pragma unroll
       for (int k = 0; k < S::nc(P); ++k) {
         const int c = k;
-        dma16_nt(voff, c < 8 ? tp + (GC * 8 + c) * 64 : pp + GC * 64,
-              cs_l + cslot * BPW * kCodeChunks * 1024 + c * 1024);
+        const uint32_t dst = cs_l + cslot * BPW * kCodeChunks * 1024 + c * 1024;
+        if (c < 8) dma16_nt(voff, tp + (GC * 8 + c) * 64, dst);
+        else dma16_nt(voff_p, pp + GC * PB, dst);
       }
     }
   };
@@ -1046,7 +1066,10 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
 #pragma unroll
       for (int t = 0; t < NTW; ++t) raw[h][t] = cw[(h * 4 + T0 + t) * 64 + lane];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) sz[t] = cw[512 + (T0 + t) * 16 + nn];
+    for (int t = 0; t < NTW; ++t) {
+      if constexpr (kHalf) sz[t] = expand_pairs(reinterpret_cast<const u32x2*>(cw + 512)[(T0 + t) * 16 + nn]);
+      else sz[t] = cw[512 + (T0 + t) * 16 + nn];
+    }
 
     // zero-point part of byte group G
     {
@@ -1144,17 +1167,17 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   else big_select<MP, W, BPW>(sk, A, blockIdx.x * BPW, wave, hh, nn);
 }
 
-template <int MT>
+template <int MT, bool kHalf>
 __global__ __launch_bounds__(64 * BigShape<MT>::W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void coarse_mfma_kernel(BigArgs BA) {
   extern __shared__ __align__(16) unsigned char smem[];
   if constexpr (BigShape<MT>::WPB == 2) {
     if (threadIdx.x >= 64 * BigShape<MT>::BPW) {
-      big_wave<MT, 1>(BA, smem);
+      big_wave<MT, 1, kHalf>(BA, smem);
       return;
     }
   }
-  big_wave<MT, 0>(BA, smem);
+  big_wave<MT, 0, kHalf>(BA, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -2494,12 +2517,12 @@ size_t resident_lds_bytes(int K, int MP) {
   return groups * 16 * MP * 16 + groups * MP * sizeof(float) + blocks * MP * 64 * sizeof(float);
 }
 
-template <int MP>
-hipError_t launch_resident(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+template <int MP, bool kHalf>
+hipError_t launch_resident_k(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const size_t lds = resident_lds_bytes(A.kx, MP);
   static bool attr_set = false;   // the attribute only ever grows to kMaxLds
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&coarse_resident_kernel<MP>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&coarse_resident_kernel<MP, kHalf>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -2507,8 +2530,12 @@ hipError_t launch_resident(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hi
   constexpr int waves = res_waves<MP>();
   constexpr int blocks = waves * res_nt(MP) / 4;   // 4 / res_nt waves per 64-column block
   dim3 grid((A.nblk + blocks - 1) / blocks);
-  hipExtLaunchKernelGGL(coarse_resident_kernel<MP>, grid, dim3(64 * waves), lds, s, e0, e1, 0, A);
+  hipExtLaunchKernelGGL(coarse_resident_kernel<MP, kHalf>, grid, dim3(64 * waves), lds, s, e0, e1, 0, A);
   return hipGetLastError();
+}
+template <int MP>
+hipError_t launch_resident(const CoarseArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return A.half_pairs ? launch_resident_k<MP, true>(A, s, e0, e1) : launch_resident_k<MP, false>(A, s, e0, e1);
 }
 
 template <int MT>
@@ -2527,8 +2554,8 @@ hipError_t launch_h16(const HArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e
   return hipGetLastError();
 }
 
-template <int MT>
-hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+template <int MT, bool kHalf>
+hipError_t launch_big_k(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD, BigShape<MT>::CD, BigShape<MT>::BPW, BigShape<MT>::GPS);
   static_assert(lds <= kMaxLds, "LDS budget of the many-row kernel");
   static_assert((size_t)BigShape<MT>::BPW * 16 * MT * kScStride * sizeof(float) <= lds,
@@ -2536,14 +2563,18 @@ hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t
   static_assert(lds <= kMaxLds, "LDS of one workgroup");
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&coarse_mfma_kernel<MT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&coarse_mfma_kernel<MT, kHalf>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((A.c.nblk + BigShape<MT>::BPW - 1) / BigShape<MT>::BPW);
-  hipExtLaunchKernelGGL(coarse_mfma_kernel<MT>, grid, dim3(64 * BigShape<MT>::W), lds, s, e0, e1, 0, A);
+  hipExtLaunchKernelGGL(coarse_mfma_kernel<MT, kHalf>, grid, dim3(64 * BigShape<MT>::W), lds, s, e0, e1, 0, A);
   return hipGetLastError();
+}
+template <int MT>
+hipError_t launch_big(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return A.c.half_pairs ? launch_big_k<MT, true>(A, s, e0, e1) : launch_big_k<MT, false>(A, s, e0, e1);
 }
 
 // Rows the resident kernel is instantiated for (M padded up).  One row runs
@@ -2650,6 +2681,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
   CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
                reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out, row_out, topk_only,
                static_cast<unsigned long long*>(workspace), M, kx ? kx : K};
+  A.half_pairs = A.kx < A.K;   // a 4-bit head in its 2K-long form: draft_head_tile_int4's pairs
   hipError_t e = hipSuccess;
   const int ks = A.kx;   // the row length of x the resident kernel stages
   if (use_resident(M, ks)) {

@@ -71,6 +71,32 @@ int check_shape(int64_t N, int64_t K) {
   return DH_OK;
 }
 
+// The many-row kernels take each group's zero-point term as the one bf16
+// weight S - ZS against the group's x sum, and the fp16 one forms each weight
+// (S/4) v as an fp16 value, exact for |S| <= 255.  The page's quantiser meets
+// both: S = bf16(4 (hi - lo) / 3) (under 255 for a group range under about
+// 191) and ZS = bf16((4 + z) (hi - lo) / 3), z in 0..3, within a factor 1.75
+// of S, so that S - ZS has at most 8 significant bits.  (The 4-bit head's
+// pairs, scaled by 16 instead of 4, meet the same bounds at a quarter of the
+// range.)  NG: groups per row, for the message.
+int check_pairs(const uint16_t* S, const uint16_t* ZS, int64_t count, int64_t NG) {
+  for (int64_t i = 0; i < count; ++i) {
+    const float s = bf16_to_f32(S[i]), zs = bf16_to_f32(ZS[i]);
+    if (!(s >= -255.0f && s <= 255.0f))
+      return dh::fail(DH_EUNSUP, "tile: scale S[%lld][%lld] = %g is outside [-255, 255], the range the device "
+                      "kernels represent exactly", (long long)(i / NG), (long long)(i % NG), (double)s);
+    const float d = s - zs;
+    uint32_t db;
+    std::memcpy(&db, &d, 4);
+    if (!std::isfinite(zs) || (double)d != (double)s - (double)zs || (db & 0xFFFFu) != 0u)
+      return dh::fail(DH_EUNSUP, "tile: S - ZS at [%lld][%lld] (%g - %g) is not a bf16 value, the form the device "
+                      "kernels take the zero-point term in", (long long)(i / NG), (long long)(i % NG), (double)s,
+                      (double)zs);
+  }
+  return DH_OK;
+}
+
+
 template <class F>
 void parallel_rows(int64_t N, int nthreads, F&& body) {
   unsigned hw = std::thread::hardware_concurrency();
@@ -216,25 +242,8 @@ int draft_head_tile(const uint8_t* packed, const uint16_t* S, const uint16_t* ZS
   int rc = check_shape(N, K);
   if (rc) return rc;
   const int64_t Q = K / 4, NG4 = K / 512, NG = K / DH_GROUP;
-  // The many-row kernels take each group's zero-point term as the one bf16
-  // weight S - ZS against the group's x sum, and the fp16 one forms each
-  // weight (S/4) v as an fp16 value, exact for |S| <= 255.  The page's
-  // quantiser meets both: S = bf16(4 (hi - lo) / 3) (under 255 for a group
-  // range under about 191) and ZS = bf16((4 + z) (hi - lo) / 3), z in 0..3,
-  // within a factor 1.75 of S, so that S - ZS has at most 8 significant bits.
-  for (int64_t i = 0; i < N * NG; ++i) {
-    const float s = bf16_to_f32(S[i]), zs = bf16_to_f32(ZS[i]);
-    if (!(s >= -255.0f && s <= 255.0f))
-      return dh::fail(DH_EUNSUP, "tile: scale S[%lld][%lld] = %g is outside [-255, 255], the range the device "
-                      "kernels represent exactly", (long long)(i / NG), (long long)(i % NG), (double)s);
-    const float d = s - zs;
-    uint32_t db;
-    std::memcpy(&db, &d, 4);
-    if (!std::isfinite(zs) || (double)d != (double)s - (double)zs || (db & 0xFFFFu) != 0u)
-      return dh::fail(DH_EUNSUP, "tile: S - ZS at [%lld][%lld] (%g - %g) is not a bf16 value, the form the device "
-                      "kernels take the zero-point term in", (long long)(i / NG), (long long)(i % NG), (double)s,
-                      (double)zs);
-  }
+  rc = check_pairs(S, ZS, N * NG, NG);
+  if (rc) return rc;
   const int64_t nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
   parallel_rows(nblk, 0, [&](int64_t a, int64_t bend) {
     for (int64_t b = a; b < bend; ++b) {
@@ -253,6 +262,45 @@ int draft_head_tile(const uint8_t* packed, const uint16_t* S, const uint16_t* ZS
           pairs[off] = valid ? (static_cast<uint32_t>(S[n * NG + g]) |
                                 (static_cast<uint32_t>(ZS[n * NG + g]) << 16))
                              : 0u;
+        }
+      }
+    }
+  });
+  return dh::ok();
+}
+
+int draft_head_tile_int4(const uint8_t* packed4, const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K,
+                         uint8_t* tiled, uint32_t* pairs) {
+  if (!packed4 || !S || !ZS || !tiled || !pairs) return dh::fail(DH_EINVAL, "tile_int4: null pointer");
+  int rc = check_shape4(N, K);
+  if (rc) return rc;
+  const int64_t H = K / 2, NG = K / DH_GROUP, NG4 = K / 256;   // NG4: byte groups of the 2K-long form
+  rc = check_pairs(S, ZS, N * NG, NG);
+  if (rc) return rc;
+  const int64_t nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
+  parallel_rows(nblk, 0, [&](int64_t a, int64_t bend) {
+    for (int64_t b = a; b < bend; ++b) {
+      for (int64_t col = 0; col < DH_BLOCK_N; ++col) {
+        const int64_t n = b * DH_BLOCK_N + col;
+        const bool valid = n < N;
+        const int64_t t = col / 16, c = col % 16;
+        // the bytes of the 2K-long form (draft_head_int4_as_int2's shuffle),
+        // placed as draft_head_tile places a 2-bit head of length 2K
+        for (int64_t j = 0; j < H; ++j) {
+          uint8_t v = 0;
+          if (valid) {
+            const uint32_t b4 = packed4[n * H + j], lo = b4 & 15u, hi = b4 >> 4;
+            v = static_cast<uint8_t>((lo >> 2) | ((hi >> 2) << 2) | ((lo & 3u) << 4) | ((hi & 3u) << 6));
+          }
+          const int64_t G = j / 128, h = (j % 128) / 64, s = (j % 64) / 16, wb = j % 16;
+          tiled[((((b * NG4 + G) * 2 + h) * 4 + t) * 64 + s * 16 + c) * 16 + wb] = v;
+        }
+        // pairs of quarters 0 and 1 of each byte group (the head's own groups);
+        // quarters 2 and 3 carry (S/4, S/4), which the kernels derive
+        for (int64_t g = 0; g < NG; ++g) {
+          const int64_t q = g / NG4, G = g % NG4;
+          pairs[((b * NG4 + G) * 4 + t) * 32 + c * 2 + q] =
+              valid ? (static_cast<uint32_t>(S[n * NG + g]) | (static_cast<uint32_t>(ZS[n * NG + g]) << 16)) : 0u;
         }
       }
     }

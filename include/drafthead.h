@@ -145,6 +145,22 @@ int draft_head_int4_as_int2(const uint8_t* packed4, const uint16_t* S, const uin
                             uint8_t* packed2, uint16_t* S2, uint16_t* ZS2);
 
 /*
+ * HOST.  The device form of a 4-bit head, which draft_head_coarse_int4 and
+ * draft_head_forward_int4 take: tiled holds exactly the codes of
+ * draft_head_tile(draft_head_int4_as_int2(...), N, 2K) (NBLK*64 * K/2 bytes);
+ * pairs holds only the head's own (S, ZS), NBLK*64 * K/128 entries (half of
+ * that form's), laid out as quarters 0 and 1 of each 2K-form byte group:
+ *   pairs[((b*NG4 + G)*4 + t)*32 + c*2 + q] = S | ZS << 16 of column
+ *   64b + 16t + c, group q*NG4 + G   (NG4 = K/256, q = 0, 1)
+ * The kernels form the pairs of quarters 2 and 3, (S/4, S/4), themselves, so
+ * a call streams N*K/2 code bytes and N*K/128 pairs, the 4-bit head's size.
+ *   packed4, S, ZS  draft_head_quantize_pack_int4's arrays;  tiled, pairs  out
+ * Limits and errors: as draft_head_quantize_pack_int4 and draft_head_tile.
+ */
+int draft_head_tile_int4(const uint8_t* packed4, const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K,
+                         uint8_t* tiled, uint32_t* pairs);
+
+/*
  * Bytes of device workspace draft_head_coarse / draft_head_forward need for M
  * rows of length K: 1,024 bytes of per-row hand-off words for the one-call
  * path's rerank (a row's exact logits may be split over several workgroups),
@@ -321,8 +337,8 @@ int draft_head_forward_nvfp4(const void* x, int M, int K, int N, const uint8_t* 
 /*
  * DEVICE.  draft_head_coarse and draft_head_forward for a 4-bit head (the
  * page's BITS = 4 configuration, KCAND = 1 in its measurements): tiled and
- * pairs are draft_head_tile(draft_head_int4_as_int2(...), N, 2K), the 2-bit
- * form of length 2K, which the coarse kernels run with x read twice over
+ * pairs are draft_head_tile_int4's, the 2-bit form of length 2K with the
+ * head's own pairs, which the coarse kernels run with x read twice over
  * (x' = (x, x)); x, w and everything else are as for the 2-bit calls with K
  * the head's own length.  The workspace is draft_head_workspace_bytes(M, 2K).
  * Limits: K a positive multiple of 256 with 2K <= DH_MAX_K.

@@ -29,7 +29,8 @@ def test_library_exports_every_header_symbol(lib):
                           "draft_head_stream_read", "draft_head_logits_row", "draft_head_rerank_e4m3",
                           "draft_head_forward_e4m3", "draft_head_rerank_nvfp4", "draft_head_forward_nvfp4",
                           "draft_head_quantize_pack_int4",
-                          "draft_head_int4_as_int2", "draft_head_coarse_int4", "draft_head_forward_int4",
+                          "draft_head_int4_as_int2", "draft_head_tile_int4", "draft_head_coarse_int4",
+                          "draft_head_forward_int4",
                           "draft_head_forward_noalloc", "draft_head_forward_row"}
     for name in names:
         assert hasattr(lib, name), name
@@ -354,6 +355,28 @@ def test_int4_as_int2_is_the_same_head():
     assert np.array_equal(w2[:, :k] + w2[:, k:], oracle.effective_weight_int4(packed4, S, ZS))
 
 
+@pytest.mark.parametrize("n,k", [(64, 256), (100, 768), (129, 1536)])
+def test_tile_int4_is_the_2k_form_with_its_own_pairs(lib, n, k):
+    """draft_head_tile_int4's codes are those of the tiled 2K-long form, and
+    its pairs are that form's quarters 0 and 1 (quarters 2 and 3 of each byte
+    group hold (S/4, S/4), which the kernels derive): N K/2 code bytes and
+    N K/128 pairs, the 4-bit head's own size."""
+    rng = np.random.default_rng(n + k)
+    w = oracle.bf16.from_f32((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    packed4 = B.draft_head_quantize_pack_int4(w)
+    tiled4, pairs4 = B.draft_head_tile_int4(*packed4)
+    tiled2, pairs2 = B.draft_head_tile(*B.draft_head_int4_as_int2(*packed4))
+    assert np.array_equal(tiled4, tiled2)
+    nblk = (n + 63) // 64
+    assert pairs4.size == nblk * 64 * (k // 128) and pairs2.size == 2 * pairs4.size
+    full = pairs2.reshape(nblk, k // 256, 4, 16, 4)      # [block][byte group][t][c][quarter]
+    half = pairs4.reshape(nblk, k // 256, 4, 16, 2)
+    assert np.array_equal(half, full[..., :2])
+    s = full[..., :2] & 0xFFFF                            # what the kernels derive for quarters 2 and 3
+    s4 = oracle.bf16.from_f32(oracle.bf16.to_f32(s.astype(np.uint16)) * np.float32(0.25)).astype(np.uint32)
+    assert np.array_equal(full[..., 2:], s4 | (s4 << 16))
+
+
 def test_int4_validation(lib):
     p = np.zeros(4096, np.uint8).ctypes.data
     _err(lib, lib.draft_head_quantize_pack_int4(None, 4, 256, 256, p, p, p, 0), B.DH_EINVAL)
@@ -362,6 +385,8 @@ def test_int4_validation(lib):
     _err(lib, lib.draft_head_quantize_pack_int4(p, 4, 65536, 65536, p, p, p, 0), B.DH_ESHAPE)
     _err(lib, lib.draft_head_int4_as_int2(p, p, None, 4, 256, p, p, p), B.DH_EINVAL)
     _err(lib, lib.draft_head_int4_as_int2(p, p, p, 0, 256, p, p, p), B.DH_ESHAPE)
+    _err(lib, lib.draft_head_tile_int4(p, p, None, 4, 256, p, p), B.DH_EINVAL)
+    _err(lib, lib.draft_head_tile_int4(p, p, p, 4, 384, p, p), B.DH_ESHAPE)
 
 
 def test_int4_device_validation(lib):
