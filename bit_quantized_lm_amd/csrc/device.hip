@@ -1479,26 +1479,29 @@ void coarse_h16_kernel(HArgs HA) {
   }
   // Every wave's DMA writes have landed and every wave is done with the ring:
   // the LDS takes the keys of the workgroup's 8 blocks, row rho = lb MP + m
-  // (block lb, row m) in 64 words whose 16-byte pieces are XOR-swizzled by rho
-  // mod 16 (piece c at c ^ (rho & 15): conflict-free for the writes below and
-  // for sixteen consecutive rows read piece by piece).  Then thread q selects
-  // the lists q and q + 512 (list l: block l / M, row l % M).
+  // (block lb, row m) in 16 pieces of 16 bytes, piece g holding columns g,
+  // g + 16, g + 32, g + 48 (one lane's four keys of the row: one 16-byte
+  // write) at position g ^ (rho mod 16), so that the sixteen lanes of a
+  // write, and sixteen consecutive rows read piece by piece, meet every bank
+  // once.  Then thread q selects the lists q and q + 512 (list l: block
+  // l / M, row l % M).
   u32x4* sk = reinterpret_cast<u32x4*>(smem);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int col = 16 * t + nn, n = 64 * b + col;
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * i + 4 * hh + r, rho = wave * MP + row;
+      uint32_t kk[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * i + 4 * hh + r, rho = wave * MP + row;
+      for (int t = 0; t < 4; ++t) {
+        const int n = 64 * b + 16 * t + nn;
         const bool ok = blk_ok && n < A.N && row < A.M;
         const float sv = acc[i][t][r] * rs[i][r];
-        reinterpret_cast<uint32_t*>(sk + rho * 16 + ((col >> 2) ^ (row & 15)))[col & 3] =
-            ok ? f32_key(sv + 0.0f) : 0u;   // -0 as +0
+        kk[t] = ok ? f32_key(sv + 0.0f) : 0u;   // -0 as +0
         if (ok) store_scores(A, row, n, sv);
       }
+      sk[rho * 16 + (nn ^ (row & 15))] = u32x4{kk[0], kk[1], kk[2], kk[3]};
     }
   __syncthreads();
   for (int l = threadIdx.x; l < kHBlocks * A.M; l += 64 * kHBlocks) {
@@ -1508,12 +1511,13 @@ void coarse_h16_kernel(HArgs HA) {
     const int sw = m & 15;
     uint32_t key[64];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const u32x4 v = row[c ^ sw];
+    for (int g = 0; g < 16; ++g) {
+      const u32x4 v = row[g ^ sw];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) key[4 * c + e] = v[e];
+      for (int t = 0; t < 4; ++t) key[16 * t + g] = v[t];
     }
-    emit_list8(key, [&](int c) { return reinterpret_cast<const uint32_t*>(row + ((c >> 2) ^ sw))[c & 3]; }, A, m, bq);
+    emit_list8(key, [&](int c) { return reinterpret_cast<const uint32_t*>(row + ((c & 15) ^ sw))[c >> 4]; }, A, m,
+               bq);
   }
 }
 
