@@ -59,11 +59,13 @@ WEIGHT_BYTES = N * (K // 4) + 2 * 2 * N * (K // 128)       # 178,790,400
 
 
 def coarse_kernel_name(m: int) -> str:
-    """The coarse kernel one launch at M rows runs (K = 5120; one row runs the
-    two-row instance)."""
+    """The coarse kernel one launch at M rows runs (K = 5120 and the 2-bit
+    head; one row runs the two-row instance; from three row tiles on, the
+    fp16 many-row kernel)."""
     if m <= 8:
-        return f"coarse_resident_kernel<{2 if m <= 2 else 4 if m <= 4 else 8}>"
-    return f"coarse_mfma_kernel<{min((m + 15) // 16, 5)}>"
+        return f"coarse_resident_kernel<{2 if m <= 2 else 4 if m <= 4 else 8}, false>"
+    mt = min((m + 15) // 16, 5)
+    return f"coarse_h16_kernel<{mt}>" if mt >= 3 else f"coarse_mfma_kernel<{mt}, false>"
 
 
 def coarse_alg_bytes(m: int) -> int:
