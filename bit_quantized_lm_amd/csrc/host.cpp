@@ -4,6 +4,7 @@
 // Built with -ffp-contract=off: the quantiser must round every float32
 // operation on its own, as the separate torch element-wise operations of
 // `_quantize_head_now` on the radiance_drafthead.py page do.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -116,37 +117,50 @@ void parallel_rows(int64_t N, int nthreads, F&& body) {
   for (auto& th : pool) th.join();
 }
 
-// One row: codes into `codes` (K bytes), scale pair into S/ZS (K/128 each).
-// levels / premul: 3 / 4 for the 2-bit head, 15 / 16 for the 4-bit one.
+// The quantiser's arithmetic, one float32 operation at a time (this file is
+// built without contraction, so no multiply-add is fused): that order is what
+// makes the stored bytes equal, bit for bit, to what the page's quantiser
+// (float32 tensor operations, round half to even) writes.
+struct Grid {
+  float step, zero;   // the group's grid: level i sits at (i - zero) * step
+};
+
+// An asymmetric grid of levels + 1 points over [lo, hi]: the step (at least
+// the floor that keeps a constant group finite) and the level nearest zero.
+Grid group_grid(float lo, float hi, float levels) {
+  float step = (hi - lo) / levels;
+  if (step < 1e-8f) step = 1e-8f;
+  float zero = std::nearbyint(-lo / step);   // the default rounding mode: to nearest, ties to even
+  zero = std::min(std::max(zero, 0.0f), levels);
+  return {step, zero};
+}
+
+// A weight's code: its position on the grid, rounded to the nearest level.
+uint8_t grid_code(float w, const Grid& g, float levels) {
+  float pos = w / g.step;
+  pos = pos + g.zero;
+  return static_cast<uint8_t>(std::min(std::max(std::nearbyint(pos), 0.0f), levels));
+}
+
+// One row of K weights: its codes (K bytes) and its groups' stored pairs,
+// S = bf16(premul step) and ZS = bf16(premul step + zero step): the decode's
+// bias 1 + v/premul folded in (premul = 4 at two bits, 16 at four).
 void quantize_row(const uint16_t* w, int64_t K, uint8_t* codes, uint16_t* S, uint16_t* ZS, float levels = 3.0f,
                   float premul = 4.0f) {
-  const float three = levels, four = premul, floor_sc = 1e-8f;
   for (int64_t g = 0; g < K / DH_GROUP; ++g) {
     const uint16_t* wg = w + g * DH_GROUP;
     float lo = bf16_to_f32(wg[0]), hi = lo;
     for (int i = 1; i < DH_GROUP; ++i) {
-      float v = bf16_to_f32(wg[i]);
-      lo = v < lo ? v : lo;
-      hi = v > hi ? v : hi;
+      const float v = bf16_to_f32(wg[i]);
+      lo = std::min(lo, v);
+      hi = std::max(hi, v);
     }
-    float range = hi - lo;
-    float sc = range / three;
-    if (sc < floor_sc) sc = floor_sc;
-    float neg_lo = -lo;
-    float zp = std::nearbyint(neg_lo / sc);  // default rounding mode: to nearest even
-    zp = zp < 0.0f ? 0.0f : (zp > three ? three : zp);
-    for (int i = 0; i < DH_GROUP; ++i) {
-      float t = bf16_to_f32(wg[i]) / sc;
-      t = t + zp;
-      float q = std::nearbyint(t);
-      q = q < 0.0f ? 0.0f : (q > three ? three : q);
-      codes[g * DH_GROUP + i] = static_cast<uint8_t>(q);
-    }
-    float s4 = four * sc;
-    float zpsc = zp * sc;
-    float zs4 = s4 + zpsc;
-    S[g] = f32_to_bf16(s4);
-    ZS[g] = f32_to_bf16(zs4);
+    const Grid grid = group_grid(lo, hi, levels);
+    for (int i = 0; i < DH_GROUP; ++i) codes[g * DH_GROUP + i] = grid_code(bf16_to_f32(wg[i]), grid, levels);
+    const float s_f32 = premul * grid.step;
+    const float zs_f32 = s_f32 + grid.zero * grid.step;
+    S[g] = f32_to_bf16(s_f32);
+    ZS[g] = f32_to_bf16(zs_f32);
   }
 }
 

@@ -72,15 +72,17 @@ int draft_head_sizes(int64_t N, int64_t K, size_t* packed_bytes, size_t* scale_e
                      size_t* tiled_bytes, size_t* tiled_pairs);
 
 /*
- * HOST.  Quantise a bf16 weight to asymmetric min/max int2 and pack it.
- * Follows `_quantize_head_now` on the radiance_drafthead.py page: per (row n,
- * group g of 128 consecutive k), in float32 with every operation rounded on
- * its own (no fused multiply-add):
- *   lo, hi = min, max of the group;  sc = max((hi - lo) / 3, 1e-8)
- *   zp = clamp(rne(-lo / sc), 0, 3);  q = clamp(rne(w / sc + zp), 0, 3)
- *   S = bf16(4 sc);  ZS = bf16(4 sc + zp sc)    (round to nearest even)
- * and the quarter-split packing of the module docstring: byte j of a row holds
- * the codes of k = j, K/4+j, K/2+j, 3K/4+j in bits 0-1, 2-3, 4-5, 6-7.
+ * HOST.  Quantise a bf16 weight to asymmetric min/max int2 and pack it, as
+ * the radiance_drafthead.py page's load-time quantiser does: each group of
+ * 128 consecutive k of a row gets a grid of four levels spanning the group's
+ * range, with step max((hi - lo)/3, 1e-8) and zero level -lo/step rounded to
+ * nearest even and clamped to 0..3; a weight's code is w/step + zero rounded
+ * to nearest even and clamped; the group stores S = bf16(4 step) and
+ * ZS = bf16(4 step + zero step).  Every step is one float32 operation rounded
+ * on its own, as the page's tensor operations are, so the bytes match its
+ * quantiser exactly.  Packing (the module docstring's "Quarter-split
+ * packing"): byte j of a row holds the codes of k = j, K/4+j, K/2+j, 3K/4+j in
+ * bits 0-1, 2-3, 4-5, 6-7.
  *   w        bf16 bits, row-major [N][ldw], ldw >= K (read only)
  *   packed   out, uint8 [N][K/4]
  *   S, ZS    out, bf16 bits [N][K/128] each

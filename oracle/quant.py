@@ -1,69 +1,80 @@
 """Quantiser, packing and the effective weight (oracle).
 
-Follows the quantiser `_quantize_head_now` on the radiance_drafthead.py page
-(asymmetric min/max at 2 bits, group 128 along K, quarter-split packing,
-premultiplied bf16 scale pair) and the module docstring's description of the
-packing ("Quarter-split packing") and of the collapse of the 1.0 bias
-("Bit-pattern dequant, hoisted").
+What the radiance_drafthead.py page quantises (its load-time quantiser and
+the module docstring's "Quarter-split packing" and "Bit-pattern dequant,
+hoisted" paragraphs): every group of 128 consecutive k of a head row gets an
+asymmetric grid of 2^BITS levels spanning the group's range; each weight
+becomes the index of its nearest grid level; the grid is stored as one bf16
+pair premultiplied by the decode's bias (S = 4 step, ZS = S + zero * step at
+two bits), and the codes are packed four to a byte in quarter-split order.
 
-Arithmetic precision: the page runs the quantiser as separate torch float32
-element-wise operations, so every operation here is a separate float32
-operation (numpy evaluates each one on its own and rounds it; there is no
-fused multiply-add).  Reading: `torch.round` rounds half to even, and numpy's
-`np.round` does the same.
+Precision: the page computes the grid and the codes with separate float32
+tensor operations, so this oracle does the same, one float32 operation at a
+time (numpy rounds each on its own; no fused multiply-add), and rounds half
+to even where the page rounds (torch's rounding; the hand-derived worked
+example in the tests tells the two rules apart).  Only that operation order
+is kept from the page: it is what makes the stored bytes reproducible bit
+for bit.
 """
 import numpy as np
 
 from . import bf16
 
-GROUP = 128          # quantisation group along K (module constant GROUP)
+GROUP = 128          # quantisation group along K
 BITS = 2
 LEVELS = (1 << BITS) - 1   # highest code, 3
-PREMUL = 4.0         # bf16 1 + v/4 bias: the stored scales are premultiplied by 4
-CHUNK_ROWS = 8192
+PREMUL = 4.0         # the decode's bias 1 + v/4: the stored pair carries 4 x the grid step
+STEP_FLOOR = 1e-8    # smallest grid step (a constant group)
+GROUPS_PER_PASS = 1 << 17   # groups quantised per numpy pass (bounds the temporaries only)
 
 
-def quantize(w_bits):
-    """Per (row n, group g of 128 consecutive k): min/max asymmetric int2.
+def _grid(lo, hi, levels):
+    """The group's grid in float32: step = max((hi - lo) / levels, floor) and
+    the zero level, -lo / step rounded to nearest even and clamped to the
+    codes."""
+    step = np.maximum((hi - lo) / np.float32(levels), np.float32(STEP_FLOOR))
+    zero = np.clip(np.round(-lo / step), np.float32(0), np.float32(levels))
+    return step, zero
 
-    Steps, as in `_quantize_head_now` (row chunk loop body):
-      lo, hi = min and max of the group (float32)
-      sc = max((hi - lo) / 3, 1e-8)
-      zp = clamp(round(-lo / sc), 0, 3)
-      q  = clamp(round(w / sc + zp), 0, 3)
-      S  = bf16(4 * sc)
-      ZS = bf16(4 * sc + zp * sc)
-    Returns (codes uint8 [N][K], S bits uint16 [N][K/128], ZS bits uint16 [N][K/128]).
-    """
+
+def _encode(w, step, zero, levels):
+    """Codes of the weights w [groups][128] on their grids: w / step + zero,
+    rounded to nearest even, clamped (two float32 operations, then the round)."""
+    pos = w / step[:, None]
+    pos = pos + zero[:, None]
+    return np.clip(np.round(pos), np.float32(0), np.float32(levels)).astype(np.uint8)
+
+
+def _stored_pair(step, zero, premul):
+    """The pair the head stores: S = bf16(premul * step), ZS = bf16(S' +
+    zero * step) with S' the float32 premul * step."""
+    s_f32 = np.float32(premul) * step
+    return bf16.from_f32(s_f32), bf16.from_f32(s_f32 + zero * step)
+
+
+def _quantize_groups(w_bits, levels, premul):
+    """Codes [N][K] and pairs [N][K/128] of a head, all groups at once."""
     w_bits = np.asarray(w_bits, dtype=np.uint16)
     n, k = w_bits.shape
     if k % GROUP:
         raise ValueError("K must be a multiple of the group size 128")
-    codes = np.empty((n, k), dtype=np.uint8)
-    S = np.empty((n, k // GROUP), dtype=np.uint16)
-    ZS = np.empty((n, k // GROUP), dtype=np.uint16)
-    for i in range(0, n, CHUNK_ROWS):       # row chunks bound memory only
-        j = min(i + CHUNK_ROWS, n)
-        codes[i:j], S[i:j], ZS[i:j] = _quantize_rows(w_bits[i:j])
-    return codes, S, ZS
+    flat = w_bits.reshape(-1, GROUP)          # one group per row, in (n, g) order
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    S = np.empty(flat.shape[0], dtype=np.uint16)
+    ZS = np.empty(flat.shape[0], dtype=np.uint16)
+    for a in range(0, flat.shape[0], GROUPS_PER_PASS):
+        b = min(a + GROUPS_PER_PASS, flat.shape[0])
+        w = bf16.to_f32(flat[a:b])
+        step, zero = _grid(w.min(axis=1), w.max(axis=1), levels)
+        codes[a:b] = _encode(w, step, zero, levels)
+        S[a:b], ZS[a:b] = _stored_pair(step, zero, premul)
+    return codes.reshape(n, k), S.reshape(n, k // GROUP), ZS.reshape(n, k // GROUP)
 
 
-def _quantize_rows(w_bits, levels=LEVELS, premul=PREMUL):
-    n, k = w_bits.shape
-    wf = bf16.to_f32(w_bits).reshape(n, k // GROUP, GROUP)
-    lo = wf.min(axis=2)
-    hi = wf.max(axis=2)
-    sc = (hi - lo) / np.float32(levels)
-    sc = np.maximum(sc, np.float32(1e-8))
-    zp = np.clip(np.round(-lo / sc), np.float32(0), np.float32(levels))
-    t = wf / sc[:, :, None]
-    t = t + zp[:, :, None]
-    q = np.clip(np.round(t), np.float32(0), np.float32(levels)).astype(np.uint8)
-    s4 = np.float32(premul) * sc
-    zpsc = zp * sc
-    S = bf16.from_f32(s4)
-    ZS = bf16.from_f32(s4 + zpsc)
-    return q.reshape(n, k), S, ZS
+def quantize(w_bits):
+    """The 2-bit head: codes uint8 [N][K] (0..3), S and ZS bf16 bits
+    uint16 [N][K/128]; the weight of code v is (S/4) v - (ZS - S)."""
+    return _quantize_groups(w_bits, LEVELS, PREMUL)
 
 
 # ------------------------------------------------------------------ 4 bits
@@ -72,24 +83,10 @@ PREMUL4 = 16.0       # bf16 1 + v/16 bias: the 4-bit scales are premultiplied by
 
 
 def quantize_int4(w_bits):
-    """The page's quantiser at BITS = 4 (`_quantize_head_now` with lv = 15 and
-    the bias 16): per (row n, group g of 128 consecutive k)
-      sc = max((hi - lo) / 15, 1e-8);  zp = clamp(round(-lo / sc), 0, 15)
-      q  = clamp(round(w / sc + zp), 0, 15)
-      S  = bf16(16 * sc);  ZS = bf16(16 * sc + zp * sc)
-    each a separate float32 operation.  Returns (codes, S bits, ZS bits).
-    """
-    w_bits = np.asarray(w_bits, dtype=np.uint16)
-    n, k = w_bits.shape
-    if k % GROUP:
-        raise ValueError("K must be a multiple of the group size 128")
-    codes = np.empty((n, k), dtype=np.uint8)
-    S = np.empty((n, k // GROUP), dtype=np.uint16)
-    ZS = np.empty((n, k // GROUP), dtype=np.uint16)
-    for i in range(0, n, CHUNK_ROWS):
-        j = min(i + CHUNK_ROWS, n)
-        codes[i:j], S[i:j], ZS[i:j] = _quantize_rows(w_bits[i:j], LEVELS4, PREMUL4)
-    return codes, S, ZS
+    """The 4-bit head (the page's BITS = 4 configuration): the same grid with
+    16 levels and the stored pair premultiplied by 16 (the bias 1 + v/16), so
+    the weight of code v is (S/16) v - (ZS - S).  Returns (codes, S, ZS)."""
+    return _quantize_groups(w_bits, LEVELS4, PREMUL4)
 
 
 def pack_half_split(codes):

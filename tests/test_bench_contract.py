@@ -33,9 +33,11 @@ def test_algorithmic_bytes():
 
 def test_coarse_kernel_names():
     b = _bench()
-    assert b.coarse_kernel_name(1) == "coarse_resident_kernel<2>"
-    assert b.coarse_kernel_name(2) == "coarse_resident_kernel<2>"
-    assert b.coarse_kernel_name(3) == "coarse_resident_kernel<4>"
-    assert b.coarse_kernel_name(8) == "coarse_resident_kernel<8>"
-    assert b.coarse_kernel_name(16) == "coarse_mfma_kernel<1>"
-    assert b.coarse_kernel_name(72) == "coarse_mfma_kernel<5>"
+    assert b.coarse_kernel_name(1) == "coarse_resident_kernel<2, false>"
+    assert b.coarse_kernel_name(2) == "coarse_resident_kernel<2, false>"
+    assert b.coarse_kernel_name(3) == "coarse_resident_kernel<4, false>"
+    assert b.coarse_kernel_name(8) == "coarse_resident_kernel<8, false>"
+    assert b.coarse_kernel_name(16) == "coarse_mfma_kernel<1, false>"
+    assert b.coarse_kernel_name(32) == "coarse_mfma_kernel<2, false>"
+    assert b.coarse_kernel_name(33) == "coarse_h16_kernel<3>"
+    assert b.coarse_kernel_name(72) == "coarse_h16_kernel<5>"
