@@ -166,6 +166,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // page hands to its caller (`_draft_head_int2`'s store of Y: the coarse score
 // rounded to bf16, or -inf everywhere for a top-k caller), into which the
 // rerank then writes the exact values.
+// Whether the call wants the optional full outputs (uniform).  The epilogues
+// test it once and store in a loop of their own, so that the common case runs
+// no per-score branch.
+__device__ __forceinline__ bool wants_scores(const CoarseArgs& A) { return A.coarse_out || A.row_out; }
 __device__ __forceinline__ void store_scores(const CoarseArgs& A, int m, int n, float sv) {
   if (A.coarse_out) A.coarse_out[(size_t)m * A.N + n] = sv;
   if (A.row_out) A.row_out[(size_t)m * A.N + n] = (uint16_t)(A.topk_only ? 0xFF80u : f32_to_bf16_rne(sv));
@@ -282,6 +286,9 @@ __device__ __forceinline__ uint32_t f32_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// f32_key(f) where ok, else 0, computed without a branch (a guarded key
+// makes the compiler wrap each one in a masked region of its own).
+__device__ __forceinline__ uint32_t f32_key_if(bool ok, float f) { return f32_key(f + 0.0f) & (0u - (uint32_t)ok); }
 __device__ __forceinline__ float key_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
@@ -393,10 +400,20 @@ __device__ __forceinline__ void block_select(Value value, const CoarseArgs& A, i
       for (int t = 0; t < 4; ++t) {
         const int n = b * 64 + 16 * t + nn;
         const bool ok = row_ok && n < A.N;
-        const float sv = pi < NP ? value(i, r, t) : 0.f;
-        k[j][t] = ok ? f32_key(sv + 0.0f) : 0u;   // -0 counts as +0, as in a float compare
+        k[j][t] = f32_key_if(ok, pi < NP ? value(i, r, t) : 0.f);   // -0 counts as +0, as in a float compare
         c[j][t] = 16 * t + nn;
-        if (ok) store_scores(A, m, n, sv);
+      }
+    }
+    if (wants_scores(A)) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int pi = p0 + j, i = pi / MR, r = pi % MR;
+        const int m = m0 + 16 * i + 4 * hh + r;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int n = b * 64 + 16 * t + nn;
+          if (live[j] && m < A.M && n < A.N) store_scores(A, m, n, value(i, r, t));
+        }
       }
     }
     bool any = false;
@@ -436,11 +453,19 @@ __device__ __forceinline__ void res_select(const float* sc, const CoarseArgs& A,
     for (int t = 0; t < 4; ++t) {
       const int n = (b0 + lbq[j]) * 64 + 16 * t + nn;
       const bool ok = live[j] && n < A.N;
-      const float sv = ok ? sc[(lbq[j] * MP + mq[j]) * 64 + 16 * t + nn] : 0.f;
-      k[j][t] = ok ? f32_key(sv + 0.0f) : 0u;   // -0 counts as +0, as in a float compare
+      const int li = live[j] ? lbq[j] * MP + mq[j] : 0;   // a row in the score area either way
+      k[j][t] = f32_key_if(ok, sc[li * 64 + 16 * t + nn]);   // -0 counts as +0, as in a float compare
       c[j][t] = 16 * t + nn;
-      if (ok) store_scores(A, mq[j], n, sv);
     }
+  }
+  if (wants_scores(A)) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int n = (b0 + lbq[j]) * 64 + 16 * t + nn;
+        if (live[j] && n < A.N) store_scores(A, mq[j], n, sc[(lbq[j] * MP + mq[j]) * 64 + 16 * t + nn]);
+      }
   }
   row16_select<NB>(k, c, A.kcand, nn, kk, kc);
 #pragma unroll
@@ -1158,9 +1183,21 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * i + 4 * hh + r;
-        sk[(lb * MP + row) * kScStride + col] = n_ok ? f32_key(acc[i][t][r] + 0.0f) : 0u;   // -0 as +0
-        if (n_ok && row < A.M) store_scores(A, row, n, acc[i][t][r]);
+        sk[(lb * MP + row) * kScStride + col] = f32_key_if(n_ok, acc[i][t][r]);   // -0 as +0
       }
+  }
+  if (wants_scores(A)) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const int n = 64 * b + 16 * (T0 + t) + nn;
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * i + 4 * hh + r;
+          if (blk_ok && n < A.N && row < A.M) store_scores(A, row, n, acc[i][t][r]);
+        }
+    }
   }
   __syncthreads();
   if (A.kcand <= 8) lane_select8<MP, BPW>(sk, A, blockIdx.x * BPW, wave, W, lane);
@@ -1496,13 +1533,21 @@ void coarse_h16_kernel(HArgs HA) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int n = 64 * b + 16 * t + nn;
-        const bool ok = blk_ok && n < A.N && row < A.M;
-        const float sv = acc[i][t][r] * rs[i][r];
-        kk[t] = ok ? f32_key(sv + 0.0f) : 0u;   // -0 as +0
-        if (ok) store_scores(A, row, n, sv);
+        kk[t] = f32_key_if(blk_ok && n < A.N && row < A.M, acc[i][t][r] * rs[i][r]);   // -0 as +0
       }
       sk[rho * 16 + (nn ^ (row & 15))] = u32x4{kk[0], kk[1], kk[2], kk[3]};
     }
+  if (wants_scores(A)) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int row = 16 * i + 4 * hh + r, n = 64 * b + 16 * t + nn;
+          if (blk_ok && n < A.N && row < A.M) store_scores(A, row, n, acc[i][t][r] * rs[i][r]);
+        }
+  }
   __syncthreads();
   for (int l = threadIdx.x; l < kHBlocks * A.M; l += 64 * kHBlocks) {
     const int lb = l / A.M, m = l - lb * A.M, bq = blockIdx.x * kHBlocks + lb;
