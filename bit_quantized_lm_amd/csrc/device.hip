@@ -58,6 +58,24 @@ __device__ __forceinline__ bf16x8 decode_quarter(uint32_t d0, uint32_t o0, uint3
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// A 4-bit head in its 2K-long 2-bit form (draft_head_tile_int4) holds, per
+// byte, the high halves vh of the codes of k and K/2 + k in quarters 0 and
+// 1 and their low halves vl in quarters 2 and 3.  Half H (0: k, 1: K/2 + k)
+// of a byte decodes to its whole 4-bit code, 4 vh + vl, as a bf16 denormal
+// v 2^-133 (the code in mantissa bits 0..3; quarters H and H + 2 read the
+// same x, so one MFMA takes both).
+template <int H>
+__device__ __forceinline__ uint32_t nibble_pair(uint32_t w) {
+  constexpr uint32_t m = 0x00030003u;
+  const uint32_t hi = H == 0 ? (w & m) << 2 : w & (m << 2);   // 4 vh, in bits 2..3
+  return hi + ((w >> (4 + 2 * H)) & m);                        // + vl
+}
+template <int H>
+__device__ __forceinline__ bf16x8 decode_half4(uint32_t d0, uint32_t o0, uint32_t d1, uint32_t o1) {
+  u32x4 v = {nibble_pair<H>(d0), nibble_pair<H>(o0), nibble_pair<H>(d1), nibble_pair<H>(o1)};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 constexpr int kXScaleLog2 = 64;   // x is staged as x * 2^64
 
 // Multiplier turning the MFMA sum D = sum x 2^64 v 2^(2q-133) of quarter q into
@@ -65,6 +83,8 @@ constexpr int kXScaleLog2 = 64;   // x is staged as x * 2^64
 __device__ __forceinline__ float quarter_scale(float S, int q) {
   return __builtin_ldexpf(S, 133 - kXScaleLog2 - 2 - 2 * q);
 }
+// The same for a 4-bit half decoded by decode_half4: (S/16) v with v 2^-133.
+__device__ __forceinline__ float half4_scale(float S) { return __builtin_ldexpf(S, 133 - kXScaleLog2 - 4); }
 
 // bf16 x (bits) scaled by 2^64, exactly (|x| < 2^63 stays finite).
 __device__ __forceinline__ uint32_t scale_x_pair(uint32_t w) {
@@ -963,32 +983,46 @@ __device__ __forceinline__ void big_select(const uint32_t* sk, const CoarseArgs&
 // scheduling barrier per slice keeps one slice's decoded operands live at a
 // time.  xb, xn: this lane's fragment 0 (A row nn, k-slot hh) in this group's
 // slab and the next one's.
-template <int MT, int NTW, int Q, int MP, bool kNext>
+// kMode 0: quarter Q of a 2-bit head; 1: half Q (0 or 1) of a 4-bit head, its
+// two quarters in one decode; 2: a 4-bit head's quarter 2 or 3, which half
+// Q - 2 already holds: no fragments, no MFMA, cg left as it is (read by no
+// update: a 4-bit head scales only after its halves, at quarters 1 and 2).
+template <int MT, int NTW, int Q, int MP, bool kNext, int kMode = 0>
 __device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MT][NTW], f32x4 (&acc)[MT][NTW],
                                               const f32x4 (&cp)[MT][NTW], const float (&sp)[NTW],
                                               u32x4 (&a)[2][MT], const u32x4 (&raw)[2][NTW],
                                               const u32x4 (&raw8)[2][NTW], const u32x4* xb, const u32x4* xn) {
   constexpr uint32_t mask = 0x00030003u << (2 * Q);
+  constexpr bool kMma = kMode != 2;
+  constexpr bool kUpd = !(kMode == 1 && Q == 0) && !(kMode == 2 && Q == 3);   // the previous group had sums
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int h = ks >> 1, e = ks & 1;
     if (ks < 3) {
       const int f = (((ks + 1) >> 1) * 2 + ((ks + 1) & 1)) * 4;
+      if constexpr (kMma) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i) a[(ks + 1) & 1][i] = xb[f * MP + 16 * i];
-    } else if (kNext) {
+        for (int i = 0; i < MT; ++i) a[(ks + 1) & 1][i] = xb[f * MP + 16 * i];
+      }
+    } else if (kNext && (kMma || Q == 3)) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) a[0][i] = xn[16 * i];
     }
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
-      const bf16x8 bv = decode_quarter(raw[h][t][2 * e], raw8[h][t][2 * e], raw[h][t][2 * e + 1],
-                                       raw8[h][t][2 * e + 1], mask);
+      bf16x8 bv;
+      if constexpr (kMode == 0)
+        bv = decode_quarter(raw[h][t][2 * e], raw8[h][t][2 * e], raw[h][t][2 * e + 1], raw8[h][t][2 * e + 1],
+                            mask);
+      else if constexpr (kMode == 1)
+        bv = decode_half4<Q & 1>(raw[h][t][2 * e], raw8[h][t][2 * e], raw[h][t][2 * e + 1],
+                                 raw8[h][t][2 * e + 1]);
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        cg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks & 1][i]), bv,
-                                                           ks ? cg[i][t] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        acc[i][t][ks] = __builtin_fmaf(sp[t], cp[i][t][ks], acc[i][t][ks]);
+        if constexpr (kMma)
+          cg[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks & 1][i]), bv,
+                                                             ks ? cg[i][t] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        if constexpr (kUpd) acc[i][t][ks] = __builtin_fmaf(sp[t], cp[i][t][ks], acc[i][t][ks]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1127,12 +1161,16 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
     auto group = [&](auto qc, int j) {
       constexpr int Q = decltype(qc)::value, t = Q % GPS;
       float sq[NTW];
+      // a 4-bit head decodes whole codes in quarters 0 and 1 (halves of its
+      // K) and has nothing left for quarters 2 and 3
+      constexpr int kMode = kHalf ? (Q < 2 ? 1 : 2) : 0;
 #pragma unroll
-      for (int u = 0; u < NTW; ++u) sq[u] = quarter_scale(lo_bf16(sz[u][Q]), Q);
+      for (int u = 0; u < NTW; ++u)
+        sq[u] = kMode == 0 ? quarter_scale(lo_bf16(sz[u][Q]), Q) : kMode == 1 ? half4_scale(lo_bf16(sz[u][Q])) : 0.f;
       const u32x4* xb = xl + ((j % NBUF) * GPS + t) * 16 * MP;
       const u32x4* xn = t + 1 < GPS ? xb + 16 * MP : xl + ((j + 1) % NBUF) * GPS * 16 * MP;
-      big_group_mma<MT, NTW, Q, MP, (t + 1 < GPS) || S::XW == 2>(cgs[Q & 1], acc, cgs[(Q + 1) & 1], sp, a, raw,
-                                                                 raw8, xb, xn);
+      big_group_mma<MT, NTW, Q, MP, (t + 1 < GPS) || S::XW == 2, kMode>(cgs[Q & 1], acc, cgs[(Q + 1) & 1], sp, a,
+                                                                        raw, raw8, xb, xn);
 #pragma unroll
       for (int u = 0; u < NTW; ++u) sp[u] = sq[u];
     };
@@ -1156,13 +1194,15 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       stage(std::integral_constant<int, 3>{});
     }
   }
-  // the last group's scale update
+  // the last group's scale update (a 4-bit head's last quarter has no sums)
+  if constexpr (!kHalf) {
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int t = 0; t < NTW; ++t)
+      for (int t = 0; t < NTW; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][t][r] = __builtin_fmaf(sp[t], cgs[1][i][t][r], acc[i][t][r]);
+        for (int r = 0; r < 4; ++r) acc[i][t][r] = __builtin_fmaf(sp[t], cgs[1][i][t][r], acc[i][t][r]);
+  }
   wait_vm<0>();
   if constexpr (WPB == 1) {   // one wave holds the whole block: its lists from registers
     if (!blk_ok) return;
