@@ -35,43 +35,45 @@ constexpr void bitonic8_desc(uint32_t (&v)[8]) {
       if ((i & d) == 0) cx_desc(v[i], v[i + d]);
 }
 
-// key[c]: the order-preserving unsigned image of column c's score (0 for a
-// column that does not exist); key_at(c) the same value, for the rebuild's
-// loop over a run-time column (on the device a read of the row in LDS, so
-// that key[] is only ever indexed by constants and stays in registers).
-// slot[i] receives 63 - column of the i-th best (score desc, column asc), or
-// 64 where fewer than i + 1 columns exist.
+// The eight best of a row of 64 keys taken as eight runs of eight.
+// run_at(r, ch) fills ch[0..7] with the keys of run r (each column once over
+// the eight runs), each key's low 6 bits already replaced by 63 - its column;
+// key_at(c) is column c's full key, for the rebuild's loop over a run-time
+// column.  slot[i] receives 63 - column of the i-th best (score desc, column
+// asc), or 64 where fewer than i + 1 columns exist.
 //
-// Each key's low 6 bits are replaced by 63 - column, so the keys of a row are
-// distinct and, between scores whose keys differ above bit 5, order as (score
-// desc, column asc).  Eight sorted runs of eight (Batcher's network) are
+// Replacing each key's low 6 bits by 63 - column makes the keys of a row
+// distinct and, between scores whose keys differ above bit 5, orders them as
+// (score desc, column asc).  The runs are sorted by Batcher's network and
 // merged into the eight largest (bitonic merge of the current eight with the
 // next run reversed), tracking the largest key left out.  That is the exact
 // list unless two of the eight, or the eighth and the best key left out,
 // agree above bit 5 (scores within 63 units in the last place of each
 // other); such a list is rebuilt with 64-bit keys (full key, then 63 -
 // column) over the columns whose keys reach the eighth's upper bits.
-template <class KeyAt>
-constexpr void select8_row(const uint32_t (&key)[64], KeyAt key_at, uint32_t (&slot)[8]) {
-  uint32_t run[8] = {}, ninth = 0u;
-#pragma unroll
-  for (int c8 = 0; c8 < 8; ++c8) {
+// kRolled: the run loop is not unrolled (small code, for an epilogue that
+// runs once per kernel and would otherwise wait on instruction fetch).
+template <bool kRolled, class RunAt, class KeyAt>
+constexpr void select8_runs(RunAt run_at, KeyAt key_at, uint32_t (&slot)[8]) {
+  uint32_t run[8] = {}, ninth = 0u;   // merging into zeros keeps the first run as it is
+  auto merge = [&](int r) {
     uint32_t ch[8] = {};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ch[e] = (key[8 * c8 + e] & ~63u) | (uint32_t)(63 - 8 * c8 - e);
+    run_at(r, ch);
     sort8_desc(ch);
-    if (c8 == 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) run[i] = ch[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t hi = umax32(run[i], ch[7 - i]);
-        ninth = umax32(ninth, umin32(run[i], ch[7 - i]));
-        run[i] = hi;
-      }
-      bitonic8_desc(run);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t hi = umax32(run[i], ch[7 - i]);
+      ninth = umax32(ninth, umin32(run[i], ch[7 - i]));
+      run[i] = hi;
     }
+    bitonic8_desc(run);
+  };
+  if constexpr (kRolled) {
+#pragma unroll 1
+    for (int r = 0; r < 8; ++r) merge(r);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) merge(r);
   }
   // exact unless upper parts agree where the order or the cut depends on them
   const uint32_t p8 = run[7] >> 6;
@@ -98,6 +100,20 @@ constexpr void select8_row(const uint32_t (&key)[64], KeyAt key_at, uint32_t (&s
 #pragma unroll
     for (int i = 0; i < 8; ++i) slot[i] = top[i] ? (uint32_t)(top[i] & 63ull) : 64u;
   }
+}
+
+// key[c]: the order-preserving unsigned image of column c's score (0 for a
+// column that does not exist), held in registers (indexed by constants only);
+// key_at(c) the same value, for the rebuild's loop.  Runs are eight
+// consecutive columns.
+template <class KeyAt>
+constexpr void select8_row(const uint32_t (&key)[64], KeyAt key_at, uint32_t (&slot)[8]) {
+  select8_runs<false>(
+      [&](int r, uint32_t(&ch)[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ch[e] = (key[8 * r + e] & ~63u) | (uint32_t)(63 - 8 * r - e);
+      },
+      key_at, slot);
 }
 
 }  // namespace dh

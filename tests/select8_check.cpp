@@ -1,5 +1,6 @@
 // Host check of the per-thread top-8 selection (select8.h), the code the
-// many-row coarse kernel runs: against a sort by (key desc, column asc) on
+// many-row coarse kernels run (unrolled over consecutive columns, and rolled
+// over the fp16 kernel's runs): against a sort by (key desc, column asc) on
 // random rows, rows with exact ties, rows with near-ties (keys a few units
 // apart, so their upper 26 bits agree) and rows with missing columns (key 0),
 // plus the sorting networks on all 256 zero-one inputs.  Exit status 0 = all
@@ -44,8 +45,18 @@ int main() {
     }
     const int nvalid = mode == 5 ? 1 + (int)(rng() % 64) : 64;
     for (int c = nvalid; c < 64; ++c) key[c] = 0u;
-    uint32_t slot[8];
+    uint32_t slot[8], slot2[8];
     dh::select8_row(key, [&](int c) { return key[c]; }, slot);
+    // the rolled form over runs of non-consecutive columns (the fp16 kernel's
+    // LDS pieces: run r = columns g, g + 16, g + 32, g + 48 for g = 2r, 2r + 1)
+    dh::select8_runs<true>(
+        [&](int r, uint32_t(&ch)[8]) {
+          for (int e = 0; e < 8; ++e) {
+            const int g = 2 * r + (e >> 2), col = 16 * (e & 3) + g;
+            ch[e] = (key[col] & ~63u) | (uint32_t)(63 - col);
+          }
+        },
+        [&](int c) { return key[c]; }, slot2);
     std::vector<int> cols;
     for (int c = 0; c < 64; ++c)
       if (key[c]) cols.push_back(c);
@@ -53,8 +64,10 @@ int main() {
     bool fast = true;
     for (int i = 0; i < 8; ++i) {
       const uint32_t want = i < (int)cols.size() ? (uint32_t)(63 - cols[i]) : 64u;
-      if (slot[i] != want) {
-        if (failures < 10) std::printf("trial %d mode %d slot %d: got %u want %u\n", trial, mode, i, slot[i], want);
+      if (slot[i] != want || slot2[i] != want) {
+        if (failures < 10)
+          std::printf("trial %d mode %d slot %d: got %u / %u (rolled) want %u\n", trial, mode, i, slot[i], slot2[i],
+                      want);
         ++failures;
       }
     }
