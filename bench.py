@@ -174,6 +174,29 @@ class Rig:
         self.last_coarse_pct = {f"p{q}": round(float(np.percentile(coarse_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
         return total_ms / 1e3 / steps, float(np.mean(coarse_ms)) / 1e3, wall
 
+    def tiny_call_us(self, steps=500):
+        """Per-call time of the tiny configuration (M = 1, K = 1024, N = 16384,
+        KCAND = 8, R = 32): launch latency more than bandwidth (its 4.2 MB of
+        codes and pairs stay in the Infinity Cache between calls)."""
+        torch, B = self.torch, self.B
+        from bit_quantized_lm_amd import workload
+        cfg = workload.CONFIGS["tiny"]
+        x_host, w = workload.make_inputs(cfg)
+        head = B.DraftHead.from_weight(w, kcand=cfg.kcand, R=cfg.rerank, device=self.dev)
+        x = torch.from_numpy(x_host.view(np.int16)).to(self.dev)
+        out = B.forward_buffers(cfg.m, cfg.n, cfg.kcand, cfg.rerank, self.dev)
+        ws = B.workspace_for(cfg.m, cfg.k, self.dev)
+        for i in range(50):
+            head(x, stream=self.stream, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(steps):
+            head(x, stream=self.stream, out=out, workspace=ws)
+        e.record()
+        torch.cuda.synchronize()
+        return {"us_per_call": round(s.elapsed_time(e) / steps * 1e3, 2), "M": cfg.m, "K": cfg.k, "N": cfg.n}
+
     def e4m3_call_us(self, ms=(1, 8, 72), steps=200):
         """Per-call time with the rerank reading an e4m3 copy of the head
         (a synthetic per-channel FP8 head; coarse pass unchanged)."""
@@ -572,6 +595,8 @@ def main():
         extra["logits_row_us"] = {str(mm): rig.logits_row_us(mm) for mm in (1, 8, 72)}
         extra["forward_row_us_per_call"] = {str(mm): rig.forward_row_us(mm) for mm in (1, 8, 72)}
         log(f"one call with the caller's bf16 row built inside it: {extra['forward_row_us_per_call']}")
+        extra["tiny_config_call"] = rig.tiny_call_us()
+        log(f"one call of the tiny configuration: {extra['tiny_config_call']}")
         extra["e4m3_rerank_us_per_call"] = rig.e4m3_call_us()
         extra["graph_replay_us_per_call"] = {str(m): rig.graph_us(m) for m in (1, 8, 72)}
         log(f"one call inside a replayed HIP graph: {extra['graph_replay_us_per_call']}")
