@@ -736,7 +736,10 @@ def test_nvfp4_rerank_full_shape(dev, full):
 
 # ------------------------------------------------------------ 4-bit head
 @pytest.mark.parametrize("m,k,n,kcand,r", [(1, 256, 3000, 1, 32), (3, 768, 5000, 1, 32), (8, 1024, 20000, 8, 32),
-                                           (20, 512, 3000, 1, 16), (5, 2048, 5000, 4, 32), (72, 1024, 2100, 1, 32)])
+                                           (20, 512, 3000, 1, 16), (5, 2048, 5000, 4, 32), (72, 1024, 2100, 1, 32),
+                                           # every row-tile count of the many-row kernel's 4-bit form
+                                           (9, 1024, 3000, 1, 32), (40, 512, 2000, 1, 32), (57, 1024, 2500, 4, 32),
+                                           (64, 2560, 2600, 1, 32)])
 def test_int4_parity(dev, m, k, n, kcand, r):
     """The 4-bit head (run as its 2K-long 2-bit form) against the oracle's own
     4-bit definition."""
