@@ -250,8 +250,8 @@ class Rig:
 
     def int4_call_us(self, ms=(1, 8, 72), steps=200, copies=2):
         """Per-call time of the 4-bit head at KCAND = 1 (the page's 4-bit
-        configuration), run as its 2K-long 2-bit form with the head's own
-        pairs (N K/2 + 4 N K/128 = 337,715,200 bytes a call); weights rotated."""
+        configuration), its own bytes and pairs (draft_head_tile_int4:
+        N K/2 + 4 N K/128 = 337,715,200 bytes a call); weights rotated."""
         torch, B = self.torch, self.B
         packed4 = B.draft_head_quantize_pack_int4(self.w_host)
         tiled, pairs = B.draft_head_tile_int4(*packed4)

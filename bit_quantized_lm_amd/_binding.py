@@ -209,9 +209,9 @@ def draft_head_tile(packed: np.ndarray, S: np.ndarray, ZS: np.ndarray):
 
 
 def draft_head_tile_int4(packed4: np.ndarray, S: np.ndarray, ZS: np.ndarray):
-    """A 4-bit head's canonical arrays -> the device form of its 2K-long 2-bit
-    form: (tiled codes uint8 [NBLK*64*K/2], pairs uint32 [NBLK*64*K/128], the
-    head's own pairs only)."""
+    """A 4-bit head's canonical arrays -> its device form: its own code bytes
+    in the tiles of a 2-bit head of length 2K, and its own pairs (tiled uint8
+    [NBLK*64*K/2], pairs uint32 [NBLK*64*K/128])."""
     lib = load_library()
     packed4 = np.ascontiguousarray(packed4, dtype=np.uint8)
     S = np.ascontiguousarray(S, dtype=np.uint16)
@@ -264,7 +264,7 @@ def _ws(workspace):
 def draft_head_coarse(x, tiled, pairs, N: int, kcand: int = 8, cand_val=None, cand_id=None,
                       coarse_out=None, workspace=None, stream=None, bits: int = 2):
     """x: CUDA bf16 [M][K]; tiled/pairs: CUDA tensors in the draft_head_tile layout
-    (bits = 4: of the head's 2K-long 2-bit form); workspace: CUDA tensor of
+    (bits = 4: draft_head_tile_int4's form); workspace: CUDA tensor of
     draft_head_workspace_bytes(M, K) bytes (2K for bits = 4; allocated when None).
     Returns (cand_val fp32 [M][NBLK*kcand], cand_id int32 [M][NBLK*kcand])."""
     import torch

@@ -58,22 +58,17 @@ __device__ __forceinline__ bf16x8 decode_quarter(uint32_t d0, uint32_t o0, uint3
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// A 4-bit head in its 2K-long 2-bit form (draft_head_tile_int4) holds, per
-// byte, the high halves vh of the codes of k and K/2 + k in quarters 0 and
-// 1 and their low halves vl in quarters 2 and 3.  Half H (0: k, 1: K/2 + k)
-// of a byte decodes to its whole 4-bit code, 4 vh + vl, as a bf16 denormal
-// v 2^-133 (the code in mantissa bits 0..3; quarters H and H + 2 read the
-// same x, so one MFMA takes both).
-template <int H>
-__device__ __forceinline__ uint32_t nibble_pair(uint32_t w) {
-  constexpr uint32_t m = 0x00030003u;
-  const uint32_t hi = H == 0 ? (w & m) << 2 : w & (m << 2);   // 4 vh, in bits 2..3
-  return hi + ((w >> (4 + 2 * H)) & m);                        // + vl
-}
+// A 4-bit head as draft_head_tile_int4 lays it out: the page's own code
+// bytes (the code of k in bits 0..3, that of K/2 + k in bits 4..7), tiled as
+// a 2-bit head of length 2K, whose quarters 0 and 1 cover the same k as the
+// two nibbles (byte j, quarter q of that form: k' = j + q K/2).  Half H of a
+// byte pair masked in place with 0x000F000F << 4H is a bf16 halfword holding
+// v * 2^(4H-133): for H = 1 the code's high bit is the exponent's low bit,
+// which reads the same way (a pattern b < 256 is the value b * 2^-133, as in
+// quarter 3 above).  One AND per two weights, as for a quarter.
 template <int H>
 __device__ __forceinline__ bf16x8 decode_half4(uint32_t d0, uint32_t o0, uint32_t d1, uint32_t o1) {
-  u32x4 v = {nibble_pair<H>(d0), nibble_pair<H>(o0), nibble_pair<H>(d1), nibble_pair<H>(o1)};
-  return __builtin_bit_cast(bf16x8, v);
+  return decode_quarter(d0, o0, d1, o1, 0x000F000Fu << (4 * H));
 }
 
 constexpr int kXScaleLog2 = 64;   // x is staged as x * 2^64
@@ -83,8 +78,11 @@ constexpr int kXScaleLog2 = 64;   // x is staged as x * 2^64
 __device__ __forceinline__ float quarter_scale(float S, int q) {
   return __builtin_ldexpf(S, 133 - kXScaleLog2 - 2 - 2 * q);
 }
-// The same for a 4-bit half decoded by decode_half4: (S/16) v with v 2^-133.
-__device__ __forceinline__ float half4_scale(float S) { return __builtin_ldexpf(S, 133 - kXScaleLog2 - 4); }
+// The same for half H of a 4-bit head (decode_half4, v 2^(4H-133)): (S/16)
+// sum x v, the page's 4-bit weight (S/16) v before its zero point.
+__device__ __forceinline__ float half4_scale(float S, int H) {
+  return __builtin_ldexpf(S, 133 - kXScaleLog2 - 4 - 4 * H);
+}
 
 // bf16 x (bits) scaled by 2^64, exactly (|x| < 2^63 stays finite).
 __device__ __forceinline__ uint32_t scale_x_pair(uint32_t w) {
@@ -154,7 +152,7 @@ struct CoarseArgs {
   unsigned long long* hand;   // per-row hand-off words of the rerank; workgroup 0 zeroes hand[0..ncnt)
   int ncnt;
   int kx;          // row length of x: K, or K / 2 for a 4-bit head run at length K (x' = (x, x))
-  int half_pairs;  // pairs hold quarters 0 and 1 only (a 4-bit head's form, draft_head_tile_int4)
+  int half_pairs;  // a 4-bit head (draft_head_tile_int4): code nibbles, pairs of quarters 0 and 1 only
 };
 
 // The rerank's per-row hand-off words are only ever written with agent-scope
@@ -167,15 +165,10 @@ __device__ __forceinline__ void zero_counters(const CoarseArgs& A) {
     __hip_atomic_store(A.hand + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A 4-bit head's pairs in its 2K-long form (draft_head_tile_int4): for each
-// (column, byte group) the pairs of quarters 0 and 1 are stored, the head's
-// own (S, ZS); quarters 2 and 3 carry (S/4, S/4) of the same columns, formed
-// here (S/4 is exact in bf16, so the truncation drops only zero bits).
-__device__ __forceinline__ u32x4 expand_pairs(u32x2 p) {
-  const uint32_t s0 = __float_as_uint(__uint_as_float(p[0] << 16) * 0.25f) >> 16;
-  const uint32_t s1 = __float_as_uint(__uint_as_float(p[1] << 16) * 0.25f) >> 16;
-  return u32x4{p[0], p[1], s0 | (s0 << 16), s1 | (s1 << 16)};
-}
+// A 4-bit head's pairs (draft_head_tile_int4): per (column, byte group) the
+// head's own (S, ZS) of its two halves, in the slots of quarters 0 and 1;
+// quarters 2 and 3 hold nothing (zero pairs: no code part, no zero point).
+__device__ __forceinline__ u32x4 half_pairs4(u32x2 p) { return u32x4{p[0], p[1], 0u, 0u}; }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -199,14 +192,15 @@ __device__ __forceinline__ void store_scores(const CoarseArgs& A, int m, int n, 
 // `xb` points at this lane's fragment 0 of the group (A row nn, k-slot hh),
 // fragment f of M-tile i at xb[f * fstride + 16 * i]; `Xg` at the group's X[row].
 // MFMA phase of one group (quarter Q of a byte group; Q < 0: quarter `q`
-// known at run time): cg = sum over the group's k of x 2^64 * v 2^(2q-133).
+// known at run time): cg = sum over the group's k of x 2^64 * v 2^(2q-133);
+// with kHalf, half q of a 4-bit head's bytes (v 2^(4q-133), decode_half4).
 // The wave covers NT 16-column tiles; raw8 holds raw >> 8 (the odd byte pairs
 // moved down), computed once per byte group.
-template <int MT, int Q, int NT>
+template <int MT, int Q, int NT, bool kHalf = false>
 __device__ __forceinline__ void group_mma(f32x4 (&cg)[MT][NT], const u32x4 (&raw)[2][NT],
                                           const u32x4 (&raw8)[2][NT], const u32x4* xb, int fstride,
                                           int q = Q) {
-  const uint32_t mask = 0x00030003u << (2 * q);
+  const uint32_t mask = kHalf ? 0x000F000Fu << (4 * q) : 0x00030003u << (2 * q);
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -233,8 +227,9 @@ __device__ __forceinline__ void group_mma(f32x4 (&cg)[MT][NT], const u32x4 (&raw
 
 // Scale phase of one group: acc += (S/4) sum x v - (ZS - S) sum x, with S, ZS
 // the group's premultiplied pair (the page's S * p - ZS * X written for codes
-// decoded without the 1.0 bias).  Rows 16i + 4hh + r, r < MR.
-template <int MT, int MR, int Q, int NT>
+// decoded without the 1.0 bias; with kHalf a 4-bit head's half, (S/16) sum x v).
+// Rows 16i + 4hh + r, r < MR.
+template <int MT, int MR, int Q, int NT, bool kHalf = false>
 __device__ __forceinline__ void group_scale(f32x4 (&acc)[MT][NT], const f32x4 (&cg)[MT][NT],
                                             const u32x4 (&sz)[NT], const float* Xg, int hh, int q = Q) {
   float X[MT][MR];
@@ -248,7 +243,7 @@ __device__ __forceinline__ void group_scale(f32x4 (&acc)[MT][NT], const f32x4 (&
     if constexpr (Q >= 0) pr = sz[t][Q];
     else pr = q == 0 ? sz[t][0] : q == 1 ? sz[t][1] : q == 2 ? sz[t][2] : sz[t][3];
     const float S = lo_bf16(pr);
-    const float Sq = quarter_scale(S, q), nzp = S - hi_bf16(pr);
+    const float Sq = kHalf ? half4_scale(S, q) : quarter_scale(S, q), nzp = S - hi_bf16(pr);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -560,9 +555,9 @@ void coarse_resident_kernel(CoarseArgs A) {
   constexpr int MR = MP < 4 ? MP : 4;  // accumulator rows r that can hold a live row
   extern __shared__ __align__(16) unsigned char smem[];
   const int NG4 = A.K >> 9, Q4 = A.K >> 2;
-  // x rows of length kx < K (a 4-bit head in its 2K-long form, read as
-  // (x, x)): quarters 2 and 3 see the x of quarters 0 and 1, so only those
-  // are staged (QN = 2 quarters per byte group; else 4).
+  // x rows of length kx < K (a 4-bit head in the tiles of a 2-bit head of
+  // length 2K): only quarters 0 and 1, its two halves, carry codes, so only
+  // their x is staged (QN = 2 quarters per byte group; else 4).
   const int QN = A.kx < A.K ? 2 : 4, NGS = A.kx >> 7;   // staged quarters, staged groups
   u32x4* xs = reinterpret_cast<u32x4*>(smem);                               // [NGS][16][MP]
   float* Xs = reinterpret_cast<float*>(smem + (size_t)NGS * 16 * MP * 16);      // [NGS][MP]
@@ -589,7 +584,7 @@ void coarse_resident_kernel(CoarseArgs A) {
       for (int t = 0; t < NT; ++t) raw[h][t] = __builtin_nontemporal_load(tp + ((G * 2 + h) * 4 + t) * 64 + lane);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if constexpr (kHalf) sz[t] = expand_pairs(__builtin_nontemporal_load(pp2 + (G * 4 + t) * 16 + nn));
+      if constexpr (kHalf) sz[t] = half_pairs4(__builtin_nontemporal_load(pp2 + (G * 4 + t) * 16 + nn));
       else sz[t] = __builtin_nontemporal_load(pp + (G * 4 + t) * 16 + nn);
     }
   };
@@ -665,20 +660,26 @@ void coarse_resident_kernel(CoarseArgs A) {
   auto byte_group = [&](int G, const u32x4 (&raw)[2][NT], const u32x4 (&sz)[NT]) {
     const u32x4* xb = xs + (size_t)(G * QN * 16 + hh) * MP + arow;
     const float* Xg = Xs + G * QN * MP + ((4 * hh) & (MP - 1));
-    const int q2 = QN == 4 ? 2 : 0, q3 = QN == 4 ? 3 : 1;   // staged quarter of quarters 2, 3
     u32x4 raw8[2][NT];
     shift_codes(raw, raw8);
     // each group's scale update is issued after the next group's MFMAs, so it
     // does not wait on results that were just issued
     f32x4 c0[1][NT], c1[1][NT];
-    group_mma<1, 0, NT>(c0, raw, raw8, xb, MP);
-    group_mma<1, 1, NT>(c1, raw, raw8, xb + 16 * MP, MP);
-    group_scale<1, MR, 0, NT>(acc, c0, sz, Xg, 0);
-    group_mma<1, 2, NT>(c0, raw, raw8, xb + q2 * 16 * MP, MP);
-    group_scale<1, MR, 1, NT>(acc, c1, sz, Xg + MP, 0);
-    group_mma<1, 3, NT>(c1, raw, raw8, xb + q3 * 16 * MP, MP);
-    group_scale<1, MR, 2, NT>(acc, c0, sz, Xg + q2 * MP, 0);
-    group_scale<1, MR, 3, NT>(acc, c1, sz, Xg + q3 * MP, 0);
+    if constexpr (kHalf) {   // a 4-bit head: its two halves, whole codes
+      group_mma<1, 0, NT, true>(c0, raw, raw8, xb, MP);
+      group_mma<1, 1, NT, true>(c1, raw, raw8, xb + 16 * MP, MP);
+      group_scale<1, MR, 0, NT, true>(acc, c0, sz, Xg, 0);
+      group_scale<1, MR, 1, NT, true>(acc, c1, sz, Xg + MP, 0);
+    } else {
+      group_mma<1, 0, NT>(c0, raw, raw8, xb, MP);
+      group_mma<1, 1, NT>(c1, raw, raw8, xb + 16 * MP, MP);
+      group_scale<1, MR, 0, NT>(acc, c0, sz, Xg, 0);
+      group_mma<1, 2, NT>(c0, raw, raw8, xb + 32 * MP, MP);
+      group_scale<1, MR, 1, NT>(acc, c1, sz, Xg + MP, 0);
+      group_mma<1, 3, NT>(c1, raw, raw8, xb + 48 * MP, MP);
+      group_scale<1, MR, 2, NT>(acc, c0, sz, Xg + 2 * MP, 0);
+      group_scale<1, MR, 3, NT>(acc, c1, sz, Xg + 3 * MP, 0);
+    }
   };
   // Two forms of the same stream.  From two rows on, each ring set is
   // refilled right after its byte group is done, so D byte groups are in
@@ -746,12 +747,13 @@ void coarse_resident_kernel(CoarseArgs A) {
 // product is exact and only fp32 sums round.
 //
 // prep_x_kernel writes x for one launch into the caller's workspace in the
-// order the kernel consumes it, rows >= M zero (MP = 16 MT rows):
-//   x slab of group g = 4G + q (byte group G, quarter q): 16 fragments x MP
-//     rows, 16 bytes each, x * 2^64 in decode order (256 MT entries);
+// order the kernel consumes it, rows >= M zero (MP = 16 MT rows; QPB groups
+// per byte group, dh::big_qpb: four quarters, or a 4-bit head's two halves):
+//   x slab of group g = QPB G + q (byte group G, quarter q): 16 fragments x
+//     MP rows, 16 bytes each, x * 2^64 in decode order (256 MT entries);
 //   zero-point slab of byte group G: 256 entries; entry hh*MP + m (hh < 2)
 //     holds row m's k-slots 8hh..8hh+7 of that product:
-//     X_hi(q0..q3) X_mid(q0..q3) | X_lo(q0..q3) 0 0 0 0.
+//     X_hi(q0..q3) X_mid(q0..q3) | X_lo(q0..q3) 0 0 0 0 (X of q >= QPB: 0).
 //
 // Workgroup = 4 blocks of 64 columns.  From MT = 3 on, two waves share a
 // block, wave (block lb, part p) holding column tiles 2p and 2p + 1 for all
@@ -765,14 +767,16 @@ void coarse_resident_kernel(CoarseArgs A) {
 // runs beside the matrix cores instead of between two MFMA phases.
 //
 // Every global read of the main loop is a direct-to-LDS DMA.  Stage j (GPS
-// groups, GPS = 1 or 2, SPB = 4 / GPS stages per byte group; j < 0: the
+// groups, GPS = 1 or 2, SPB = QPB / GPS stages per byte group; j < 0: the
 // prologue) issues, in this order and every time, even where the data does
 // not exist (then a harmless copy into a slot that is free, or that later
 // receives the same bytes):
 //   X(j + XD)  the wave's chunks of that stage's x slabs               NX ops
-//   at j = SPB G + 1 (after every wave read byte group G's codes):
+//   at j = SPB G + 1 (after every wave read byte group G's codes; with one
+//   stage per byte group, at j = G, after the barrier that ended G - 1):
 //   B(G + 1)   its chunks of byte group G + 1's zero-point slab       NB ops
 //   C(G + CD)  the wave's chunks of that byte group's codes/pairs      NC ops
+//              (G + CD - 1 with one stage per byte group)
 // and ends with one vmcnt wait that completes X(j + XW) and, at the end of a
 // byte group, C and B of the next one, then a barrier.  With XW = 2 the
 // next stage's first x fragments are read before that barrier.  The number
@@ -823,7 +827,7 @@ __device__ __forceinline__ void wait_vm() {
 // four group sums for the zero-point slab.  x has rows of kx elements;
 // element k of x' is x[k mod kx] (kx = K, or K/2).
 __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t* __restrict__ x, int M, int MP, int K, int kx,
-                                                     u32x4* __restrict__ xslab, u32x4* __restrict__ zslab) {
+                                                     int qpb, u32x4* __restrict__ xslab, u32x4* __restrict__ zslab) {
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int NG4 = K >> 9, Q4 = K >> 2;
   if (w >= MP * NG4) return;   // whole waves leave together
@@ -833,11 +837,12 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t* __restrict_
   const u32x4 v = m < M ? *reinterpret_cast<const u32x4*>(x + (size_t)m * kx + (k < kx ? k : k - kx))
                         : u32x4{0u, 0u, 0u, 0u};
   float sum;
-  xslab[((size_t)(4 * G + q) * 16 + f) * MP + m] = permute_x(v, sum);
+  const u32x4 xv = permute_x(v, sum);
+  if (q < qpb) xslab[((size_t)(qpb * G + q) * 16 + f) * MP + m] = xv;
   sum = row16_sum(sum);
   float X[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) X[u] = __shfl(sum, 16 * u, 64);
+  for (int u = 0; u < 4; ++u) X[u] = u < qpb ? __shfl(sum, 16 * u, 64) : 0.f;
   if (lane < 2) {
     uint32_t part[3][4];
 #pragma unroll
@@ -986,18 +991,17 @@ __device__ __forceinline__ void big_select(const uint32_t* sk, const CoarseArgs&
 // scheduling barrier per slice keeps one slice's decoded operands live at a
 // time.  xb, xn: this lane's fragment 0 (A row nn, k-slot hh) in this group's
 // slab and the next one's.
-// kMode 0: quarter Q of a 2-bit head; 1: half Q (0 or 1) of a 4-bit head, its
-// two quarters in one decode; 2: a 4-bit head's quarter 2 or 3, which half
-// Q - 2 already holds: no fragments, no MFMA, cg left as it is (read by no
-// update: a 4-bit head scales only after its halves, at quarters 1 and 2).
-template <int MT, int NTW, int Q, int MP, bool kNext, int kMode = 0>
+// kMode 0: quarter Q of a 2-bit head; 1: half Q (0 or 1) of a 4-bit head,
+// whole codes (decode_half4); 2: a 4-bit head's quarter 2 or 3 where its byte
+// groups keep four stages: no codes, no fragments, no MFMA, cg left as it is.
+// kUpd: the previous group had sums to scale (not so after a kMode 2 group).
+template <int MT, int NTW, int Q, int MP, bool kNext, int kMode, bool kUpd>
 __device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MT][NTW], f32x4 (&acc)[MT][NTW],
                                               const f32x4 (&cp)[MT][NTW], const float (&sp)[NTW],
                                               u32x4 (&a)[2][MT], const u32x4 (&raw)[2][NTW],
                                               const u32x4 (&raw8)[2][NTW], const u32x4* xb, const u32x4* xn) {
   constexpr uint32_t mask = 0x00030003u << (2 * Q);
   constexpr bool kMma = kMode != 2;
-  constexpr bool kUpd = !(kMode == 1 && Q == 0) && !(kMode == 2 && Q == 3);   // the previous group had sums
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int h = ks >> 1, e = ks & 1;
@@ -1037,14 +1041,15 @@ __device__ __forceinline__ void big_group_mma(f32x4 (&cg)[MT][NTW], f32x4 (&acc)
 // block's selection (from LDS when two waves share the block).
 template <int MT, int P, bool kHalf>
 __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem) {
-  using S = BigShape<MT>;
+  constexpr int QPB = dh::big_qpb(kHalf, MT);   // groups (stages' worth of x slabs) per byte group
+  using S = BigShape<MT, QPB>;
   constexpr int MP = 16 * MT, XD = S::XD, NBUF = XD + 1, W = S::W, WPB = S::WPB, CD = S::CD, BPW = S::BPW;
   constexpr int NTW = S::NTW, T0 = P * NTW;
   const CoarseArgs& A = BA.c;
   constexpr int GPS = S::GPS, SPB = S::SPB;
   u32x4* xs = reinterpret_cast<u32x4*>(smem);     // [NBUF][GPS][16][MP]
   u32x4* cs = xs + NBUF * GPS * 16 * MP;          // [CD slots][BPW blocks][9 chunks][64]
-  u32x4* zs = cs + CD * BPW * kCodeChunks * 64;   // [256]
+  u32x4* zs = cs + CD * BPW * kCodeChunks * 64;   // [ZPS][256]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1052,7 +1057,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   const int lb = wave & (BPW - 1);
   const int b = blockIdx.x * BPW + lb;
   const bool blk_ok = b < A.nblk;
-  const int NG4 = A.K >> 9, NGRP = A.K >> 7;
+  const int NG4 = A.K >> 9, NGRP = QPB * NG4;
   if constexpr (P == 0) zero_counters(A);
 
   // A block past the last one streams block 0 (valid memory) and writes nothing.
@@ -1072,21 +1077,22 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
   auto issue = [&](int j) {
 #pragma unroll
     for (int k = 0; k < S::nx(P); ++k) {   // chunks lb + BPW k of the stage's GPS slabs
-      const dh::XOp o = dh::x_op<MT>(j, lb, k, NGRP);
+      const dh::XOp o = dh::x_op<S>(j, lb, k, NGRP);
       dma16(voff, BA.xslab + (size_t)o.slab * 256 * MT + o.chunk * 64, xs_l + o.dst * 1024);
     }
-    if (dh::stage_has_byte_ops<MT>(j)) {
+    if (dh::stage_has_byte_ops<S>(j)) {
       // the zero-point slab first: it is waited for at the byte group's end,
       // the codes (issued after it, so not waited for with it) CD byte groups
       // later
-      const int GB = dh::zp_group<MT>(j, NG4);
+      const int GB = dh::zp_group<S>(j, NG4);
+      const uint32_t zslot = (uint32_t)dh::zp_slot<S>(j);
 #pragma unroll
       for (int k = 0; k < S::nb(P); ++k) {   // zero-point chunks lb nb + k of four
         const int c = lb * S::nb(P) + k;
-        dma16(voff, BA.zslab + (size_t)GB * kZpEntries + c * 64, zs_l + c * 1024);
+        dma16(voff, BA.zslab + (size_t)GB * kZpEntries + c * 64, zs_l + zslot * 4096 + c * 1024);
       }
-      const int GC = dh::code_group<MT>(j, NG4);   // never negative: the prologue starts at 1 - SPB CD or before
-      const uint32_t cslot = (uint32_t)dh::code_slot<MT>(j);
+      const int GC = dh::code_group<S>(j, NG4);
+      const uint32_t cslot = (uint32_t)dh::code_slot<S>(j);
 #pragma unroll
       for (int k = 0; k < S::nc(P); ++k) {
         const int c = k;
@@ -1099,7 +1105,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
 
 #pragma unroll
   for (int j = -S::PRO; j < 0; ++j) issue(j);
-  wait_vm<big_wait<MT, P>(SPB - 1)>();
+  wait_vm<big_wait<S, P>(SPB - 1)>();
   __syncthreads();
 
   // cgs[Q & 1] receives group Q's MFMA sums; the other set still holds the
@@ -1129,7 +1135,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       for (int t = 0; t < NTW; ++t) raw[h][t] = cw[(h * 4 + T0 + t) * 64 + lane];
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
-      if constexpr (kHalf) sz[t] = expand_pairs(reinterpret_cast<const u32x2*>(cw + 512)[(T0 + t) * 16 + nn]);
+      if constexpr (kHalf) sz[t] = half_pairs4(reinterpret_cast<const u32x2*>(cw + 512)[(T0 + t) * 16 + nn]);
       else sz[t] = cw[512 + (T0 + t) * 16 + nn];
     }
 
@@ -1137,7 +1143,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
     {
       u32x4 za[MT];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) za[i] = zs[(hh & 1) * MP + 16 * i + nn];
+      for (int i = 0; i < MT; ++i) za[i] = zs[(G % S::ZPS) * kZpEntries + (hh & 1) * MP + 16 * i + nn];
       if (hh >= 2) {
 #pragma unroll
         for (int i = 0; i < MT; ++i) za[i] = u32x4{0u, 0u, 0u, 0u};
@@ -1164,16 +1170,18 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
     auto group = [&](auto qc, int j) {
       constexpr int Q = decltype(qc)::value, t = Q % GPS;
       float sq[NTW];
-      // a 4-bit head decodes whole codes in quarters 0 and 1 (halves of its
-      // K) and has nothing left for quarters 2 and 3
+      // a 4-bit head decodes whole codes in quarters 0 and 1 (the halves of
+      // its K) and, where its byte groups keep four stages, has nothing in
+      // quarters 2 and 3 (after which no sums are left to scale)
       constexpr int kMode = kHalf ? (Q < 2 ? 1 : 2) : 0;
+      constexpr bool kUpd = !(kHalf && QPB == 4 && (Q == 0 || Q == 3));
 #pragma unroll
       for (int u = 0; u < NTW; ++u)
-        sq[u] = kMode == 0 ? quarter_scale(lo_bf16(sz[u][Q]), Q) : kMode == 1 ? half4_scale(lo_bf16(sz[u][Q])) : 0.f;
+        sq[u] = kMode == 0 ? quarter_scale(lo_bf16(sz[u][Q]), Q) : kMode == 1 ? half4_scale(lo_bf16(sz[u][Q]), Q) : 0.f;
       const u32x4* xb = xl + ((j % NBUF) * GPS + t) * 16 * MP;
       const u32x4* xn = t + 1 < GPS ? xb + 16 * MP : xl + ((j + 1) % NBUF) * GPS * 16 * MP;
-      big_group_mma<MT, NTW, Q, MP, (t + 1 < GPS) || S::XW == 2, kMode>(cgs[Q & 1], acc, cgs[(Q + 1) & 1], sp, a,
-                                                                        raw, raw8, xb, xn);
+      big_group_mma<MT, NTW, Q, MP, (t + 1 < GPS) || S::XW == 2, kMode, kUpd>(cgs[Q & 1], acc, cgs[(Q + 1) & 1],
+                                                                              sp, a, raw, raw8, xb, xn);
 #pragma unroll
       for (int u = 0; u < NTW; ++u) sp[u] = sq[u];
     };
@@ -1183,7 +1191,7 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       issue(j);
       group(std::integral_constant<int, GPS * Qs>{}, j);
       if constexpr (GPS == 2) group(std::integral_constant<int, GPS * Qs + 1>{}, j);
-      wait_vm<big_wait<MT, P>(Qs)>();
+      wait_vm<big_wait<S, P>(Qs)>();
       __syncthreads();
       if constexpr (S::XW == 1) {   // the next stage's first fragments, now visible
 #pragma unroll
@@ -1191,14 +1199,14 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       }
     };
     stage(std::integral_constant<int, 0>{});
-    stage(std::integral_constant<int, 1>{});
+    if constexpr (SPB >= 2) stage(std::integral_constant<int, 1>{});
     if constexpr (SPB == 4) {
       stage(std::integral_constant<int, 2>{});
       stage(std::integral_constant<int, 3>{});
     }
   }
-  // the last group's scale update (a 4-bit head's last quarter has no sums)
-  if constexpr (!kHalf) {
+  // the last group's scale update (none after a kMode 2 group)
+  if constexpr (!(kHalf && QPB == 4)) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -2650,10 +2658,10 @@ hipError_t launch_h16(const HArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e
 
 template <int MT, bool kHalf>
 hipError_t launch_big_k(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  constexpr size_t lds = big_lds_bytes(MT, BigShape<MT>::XD, BigShape<MT>::CD, BigShape<MT>::BPW, BigShape<MT>::GPS);
+  using S = BigShape<MT, dh::big_qpb(kHalf, MT)>;
+  constexpr size_t lds = big_lds_bytes<S>();
   static_assert(lds <= kMaxLds, "LDS budget of the many-row kernel");
-  static_assert((size_t)BigShape<MT>::BPW * 16 * MT * kScStride * sizeof(float) <= lds,
-                "the score area reuses the ring's LDS");
+  static_assert((size_t)S::BPW * 16 * MT * kScStride * sizeof(float) <= lds, "the score area reuses the ring's LDS");
   static_assert(lds <= kMaxLds, "LDS of one workgroup");
   static bool attr_set = false;
   if (!attr_set) {
@@ -2662,8 +2670,8 @@ hipError_t launch_big_k(const BigArgs& A, hipStream_t s, hipEvent_t e0, hipEvent
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((A.c.nblk + BigShape<MT>::BPW - 1) / BigShape<MT>::BPW);
-  hipExtLaunchKernelGGL(coarse_mfma_kernel<MT, kHalf>, grid, dim3(64 * BigShape<MT>::W), lds, s, e0, e1, 0, A);
+  dim3 grid((A.c.nblk + S::BPW - 1) / S::BPW);
+  hipExtLaunchKernelGGL(coarse_mfma_kernel<MT, kHalf>, grid, dim3(64 * S::W), lds, s, e0, e1, 0, A);
   return hipGetLastError();
 }
 template <int MT>
@@ -2692,7 +2700,7 @@ bool use_h16(int K, int kx, int mt) { return mt >= 3 && kx == K && K <= kPrepHMa
 
 // Up to 8 rows whose x fits the workgroup's LDS take the resident kernel (no
 // workspace); every other M the many-row kernel, in launches of up to 80 rows.
-// ks: the staged row length of x (K, or K/2 for a 4-bit head in its 2K-long form).
+// ks: the staged row length of x (K, or K/2 for a 4-bit head in the tiles of a 2-bit head of length K).
 bool use_resident(int M, int ks) { return M <= 8 && resident_lds_bytes(ks, resident_rows(M, ks)) <= kMaxLds; }
 
 // Workspace: the rerank's per-row hand-off words, then (many-row kernel
@@ -2775,7 +2783,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
   CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
                reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out, row_out, topk_only,
                static_cast<unsigned long long*>(workspace), M, kx ? kx : K};
-  A.half_pairs = A.kx < A.K;   // a 4-bit head in its 2K-long form: draft_head_tile_int4's pairs
+  A.half_pairs = A.kx < A.K;   // a 4-bit head as draft_head_tile_int4 lays it out
   hipError_t e = hipSuccess;
   const int ks = A.kx;   // the row length of x the resident kernel stages
   if (use_resident(M, ks)) {
@@ -2820,7 +2828,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
       continue;
     }
     hipLaunchKernelGGL(prep_x_kernel, dim3((mp * NG4 + 3) / 4), dim3(256), 0, s, B.x, B.M, mp, K, A.kx,
-                       xslab, zslab);
+                       dh::big_qpb(A.half_pairs, mt), xslab, zslab);
     if ((e = hipGetLastError()) != hipSuccess)
       return dh::fail(DH_EHIP, "prep_x_kernel: %s", hipGetErrorString(e));
     const BigArgs BA{B, xslab, zslab};
@@ -3079,8 +3087,8 @@ int draft_head_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, i
 namespace {
 
 // One call: coarse launch(es), then rerank + argmax on the rows src describes.
-// int4: the coarse head is a 4-bit one in its 2K-long 2-bit form (x is read
-// twice over); the rerank reads rows of length K as always.
+// int4: the coarse head is a 4-bit one in the tiles of a 2-bit head of
+// length 2K (draft_head_tile_int4); the rerank reads rows of length K as always.
 int validate_forward(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
                      const RowSrc& src, int kcand, int R, const float* cand_val, const int32_t* cand_id,
                      const int32_t* rr_id, const float* rr_val, const int32_t* out_id, const float* out_val,

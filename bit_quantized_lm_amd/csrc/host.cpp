@@ -288,7 +288,7 @@ int draft_head_tile_int4(const uint8_t* packed4, const uint16_t* S, const uint16
   if (!packed4 || !S || !ZS || !tiled || !pairs) return dh::fail(DH_EINVAL, "tile_int4: null pointer");
   int rc = check_shape4(N, K);
   if (rc) return rc;
-  const int64_t H = K / 2, NG = K / DH_GROUP, NG4 = K / 256;   // NG4: byte groups of the 2K-long form
+  const int64_t H = K / 2, NG = K / DH_GROUP, NG4 = K / 256;   // NG4: byte groups of 128 bytes a row
   rc = check_pairs(S, ZS, N * NG, NG);
   if (rc) return rc;
   const int64_t nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
@@ -298,19 +298,13 @@ int draft_head_tile_int4(const uint8_t* packed4, const uint16_t* S, const uint16
         const int64_t n = b * DH_BLOCK_N + col;
         const bool valid = n < N;
         const int64_t t = col / 16, c = col % 16;
-        // the bytes of the 2K-long form (draft_head_int4_as_int2's shuffle),
-        // placed as draft_head_tile places a 2-bit head of length 2K
+        // the head's own bytes, placed as draft_head_tile places a 2-bit head
+        // of length 2K (the same byte count)
         for (int64_t j = 0; j < H; ++j) {
-          uint8_t v = 0;
-          if (valid) {
-            const uint32_t b4 = packed4[n * H + j], lo = b4 & 15u, hi = b4 >> 4;
-            v = static_cast<uint8_t>((lo >> 2) | ((hi >> 2) << 2) | ((lo & 3u) << 4) | ((hi & 3u) << 6));
-          }
           const int64_t G = j / 128, h = (j % 128) / 64, s = (j % 64) / 16, wb = j % 16;
-          tiled[((((b * NG4 + G) * 2 + h) * 4 + t) * 64 + s * 16 + c) * 16 + wb] = v;
+          tiled[((((b * NG4 + G) * 2 + h) * 4 + t) * 64 + s * 16 + c) * 16 + wb] = valid ? packed4[n * H + j] : 0;
         }
-        // pairs of quarters 0 and 1 of each byte group (the head's own groups);
-        // quarters 2 and 3 carry (S/4, S/4), which the kernels derive
+        // pairs of quarters 0 and 1 of each byte group: nibble q's groups
         for (int64_t g = 0; g < NG; ++g) {
           const int64_t q = g / NG4, G = g % NG4;
           pairs[((b * NG4 + G) * 4 + t) * 32 + c * 2 + q] =

@@ -13,8 +13,18 @@ constexpr int kMaxMT = 5;            // 16-row tiles per launch (80 rows)
 constexpr int kCodeChunks = 9;       // 1 KB chunks of one block's byte group: 8 code + 1 pair
 constexpr int kZpEntries = 256;      // zero-point slab entries (16 bytes)
 
-template <int MT>
+// Groups of 128 k a byte group of the many-row kernel holds: a 2-bit head's
+// four quarters; a 4-bit head's two halves (the code of k in one nibble, of
+// K/2 + k in the other) from three row tiles on.  With one or two row tiles
+// a 4-bit head keeps the 2-bit head's four stages per byte group, the last
+// two without codes, so that its codes, in the single code slot there, have
+// three stages to arrive instead of one.
+constexpr int big_qpb(bool half, int MT) { return half && MT >= 3 ? 2 : 4; }
+
+template <int MT_, int QPB_ = 4>
 struct BigShape {
+  static constexpr int MT = MT_;                    // 16-row tiles
+  static constexpr int QPB = QPB_;                  // groups per byte group
   static constexpr int WPB = MT >= 3 ? 2 : 1;       // waves per block
   static constexpr int BPW = 4;                     // blocks per workgroup
   static constexpr int NTW = 4 / WPB;               // column tiles per wave
@@ -31,11 +41,25 @@ struct BigShape {
   // schedule and of the barriers) is two groups, so the eight waves meet at
   // half as many barriers; below, a stage is one group.  XD and XW count stages.
   static constexpr int GPS = MT >= 4 ? 2 : 1;       // groups per stage
-  static constexpr int SPB = 4 / GPS;               // stages per byte group
+  static constexpr int SPB = QPB / GPS;             // stages per byte group: 4, 2 or 1
   static constexpr int XD = MT >= 4 ? 1 : MT == 3 ? 5 : MT == 2 ? 3 : 6;
   static constexpr int CD = MT <= 2 ? 1 : 2;
   static constexpr int XW = XD >= 4 ? 2 : 1;        // stage's slabs completed XW stages ahead
-  static constexpr int PRO = XD > SPB * CD - 1 ? XD : SPB * CD - 1;   // prologue stages
+  // Byte ops (zero-point slab, codes and pairs) are issued at the stages with
+  // j mod SPB == BYTE, right after a barrier that every wave passes holding
+  // the codes it read from the slot they refill.  With several stages per
+  // byte group that is the barrier after the byte group's first stage, and
+  // the codes of byte group G + CD go into the slot of G.  With one stage per
+  // byte group it is the barrier that ended the previous byte group: the
+  // codes of G + CD - 1 go into the slot of G - 1 (LAG = 1), and the
+  // zero-point slab, read at the start of each byte group, has two slots.
+  static constexpr int BYTE = 1 % SPB;
+  static constexpr int LAG = SPB == 1 ? 1 : 0;
+  static constexpr int ZPS = SPB == 1 ? 2 : 1;      // zero-point slots
+  // prologue stages: the x slabs of stages 0 .. XD - 1 and the codes of byte
+  // groups 0 .. CD - LAG - 1 (issued at stage SPB (G - CD + LAG) + BYTE)
+  static constexpr int PRO_C = SPB * (CD - LAG) - BYTE;
+  static constexpr int PRO = XD > PRO_C ? XD : PRO_C;
   // DMA ops per iteration of a wave of part p.  With two waves per block the
   // parts issue different streams: part 1 the x slabs (chunks lb + BPW k),
   // part 0 its block's codes and scale pairs and its share of the zero-point
@@ -48,23 +72,33 @@ struct BigShape {
   static constexpr int nb(int p) { return p == 0 ? 4 / BPW : 0; }
 };
 
-constexpr size_t big_lds_bytes(int MT, int XD, int CD, int BPW, int GPS) {
-  return (size_t)(XD + 1) * GPS * 4096 * MT + (size_t)CD * BPW * kCodeChunks * 1024 + (size_t)kZpEntries * 16;
+template <class S>
+constexpr size_t big_lds_bytes() {
+  return (size_t)(S::XD + 1) * S::GPS * 4096 * S::MT + (size_t)S::CD * S::BPW * kCodeChunks * 1024 +
+         (size_t)S::ZPS * kZpEntries * 16;
 }
+
+// floor(j / SPB) for any stage j (the prologue's are negative)
+template <class S>
+constexpr int stage_byte_group(int j) {
+  return j >= 0 ? j / S::SPB : -((-j + S::SPB - 1) / S::SPB);
+}
+template <class S>
+constexpr int stage_mod(int j) { return j - S::SPB * stage_byte_group<S>(j); }
 
 // One stage's x-slab ops: stage j fetches the slabs of stage gx = j + XD into
 // slot gx mod NBUF; before the start (gx < 0, prologue) a slot's first stage,
 // which that slot receives again later.  Op k of a wave of block lb is chunk
 // c = lb + BPW k of the stage's GPS slabs: slab t = c / (4 MT), chunk cc.
+// NGRP: the slabs (groups) of the row, QPB per byte group.
 struct XOp {
   int slab;    // source slab (group) index, clamped to the last group
   int chunk;   // 1 KB chunk of the slab (64 entries of 16 bytes)
   int dst;     // destination: 1 KB chunk index in the x ring
 };
-template <int MT>
+template <class S>
 constexpr XOp x_op(int j, int lb, int k, int NGRP) {
-  using S = BigShape<MT>;
-  constexpr int NBUF = S::XD + 1;
+  constexpr int NBUF = S::XD + 1, MT = S::MT;
   int gx = j + S::XD;
   if (gx < 0) gx = (gx % NBUF + NBUF) % NBUF;
   const int xslot = gx % NBUF;
@@ -73,46 +107,45 @@ constexpr XOp x_op(int j, int lb, int k, int NGRP) {
   return XOp{g, cc, (xslot * S::GPS + t) * 4 * MT + cc};
 }
 
-// Whether stage j issues the byte-group ops (zero-point slab, then codes):
-// the second stage of a byte group, after every wave read that byte group's
-// codes.
-template <int MT>
+// Whether stage j issues the byte-group ops (zero-point slab, then codes).
+template <class S>
 constexpr bool stage_has_byte_ops(int j) {
-  using S = BigShape<MT>;
-  return (j & (S::SPB - 1)) == 1 % S::SPB;
+  return stage_mod<S>(j) == S::BYTE;
 }
-template <int MT>
-constexpr int stage_byte_group(int j) {   // floor(j / SPB)
-  using S = BigShape<MT>;
-  return j >> (S::SPB == 4 ? 2 : S::SPB == 2 ? 1 : 0);
-}
-// Byte group whose zero-point slab stage j fetches (the next one, clamped).
-template <int MT>
+// Byte group whose zero-point slab stage j fetches (the next one, clamped),
+// and its slot.
+template <class S>
 constexpr int zp_group(int j, int NG4) {
-  const int GB = stage_byte_group<MT>(j) + 1;
+  const int GB = stage_byte_group<S>(j) + 1;
   return GB < 0 ? 0 : GB < NG4 ? GB : NG4 - 1;
 }
-// Byte group whose codes stage j fetches (CD ahead, clamped) and its slot.
-template <int MT>
-constexpr int code_slot(int j) {
-  return (stage_byte_group<MT>(j) + BigShape<MT>::CD) % BigShape<MT>::CD;
+template <class S>
+constexpr int zp_slot(int j) {
+  return ((stage_byte_group<S>(j) + 1) % S::ZPS + S::ZPS) % S::ZPS;
 }
-template <int MT>
+// Byte group whose codes stage j fetches (CD - LAG ahead, clamped: a
+// prologue stage before the first byte group's fetches byte group 0 into a
+// slot that receives its own byte group later) and its slot.
+template <class S>
+constexpr int code_slot(int j) {
+  return ((stage_byte_group<S>(j) + S::CD - S::LAG) % S::CD + S::CD) % S::CD;
+}
+template <class S>
 constexpr int code_group(int j, int NG4) {
-  const int GC = stage_byte_group<MT>(j) + BigShape<MT>::CD;
-  return GC < NG4 ? GC : NG4 - 1;
+  const int GC = stage_byte_group<S>(j) + S::CD - S::LAG;
+  return GC < 0 ? 0 : GC < NG4 ? GC : NG4 - 1;
 }
 
 // Ops a wave of part P may leave outstanding at the end of a stage with
 // j mod SPB == Q: those issued after X(j + XW) and, for the byte group's last
-// stage (Q == SPB - 1), after the B and C of the next byte group (issued at
-// j + 2 - SPB and j + 2 - SPB CD).  The prologue's final wait (X(XW - 1),
-// C(0), B(0)) is the Q == SPB - 1 case.
-template <int MT, int P>
+// stage (Q == SPB - 1), after the zero-point slab and the codes of the next
+// byte group, issued at stages Q + 1 - SPB + BYTE and that plus
+// SPB (1 - CD + LAG) (relative to j - Q).  The prologue's final wait
+// (X(XW - 1), codes and zero-point slab of byte group 0) is the
+// Q == SPB - 1 case.
+template <class S, int P>
 constexpr int big_wait(int Q) {
-  using S = BigShape<MT>;
-  auto m4 = [](int j) { return ((j % S::SPB) + S::SPB) % S::SPB; };
-  auto cb = [&](int j) { return m4(j) == 1 % S::SPB ? S::nc(P) + S::nb(P) : 0; };
+  auto cb = [&](int j) { return stage_mod<S>(j) == S::BYTE ? S::nc(P) + S::nb(P) : 0; };
   auto ops = [&](int j) { return S::nx(P) + cb(j); };
   auto after = [&](int j0, int in_iter) {   // ops after one issued in iteration j0
     int n = in_iter;
@@ -123,8 +156,9 @@ constexpr int big_wait(int Q) {
   auto take = [&](int n) { best = n < best ? n : best; };
   if (S::nx(P)) take(after(Q + S::XW - S::XD, cb(Q + S::XW - S::XD)));
   if (Q == S::SPB - 1) {
-    if (S::nc(P)) take(after(Q + 2 - S::SPB * S::CD, 0));   // C last in its stage
-    if (S::nb(P)) take(after(Q + 2 - S::SPB, S::nc(P)));     // B followed by that stage's C
+    const int jb = Q + 1 - S::SPB + S::BYTE;                       // the zero-point slab's stage
+    if (S::nc(P)) take(after(jb + S::SPB * (1 - S::CD + S::LAG), 0));   // codes: last in their stage
+    if (S::nb(P)) take(after(jb, S::nc(P)));                       // followed by that stage's codes
   }
   return best < 63 ? best : 63;   // 63: nothing this iteration must complete
 }

@@ -148,14 +148,16 @@ int draft_head_int4_as_int2(const uint8_t* packed4, const uint16_t* S, const uin
 
 /*
  * HOST.  The device form of a 4-bit head, which draft_head_coarse_int4 and
- * draft_head_forward_int4 take: tiled holds exactly the codes of
- * draft_head_tile(draft_head_int4_as_int2(...), N, 2K) (NBLK*64 * K/2 bytes);
- * pairs holds only the head's own (S, ZS), NBLK*64 * K/128 entries (half of
- * that form's), laid out as quarters 0 and 1 of each 2K-form byte group:
+ * draft_head_forward_int4 take: the page's own code bytes (byte j: the code
+ * of k = j in bits 0-3, of K/2 + j in bits 4-7), placed as draft_head_tile
+ * places a 2-bit head of length 2K, whose bytes have the same count
+ * (tiled = draft_head_tile(packed4 as [N][2K/4], N, 2K)'s codes, NBLK*64 *
+ * K/2 bytes); quarter q < 2 of that form covers the k of nibble q.  pairs
+ * holds the head's own (S, ZS), NBLK*64 * K/128 entries, in the slots of
+ * quarters 0 and 1 of each byte group of that form:
  *   pairs[((b*NG4 + G)*4 + t)*32 + c*2 + q] = S | ZS << 16 of column
  *   64b + 16t + c, group q*NG4 + G   (NG4 = K/256, q = 0, 1)
- * The kernels form the pairs of quarters 2 and 3, (S/4, S/4), themselves, so
- * a call streams N*K/2 code bytes and N*K/128 pairs, the 4-bit head's size.
+ * A call streams N*K/2 code bytes and N*K/128 pairs, the 4-bit head's size.
  *   packed4, S, ZS  draft_head_quantize_pack_int4's arrays;  tiled, pairs  out
  * Limits and errors: as draft_head_quantize_pack_int4 and draft_head_tile.
  */
@@ -339,10 +341,10 @@ int draft_head_forward_nvfp4(const void* x, int M, int K, int N, const uint8_t* 
 /*
  * DEVICE.  draft_head_coarse and draft_head_forward for a 4-bit head (the
  * page's BITS = 4 configuration, KCAND = 1 in its measurements): tiled and
- * pairs are draft_head_tile_int4's, the 2-bit form of length 2K with the
- * head's own pairs, which the coarse kernels run with x read twice over
- * (x' = (x, x)); x, w and everything else are as for the 2-bit calls with K
- * the head's own length.  The workspace is draft_head_workspace_bytes(M, 2K).
+ * pairs are draft_head_tile_int4's, which the coarse kernels run in the
+ * tiles of a 2-bit head of length 2K, each byte's two codes decoded whole;
+ * x, w and everything else are as for the 2-bit calls with K the head's own
+ * length.  The workspace is draft_head_workspace_bytes(M, 2K).
  * Limits: K a positive multiple of 256 with 2K <= DH_MAX_K.
  * Errors: as draft_head_coarse / draft_head_forward.
  */

@@ -1,10 +1,11 @@
-// Host check of the many-row coarse kernel's DMA ring schedule (ring_plan.h):
-// for every row-tile count, every row length K the kernel takes up to 40960,
-// every wave part and block and every stage, each DMA op must read inside its
-// source buffer and write inside its LDS ring, the LDS must fit, and every
-// wait count must complete the ops the next stage reads (counted here op by
+// Host check of the many-row coarse kernels' DMA ring schedules (ring_plan.h):
+// for every row-tile count, every row length the kernel takes up to 40960,
+// every wave and every stage, each DMA op must read inside its source buffer
+// and write inside its LDS ring, the LDS must fit, and every LDS read must
+// find its data in place and not rewritten while it is read (simulated op by
 // op, independently of big_wait's closed form).  Exit status 0 = all hold.
 #include <cstdio>
+#include <utility>
 #include <vector>
 
 #include "../bit_quantized_lm_amd/csrc/ring_plan.h"
@@ -20,91 +21,122 @@ static int failures = 0;
     }                                                 \
   } while (0)
 
-template <int MT>
-void check_shape() {
-  using S = BigShape<MT>;
-  constexpr int NBUF = S::XD + 1, SPB = S::SPB;
-  const size_t lds = big_lds_bytes(MT, S::XD, S::CD, S::BPW, S::GPS);
-  CHECK(lds <= 160 * 1024, "MT %d: LDS %zu\n", MT, lds);
-  CHECK((size_t)S::BPW * 16 * MT * 68 * 4 <= lds, "MT %d: score area\n", MT);
-  CHECK(S::W * 64 <= 1024 && S::GPS * SPB == 4, "MT %d: shape\n", MT);
-  // ops a wave of part P issues in stage j (x first, then zero-point, then codes)
-  auto ops = [&](int P, int j) {
-    return S::nx(P) + (stage_has_byte_ops<MT>(j) ? S::nb(P) + S::nc(P) : 0);
+// The many-row kernel's schedule for one shape S and one row length (NG4
+// byte groups), simulated op by op.  Every wave (part P, block lb) issues its
+// ops of each stage in order; the prologue's stages -PRO .. -1 end with one
+// wait and a barrier, every main stage with the wait big_wait(j mod SPB) and
+// a barrier.  A wait completes all but the last n of the wave's ops; an op
+// may land at any time between its issue and the wait that completes it.
+// Every LDS chunk is written by one wave only.  A read of chunk T expecting
+// data d during stages r0 .. r1 (after the barrier that ends stage r0 - 1)
+// holds when the last op into T issued before stage r0 carries d and is
+// complete at that barrier, and no op into T with other data is issued in
+// stages r0 .. r1.  The reads: stage r reads the GPS x slabs of its groups
+// (the first of them from stage r - 1 on when XW = 2: the next stage's first
+// fragments are read before the barrier); the first stage of byte group G
+// reads the codes and pairs of every block and the zero-point slab of G.
+struct SimOp {
+  int stage, data, done;   // done: the barrier (end of stage) completing it, or INT_MAX
+};
+template <class S>
+void check_big_k(int NG4) {
+  constexpr int NBUF = S::XD + 1, SPB = S::SPB, MT = S::MT;
+  const int NGRP = S::QPB * NG4, NST = SPB * NG4;
+  // LDS chunk ids: x ring, then codes [slot][block][chunk], then zero point [slot][chunk]
+  const int nx_chunks = NBUF * S::GPS * 4 * MT, ncode = S::CD * S::BPW * kCodeChunks;
+  const int T_CODE = nx_chunks, T_ZP = nx_chunks + ncode, NT = T_ZP + S::ZPS * 4;
+  std::vector<std::vector<SimOp>> tgt(NT);
+  std::vector<int> writer(NT, -1);
+  struct WaveState {
+    std::vector<std::pair<int, int>> ops;   // (target, index in tgt[target])
+    size_t done = 0;
   };
-  auto ops_after = [&](int P, int s0, int after_in_s0, int s1) {   // after an op of stage s0, to the end of s1
-    int n = after_in_s0;
-    for (int s = s0 + 1; s <= s1; ++s) n += ops(P, s);
-    return n;
+  std::vector<WaveState> waves(S::WPB * S::BPW);
+  auto issue = [&](int wid, int j, int T, int data) {
+    CHECK(T >= 0 && T < NT, "%d/%d NG4 %d: target %d\n", MT, S::QPB, NG4, T);
+    if (T < 0 || T >= NT) return;
+    CHECK(writer[T] < 0 || writer[T] == wid, "%d/%d: chunk %d written by two waves\n", MT, S::QPB, T);
+    writer[T] = wid;
+    tgt[T].push_back({j, data, 1 << 30});
+    waves[wid].ops.push_back({T, (int)tgt[T].size() - 1});
   };
-  for (int P = 0; P < S::WPB; ++P) {
-    for (int Q = 0; Q < SPB; ++Q) {
-      const int w = P == 0 ? big_wait<MT, 0>(Q) : big_wait<MT, 1>(Q);
-      CHECK(w >= 0 && w <= 63, "MT %d P %d: wait %d\n", MT, P, w);
+  auto wait = [&](int wid, int n, int j) {
+    WaveState& w = waves[wid];
+    for (; w.done + n < w.ops.size(); ++w.done) tgt[w.ops[w.done].first][w.ops[w.done].second].done = j;
+  };
+  auto read = [&](int T, int data, int r0, int r1, const char* what) {
+    const std::vector<SimOp>& v = tgt[T];
+    int last = -1;
+    for (int i = 0; i < (int)v.size(); ++i) {
+      if (v[i].stage < r0) last = i;
+      else if (v[i].stage <= r1)
+        CHECK(v[i].data == data, "%d/%d NG4 %d: %s chunk %d rewritten at stage %d while read in %d..%d\n", MT,
+              S::QPB, NG4, what, T, v[i].stage, r0, r1);
     }
-  }
-  for (int K = 512; K <= 40960; K += 512) {
-    const int NG4 = K / 512, NGRP = K / 128, NST = SPB * NG4;
-    for (int P = 0; P < S::WPB; ++P) {
-      auto wait_at = [&](int j) {   // the count waited for at the end of stage j
-        const int Q = ((j % SPB) + SPB) % SPB;
-        return P == 0 ? big_wait<MT, 0>(Q) : big_wait<MT, 1>(Q);
-      };
+    CHECK(last >= 0 && v[last].data == data && v[last].done <= r0 - 1,
+          "%d/%d NG4 %d: %s chunk %d (data %d) not in place for stages %d..%d\n", MT, S::QPB, NG4, what, T, data, r0,
+          r1);
+  };
+  auto issue_stage = [&](int j) {
+    for (int P = 0; P < S::WPB; ++P)
       for (int lb = 0; lb < S::BPW; ++lb) {
-        for (int j = -S::PRO; j < NST; ++j) {
-          for (int k = 0; k < S::nx(P); ++k) {
-            const XOp o = x_op<MT>(j, lb, k, NGRP);
-            CHECK(o.slab >= 0 && o.slab < NGRP && o.chunk >= 0 && o.chunk < 4 * MT && o.dst >= 0 &&
-                      o.dst < NBUF * S::GPS * 4 * MT,
-                  "MT %d K %d P %d lb %d j %d k %d: x op slab %d chunk %d dst %d\n", MT, K, P, lb, j, k, o.slab,
-                  o.chunk, o.dst);
+        const int wid = P * S::BPW + lb;
+        for (int k = 0; k < S::nx(P); ++k) {
+          const XOp o = x_op<S>(j, lb, k, NGRP);
+          CHECK(o.slab >= 0 && o.slab < NGRP && o.chunk >= 0 && o.chunk < 4 * MT,
+                "%d/%d NG4 %d j %d: x op slab %d chunk %d\n", MT, S::QPB, NG4, j, o.slab, o.chunk);
+          issue(wid, j, o.dst, o.slab * 64 + o.chunk);
+        }
+        if (stage_has_byte_ops<S>(j)) {
+          const int GB = zp_group<S>(j, NG4), GC = code_group<S>(j, NG4), cs = code_slot<S>(j), zs = zp_slot<S>(j);
+          CHECK(GB >= 0 && GB < NG4 && GC >= 0 && GC < NG4 && cs >= 0 && cs < S::CD && zs >= 0 && zs < S::ZPS,
+                "%d/%d NG4 %d j %d: byte ops GB %d GC %d slots %d %d\n", MT, S::QPB, NG4, j, GB, GC, cs, zs);
+          for (int k = 0; k < S::nb(P); ++k) {
+            const int c = lb * S::nb(P) + k;
+            CHECK(c < 4, "%d/%d: zero-point chunk %d\n", MT, S::QPB, c);
+            issue(wid, j, T_ZP + zs * 4 + c, GB * 4 + c);
           }
-          if (stage_has_byte_ops<MT>(j)) {
-            const int GB = zp_group<MT>(j, NG4), GC = code_group<MT>(j, NG4), cs = code_slot<MT>(j);
-            CHECK(GB >= 0 && GB < NG4 && GC >= 0 && GC < NG4 && cs >= 0 && cs < S::CD,
-                  "MT %d K %d j %d: byte ops GB %d GC %d slot %d\n", MT, K, j, GB, GC, cs);
-            for (int k = 0; k < S::nb(P); ++k) CHECK(lb * S::nb(P) + k < 4, "MT %d: zero-point chunk\n", MT);
-          }
+          for (int k = 0; k < S::nc(P); ++k) issue(wid, j, T_CODE + (cs * S::BPW + lb) * kCodeChunks + k, GC * 16 + k);
         }
       }
-      // stage j reads its slabs from slot j mod NBUF: they were fetched by
-      // stage j - XD and completed by the wait at the end of stage j - XW
-      if (S::nx(P)) {
-        for (int j = 0; j < NST; ++j) {
-          const int s = j - S::XD;
-          if (s < -S::PRO) continue;
-          const int after = stage_has_byte_ops<MT>(s) ? S::nb(P) + S::nc(P) : 0;
-          const int need = ops_after(P, s, after, j - S::XW);
-          CHECK(wait_at(j - S::XW) <= need, "MT %d K %d P %d: slabs of stage %d not waited for\n", MT, K, P, j);
-          for (int t = 0; t < S::GPS; ++t) {   // the slot holds stage j when it is read
-            const XOp o = x_op<MT>(s, 0, t * 4 * MT / S::BPW, NGRP);
-            CHECK(o.dst / (4 * MT) == (j % NBUF) * S::GPS + t, "MT %d: slot of stage %d\n", MT, j);
-          }
-          for (int s2 = s + 1; s2 <= j; ++s2) {   // nothing else lands in that slot before it is read
-            const XOp o = x_op<MT>(s2, 0, 0, NGRP);
-            CHECK(o.dst / (4 * MT) / S::GPS != j % NBUF, "MT %d: slot of stage %d overwritten at %d\n", MT, j, s2);
-          }
-        }
-      }
-      // byte group G + 1's codes and zero-point slab complete at the end of
-      // byte group G (its last stage)
-      for (int G = 0; G + 1 < NG4; ++G) {
-        const int end = SPB * G + SPB - 1;
-        if (S::nc(P)) {
-          const int sc = SPB * (G + 1 - S::CD) + 1;
-          CHECK(code_group<MT>(sc, NG4) == G + 1 && stage_has_byte_ops<MT>(sc), "MT %d: code stage\n", MT);
-          if (sc >= -S::PRO) CHECK(wait_at(end) <= ops_after(P, sc, 0, end), "MT %d K %d: codes of %d\n", MT, K, G + 1);
-        }
-        if (S::nb(P)) {
-          const int sb = SPB * G + 1;
-          CHECK(zp_group<MT>(sb, NG4) == G + 1, "MT %d: zero-point stage\n", MT);
-          CHECK(wait_at(end) <= ops_after(P, sb, S::nc(P), end), "MT %d K %d: zero point of %d\n", MT, K, G + 1);
-        }
-      }
-    }
+  };
+  auto wait_stage = [&](int j, int Q) {
+    for (int P = 0; P < S::WPB; ++P)
+      for (int lb = 0; lb < S::BPW; ++lb) wait(P * S::BPW + lb, P == 0 ? big_wait<S, 0>(Q) : big_wait<S, 1>(Q), j);
+  };
+  for (int j = -S::PRO; j < 0; ++j) issue_stage(j);
+  wait_stage(-1, SPB - 1);
+  for (int j = 0; j < NST; ++j) {
+    issue_stage(j);
+    wait_stage(j, j % SPB);
   }
+  // the reads, checked against the whole history (a read looks only at the
+  // ops issued up to the end of its window, and at the barrier before it)
+  for (int G = 0; G < NG4; ++G) {   // byte group G's codes, pairs and zero-point slab, read at its start
+    const int j = SPB * G;
+    for (int lb = 0; lb < S::BPW; ++lb)
+      for (int k = 0; k < kCodeChunks; ++k)
+        read(T_CODE + ((G % S::CD) * S::BPW + lb) * kCodeChunks + k, G * 16 + k, j, j, "code");
+    for (int c = 0; c < 4; ++c) read(T_ZP + (G % S::ZPS) * 4 + c, G * 4 + c, j, j, "zero-point");
+  }
+  for (int j = 0; j < NST; ++j)
+    for (int t = 0; t < S::GPS; ++t) {
+      const int r0 = t == 0 && S::XW == 2 && j > 0 ? j - 1 : j;
+      for (int cc = 0; cc < 4 * MT; ++cc)
+        read(((j % NBUF) * S::GPS + t) * 4 * MT + cc, (S::GPS * j + t) * 64 + cc, r0, j, "x");
+    }
 }
 
+template <class S>
+void check_big() {
+  const size_t lds = big_lds_bytes<S>();
+  CHECK(lds <= 160 * 1024, "%d/%d: LDS %zu\n", S::MT, S::QPB, lds);
+  CHECK((size_t)S::BPW * 16 * S::MT * 68 * 4 <= lds, "%d/%d: score area\n", S::MT, S::QPB);
+  CHECK(S::W * 64 <= 1024 && S::GPS * S::SPB == S::QPB, "%d/%d: shape\n", S::MT, S::QPB);
+  for (int Q = 0; Q < S::SPB; ++Q)
+    for (int w : {big_wait<S, 0>(Q), big_wait<S, 1>(Q)}) CHECK(w >= 0 && w <= 63, "%d/%d: wait %d\n", S::MT, S::QPB, w);
+  for (int NG4 = 1; NG4 <= 80; ++NG4) check_big_k<S>(NG4);   // row lengths up to 40960
+}
 
 // The fp16 many-row kernel's schedule (dh::h16_*), simulated op by op: every
 // wave's ops in issue order, each wait completing all but the last
@@ -199,11 +231,14 @@ void check_h16(int K) {
 }
 
 int main() {
-  check_shape<1>();
-  check_shape<2>();
-  check_shape<3>();
-  check_shape<4>();
-  check_shape<5>();
+  check_big<BigShape<1>>();
+  check_big<BigShape<2>>();
+  check_big<BigShape<3>>();
+  check_big<BigShape<4>>();
+  check_big<BigShape<5>>();
+  check_big<BigShape<3, 2>>();   // a 4-bit head's two halves per byte group
+  check_big<BigShape<4, 2>>();
+  check_big<BigShape<5, 2>>();
   for (int K = 512; K <= 16384; K += 512) {   // the fp16 kernel's row lengths
     check_h16<3>(K);
     check_h16<4>(K);

@@ -741,8 +741,8 @@ def test_nvfp4_rerank_full_shape(dev, full):
                                            (9, 1024, 3000, 1, 32), (40, 512, 2000, 1, 32), (57, 1024, 2500, 4, 32),
                                            (64, 2560, 2600, 1, 32)])
 def test_int4_parity(dev, m, k, n, kcand, r):
-    """The 4-bit head (run as its 2K-long 2-bit form) against the oracle's own
-    4-bit definition."""
+    """The 4-bit head (its own bytes, draft_head_tile_int4) against the
+    oracle's own 4-bit definition."""
     w = workload.gen_weight(n, k, seed=3000 + n)
     x = workload.gen_x(m, k, seed=3001 + n)
     _log(f"int4 case m={m} k={k} n={n} kcand={kcand} r={r}")

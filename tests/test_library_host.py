@@ -356,25 +356,36 @@ def test_int4_as_int2_is_the_same_head():
 
 
 @pytest.mark.parametrize("n,k", [(64, 256), (100, 768), (129, 1536)])
-def test_tile_int4_is_the_2k_form_with_its_own_pairs(lib, n, k):
-    """draft_head_tile_int4's codes are those of the tiled 2K-long form, and
-    its pairs are that form's quarters 0 and 1 (quarters 2 and 3 of each byte
-    group hold (S/4, S/4), which the kernels derive): N K/2 code bytes and
-    N K/128 pairs, the 4-bit head's own size."""
+def test_tile_int4_places_the_heads_own_bytes_and_pairs(lib, n, k):
+    """draft_head_tile_int4's codes are the 4-bit head's own bytes placed as
+    draft_head_tile places a 2-bit head of length 2K (same byte count), and
+    its pairs are that form's quarters 0 and 1, the head's own (S, ZS) of the
+    groups of nibbles 0 and 1: N K/2 code bytes and N K/128 pairs, the 4-bit
+    head's own size."""
     rng = np.random.default_rng(n + k)
     w = oracle.bf16.from_f32((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
-    packed4 = B.draft_head_quantize_pack_int4(w)
-    tiled4, pairs4 = B.draft_head_tile_int4(*packed4)
-    tiled2, pairs2 = B.draft_head_tile(*B.draft_head_int4_as_int2(*packed4))
+    packed4, S, ZS = B.draft_head_quantize_pack_int4(w)
+    tiled4, pairs4 = B.draft_head_tile_int4(packed4, S, ZS)
+    # draft_head_tile on the same bytes read as a 2-bit head of length 2K, with
+    # the 2K-long head's pairs (the head's own in groups < K/128)
+    _, S2, ZS2 = B.draft_head_int4_as_int2(packed4, S, ZS)
+    tiled2, pairs2 = B.draft_head_tile(packed4, S2, ZS2)
     assert np.array_equal(tiled4, tiled2)
     nblk = (n + 63) // 64
+    assert tiled4.size == nblk * 64 * k // 2
     assert pairs4.size == nblk * 64 * (k // 128) and pairs2.size == 2 * pairs4.size
     full = pairs2.reshape(nblk, k // 256, 4, 16, 4)      # [block][byte group][t][c][quarter]
     half = pairs4.reshape(nblk, k // 256, 4, 16, 2)
     assert np.array_equal(half, full[..., :2])
-    s = full[..., :2] & 0xFFFF                            # what the kernels derive for quarters 2 and 3
-    s4 = oracle.bf16.from_f32(oracle.bf16.to_f32(s.astype(np.uint16)) * np.float32(0.25)).astype(np.uint32)
-    assert np.array_equal(full[..., 2:], s4 | (s4 << 16))
+    # quarter q < 2 of byte group G is group q K/256 + G: the code of k = j in
+    # the low nibble, of K/2 + j in the high one, with the head's own pairs
+    col = np.arange(n)
+    b, t, c = col // 64, (col % 64) // 16, col % 16
+    for q in range(2):
+        for G in range(k // 256):
+            got = half[b, G, t, c, q]
+            assert np.array_equal(got & 0xFFFF, S[:, q * (k // 256) + G])
+            assert np.array_equal(got >> 16, ZS[:, q * (k // 256) + G])
 
 
 def test_int4_validation(lib):
