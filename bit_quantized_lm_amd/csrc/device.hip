@@ -1575,17 +1575,20 @@ void coarse_h16_kernel(HArgs HA) {
   // l / M, row l % M).
   u32x4* sk = reinterpret_cast<u32x4*>(smem);
   __syncthreads();
+  // masks of the live columns and rows, as bits (conditions the compiler
+  // would otherwise turn into branches around every key)
+  uint32_t colm[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) colm[t] = 0u - (uint32_t)(blk_ok & (64 * b + 16 * t + nn < A.N));
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * i + 4 * hh + r, rho = wave * MP + row;
+      const uint32_t rowm = 0u - (uint32_t)(row < A.M);
       uint32_t kk[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = 64 * b + 16 * t + nn;
-        kk[t] = f32_key_if(blk_ok && n < A.N && row < A.M, acc[i][t][r] * rs[i][r]);   // -0 as +0
-      }
+      for (int t = 0; t < 4; ++t) kk[t] = f32_key(acc[i][t][r] * rs[i][r] + 0.0f) & colm[t] & rowm;   // -0 as +0
       sk[rho * 16 + (nn ^ (row & 15))] = u32x4{kk[0], kk[1], kk[2], kk[3]};
     }
   if (wants_scores(A)) {
