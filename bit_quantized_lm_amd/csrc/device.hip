@@ -875,14 +875,15 @@ struct BigArgs {
 constexpr int kScStride = 68;
 
 // The top-kcand list (kcand <= 8) of row m, block b, selected by this thread
-// alone from the row's 64 keys in LDS: run_at(r, ch) the keys of run r with
-// their columns in the low 6 bits, key_at(c) column c's key (select8_runs;
+// alone from the row's 64 keys in LDS: load_at(r, raw) the keys of run r,
+// tag_at(r, e) 63 - the column of its element e, key_at(c) column c's key (select8_runs;
 // the run loop is rolled: the epilogue runs once per kernel, and its
 // unrolled code would mostly wait for instruction fetch).
-template <class RunAt, class KeyAt>
-__device__ __forceinline__ void emit_list8(RunAt run_at, KeyAt key_at, const CoarseArgs& A, int m, int b) {
+template <class LoadAt, class TagAt, class KeyAt>
+__device__ __forceinline__ void emit_list8(LoadAt load_at, TagAt tag_at, KeyAt key_at, const CoarseArgs& A, int m,
+                                           int b) {
   uint32_t slot[8];   // 63 - column, or 64 for an empty slot
-  dh::select8_runs<true>(run_at, key_at, slot);
+  dh::select8_runs<true>(load_at, tag_at, key_at, slot);
   float val[8];
   int32_t id[8];
 #pragma unroll
@@ -938,15 +939,15 @@ __device__ __forceinline__ void lane_select8(const uint32_t* sk, const CoarseArg
     if (b >= A.nblk) continue;
     const uint32_t* row = sk + (lb * MP + m) * kScStride;
     emit_list8(
-        [&](int r, uint32_t(&ch)[8]) {   // run r: columns 8r .. 8r + 7
+        [&](int r, uint32_t(&raw)[8]) {   // run r: columns 8r .. 8r + 7
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(row + 8 * r + 4 * h);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ch[4 * h + e] = (v[e] & ~63u) | (uint32_t)(63 - 8 * r - 4 * h - e);
+            for (int e = 0; e < 4; ++e) raw[4 * h + e] = v[e];
           }
         },
-        [&](int c) { return row[c]; }, A, m, b);
+        [](int r, int e) { return 63 - 8 * r - e; }, [&](int c) { return row[c]; }, A, m, b);
   }
 }
 
@@ -1609,15 +1610,15 @@ void coarse_h16_kernel(HArgs HA) {
     const u32x4* row = sk + (lb * MP + m) * 16;
     const int sw = m & 15;
     emit_list8(
-        [&](int r, uint32_t(&ch)[8]) {   // run r: pieces 2r and 2r + 1 (columns g, g + 16, g + 32, g + 48)
+        [&](int r, uint32_t(&raw)[8]) {   // run r: pieces 2r and 2r + 1 (columns g, g + 16, g + 32, g + 48)
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int g = 2 * r + h;
-            const u32x4 v = row[g ^ sw];
+            const u32x4 v = row[(2 * r + h) ^ sw];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) ch[4 * h + t] = (v[t] & ~63u) | (uint32_t)(63 - 16 * t - g);
+            for (int t = 0; t < 4; ++t) raw[4 * h + t] = v[t];
           }
         },
+        [](int r, int e) { return 63 - 16 * (e & 3) - 2 * r - (e >> 2); },
         [&](int c) { return reinterpret_cast<const uint32_t*>(row + ((c & 15) ^ sw))[c >> 4]; }, A, m, bq);
   }
 }

@@ -36,9 +36,9 @@ constexpr void bitonic8_desc(uint32_t (&v)[8]) {
 }
 
 // The eight best of a row of 64 keys taken as eight runs of eight.
-// run_at(r, ch) fills ch[0..7] with the keys of run r (each column once over
-// the eight runs), each key's low 6 bits already replaced by 63 - its column;
-// key_at(c) is column c's full key, for the rebuild's loop over a run-time
+// load_at(r, raw) fills raw[0..7] with the keys of run r (each column once
+// over the eight runs) and tag_at(r, e) is 63 - the column of element e of
+// run r; key_at(c) is column c's key, for the rebuild's loop over a run-time
 // column.  slot[i] receives 63 - column of the i-th best (score desc, column
 // asc), or 64 where fewer than i + 1 columns exist.
 //
@@ -52,13 +52,13 @@ constexpr void bitonic8_desc(uint32_t (&v)[8]) {
 // other); such a list is rebuilt with 64-bit keys (full key, then 63 -
 // column) over the columns whose keys reach the eighth's upper bits.
 // kRolled: the run loop is not unrolled (small code, for an epilogue that
-// runs once per kernel and would otherwise wait on instruction fetch).
-template <bool kRolled, class RunAt, class KeyAt>
-constexpr void select8_runs(RunAt run_at, KeyAt key_at, uint32_t (&slot)[8]) {
+// runs once per kernel and would otherwise wait on instruction fetch), and
+// run r + 1 is loaded before run r is merged, so that its loads (from LDS in
+// the kernel) are in flight during the merge.
+template <bool kRolled, class LoadAt, class TagAt, class KeyAt>
+constexpr void select8_runs(LoadAt load_at, TagAt tag_at, KeyAt key_at, uint32_t (&slot)[8]) {
   uint32_t run[8] = {}, ninth = 0u;   // merging into zeros keeps the first run as it is
-  auto merge = [&](int r) {
-    uint32_t ch[8] = {};
-    run_at(r, ch);
+  auto merge = [&](uint32_t(&ch)[8]) {
     sort8_desc(ch);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -68,12 +68,28 @@ constexpr void select8_runs(RunAt run_at, KeyAt key_at, uint32_t (&slot)[8]) {
     }
     bitonic8_desc(run);
   };
+  auto tagged = [&](int r, const uint32_t(&raw)[8], uint32_t(&ch)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ch[e] = (raw[e] & ~63u) | (uint32_t)tag_at(r, e);
+  };
   if constexpr (kRolled) {
+    uint32_t raw[8] = {};
+    load_at(0, raw);
 #pragma unroll 1
-    for (int r = 0; r < 8; ++r) merge(r);
+    for (int r = 0; r < 8; ++r) {
+      uint32_t ch[8] = {};
+      tagged(r, raw, ch);
+      load_at(r < 7 ? r + 1 : 7, raw);   // the last iteration reads run 7 again, unused
+      merge(ch);
+    }
   } else {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) merge(r);
+    for (int r = 0; r < 8; ++r) {
+      uint32_t raw[8] = {}, ch[8] = {};
+      load_at(r, raw);
+      tagged(r, raw, ch);
+      merge(ch);
+    }
   }
   // exact unless upper parts agree where the order or the cut depends on them
   const uint32_t p8 = run[7] >> 6;
@@ -109,11 +125,11 @@ constexpr void select8_runs(RunAt run_at, KeyAt key_at, uint32_t (&slot)[8]) {
 template <class KeyAt>
 constexpr void select8_row(const uint32_t (&key)[64], KeyAt key_at, uint32_t (&slot)[8]) {
   select8_runs<false>(
-      [&](int r, uint32_t(&ch)[8]) {
+      [&](int r, uint32_t(&raw)[8]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ch[e] = (key[8 * r + e] & ~63u) | (uint32_t)(63 - 8 * r - e);
+        for (int e = 0; e < 8; ++e) raw[e] = key[8 * r + e];
       },
-      key_at, slot);
+      [](int r, int e) { return 63 - 8 * r - e; }, key_at, slot);
 }
 
 }  // namespace dh

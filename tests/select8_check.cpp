@@ -49,14 +49,12 @@ int main() {
     dh::select8_row(key, [&](int c) { return key[c]; }, slot);
     // the rolled form over runs of non-consecutive columns (the fp16 kernel's
     // LDS pieces: run r = columns g, g + 16, g + 32, g + 48 for g = 2r, 2r + 1)
+    auto col_of = [](int r, int e) { return 16 * (e & 3) + 2 * r + (e >> 2); };
     dh::select8_runs<true>(
-        [&](int r, uint32_t(&ch)[8]) {
-          for (int e = 0; e < 8; ++e) {
-            const int g = 2 * r + (e >> 2), col = 16 * (e & 3) + g;
-            ch[e] = (key[col] & ~63u) | (uint32_t)(63 - col);
-          }
+        [&](int r, uint32_t(&raw)[8]) {
+          for (int e = 0; e < 8; ++e) raw[e] = key[col_of(r, e)];
         },
-        [&](int c) { return key[c]; }, slot2);
+        [&](int r, int e) { return 63 - col_of(r, e); }, [&](int c) { return key[c]; }, slot2);
     std::vector<int> cols;
     for (int c = 0; c < 64; ++c)
       if (key[c]) cols.push_back(c);
