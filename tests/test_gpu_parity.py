@@ -739,7 +739,12 @@ def test_nvfp4_rerank_full_shape(dev, full):
                                            (20, 512, 3000, 1, 16), (5, 2048, 5000, 4, 32), (72, 1024, 2100, 1, 32),
                                            # every row-tile count of the many-row kernel's 4-bit form
                                            (9, 1024, 3000, 1, 32), (40, 512, 2000, 1, 32), (57, 1024, 2500, 4, 32),
-                                           (64, 2560, 2600, 1, 32)])
+                                           (64, 2560, 2600, 1, 32),
+                                           # one byte group (K = 256) with two groups a byte group: three,
+                                           # four and five row tiles (one stage a byte group at four and five)
+                                           (33, 256, 1500, 1, 16), (49, 256, 1500, 2, 32), (80, 256, 1100, 1, 16),
+                                           # two byte groups at five row tiles, ragged N
+                                           (75, 512, 1333, 8, 32)])
 def test_int4_parity(dev, m, k, n, kcand, r):
     """The 4-bit head (its own bytes, draft_head_tile_int4) against the
     oracle's own 4-bit definition."""
