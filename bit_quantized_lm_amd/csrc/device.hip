@@ -94,15 +94,16 @@ __device__ __forceinline__ uint32_t scale_x_pair(uint32_t w) {
 // ---------------------------------------------------------------------------
 // Coarse pass building blocks.
 //
-// A wave owns one 64-column block b and computes its coarse scores for up to
-// 16*MT rows with bf16 MFMA 16x16x32: the A operand is x (rows), the B operand
-// the decoded weight (1 + v/4), one 16-column tile per MFMA, four tiles per
-// block.  Lane (hh, nn) = (lane / 16, lane % 16) supplies row nn of A and
-// column nn of B for k-slots 8hh..8hh+7; the accumulator holds rows 4hh + r,
-// column nn.  K is walked as groups (byte group G, quarter q): code byte j of
-// byte group G (j / 128 = G) carries one code of each of the groups q*NG4 + G.
-// After a group's MFMAs the accumulator takes the page's premultiplied pair:
-// acc += S * p - ZS * X, p = sum_k x (1 + v/4), X = sum_k x.
+// A wave computes coarse scores of 64-column blocks for up to 16*MT rows with
+// bf16 MFMA 16x16x32: the A operand is x * 2^64 (rows), the B operand the
+// decoded codes v 2^(2q-133) (decode_quarter), one 16-column tile per MFMA,
+// four tiles per block.  Lane (hh, nn) = (lane / 16, lane % 16) supplies row
+// nn of A and column nn of B for k-slots 8hh..8hh+7; the accumulator holds
+// rows 4hh + r, column nn.  K is walked as groups (byte group G, quarter q):
+// code byte j of byte group G (j / 128 = G) carries one code of each of the
+// groups q*NG4 + G.  After a group's MFMAs the accumulator takes the page's
+// premultiplied pair, S * p - ZS * X with p = sum_k x (1 + v/4) and X =
+// sum_k x, written for codes without the 1.0 bias: (S/4) sum_k x v - (ZS - S) X.
 //
 // x fragments live in LDS in the decode order: fragment f = (h*2 + e)*4 + s of
 // a group holds x at k = q*K/4 + 128*G + 64h + 16s + 8e + {0,2,1,3,4,6,5,7}.
