@@ -891,8 +891,12 @@ __device__ __forceinline__ void emit_list8(LoadAt load_at, TagAt tag_at, KeyAt k
   for (int i = 0; i < 8; ++i) {
     const bool ok = slot[i] < 64u;
     const int col = 63 - (int)(ok ? slot[i] : 63u);
-    val[i] = ok ? key_f32(key_at(col)) : -__builtin_inff();
-    id[i] = ok ? b * 64 + col : -1;
+    // read for every slot (column 0 for an empty one) and selected by bits,
+    // so that the eight reads are in flight together (a conditional read
+    // becomes a branch and a wait of its own)
+    const uint32_t kv = key_at(col), okm = 0u - (uint32_t)ok;
+    val[i] = __uint_as_float((__float_as_uint(key_f32(kv)) & okm) | (0xFF800000u & ~okm));   // else -inf
+    id[i] = (int)(((uint32_t)(b * 64 + col) & okm) | ~okm);                                 // else -1
   }
   const size_t base = ((size_t)m * A.nblk + b) * A.kcand;
   if (A.kcand == 8) {   // 32-byte aligned: the list is two 16-byte pieces
