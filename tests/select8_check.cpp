@@ -2,7 +2,9 @@
 // many-row coarse kernels run (unrolled over consecutive columns, and rolled
 // over the fp16 kernel's runs): against a sort by (key desc, column asc) on
 // random rows, rows with exact ties, rows with near-ties (keys a few units
-// apart, so their upper 26 bits agree) and rows with missing columns (key 0),
+// apart, so their upper 26 bits agree), rows with missing columns (key 0) and
+// rows with a planted cut (the 8th and 9th keys within 63 units, the other
+// seven far above, so only the check of the best key left out catches it),
 // plus the sorting networks on all 256 zero-one inputs.  Exit status 0 = all
 // agree.
 #include <algorithm>
@@ -45,6 +47,17 @@ int main() {
     }
     const int nvalid = mode == 5 ? 1 + (int)(rng() % 64) : 64;
     for (int c = nvalid; c < 64; ++c) key[c] = 0u;
+    if (trial % 7 == 6) {   // a planted cut: the 8th and 9th within 63 units, their columns in the wrong order
+      int perm[64];
+      for (int c = 0; c < 64; ++c) perm[c] = c;
+      for (int c = 63; c > 0; --c) std::swap(perm[c], perm[rng() % (c + 1)]);
+      for (int c = 0; c < 64; ++c) key[c] = key_of(nrm(rng) * 0.1f);
+      const uint32_t K = key_of(4.0f) & ~63u;
+      for (int i = 0; i < 7; ++i) key[perm[i]] = K + 64u * 1000u * (uint32_t)(i + 1);
+      const int c8 = std::max(perm[7], perm[8]), c9 = std::min(perm[7], perm[8]);
+      key[c8] = K + 40u;   // the 8th, at the higher column
+      key[c9] = K + 10u;   // the 9th: its column tag puts it above the 8th
+    }
     uint32_t slot[8], slot2[8];
     dh::select8_row(key, [&](int c) { return key[c]; }, slot);
     // the rolled form over runs of non-consecutive columns (the fp16 kernel's
