@@ -1086,10 +1086,10 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
       const dh::XOp o = dh::x_op<S>(j, lb, k, NGRP);
       dma16(voff, BA.xslab + (size_t)o.slab * 256 * MT + o.chunk * 64, xs_l + o.dst * 1024);
     }
-    if (dh::stage_has_byte_ops<S>(j)) {
-      // the zero-point slab first: it is waited for at the byte group's end,
-      // the codes (issued after it, so not waited for with it) CD byte groups
-      // later
+    if (dh::stage_has_zp_ops<S>(j)) {
+      // the zero-point slab before the codes: it is waited for at the byte
+      // group's end, the codes (issued after it, so not waited for with it)
+      // CD byte groups later
       const int GB = dh::zp_group<S>(j, NG4);
       const uint32_t zslot = (uint32_t)dh::zp_slot<S>(j);
 #pragma unroll
@@ -1097,6 +1097,11 @@ __device__ __forceinline__ void big_wave(const BigArgs& BA, unsigned char* smem)
         const int c = lb * S::nb(P) + k;
         dma16(voff, BA.zslab + (size_t)GB * kZpEntries + c * 64, zs_l + zslot * 4096 + c * 1024);
       }
+    }
+    if (dh::stage_has_code_ops<S>(j)) {
+      // with one wave per block (S::CODE == 0) the slot refilled here is the
+      // one this wave has just read: its LDS reads must have returned
+      if constexpr (S::CODE == 0) __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
       const int GC = dh::code_group<S>(j, NG4);
       const uint32_t cslot = (uint32_t)dh::code_slot<S>(j);
 #pragma unroll

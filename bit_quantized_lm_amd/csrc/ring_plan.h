@@ -56,9 +56,15 @@ struct BigShape {
   static constexpr int BYTE = 1 % SPB;
   static constexpr int LAG = SPB == 1 ? 1 : 0;
   static constexpr int ZPS = SPB == 1 ? 2 : 1;      // zero-point slots
+  // With one wave per block a block's code slot is read by that wave alone,
+  // at the start of the byte group: the wave refills it right after its own
+  // reads (j mod SPB == 0, its LDS reads waited for), a stage earlier than
+  // a barrier would allow; the zero-point slab, read by every wave, keeps
+  // stage BYTE.
+  static constexpr int CODE = WPB == 1 ? 0 : BYTE;
   // prologue stages: the x slabs of stages 0 .. XD - 1 and the codes of byte
-  // groups 0 .. CD - LAG - 1 (issued at stage SPB (G - CD + LAG) + BYTE)
-  static constexpr int PRO_C = SPB * (CD - LAG) - BYTE;
+  // groups 0 .. CD - LAG - 1 (issued at stage SPB (G - CD + LAG) + CODE)
+  static constexpr int PRO_C = SPB * (CD - LAG) - CODE;
   static constexpr int PRO = XD > PRO_C ? XD : PRO_C;
   // DMA ops per iteration of a wave of part p.  With two waves per block the
   // parts issue different streams: part 1 the x slabs (chunks lb + BPW k),
@@ -107,10 +113,15 @@ constexpr XOp x_op(int j, int lb, int k, int NGRP) {
   return XOp{g, cc, (xslot * S::GPS + t) * 4 * MT + cc};
 }
 
-// Whether stage j issues the byte-group ops (zero-point slab, then codes).
+// Whether stage j issues the zero-point slab's ops, and the codes' (after
+// the zero-point slab's where a stage issues both).
 template <class S>
-constexpr bool stage_has_byte_ops(int j) {
+constexpr bool stage_has_zp_ops(int j) {
   return stage_mod<S>(j) == S::BYTE;
+}
+template <class S>
+constexpr bool stage_has_code_ops(int j) {
+  return stage_mod<S>(j) == S::CODE;
 }
 // Byte group whose zero-point slab stage j fetches (the next one, clamped),
 // and its slot.
@@ -139,13 +150,14 @@ constexpr int code_group(int j, int NG4) {
 // Ops a wave of part P may leave outstanding at the end of a stage with
 // j mod SPB == Q: those issued after X(j + XW) and, for the byte group's last
 // stage (Q == SPB - 1), after the zero-point slab and the codes of the next
-// byte group, issued at stages Q + 1 - SPB + BYTE and that plus
-// SPB (1 - CD + LAG) (relative to j - Q).  The prologue's final wait
-// (X(XW - 1), codes and zero-point slab of byte group 0) is the
-// Q == SPB - 1 case.
+// byte group, issued at stages BYTE and CODE + SPB (1 - CD + LAG) (relative
+// to j - Q).  The prologue's final wait (X(XW - 1), codes and zero-point
+// slab of byte group 0) is the Q == SPB - 1 case.
 template <class S, int P>
 constexpr int big_wait(int Q) {
-  auto cb = [&](int j) { return stage_mod<S>(j) == S::BYTE ? S::nc(P) + S::nb(P) : 0; };
+  auto zc = [&](int j) { return stage_mod<S>(j) == S::BYTE ? S::nb(P) : 0; };
+  auto cc = [&](int j) { return stage_mod<S>(j) == S::CODE ? S::nc(P) : 0; };
+  auto cb = [&](int j) { return zc(j) + cc(j); };
   auto ops = [&](int j) { return S::nx(P) + cb(j); };
   auto after = [&](int j0, int in_iter) {   // ops after one issued in iteration j0
     int n = in_iter;
@@ -156,9 +168,10 @@ constexpr int big_wait(int Q) {
   auto take = [&](int n) { best = n < best ? n : best; };
   if (S::nx(P)) take(after(Q + S::XW - S::XD, cb(Q + S::XW - S::XD)));
   if (Q == S::SPB - 1) {
-    const int jb = Q + 1 - S::SPB + S::BYTE;                       // the zero-point slab's stage
-    if (S::nc(P)) take(after(jb + S::SPB * (1 - S::CD + S::LAG), 0));   // codes: last in their stage
-    if (S::nb(P)) take(after(jb, S::nc(P)));                       // followed by that stage's codes
+    const int j0 = Q + 1 - S::SPB;   // the byte group's first stage
+    const int jb = j0 + S::BYTE;     // the zero-point slab's stage
+    if (S::nc(P)) take(after(j0 + S::CODE + S::SPB * (1 - S::CD + S::LAG), 0));   // codes: last in their stage
+    if (S::nb(P)) take(after(jb, cc(jb)));   // followed by that stage's codes, if any
   }
   return best < 63 ? best : 63;   // 63: nothing this iteration must complete
 }

@@ -27,16 +27,22 @@ static int failures = 0;
 // wait and a barrier, every main stage with the wait big_wait(j mod SPB) and
 // a barrier.  A wait completes all but the last n of the wave's ops; an op
 // may land at any time between its issue and the wait that completes it.
-// Every LDS chunk is written by one wave only.  A read of chunk T expecting
-// data d during stages r0 .. r1 (after the barrier that ends stage r0 - 1)
-// holds when the last op into T issued before stage r0 carries d and is
-// complete at that barrier, and no op into T with other data is issued in
-// stages r0 .. r1.  The reads: stage r reads the GPS x slabs of its groups
-// (the first of them from stage r - 1 on when XW = 2: the next stage's first
-// fragments are read before the barrier); the first stage of byte group G
-// reads the codes and pairs of every block and the zero-point slab of G.
+// Every LDS chunk is written by one wave only.  Time runs in half stages:
+// 2j is the start of stage j (the byte group's reads of its codes and
+// zero-point slab, before the stage issues anything), 2j + 1 the rest of it
+// (its ops, then its compute); the barrier ending stage j is at 2j + 2.  A
+// read of chunk T expecting data d during times t0 .. t1 holds when the last
+// op into T issued before t0 carries d and is complete at a barrier no later
+// than t0, and no op into T with other data is issued in t0 .. t1.  The
+// reads: stage r reads the GPS x slabs of its groups during 2r + 1 (the
+// first of them from 2r - 1 on when XW = 2: the next stage's first fragments
+// are read before the barrier); byte group G's first stage reads the codes
+// and pairs of every block and the zero-point slab of G at 2 SPB G.  Where
+// one wave reads a block's codes (WPB = 1) it refills their slot in that same
+// stage, after those reads.
 struct SimOp {
-  int stage, data, done;   // done: the barrier (end of stage) completing it, or INT_MAX
+  int time, data, done;   // time: 2 stage + 1; done: the time of the barrier completing it, or a large value
+  int wave;
 };
 template <class S>
 void check_big_k(int NG4) {
@@ -57,25 +63,29 @@ void check_big_k(int NG4) {
     if (T < 0 || T >= NT) return;
     CHECK(writer[T] < 0 || writer[T] == wid, "%d/%d: chunk %d written by two waves\n", MT, S::QPB, T);
     writer[T] = wid;
-    tgt[T].push_back({j, data, 1 << 30});
+    tgt[T].push_back({2 * j + 1, data, 1 << 30, wid});
     waves[wid].ops.push_back({T, (int)tgt[T].size() - 1});
   };
   auto wait = [&](int wid, int n, int j) {
     WaveState& w = waves[wid];
-    for (; w.done + n < w.ops.size(); ++w.done) tgt[w.ops[w.done].first][w.ops[w.done].second].done = j;
+    for (; w.done + n < w.ops.size(); ++w.done) tgt[w.ops[w.done].first][w.ops[w.done].second].done = 2 * j + 2;
   };
-  auto read = [&](int T, int data, int r0, int r1, const char* what) {
+  // only: the one wave that reads the chunk (-1: every wave reads it).  An
+  // op of another wave is ordered after the read only by a barrier, so for
+  // it the read lasts to the end of its stage (t1 | 1); the reading wave's
+  // own ops follow its reads in program order.
+  auto read = [&](int T, int data, int t0, int t1, int only, const char* what) {
     const std::vector<SimOp>& v = tgt[T];
     int last = -1;
     for (int i = 0; i < (int)v.size(); ++i) {
-      if (v[i].stage < r0) last = i;
-      else if (v[i].stage <= r1)
-        CHECK(v[i].data == data, "%d/%d NG4 %d: %s chunk %d rewritten at stage %d while read in %d..%d\n", MT,
-              S::QPB, NG4, what, T, v[i].stage, r0, r1);
+      if (v[i].time < t0) last = i;
+      else if (v[i].time <= (v[i].wave == only ? t1 : t1 | 1))
+        CHECK(v[i].data == data, "%d/%d NG4 %d: %s chunk %d rewritten at time %d while read in %d..%d\n", MT,
+              S::QPB, NG4, what, T, v[i].time, t0, t1);
     }
-    CHECK(last >= 0 && v[last].data == data && v[last].done <= r0 - 1,
-          "%d/%d NG4 %d: %s chunk %d (data %d) not in place for stages %d..%d\n", MT, S::QPB, NG4, what, T, data, r0,
-          r1);
+    CHECK(last >= 0 && v[last].data == data && v[last].done <= t0,
+          "%d/%d NG4 %d: %s chunk %d (data %d) not in place for times %d..%d\n", MT, S::QPB, NG4, what, T, data, t0,
+          t1);
   };
   auto issue_stage = [&](int j) {
     for (int P = 0; P < S::WPB; ++P)
@@ -87,15 +97,22 @@ void check_big_k(int NG4) {
                 "%d/%d NG4 %d j %d: x op slab %d chunk %d\n", MT, S::QPB, NG4, j, o.slab, o.chunk);
           issue(wid, j, o.dst, o.slab * 64 + o.chunk);
         }
-        if (stage_has_byte_ops<S>(j)) {
-          const int GB = zp_group<S>(j, NG4), GC = code_group<S>(j, NG4), cs = code_slot<S>(j), zs = zp_slot<S>(j);
-          CHECK(GB >= 0 && GB < NG4 && GC >= 0 && GC < NG4 && cs >= 0 && cs < S::CD && zs >= 0 && zs < S::ZPS,
-                "%d/%d NG4 %d j %d: byte ops GB %d GC %d slots %d %d\n", MT, S::QPB, NG4, j, GB, GC, cs, zs);
+        if (stage_has_zp_ops<S>(j)) {
+          const int GB = zp_group<S>(j, NG4), zs = zp_slot<S>(j);
+          CHECK(GB >= 0 && GB < NG4 && zs >= 0 && zs < S::ZPS, "%d/%d NG4 %d j %d: zero-point ops GB %d slot %d\n", MT,
+                S::QPB, NG4, j, GB, zs);
           for (int k = 0; k < S::nb(P); ++k) {
             const int c = lb * S::nb(P) + k;
             CHECK(c < 4, "%d/%d: zero-point chunk %d\n", MT, S::QPB, c);
             issue(wid, j, T_ZP + zs * 4 + c, GB * 4 + c);
           }
+        }
+        if (stage_has_code_ops<S>(j)) {
+          const int GC = code_group<S>(j, NG4), cs = code_slot<S>(j);
+          CHECK(GC >= 0 && GC < NG4 && cs >= 0 && cs < S::CD, "%d/%d NG4 %d j %d: code ops GC %d slot %d\n", MT,
+                S::QPB, NG4, j, GC, cs);
+          CHECK(S::CODE == S::BYTE || S::WPB == 1, "%d/%d: codes refilled before a barrier with two waves a block\n",
+                MT, S::QPB);
           for (int k = 0; k < S::nc(P); ++k) issue(wid, j, T_CODE + (cs * S::BPW + lb) * kCodeChunks + k, GC * 16 + k);
         }
       }
@@ -116,14 +133,15 @@ void check_big_k(int NG4) {
     const int j = SPB * G;
     for (int lb = 0; lb < S::BPW; ++lb)
       for (int k = 0; k < kCodeChunks; ++k)
-        read(T_CODE + ((G % S::CD) * S::BPW + lb) * kCodeChunks + k, G * 16 + k, j, j, "code");
-    for (int c = 0; c < 4; ++c) read(T_ZP + (G % S::ZPS) * 4 + c, G * 4 + c, j, j, "zero-point");
+        read(T_CODE + ((G % S::CD) * S::BPW + lb) * kCodeChunks + k, G * 16 + k, 2 * j, 2 * j,
+             S::WPB == 1 ? lb : -1, "code");   // read by the block's waves
+    for (int c = 0; c < 4; ++c) read(T_ZP + (G % S::ZPS) * 4 + c, G * 4 + c, 2 * j, 2 * j, -1, "zero-point");
   }
   for (int j = 0; j < NST; ++j)
     for (int t = 0; t < S::GPS; ++t) {
-      const int r0 = t == 0 && S::XW == 2 && j > 0 ? j - 1 : j;
+      const int r0 = t == 0 && S::XW == 2 && j > 0 ? j - 1 : j;   // read during stages r0 .. j
       for (int cc = 0; cc < 4 * MT; ++cc)
-        read(((j % NBUF) * S::GPS + t) * 4 * MT + cc, (S::GPS * j + t) * 64 + cc, r0, j, "x");
+        read(((j % NBUF) * S::GPS + t) * 4 * MT + cc, (S::GPS * j + t) * 64 + cc, 2 * r0, 2 * j + 1, -1, "x");
     }
 }
 
