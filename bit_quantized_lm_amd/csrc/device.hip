@@ -2244,15 +2244,17 @@ __device__ __forceinline__ int lane_prefix(unsigned long long bal) {
 // four waves (+3 us): fewer parts repeat the list less, but load the R rows
 // of W through fewer CUs.
 constexpr int kWideThreads = 512;
-// From this many rows on, the one-call path takes each row in one
-// workgroup, each wave holding the loads of kRerankRows candidate rows at
-// once (32 rows in flight at R = 32): no hand-off between workgroups, and
-// with this many rows the R rows of W still arrive through enough CUs
-// (per call, one part against four: 132.4 / 133.5 us at M = 72, 99.4 /
-// 99.1 at 48, 73.8 / 71.5 at 32, 50.2 / 47.8 at 8: with few rows, a row's
-// 320 KB of W through one CU takes longer than the hand-off).
-constexpr int kRerankOnePartM = 64;
-constexpr int kRerankRows = 4;
+// From this many rows on, the one-call path takes each row in two
+// workgroups, each wave holding the loads of kRerankRows candidate rows at
+// once (16 rows in flight per workgroup at R = 32): with this many rows the
+// R rows of W still arrive through enough CUs, and one hand-off between two
+// parts costs less than four parts' (per call, one part against four:
+// 132.4 / 133.5 us at M = 72, 99.4 / 99.1 at 48, 73.8 / 71.5 at 32, 50.2 /
+// 47.8 at 8: with few rows, a row's 320 KB of W through one CU takes longer
+// than the hand-off; two parts against one, on another box: 118.7-119.2 /
+// 119.7 us at M = 72, 105.7-105.8 / 106.2-107.2 at 64).
+constexpr int kRerankManyRowsM = 64;
+constexpr int kRerankRows = 2;
 // Dynamic LDS of the block-maximum rerank: x of one row (K <= DH_MAX_K).
 constexpr size_t kWideMaxLds = (size_t)2 * DH_MAX_K;
 
@@ -2898,7 +2900,7 @@ hipError_t launch_wide(const void* x, const RowSrc& src, int M, int K, int N, co
     if (src.kind == kRowsNvfp4) return launch(rerank_wide_kernel<kArgmax, kRowsNvfp4, NTHR, NR>);
     return launch(rerank_wide_kernel<kArgmax, kRowsBf16, NTHR, NR>);
   };
-  if (kArgmax && M >= kRerankOnePartM)
+  if (kArgmax && M >= kRerankManyRowsM)
     return go(std::integral_constant<int, kWideThreads>{}, std::integral_constant<int, kRerankRows>{});
   return go(std::integral_constant<int, kWideThreads>{}, std::integral_constant<int, 1>{});
 }
