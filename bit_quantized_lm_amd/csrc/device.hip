@@ -2252,8 +2252,9 @@ constexpr int kWideThreads = 512;
 // 132.4 / 133.5 us at M = 72, 99.4 / 99.1 at 48, 73.8 / 71.5 at 32, 50.2 /
 // 47.8 at 8: with few rows, a row's 320 KB of W through one CU takes longer
 // than the hand-off; two parts against one, on another box: 118.7-119.2 /
-// 119.7 us at M = 72, 105.7-105.8 / 106.2-107.2 at 64).
-constexpr int kRerankManyRowsM = 64;
+// 119.7 us at M = 72, 105.7-105.8 / 106.2-107.2 at 64; two against four:
+// 90.8-91.0 / 91.5-92.2 us at M = 48, equal at 16 and 32).
+constexpr int kRerankManyRowsM = 48;
 constexpr int kRerankRows = 2;
 // Dynamic LDS of the block-maximum rerank: x of one row (K <= DH_MAX_K).
 constexpr size_t kWideMaxLds = (size_t)2 * DH_MAX_K;
