@@ -1439,9 +1439,11 @@ __device__ __forceinline__ f16x8 decode_h16(uint32_t d0, uint32_t o0, uint32_t d
 }
 
 template <int MT>
-__global__ __launch_bounds__(64 * kHBlocks) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * dh::h16_waves(MT))
+__attribute__((amdgpu_waves_per_eu(dh::h16_waves(MT) / 4, dh::h16_waves(MT) / 4)))
 void coarse_h16_kernel(HArgs HA) {
   constexpr int MP = 16 * MT, NX = dh::h16_xops(MT), SLOTS = dh::kH16Slots;
+  constexpr int NTW = dh::h16_ntw(MT), WPB = 4 / NTW, W = dh::h16_waves(MT);   // tiles a wave, waves a block
   const CoarseArgs& A = HA.c;
   extern __shared__ __align__(16) unsigned char smem[];
   u32x4* xs = reinterpret_cast<u32x4*>(smem);                     // [SLOTS][16][MP]
@@ -1450,8 +1452,9 @@ void coarse_h16_kernel(HArgs HA) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lb = wave / WPB, part = wave % WPB, T0 = NTW * part;   // block, and the wave's first column tile
   const int hh = lane >> 4, nn = lane & 15;
-  const int b = blockIdx.x * kHBlocks + wave;
+  const int b = blockIdx.x * kHBlocks + lb;
   const bool blk_ok = b < A.nblk;
   const int NG4 = A.K >> 9, NSTAGE = 4 * NG4;
   zero_counters(A);
@@ -1460,7 +1463,7 @@ void coarse_h16_kernel(HArgs HA) {
   const u32x4* tp = A.tiled + (size_t)(blk_ok ? b : 0) * NG4 * 512;
   const u32x4* pp = A.pairs + (size_t)(blk_ok ? b : 0) * NG4 * 64;
   const uint32_t voff = lane * 16;
-  const uint32_t xs_l = lds_addr(xs), zs_l = lds_addr(zs), cs_l = lds_addr(cs + wave * kCodeChunks * 64);
+  const uint32_t xs_l = lds_addr(xs), zs_l = lds_addr(zs), cs_l = lds_addr(cs + lb * kCodeChunks * 64);
 
   auto issue_x = [&](int j) {   // slab of stage j (clamped to the last) into its slot
     const int slab = dh::h16_slab(j, NSTAGE);
@@ -1471,13 +1474,15 @@ void coarse_h16_kernel(HArgs HA) {
       dma16(voff, HA.xslab + (size_t)slab * 256 * MT + c * 64, dst + c * 1024);
     }
   };
-  auto issue_bytes = [&](int G) {   // zero-point slab and codes of byte group G (clamped)
+  auto issue_bytes = [&](int G) {   // zero-point slab and the wave's codes of byte group G (clamped)
     const int Gc = dh::h16_byte_group(G, NG4);
     const int c = wave & 3;
     dma16(voff, HA.zslab + (size_t)Gc * kZpEntries + c * 64, zs_l + (uint32_t)((Gc & 1) * 4096 + c * 1024));
 #pragma unroll
-    for (int k = 0; k < kCodeChunks; ++k)
-      dma16_nt(voff, k < 8 ? tp + (Gc * 8 + k) * 64 : pp + Gc * 64, cs_l + k * 1024);
+    for (int k = 0; k < dh::h16_code_ops(MT); ++k) {
+      const int ch = dh::h16_code_chunk(MT, part, k);
+      dma16_nt(voff, ch < 8 ? tp + (Gc * 8 + ch) * 64 : pp + Gc * 64, cs_l + ch * 1024);
+    }
   };
 
   // prologue: slabs of stages 0 .. kH16XD - 1, byte group 0
@@ -1487,23 +1492,24 @@ void coarse_h16_kernel(HArgs HA) {
   wait_vm<0>();
   __syncthreads();
 
-  f32x4 acc[MT][4];
+  f32x4 acc[MT][NTW];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const u32x4* xl = xs + hh * MP + nn;   // this lane's fragment 0 (A row nn, k-slot hh) of slot 0
-  const u32x4* cw = cs + wave * kCodeChunks * 64;
+  const u32x4* cw = cs + lb * kCodeChunks * 64;
   for (int G = 0; G < NG4; ++G) {
-    // byte group G's codes and scale pairs (the slot is refilled at stage 4G + 1)
-    u32x4 raw[2][4], raw8[2][4], sz[4];
+    // byte group G's codes and scale pairs of the wave's tiles (the slot is
+    // refilled at stage 4G + 1)
+    u32x4 raw[2][NTW], raw8[2][NTW], sz[NTW];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) raw[h][t] = cw[(h * 4 + t) * 64 + lane];
+      for (int t = 0; t < NTW; ++t) raw[h][t] = cw[(h * 4 + T0 + t) * 64 + lane];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sz[t] = cw[512 + t * 16 + nn];
+    for (int t = 0; t < NTW; ++t) sz[t] = cw[512 + (T0 + t) * 16 + nn];
     shift_codes(raw, raw8);
     // zero-point part of byte group G: rows' X parts against S - ZS (exact in bf16)
     {
@@ -1512,7 +1518,7 @@ void coarse_h16_kernel(HArgs HA) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) za[i] = hh < 2 ? zg[(hh & 1) * MP + 16 * i + nn] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < NTW; ++t) {
         uint32_t d[4];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) d[qq] = __float_as_uint(lo_bf16(sz[t][qq]) - hi_bf16(sz[t][qq]));
@@ -1533,9 +1539,9 @@ void coarse_h16_kernel(HArgs HA) {
       // the code bits of quarter Q, and the exponent field of 1.0 (disjoint from them)
       const uint32_t mask = __builtin_amdgcn_readfirstlane(0x00030003u << (2 * Q));
       const uint32_t one = 0x3C003C00u;
-      f16x2 tt[4];
+      f16x2 tt[NTW];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {   // T = (S/4) 2^(10 - 2Q) = S 2^(8 - 2Q), exact in fp16
+      for (int t = 0; t < NTW; ++t) {   // T = (S/4) 2^(10 - 2Q) = S 2^(8 - 2Q), exact in fp16
         const _Float16 tv = (_Float16)__builtin_ldexpf(lo_bf16(sz[t][Q]), 8 - 2 * Q);
         tt[t] = f16x2{tv, tv};
       }
@@ -1547,7 +1553,7 @@ void coarse_h16_kernel(HArgs HA) {
 #pragma unroll
         for (int i = 0; i < MT; ++i) a[i] = xb[((h * 2 + e) * 4) * MP + 16 * i];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < NTW; ++t) {
           const f16x8 bv = decode_h16(raw[h][t][2 * e], raw8[h][t][2 * e], raw[h][t][2 * e + 1],
                                       raw8[h][t][2 * e + 1], mask, one, tt[t]);
 #pragma unroll
@@ -1571,36 +1577,33 @@ void coarse_h16_kernel(HArgs HA) {
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) rs[i][r] = __builtin_ldexpf(1.0f, -HA.fexp[16 * i + 4 * hh + r]);
-  if (A.kcand > 8) {   // lists longer than eight: the 16-lane rounds, from registers
-    if (!blk_ok) return;
-    block_select<MT, 4>([&](int i, int r, int t) { return acc[i][t][r] * rs[i][r]; }, A, b, hh, nn);
-    return;
-  }
   // Every wave's DMA writes have landed and every wave is done with the ring:
   // the LDS takes the keys of the workgroup's 8 blocks, row rho = lb MP + m
   // (block lb, row m) in 16 pieces of 16 bytes, piece g holding columns g,
-  // g + 16, g + 32, g + 48 (one lane's four keys of the row: one 16-byte
-  // write) at position g ^ (rho mod 16), so that the sixteen lanes of a
-  // write, and sixteen consecutive rows read piece by piece, meet every bank
-  // once.  Then thread q selects the lists q and q + 512 (list l: block
-  // l / M, row l % M).
+  // g + 16, g + 32, g + 48 (tiles 0..3 of column g: written by the block's
+  // one wave, or its two waves 8 bytes each) at position g ^ (rho mod 16), so that
+  // sixteen consecutive rows read piece by piece meet every bank once.  Then
+  // thread q selects list q (list l: block l / M, row l % M).  (The fp16
+  // kernel takes lists of at most eight.)
   u32x4* sk = reinterpret_cast<u32x4*>(smem);
   __syncthreads();
   // masks of the live columns and rows, as bits (conditions the compiler
   // would otherwise turn into branches around every key)
-  uint32_t colm[4];
+  uint32_t colm[NTW];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) colm[t] = 0u - (uint32_t)(blk_ok & (64 * b + 16 * t + nn < A.N));
+  for (int t = 0; t < NTW; ++t) colm[t] = 0u - (uint32_t)(blk_ok & (64 * b + 16 * (T0 + t) + nn < A.N));
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 16 * i + 4 * hh + r, rho = wave * MP + row;
+      const int row = 16 * i + 4 * hh + r, rho = lb * MP + row;
       const uint32_t rowm = 0u - (uint32_t)(row < A.M);
-      uint32_t kk[4];
+      uint32_t kk[NTW];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kk[t] = f32_key(acc[i][t][r] * rs[i][r] + 0.0f) & colm[t] & rowm;   // -0 as +0
-      sk[rho * 16 + (nn ^ (row & 15))] = u32x4{kk[0], kk[1], kk[2], kk[3]};
+      for (int t = 0; t < NTW; ++t) kk[t] = f32_key(acc[i][t][r] * rs[i][r] + 0.0f) & colm[t] & rowm;   // -0 as +0
+      u32x4* piece = sk + rho * 16 + (nn ^ (row & 15));
+      if constexpr (NTW == 4) *piece = u32x4{kk[0], kk[1], kk[2], kk[3]};
+      else reinterpret_cast<u32x2*>(piece)[part] = u32x2{kk[0], kk[1]};
     }
   if (wants_scores(A)) {
 #pragma unroll
@@ -1608,16 +1611,16 @@ void coarse_h16_kernel(HArgs HA) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int row = 16 * i + 4 * hh + r, n = 64 * b + 16 * t + nn;
+        for (int t = 0; t < NTW; ++t) {
+          const int row = 16 * i + 4 * hh + r, n = 64 * b + 16 * (T0 + t) + nn;
           if (blk_ok && n < A.N && row < A.M) store_scores(A, row, n, acc[i][t][r] * rs[i][r]);
         }
   }
   __syncthreads();
-  for (int l = threadIdx.x; l < kHBlocks * A.M; l += 64 * kHBlocks) {
-    const int lb = l / A.M, m = l - lb * A.M, bq = blockIdx.x * kHBlocks + lb;
+  for (int l = threadIdx.x; l < kHBlocks * A.M; l += 64 * W) {
+    const int lbl = l / A.M, m = l - lbl * A.M, bq = blockIdx.x * kHBlocks + lbl;
     if (bq >= A.nblk) continue;
-    const u32x4* row = sk + (lb * MP + m) * 16;
+    const u32x4* row = sk + (lbl * MP + m) * 16;
     const int sw = m & 15;
     emit_list8(
         [&](int r, uint32_t(&raw)[8]) {   // run r: pieces 2r and 2r + 1 (columns g, g + 16, g + 32, g + 48)
@@ -2669,7 +2672,7 @@ hipError_t launch_h16(const HArgs& A, hipStream_t s, hipEvent_t e0, hipEvent_t e
     attr_set = true;
   }
   dim3 grid((A.c.nblk + kHBlocks - 1) / kHBlocks);
-  hipExtLaunchKernelGGL(coarse_h16_kernel<MT>, grid, dim3(64 * kHBlocks), lds, s, e0, e1, 0, A);
+  hipExtLaunchKernelGGL(coarse_h16_kernel<MT>, grid, dim3(64 * dh::h16_waves(MT)), lds, s, e0, e1, 0, A);
   return hipGetLastError();
 }
 
@@ -2713,7 +2716,9 @@ int resident_rows(int M, int K) {
 // bf16 kernel, faster there on the same box: M = 16 54.7 against 68.0 us, M =
 // 32 70.6 against 78.3 us per call; M = 48, 64, 72: 92.7, 106.0, 120.1 us
 // against 98.4, 113.4, 130.8 us).
-bool use_h16(int K, int kx, int mt) { return mt >= 3 && kx == K && K <= kPrepHMaxG * 4 * 512; }
+bool use_h16(int K, int kx, int mt, int kcand) {
+  return mt >= 3 && kx == K && K <= kPrepHMaxG * 4 * 512 && kcand <= 8;
+}
 
 // Up to 8 rows whose x fits the workgroup's LDS take the resident kernel (no
 // workspace); every other M the many-row kernel, in launches of up to 80 rows.
@@ -2831,7 +2836,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
     int* fexp = reinterpret_cast<int*>(zslab + (size_t)NG4 * kZpEntries);
     hipEvent_t b0 = m0 == 0 ? ev0 : nullptr;
     hipEvent_t b1 = m0 + 16 * kMaxMT >= M ? ev1 : nullptr;
-    if (use_h16(K, A.kx, mt)) {
+    if (use_h16(K, A.kx, mt, A.kcand)) {
       hipLaunchKernelGGL(prep_xh_kernel, dim3(mp), dim3(256), 0, s, B.x, B.M, mp, K, xslab, zslab, fexp);
       if ((e = hipGetLastError()) != hipSuccess)
         return dh::fail(DH_EHIP, "prep_xh_kernel: %s", hipGetErrorString(e));

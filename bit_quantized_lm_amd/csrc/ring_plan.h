@@ -176,33 +176,48 @@ constexpr int big_wait(int Q) {
   return best < 63 ? best : 63;   // 63: nothing this iteration must complete
 }
 
-// DMA schedule of the fp16 many-row kernel: kH16Blocks waves, one 64-column
-// block each, all issuing the same number of ops in the same order.  Stage
-// j = 4G + q (quarter q of byte group G) reads x slab j (group 4G + q) from
-// slot j mod kH16Slots.  At its start a wave issues h16_xops(MT) ops of slab
-// j + kH16XD (clamped to the last slab) into that slab's slot, and at q == 1
-// its byte ops for byte group G + 1 (clamped): one zero-point op (chunk wave
-// mod 4 into zero-point slot (G + 1) mod 2), then its block's kCodeChunks
-// code and pair ops into its own code slot.  At the end of the stage it
-// waits until at most h16_wait(MT, q) of its ops are outstanding and meets
-// the others at a barrier.
+// DMA schedule of the fp16 many-row kernel: kH16Blocks 64-column blocks a
+// workgroup, each held by 4 / h16_ntw(MT) waves of h16_ntw(MT) column tiles
+// (two waves a block up to four row tiles, where their registers allow four
+// waves per SIMD; one at five); every wave issues the same number of ops in
+// the same order.  Stage j = 4G + q (quarter q of byte group G) reads x slab
+// j (group 4G + q) from slot j mod kH16Slots.  At its start a wave issues
+// h16_xops(MT) ops of slab j + kH16XD (clamped to the last slab) into that
+// slab's slot, and at q == 1 its byte ops for byte group G + 1 (clamped): one
+// zero-point op (chunk wave mod 4 into zero-point slot (G + 1) mod 2), then
+// the code chunks of its tiles and the block's pair chunk (h16_code_chunk)
+// into its block's code slot.  At the end of the stage it waits until at
+// most h16_wait(MT, q) of its ops are outstanding and meets the others at a
+// barrier.  Chunks that several waves fetch (x chunks past the slab's, the
+// zero-point chunks, a block's pair chunk) are the same bytes into the same
+// place.
 constexpr int kH16Blocks = 8;
 constexpr int kH16XD = 2;
 constexpr int kH16Slots = kH16XD + 1;
-constexpr int kH16ByteOps = 1 + kCodeChunks;
-constexpr int h16_xops(int MT) { return (4 * MT + kH16Blocks - 1) / kH16Blocks; }
+constexpr int h16_ntw(int MT) { return MT >= 5 ? 4 : 2; }                 // column tiles a wave
+constexpr int h16_waves(int MT) { return kH16Blocks * 4 / h16_ntw(MT); }   // waves a workgroup
+// a wave's code ops: every chunk of its block (one wave a block), or its two
+// tiles' chunks of the two halves and the pair chunk
+constexpr int h16_code_ops(int MT) { return h16_ntw(MT) == 4 ? kCodeChunks : 5; }
+constexpr int h16_byte_ops(int MT) { return 1 + h16_code_ops(MT); }
+constexpr int h16_xops(int MT) { return (4 * MT + h16_waves(MT) - 1) / h16_waves(MT); }
 // chunk of a slab (of 4 MT) that op k of a wave fetches: past the slab, a
 // repeat of chunk c - 4 MT (the same bytes into the same place)
 constexpr int h16_xchunk(int MT, int wave, int k) {
-  const int c = wave + kH16Blocks * k;
+  const int c = wave + h16_waves(MT) * k;
   return c >= 4 * MT ? c - 4 * MT : c;
+}
+// code chunk (h * 4 + t: half h of column tile t; 8: the block's pairs) of
+// code op k of the wave of part p of its block (tiles p NTW .. p NTW + NTW - 1)
+constexpr int h16_code_chunk(int MT, int p, int k) {
+  return h16_ntw(MT) == 4 ? k : k < 4 ? (k >> 1) * 4 + 2 * p + (k & 1) : 8;
 }
 constexpr int h16_slab(int j, int nstage) { return j < nstage ? j : nstage - 1; }
 constexpr int h16_byte_group(int G, int NG4) { return G < NG4 ? G : NG4 - 1; }
 // Ops issued after slab j + 1's (and, at q == 3, after byte group G + 1's)
 // by the end of stage j: the byte ops of stage j - 1 when it had q == 1, and
 // this stage's x ops and, at q == 1, its byte ops.
-constexpr int h16_wait(int MT, int q) { return q == 1 || q == 2 ? h16_xops(MT) + kH16ByteOps : h16_xops(MT); }
+constexpr int h16_wait(int MT, int q) { return q == 1 || q == 2 ? h16_xops(MT) + h16_byte_ops(MT) : h16_xops(MT); }
 constexpr size_t h16_ring_bytes(int MT) {
   return (size_t)kH16Slots * MT * 4096 + (size_t)kH16Blocks * kCodeChunks * 1024 + (size_t)2 * kZpEntries * 16;
 }

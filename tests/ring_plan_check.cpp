@@ -168,14 +168,15 @@ void check_big() {
 // pairs and zero-point slab into registers.
 template <int MT>
 void check_h16(int K) {
-  constexpr int W = kH16Blocks, SLOTS = kH16Slots;
+  constexpr int W = h16_waves(MT), SLOTS = kH16Slots, WPB = 4 / h16_ntw(MT);
   const int NG4 = K / 512, NST = 4 * NG4;
-  CHECK(h16_ring_bytes(MT) <= 160 * 1024 && (size_t)W * 16 * MT * 64 * 4 <= 160 * 1024, "h16 MT %d: LDS\n", MT);
+  CHECK(h16_ring_bytes(MT) <= 160 * 1024 && (size_t)kH16Blocks * 16 * MT * 64 * 4 <= 160 * 1024, "h16 MT %d: LDS\n",
+        MT);
   CHECK(h16_wait(MT, 0) <= 63 && h16_wait(MT, 1) <= 63, "h16 MT %d: wait range\n", MT);
   struct Op {
     int kind;   // 0: x chunk, 1: zero-point chunk, 2: code or pair chunk
     int data;   // x: slab * 64 + chunk; zero point: byte group * 4 + chunk; codes: byte group * 16 + chunk
-    int slot;   // x: ring slot; zero point: slot 0 or 1; codes: 0
+    int slot;   // x: ring slot; zero point: slot 0 or 1; codes: the block (its code slot)
   };
   for (int w = 0; w < W; ++w) {
     std::vector<Op> ops;
@@ -195,8 +196,10 @@ void check_h16(int K) {
       CHECK(Gc >= 0 && Gc < NG4, "h16 MT %d K %d: byte group %d\n", MT, K, Gc);
       ops.push_back({1, Gc * 4 + (w & 3), Gc & 1});
       done.push_back(0);
-      for (int k = 0; k < kCodeChunks; ++k) {
-        ops.push_back({2, Gc * 16 + k, 0});
+      for (int k = 0; k < h16_code_ops(MT); ++k) {
+        const int ch = h16_code_chunk(MT, w % WPB, k);
+        CHECK(ch >= 0 && ch < kCodeChunks, "h16: code chunk %d\n", ch);
+        ops.push_back({2, Gc * 16 + ch, w / WPB});
         done.push_back(0);
       }
     };
@@ -224,9 +227,10 @@ void check_h16(int K) {
     wait(0);
     for (int j = 0; j < NST; ++j) {
       const int q = j & 3, G = j >> 2;
-      if (q == 0) {   // byte group G's codes and zero-point chunk, and slab j, complete
-        for (int k = 0; k < kCodeChunks; ++k)
-          CHECK(complete(2, G * 16 + k, 0), "h16 MT %d K %d w %d: codes of %d\n", MT, K, w, G);
+      if (q == 0) {   // byte group G's codes (the chunks this wave reads) and zero-point chunk complete
+        for (int k = 0; k < h16_code_ops(MT); ++k)
+          CHECK(complete(2, G * 16 + h16_code_chunk(MT, w % WPB, k), w / WPB), "h16 MT %d K %d w %d: codes of %d\n",
+                MT, K, w, G);
         CHECK(complete(1, G * 4 + (w & 3), G & 1), "h16 MT %d K %d w %d: zero point of %d\n", MT, K, w, G);
       }
       const size_t from = ops.size();
@@ -239,6 +243,15 @@ void check_h16(int K) {
           CHECK(complete(0, (j + 1) * 64 + h16_xchunk(MT, w, k), (j + 1) % SLOTS), "h16 MT %d K %d w %d: slab %d\n",
                 MT, K, w, j + 1);
     }
+  }
+  for (int p = 0; p < WPB; ++p) {   // a wave fetches the chunks it reads: both halves of its tiles, and the pairs
+    bool got[kCodeChunks] = {};
+    for (int k = 0; k < h16_code_ops(MT); ++k) got[h16_code_chunk(MT, p, k)] = true;
+    const int ntw = h16_ntw(MT);
+    for (int h = 0; h < 2; ++h)
+      for (int t = ntw * p; t < ntw * p + ntw; ++t)
+        CHECK(got[h * 4 + t], "h16 MT %d: part %d misses chunk %d\n", MT, p, h * 4 + t);
+    CHECK(got[8], "h16 MT %d: part %d misses the pairs\n", MT, p);
   }
   for (int c = 0; c < 4 * MT; ++c) {   // every chunk of a slab is some wave's
     bool any = false;
