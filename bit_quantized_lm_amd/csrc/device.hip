@@ -1697,6 +1697,28 @@ __device__ __forceinline__ float round_bf16(float f) {
   return f != f ? f : __uint_as_float(r);
 }
 
+// x.lo * w.lo + x.hi * w.hi + acc for two bf16 pairs (v_dot2c_f32_bf16): the
+// products of bf16 values are exact in fp32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float bf16_dot2(uint32_t x, uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, w), acc, false);
+}
+
+// Sum over the wave, the same in every lane, in a fixed order: pairs, quads,
+// eights and rows of 16 by DPP, then the four rows.  Every lane must be active.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_plus(float s) {
+  return s + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float s) {
+  s = dpp_plus<0xB1>(s);    // quad_perm 1,0,3,2
+  s = dpp_plus<0x4E>(s);    // quad_perm 2,3,0,1
+  s = dpp_plus<0x141>(s);   // row_half_mirror: lane i and 7 - i of each eight
+  s = dpp_plus<0x140>(s);   // row_mirror: lane i and 15 - i of each row
+  const auto row = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), l)); };
+  return (row(0) + row(16)) + (row(32) + row(48));
+}
+
 // x of one row in the lane layout of the rerank's dot for rows of kind kKind:
 // one chunk of the row (K elements, K a multiple of 256), clamped loads
 // (positions past K read the last valid piece and are masked in the dot).
@@ -1755,9 +1777,9 @@ __device__ void wave_dots(const RowSrc& S, const int (&ids)[NR], const uint16_t*
 #pragma unroll
           for (int i = 0; i < NR; ++i)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              s0[i] = __builtin_fmaf(lo_bf16(xc.v[j][0][c]), lo_bf16(wv[i][j][c]), s0[i]);
-              s1[i] = __builtin_fmaf(hi_bf16(xc.v[j][0][c]), hi_bf16(wv[i][j][c]), s1[i]);
+            for (int c = 0; c < 4; c += 2) {   // one dot2 per bf16 pair: products exact, fp32 sums
+              s0[i] = bf16_dot2(xc.v[j][0][c], wv[i][j][c], s0[i]);
+              s1[i] = bf16_dot2(xc.v[j][0][c + 1], wv[i][j][c + 1], s1[i]);
             }
         }
       }
@@ -1838,8 +1860,7 @@ __device__ void wave_dots(const RowSrc& S, const int (&ids)[NR], const uint16_t*
   }
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    float sum = s0[i] + s1[i];
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    const float sum = wave_sum(s0[i] + s1[i]);
     out[i] = ids[i] < 0 ? -__builtin_inff() : sum;
   }
 }
