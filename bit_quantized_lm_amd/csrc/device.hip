@@ -2290,7 +2290,7 @@ struct WideShared {
   unsigned long long keys[DH_MAX_R];
   unsigned long long list[DH_MAX_R];
   unsigned long long T;
-  int nq, ns, qcur;
+  int ns, qcur;
   uint32_t wbest[16][2];   // per wave: its best exact logit (value bits, id)
 };
 
@@ -2337,47 +2337,13 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
   }
   sh.bmax[wave][lane] = bw;
   if (tid == 0) {
-    sh.nq = 0;
     sh.qcur = 0;
     sh.ns = 0;
   }
-  __syncthreads();
-  // T' = (to, 0) with to the R-th largest of the 64 lane maxima's upper
-  // halves (bisection over its bits, counting lanes by ballot; every wave
-  // finds the same value): at least R lanes hold a block maximum >= T', so
-  // T' is at most the R-th largest block maximum.
-  uint32_t bo = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) bo = max(bo, sh.bmax[w][lane]);
-  uint32_t to = 0u, tl = 0u;
-  if (R <= 64) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t t = to | (1u << bit);
-      if (__popcll(__ballot(bo >= t)) >= R) to = t;
-    }
-    int nw = 0;
-#pragma unroll
-    for (int jj = 0; jj < JW; ++jj) nw += __popcll(__ballot(at_least(jj, to, 0u)));
-    if (lane == 0) atomicAdd(&sh.nq, nw);
-  }
-  __syncthreads();
-  if (to == 0u || sh.nq * kcand > DH_MAX_R) {   // uniform: the exact R-th largest maximum
-    if (wave == 0) {
-      const unsigned long long T = wave_kth_largest_of<kFastNV, 1>(
-          [&](int j) -> unsigned long long {
-            const uint32_t o = *reinterpret_cast<volatile uint32_t*>(so + 64 * j + lane);
-            return o ? ((unsigned long long)o << 32) | lower(j) : 0ull;
-          },
-          R, sh.hist);
-      if (lane == 0) sh.T = T;
-    }
-    __syncthreads();
-    to = (uint32_t)(sh.T >> 32);
-    tl = (uint32_t)sh.T;
-  } else if (tid == 0) {
-    sh.T = (unsigned long long)to << 32;
-  }
-  {   // the qualifying blocks, compacted (their order does not matter)
+  // The blocks whose maximum is >= (to, tl), compacted into sh.qual (their
+  // order does not matter; entries past its capacity are dropped, and then
+  // the count rules this threshold out).
+  auto compact = [&](uint32_t to, uint32_t tl) {
     unsigned long long bal[JW];
     int nw = 0;
 #pragma unroll
@@ -2387,20 +2353,57 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
     }
     int base = 0;
     if (lane == 0) base = atomicAdd(&sh.qcur, nw);
-    base = __shfl(base, 0, 64);
+    base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
-      if ((bal[jj] >> lane) & 1ull) sh.qual[base + lane_prefix(bal[jj])] = lane + 64 * (JW * wave + jj);
+      const int q = base + lane_prefix(bal[jj]);
+      if (((bal[jj] >> lane) & 1ull) && q < DH_MAX_R) sh.qual[q] = lane + 64 * (JW * wave + jj);
       base += __popcll(bal[jj]);
     }
+  };
+  __syncthreads();
+  // T' = (to, 0) with to the R-th largest of the 64 lane maxima's upper
+  // halves (bisection over its bits, counting lanes by ballot; every wave
+  // finds the same value): at least R lanes hold a block maximum >= T', so
+  // T' is at most the R-th largest block maximum.  Its blocks are compacted
+  // at once; the count decides after one barrier whether T' stands.
+  uint32_t to = 0u;
+  if (R <= 64) {
+    uint32_t bo = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) bo = max(bo, sh.bmax[w][lane]);
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t t = to | (1u << bit);
+      if (__popcll(__ballot(bo >= t)) >= R) to = t;
+    }
+    compact(to, 0u);
   }
   __syncthreads();
-  if (tid == 0) sh.nq = sh.qcur;
-  __syncthreads();
+  int nq = sh.qcur;
+  unsigned long long T = (unsigned long long)to << 32;
+  if (R > 64 || to == 0u || nq * kcand > DH_MAX_R) {   // uniform: the exact R-th largest maximum
+    __syncthreads();   // every thread has read qcur
+    if (wave == 0) {
+      T = wave_kth_largest_of<kFastNV, 1>(
+          [&](int j) -> unsigned long long {
+            const uint32_t o = *reinterpret_cast<volatile uint32_t*>(so + 64 * j + lane);
+            return o ? ((unsigned long long)o << 32) | lower(j) : 0ull;
+          },
+          R, sh.hist);
+      if (lane == 0) {
+        sh.T = T;
+        sh.qcur = 0;
+      }
+    }
+    __syncthreads();
+    T = sh.T;
+    compact((uint32_t)(T >> 32), (uint32_t)T);
+    __syncthreads();
+    nq = sh.qcur;
+  }
   for (int i = tid; i < R; i += NTHR) sh.list[i] = 0ull;   // a rank no survivor takes stays empty
-  if (sh.nq > 0) {   // the survivors, gathered by the whole workgroup (their order does not matter)
-    const int items = sh.nq * kcand;   // <= DH_MAX_R; no block qualifies only where none has a maximum
-    const unsigned long long T = sh.T;
+  if (nq > 0) {   // the survivors, gathered by the whole workgroup (their order does not matter)
+    const int items = nq * kcand;   // <= DH_MAX_R; no block qualifies only where none has a maximum
     float v[kGather];
     int id[kGather], slot[kGather];
 #pragma unroll
@@ -2418,8 +2421,21 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
     }
   }
   __syncthreads();
-  {   // rank the survivors (distinct keys): list[rank] for rank < R
-    const int ns = sh.ns;   // R <= ns <= DH_MAX_R
+  // Rank the survivors (distinct keys): list[rank] for rank < R, a key's
+  // rank being the number of survivors above it.  Up to 64 survivors (NTHR
+  // >= 512): eight lanes per key, each counting every eighth survivor, summed
+  // over the eight by DPP; more: one thread per key.
+  const int ns = sh.ns;   // R <= ns <= DH_MAX_R
+  if (NTHR >= 512 && ns <= 64) {   // uniform
+    const int i = tid >> 3, c = tid & 7;
+    const unsigned long long key = i < ns ? sh.keys[i] : 0ull;
+    int above = 0;
+    for (int j = c; j < ns; j += 8) above += sh.keys[j] > key;
+    above += __builtin_amdgcn_update_dpp(0, above, 0xB1, 0xF, 0xF, false);    // quad_perm 1,0,3,2
+    above += __builtin_amdgcn_update_dpp(0, above, 0x4E, 0xF, 0xF, false);    // quad_perm 2,3,0,1
+    above += __builtin_amdgcn_update_dpp(0, above, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    if (c == 0 && i < ns && above < R) sh.list[above] = key;
+  } else {
     for (int i = tid; i < ns; i += NTHR) {
       const unsigned long long key = sh.keys[i];
       int above = 0;
