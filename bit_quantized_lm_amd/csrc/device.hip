@@ -137,6 +137,7 @@ struct RerankArgs {
   float* out_val;
   unsigned long long* hand;   // per-row hand-off words (rows split over several workgroups)
   uint16_t* row_out;          // optional bf16 row [M][N]: each reranked id's exact value is written over it
+  const float* bmax;          // optional [M][nblk]: the block maxima, contiguous (else read at slot b*kcand)
 };
 
 struct CoarseArgs {
@@ -154,6 +155,7 @@ struct CoarseArgs {
   int ncnt;
   int kx;          // row length of x: K, or K / 2 for a 4-bit head run at length K (x' = (x, x))
   int half_pairs;  // a 4-bit head (draft_head_tile_int4): code nibbles, pairs of quarters 0 and 1 only
+  float* bmax;     // optional [M][nblk]: each block's maximum (its slot 0's value) once more, contiguous
 };
 
 // The rerank's per-row hand-off words are only ever written with agent-scope
@@ -392,6 +394,7 @@ __device__ __forceinline__ void write_list(const CoarseArgs& A, int m, int b, co
       A.cand_id[base + cs] = kk[sl] ? b * 64 + (int)kc[sl] : -1;
     }
   }
+  if (A.bmax && nn == 0) A.bmax[(size_t)m * A.nblk + b] = kk[0] ? key_f32(kk[0]) : NEG_INF;
 }
 
 // Top-kcand of block b for the rows a wave's accumulators hold: rows m0 + 16 i
@@ -2313,10 +2316,14 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
   // lower j first).  Each wave holds JW of every lane's kFastNV maxima.
   constexpr int NW = NTHR / 64, JW = kFastNV / NW;
   static_assert(kFastNV % NW == 0 && NW <= 16, "maxima split over the waves");
+  // the maxima: contiguous where the coarse kernel wrote them so, else slot
+  // b*kcand of the candidate array (the same value)
+  const float* mx = A.bmax ? A.bmax + (size_t)m * nblk : cv;
+  const int mstride = A.bmax ? 1 : kcand;
   uint32_t mo[JW];
 #pragma unroll
   for (int jj = 0; jj < JW; ++jj)
-    mo[jj] = __float_as_uint(cv[min(lane + 64 * (JW * wave + jj), nblk - 1) * kcand]);   // clamped loads
+    mo[jj] = __float_as_uint(mx[min(lane + 64 * (JW * wave + jj), nblk - 1) * mstride]);   // clamped loads
 #pragma unroll
   for (int jj = 0; jj < JW; ++jj)
     mo[jj] = lane + 64 * (JW * wave + jj) < nblk ? (uint32_t)(slot_key(__uint_as_float(mo[jj]), 0) >> 32) : 0u;
@@ -2762,13 +2769,16 @@ bool use_h16(int K, int kx, int mt, int kcand) {
 // ks: the staged row length of x (K, or K/2 for a 4-bit head in the tiles of a 2-bit head of length K).
 bool use_resident(int M, int ks) { return M <= 8 && resident_lds_bytes(ks, resident_rows(M, ks)) <= kMaxLds; }
 
-// Workspace: the rerank's per-row hand-off words, then (many-row kernel
-// only) the x of one launch.
+// Workspace: the rerank's per-row hand-off words, then the resident kernel's
+// block maxima (up to 8 rows of up to 64 kFastNV blocks, read by the
+// block-maximum rerank of the one-call path) or the many-row kernel's x of
+// one launch.
 constexpr size_t kHeaderBytes = DH_MAX_M * sizeof(unsigned long long);
+constexpr size_t kMaximaBytes = (size_t)8 * 64 * kFastNV * sizeof(float);
 
 // ks: the staged row length of x when it differs from K (0: K).
 size_t coarse_workspace_bytes(int M, int K, int ks = 0) {
-  if (use_resident(M, ks ? ks : K)) return kHeaderBytes;
+  if (use_resident(M, ks ? ks : K)) return kHeaderBytes + kMaximaBytes;
   return kHeaderBytes + big_workspace_bytes(std::min((M + 15) / 16, kMaxMT), K);
 }
 
@@ -2836,16 +2846,19 @@ int validate_argmax(const int32_t* rr_id, const float* rr_val, int M, int R, con
 // kx: row length of x (K, or K/2 for a 4-bit head run at length K).
 int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs, int kcand,
                   float* cand_val, int32_t* cand_id, float* coarse_out, void* workspace, hipStream_t s,
-                  hipEvent_t ev0, hipEvent_t ev1, int kx = 0, uint16_t* row_out = nullptr, int topk_only = 0) {
+                  hipEvent_t ev0, hipEvent_t ev1, int kx = 0, uint16_t* row_out = nullptr, int topk_only = 0,
+                  float* bmax = nullptr) {
   const int nblk = (N + DH_BLOCK_N - 1) / DH_BLOCK_N;
   const int ncand = nblk * kcand;
   CoarseArgs A{static_cast<const uint16_t*>(x), M, K, N, nblk, reinterpret_cast<const u32x4*>(tiled),
                reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out, row_out, topk_only,
                static_cast<unsigned long long*>(workspace), M, kx ? kx : K};
   A.half_pairs = A.kx < A.K;   // a 4-bit head as draft_head_tile_int4 lays it out
+  A.bmax = nullptr;
   hipError_t e = hipSuccess;
   const int ks = A.kx;   // the row length of x the resident kernel stages
   if (use_resident(M, ks)) {
+    A.bmax = bmax;
     switch (resident_rows(M, ks)) {
       case 1: e = launch_resident<1>(A, s, ev0, ev1); break;
       case 2: e = launch_resident<2>(A, s, ev0, ev1); break;
@@ -2918,9 +2931,9 @@ template <bool kArgmax>
 hipError_t launch_wide(const void* x, const RowSrc& src, int M, int K, int N, const float* cand_val,
                        const int32_t* cand_id, int nblk, int kcand, int R, int32_t* rr_id, float* rr_val,
                        int32_t* out_id, float* out_val, unsigned long long* hand, hipStream_t s,
-                       uint16_t* row_out = nullptr) {
+                       uint16_t* row_out = nullptr, const float* bmax = nullptr) {
   const RerankArgs A{static_cast<const uint16_t*>(x), src, K, N, cand_val,
-                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, hand, row_out};
+                     cand_id, nblk, kcand, R, rr_id, rr_val, out_id, out_val, hand, row_out, bmax};
   auto go = [&](auto nthr, auto nr) {
     constexpr int NTHR = decltype(nthr)::value, NW = NTHR / 64, NR = decltype(nr)::value;
     // ids must fit the hand-off key to split a row; otherwise one part per row
@@ -3174,14 +3187,19 @@ int launch_forward(const void* x, int M, int K, int N, const uint8_t* tiled, con
                    uint16_t* row_out = nullptr, int topk_only = 0) {
   const int ncand = ((N + DH_BLOCK_N - 1) / DH_BLOCK_N) * kcand;
   const int Kc = int4 ? 2 * K : K;
+  int nblk, kc;
+  const bool fast = fast_rerank(N, ncand, R, nblk, kc);
+  // the resident kernel also writes the block maxima contiguously for the
+  // block-maximum rerank (nblk <= 64 kFastNV there)
+  float* bmax = fast && use_resident(M, K)
+                    ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kHeaderBytes) : nullptr;
   int rc = launch_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace, s,
                          reinterpret_cast<hipEvent_t>(coarse_start_event),
-                         reinterpret_cast<hipEvent_t>(coarse_stop_event), K, row_out, topk_only);
+                         reinterpret_cast<hipEvent_t>(coarse_stop_event), K, row_out, topk_only, bmax);
   if (rc) return rc;
-  int nblk, kc;
-  if (fast_rerank(N, ncand, R, nblk, kc)) {   // rerank and argmax in one kernel
+  if (fast) {   // rerank and argmax in one kernel
     hipError_t e = launch_wide<true>(x, src, M, K, N, cand_val, cand_id, nblk, kc, R, rr_id, rr_val, out_id, out_val,
-                                     static_cast<unsigned long long*>(workspace), s, row_out);
+                                     static_cast<unsigned long long*>(workspace), s, row_out, bmax);
     if (e != hipSuccess) return dh::fail(DH_EHIP, "rerank_wide_kernel: %s", hipGetErrorString(e));
     return dh::ok();
   }

@@ -168,11 +168,13 @@ int draft_head_tile_int4(const uint8_t* packed4, const uint16_t* S, const uint16
  * Bytes of device workspace draft_head_coarse / draft_head_forward need for M
  * rows of length K: 1,024 bytes of per-row hand-off words for the one-call
  * path's rerank (a row's exact logits may be split over several workgroups),
- * plus, unless M <= 8 and the resident kernel holds all of x in LDS (any K at
- * M = 1; K <= 39424, 19456, 8704 at M = 2, 3..4, 5..8), the x of one launch
- * of up to 80 rows laid out for the many-row kernel: (K/128) * 4096 * MT +
- * (K/512) * 4096 + 512 bytes with MT = min(ceil(M/16), 5) (861,696 bytes in
- * all at M = 72, K = 5120).
+ * plus, where M <= 8 and the resident kernel holds all of x in LDS (any K at
+ * M = 1; K <= 39424, 19456, 8704 at M = 2, 3..4, 5..8), 65,536 bytes in which
+ * the one-call path's coarse kernel writes each block's maximum once more,
+ * contiguously, for its rerank (66,560 bytes in all); otherwise the x of one
+ * launch of up to 80 rows laid out for the many-row kernel: (K/128) * 4096 *
+ * MT + (K/512) * 4096 + 512 bytes with MT = min(ceil(M/16), 5) (861,696 bytes
+ * in all at M = 72, K = 5120).
  * Errors: DH_EINVAL (null pointer, M < 1), DH_EUNSUP (M > DH_MAX_M), DH_ESHAPE.
  */
 int draft_head_workspace_bytes(int M, int K, size_t* bytes);

@@ -144,11 +144,12 @@ def test_quantize_pack_validation(lib):
 
 def test_workspace_bytes(lib):
     # 1 KiB of per-row hand-off words (128 rows, 8 bytes); the resident
-    # kernel (up to 8 rows while x fits its LDS) needs nothing more
-    # (LDS (K/128) * (256 MP + 4 MP) + blocks * MP * 256 within 160 KB)
+    # kernel (up to 8 rows while x fits its LDS: (K/128) * (256 MP + 4 MP) +
+    # blocks * MP * 256 within 160 KB) adds 64 KiB of block maxima (8 rows of
+    # up to 2048 blocks, fp32)
     head = 1024
     for m, k in ((1, 5120), (1, 65536), (2, 39424), (4, 19456), (8, 5120), (8, 8704)):
-        assert B.draft_head_workspace_bytes(m, k) == head, (m, k)
+        assert B.draft_head_workspace_bytes(m, k) == head + 65536, (m, k)
     # many-row kernel: + (K/128) * 4096 * MT + (K/512) * 4096 + 512 with MT = min(ceil(M/16), 5)
     for m, k in ((2, 39936), (4, 19968), (8, 9216), (9, 512), (16, 1024), (17, 1024), (72, 5120),
                  (80, 5120), (81, 5120), (128, 5120)):
@@ -196,7 +197,7 @@ def test_coarse_validation(lib, via):
     _err(lib, call(wsb=B.draft_head_workspace_bytes(1, 512) - 1), B.DH_EINVAL)
     _err(lib, call(ws=MIS), B.DH_EINVAL)
     need = B.draft_head_workspace_bytes(9, 512)
-    _err(lib, call(M=9), B.DH_EINVAL)
+    _err(lib, call(M=9, K=4096), B.DH_EINVAL)   # one row's workspace at K = 512: too small for 9 x 4096
     _err(lib, call(M=9, ws=FAKE, wsb=need - 16), B.DH_EINVAL)
     _err(lib, call(M=9, ws=MIS, wsb=need), B.DH_EINVAL)
     _err(lib, call(M=9, ws=None, wsb=need), B.DH_EINVAL)
@@ -320,7 +321,7 @@ def test_forward_validation(lib):
         a.update(kw)
         return lib.draft_head_forward(a["x"], a["M"], a["K"], a["N"], a["t"], a["p"], a["w"], a["ldw"],
                                       a["kc"], a["R"], a["cv"], a["ci"], a["ri"], a["rv"], a["oi"],
-                                      a["ov"], a["co"], FAKE, 16384, a["s"], None, None)
+                                      a["ov"], a["co"], FAKE, 1 << 20, a["s"], None, None)
     _err(lib, call(w=None), B.DH_EINVAL)
     _err(lib, call(ri=None), B.DH_EINVAL)
     _err(lib, call(oi=None), B.DH_EINVAL)
