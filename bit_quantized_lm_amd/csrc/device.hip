@@ -517,6 +517,21 @@ __device__ __forceinline__ float row16_sum(float s) {
   return s;
 }
 
+// Lane l's value, in every lane (a lane read, not a shuffle through LDS).
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Maximum over the wave (every lane active): over each DPP row, then the
+// four rows' by lane reads.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_row<0xB1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_row<0x4E>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_row<0x141>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_row<0x140>(__float_as_uint(v))));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
 // ---------------------------------------------------------------------------
 // Coarse kernel, x resident in LDS (M <= 8 and the whole x fits).
 //
@@ -846,7 +861,7 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t* __restrict_
   sum = row16_sum(sum);
   float X[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) X[u] = u < qpb ? __shfl(sum, 16 * u, 64) : 0.f;
+  for (int u = 0; u < 4; ++u) X[u] = u < qpb ? lane_value(sum, 16 * u) : 0.f;
   if (lane < 2) {
     uint32_t part[3][4];
 #pragma unroll
@@ -1360,7 +1375,7 @@ __global__ __launch_bounds__(256) void prep_xh_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fmaxf(fabsf(lo_bf16(v[i][c])), fabsf(hi_bf16(v[i][c]))));
   }
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  mx = wave_max(mx);
   if (lane == 0) wmax[wave] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
@@ -1394,7 +1409,7 @@ __global__ __launch_bounds__(256) void prep_xh_kernel(const uint16_t* __restrict
     sum = row16_sum(sum);
     float X[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) X[u] = __builtin_ldexpf(__shfl(sum, 16 * u, 64), fx);
+    for (int u = 0; u < 4; ++u) X[u] = __builtin_ldexpf(lane_value(sum, 16 * u), fx);
     if (lane < 2) {
       uint32_t part[3][4];
 #pragma unroll
