@@ -897,10 +897,11 @@ constexpr int kScStride = 68;
 // alone from the row's 64 keys in LDS: load_at(r, raw) the keys of run r,
 // tag_at(r, e) 63 - the column of its element e, key_at(c) column c's key (select8_runs;
 // the run loop is rolled: the epilogue runs once per kernel, and its
-// unrolled code would mostly wait for instruction fetch).
+// unrolled code would mostly wait for instruction fetch).  The values written
+// are the keys' scores times `scale` (a power of two: exact, order kept).
 template <class LoadAt, class TagAt, class KeyAt>
 __device__ __forceinline__ void emit_list8(LoadAt load_at, TagAt tag_at, KeyAt key_at, const CoarseArgs& A, int m,
-                                           int b) {
+                                           int b, float scale = 1.0f) {
   uint32_t slot[8];   // 63 - column, or 64 for an empty slot
   dh::select8_runs<true>(load_at, tag_at, key_at, slot);
   float val[8];
@@ -913,7 +914,7 @@ __device__ __forceinline__ void emit_list8(LoadAt load_at, TagAt tag_at, KeyAt k
     // so that the eight reads are in flight together (a conditional read
     // becomes a branch and a wait of its own)
     const uint32_t kv = key_at(col), okm = 0u - (uint32_t)ok;
-    val[i] = __uint_as_float((__float_as_uint(key_f32(kv)) & okm) | (0xFF800000u & ~okm));   // else -inf
+    val[i] = __uint_as_float((__float_as_uint(key_f32(kv) * scale) & okm) | (0xFF800000u & ~okm));   // else -inf
     id[i] = (int)(((uint32_t)(b * 64 + col) & okm) | ~okm);                                 // else -1
   }
   const size_t base = ((size_t)m * A.nblk + b) * A.kcand;
@@ -1589,14 +1590,11 @@ void coarse_h16_kernel(HArgs HA) {
     stage(std::integral_constant<int, 3>{});
   }
   wait_vm<0>();
-  // the coarse scores: the accumulators times 2^-f of their rows
-  float rs[MT][4];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rs[i][r] = __builtin_ldexpf(1.0f, -HA.fexp[16 * i + 4 * hh + r]);
   // Every wave's DMA writes have landed and every wave is done with the ring:
-  // the LDS takes the keys of the workgroup's 8 blocks, row rho = lb MP + m
+  // the LDS takes the keys of the workgroup's 8 blocks (of the accumulators:
+  // a row's coarse scores are its accumulators times 2^-f, a power of two
+  // that keeps their order and is applied to the values a list writes), row
+  // rho = lb MP + m
   // (block lb, row m) in 16 pieces of 16 bytes, piece g holding columns g,
   // g + 16, g + 32, g + 48 (tiles 0..3 of column g: written by the block's
   // one wave, or its two waves 8 bytes each) at position g ^ (rho mod 16), so that
@@ -1604,6 +1602,15 @@ void coarse_h16_kernel(HArgs HA) {
   // thread q selects list q (list l: block l / M, row l % M).  (The fp16
   // kernel takes lists of at most eight.)
   u32x4* sk = reinterpret_cast<u32x4*>(smem);
+  // the 2^-f of the rows of this thread's lists, requested now so that they
+  // arrive during the key phase and the selection
+  constexpr int kNL = (kHBlocks * MP + 64 * W - 1) / (64 * W);   // lists a thread takes, at most
+  float lsc[kNL];
+#pragma unroll
+  for (int u = 0; u < kNL; ++u) {
+    const int l = threadIdx.x + 64 * W * u;
+    lsc[u] = __builtin_ldexpf(1.0f, -HA.fexp[l < kHBlocks * A.M ? l % A.M : 0]);
+  }
   __syncthreads();
   // masks of the live columns and rows, as bits (conditions the compiler
   // would otherwise turn into branches around every key)
@@ -1618,7 +1625,7 @@ void coarse_h16_kernel(HArgs HA) {
       const uint32_t rowm = 0u - (uint32_t)(row < A.M);
       uint32_t kk[NTW];
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) kk[t] = f32_key(acc[i][t][r] * rs[i][r] + 0.0f) & colm[t] & rowm;   // -0 as +0
+      for (int t = 0; t < NTW; ++t) kk[t] = f32_key(acc[i][t][r] + 0.0f) & colm[t] & rowm;   // -0 as +0
       u32x4* piece = sk + rho * 16 + (nn ^ (row & 15));
       if constexpr (NTW == 4) *piece = u32x4{kk[0], kk[1], kk[2], kk[3]};
       else reinterpret_cast<u32x2*>(piece)[part] = u32x2{kk[0], kk[1]};
@@ -1627,17 +1634,25 @@ void coarse_h16_kernel(HArgs HA) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r) {
+        const float rs = __builtin_ldexpf(1.0f, -HA.fexp[16 * i + 4 * hh + r]);
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
           const int row = 16 * i + 4 * hh + r, n = 64 * b + 16 * (T0 + t) + nn;
-          if (blk_ok && n < A.N && row < A.M) store_scores(A, row, n, acc[i][t][r] * rs[i][r]);
+          if (blk_ok && n < A.N && row < A.M) store_scores(A, row, n, acc[i][t][r] * rs);
         }
+      }
   }
   __syncthreads();
-  for (int l = threadIdx.x; l < kHBlocks * A.M; l += 64 * W) {
+#pragma unroll 1
+  for (int u = 0; u < kNL; ++u) {   // rolled, as the selection in it
+    const int l = threadIdx.x + 64 * W * u;
+    if (l >= kHBlocks * A.M) break;
     const int lbl = l / A.M, m = l - lbl * A.M, bq = blockIdx.x * kHBlocks + lbl;
     if (bq >= A.nblk) continue;
+    float sc = lsc[0];
+#pragma unroll
+    for (int v = 1; v < kNL; ++v) sc = u == v ? lsc[v] : sc;
     const u32x4* row = sk + (lbl * MP + m) * 16;
     const int sw = m & 15;
     emit_list8(
@@ -1650,7 +1665,7 @@ void coarse_h16_kernel(HArgs HA) {
           }
         },
         [](int r, int e) { return 63 - 16 * (e & 3) - 2 * r - (e >> 2); },
-        [&](int c) { return reinterpret_cast<const uint32_t*>(row + ((c & 15) ^ sw))[c >> 4]; }, A, m, bq);
+        [&](int c) { return reinterpret_cast<const uint32_t*>(row + ((c & 15) ^ sw))[c >> 4]; }, A, m, bq, sc);
   }
 }
 
