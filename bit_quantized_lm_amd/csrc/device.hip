@@ -2285,15 +2285,19 @@ __device__ __forceinline__ int lane_prefix(unsigned long long bal) {
 // draft_head_coarse writes, so slot b*kcand holds block b's maximum and slot
 // order is column order among equal values):
 //   1. The waves read the block maxima (block lane + 64 j: 32 per lane over
-//      all waves) as (value, slot) keys.  With R <= 64, T' = the R-th largest
-//      of the 64 lane maxima (their value halves, by bisection over the bits
-//      with ballots) is at most the R-th largest block maximum, so every one
-//      of the row's R best candidates is >= T'; if T' lets more than
-//      DH_MAX_R / kcand blocks through (or R > 64), T' = the exact R-th
-//      largest block maximum (radix select by wave 0).
-//   2. The candidates >= T' of the blocks whose maximum is >= T' survive
-//      (at least R, at most DH_MAX_R); each is ranked by counting the
-//      survivors above it, and the first R ranks are the list.
+//      all waves; from the contiguous copy the resident coarse kernel writes
+//      for the one-call path, else at slot b*kcand) as (value, slot) keys.
+//      With R <= 64, T' = the R-th largest of the 64 lane maxima (their
+//      value halves, by bisection over the bits with ballots) is at most the
+//      R-th largest block maximum, so every one of the row's R best
+//      candidates is >= T'; the blocks at or above it are compacted in the
+//      same pass that counts them.  If T' lets more than DH_MAX_R / kcand
+//      blocks through (or R > 64), T' = the exact R-th largest block maximum
+//      (radix select by wave 0) and the blocks are compacted again.
+//   2. The candidates >= T' of those blocks survive (at least R, at most
+//      DH_MAX_R); each is ranked by counting the survivors above it (eight
+//      lanes per key up to 64 survivors), and the first R ranks are the
+//      list.
 // Eight waves per workgroup, four workgroups per row at R = 32: measured per
 // call (K = 5120, N = 124160) against four waves in eight parts, sixteen in
 // two and sixteen in one: 41.2 / 42.5 / 42.9 / 45.3 us at M = 1, 46.4 / 48.2
