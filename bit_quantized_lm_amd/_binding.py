@@ -20,7 +20,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "drafthead.h")
 
 DH_OK, DH_EINVAL, DH_ESHAPE, DH_EUNSUP, DH_EHIP = 0, -1, -2, -3, -4
-DH_NOALLOC_SCRATCH_BYTES = 2 << 20
+DH_NOALLOC_SCRATCH_BYTES = 4 << 20
 BLOCK_N = 64
 GROUP = 128
 

@@ -918,6 +918,7 @@ __device__ __forceinline__ void emit_list8(LoadAt load_at, TagAt tag_at, KeyAt k
     id[i] = (int)(((uint32_t)(b * 64 + col) & okm) | ~okm);                                 // else -1
   }
   const size_t base = ((size_t)m * A.nblk + b) * A.kcand;
+  if (A.bmax) A.bmax[(size_t)m * A.nblk + b] = val[0];
   if (A.kcand == 8) {   // 32-byte aligned: the list is two 16-byte pieces
     reinterpret_cast<f32x4*>(A.cand_val + base)[0] = f32x4{val[0], val[1], val[2], val[3]};
     reinterpret_cast<f32x4*>(A.cand_val + base)[1] = f32x4{val[4], val[5], val[6], val[7]};
@@ -2803,17 +2804,27 @@ bool use_h16(int K, int kx, int mt, int kcand) {
 // ks: the staged row length of x (K, or K/2 for a 4-bit head in the tiles of a 2-bit head of length K).
 bool use_resident(int M, int ks) { return M <= 8 && resident_lds_bytes(ks, resident_rows(M, ks)) <= kMaxLds; }
 
-// Workspace: the rerank's per-row hand-off words, then the resident kernel's
-// block maxima (up to 8 rows of up to 64 kFastNV blocks, read by the
-// block-maximum rerank of the one-call path) or the many-row kernel's x of
-// one launch.
+// Workspace: the rerank's per-row hand-off words; then for the resident
+// kernel the block maxima of up to 8 rows, or for the many-row kernels the x
+// of one launch followed by the block maxima of all M rows.  The maxima (up
+// to 64 kFastNV blocks a row, fp32) are a contiguous copy of each block's
+// slot 0 that the one-call path's coarse pass writes for its block-maximum
+// rerank.
 constexpr size_t kHeaderBytes = DH_MAX_M * sizeof(unsigned long long);
-constexpr size_t kMaximaBytes = (size_t)8 * 64 * kFastNV * sizeof(float);
+constexpr size_t kMaximaRowBytes = (size_t)64 * kFastNV * sizeof(float);
+constexpr size_t kMaximaBytes = 8 * kMaximaRowBytes;
 
 // ks: the staged row length of x when it differs from K (0: K).
 size_t coarse_workspace_bytes(int M, int K, int ks = 0) {
   if (use_resident(M, ks ? ks : K)) return kHeaderBytes + kMaximaBytes;
-  return kHeaderBytes + big_workspace_bytes(std::min((M + 15) / 16, kMaxMT), K);
+  return kHeaderBytes + big_workspace_bytes(std::min((M + 15) / 16, kMaxMT), K) + (size_t)M * kMaximaRowBytes;
+}
+
+// Where the block maxima go in a workspace laid out for (M, K, ks).
+float* workspace_maxima(void* workspace, int M, int K, int ks) {
+  unsigned char* w = static_cast<unsigned char*>(workspace) + kHeaderBytes;
+  if (!use_resident(M, ks ? ks : K)) w += big_workspace_bytes(std::min((M + 15) / 16, kMaxMT), K);
+  return reinterpret_cast<float*>(w);
 }
 
 int validate_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, const uint32_t* pairs,
@@ -2888,11 +2899,10 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
                reinterpret_cast<const u32x4*>(pairs), kcand, cand_val, cand_id, coarse_out, row_out, topk_only,
                static_cast<unsigned long long*>(workspace), M, kx ? kx : K};
   A.half_pairs = A.kx < A.K;   // a 4-bit head as draft_head_tile_int4 lays it out
-  A.bmax = nullptr;
+  A.bmax = bmax;
   hipError_t e = hipSuccess;
   const int ks = A.kx;   // the row length of x the resident kernel stages
   if (use_resident(M, ks)) {
-    A.bmax = bmax;
     switch (resident_rows(M, ks)) {
       case 1: e = launch_resident<1>(A, s, ev0, ev1); break;
       case 2: e = launch_resident<2>(A, s, ev0, ev1); break;
@@ -2913,6 +2923,7 @@ int launch_coarse(const void* x, int M, int K, int N, const uint8_t* tiled, cons
     B.cand_id = cand_id + (size_t)m0 * ncand;
     B.coarse_out = coarse_out ? coarse_out + (size_t)m0 * N : nullptr;
     B.row_out = row_out ? row_out + (size_t)m0 * N : nullptr;
+    B.bmax = bmax ? bmax + (size_t)m0 * nblk : nullptr;
     B.ncnt = m0 == 0 ? M : 0;
     const int mt = (B.M + 15) / 16, mp = 16 * mt;
     u32x4* xslab = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(workspace) + kHeaderBytes);
@@ -3223,10 +3234,9 @@ int launch_forward(const void* x, int M, int K, int N, const uint8_t* tiled, con
   const int Kc = int4 ? 2 * K : K;
   int nblk, kc;
   const bool fast = fast_rerank(N, ncand, R, nblk, kc);
-  // the resident kernel also writes the block maxima contiguously for the
+  // the coarse pass also writes the block maxima contiguously for the
   // block-maximum rerank (nblk <= 64 kFastNV there)
-  float* bmax = fast && use_resident(M, K)
-                    ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kHeaderBytes) : nullptr;
+  float* bmax = fast ? workspace_maxima(workspace, M, Kc, K) : nullptr;
   int rc = launch_coarse(x, M, Kc, N, tiled, pairs, kcand, cand_val, cand_id, coarse_out, workspace, s,
                          reinterpret_cast<hipEvent_t>(coarse_start_event),
                          reinterpret_cast<hipEvent_t>(coarse_stop_event), K, row_out, topk_only, bmax);

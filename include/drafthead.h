@@ -55,7 +55,7 @@ extern "C" {
 #define DH_MAX_K 65536
 #define DH_MAX_KCAND 64
 #define DH_MAX_R 1024
-#define DH_NOALLOC_SCRATCH_BYTES (2u << 20)   /* draft_head_forward_noalloc's static scratch per GPU */
+#define DH_NOALLOC_SCRATCH_BYTES (4u << 20)   /* draft_head_forward_noalloc's static scratch per GPU */
 
 /* Message describing the last error returned on the calling thread ("" if none). */
 const char* draft_head_last_error(void);
@@ -172,9 +172,10 @@ int draft_head_tile_int4(const uint8_t* packed4, const uint16_t* S, const uint16
  * M = 1; K <= 39424, 19456, 8704 at M = 2, 3..4, 5..8), 65,536 bytes in which
  * the one-call path's coarse kernel writes each block's maximum once more,
  * contiguously, for its rerank (66,560 bytes in all); otherwise the x of one
- * launch of up to 80 rows laid out for the many-row kernel: (K/128) * 4096 *
- * MT + (K/512) * 4096 + 512 bytes with MT = min(ceil(M/16), 5) (861,696 bytes
- * in all at M = 72, K = 5120).
+ * launch of up to 80 rows laid out for the many-row kernel, (K/128) * 4096 *
+ * MT + (K/512) * 4096 + 512 bytes with MT = min(ceil(M/16), 5), and the block
+ * maxima of the M rows, 8,192 * M bytes (1,451,520 bytes in all at M = 72,
+ * K = 5120).
  * Errors: DH_EINVAL (null pointer, M < 1), DH_EUNSUP (M > DH_MAX_M), DH_ESHAPE.
  */
 int draft_head_workspace_bytes(int M, int K, size_t* bytes);
@@ -298,12 +299,12 @@ int draft_head_forward(const void* x, int M, int K, int N, const uint8_t* tiled,
  * DEVICE.  draft_head_forward without a workspace, for callers that cannot
  * allocate device memory: code under HIP graph capture, serving loops and
  * harnesses that forbid hipMalloc.  The scratch the call needs lives in a
- * static device array of DH_NOALLOC_SCRATCH_BYTES (2 MiB) that the library
+ * static device array of DH_NOALLOC_SCRATCH_BYTES (4 MiB) that the library
  * holds on every GPU it runs on until the process ends; the call itself
  * makes no hipMalloc, hipFree or other allocating call.  The caller still
  * passes every input and output, as for draft_head_forward.
  * Limit: draft_head_workspace_bytes(M, K) <= DH_NOALLOC_SCRATCH_BYTES (any M
- * up to DH_MAX_M at K <= 12,288; M <= 8 wherever the resident kernel holds
+ * up to DH_MAX_M at K <= 18,432; M <= 8 wherever the resident kernel holds
  * x).  Every call on one GPU shares that GPU's array and overwrites it:
  * calls that overlap on one GPU race, so order them (one stream).  The
  * stream must belong to the current device.

@@ -150,12 +150,14 @@ def test_workspace_bytes(lib):
     head = 1024
     for m, k in ((1, 5120), (1, 65536), (2, 39424), (4, 19456), (8, 5120), (8, 8704)):
         assert B.draft_head_workspace_bytes(m, k) == head + 65536, (m, k)
-    # many-row kernel: + (K/128) * 4096 * MT + (K/512) * 4096 + 512 with MT = min(ceil(M/16), 5)
+    # many-row kernel: + (K/128) * 4096 * MT + (K/512) * 4096 + 512 with MT = min(ceil(M/16), 5),
+    # then 8 KiB of block maxima per row
     for m, k in ((2, 39936), (4, 19968), (8, 9216), (9, 512), (16, 1024), (17, 1024), (72, 5120),
                  (80, 5120), (81, 5120), (128, 5120)):
         mt = min((m + 15) // 16, 5)
-        assert B.draft_head_workspace_bytes(m, k) == head + (k // 128) * 4096 * mt + (k // 512) * 4096 + 512, (m, k)
-    assert B.draft_head_workspace_bytes(72, 5120) == 861_696
+        assert B.draft_head_workspace_bytes(m, k) == \
+            head + (k // 128) * 4096 * mt + (k // 512) * 4096 + 512 + 8192 * m, (m, k)
+    assert B.draft_head_workspace_bytes(72, 5120) == 1_451_520
     out = ctypes.c_size_t()
     _err(lib, lib.draft_head_workspace_bytes(1, 512, None), B.DH_EINVAL)
     _err(lib, lib.draft_head_workspace_bytes(0, 512, ctypes.byref(out)), B.DH_EINVAL)
@@ -431,10 +433,10 @@ def test_forward_noalloc_validation(lib):
     _err(lib, call(M=129), B.DH_EUNSUP)
     _err(lib, call(K=768), B.DH_ESHAPE)
     _err(lib, call(R=81), B.DH_EUNSUP)
-    # the largest K the scratch takes at 80 rows, and the next multiple of 512
-    assert B.draft_head_workspace_bytes(80, 12288) <= B.DH_NOALLOC_SCRATCH_BYTES
-    assert B.draft_head_workspace_bytes(80, 12800) > B.DH_NOALLOC_SCRATCH_BYTES
-    _err(lib, call(M=80, K=12800, ldw=12800), B.DH_EUNSUP)
+    # the largest K the scratch takes at 128 rows, and the next multiple of 512
+    assert B.draft_head_workspace_bytes(128, 18432) <= B.DH_NOALLOC_SCRATCH_BYTES
+    assert B.draft_head_workspace_bytes(128, 18944) > B.DH_NOALLOC_SCRATCH_BYTES
+    _err(lib, call(M=128, K=18944, ldw=18944), B.DH_EUNSUP)
     assert b"scratch" in lib.draft_head_last_error()
     _err(lib, call(M=72, K=65536, ldw=65536), B.DH_EUNSUP)
 
