@@ -88,6 +88,7 @@ CASES = [
     (4, 1024, 5000, 16, 32),
     (2, 512, 131072, 8, 32),
     (8, 512, 131072, 8, 32),   # the one-call path's block-maxima copy full: 8 rows x 2048 blocks
+    (17, 512, 5000, 16, 32),   # many rows, lists longer than eight, the block-maximum rerank
     (2, 512, 131100, 8, 32),
     # R > 64 (exact threshold by radix select) in the separate rerank kernel
     (20, 512, 70000, 8, 100),
