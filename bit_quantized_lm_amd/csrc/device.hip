@@ -2289,7 +2289,7 @@ __device__ __forceinline__ int lane_prefix(unsigned long long bal) {
 //      all waves; from the contiguous copy the resident coarse kernel writes
 //      for the one-call path, else at slot b*kcand) as (value, slot) keys.
 //      With R <= 64, T' = the R-th largest of the 64 lane maxima (their
-//      value halves, by bisection over the bits with ballots) is at most the
+//      value halves cut to 16 bits, by bisection with ballots) is at most the
 //      R-th largest block maximum, so every one of the row's R best
 //      candidates is >= T'; the blocks at or above it are compacted in the
 //      same pass that counts them.  If T' lets more than DH_MAX_R / kcand
@@ -2405,16 +2405,18 @@ __device__ void rerank_list(WideShared& sh, const RerankArgs& A, int m) {
   };
   __syncthreads();
   // T' = (to, 0) with to the R-th largest of the 64 lane maxima's upper
-  // halves (bisection over its bits, counting lanes by ballot; every wave
-  // finds the same value): at least R lanes hold a block maximum >= T', so
-  // T' is at most the R-th largest block maximum.  Its blocks are compacted
-  // at once; the count decides after one barrier whether T' stands.
+  // halves cut to their top 16 bits (bisection over those bits, counting
+  // lanes by ballot; every wave finds the same value): at least R lanes hold
+  // a block maximum >= T', so T' is at most the R-th largest block maximum
+  // (the cut lowers it by less than one bf16 step, letting a few more blocks
+  // through for half the steps).  Its blocks are compacted at once; the
+  // count decides after one barrier whether T' stands.
   uint32_t to = 0u;
   if (R <= 64) {
     uint32_t bo = 0u;
 #pragma unroll
     for (int w = 0; w < NW; ++w) bo = max(bo, sh.bmax[w][lane]);
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 31; bit >= 16; --bit) {
       const uint32_t t = to | (1u << bit);
       if (__popcll(__ballot(bo >= t)) >= R) to = t;
     }
