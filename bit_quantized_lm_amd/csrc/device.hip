@@ -2286,8 +2286,8 @@ __device__ __forceinline__ int lane_prefix(unsigned long long bal) {
 // draft_head_coarse writes, so slot b*kcand holds block b's maximum and slot
 // order is column order among equal values):
 //   1. The waves read the block maxima (block lane + 64 j: 32 per lane over
-//      all waves; from the contiguous copy the resident coarse kernel writes
-//      for the one-call path, else at slot b*kcand) as (value, slot) keys.
+//      all waves; from the contiguous copy the coarse kernels write for the
+//      one-call path, else at slot b*kcand) as (value, slot) keys.
 //      With R <= 64, T' = the R-th largest of the 64 lane maxima (their
 //      value halves cut to 16 bits, by bisection with ballots) is at most the
 //      R-th largest block maximum, so every one of the row's R best
